@@ -1,0 +1,251 @@
+"""Grouped GEMMs and the unfused forward / backward of the grouped MLP.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources:
+* "GEMM + Swiglu fused Grouped MLP for MXFP8" -- sequence diagram: forward
+  FC1 GLU kernel (x and fc1 weight in MXFP8, prob, bf16 pre-activation
+  ``c_tensor``, MXFP8 activation row + column) then the fc2 GEMM; backward
+  FC2 dGLU kernel (dy in MXFP8, saved pre-activation, fc2 weight column-wise ->
+  fc1 grad in MXFP8 and ``dprob``), FC1 dgrad, and both wgrads as grouped GEMMs.
+* "Reduce NVFP4 quantization work for the fused GroupedMLP fc2 input ..." --
+  Description and commits: the SReLU path, the accumulator rounded through the
+  C dtype (bf16) before the activation, the fc2 input re-built in backward.
+* The MLP statement: GroupedLinear (fc1) + SwiGLU or squared ReLU scaled by the
+  router probability + GroupedLinear (fc2) over per-expert token splits.
+
+The fused path reaches exactly the result of this unfused per-expert sequence:
+quantize -> GEMM -> bf16 -> activation * prob -> bf16 -> quantize -> GEMM.
+Activation recompute regenerates the same bf16 activation, so it has no
+separate definition here.
+
+Readings (the pages are silent on these):
+* Linear weights are stored [out, in]: W1 [E, F1, H], W2 [E, H, ffn].
+* SwiGLU: h = [gate | up] along F1 = 2 * ffn; a = silu(gate) * up * p.
+  SReLU: F1 = ffn; a = max(h, 0)^2 * p.  p multiplies after the activation,
+  before the bf16 rounding.
+* h, a, y, da, dh, dx and the weight gradients are bf16 (round to nearest
+  even); dprob is fp32.  Activations are evaluated in fp64 from bf16 h.
+* Backward operands: dy row-wise (blocks along H) times W2 quantized along H
+  (da); dh row-wise (blocks along F1) times W1 quantized along F1 (dx); the
+  wgrads contract over tokens with both operands column-wise.  For NVFP4 the
+  column-wise (wgrad) operands carry the RHT with one recipe-wide mask (the
+  same orthogonal transform on both, so it cancels in the product); weights
+  never get the RHT.
+* NVFP4 global scales: per group from the pre-RHT amax for row-wise casts and
+  the post-RHT amax for column-wise casts; per expert (amax of the whole
+  weight matrix) for weights.
+* Empty experts contribute no rows and a zero weight gradient.
+"""
+import numpy as np
+
+from .formats import bf16_bits_to_f64, f64_to_bf16_bits, round_bf16
+from .quant import (mxfp8_dequant_rows, mxfp8_group_quantize, mxfp8_quantize_rows,
+                    nvfp4_dequant_packed, nvfp4_group_quantize_with_amax, padded)
+from .rht import group_hadamard_amax
+
+SWIGLU = "swiglu"
+SRELU = "srelu"
+MXFP8 = "mxfp8"
+NVFP4 = "nvfp4"
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def act_forward(h, activation):
+    """Activation value without the prob, from bf16 h (fp64)."""
+    if activation == SWIGLU:
+        f = h.shape[1] // 2
+        g, u = h[:, :f], h[:, f:]
+        return g * _sigmoid(g) * u
+    r = np.maximum(h, 0.0)
+    return r * r
+
+
+def act_backward(h, da, p, activation):
+    """(dh, dprob) for a = act(h) * p given da = dL/da; dh unrounded fp64, dprob fp64."""
+    if activation == SWIGLU:
+        f = h.shape[1] // 2
+        g, u = h[:, :f], h[:, f:]
+        sg = _sigmoid(g)
+        silu = g * sg
+        dgate = da * p[:, None] * u * sg * (1.0 + g * (1.0 - sg))
+        dup = da * p[:, None] * silu
+        dprob = np.sum(da * silu * u, axis=1)
+        return np.concatenate([dgate, dup], axis=1), dprob
+    r = np.maximum(h, 0.0)
+    dh = da * p[:, None] * 2.0 * r
+    dprob = np.sum(da * r * r, axis=1)
+    return dh, dprob
+
+
+# ----------------------------------------------------------------------------- GEMM
+def grouped_gemm_nt(a_groups, b_groups):
+    """C_g = A_g @ B_g^T in fp64 for every group (A_g [m, K], B_g [n, K])."""
+    return [a @ b.T for a, b in zip(a_groups, b_groups)]
+
+
+def _split_rows(t, m_splits):
+    out, off = [], 0
+    for m in m_splits:
+        out.append(t[off:off + m])
+        off += m
+    return out
+
+
+# ----------------------------------------------------------------------------- operands
+class Recipe:
+    def __init__(self, kind, sign_mask=0):
+        assert kind in (MXFP8, NVFP4)
+        self.kind = kind
+        self.sign_mask = int(sign_mask) & 0xFFFF
+
+
+def quantize_activation(x_bits, m_splits, recipe, row=True, col=True, amax=None):
+    """Group-quantize an activation-like tensor; returns (quantized dict, dequantized views).
+
+    Dequantized views: ``row`` [M, K] fp64 and ``col`` = per-group [K, P_g] fp64.
+    For NVFP4 the per-group (pre, post) amax is computed here unless given.
+    """
+    deq = {}
+    if recipe.kind == MXFP8:
+        q = mxfp8_group_quantize(x_bits, m_splits, row=row, col=col)
+        if row:
+            deq["row"] = mxfp8_dequant_rows(q["row_data"], q["row_scale"])
+        if col:
+            deq["col"] = [mxfp8_dequant_rows(d, s) for d, s in q["col_groups"]]
+        return q, deq
+    if amax is None:
+        amax = group_hadamard_amax(x_bits, m_splits, recipe.sign_mask)
+    pre, post = amax
+    q = nvfp4_group_quantize_with_amax(x_bits, m_splits, pre, post, recipe.sign_mask,
+                                       row=row, col=col, rht=True)
+    q["amax_pre"], q["amax_post"] = pre, post
+    if row:
+        rows = []
+        for g, xg in enumerate(_split_rows(np.arange(x_bits.shape[0]), m_splits)):
+            if len(xg):
+                rows.append(nvfp4_dequant_packed(q["row_data"][xg], q["row_scale"][xg], pre[g]))
+        deq["row"] = np.concatenate(rows) if rows else np.zeros((0, x_bits.shape[1]))
+    if col:
+        deq["col"] = [nvfp4_dequant_packed(d, s, post[g]) for g, (d, s) in enumerate(q["col_groups"])]
+    return q, deq
+
+
+def quantize_weight(w_bits, recipe):
+    """Quantize stacked weights [E, N, K] for fprop (blocks along K) and dgrad (blocks along N).
+
+    Returns (quantized dict, dequantized dict) with ``row`` = [E, N, K] and ``colT`` =
+    [E, K, N] (the dgrad operand stored with its contraction dim N last).
+    """
+    e, n, k = w_bits.shape
+    flat = w_bits.reshape(e * n, k)
+    splits = [n] * e
+    if recipe.kind == MXFP8:
+        q = mxfp8_group_quantize(flat, splits, row=True, col=True)
+        row = mxfp8_dequant_rows(q["row_data"], q["row_scale"]).reshape(e, n, k)
+        colT = np.stack([mxfp8_dequant_rows(d, s) for d, s in q["col_groups"]]) if e else np.zeros((0, k, n))
+        return q, {"row": row, "colT": colT}
+    w = bf16_bits_to_f64(flat).reshape(e, n, k)
+    amax = np.array([np.max(np.abs(w[i])) if w[i].size else 0.0 for i in range(e)], dtype=np.float32)
+    q = nvfp4_group_quantize_with_amax(flat, splits, amax, amax, 0, row=True, col=True, rht=False)
+    q["amax"] = amax
+    row = np.stack([nvfp4_dequant_packed(q["row_data"][i * n:(i + 1) * n], q["row_scale"][i * n:(i + 1) * n],
+                                         amax[i]) for i in range(e)])
+    colT = np.stack([nvfp4_dequant_packed(d, s, amax[i]) for i, (d, s) in enumerate(q["col_groups"])])
+    return q, {"row": row, "colT": colT}
+
+
+# ----------------------------------------------------------------------------- forward
+def forward(x_bits, m_splits, w1_bits, w2_bits, probs, activation, recipe, wq1=None, wq2=None):
+    """Unfused grouped MLP forward.  Returns a dict of every intermediate.
+
+    y = bf16( Q(a) . Q(W2)^T ),  a = bf16( act(h) * p ),  h = bf16( Q(x) . Q(W1)^T ).
+    """
+    m_splits = [int(m) for m in m_splits]
+    p = np.asarray(probs, dtype=np.float32).astype(np.float64)
+    if wq1 is None:
+        wq1 = quantize_weight(w1_bits, recipe)
+    if wq2 is None:
+        wq2 = quantize_weight(w2_bits, recipe)
+    xq, xd = quantize_activation(x_bits, m_splits, recipe, row=True, col=True)
+    h_groups = grouped_gemm_nt(_split_rows(xd["row"], m_splits), list(wq1[1]["row"]))
+    h = round_bf16(np.concatenate(h_groups)) if h_groups else np.zeros((0, w1_bits.shape[1]))
+    a = round_bf16(act_forward(h, activation) * p[:, None])
+    a_bits = f64_to_bf16_bits(a)
+    aq, ad = quantize_activation(a_bits, m_splits, recipe, row=True, col=True)
+    y_groups = grouped_gemm_nt(_split_rows(ad["row"], m_splits), list(wq2[1]["row"]))
+    y = np.concatenate(y_groups) if y_groups else np.zeros((0, w2_bits.shape[1]))
+    return {
+        "m_splits": m_splits, "activation": activation, "recipe": recipe, "probs": p,
+        "xq": xq, "xd": xd, "wq1": wq1, "wq2": wq2,
+        "h_f64": np.concatenate(h_groups) if h_groups else h, "h": h, "h_bits": f64_to_bf16_bits(h),
+        "a": a, "a_bits": a_bits, "aq": aq, "ad": ad,
+        "y_f64": y, "y_bits": f64_to_bf16_bits(y),
+    }
+
+
+# ----------------------------------------------------------------------------- backward
+def backward(fwd, dy_bits):
+    """Unfused grouped MLP backward from the forward's intermediates.
+
+    da = bf16( Q_row(dy) . Q(W2 along H) ),  (dh, dprob) = act'(h, da, p) with dh -> bf16,
+    dx = bf16( Q_row(dh) . Q(W1 along F1) ),
+    dW2_g = bf16( Q_col(dy_g)^T . Q_col(a_g) ),  dW1_g = bf16( Q_col(dh_g)^T . Q_col(x_g) ).
+    """
+    m_splits, recipe, act = fwd["m_splits"], fwd["recipe"], fwd["activation"]
+    p = fwd["probs"]
+    e = len(m_splits)
+    dyq, dyd = quantize_activation(dy_bits, m_splits, recipe, row=True, col=True)
+    da_groups = grouped_gemm_nt(_split_rows(dyd["row"], m_splits), list(fwd["wq2"][1]["colT"]))
+    da = round_bf16(np.concatenate(da_groups))
+    dh_raw, dprob = act_backward(fwd["h"], da, p, act)
+    dh = round_bf16(dh_raw)
+    dh_bits = f64_to_bf16_bits(dh)
+    dhq, dhd = quantize_activation(dh_bits, m_splits, recipe, row=True, col=True)
+    dx_groups = grouped_gemm_nt(_split_rows(dhd["row"], m_splits), list(fwd["wq1"][1]["colT"]))
+    dx = np.concatenate(dx_groups)
+    n_h, n_f = dy_bits.shape[1], fwd["a"].shape[1]
+    n_f1 = dh.shape[1]
+    dw2 = np.zeros((e, n_h, n_f))
+    dw1 = np.zeros((e, n_f1, n_h))
+    for g in range(e):
+        if m_splits[g] == 0:
+            continue
+        dw2[g] = dyd["col"][g] @ fwd["ad"]["col"][g].T
+        dw1[g] = dhd["col"][g] @ fwd["xd"]["col"][g].T
+    return {
+        "dyq": dyq, "dyd": dyd, "da_f64": np.concatenate(da_groups), "da": da,
+        "dh": dh, "dh_bits": dh_bits, "dhq": dhq, "dhd": dhd,
+        "dprob": dprob.astype(np.float32),
+        "dx_f64": dx, "dx_bits": f64_to_bf16_bits(dx),
+        "dw1_f64": dw1, "dw1_bits": f64_to_bf16_bits(dw1),
+        "dw2_f64": dw2, "dw2_bits": f64_to_bf16_bits(dw2),
+    }
+
+
+def reference_mlp_f64(x, m_splits, w1, w2, probs, activation):
+    """Unquantized fp64 grouped MLP forward (no rounding anywhere), for format-error sanity checks."""
+    out, off = [], 0
+    for g, m in enumerate(m_splits):
+        xg = x[off:off + m]
+        h = xg @ w1[g].T
+        a = act_forward(h, activation) * probs[off:off + m, None]
+        out.append(a @ w2[g].T)
+        off += m
+    return np.concatenate(out)
+
+
+def rel_fro(a, b):
+    """Relative Frobenius error ||a - b|| / ||b||."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb else float(np.linalg.norm(a - b))
+
+
+__all__ = ["forward", "backward", "grouped_gemm_nt", "quantize_activation", "quantize_weight",
+           "act_forward", "act_backward", "Recipe", "reference_mlp_f64", "rel_fro",
+           "SWIGLU", "SRELU", "MXFP8", "NVFP4", "padded", "mxfp8_quantize_rows"]

@@ -1,0 +1,138 @@
+"""Pins for the oracle's grouped GEMMs, activations and forward / backward (CPU only)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from oracle import mlp as O
+from workloads import small_case
+
+
+def test_grouped_gemm_brute_force_loops():
+    rng = np.random.default_rng(20)
+    splits = [0, 1, 31, 33, 0, 64]
+    n, k = 5, 9
+    a = rng.integers(-3, 4, size=(sum(splits), k)).astype(np.float64)
+    b = rng.integers(-3, 4, size=(len(splits), n, k)).astype(np.float64)
+    got = O.grouped_gemm_nt(O._split_rows(a, splits), list(b))
+    off = 0
+    for g, m in enumerate(splits):
+        want = np.zeros((m, n))
+        for i in range(m):
+            for j in range(n):
+                s = 0.0
+                for t in range(k):
+                    s += a[off + i, t] * b[g, j, t]
+                want[i, j] = s
+        assert np.array_equal(got[g], want)
+        off += m
+
+
+def test_one_expert_is_a_dense_gemm():
+    rng = np.random.default_rng(21)
+    a = rng.standard_normal((40, 64))
+    b = rng.standard_normal((24, 64))
+    got = O.grouped_gemm_nt([a], [b])[0]
+    want = torch.nn.functional.linear(torch.from_numpy(a), torch.from_numpy(b)).numpy()
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("act", [O.SWIGLU, O.SRELU])
+def test_activation_derivatives_by_central_differences(act):
+    rng = np.random.default_rng(22)
+    f = 6
+    n1 = 2 * f if act == O.SWIGLU else f
+    h = rng.standard_normal((4, n1)) * 2
+    h[0, 0] = 0.0
+    h[1, 1] = -1.5
+    p = rng.random(4)
+    da = rng.standard_normal((4, f))
+    dh, dprob = O.act_backward(h, da, p, act)
+    eps = 1e-6
+
+    def loss(hh, pp):
+        return np.sum(da * O.act_forward(hh, act) * pp[:, None])
+
+    for i in range(4):
+        for j in range(n1):
+            if act == O.SRELU and abs(h[i, j]) < 1e-3:
+                continue
+            hp, hm = h.copy(), h.copy()
+            hp[i, j] += eps
+            hm[i, j] -= eps
+            num = (loss(hp, p) - loss(hm, p)) / (2 * eps)
+            assert abs(num - dh[i, j]) < 1e-6 * max(1, abs(num))
+        pp, pm = p.copy(), p.copy()
+        pp[i] += eps
+        pm[i] -= eps
+        num = (loss(h, pp) - loss(h, pm)) / (2 * eps)
+        assert abs(num - dprob[i]) < 1e-6 * max(1, abs(num))
+    if act == O.SRELU:
+        assert dh[1, 1] == 0.0 and dh[0, 0] == 0.0
+
+
+def _torch_reference(wl, act):
+    """fp64 autograd of the unquantized grouped MLP (no rounding anywhere)."""
+    x = torch.from_numpy(F.bf16_bits_to_f64(wl.x)).requires_grad_()
+    w1 = torch.from_numpy(F.bf16_bits_to_f64(wl.w1)).requires_grad_()
+    w2 = torch.from_numpy(F.bf16_bits_to_f64(wl.w2)).requires_grad_()
+    p = torch.from_numpy(wl.probs.astype(np.float64)).requires_grad_()
+    ys, off = [], 0
+    for g, m in enumerate(wl.m_splits.tolist()):
+        h = x[off:off + m] @ w1[g].T
+        if act == O.SWIGLU:
+            f = h.shape[1] // 2
+            a = torch.nn.functional.silu(h[:, :f]) * h[:, f:]
+        else:
+            a = torch.relu(h) ** 2
+        ys.append((a * p[off:off + m, None]) @ w2[g].T)
+        off += m
+    y = torch.cat(ys)
+    dy = torch.from_numpy(F.bf16_bits_to_f64(wl.dy))
+    (y * dy).sum().backward()
+    return y.detach().numpy(), x.grad.numpy(), p.grad.numpy(), w1.grad.numpy(), w2.grad.numpy()
+
+
+@pytest.mark.parametrize("recipe,act,tol", [(O.MXFP8, O.SWIGLU, 0.12), (O.NVFP4, O.SRELU, 0.35),
+                                             (O.MXFP8, O.SRELU, 0.12), (O.NVFP4, O.SWIGLU, 0.35)])
+def test_forward_backward_close_to_unquantized_autograd(recipe, act, tol):
+    """Within the quantization-format error of torch fp64 autograd of the same MLP.
+
+    Catches transposed operands, swapped gate/up halves, a missing prob or a wrong
+    derivative anywhere in the oracle's forward or backward: each of those is O(1) off.
+    """
+    wl = small_case([0, 37, 64, 5, 90], 64, 96, activation=act, recipe=recipe, seed=3)
+    rec = O.Recipe(recipe, wl.sign_mask)
+    fwd = O.forward(wl.x, wl.m_splits, wl.w1, wl.w2, wl.probs, act, rec)
+    bwd = O.backward(fwd, wl.dy)
+    y, dx, dp, dw1, dw2 = _torch_reference(wl, act)
+    assert O.rel_fro(fwd["y_f64"], y) < tol
+    assert O.rel_fro(bwd["dx_f64"], dx) < tol * 1.5
+    assert O.rel_fro(bwd["dprob"], dp) < tol
+    assert O.rel_fro(bwd["dw1_f64"], dw1) < tol * 1.5
+    assert O.rel_fro(bwd["dw2_f64"], dw2) < tol
+    # empty expert: zero weight gradient
+    assert np.all(bwd["dw1_f64"][0] == 0) and np.all(bwd["dw2_f64"][0] == 0)
+
+
+def test_recompute_regenerates_the_activation_bitwise():
+    """Rebuilding a from the saved bf16 h gives the forward's a and the same column-wise cast."""
+    wl = small_case([33, 0, 70], 64, 64, activation=O.SRELU, recipe=O.NVFP4, seed=4)
+    rec = O.Recipe(O.NVFP4, wl.sign_mask)
+    fwd = O.forward(wl.x, wl.m_splits, wl.w1, wl.w2, wl.probs, O.SRELU, rec)
+    a2 = F.round_bf16(O.act_forward(fwd["h"], O.SRELU) * fwd["probs"][:, None])
+    a2_bits = F.f64_to_bf16_bits(a2)
+    assert np.array_equal(a2_bits, fwd["a_bits"])
+    # quantize the regenerated tensor with the forward's saved amax: identical column-wise data
+    q2, _ = O.quantize_activation(a2_bits, fwd["m_splits"], rec, row=False, col=True,
+                                  amax=(fwd["aq"]["amax_pre"], fwd["aq"]["amax_post"]))
+    assert np.array_equal(q2["col_data"], fwd["aq"]["col_data"])
+    assert np.array_equal(q2["col_scale"], fwd["aq"]["col_scale"])
+
+
+def test_swiglu_halves_and_prob_placement():
+    h = np.array([[1.0, -2.0, 3.0, 0.5]])       # gate = [1, -2], up = [3, 0.5]
+    got = O.act_forward(h, O.SWIGLU)
+    sig = lambda z: 1 / (1 + np.exp(-z))
+    assert np.allclose(got, [[1 * sig(1) * 3, -2 * sig(-2) * 0.5]], rtol=1e-15)
+    assert np.array_equal(O.act_forward(np.array([[-1.0, 2.0]]), O.SRELU), [[0.0, 4.0]])
