@@ -1,0 +1,259 @@
+/*
+ * gmlp -- fused MoE grouped MLP with MXFP8 / NVFP4 group quantization on MI355X (gfx950).
+ *
+ * C ABI of libgmlp.so.  Every entry point is stream-ordered on the caller's
+ * hipStream_t, performs no host synchronisation and no device allocation, and
+ * keeps no pointer beyond the call.  All tensors are caller-owned device
+ * buffers passed as plain pointers; sizes are host integers.
+ *
+ * Errors: every argument is validated before anything is enqueued.  On error
+ * nothing is enqueued, a status is returned and gmlp_last_error() (thread-local)
+ * names the reason.  A failure of the launch itself returns GMLP_HIP_ERROR.
+ * Device-side split sizes that do not add up to the host row count M are
+ * clamped on the device so that no kernel reads or writes out of bounds; the
+ * condition is recorded in the workspace and reported by gmlp_read_device_flags().
+ *
+ * Sources (the pages this library implements):
+ *  [MX]  "GEMM + Swiglu fused Grouped MLP for MXFP8" (TransformerEngine PR 2769):
+ *        Greptile summary and sequence diagram.
+ *  [NV]  "Reduce NVFP4 quantization work for the fused GroupedMLP fc2 input with
+ *        activation recompute" (TransformerEngine PR 3837): Description, Changes,
+ *        commit messages.
+ *  [FB]  "Add NVTE_CUTEDSL_FUSED_GROUPED_MLP_WARN_FALLBACK ..." (TransformerEngine
+ *        PR 3631): Changes (the reasons a grouped MLP cannot be fused).
+ *
+ * Notation: G groups (experts), group g owns m_g consecutive rows, M = sum m_g.
+ * P_g = m_g rounded up to 128.  "row-wise" = blocks along the last dimension;
+ * "column-wise" = each group's [m_g, K] slab transposed to [K, P_g] (zero
+ * padded) with blocks along tokens; group g's column-wise data starts at element
+ * K * sum_{h<g} P_h.
+ *
+ * MXFP8: 32-element blocks, E4M3 data (round to nearest even, saturating),
+ *   E8M0 scale code = clamp(floor(log2 amax) - 8, -127, 127) + 127; an all-zero
+ *   block gets code 127.
+ * MXFP8 MFMA-ready scales: for a scale matrix [R, nkb] the u32 array
+ *   [ceil(nkb/4), R] whose word (t, r) holds blocks 4t..4t+3 of row r in bytes
+ *   0..3 (missing blocks = 127).  Column-wise: each group's [K, P_g/32] matrix
+ *   converted on its own, at word offset K * sum_{h<g} P_h/128.
+ * NVFP4: 16-element blocks, E2M1 data packed two per byte (element 2i in the low
+ *   nibble), E4M3 block scales, fp32 global scale S = 2688 / amax per group
+ *   (S = 1 if amax = 0; clipped to FLT_MAX).  Row-wise casts use the group's
+ *   pre-RHT amax; column-wise casts apply the signed 16x16 Hadamard transform
+ *   along tokens and use the post-RHT amax [NV, Changes].
+ */
+#ifndef GMLP_H
+#define GMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GMLP_OK = 0,
+  GMLP_INVALID_ARG = 1,   /* a null pointer, a bad size or an inconsistent argument */
+  GMLP_UNSUPPORTED = 2,   /* device, recipe, activation or dimensions the library does not handle [FB] */
+  GMLP_WORKSPACE = 3,     /* workspace or context buffer smaller than gmlp_query_sizes() reports */
+  GMLP_HIP_ERROR = 4      /* a HIP runtime call or kernel launch failed */
+} gmlp_status;
+
+typedef enum { GMLP_MXFP8 = 0, GMLP_NVFP4_RHT = 1 } gmlp_recipe_kind;
+typedef enum { GMLP_SWIGLU = 0, GMLP_SRELU = 1 } gmlp_activation;
+typedef enum { GMLP_OUT_BF16 = 0, GMLP_OUT_FP32 = 1 } gmlp_out_dtype;
+
+/* Recipe [FB, Changes]: MXFP8 (E4M3 data for activations and gradients alike),
+ * or NVFP4 with the randomized Hadamard transform (NVFP4 without RHT is not
+ * supported).  rht_sign_mask: bit j set = token j of each 16-token block is
+ * negated before the Hadamard [NV, Changes]; ignored for MXFP8. */
+typedef struct {
+  int32_t kind;            /* gmlp_recipe_kind */
+  uint32_t rht_sign_mask;  /* low 16 bits used */
+} gmlp_recipe;
+
+/* A group-quantized tensor [MX, Greptile summary: flat 1-D data and scale
+ * buffers with per-group offsets].  Every pointer is device memory owned by the
+ * caller; a pointer the call does not need may be NULL.
+ *   row_data       MXFP8 u8 [M, K];              NVFP4 u8 [M, K/2]
+ *   row_scale      MXFP8 E8M0 u8 [M, K/32];      NVFP4 E4M3 u8 [M, K/16]
+ *   row_scale_mfma MXFP8 u32 [ceil(K/128), M]    (unused for NVFP4)
+ *   col_data       MXFP8 u8 [K * sum P_g];       NVFP4 u8 [K * sum P_g / 2]
+ *   col_scale      MXFP8 u8 [K * sum P_g / 32];  NVFP4 u8 [K * sum P_g / 16]
+ *   col_scale_mfma MXFP8 u32 [K * sum P_g/128]
+ *   amax_pre, amax_post  NVFP4 fp32 [G] (per-group pre-/post-RHT amax) */
+typedef struct {
+  void* row_data;
+  void* row_scale;
+  void* row_scale_mfma;
+  void* col_data;
+  void* col_scale;
+  void* col_scale_mfma;
+  float* amax_pre;
+  float* amax_post;
+} gmlp_grouped_q;
+
+/* Quantized stacked weights for one GroupedLinear, W [E, N, K] (Linear layout
+ * [out, in]) [MX, Greptile summary: stacked and discrete weights].
+ *   fprop operand: blocks along K  -> row_data [E*N, K(/2)], row scales
+ *   dgrad operand: blocks along N  -> col_data [E, K, N(/2)], col scales (W^T per expert)
+ *   NVFP4: amax [E] (one global scale per expert for both casts; weights get no RHT). */
+typedef gmlp_grouped_q gmlp_weight_q;
+
+/* ------------------------------------------------------------------ queries */
+
+/* Thread-local text of the last error (never NULL). */
+const char* gmlp_last_error(void);
+
+/* Host-only support check [FB, Changes: system / recipe / activation / dims].
+ * arch: a gfx target name such as "gfx950", or NULL to query device 0.
+ * Returns GMLP_OK or GMLP_UNSUPPORTED / GMLP_INVALID_ARG with the reason set. */
+gmlp_status gmlp_check_support(const char* arch, int32_t experts, int64_t hidden, int64_t ffn,
+                               int32_t activation, gmlp_recipe recipe);
+
+/* Sizes (bytes) of the caller-owned buffers for one forward + backward:
+ *   ctx_bytes: tensors the forward saves for the backward;
+ *   ws_bytes:  scratch of one forward or backward call;
+ *   quant_ws_bytes: scratch of the stand-alone quantize calls. */
+typedef struct {
+  size_t ctx_bytes;
+  size_t ws_bytes;
+  size_t quant_ws_bytes;
+} gmlp_sizes;
+
+gmlp_status gmlp_query_sizes(int64_t M, int32_t experts, int64_t hidden, int64_t ffn,
+                             int32_t activation, gmlp_recipe recipe, int32_t recompute,
+                             gmlp_sizes* out);
+
+/* Reads (synchronously, on the given stream) the device flag word that kernels
+ * set when the device split sizes were clamped (bit 0: negative split, bit 1:
+ * splits sum past M, bit 2: splits sum short of M).  Diagnostic only. */
+gmlp_status gmlp_read_device_flags(const void* ws, uint32_t* flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------ group quantization */
+
+/* Group quantize a bf16 tensor x [M, K] whose rows are split into G groups by
+ * the device int32 array m_splits [G] [MX, sequence diagram: MXFP8 quantize of
+ * x and dy; NV, Description: the fc2-input group quantize].
+ * MXFP8: one pass, row-wise and/or column-wise.  NVFP4: the Hadamard-amax pass
+ * (writes out->amax_pre/post) followed by the cast, as two launches.
+ * K % 32 == 0.  ws: >= quant_ws_bytes of gmlp_query_sizes. */
+gmlp_status gmlp_group_quantize(const void* x, int64_t M, int64_t K, const int32_t* m_splits,
+                                int32_t G, gmlp_recipe recipe, int32_t want_row, int32_t want_col,
+                                const gmlp_grouped_q* out, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Per-group pre-RHT amax (max |x| over the group's rows) and post-RHT amax (max
+ * |bf16(H S x)| over every 16-token block of every column of the group, padded
+ * with zeros), both in one read of x [NV, Changes: nvfp4_group_hadamard_amax].
+ * Outputs fp32 [G]. */
+gmlp_status gmlp_group_hadamard_amax(const void* x, int64_t M, int64_t K, const int32_t* m_splits,
+                                     int32_t G, uint32_t rht_sign_mask, float* amax_pre,
+                                     float* amax_post, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* NVFP4 cast from given per-group amax (out->amax_pre / amax_post are read, not
+ * written) [NV, Changes: nvfp4_group_quantize_with_amax].  Row-wise with the
+ * pre-RHT amax, column-wise (with the RHT) with the post-RHT amax. */
+gmlp_status gmlp_group_quantize_with_amax(const void* x, int64_t M, int64_t K,
+                                          const int32_t* m_splits, int32_t G, gmlp_recipe recipe,
+                                          int32_t want_row, int32_t want_col,
+                                          const gmlp_grouped_q* out, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
+
+/* Quantize weights W [E, N, K] bf16 for fprop (blocks along K) and dgrad (blocks
+ * along N), no RHT.  w: stacked base pointer, or NULL with w_ptrs = a HOST array
+ * of E device pointers to the experts' [N, K] matrices (discrete weights) [MX,
+ * Greptile summary].  Output in the stacked layout of gmlp_weight_q.  N, K must be
+ * multiples of 128.  Scale words are per expert: row_scale_mfma [E][K/128][N],
+ * col_scale_mfma [E][N/128][K]. */
+gmlp_status gmlp_weight_quantize(const void* w, const void* const* w_ptrs, int32_t E, int64_t N,
+                                 int64_t K, gmlp_recipe recipe, const gmlp_weight_q* out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ grouped GEMM (test / debug export) */
+
+typedef enum {
+  GMLP_GEMM_FPROP = 0,  /* C[rows of group g, N] = A_g [m_g, K] . B_g [N, K]^T   (A row-wise, B = weight) */
+  GMLP_GEMM_WGRAD = 1   /* C_g [N_a, N_b] = A_g [N_a, P_g] . B_g [N_b, P_g]^T       (both column-wise)   */
+} gmlp_gemm_layout;
+
+/* One grouped GEMM on already-quantized operands, fp32 accumulation, output
+ * bf16 or fp32 (round to nearest even) [MX, sequence diagram: the fc1, fc2,
+ * dgrad and wgrad grouped GEMMs].
+ * FPROP: a = row-wise quantized [M, K] tensor, b = weight fprop operand
+ *        (b->row_*), n = N, k = K; C [M, N].
+ * WGRAD: a, b = column-wise quantized tensors with rows N_a = n, N_b = k;
+ *        C [G, n, k]; empty groups write zeros. */
+gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_grouped_q* a,
+                              const gmlp_grouped_q* b, const int32_t* m_splits, int32_t G,
+                              int64_t M, int64_t n, int64_t k, void* c, int32_t out_dtype,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ fused grouped MLP */
+
+/* Forward [MX, sequence diagram; NV, Description and Changes]:
+ *   h = bf16(Q(x) Q(W1)^T)   a = bf16(act(h) * prob)   y = bf16(Q(a) Q(W2)^T)
+ * act = SwiGLU (h = [gate | up], F1 = 2 ffn) or squared ReLU (F1 = ffn).
+ * recompute != 0: the forward casts the fc2 input row-wise only and the
+ * backward rebuilds it from h (NVFP4: with the amax saved here).
+ * ctx must stay untouched between this call and the matching backward. */
+typedef struct {
+  const void* x;              /* bf16 [M, H] */
+  const int32_t* m_splits;    /* device int32 [E] */
+  int64_t M;                  /* host total rows */
+  int32_t E;
+  int64_t H, ffn;
+  const gmlp_weight_q* w1;    /* quantized [E, F1, H] */
+  const gmlp_weight_q* w2;    /* quantized [E, H, ffn] */
+  const float* probs;         /* fp32 [M] */
+  int32_t activation;         /* gmlp_activation */
+  gmlp_recipe recipe;
+  int32_t recompute;
+  int32_t input_requires_grad;
+  int32_t weight_requires_grad;
+  void* y;                    /* bf16 [M, H] out */
+  void* ctx; size_t ctx_bytes;
+  void* ws;  size_t ws_bytes;
+} gmlp_fwd_args;
+
+/* Backward [MX, sequence diagram; NV, commits]:
+ *   da = bf16(Q(dy) Q(W2 along H))        (dh, dprob) = act'(h, da, prob), dh -> bf16
+ *   dx = bf16(Q(dh) Q(W1 along F1))       dW2_g = Q_c(dy_g)^T Q_c(a_g)   dW1_g = Q_c(dh_g)^T Q_c(x_g)
+ * dprobs[m] = sum_f da[m,f] act(h)[m,f], summed in a fixed order. */
+typedef struct {
+  const void* dy;             /* bf16 [M, H] */
+  const int32_t* m_splits;
+  int64_t M;
+  int32_t E;
+  int64_t H, ffn;
+  const gmlp_weight_q* w1;    /* uses the dgrad operand (col_*) */
+  const gmlp_weight_q* w2;
+  const float* probs;
+  int32_t activation;
+  gmlp_recipe recipe;
+  int32_t recompute;          /* must match the forward */
+  int32_t input_requires_grad;
+  int32_t weight_requires_grad;
+  void* dx;                   /* bf16 [M, H] (may be NULL if !input_requires_grad) */
+  float* dprobs;              /* fp32 [M] */
+  void* dw1;                  /* [E, F1, H] in wgrad_dtype (NULL if !weight_requires_grad) */
+  void* dw2;                  /* [E, H, ffn] */
+  int32_t wgrad_dtype;        /* gmlp_out_dtype */
+  const void* ctx; size_t ctx_bytes;
+  void* ws; size_t ws_bytes;
+} gmlp_bwd_args;
+
+gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* args, hipStream_t stream);
+gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* args, hipStream_t stream);
+
+/* Launch counts of the last forward / backward on this thread, by kernel kind
+ * (0 scan, 1 mxfp8 quantize, 2 hadamard amax, 3 nvfp4 cast, 4 gemm, 5 dprob
+ * reduce, 6 fill).  Lets a test check that a recompute backward issues no
+ * second Hadamard-amax pass [NV, Description]. */
+gmlp_status gmlp_last_launch_counts(int32_t* counts, int32_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GMLP_H */

@@ -1,0 +1,397 @@
+"""Fused MoE grouped MLP with MXFP8 / NVFP4 group quantization on MI355X (gfx950).
+
+Python binding of libgmlp.so (include/gmlp.h): argument marshalling only.  Every
+step of the path runs in the library's HIP kernels; torch only allocates device
+memory and supplies the stream.  The library must be built (python -m
+nvfp4_block_scaled_mxfp8_amd.build); nothing here falls back to another
+implementation when it is missing.
+
+Names follow the C ABI: group_quantize, group_hadamard_amax,
+group_quantize_with_amax, weight_quantize, grouped_gemm, grouped_mlp_forward,
+grouped_mlp_backward.
+"""
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgmlp.so")
+
+MXFP8, NVFP4_RHT = 0, 1
+SWIGLU, SRELU = 0, 1
+OUT_BF16, OUT_FP32 = 0, 1
+GEMM_FPROP, GEMM_WGRAD = 0, 1
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP_ERROR"}
+COL_PAD = 128
+LAUNCH_KINDS = ("scan", "mxfp8_quantize", "hadamard_amax", "nvfp4_quantize", "gemm", "dprob_reduce", "fill")
+
+
+class GmlpError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"gmlp {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+# ----------------------------------------------------------------------------- C structs
+class Recipe(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("rht_sign_mask", ctypes.c_uint32)]
+
+
+_Q_FIELDS = ("row_data", "row_scale", "row_scale_mfma", "col_data", "col_scale", "col_scale_mfma",
+             "amax_pre", "amax_post")
+
+
+class GroupedQ(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _Q_FIELDS]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [("ctx_bytes", ctypes.c_size_t), ("ws_bytes", ctypes.c_size_t),
+                ("quant_ws_bytes", ctypes.c_size_t)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("m_splits", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("E", ctypes.c_int32), ("H", ctypes.c_int64), ("ffn", ctypes.c_int64),
+                ("w1", ctypes.POINTER(GroupedQ)), ("w2", ctypes.POINTER(GroupedQ)),
+                ("probs", ctypes.c_void_p), ("activation", ctypes.c_int32), ("recipe", Recipe),
+                ("recompute", ctypes.c_int32), ("input_requires_grad", ctypes.c_int32),
+                ("weight_requires_grad", ctypes.c_int32), ("y", ctypes.c_void_p),
+                ("ctx", ctypes.c_void_p), ("ctx_bytes", ctypes.c_size_t),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("dy", ctypes.c_void_p), ("m_splits", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("E", ctypes.c_int32), ("H", ctypes.c_int64), ("ffn", ctypes.c_int64),
+                ("w1", ctypes.POINTER(GroupedQ)), ("w2", ctypes.POINTER(GroupedQ)),
+                ("probs", ctypes.c_void_p), ("activation", ctypes.c_int32), ("recipe", Recipe),
+                ("recompute", ctypes.c_int32), ("input_requires_grad", ctypes.c_int32),
+                ("weight_requires_grad", ctypes.c_int32), ("dx", ctypes.c_void_p),
+                ("dprobs", ctypes.c_void_p), ("dw1", ctypes.c_void_p), ("dw2", ctypes.c_void_p),
+                ("wgrad_dtype", ctypes.c_int32), ("ctx", ctypes.c_void_p),
+                ("ctx_bytes", ctypes.c_size_t), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+_SIGS = {
+    "gmlp_last_error": (ctypes.c_char_p, []),
+    "gmlp_check_support": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int32, Recipe]),
+    "gmlp_query_sizes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int32, Recipe, ctypes.c_int32, ctypes.POINTER(Sizes)]),
+    "gmlp_read_device_flags": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32), ctypes.c_void_p]),
+    "gmlp_group_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_int32, Recipe, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(GroupedQ), ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]),
+    "gmlp_group_hadamard_amax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                                ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "gmlp_group_quantize_with_amax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                     ctypes.c_void_p, ctypes.c_int32, Recipe, ctypes.c_int32,
+                                                     ctypes.c_int32, ctypes.POINTER(GroupedQ), ctypes.c_void_p,
+                                                     ctypes.c_size_t, ctypes.c_void_p]),
+    "gmlp_weight_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                            ctypes.c_int64, Recipe, ctypes.POINTER(GroupedQ), ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]),
+    "gmlp_grouped_gemm": (ctypes.c_int, [ctypes.c_int32, Recipe, ctypes.POINTER(GroupedQ),
+                                         ctypes.POINTER(GroupedQ), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "gmlp_grouped_mlp_forward": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
+    "gmlp_grouped_mlp_backward": (ctypes.c_int, [ctypes.POINTER(BwdArgs), ctypes.c_void_p]),
+    "gmlp_last_launch_counts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libgmlp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m nvfp4_block_scaled_mxfp8_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise GmlpError(status, lib().gmlp_last_error().decode())
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def recipe(kind="mxfp8", sign_mask=0):
+    k = {"mxfp8": MXFP8, "nvfp4": NVFP4_RHT, MXFP8: MXFP8, NVFP4_RHT: NVFP4_RHT}[kind]
+    return Recipe(k, int(sign_mask) & 0xFFFF)
+
+
+def activation_id(act):
+    """'swiglu' / 'srelu' -> the C enum; integers pass through (the library validates them)."""
+    return act if isinstance(act, int) else {"swiglu": SWIGLU, "srelu": SRELU}[act]
+
+
+def last_error():
+    return lib().gmlp_last_error().decode()
+
+
+def last_launch_counts():
+    c = (ctypes.c_int32 * 8)()
+    _check(lib().gmlp_last_launch_counts(c, 8))
+    return dict(zip(LAUNCH_KINDS, list(c)[:7]))
+
+
+def check_support(experts, hidden, ffn, activation="swiglu", rec=None, arch=None):
+    """(ok, reason) -- host-only support query; arch=None asks device 0."""
+    rec = rec if rec is not None else recipe()
+    st = lib().gmlp_check_support(arch.encode() if arch else None, experts, hidden, ffn,
+                                  activation_id(activation), rec)
+    return st == 0, ("" if st == 0 else last_error()), st
+
+
+def query_sizes(M, experts, hidden, ffn, activation="swiglu", rec=None, recompute=False):
+    rec = rec if rec is not None else recipe()
+    s = Sizes()
+    _check(lib().gmlp_query_sizes(M, experts, hidden, ffn, activation_id(activation), rec, int(recompute),
+                                  ctypes.byref(s)))
+    return {"ctx_bytes": s.ctx_bytes, "ws_bytes": s.ws_bytes, "quant_ws_bytes": s.quant_ws_bytes}
+
+
+def quant_workspace(G, device):
+    n = query_sizes(0, G, 128, 128)["quant_ws_bytes"]
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def read_device_flags(ws):
+    v = ctypes.c_uint32(0)
+    _check(lib().gmlp_read_device_flags(_p(ws), ctypes.byref(v), _stream(ws.device)))
+    return v.value
+
+
+# ----------------------------------------------------------------------------- quantized tensors
+@dataclass
+class QTensor:
+    """Device buffers of a group-quantized tensor (layouts as in include/gmlp.h)."""
+    kind: int
+    bufs: dict = field(default_factory=dict)
+
+    def struct(self):
+        return GroupedQ(*[self.bufs[n].data_ptr() if self.bufs.get(n) is not None else None for n in _Q_FIELDS])
+
+
+def col_rows_bound(M, G):
+    return M + (COL_PAD - 1) * G
+
+
+def alloc_grouped_q(rec, M, K, G, row=True, col=True, device="cuda"):
+    """Buffers for group_quantize of [M, K] into G groups (column-wise sized for the worst padding)."""
+    u8 = dict(dtype=torch.uint8, device=device)
+    PR = col_rows_bound(M, G)
+    b = {}
+    if rec.kind == MXFP8:
+        if row:
+            b["row_data"] = torch.empty(M * K, **u8)
+            b["row_scale"] = torch.empty(M * K // 32, **u8)
+            b["row_scale_mfma"] = torch.empty(((K + 127) // 128) * M, dtype=torch.int32, device=device)
+        if col:
+            b["col_data"] = torch.empty(K * PR, **u8)
+            b["col_scale"] = torch.empty(K * PR // 32, **u8)
+            b["col_scale_mfma"] = torch.empty(K * ((M + 127) // 128 + G), dtype=torch.int32, device=device)
+    else:
+        if row:
+            b["row_data"] = torch.empty(M * K // 2, **u8)
+            b["row_scale"] = torch.empty(M * K // 16, **u8)
+        if col:
+            b["col_data"] = torch.empty(K * PR // 2, **u8)
+            b["col_scale"] = torch.empty(K * PR // 16, **u8)
+        b["amax_pre"] = torch.empty(G, dtype=torch.float32, device=device)
+        b["amax_post"] = torch.empty(G, dtype=torch.float32, device=device)
+    return QTensor(rec.kind, b)
+
+
+def _bits(x):
+    """bf16 tensor (or int16 bit view) -> contiguous tensor whose storage is the bf16 bits."""
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"expected bf16 data, got {x.dtype}")
+    return x.contiguous()
+
+
+def group_quantize(x, m_splits, rec, want_row=True, want_col=True, out=None, ws=None):
+    x = _bits(x)
+    M, K = x.shape
+    G = m_splits.numel()
+    out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
+    ws = ws if ws is not None else quant_workspace(G, x.device)
+    q = out.struct()
+    _check(lib().gmlp_group_quantize(_p(x), M, K, _p(m_splits), G, rec, int(want_row), int(want_col),
+                                     ctypes.byref(q), _p(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+def group_hadamard_amax(x, m_splits, sign_mask, ws=None):
+    x = _bits(x)
+    M, K = x.shape
+    G = m_splits.numel()
+    pre = torch.empty(G, dtype=torch.float32, device=x.device)
+    post = torch.empty(G, dtype=torch.float32, device=x.device)
+    ws = ws if ws is not None else quant_workspace(G, x.device)
+    _check(lib().gmlp_group_hadamard_amax(_p(x), M, K, _p(m_splits), G, int(sign_mask) & 0xFFFF, _p(pre),
+                                          _p(post), _p(ws), ws.numel(), _stream(x.device)))
+    return pre, post
+
+
+def group_quantize_with_amax(x, m_splits, rec, amax_pre, amax_post, want_row=True, want_col=True, out=None,
+                             ws=None):
+    x = _bits(x)
+    M, K = x.shape
+    G = m_splits.numel()
+    out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
+    out.bufs["amax_pre"] = amax_pre
+    out.bufs["amax_post"] = amax_post
+    ws = ws if ws is not None else quant_workspace(G, x.device)
+    q = out.struct()
+    _check(lib().gmlp_group_quantize_with_amax(_p(x), M, K, _p(m_splits), G, rec, int(want_row), int(want_col),
+                                               ctypes.byref(q), _p(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+def alloc_weight_q(rec, E, N, K, device="cuda"):
+    u8 = dict(dtype=torch.uint8, device=device)
+    b = {}
+    if rec.kind == MXFP8:
+        b["row_data"] = torch.empty(E * N * K, **u8)
+        b["row_scale"] = torch.empty(E * N * K // 32, **u8)
+        b["row_scale_mfma"] = torch.empty(E * ((K + 127) // 128) * N, dtype=torch.int32, device=device)
+        b["col_data"] = torch.empty(E * K * N, **u8)
+        b["col_scale"] = torch.empty(E * K * N // 32, **u8)
+        b["col_scale_mfma"] = torch.empty(E * ((N + 127) // 128) * K, dtype=torch.int32, device=device)
+    else:
+        b["row_data"] = torch.empty(E * N * K // 2, **u8)
+        b["row_scale"] = torch.empty(E * N * K // 16, **u8)
+        b["col_data"] = torch.empty(E * K * N // 2, **u8)
+        b["col_scale"] = torch.empty(E * K * N // 16, **u8)
+        b["amax_pre"] = torch.empty(E, dtype=torch.float32, device=device)
+    return QTensor(rec.kind, b)
+
+
+def weight_quantize(w, rec, out=None):
+    """w: stacked bf16 [E, N, K] tensor, or a list of E [N, K] tensors (discrete weights)."""
+    if isinstance(w, (list, tuple)):
+        ws_list = [_bits(t) for t in w]
+        E = len(ws_list)
+        N, K = ws_list[0].shape
+        dev = ws_list[0].device
+        ptrs = (ctypes.c_void_p * E)(*[t.data_ptr() for t in ws_list])
+        base = ctypes.c_void_p(0)
+    else:
+        w = _bits(w)
+        E, N, K = w.shape
+        dev = w.device
+        ptrs = None
+        base = _p(w)
+    out = out or alloc_weight_q(rec, E, N, K, dev)
+    ws = quant_workspace(1, dev)
+    q = out.struct()
+    _check(lib().gmlp_weight_quantize(base, ptrs, E, N, K, rec, ctypes.byref(q), _p(ws), ws.numel(),
+                                      _stream(dev)))
+    return out
+
+
+def grouped_gemm(layout, rec, a, b, m_splits, M, n, k, out_dtype=OUT_BF16, ws=None):
+    G = m_splits.numel()
+    dev = m_splits.device
+    dt = torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16
+    c = torch.empty((M, n) if layout == GEMM_FPROP else (G, n, k), dtype=dt, device=dev)
+    ws = ws if ws is not None else quant_workspace(G, dev)
+    qa, qb = a.struct(), b.struct()
+    _check(lib().gmlp_grouped_gemm(layout, rec, ctypes.byref(qa), ctypes.byref(qb), _p(m_splits), G, M, n, k,
+                                   _p(c), out_dtype, _p(ws), ws.numel(), _stream(dev)))
+    return c
+
+
+# ----------------------------------------------------------------------------- fused MLP
+@dataclass
+class MlpContext:
+    """What the forward leaves for the backward (opaque buffer + the call's settings)."""
+    buf: torch.Tensor
+    M: int
+    E: int
+    H: int
+    ffn: int
+    activation: int
+    rec: Recipe
+    recompute: bool
+    input_requires_grad: bool
+    weight_requires_grad: bool
+
+
+def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute=False,
+                        input_requires_grad=True, weight_requires_grad=True, ws=None, y=None, ctx=None):
+    x = _bits(x)
+    M, H = x.shape
+    E = m_splits.numel()
+    act = activation_id(activation)
+    ffn = ffn_from_w2(w2q, rec, E, H)
+    sizes = query_sizes(M, E, H, ffn, act, rec, recompute)
+    dev = x.device
+    ws = ws if ws is not None else torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
+    cbuf = ctx.buf if ctx is not None else torch.empty(sizes["ctx_bytes"], dtype=torch.uint8, device=dev)
+    y = y if y is not None else torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    s1, s2 = w1q.struct(), w2q.struct()
+    a = FwdArgs(x.data_ptr(), m_splits.data_ptr(), M, E, H, ffn, ctypes.pointer(s1), ctypes.pointer(s2),
+                probs.data_ptr() if M else None, act, rec, int(recompute), int(input_requires_grad),
+                int(weight_requires_grad), y.data_ptr() if M else None, cbuf.data_ptr(), cbuf.numel(),
+                ws.data_ptr(), ws.numel())
+    _check(lib().gmlp_grouped_mlp_forward(ctypes.byref(a), _stream(dev)))
+    c = MlpContext(cbuf, M, E, H, ffn, act, rec, bool(recompute), bool(input_requires_grad),
+                   bool(weight_requires_grad))
+    return y, c
+
+
+def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF16, ws=None, out=None):
+    dy = _bits(dy)
+    M, H = dy.shape
+    E, ffn, act = ctx.E, ctx.ffn, ctx.activation
+    F1 = 2 * ffn if act == SWIGLU else ffn
+    dev = dy.device
+    sizes = query_sizes(M, E, H, ffn, act, ctx.rec, ctx.recompute)
+    ws = ws if ws is not None else torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
+    wdt = torch.float32 if wgrad_dtype == OUT_FP32 else torch.bfloat16
+    o = out or {}
+    dx = o.get("dx") if ctx.input_requires_grad else None
+    if ctx.input_requires_grad and dx is None:
+        dx = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    dprobs = o.get("dprobs", torch.empty(M, dtype=torch.float32, device=dev))
+    dw1 = dw2 = None
+    if ctx.weight_requires_grad:
+        dw1 = o.get("dw1", torch.empty((E, F1, H), dtype=wdt, device=dev))
+        dw2 = o.get("dw2", torch.empty((E, H, ffn), dtype=wdt, device=dev))
+    s1, s2 = w1q.struct(), w2q.struct()
+    a = BwdArgs(dy.data_ptr(), m_splits.data_ptr(), M, E, H, ffn, ctypes.pointer(s1), ctypes.pointer(s2),
+                probs.data_ptr() if M else None, act, ctx.rec, int(ctx.recompute), int(ctx.input_requires_grad),
+                int(ctx.weight_requires_grad), dx.data_ptr() if (dx is not None and M) else None,
+                dprobs.data_ptr() if M else None, dw1.data_ptr() if dw1 is not None else None,
+                dw2.data_ptr() if dw2 is not None else None, wgrad_dtype, ctx.buf.data_ptr(), ctx.buf.numel(),
+                ws.data_ptr(), ws.numel())
+    _check(lib().gmlp_grouped_mlp_backward(ctypes.byref(a), _stream(dev)))
+    return {"dx": dx, "dprobs": dprobs, "dw1": dw1, "dw2": dw2}
+
+
+def ffn_from_w2(w2q, rec, E, H):
+    n = w2q.bufs["row_data"].numel()
+    return (n // (E * H)) if rec.kind == MXFP8 else (2 * n // (E * H))

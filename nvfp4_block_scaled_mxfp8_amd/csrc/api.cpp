@@ -1,0 +1,724 @@
+// C ABI of libgmlp: validation, workspace carving and the launch plan of the fused grouped MLP.
+//
+// The launch plan follows "GEMM + Swiglu fused Grouped MLP for MXFP8" (sequence
+// diagram) for MXFP8 and "Reduce NVFP4 quantization work for the fused
+// GroupedMLP fc2 input with activation recompute" (Description, Changes) for
+// NVFP4: the recompute decision is taken before the fc2-input cast, so the
+// forward casts fc2_x row-wise only when the backward rebuilds it; the forward
+// keeps the fc2_x (pre, post) amax; the backward casts the rebuilt fc2_x with
+// that amax and runs no second Hadamard-amax pass.
+#include "../../include/gmlp.h"
+#include "kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+using namespace gmlp;
+
+namespace {
+
+thread_local std::string g_err;
+thread_local int32_t g_counts[8];
+
+enum { CNT_SCAN = 0, CNT_MXQ = 1, CNT_HAMAX = 2, CNT_NVQ = 3, CNT_GEMM = 4, CNT_DPROB = 5, CNT_FILL = 6 };
+
+gmlp_status fail(gmlp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+gmlp_status ok() {
+  g_err.clear();
+  return GMLP_OK;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(GMLP_HIP_ERROR, "system: %s failed: %s", #expr, \
+                                      hipGetErrorString(e_));                          \
+  } while (0)
+
+// Bump allocator over a caller buffer (base == nullptr: sizing pass).
+struct Bump {
+  uint8_t* base;
+  size_t off = 0;
+  explicit Bump(void* b) : base(static_cast<uint8_t*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+SplitTables carve_tables(Bump& b, int G) {
+  SplitTables T;
+  T.flags = b.take<uint32_t>(1);
+  T.row_off = b.take<int32_t>(G + 1);
+  T.col_off = b.take<int32_t>(G + 1);
+  T.colw_off = b.take<int32_t>(G + 1);
+  T.t128_off = b.take<int32_t>(G + 1);
+  T.t256_off = b.take<int32_t>(G + 1);
+  return T;
+}
+
+bool is_mx(const gmlp_recipe& r) { return r.kind == GMLP_MXFP8; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// Upper bounds of the padded column-wise extents for M rows in G groups.
+int64_t pad_rows_bound(int64_t M, int G) { return M + 127LL * G; }
+int64_t pad_words_bound(int64_t M, int G) { return ceil_div(M, 128) + G; }
+
+// Buffers of one group-quantized activation tensor [M, K].
+struct QBuf {
+  gmlp_grouped_q q{};
+};
+
+QBuf carve_q(Bump& b, const gmlp_recipe& r, int64_t M, int64_t K, int G, bool row, bool col, bool amax) {
+  QBuf o;
+  const int64_t PR = pad_rows_bound(M, G);
+  if (is_mx(r)) {
+    if (row) {
+      o.q.row_data = b.take<uint8_t>(M * K);
+      o.q.row_scale_mfma = b.take<uint32_t>(ceil_div(K, 128) * M);
+    }
+    if (col) {
+      o.q.col_data = b.take<uint8_t>(K * PR);
+      o.q.col_scale_mfma = b.take<uint32_t>(K * pad_words_bound(M, G));
+    }
+  } else {
+    if (row) {
+      o.q.row_data = b.take<uint8_t>(M * K / 2);
+      o.q.row_scale = b.take<uint8_t>(M * K / 16);
+    }
+    if (col) {
+      o.q.col_data = b.take<uint8_t>(K * PR / 2);
+      o.q.col_scale = b.take<uint8_t>(K * PR / 16);
+    }
+    if (amax) {
+      o.q.amax_pre = b.take<float>(G);
+      o.q.amax_post = b.take<float>(G);
+    }
+  }
+  return o;
+}
+
+struct Launcher {
+  hipStream_t s;
+  gmlp_status st = GMLP_OK;
+  bool check(hipError_t e, const char* what) {
+    if (e != hipSuccess) {
+      fail(GMLP_HIP_ERROR, "system: launching %s failed: %s", what, hipGetErrorString(e));
+      st = GMLP_HIP_ERROR;
+      return false;
+    }
+    return true;
+  }
+};
+
+// ----------------------------------------------------------------------------- validation
+gmlp_status check_recipe(const gmlp_recipe& r) {
+  if (r.kind != GMLP_MXFP8 && r.kind != GMLP_NVFP4_RHT)
+    return fail(GMLP_UNSUPPORTED, "recipe: requires an MXFP8 or NVFP4 (with RHT) recipe, got kind %d", r.kind);
+  return GMLP_OK;
+}
+
+gmlp_status check_dims(int64_t M, int64_t K, int G) {
+  if (G < 1) return fail(GMLP_INVALID_ARG, "dims: number of groups must be >= 1, got %d", G);
+  if (M < 0) return fail(GMLP_INVALID_ARG, "dims: M must be >= 0, got %lld", (long long)M);
+  if (K <= 0 || K % 32 != 0) return fail(GMLP_UNSUPPORTED, "dims: K must be a positive multiple of 32, got %lld", (long long)K);
+  if (M + 127LL * G > (1LL << 30)) return fail(GMLP_UNSUPPORTED, "dims: M = %lld rows is too large", (long long)M);
+  return GMLP_OK;
+}
+
+gmlp_status quant_core(const void* x, int64_t M, int64_t K, const int32_t* m_splits, int G, const gmlp_recipe& r,
+                       bool row, bool col, const gmlp_grouped_q* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream, bool compute_amax) {
+  gmlp_status st;
+  if ((st = check_recipe(r)) != GMLP_OK) return st;
+  if ((st = check_dims(M, K, G)) != GMLP_OK) return st;
+  if (!out || (M > 0 && !x) || !m_splits) return fail(GMLP_INVALID_ARG, "null pointer argument");
+  if (!row && !col && !compute_amax) return fail(GMLP_INVALID_ARG, "nothing requested (want_row = want_col = 0)");
+  const bool rows_exist = M > 0;   // an empty tensor has no row-wise buffers to check
+  if (is_mx(r)) {
+    if (rows_exist && row && (!out->row_data || (!out->row_scale && !out->row_scale_mfma)))
+      return fail(GMLP_INVALID_ARG, "row-wise output buffers missing");
+    if (col && (!out->col_data || (!out->col_scale && !out->col_scale_mfma)))
+      return fail(GMLP_INVALID_ARG, "column-wise output buffers missing");
+  } else {
+    if (rows_exist && row && (!out->row_data || !out->row_scale))
+      return fail(GMLP_INVALID_ARG, "row-wise output buffers missing");
+    if (col && (!out->col_data || !out->col_scale)) return fail(GMLP_INVALID_ARG, "column-wise output buffers missing");
+    if (!out->amax_pre || !out->amax_post) return fail(GMLP_INVALID_ARG, "NVFP4 needs amax_pre and amax_post");
+  }
+  Bump b(ws);
+  SplitTables T = carve_tables(b, G);
+  if (!ws || ws_bytes < b.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", b.off);
+  Launcher L{stream};
+  if (!L.check(launch_fill_u32(T.flags, 0u, 1, stream), "fill")) return L.st;
+  if (!L.check(launch_scan(m_splits, G, M, T, stream), "scan")) return L.st;
+  g_counts[CNT_SCAN]++;
+  const uint16_t* xx = static_cast<const uint16_t*>(x);
+  if (is_mx(r)) {
+    MxOut o{static_cast<uint8_t*>(row ? out->row_data : nullptr), static_cast<uint8_t*>(row ? out->row_scale : nullptr),
+            static_cast<uint32_t*>(row ? out->row_scale_mfma : nullptr),
+            static_cast<uint8_t*>(col ? out->col_data : nullptr), static_cast<uint8_t*>(col ? out->col_scale : nullptr),
+            static_cast<uint32_t*>(col ? out->col_scale_mfma : nullptr)};
+    if (!L.check(launch_mxfp8_quant(xx, M, K, T, G, row, col, o, stream), "mxfp8 quantize")) return L.st;
+    g_counts[CNT_MXQ]++;
+    return ok();
+  }
+  if (compute_amax) {
+    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(out->amax_pre), 0u, G, stream), "fill")) return L.st;
+    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(out->amax_post), 0u, G, stream), "fill")) return L.st;
+    if (!L.check(launch_hadamard_amax(xx, M, K, T, G, r.rht_sign_mask & 0xFFFFu, out->amax_pre, out->amax_post,
+                                      stream), "hadamard amax"))
+      return L.st;
+    g_counts[CNT_HAMAX]++;
+  }
+  if (row || col) {
+    NvOut o{static_cast<uint8_t*>(out->row_data), static_cast<uint8_t*>(out->row_scale),
+            static_cast<uint8_t*>(out->col_data), static_cast<uint8_t*>(out->col_scale)};
+    if (!L.check(launch_nvfp4_quant(xx, M, K, T, G, r.rht_sign_mask & 0xFFFFu, true, row, col, out->amax_pre,
+                                    out->amax_post, o, stream), "nvfp4 quantize"))
+      return L.st;
+    g_counts[CNT_NVQ]++;
+  }
+  return ok();
+}
+
+// Operand of the GEMM kernels from a quantized tensor.
+GemmOperand op_row(const gmlp_grouped_q& q, const float* amax) {
+  GemmOperand o;
+  o.data = static_cast<const uint8_t*>(q.row_data);
+  o.scale_mfma = static_cast<const uint32_t*>(q.row_scale_mfma);
+  o.scale = static_cast<const uint8_t*>(q.row_scale);
+  o.amax = amax;
+  return o;
+}
+GemmOperand op_col(const gmlp_grouped_q& q, const float* amax) {
+  GemmOperand o;
+  o.data = static_cast<const uint8_t*>(q.col_data);
+  o.scale_mfma = static_cast<const uint32_t*>(q.col_scale_mfma);
+  o.scale = static_cast<const uint8_t*>(q.col_scale);
+  o.amax = amax;
+  return o;
+}
+
+GemmArgs gemm_base(int mode, const gmlp_recipe& r, int epi, SplitTables T, int G) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.mode = mode;
+  g.fmt = is_mx(r) ? FMT_MXFP8 : FMT_NVFP4;
+  g.epi = epi;
+  g.T = T;
+  g.G = G;
+  return g;
+}
+
+gmlp_status weight_ok(const gmlp_weight_q* w, const gmlp_recipe& r, bool fprop, bool dgrad) {
+  if (!w) return fail(GMLP_INVALID_ARG, "null weight descriptor");
+  if (fprop && (!w->row_data || (is_mx(r) ? !w->row_scale_mfma : !w->row_scale)))
+    return fail(GMLP_INVALID_ARG, "weight fprop operand (row-wise data and scales) missing");
+  if (dgrad && (!w->col_data || (is_mx(r) ? !w->col_scale_mfma : !w->col_scale)))
+    return fail(GMLP_INVALID_ARG, "weight dgrad operand (column-wise data and scales) missing");
+  if (!is_mx(r) && !w->amax_pre) return fail(GMLP_INVALID_ARG, "NVFP4 weights need their per-expert amax (amax_pre)");
+  return GMLP_OK;
+}
+
+// ----------------------------------------------------------------------------- MLP plan
+struct FwdCtx {     // saved tensors (in ctx)
+  uint16_t* h;
+  QBuf xq_col;      // column-wise x (+ NVFP4 amax)
+  QBuf aq_col;      // column-wise fc2 input when not recomputing
+  float* a_pre;     // NVFP4 fc2-input amax (kept for the recompute cast)
+  float* a_post;
+};
+
+FwdCtx carve_ctx(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, const gmlp_recipe& r, bool recompute) {
+  const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
+  FwdCtx c{};
+  c.h = b.take<uint16_t>(M * F1);
+  c.xq_col = carve_q(b, r, M, H, E, false, true, true);
+  if (!recompute) c.aq_col = carve_q(b, r, M, ffn, E, false, true, false);
+  if (!is_mx(r)) {
+    c.a_pre = b.take<float>(E);
+    c.a_post = b.take<float>(E);
+  }
+  return c;
+}
+
+struct FwdWs {
+  SplitTables T;
+  QBuf xq_row;
+  uint16_t* a;
+  QBuf aq_row;
+};
+FwdWs carve_fwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, const gmlp_recipe& r) {
+  FwdWs w;
+  w.T = carve_tables(b, E);
+  w.xq_row = carve_q(b, r, M, H, E, true, false, false);
+  w.a = b.take<uint16_t>(M * ffn);
+  w.aq_row = carve_q(b, r, M, ffn, E, true, false, false);
+  return w;
+}
+
+struct BwdWs {
+  SplitTables T;
+  QBuf dyq;
+  uint16_t* dh;
+  QBuf dhq;
+  uint16_t* a2;
+  QBuf a2q;
+  float* dprob_part;
+};
+int dact_ntiles(int64_t ffn) { return (int)ceil_div(ffn, 256); }
+BwdWs carve_bwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, const gmlp_recipe& r, bool recompute) {
+  const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
+  BwdWs w{};
+  w.T = carve_tables(b, E);
+  w.dyq = carve_q(b, r, M, H, E, true, true, true);
+  w.dh = b.take<uint16_t>(M * F1);
+  w.dhq = carve_q(b, r, M, F1, E, true, true, true);
+  if (recompute) {
+    w.a2 = b.take<uint16_t>(M * ffn);
+    w.a2q = carve_q(b, r, M, ffn, E, false, true, false);
+  }
+  w.dprob_part = b.take<float>((size_t)dact_ntiles(ffn) * M);
+  return w;
+}
+
+gmlp_status mlp_common_checks(int64_t M, int E, int64_t H, int64_t ffn, int act, const gmlp_recipe& r) {
+  gmlp_status st;
+  if ((st = check_recipe(r)) != GMLP_OK) return st;
+  if (act != GMLP_SWIGLU && act != GMLP_SRELU) return fail(GMLP_UNSUPPORTED, "activation: unsupported activation %d", act);
+  if ((st = check_dims(M, H, E)) != GMLP_OK) return st;
+  if (ffn <= 0 || ffn % 128 != 0) return fail(GMLP_UNSUPPORTED, "dims: ffn must be a positive multiple of 128, got %lld", (long long)ffn);
+  if (H % 128 != 0) return fail(GMLP_UNSUPPORTED, "dims: hidden must be a multiple of 128, got %lld", (long long)H);
+  return GMLP_OK;
+}
+
+}  // namespace
+
+// =============================================================================== C ABI
+extern "C" {
+
+const char* gmlp_last_error(void) { return g_err.c_str(); }
+
+gmlp_status gmlp_check_support(const char* arch, int32_t experts, int64_t hidden, int64_t ffn, int32_t activation,
+                               gmlp_recipe recipe) {
+  char name[256] = {0};
+  if (arch) {
+    strncpy(name, arch, sizeof(name) - 1);
+  } else {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n == 0) return fail(GMLP_UNSUPPORTED, "system: no HIP device available");
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, 0) != hipSuccess) return fail(GMLP_UNSUPPORTED, "system: cannot query device 0");
+    strncpy(name, p.gcnArchName, sizeof(name) - 1);
+  }
+  if (strncmp(name, "gfx950", 6) != 0)
+    return fail(GMLP_UNSUPPORTED, "system: unsupported device architecture %s (this library is built for gfx950)", name);
+  gmlp_status st = mlp_common_checks(0, experts, hidden, ffn, activation, recipe);
+  if (st != GMLP_OK) return st;
+  return ok();
+}
+
+gmlp_status gmlp_query_sizes(int64_t M, int32_t experts, int64_t hidden, int64_t ffn, int32_t activation,
+                             gmlp_recipe recipe, int32_t recompute, gmlp_sizes* out) {
+  if (!out) return fail(GMLP_INVALID_ARG, "null output");
+  gmlp_status st = mlp_common_checks(M, experts, hidden, ffn, activation, recipe);
+  if (st != GMLP_OK) return st;
+  Bump c(nullptr);
+  carve_ctx(c, M, experts, hidden, ffn, activation, recipe, recompute != 0);
+  Bump f(nullptr);
+  carve_fwd_ws(f, M, experts, hidden, ffn, recipe);
+  Bump b(nullptr);
+  carve_bwd_ws(b, M, experts, hidden, ffn, activation, recipe, recompute != 0);
+  Bump q(nullptr);
+  carve_tables(q, experts);
+  out->ctx_bytes = c.off + 256;
+  out->ws_bytes = std::max(f.off, b.off) + 256;
+  out->quant_ws_bytes = q.off + 256;
+  return ok();
+}
+
+gmlp_status gmlp_read_device_flags(const void* ws, uint32_t* flags, hipStream_t stream) {
+  if (!ws || !flags) return fail(GMLP_INVALID_ARG, "null pointer argument");
+  HIP_TRY(hipMemcpyAsync(flags, ws, sizeof(uint32_t), hipMemcpyDeviceToHost, stream));
+  HIP_TRY(hipStreamSynchronize(stream));
+  return ok();
+}
+
+gmlp_status gmlp_last_launch_counts(int32_t* counts, int32_t n) {
+  if (!counts) return fail(GMLP_INVALID_ARG, "null pointer argument");
+  for (int i = 0; i < n && i < 8; ++i) counts[i] = g_counts[i];
+  return ok();
+}
+
+gmlp_status gmlp_group_quantize(const void* x, int64_t M, int64_t K, const int32_t* m_splits, int32_t G,
+                                gmlp_recipe recipe, int32_t want_row, int32_t want_col, const gmlp_grouped_q* out,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  memset(g_counts, 0, sizeof(g_counts));
+  return quant_core(x, M, K, m_splits, G, recipe, want_row != 0, want_col != 0, out, ws, ws_bytes, stream,
+                    !is_mx(recipe));
+}
+
+gmlp_status gmlp_group_hadamard_amax(const void* x, int64_t M, int64_t K, const int32_t* m_splits, int32_t G,
+                                     uint32_t rht_sign_mask, float* amax_pre, float* amax_post, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  memset(g_counts, 0, sizeof(g_counts));
+  gmlp_grouped_q q{};
+  q.amax_pre = amax_pre;
+  q.amax_post = amax_post;
+  gmlp_recipe r{GMLP_NVFP4_RHT, rht_sign_mask};
+  return quant_core(x, M, K, m_splits, G, r, false, false, &q, ws, ws_bytes, stream, true);
+}
+
+gmlp_status gmlp_group_quantize_with_amax(const void* x, int64_t M, int64_t K, const int32_t* m_splits, int32_t G,
+                                          gmlp_recipe recipe, int32_t want_row, int32_t want_col,
+                                          const gmlp_grouped_q* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  memset(g_counts, 0, sizeof(g_counts));
+  if (recipe.kind != GMLP_NVFP4_RHT)
+    return fail(GMLP_UNSUPPORTED, "recipe: quantize_with_amax applies to the NVFP4 recipe only");
+  if (!want_row && !want_col) return fail(GMLP_INVALID_ARG, "nothing requested (want_row = want_col = 0)");
+  return quant_core(x, M, K, m_splits, G, recipe, want_row != 0, want_col != 0, out, ws, ws_bytes, stream, false);
+}
+
+gmlp_status gmlp_weight_quantize(const void* w, const void* const* w_ptrs, int32_t E, int64_t N, int64_t K,
+                                 gmlp_recipe recipe, const gmlp_weight_q* out, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  memset(g_counts, 0, sizeof(g_counts));
+  gmlp_status st;
+  if ((st = check_recipe(recipe)) != GMLP_OK) return st;
+  if (E < 1 || N <= 0 || N % 128 != 0 || K <= 0 || K % 128 != 0)
+    return fail(GMLP_UNSUPPORTED, "dims: weights need E >= 1 and N, K positive multiples of 128");
+  if (!out || (!w && !w_ptrs)) return fail(GMLP_INVALID_ARG, "null pointer argument");
+  if (!out->row_data || !out->col_data) return fail(GMLP_INVALID_ARG, "weight output data buffers missing");
+  if (is_mx(recipe) ? (!out->row_scale_mfma || !out->col_scale_mfma) : (!out->row_scale || !out->col_scale || !out->amax_pre))
+    return fail(GMLP_INVALID_ARG, "weight output scale buffers missing");
+  Bump b(ws);
+  SplitTables T = carve_tables(b, 1);
+  int32_t* split = b.take<int32_t>(1);
+  if (!ws || ws_bytes < b.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", b.off);
+  Launcher L{stream};
+  if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(split), (uint32_t)N, 1, stream), "fill")) return L.st;
+  if (!L.check(launch_fill_u32(T.flags, 0u, 1, stream), "fill")) return L.st;
+  if (!L.check(launch_scan(split, 1, N, T, stream), "scan")) return L.st;
+  const int64_t nkt = ceil_div(K, 128), nkt_t = ceil_div(N, 128);
+  for (int e = 0; e < E; ++e) {
+    const uint16_t* src = w ? static_cast<const uint16_t*>(w) + (int64_t)e * N * K : static_cast<const uint16_t*>(w_ptrs[e]);
+    if (!src) return fail(GMLP_INVALID_ARG, "null expert weight pointer %d", e);
+    if (is_mx(recipe)) {
+      MxOut o{static_cast<uint8_t*>(out->row_data) + (int64_t)e * N * K,
+              out->row_scale ? static_cast<uint8_t*>(out->row_scale) + (int64_t)e * N * (K / 32) : nullptr,
+              static_cast<uint32_t*>(out->row_scale_mfma) + (int64_t)e * nkt * N,
+              static_cast<uint8_t*>(out->col_data) + (int64_t)e * N * K,
+              out->col_scale ? static_cast<uint8_t*>(out->col_scale) + (int64_t)e * N * (K / 32) : nullptr,
+              static_cast<uint32_t*>(out->col_scale_mfma) + (int64_t)e * nkt_t * K};
+      if (!L.check(launch_mxfp8_quant(src, N, K, T, 1, true, true, o, stream), "mxfp8 weight quantize")) return L.st;
+      g_counts[CNT_MXQ]++;
+    } else {
+      float* amax = out->amax_pre + e;
+      if (!L.check(launch_weight_amax(src, nullptr, 1, N, K, amax, stream), "weight amax")) return L.st;
+      NvOut o{static_cast<uint8_t*>(out->row_data) + (int64_t)e * N * K / 2,
+              static_cast<uint8_t*>(out->row_scale) + (int64_t)e * N * K / 16,
+              static_cast<uint8_t*>(out->col_data) + (int64_t)e * N * K / 2,
+              static_cast<uint8_t*>(out->col_scale) + (int64_t)e * N * K / 16};
+      if (!L.check(launch_nvfp4_quant(src, N, K, T, 1, 0u, false, true, true, amax, amax, o, stream),
+                   "nvfp4 weight quantize"))
+        return L.st;
+      g_counts[CNT_NVQ]++;
+    }
+  }
+  return ok();
+}
+
+gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_grouped_q* a, const gmlp_grouped_q* b,
+                              const int32_t* m_splits, int32_t G, int64_t M, int64_t n, int64_t k, void* c,
+                              int32_t out_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  memset(g_counts, 0, sizeof(g_counts));
+  gmlp_status st;
+  if ((st = check_recipe(recipe)) != GMLP_OK) return st;
+  if (layout != GMLP_GEMM_FPROP && layout != GMLP_GEMM_WGRAD) return fail(GMLP_INVALID_ARG, "unknown GEMM layout %d", layout);
+  if (!a || !b || !m_splits || !c) return fail(GMLP_INVALID_ARG, "null pointer argument");
+  if (G < 1 || M < 0 || n <= 0 || k <= 0 || n % 32 || k % 32) return fail(GMLP_UNSUPPORTED, "dims: n, k must be positive multiples of 32");
+  if (layout == GMLP_GEMM_FPROP && k % 128) return fail(GMLP_UNSUPPORTED, "dims: the FPROP contraction k must be a multiple of 128");
+  Bump bb(ws);
+  SplitTables T = carve_tables(bb, G);
+  if (!ws || ws_bytes < bb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", bb.off);
+  Launcher L{stream};
+  if (!L.check(launch_fill_u32(T.flags, 0u, 1, stream), "fill")) return L.st;
+  if (!L.check(launch_scan(m_splits, G, M, T, stream), "scan")) return L.st;
+  GemmArgs g = gemm_base(layout == GMLP_GEMM_FPROP ? MODE_FPROP : MODE_WGRAD, recipe, EPI_STORE, T, G);
+  g.M = M;
+  g.N = n;
+  g.K = k;
+  g.c = c;
+  g.out_fp32 = out_dtype == GMLP_OUT_FP32;
+  if (layout == GMLP_GEMM_FPROP) {
+    g.a = op_row(*a, a->amax_pre);
+    g.b = op_row(*b, b->amax_pre);
+  } else {
+    g.a = op_col(*a, a->amax_post);
+    g.b = op_col(*b, b->amax_post);
+  }
+  if (!L.check(launch_gemm(g, stream), "grouped gemm")) return L.st;
+  g_counts[CNT_GEMM]++;
+  return ok();
+}
+
+gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream) {
+  memset(g_counts, 0, sizeof(g_counts));
+  if (!A) return fail(GMLP_INVALID_ARG, "null args");
+  gmlp_status st = mlp_common_checks(A->M, A->E, A->H, A->ffn, A->activation, A->recipe);
+  if (st != GMLP_OK) return st;
+  if ((A->M > 0 && (!A->x || !A->probs || !A->y)) || !A->m_splits) return fail(GMLP_INVALID_ARG, "null pointer argument");
+  if ((st = weight_ok(A->w1, A->recipe, true, false)) != GMLP_OK) return st;
+  if ((st = weight_ok(A->w2, A->recipe, true, false)) != GMLP_OK) return st;
+  const bool mx = is_mx(A->recipe);
+  const bool wgrad = A->weight_requires_grad != 0;
+  const bool rec = A->recompute != 0;
+  const int E = A->E;
+  const int64_t M = A->M, H = A->H, ffn = A->ffn;
+  const gmlp_recipe& r = A->recipe;
+  Bump cb(A->ctx);
+  FwdCtx C = carve_ctx(cb, M, E, H, ffn, A->activation, r, rec);
+  if (!A->ctx || A->ctx_bytes < cb.off) return fail(GMLP_WORKSPACE, "ctx too small: need %zu bytes", cb.off);
+  Bump wb(A->ws);
+  FwdWs W = carve_fwd_ws(wb, M, E, H, ffn, r);
+  if (!A->ws || A->ws_bytes < wb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", wb.off);
+
+  Launcher L{stream};
+  if (!L.check(launch_fill_u32(W.T.flags, 0u, 1, stream), "fill")) return L.st;
+  if (!L.check(launch_scan(A->m_splits, E, M, W.T, stream), "scan")) return L.st;
+  g_counts[CNT_SCAN]++;
+  const uint16_t* x = static_cast<const uint16_t*>(A->x);
+
+  // 1. group-quantize x: row-wise for fc1, column-wise for the fc1 wgrad
+  const float* x_pre = nullptr;
+  if (mx) {
+    MxOut o{static_cast<uint8_t*>(W.xq_row.q.row_data), nullptr, static_cast<uint32_t*>(W.xq_row.q.row_scale_mfma),
+            static_cast<uint8_t*>(C.xq_col.q.col_data), nullptr, static_cast<uint32_t*>(C.xq_col.q.col_scale_mfma)};
+    if (!L.check(launch_mxfp8_quant(x, M, H, W.T, E, true, wgrad, o, stream), "mxfp8 quantize x")) return L.st;
+    g_counts[CNT_MXQ]++;
+  } else {
+    float* pre = C.xq_col.q.amax_pre;
+    float* post = C.xq_col.q.amax_post;
+    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(pre), 0u, E, stream), "fill")) return L.st;
+    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(post), 0u, E, stream), "fill")) return L.st;
+    if (!L.check(launch_hadamard_amax(x, M, H, W.T, E, r.rht_sign_mask & 0xFFFF, pre, post, stream), "amax x")) return L.st;
+    g_counts[CNT_HAMAX]++;
+    NvOut o{static_cast<uint8_t*>(W.xq_row.q.row_data), static_cast<uint8_t*>(W.xq_row.q.row_scale),
+            static_cast<uint8_t*>(C.xq_col.q.col_data), static_cast<uint8_t*>(C.xq_col.q.col_scale)};
+    if (!L.check(launch_nvfp4_quant(x, M, H, W.T, E, r.rht_sign_mask & 0xFFFF, true, true, wgrad, pre, post, o, stream),
+                 "nvfp4 quantize x"))
+      return L.st;
+    g_counts[CNT_NVQ]++;
+    x_pre = pre;
+  }
+  // 2. fc1 grouped GEMM + activation * prob epilogue: h (saved) and the bf16 fc2 input
+  {
+    GemmArgs g = gemm_base(MODE_FPROP, r, EPI_FC1, W.T, E);
+    g.M = M;
+    g.N = A->activation == GMLP_SWIGLU ? 2 * ffn : ffn;
+    g.K = H;
+    g.a = op_row(W.xq_row.q, x_pre);
+    g.b = op_row(*A->w1, A->w1->amax_pre);
+    g.act = A->activation;
+    g.ffn = ffn;
+    g.probs = A->probs;
+    g.h = C.h;
+    g.a_out = W.a;
+    if (!L.check(launch_gemm(g, stream), "fc1 gemm")) return L.st;
+    g_counts[CNT_GEMM]++;
+  }
+  // 3. fc2-input cast: row-wise always; column-wise only when the backward will not rebuild it
+  const bool a_col = wgrad && !rec;
+  const float* a_pre = nullptr;
+  if (mx) {
+    MxOut o{static_cast<uint8_t*>(W.aq_row.q.row_data), nullptr, static_cast<uint32_t*>(W.aq_row.q.row_scale_mfma),
+            a_col ? static_cast<uint8_t*>(C.aq_col.q.col_data) : nullptr, nullptr,
+            a_col ? static_cast<uint32_t*>(C.aq_col.q.col_scale_mfma) : nullptr};
+    if (!L.check(launch_mxfp8_quant(W.a, M, ffn, W.T, E, true, a_col, o, stream), "mxfp8 quantize fc2 input")) return L.st;
+    g_counts[CNT_MXQ]++;
+  } else {
+    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(C.a_pre), 0u, E, stream), "fill")) return L.st;
+    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(C.a_post), 0u, E, stream), "fill")) return L.st;
+    if (!L.check(launch_hadamard_amax(W.a, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, C.a_pre, C.a_post, stream),
+                 "amax fc2 input"))
+      return L.st;
+    g_counts[CNT_HAMAX]++;
+    NvOut o{static_cast<uint8_t*>(W.aq_row.q.row_data), static_cast<uint8_t*>(W.aq_row.q.row_scale),
+            a_col ? static_cast<uint8_t*>(C.aq_col.q.col_data) : nullptr,
+            a_col ? static_cast<uint8_t*>(C.aq_col.q.col_scale) : nullptr};
+    if (!L.check(launch_nvfp4_quant(W.a, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, true, true, a_col, C.a_pre,
+                                    C.a_post, o, stream), "nvfp4 quantize fc2 input"))
+      return L.st;
+    g_counts[CNT_NVQ]++;
+    a_pre = C.a_pre;
+  }
+  // 4. fc2 grouped GEMM
+  {
+    GemmArgs g = gemm_base(MODE_FPROP, r, EPI_STORE, W.T, E);
+    g.M = M;
+    g.N = H;
+    g.K = ffn;
+    g.a = op_row(W.aq_row.q, a_pre);
+    g.b = op_row(*A->w2, A->w2->amax_pre);
+    g.c = A->y;
+    if (!L.check(launch_gemm(g, stream), "fc2 gemm")) return L.st;
+    g_counts[CNT_GEMM]++;
+  }
+  return ok();
+}
+
+gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream) {
+  memset(g_counts, 0, sizeof(g_counts));
+  if (!A) return fail(GMLP_INVALID_ARG, "null args");
+  gmlp_status st = mlp_common_checks(A->M, A->E, A->H, A->ffn, A->activation, A->recipe);
+  if (st != GMLP_OK) return st;
+  const bool dgrad = A->input_requires_grad != 0;
+  const bool wgrad = A->weight_requires_grad != 0;
+  if (!A->m_splits || (A->M > 0 && (!A->dy || !A->probs || !A->dprobs)) || (dgrad && A->M > 0 && !A->dx) ||
+      (wgrad && (!A->dw1 || !A->dw2)))
+    return fail(GMLP_INVALID_ARG, "null pointer argument");
+  if ((st = weight_ok(A->w2, A->recipe, false, true)) != GMLP_OK) return st;
+  if (dgrad && (st = weight_ok(A->w1, A->recipe, false, true)) != GMLP_OK) return st;
+  const bool mx = is_mx(A->recipe);
+  const bool rec = A->recompute != 0;
+  const int E = A->E;
+  const int64_t M = A->M, H = A->H, ffn = A->ffn;
+  const int64_t F1 = A->activation == GMLP_SWIGLU ? 2 * ffn : ffn;
+  const gmlp_recipe& r = A->recipe;
+  const uint32_t mask = r.rht_sign_mask & 0xFFFF;
+  Bump cb(const_cast<void*>(A->ctx));
+  FwdCtx C = carve_ctx(cb, M, E, H, ffn, A->activation, r, rec);
+  if (!A->ctx || A->ctx_bytes < cb.off) return fail(GMLP_WORKSPACE, "ctx too small: need %zu bytes", cb.off);
+  Bump wb(A->ws);
+  BwdWs W = carve_bwd_ws(wb, M, E, H, ffn, A->activation, r, rec);
+  if (!A->ws || A->ws_bytes < wb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", wb.off);
+
+  Launcher L{stream};
+  if (!L.check(launch_fill_u32(W.T.flags, 0u, 1, stream), "fill")) return L.st;
+  if (!L.check(launch_scan(A->m_splits, E, M, W.T, stream), "scan")) return L.st;
+  g_counts[CNT_SCAN]++;
+
+  // quantize a bf16 tensor into q (NVFP4: its own amax pass first)
+  auto quant = [&](const uint16_t* t, int64_t K, QBuf& q, bool row, bool col) -> bool {
+    if (mx) {
+      MxOut o{static_cast<uint8_t*>(q.q.row_data), nullptr, static_cast<uint32_t*>(q.q.row_scale_mfma),
+              static_cast<uint8_t*>(q.q.col_data), nullptr, static_cast<uint32_t*>(q.q.col_scale_mfma)};
+      if (!L.check(launch_mxfp8_quant(t, M, K, W.T, E, row, col, o, stream), "mxfp8 quantize")) return false;
+      g_counts[CNT_MXQ]++;
+      return true;
+    }
+    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(q.q.amax_pre), 0u, E, stream), "fill")) return false;
+    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(q.q.amax_post), 0u, E, stream), "fill")) return false;
+    if (!L.check(launch_hadamard_amax(t, M, K, W.T, E, mask, q.q.amax_pre, q.q.amax_post, stream), "amax")) return false;
+    g_counts[CNT_HAMAX]++;
+    NvOut o{static_cast<uint8_t*>(q.q.row_data), static_cast<uint8_t*>(q.q.row_scale),
+            static_cast<uint8_t*>(q.q.col_data), static_cast<uint8_t*>(q.q.col_scale)};
+    if (!L.check(launch_nvfp4_quant(t, M, K, W.T, E, mask, true, row, col, q.q.amax_pre, q.q.amax_post, o, stream),
+                 "nvfp4 quantize"))
+      return false;
+    g_counts[CNT_NVQ]++;
+    return true;
+  };
+
+  // 1. dy: row-wise for the fc2 dgrad, column-wise for the fc2 wgrad
+  if (!quant(static_cast<const uint16_t*>(A->dy), H, W.dyq, true, wgrad)) return L.st;
+  // 2. fc2 dgrad + dGLU / dSReLU epilogue (+ rebuilt fc2 input when recomputing)
+  const int ntn = dact_ntiles(ffn);
+  {
+    GemmArgs g = gemm_base(MODE_FPROP, r, EPI_DACT, W.T, E);
+    g.M = M;
+    g.N = ffn;
+    g.K = H;
+    g.a = op_row(W.dyq.q, W.dyq.q.amax_pre);
+    g.b = op_col(*A->w2, A->w2->amax_pre);
+    g.act = A->activation;
+    g.ffn = ffn;
+    g.probs = A->probs;
+    g.h = C.h;
+    g.a_out = (rec && wgrad) ? W.a2 : nullptr;
+    g.dh = W.dh;
+    g.dprob_part = W.dprob_part;
+    if (!L.check(launch_gemm(g, stream), "fc2 dgrad gemm")) return L.st;
+    g_counts[CNT_GEMM]++;
+  }
+  if (!L.check(launch_dprob_reduce(W.dprob_part, ntn, M, A->dprobs, stream), "dprob reduce")) return L.st;
+  g_counts[CNT_DPROB]++;
+  // 3. dh: row-wise for the fc1 dgrad, column-wise for the fc1 wgrad
+  if (dgrad || wgrad)
+    if (!quant(W.dh, F1, W.dhq, dgrad, wgrad)) return L.st;
+  // 4. fc2 wgrad: column-wise dy and fc2 input (rebuilt and cast with the saved amax when recomputing)
+  if (wgrad) {
+    const gmlp_grouped_q* aq = &C.aq_col.q;
+    const float* a_post = C.a_post;
+    if (rec) {
+      if (mx) {
+        MxOut o{nullptr, nullptr, nullptr, static_cast<uint8_t*>(W.a2q.q.col_data), nullptr,
+                static_cast<uint32_t*>(W.a2q.q.col_scale_mfma)};
+        if (!L.check(launch_mxfp8_quant(W.a2, M, ffn, W.T, E, false, true, o, stream), "mxfp8 quantize rebuilt fc2 input"))
+          return L.st;
+        g_counts[CNT_MXQ]++;
+      } else {
+        NvOut o{nullptr, nullptr, static_cast<uint8_t*>(W.a2q.q.col_data), static_cast<uint8_t*>(W.a2q.q.col_scale)};
+        if (!L.check(launch_nvfp4_quant(W.a2, M, ffn, W.T, E, mask, true, false, true, C.a_pre, C.a_post, o, stream),
+                     "nvfp4 quantize rebuilt fc2 input"))
+          return L.st;
+        g_counts[CNT_NVQ]++;
+      }
+      aq = &W.a2q.q;
+    }
+    GemmArgs g = gemm_base(MODE_WGRAD, r, EPI_STORE, W.T, E);
+    g.M = M;
+    g.N = H;
+    g.K = ffn;
+    g.a = op_col(W.dyq.q, W.dyq.q.amax_post);
+    g.b = op_col(*aq, a_post);
+    g.c = A->dw2;
+    g.out_fp32 = A->wgrad_dtype == GMLP_OUT_FP32;
+    if (!L.check(launch_gemm(g, stream), "fc2 wgrad gemm")) return L.st;
+    g_counts[CNT_GEMM]++;
+  }
+  // 5. fc1 dgrad
+  if (dgrad) {
+    GemmArgs g = gemm_base(MODE_FPROP, r, EPI_STORE, W.T, E);
+    g.M = M;
+    g.N = H;
+    g.K = F1;
+    g.a = op_row(W.dhq.q, W.dhq.q.amax_pre);
+    g.b = op_col(*A->w1, A->w1->amax_pre);
+    g.c = A->dx;
+    if (!L.check(launch_gemm(g, stream), "fc1 dgrad gemm")) return L.st;
+    g_counts[CNT_GEMM]++;
+  }
+  // 6. fc1 wgrad
+  if (wgrad) {
+    GemmArgs g = gemm_base(MODE_WGRAD, r, EPI_STORE, W.T, E);
+    g.M = M;
+    g.N = F1;
+    g.K = H;
+    g.a = op_col(W.dhq.q, W.dhq.q.amax_post);
+    g.b = op_col(C.xq_col.q, C.xq_col.q.amax_post);
+    g.c = A->dw1;
+    g.out_fp32 = A->wgrad_dtype == GMLP_OUT_FP32;
+    if (!L.check(launch_gemm(g, stream), "fc1 wgrad gemm")) return L.st;
+    g_counts[CNT_GEMM]++;
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,675 @@
+// Grouped GEMMs of the MoE MLP on CDNA4 matrix cores, with the fused fc1 and fc2-dgrad epilogues.
+//
+// Sources: "GEMM + Swiglu fused Grouped MLP for MXFP8" (sequence diagram: the FC1
+// GLU kernel writes the bf16 pre-activation and the activation; the FC2 dGLU
+// kernel consumes dy, the saved pre-activation and the fc2 weight and emits the
+// fc1 grad and dprob; FC1 dgrad; wgrad grouped GEMMs) and "Reduce NVFP4
+// quantization work ..." (Description and commits: the accumulator is rounded
+// through the bf16 C dtype before the activation; the backward activation
+// kernel regenerates the fc2 input bit-exactly).
+//
+// Every GEMM here is C = A . B^T with both operands K-contiguous:
+//   FPROP  A = row-wise [rows of group g, K], B = expert g's [N, K]      (fc1, fc2, both dgrads)
+//   WGRAD  A = column-wise [N_a, P_g], B = column-wise [N_b, P_g]        (both wgrads, K = tokens)
+//
+// Workgroup tile 256 x 256, 4 waves of 128 x 128 (4 x 4 tiles of 32 x 32), K staged
+// through LDS in 128-byte rows (128 fp8, or 64 bf16 after NVFP4 dequantization),
+// double buffered, 16-byte chunks XOR-swizzled by row so that both the 16-byte
+// stores and the MFMA fragment reads are bank-conflict-free.
+//
+// MXFP8: V_MFMA_SCALE_F32_32X32X64_F8F6F4 with E8M0 block scales.  Lane (m + 32j)
+// holds row m, K bytes [16j, 16j+16) and [32+16j, 48+16j) of the 64-K step, and
+// supplies the scale of row m's 32-block j; the MFMA-ready scale word of a row
+// holds the 4 blocks of a 128-K stage, so lane group j shifts it by 8j bytes and
+// selects byte 2s for K-step s.
+// NVFP4: E2M1 x E4M3 products have at most 6 significant bits and exponents in
+// [2^-10, 2688], so the loader expands them exactly to bf16 and the GEMM runs on
+// V_MFMA_F32_32X32X16_BF16; the per-group global scales multiply the fp32
+// result.  (The block-scaled MFMA takes E8M0 scales per 32 elements; NVFP4's
+// E4M3 scales per 16 cannot be folded into it exactly.)
+#include "device_common.h"
+#include "kernels.h"
+
+namespace gmlp {
+
+constexpr int BM = 256, BN = 256;
+constexpr int BKB = 128;                         // bytes per tile row per stage
+constexpr int NTHREADS = 256;
+constexpr int OPB = BM * BKB;                    // bytes of one operand stage (32 KB)
+constexpr int SCALE_OFF = 2 * OPB;               // MXFP8 scale words of the stage: A [256] then B [256] (u32)
+constexpr int STAGE = 2 * OPB + 2048;            // A + B + scales (66 KB)
+// Epilogue staging: 128 rows x 256 bf16 (512 bytes) per buffer; the 16-byte chunk index is
+// XORed with bits 2..3 of the row so that the two rows a wave writes at once (r and r + 4)
+// fall in different banks.
+__device__ __forceinline__ int ep_off(int row, int col) {
+  return row * 256 + ((((col >> 3) ^ (((row >> 2) & 3) << 2))) << 3) + (col & 7);
+}
+
+// Wave-uniform copies (the values are uniform by construction; this tells the compiler so
+// that descriptors and bases live in SGPRs).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ T* uni_ptr(T* p) { return reinterpret_cast<T*>(uni((int64_t)reinterpret_cast<uintptr_t>(p))); }
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ (row & 7)) << 4); }
+
+// ----------------------------------------------------------------------------- activations
+// Shared by the fc1 epilogue and the fc2-dgrad recompute so that both produce the same bits;
+// every operation is an explicitly rounded fp32 op (no contraction).
+__device__ __forceinline__ float sigmoid_f(float g) { return __fdiv_rn(1.0f, __fadd_rn(1.0f, expf(-g))); }
+
+__device__ __forceinline__ float act_value(int act, float g, float u) {
+  if (act == 0) return __fmul_rn(__fmul_rn(g, sigmoid_f(g)), u);   // silu(gate) * up
+  const float r = fmaxf(g, 0.0f);
+  return __fmul_rn(r, r);                                            // relu(h)^2
+}
+__device__ __forceinline__ float act_out(int act, float g, float u, float p) {
+  return round_bf16(__fmul_rn(act_value(act, g, u), p));
+}
+// d(act * p)/dh for upstream da: d0 = d/dgate (or d/dh), d1 = d/dup; dp = da * act (dL/dp).
+__device__ __forceinline__ void act_grad(int act, float g, float u, float da, float p, float& d0, float& d1,
+                                         float& dp) {
+  if (act == 0) {
+    const float sg = sigmoid_f(g);
+    const float silu = __fmul_rn(g, sg);
+    const float dap = __fmul_rn(da, p);
+    const float dsilu = __fmul_rn(sg, __fadd_rn(1.0f, __fmul_rn(g, __fsub_rn(1.0f, sg))));
+    d0 = __fmul_rn(__fmul_rn(dap, u), dsilu);
+    d1 = __fmul_rn(dap, silu);
+    dp = __fmul_rn(da, __fmul_rn(silu, u));
+  } else {
+    const float r = fmaxf(g, 0.0f);
+    d0 = __fmul_rn(__fmul_rn(__fmul_rn(da, p), 2.0f), r);
+    d1 = 0.0f;
+    dp = __fmul_rn(da, __fmul_rn(r, r));
+  }
+}
+
+// ----------------------------------------------------------------------------- tile context
+struct Ctx {
+  int g;             // group / expert
+  int64_t arow0;     // FPROP: first global row of the tile; WGRAD: first A feature row
+  int arows;         // valid A rows in the tile
+  int64_t nrow0;     // first output column (FPROP) / B feature row (WGRAD)
+  int nt;            // n-tile index
+  int64_t kvalid;    // contraction length (K, or P_g)
+  int nk;            // stages
+  // operand bases (element offsets of row 0 of the operand matrix for this group)
+  int64_t a_base, b_base, a_ld, b_ld;
+  int64_t a_sw_base, b_sw_base, a_sw_ld, b_sw_ld;   // MXFP8 scale words: base + kt * ld + row
+  float alpha;
+};
+
+// Row of B (in the weight/feature matrix) held by tile row j, and whether it exists.
+template <int MODE, int EPI>
+__device__ __forceinline__ bool b_row(const GemmArgs& A, const Ctx& c, int j, int64_t& row) {
+  if (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
+    // SwiGLU fc1: wave wn's 128 columns are [gate f..f+63 | up f..f+63], f = nt*128 + wn*64
+    const int wn = j >> 7, q = j & 127;
+    const int64_t f = (int64_t)c.nt * 128 + wn * 64 + (q & 63);
+    row = (q < 64) ? f : A.ffn + f;
+    return f < A.ffn;
+  }
+  row = c.nrow0 + j;
+  return row < (MODE == MODE_FPROP ? A.N : A.K);
+}
+
+// ----------------------------------------------------------------------------- stage loads
+// MXFP8: direct buffer -> LDS DMA (buffer_load_dwordx4 ... lds).  One instruction moves a
+// wave's 64 x 16 bytes into 1 KB of LDS (lane l lands at +16 l), i.e. 8 tile rows; lane l
+// fetches logical chunk (l % 8) ^ (row % 8) of its row so that LDS holds the swizzled layout.
+// Wave w loads A rows and B rows [64 w, 64 w + 64) of the tile through one buffer resource
+// each, whose size ends at the last valid row: rows past it read as zero (hardware range
+// check), so partial tiles need no clamping and every lane keeps one 32-bit offset.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = uni((int)(bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes)));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uni_ptr(base)), (short)0, n, (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, 0, 0, 0);
+}
+
+struct DmaPlan {
+  __amdgpu_buffer_rsrc_t ra, rb;   // this wave's 64-row bands of A and B
+  uint32_t lane_off;               // (lane / 8) * ld + 16 * ((lane % 8) ^ (lane / 8 % 8))
+  uint32_t ld;
+};
+
+template <int MODE, int EPI>
+__device__ __forceinline__ DmaPlan make_dma_plan(const GemmArgs& A, const Ctx& c, int wave, int lane) {
+  DmaPlan d;
+  d.ld = (uint32_t)c.a_ld;
+  const int r8 = lane >> 3;
+  d.lane_off = (uint32_t)r8 * d.ld + 16u * (uint32_t)((lane & 7) ^ (r8 & 7));
+  const int64_t a_rows = min(64, max(0, c.arows - 64 * wave));
+  d.ra = make_rsrc(A.a.data + c.a_base + (c.arow0 + 64 * wave) * c.a_ld, a_rows * c.a_ld);
+  int64_t b_first, b_rows;
+  if (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
+    // band w = [gate | up][(w & 1)] rows f0 + 64 (w >> 1) .. + 64, f0 = 128 nt
+    const int64_t f = (int64_t)c.nt * 128 + 64 * (wave >> 1);
+    b_first = ((wave & 1) ? A.ffn : 0) + f;
+    b_rows = min((int64_t)64, max((int64_t)0, A.ffn - f));
+  } else {
+    const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
+    b_first = c.nrow0 + 64 * wave;
+    b_rows = min((int64_t)64, max((int64_t)0, nb - b_first));
+  }
+  d.rb = make_rsrc(A.b.data + c.b_base + b_first * c.b_ld, b_rows * c.b_ld);
+  return d;
+}
+
+__device__ __forceinline__ void mx_dma_stage(const DmaPlan& d, int kt, uint8_t* stage, int wave) {
+  const uint32_t k = (uint32_t)kt * BKB;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t voff = d.lane_off + (uint32_t)i * 8u * d.ld + k;
+    dma16(d.ra, voff, stage + wave * 8192 + i * 1024);
+    dma16(d.rb, voff, stage + OPB + wave * 8192 + i * 1024);
+  }
+}
+
+// NVFP4: thread = tile row; 64 packed E2M1 (32 bytes) + 4 E4M3 block scales per operand,
+// expanded exactly to bf16 and written to LDS by the thread.
+struct NvStage {
+  uint4 ra[2], rb[2];
+  uint32_t sa[4], sb[4];
+};
+
+template <int MODE, int EPI>
+__device__ __forceinline__ void nv_load_stage(const GemmArgs& A, const Ctx& c, int kt, int tid, NvStage& s) {
+  const int64_t k = (int64_t)kt * 64;
+  const int row = tid;
+  {
+    const int ar = min(row, c.arows - 1);
+    const int64_t e = c.a_base + (c.arow0 + ar) * c.a_ld + k;
+    s.ra[0] = *reinterpret_cast<const uint4*>(A.a.data + e / 2);
+    s.ra[1] = *reinterpret_cast<const uint4*>(A.a.data + e / 2 + 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s.sa[q] = A.a.scale[e / 16 + q];
+  }
+  {
+    int64_t br = 0;
+    if (!b_row<MODE, EPI>(A, c, row, br)) br = (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) ? 0 : c.nrow0;
+    const int64_t e = c.b_base + br * c.b_ld + k;
+    s.rb[0] = *reinterpret_cast<const uint4*>(A.b.data + e / 2);
+    s.rb[1] = *reinterpret_cast<const uint4*>(A.b.data + e / 2 + 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s.sb[q] = A.b.scale[e / 16 + q];
+  }
+}
+
+__device__ __forceinline__ void nv_store_row(uint8_t* base, int row, const uint4* r, const uint32_t* s) {
+  const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {              // 8 bf16 per chunk = one packed word
+    const float sc = e4m3_decode_pos(s[ch >> 1]);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = e2m1_decode((w[ch] >> (8 * i)) & 0xFu) * sc;
+      const float hi = e2m1_decode((w[ch] >> (8 * i + 4)) & 0xFu) * sc;
+      o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    }
+    *reinterpret_cast<uint4*>(base + swz(row, ch)) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+__device__ __forceinline__ void nv_store_stage(uint8_t* stage, int tid, const NvStage& s) {
+  nv_store_row(stage, tid, s.ra, s.sa);
+  nv_store_row(stage + OPB, tid, s.rb, s.sb);
+}
+
+// ----------------------------------------------------------------------------- MFMA stage
+template <int S>
+__device__ __forceinline__ void mx_kstep(const uint8_t* stage, int wm, int wn, int lane, const uint32_t* sca,
+                                         const uint32_t* scb, v16f (&acc)[4][4]) {
+  const int m = lane & 31, j = lane >> 5;
+  v8i bf[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int rb = wn * 128 + t * 32 + m;
+    const uint4 b0 = *reinterpret_cast<const uint4*>(stage + OPB + swz(rb, 4 * S + j));
+    const uint4 b1 = *reinterpret_cast<const uint4*>(stage + OPB + swz(rb, 4 * S + 2 + j));
+    bf[t] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  }
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm) {
+    const int ra = wm * 128 + tm * 32 + m;
+    const uint4 a0 = *reinterpret_cast<const uint4*>(stage + swz(ra, 4 * S + j));
+    const uint4 a1 = *reinterpret_cast<const uint4*>(stage + swz(ra, 4 * S + 2 + j));
+    const v8i af = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[tn], acc[tm][tn], 0, 0, 2 * S,
+                                                                     (int)sca[tm], 2 * S, (int)scb[tn]);
+  }
+  // keep the next K-step's fragment reads from being hoisted over this one (register budget)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int S>
+__device__ __forceinline__ void bf_kstep(const uint8_t* stage, int wm, int wn, int lane, v16f (&acc)[4][4]) {
+  const int m = lane & 31, j = lane >> 5;
+  v8bf af[4], bf[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint4 a = *reinterpret_cast<const uint4*>(stage + swz(wm * 128 + t * 32 + m, 2 * S + j));
+    const uint4 b = *reinterpret_cast<const uint4*>(stage + OPB + swz(wn * 128 + t * 32 + m, 2 * S + j));
+    af[t] = __builtin_bit_cast(v8bf, a);
+    bf[t] = __builtin_bit_cast(v8bf, b);
+  }
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ----------------------------------------------------------------------------- tile mapping
+// Workgroups are dealt round-robin to the 8 XCDs; renumber so that each XCD runs a
+// contiguous range of tiles (neighbouring tiles share A rows or the expert's B tile
+// in that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+  const int full = (nb / 8) * 8;
+  if (bid >= full) return bid;
+  return (bid % 8) * (nb / 8) + bid / 8;
+}
+
+template <int FMT, int MODE, int EPI>
+__device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int ntn;
+  if (MODE == MODE_FPROP) {
+    ntn = (EPI == EPI_FC1 && A.act == 0) ? (int)((A.ffn + 127) / 128) : (int)((A.N + BN - 1) / BN);
+  } else {
+    ntn = (int)((A.K + BN - 1) / BN);
+  }
+  const int tile_m = bid / ntn;
+  c.nt = bid % ntn;
+  c.alpha = 1.0f;
+  if (MODE == MODE_FPROP) {
+    if (A.G <= 0 || tile_m >= A.T.t256_off[A.G]) return false;
+    c.g = find_group(A.T.t256_off, A.G, tile_m);
+    const int64_t gstart = A.T.row_off[c.g];
+    const int m = A.T.row_off[c.g + 1] - (int)gstart;
+    mt = tile_m - A.T.t256_off[c.g];
+    c.arow0 = gstart + (int64_t)mt * BM;
+    c.arows = min(BM, m - mt * BM);
+    c.nrow0 = (int64_t)c.nt * BN;
+    c.kvalid = A.K;
+    c.a_base = 0;
+    c.a_ld = A.K;
+    // B rows per expert; weight scale words are per expert: [E][ceil(K/128)][brows]
+    const int64_t brows = (EPI == EPI_FC1 && A.act == 0) ? 2 * A.ffn : A.N;
+    c.b_base = (int64_t)c.g * brows * A.K;
+    c.b_ld = A.K;
+    c.a_sw_base = 0;
+    c.a_sw_ld = A.M;
+    c.b_sw_base = (int64_t)c.g * ((A.K + 127) / 128) * brows;
+    c.b_sw_ld = brows;
+    if (FMT == FMT_NVFP4) {
+      const float sa = nvfp4_global_scale(A.a.amax[c.g]);
+      const float sb = nvfp4_global_scale(A.b.amax[c.g]);
+      c.alpha = __fmul_rn(__fdiv_rn(1.0f, sa), __fdiv_rn(1.0f, sb));
+    }
+    c.nk = (int)((A.K + (FMT == FMT_MXFP8 ? 127 : 63)) / (FMT == FMT_MXFP8 ? 128 : 64));
+  } else {
+    const int ntm = (int)((A.N + BM - 1) / BM);
+    const int per_g = ntm;
+    c.g = tile_m / per_g;
+    if (c.g >= A.G) return false;
+    mt = tile_m % per_g;
+    const int64_t P = A.T.col_off[c.g + 1] - A.T.col_off[c.g];
+    c.arow0 = (int64_t)mt * BM;
+    c.arows = (int)min((int64_t)BM, A.N - c.arow0);
+    c.nrow0 = (int64_t)c.nt * BN;
+    c.kvalid = P;
+    c.a_base = A.N * (int64_t)A.T.col_off[c.g];
+    c.a_ld = P;
+    c.b_base = A.K * (int64_t)A.T.col_off[c.g];
+    c.b_ld = P;
+    c.a_sw_base = A.N * (int64_t)A.T.colw_off[c.g];
+    c.a_sw_ld = A.N;
+    c.b_sw_base = A.K * (int64_t)A.T.colw_off[c.g];
+    c.b_sw_ld = A.K;
+    if (FMT == FMT_NVFP4) {
+      const float sa = nvfp4_global_scale(A.a.amax[c.g]);
+      const float sb = nvfp4_global_scale(A.b.amax[c.g]);
+      c.alpha = __fmul_rn(__fdiv_rn(1.0f, sa), __fdiv_rn(1.0f, sb));
+    }
+    c.nk = (int)((P + (FMT == FMT_MXFP8 ? 127 : 63)) / (FMT == FMT_MXFP8 ? 128 : 64));
+  }
+  return true;
+}
+
+// MFMA-ready scale words of the stage's 256 A rows and 256 B rows, DMAed into LDS next to the
+// data (one 1 KB instruction each: lane l fetches the words of tile rows 4l..4l+3).  Rows past
+// the valid range read 0: their data is zero too, and those outputs are never stored.
+template <int MODE, int EPI>
+__device__ __forceinline__ void mx_dma_scales(const GemmArgs& A, const Ctx& c, int kt, uint8_t* stage, int wave,
+                                              int lane) {
+  if (wave == 0) {
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(A.a.scale_mfma + c.a_sw_base + (int64_t)kt * c.a_sw_ld + c.arow0, 4 * (int64_t)c.arows);
+    dma16(ra, 16u * lane, stage + SCALE_OFF);
+  } else if (wave == 1) {
+    const uint32_t* bw = A.b.scale_mfma + c.b_sw_base + (int64_t)kt * c.b_sw_ld;
+    if (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
+      // tile rows in 64-row bands [gate f0.. | up f0.. | gate f0+64.. | up f0+64..], f0 = 128 nt;
+      // one resource from gate row f0 to the end of the expert's up rows
+      const int64_t f0 = (int64_t)c.nt * 128;
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(bw + f0, 4 * (2 * A.ffn - f0));
+      const int band = lane >> 4;
+      const uint32_t row = (uint32_t)((band & 1) * A.ffn + (band >> 1) * 64 + 4 * (lane & 15));
+      dma16(rb, 4u * row, stage + SCALE_OFF + 1024);
+    } else {
+      const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(bw + c.nrow0, 4 * max((int64_t)0, nb - c.nrow0));
+      dma16(rb, 16u * lane, stage + SCALE_OFF + 1024);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- kernel
+template <int FMT, int MODE, int EPI>
+__device__ __forceinline__ void compute_stage(const uint8_t* stage, int wm, int wn, int lane, v16f (&acc)[4][4]) {
+  if (FMT == FMT_MXFP8) {
+    // this lane's scale words (rows 32 t + m of its wave's A and B sub-tiles), shifted so that
+    // byte 2s holds its 32-block of K-step s
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(stage + SCALE_OFF);
+    const int m = lane & 31, sh = 8 * (lane >> 5);
+    uint32_t sca[4], scb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sca[t] = w[wm * 128 + t * 32 + m] >> sh;
+      scb[t] = w[256 + wn * 128 + t * 32 + m] >> sh;
+    }
+    mx_kstep<0>(stage, wm, wn, lane, sca, scb, acc);
+    mx_kstep<1>(stage, wm, wn, lane, sca, scb, acc);
+  } else {
+    bf_kstep<0>(stage, wm, wn, lane, acc);
+    bf_kstep<1>(stage, wm, wn, lane, acc);
+    bf_kstep<2>(stage, wm, wn, lane, acc);
+    bf_kstep<3>(stage, wm, wn, lane, acc);
+  }
+}
+
+// Issues the loads of stage kt into `dst` (MXFP8: DMA straight to LDS; NVFP4: to registers).
+template <int FMT, int MODE, int EPI>
+__device__ __forceinline__ void issue_stage(const GemmArgs& A, const Ctx& c, const DmaPlan& d, int kt, uint8_t* dst,
+                                            int tid, NvStage& nv) {
+  if (FMT == FMT_MXFP8) {
+    const int wave = uni(tid >> 6);
+    mx_dma_scales<MODE, EPI>(A, c, kt, dst, wave, tid & 63);
+    mx_dma_stage(d, kt, dst, wave);
+  } else {
+    nv_load_stage<MODE, EPI>(A, c, kt, tid, nv);
+  }
+}
+
+// Completes stage kt in `dst` (NVFP4: expand and store), waits for all of its data, barrier.
+template <int FMT>
+__device__ __forceinline__ void finish_stage(uint8_t* dst, int tid, const NvStage& nv) {
+  if (FMT == FMT_NVFP4) nv_store_stage(dst, tid, nv);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+template <int FMT, int MODE, int EPI>
+__global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
+  // Two distinct LDS objects (not one array) so that the compiler can tell the buffer being
+  // read from the buffer the DMA is filling when it places its wait counts.
+  __shared__ __align__(16) uint8_t buf0[STAGE];
+  __shared__ __align__(16) uint8_t buf1[STAGE];
+  int mt = 0;
+  Ctx c;
+  if (!make_ctx<FMT, MODE, EPI>(A, mt, c)) return;
+  c.g = uni(c.g); c.arows = uni(c.arows); c.nt = uni(c.nt); c.nk = uni(c.nk);
+  c.arow0 = uni(c.arow0); c.nrow0 = uni(c.nrow0); c.kvalid = uni(c.kvalid);
+  c.a_base = uni(c.a_base); c.b_base = uni(c.b_base); c.a_ld = uni(c.a_ld); c.b_ld = uni(c.b_ld);
+  c.a_sw_base = uni(c.a_sw_base); c.b_sw_base = uni(c.b_sw_base); c.a_sw_ld = uni(c.a_sw_ld); c.b_sw_ld = uni(c.b_sw_ld);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = uni(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+
+  NvStage nv;
+  DmaPlan dp;
+  if (FMT == FMT_MXFP8) dp = make_dma_plan<MODE, EPI>(A, c, wave, lane);
+  if (c.nk > 0) {
+    issue_stage<FMT, MODE, EPI>(A, c, dp, 0, buf0, tid, nv);
+    finish_stage<FMT>(buf0, tid, nv);
+  }
+  // stages in pairs (even stage in buf0, odd stage in buf1), one loop exit, odd tail after
+  int kt = 0;
+  for (; kt + 1 < c.nk; kt += 2) {
+    issue_stage<FMT, MODE, EPI>(A, c, dp, kt + 1, buf1, tid, nv);
+    compute_stage<FMT, MODE, EPI>(buf0, wm, wn, lane, acc);
+    finish_stage<FMT>(buf1, tid, nv);
+    const bool more = kt + 2 < c.nk;
+    if (more) issue_stage<FMT, MODE, EPI>(A, c, dp, kt + 2, buf0, tid, nv);
+    compute_stage<FMT, MODE, EPI>(buf1, wm, wn, lane, acc);
+    if (more) finish_stage<FMT>(buf0, tid, nv);
+  }
+  if (kt < c.nk) compute_stage<FMT, MODE, EPI>(buf0, wm, wn, lane, acc);
+  __syncthreads();
+
+  // --------------------------------------------------------------------------- epilogues
+  const int m = lane & 31, j = lane >> 5;
+  if (EPI == EPI_STORE && A.out_fp32) {
+    // fp32 output (optional wgrad dtype): direct stores
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        const int64_t col = c.nrow0 + wn * 128 + tn * 32 + m;
+        const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + tm * 32 + 8 * (r >> 2) + 4 * j + (r & 3);
+          if (row >= c.arows || col >= ncols) continue;
+          const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + row : (int64_t)c.g * A.N + c.arow0 + row;
+          static_cast<float*>(A.c)[orow * ncols + col] = acc[tm][tn][r] * c.alpha;
+        }
+      }
+    return;
+  }
+  // Stage the bf16-rounded tile (the C dtype of every fused output) in LDS, then run the
+  // epilogue per 8-column chunk with 16-byte loads and stores.
+  {
+    uint16_t* st = reinterpret_cast<uint16_t*>(wm == 0 ? buf0 : buf1);
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = tm * 32 + 8 * (r >> 2) + 4 * j + (r & 3);      // row within this half
+          st[ep_off(row, wn * 128 + tn * 32 + m)] = (uint16_t)f32_to_bf16_bits(acc[tm][tn][r] * c.alpha);
+        }
+  }
+  __syncthreads();
+  // staged element (row, col) of the 256 x 256 tile
+  auto stg = [&](int row, int col) -> const uint4* {
+    const uint16_t* st = reinterpret_cast<const uint16_t*>(row < 128 ? buf0 : buf1);
+    return reinterpret_cast<const uint4*>(st + ep_off(row & 127, col));
+  };
+
+  if (EPI == EPI_STORE) {
+    const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
+    uint16_t* C = static_cast<uint16_t*>(A.c);
+    for (int it = 0; it < 32; ++it) {
+      const int row = it * 8 + (tid >> 5);
+      const int col = 8 * (tid & 31);
+      const int64_t gcol = c.nrow0 + col;
+      if (row >= c.arows || gcol >= ncols) continue;
+      const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + row : (int64_t)c.g * A.N + c.arow0 + row;
+      *reinterpret_cast<uint4*>(C + orow * ncols + gcol) = *stg(row, col);
+    }
+    return;
+  }
+
+  if (EPI == EPI_FC1) {
+    const int64_t F1 = (A.act == 0) ? 2 * A.ffn : A.ffn;
+    if (A.act == 0) {
+      // staged columns of wave wn: [gate f0..f0+63 | up f0..f0+63], f0 = nt*128 + wn*64
+      for (int it = 0; it < 16; ++it) {
+        const int row = it * 16 + (tid >> 4);
+        const int fl = 8 * (tid & 15);
+        const int64_t f = (int64_t)c.nt * 128 + fl;
+        if (row >= c.arows || f >= A.ffn) continue;
+        const int64_t grow = c.arow0 + row;
+        const int scol = (fl >> 6) * 128 + (fl & 63);
+        const uint4 gv = *stg(row, scol);
+        const uint4 uv = *stg(row, scol + 64);
+        *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = gv;
+        *reinterpret_cast<uint4*>(A.h + grow * F1 + A.ffn + f) = uv;
+        const float p = A.probs[grow];
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+        uint32_t ow[4];
+        for (int i = 0; i < 4; ++i) {
+          const float a0 = act_out(0, bf16_to_f32(gw[i] & 0xFFFFu), bf16_to_f32(uw[i] & 0xFFFFu), p);
+          const float a1 = act_out(0, bf16_to_f32(gw[i] >> 16), bf16_to_f32(uw[i] >> 16), p);
+          ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
+        }
+        *reinterpret_cast<uint4*>(A.a_out + grow * A.ffn + f) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    } else {
+      for (int it = 0; it < 32; ++it) {
+        const int row = it * 8 + (tid >> 5);
+        const int col = 8 * (tid & 31);
+        const int64_t f = c.nrow0 + col;
+        if (row >= c.arows || f >= A.ffn) continue;
+        const int64_t grow = c.arow0 + row;
+        const uint4 hv = *stg(row, col);
+        *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = hv;
+        const float p = A.probs[grow];
+        const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+        uint32_t ow[4];
+        for (int i = 0; i < 4; ++i) {
+          const float a0 = act_out(1, bf16_to_f32(hw[i] & 0xFFFFu), 0.0f, p);
+          const float a1 = act_out(1, bf16_to_f32(hw[i] >> 16), 0.0f, p);
+          ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
+        }
+        *reinterpret_cast<uint4*>(A.a_out + grow * A.ffn + f) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    }
+    return;
+  }
+
+  // EPI_DACT: staged tile = da [rows, f]; writes dh (+ a' when recomputing) and per-row dprob
+  // partials of this n-tile, summed over its 256 columns in a fixed order.
+  {
+    const int64_t F1 = (A.act == 0) ? 2 * A.ffn : A.ffn;
+    for (int it = 0; it < 32; ++it) {
+      const int row = it * 8 + (tid >> 5);
+      const int col = 8 * (tid & 31);
+      const int64_t f = c.nrow0 + col;
+      const bool ok = row < c.arows && f < A.ffn;
+      const int64_t grow = c.arow0 + (row < c.arows ? row : 0);
+      float psum = 0.0f;
+      if (ok) {
+        const float p = A.probs[grow];
+        const uint4 dv = *stg(row, col);
+        const uint4 gv = *reinterpret_cast<const uint4*>(A.h + grow * F1 + f);
+        uint4 uv = make_uint4(0, 0, 0, 0);
+        if (A.act == 0) uv = *reinterpret_cast<const uint4*>(A.h + grow * F1 + A.ffn + f);
+        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w},
+                       uw[4] = {uv.x, uv.y, uv.z, uv.w};
+        uint32_t o0[4], o1[4], oa[4];
+        for (int i = 0; i < 4; ++i) {
+          uint32_t r0 = 0, r1 = 0, ra = 0;
+          for (int hh = 0; hh < 2; ++hh) {
+            const float da = bf16_to_f32((dw[i] >> (16 * hh)) & 0xFFFFu);
+            const float g = bf16_to_f32((gw[i] >> (16 * hh)) & 0xFFFFu);
+            const float u = bf16_to_f32((uw[i] >> (16 * hh)) & 0xFFFFu);
+            float d0, d1, dp;
+            act_grad(A.act, g, u, da, p, d0, d1, dp);
+            psum += dp;
+            r0 |= f32_to_bf16_bits(d0) << (16 * hh);
+            r1 |= f32_to_bf16_bits(d1) << (16 * hh);
+            ra |= (__float_as_uint(act_out(A.act, g, u, p)) >> 16) << (16 * hh);
+          }
+          o0[i] = r0;
+          o1[i] = r1;
+          oa[i] = ra;
+        }
+        *reinterpret_cast<uint4*>(A.dh + grow * F1 + f) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+        if (A.act == 0) *reinterpret_cast<uint4*>(A.dh + grow * F1 + A.ffn + f) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+        if (A.a_out) *reinterpret_cast<uint4*>(A.a_out + grow * A.ffn + f) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) psum += __shfl_xor(psum, o, 64);
+      if ((tid & 31) == 0 && row < c.arows) A.dprob_part[(int64_t)c.nt * A.M + grow] = psum;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- dprob reduce
+__global__ void dprob_reduce_kernel(const float* __restrict__ part, int nparts, int64_t M, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M) return;
+  float s = 0.0f;
+  for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * M + i];
+  out[i] = s;
+}
+
+// ----------------------------------------------------------------------------- launchers
+int gemm_fprop_ntiles_n(const GemmArgs& g) {
+  if (g.epi == EPI_FC1 && g.act == 0) return (int)((g.ffn + 127) / 128);
+  return (int)((g.N + BN - 1) / BN);
+}
+
+template <int FMT, int MODE, int EPI>
+static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
+  int64_t tiles;
+  if (MODE == MODE_FPROP) {
+    tiles = ((g.M + BM - 1) / BM + g.G) * (int64_t)gemm_fprop_ntiles_n(g);
+  } else {
+    tiles = (int64_t)g.G * ((g.N + BM - 1) / BM) * ((g.K + BN - 1) / BN);
+  }
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_kernel<FMT, MODE, EPI>), dim3((unsigned)tiles), dim3(NTHREADS), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  if (g.mode == MODE_FPROP && g.M == 0) return hipSuccess;
+#define GMLP_DISPATCH(F, MO, E) \
+  if (g.fmt == F && g.mode == MO && g.epi == E) return launch_one<F, MO, E>(g, s);
+  GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_STORE)
+  GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_FC1)
+  GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_DACT)
+  GMLP_DISPATCH(FMT_MXFP8, MODE_WGRAD, EPI_STORE)
+  GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_STORE)
+  GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_FC1)
+  GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_DACT)
+  GMLP_DISPATCH(FMT_NVFP4, MODE_WGRAD, EPI_STORE)
+#undef GMLP_DISPATCH
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dprob_reduce(const float* part, int nparts, int64_t M, float* out, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(dprob_reduce_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, part, nparts, M, out);
+  return hipGetLastError();
+}
+
+}  // namespace gmlp

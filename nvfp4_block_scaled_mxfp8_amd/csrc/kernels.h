@@ -1,0 +1,88 @@
+// Private interface between the host planner (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmlp {
+
+// Per-call split tables, computed on the device from m_splits (all int32, length G+1,
+// exclusive prefix sums; row counts clamped so that row_off[G] <= M).
+struct SplitTables {
+  uint32_t* flags;     // bit 0 negative split, bit 1 sum past M, bit 2 sum short of M
+  int32_t* row_off;    // rows
+  int32_t* col_off;    // P_g = m_g rounded up to 128 (column-wise layout)
+  int32_t* colw_off;   // P_g / 128 (MFMA-ready column-wise scale words)
+  int32_t* t128_off;   // ceil(m_g / 128)  (128-row tiles)
+  int32_t* t256_off;   // ceil(m_g / 256)  (256-row tiles)
+};
+
+struct MxOut {
+  uint8_t* row_data;
+  uint8_t* row_scale;
+  uint32_t* row_scale_mfma;
+  uint8_t* col_data;
+  uint8_t* col_scale;
+  uint32_t* col_scale_mfma;
+};
+
+struct NvOut {
+  uint8_t* row_data;
+  uint8_t* row_scale;
+  uint8_t* col_data;
+  uint8_t* col_scale;
+};
+
+hipError_t launch_scan(const int32_t* m_splits, int G, int64_t M, SplitTables T, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+hipError_t launch_mxfp8_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
+                              bool row, bool col, MxOut o, hipStream_t s);
+hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
+                                uint32_t mask, float* pre, float* post, hipStream_t s);
+hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
+                              uint32_t mask, bool rht, bool row, bool col, const float* pre,
+                              const float* post, NvOut o, hipStream_t s);
+// Per-expert amax of stacked weights [E, N, K] (one group per expert, no transform).
+hipError_t launch_weight_amax(const uint16_t* w, const void* const* w_ptrs, int E, int64_t N,
+                              int64_t K, float* amax, hipStream_t s);
+// Copies discrete expert weights into a stacked bf16 buffer.
+hipError_t launch_gather_weights(const void* const* w_ptrs, int E, int64_t N, int64_t K,
+                                 uint16_t* out, hipStream_t s);
+
+// ----------------------------------------------------------------------------- GEMM
+enum GemmFmt { FMT_MXFP8 = 0, FMT_NVFP4 = 1 };
+enum GemmMode { MODE_FPROP = 0, MODE_WGRAD = 1 };
+enum GemmEpi { EPI_STORE = 0, EPI_FC1 = 1, EPI_DACT = 2 };
+
+struct GemmOperand {
+  const uint8_t* data;        // fp8 / packed fp4
+  const uint32_t* scale_mfma; // MXFP8: MFMA-ready words
+  const uint8_t* scale;       // NVFP4: E4M3 block scales (canonical)
+  const float* amax;          // NVFP4: per-group (or per-expert) amax for the global scale
+};
+
+struct GemmArgs {
+  int mode, fmt, epi;
+  GemmOperand a, b;
+  SplitTables T;
+  int G;
+  int64_t M;         // FPROP: total rows of A
+  int64_t N;         // FPROP: output columns (B rows per expert); WGRAD: rows of A per group
+  int64_t K;         // FPROP: contraction; WGRAD: rows of B per group
+  // outputs
+  void* c;           // EPI_STORE: C (bf16 or fp32)
+  int out_fp32;
+  // fused epilogue operands
+  int act;           // 0 SwiGLU, 1 SReLU
+  int64_t ffn;       // EPI_FC1 / EPI_DACT: ffn (output a width); SwiGLU F1 = 2 ffn
+  const float* probs;
+  uint16_t* h;       // EPI_FC1: out h [M, F1]; EPI_DACT: in h
+  uint16_t* a_out;   // EPI_FC1: out a [M, ffn]; EPI_DACT: out a' (recompute) or null
+  uint16_t* dh;      // EPI_DACT: out dh [M, F1]
+  float* dprob_part; // EPI_DACT: [n_tiles, M]
+};
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+int gemm_fprop_ntiles_n(const GemmArgs& g);   // N tiles of an FPROP launch (dprob partial count)
+hipError_t launch_dprob_reduce(const float* part, int nparts, int64_t M, float* out, hipStream_t s);
+
+}  // namespace gmlp

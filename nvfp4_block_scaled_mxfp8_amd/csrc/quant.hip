@@ -1,0 +1,476 @@
+// Group quantization kernels: split scan, MXFP8 row/column cast, NVFP4 Hadamard amax and cast.
+//
+// Sources: "GEMM + Swiglu fused Grouped MLP for MXFP8" (sequence diagram: MXFP8
+// row-wise data for the GEMMs, column-wise data for wgrad); "Reduce NVFP4
+// quantization work for the fused GroupedMLP fc2 input with activation
+// recompute" (Changes: nvfp4_group_hadamard_amax returns the per-group pre- and
+// post-RHT amax in one pass; nvfp4_group_quantize_with_amax casts from given
+// amax; the RHT carries the quantizer's sign mask).
+//
+// Tiling: one 256-thread workgroup per (128-token tile of one group, 128-feature
+// tile).  Token tiles never straddle groups, so every 32-token (MXFP8) or
+// 16-token (NVFP4) column block starts at a group-relative multiple of its size.
+// Each thread streams 64 contiguous bf16 of one row (8 x 16-byte loads, a wave
+// covers 32 full 256-byte row segments), casts them row-wise in registers and
+// parks them in LDS; the column pass reads one feature column per lane (a wave
+// reads 128 contiguous bytes per token: conflict-free) and writes 64 contiguous
+// tokens per lane.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace gmlp {
+
+constexpr int QT = 128;          // tokens per tile
+constexpr int QF = 128;          // features per tile
+constexpr int LDW = QF + 8;      // LDS row stride (bf16): +16 bytes keeps the 16-byte writes conflict-free
+
+// ----------------------------------------------------------------------------- split scan
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ m_splits, int G, int64_t M,
+                                                   SplitTables T) {
+  __shared__ long long s_rows[256];
+  __shared__ int s_d[4][256];
+  __shared__ long long carry_raw;
+  __shared__ int carry[5];
+  const int t = threadIdx.x;
+  if (t == 0) {
+    carry_raw = 0;
+    for (int i = 0; i < 5; ++i) carry[i] = 0;
+    T.row_off[0] = T.col_off[0] = T.colw_off[0] = T.t128_off[0] = T.t256_off[0] = 0;
+  }
+  uint32_t flags = 0;
+  __syncthreads();
+  for (int base = 0; base < G; base += 256) {
+    const int g = base + t;
+    long long m = (g < G) ? (long long)m_splits[g] : 0;
+    if (m < 0) { flags |= 1u; m = 0; }
+    // inclusive scan of the raw counts
+    s_rows[t] = m;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      long long v = (t >= o) ? s_rows[t - o] : 0;
+      __syncthreads();
+      s_rows[t] += v;
+      __syncthreads();
+    }
+    const long long incl = carry_raw + s_rows[t];
+    const long long start = min(incl - m, (long long)M);
+    const long long end = min(incl, (long long)M);
+    const int mc = (int)(end - start);
+    if (g < G) T.row_off[g + 1] = (int)end;
+    const int p = (mc + 127) & ~127;
+    int d[4] = {p, (p + 127) / 128, (mc + 127) / 128, (mc + 255) / 256};
+    for (int i = 0; i < 4; ++i) s_d[i][t] = d[i];
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      int v[4];
+      for (int i = 0; i < 4; ++i) v[i] = (t >= o) ? s_d[i][t - o] : 0;
+      __syncthreads();
+      for (int i = 0; i < 4; ++i) s_d[i][t] += v[i];
+      __syncthreads();
+    }
+    if (g < G) {
+      T.col_off[g + 1] = carry[1] + s_d[0][t];
+      T.colw_off[g + 1] = carry[2] + s_d[1][t];
+      T.t128_off[g + 1] = carry[3] + s_d[2][t];
+      T.t256_off[g + 1] = carry[4] + s_d[3][t];
+    }
+    __syncthreads();
+    if (t == 255) {
+      carry_raw = incl;
+      for (int i = 0; i < 4; ++i) carry[i + 1] += s_d[i][255];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    if (carry_raw > M) flags |= 2u;
+    if (carry_raw < M) flags |= 4u;
+  }
+  if (flags) atomicOr(T.flags, flags);
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// ----------------------------------------------------------------------------- tile bookkeeping
+struct TileInfo {
+  int g;          // group
+  int64_t gstart; // first row of the group
+  int m;          // rows of the group
+  int t0;         // first group-relative token of the tile
+  int rows;       // valid rows in the tile
+  int64_t k0;     // first feature of the tile
+  int kcols;      // valid features in the tile (multiple of 32)
+};
+
+__device__ __forceinline__ bool tile_info(const SplitTables& T, int G, int64_t K, TileInfo& ti) {
+  const int tt = blockIdx.x;
+  if (G <= 0 || tt >= T.t128_off[G]) return false;
+  ti.g = find_group(T.t128_off, G, tt);
+  ti.gstart = T.row_off[ti.g];
+  ti.m = T.row_off[ti.g + 1] - (int)ti.gstart;
+  ti.t0 = (tt - T.t128_off[ti.g]) * QT;
+  ti.rows = min(QT, ti.m - ti.t0);
+  ti.k0 = (int64_t)blockIdx.y * QF;
+  ti.kcols = (int)min((int64_t)QF, K - ti.k0);
+  return ti.rows > 0;
+}
+
+// Thread -> (row r = tid/2, 64 features at 64*(tid&1)).  Loads 64 bf16 (zero outside the
+// tile's valid rows/features) and optionally parks them in the LDS tile.
+__device__ __forceinline__ void load_row_chunk(const uint16_t* __restrict__ x, int64_t K, const TileInfo& ti,
+                                               int tid, uint4 (&q)[8], uint16_t* lds) {
+  const int r = tid >> 1;
+  const int c0 = 64 * (tid & 1);
+  const uint4* src = reinterpret_cast<const uint4*>(x + (ti.gstart + ti.t0 + r) * K + ti.k0 + c0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool ok = (r < ti.rows) && (c0 + 8 * j < ti.kcols);
+    q[j] = ok ? src[j] : make_uint4(0, 0, 0, 0);
+  }
+  if (lds) {
+    uint4* dst = reinterpret_cast<uint4*>(lds + r * LDW + c0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[j] = q[j];
+  }
+}
+
+__device__ __forceinline__ void unpack8(const uint4& q, float* v) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+
+// MXFP8 cast of 32 values: returns the scale code, writes 8 words of E4M3 bytes.
+__device__ __forceinline__ uint32_t mx_block(const float* v, uint32_t* w) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t code = e8m0_code(amax);
+  const float inv = e8m0_inv_scale(code);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = cvt_e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
+  return code;
+}
+
+// ----------------------------------------------------------------------------- MXFP8 cast
+template <bool ROW, bool COL>
+__global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                          SplitTables T, int G, MxOut o) {
+  __shared__ __align__(16) uint16_t tile[COL ? QT * LDW : 8];
+  __shared__ uint32_t colcodes[COL ? 2 * QF : 1];
+  TileInfo ti;
+  if (!tile_info(T, G, K, ti)) return;
+  const int tid = threadIdx.x;
+  uint4 q[8];
+  load_row_chunk(x, K, ti, tid, q, COL ? tile : nullptr);
+
+  if (ROW) {
+    const int r = tid >> 1;
+    const int c0 = 64 * (tid & 1);
+    const int64_t grow = ti.gstart + ti.t0 + r;
+    uint32_t codes[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) unpack8(q[4 * b + j], v + 8 * j);
+      uint32_t w[8];
+      const uint32_t code = mx_block(v, w);
+      const bool ok = (r < ti.rows) && (c0 + 32 * b < ti.kcols);
+      if (ok) {
+        uint4* dst = reinterpret_cast<uint4*>(o.row_data + grow * K + ti.k0 + c0 + 32 * b);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        if (o.row_scale) o.row_scale[grow * (K / 32) + (ti.k0 + c0) / 32 + b] = (uint8_t)code;
+      }
+      codes[b] = (c0 + 32 * b < ti.kcols) ? code : 127u;
+    }
+    if (o.row_scale_mfma) {
+      // word = blocks 0..3 of this row's 128 features: lanes 2r' and 2r'+1 of the wave hold 2 each
+      const uint32_t mine = codes[0] | (codes[1] << 8);
+      const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
+      if ((tid & 1) == 0 && r < ti.rows)
+        o.row_scale_mfma[(ti.k0 / 128) * M + grow] = mine | (other << 16);
+    }
+  }
+  if (!COL) return;
+  __syncthreads();
+  const int c = tid & (QF - 1);
+  const int half = tid >> 7;                       // tokens [64*half, 64*half + 64)
+  const int P = (ti.m + 127) & ~127;
+  const int rowsP = min(QT, P - ti.t0);            // tile tokens inside the group's padding
+  const int64_t colbase = K * (int64_t)T.col_off[ti.g];
+  uint32_t codes[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cb = 2 * half + j;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(tile[(32 * cb + i) * LDW + c]);
+    uint32_t w[8];
+    const uint32_t code = mx_block(v, w);
+    const bool inpad = 32 * cb < rowsP;
+    if (inpad && c < ti.kcols) {
+      uint4* dst = reinterpret_cast<uint4*>(o.col_data + colbase + (ti.k0 + c) * P + ti.t0 + 32 * cb);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      if (o.col_scale) o.col_scale[colbase / 32 + (ti.k0 + c) * (P / 32) + ti.t0 / 32 + cb] = (uint8_t)code;
+    }
+    codes[j] = inpad ? code : 127u;
+  }
+  if (o.col_scale_mfma) {
+    colcodes[half * QF + c] = codes[0] | (codes[1] << 8);
+    __syncthreads();
+    if (tid < QF && c < ti.kcols) {
+      const uint32_t word = colcodes[c] | (colcodes[QF + c] << 16);
+      o.col_scale_mfma[K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K + ti.k0 + c] = word;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- signed Hadamard
+// y = H16 (s * x) with H16[i][j] = (-1)^popcount(i & j): the fp32 butterfly over strides
+// 1, 2, 4, 8 (each stage maps (v[i], v[i+h]) -> (v[i] + v[i+h], v[i] - v[i+h])); the caller
+// applies the exact factor 1/4.
+__device__ __forceinline__ void signed_fwht16(float* v, uint32_t mask) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = ((mask >> j) & 1u) ? -v[j] : v[j];
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void hadamard_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                            SplitTables T, int G, uint32_t mask,
+                                                            float* __restrict__ pre, float* __restrict__ post) {
+  __shared__ __align__(16) uint16_t tile[QT * LDW];
+  __shared__ float red[2][4];
+  TileInfo ti;
+  if (!tile_info(T, G, K, ti)) return;
+  const int tid = threadIdx.x;
+  uint4 q[8];
+  load_row_chunk(x, K, ti, tid, q, tile);
+  float amax_pre = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v[8];
+    unpack8(q[j], v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax_pre = fmaxf(amax_pre, fabsf(v[i]));
+  }
+  __syncthreads();
+  const int c = tid & (QF - 1);
+  const int half = tid >> 7;
+  float amax_post = 0.0f;
+  if (c < ti.kcols) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tb = 4 * half + j;        // 16-token block; blocks past the rows read zeros
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = bf16_to_f32(tile[(16 * tb + i) * LDW + c]);
+      signed_fwht16(v, mask);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax_post = fmaxf(amax_post, fabsf(v[i]));
+    }
+  }
+  // max |bf16(y/4)| = bf16(max |y| / 4): the factor is exact and rounding is monotone
+  amax_post = round_bf16(amax_post * 0.25f);
+  amax_pre = wave_max(amax_pre);
+  amax_post = wave_max(amax_post);
+  const int wave = tid >> 6;
+  if ((tid & 63) == 0) { red[0][wave] = amax_pre; red[1][wave] = amax_post; }
+  __syncthreads();
+  if (tid == 0) {
+    float a = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    float b = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    // non-negative floats order like their bit patterns
+    atomicMax(reinterpret_cast<unsigned int*>(pre + ti.g), __float_as_uint(a));
+    atomicMax(reinterpret_cast<unsigned int*>(post + ti.g), __float_as_uint(b));
+  }
+}
+
+// ----------------------------------------------------------------------------- NVFP4 cast
+// One 16-value block with global scale S: writes 8 packed bytes (two words), returns the E4M3 code.
+//   s = fp32(fp32(b / 6) * S); q = E4M3(s); r = fp32(S / dec(q)) (0 if q == 0); c_i = E2M1(fp32(v_i * r))
+__device__ __forceinline__ uint32_t nv_block(const float* v, float S, uint32_t& lo, uint32_t& hi) {
+  float b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) b = fmaxf(b, fabsf(v[i]));
+  const float s = __fmul_rn(__fdiv_rn(b, 6.0f), S);
+  const uint32_t code = cvt_e4m3(s);
+  const float r = (code == 0) ? 0.0f : __fdiv_rn(S, e4m3_decode_pos(code));
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = __fmul_rn(v[i], r);
+  lo = cvt_e2m1x8(t);
+  hi = cvt_e2m1x8(t + 8);
+  return code;
+}
+
+template <bool ROW, bool COL>
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                          SplitTables T, int G, uint32_t mask, int rht,
+                                                          const float* __restrict__ pre,
+                                                          const float* __restrict__ post, NvOut o) {
+  __shared__ __align__(16) uint16_t tile[COL ? QT * LDW : 8];
+  TileInfo ti;
+  if (!tile_info(T, G, K, ti)) return;
+  const int tid = threadIdx.x;
+  uint4 q[8];
+  load_row_chunk(x, K, ti, tid, q, COL ? tile : nullptr);
+  if (ROW) {
+    const float S = nvfp4_global_scale(pre[ti.g]);
+    const int r = tid >> 1;
+    const int c0 = 64 * (tid & 1);
+    const int64_t grow = ti.gstart + ti.t0 + r;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float v[16];
+      unpack8(q[2 * b], v);
+      unpack8(q[2 * b + 1], v + 8);
+      uint32_t lo, hi;
+      const uint32_t code = nv_block(v, S, lo, hi);
+      if (r < ti.rows && c0 + 16 * b < ti.kcols) {
+        const int64_t e = grow * K + ti.k0 + c0 + 16 * b;       // element index
+        *reinterpret_cast<uint2*>(o.row_data + e / 2) = make_uint2(lo, hi);
+        o.row_scale[e / 16] = (uint8_t)code;
+      }
+    }
+  }
+  if (!COL) return;
+  __syncthreads();
+  const float S = nvfp4_global_scale(rht ? post[ti.g] : pre[ti.g]);
+  const int c = tid & (QF - 1);
+  const int half = tid >> 7;
+  const int P = (ti.m + 127) & ~127;
+  const int64_t colbase = K * (int64_t)T.col_off[ti.g];
+  if (c >= ti.kcols) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tb = 4 * half + j;
+    if (ti.t0 + 16 * tb >= P) break;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = bf16_to_f32(tile[(16 * tb + i) * LDW + c]);
+    if (rht) {
+      signed_fwht16(v, mask);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = round_bf16(v[i] * 0.25f);
+    }
+    uint32_t lo, hi;
+    const uint32_t code = nv_block(v, S, lo, hi);
+    const int64_t e = colbase + (ti.k0 + c) * P + ti.t0 + 16 * tb;
+    *reinterpret_cast<uint2*>(o.col_data + e / 2) = make_uint2(lo, hi);
+    o.col_scale[e / 16] = (uint8_t)code;
+  }
+}
+
+// ----------------------------------------------------------------------------- weights
+// Per-expert amax of W [E, N, K] (stacked, or discrete via w_ptrs): grid (chunks, E).
+__global__ __launch_bounds__(256) void weight_amax_kernel(const uint16_t* __restrict__ w, const void* const* w_ptrs,
+                                                          int64_t NK, float* amax) {
+  const int e = blockIdx.y;
+  const uint16_t* base = w_ptrs ? static_cast<const uint16_t*>(w_ptrs[e]) : w + (int64_t)e * NK;
+  float m = 0.0f;
+  const int64_t nvec = NK / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * blockDim.x) {
+    float v[8];
+    unpack8(reinterpret_cast<const uint4*>(base)[i], v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(amax + e), __float_as_uint(m));
+}
+
+__global__ __launch_bounds__(256) void gather_weights_kernel(const void* const* w_ptrs, int64_t NK, uint16_t* out) {
+  const int e = blockIdx.y;
+  const uint4* src = static_cast<const uint4*>(w_ptrs[e]);
+  uint4* dst = reinterpret_cast<uint4*>(out + (int64_t)e * NK);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < NK / 8; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+// ----------------------------------------------------------------------------- launchers
+static dim3 tile_grid(int64_t M, int64_t K, int G) {
+  return dim3((unsigned)((M + QT - 1) / QT + G), (unsigned)((K + QF - 1) / QF));
+}
+
+hipError_t launch_scan(const int32_t* m_splits, int G, int64_t M, SplitTables T, hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, m_splits, G, M, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G, bool row, bool col,
+                              MxOut o, hipStream_t s) {
+  if (M == 0 || (!row && !col)) return hipSuccess;
+  const dim3 grid = tile_grid(M, K, G);
+  if (row && col) hipLaunchKernelGGL((mxfp8_quant_kernel<true, true>), grid, dim3(256), 0, s, x, M, K, T, G, o);
+  else if (row) hipLaunchKernelGGL((mxfp8_quant_kernel<true, false>), grid, dim3(256), 0, s, x, M, K, T, G, o);
+  else hipLaunchKernelGGL((mxfp8_quant_kernel<false, true>), grid, dim3(256), 0, s, x, M, K, T, G, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G, uint32_t mask,
+                                float* pre, float* post, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(hadamard_amax_kernel, tile_grid(M, K, G), dim3(256), 0, s, x, M, K, T, G, mask, pre, post);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G, uint32_t mask,
+                              bool rht, bool row, bool col, const float* pre, const float* post, NvOut o,
+                              hipStream_t s) {
+  if (M == 0 || (!row && !col)) return hipSuccess;
+  const dim3 grid = tile_grid(M, K, G);
+  const int r = rht ? 1 : 0;
+  if (row && col)
+    hipLaunchKernelGGL((nvfp4_quant_kernel<true, true>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o);
+  else if (row)
+    hipLaunchKernelGGL((nvfp4_quant_kernel<true, false>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o);
+  else
+    hipLaunchKernelGGL((nvfp4_quant_kernel<false, true>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_amax(const uint16_t* w, const void* const* w_ptrs, int E, int64_t N, int64_t K,
+                              float* amax, hipStream_t s) {
+  if (E == 0) return hipSuccess;
+  hipError_t err = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 0u, E, s);
+  if (err != hipSuccess) return err;
+  const int64_t nvec = N * K / 8;
+  const unsigned chunks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((nvec + 255) / 256, 256));
+  hipLaunchKernelGGL(weight_amax_kernel, dim3(chunks, E), dim3(256), 0, s, w, w_ptrs, N * K, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_weights(const void* const* w_ptrs, int E, int64_t N, int64_t K, uint16_t* out,
+                                 hipStream_t s) {
+  if (E == 0) return hipSuccess;
+  const int64_t nvec = N * K / 8;
+  const unsigned chunks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((nvec + 255) / 256, 1024));
+  hipLaunchKernelGGL(gather_weights_kernel, dim3(chunks, E), dim3(256), 0, s, w_ptrs, N * K, out);
+  return hipGetLastError();
+}
+
+}  // namespace gmlp

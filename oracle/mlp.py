@@ -40,8 +40,10 @@ Readings (the pages are silent on these):
 import numpy as np
 
 from .formats import bf16_bits_to_f64, f64_to_bf16_bits, round_bf16
+from .formats import pack_fp4
 from .quant import (mxfp8_dequant_rows, mxfp8_group_quantize, mxfp8_quantize_rows,
-                    nvfp4_dequant_packed, nvfp4_group_quantize_with_amax, padded)
+                    nvfp4_dequant_packed, nvfp4_dequant_rows, nvfp4_group_quantize_with_amax,
+                    nvfp4_quantize_rows, padded)
 from .rht import group_hadamard_amax
 
 SWIGLU = "swiglu"
@@ -137,25 +139,32 @@ def quantize_activation(x_bits, m_splits, recipe, row=True, col=True, amax=None)
 def quantize_weight(w_bits, recipe):
     """Quantize stacked weights [E, N, K] for fprop (blocks along K) and dgrad (blocks along N).
 
-    Returns (quantized dict, dequantized dict) with ``row`` = [E, N, K] and ``colT`` =
-    [E, K, N] (the dgrad operand stored with its contraction dim N last).
+    The dgrad operand is each expert's W_e^T [K, N] cast row-wise, i.e. with blocks along N.
+    Returns (quantized dict, dequantized dict) with ``row`` = [E, N, K] and ``colT`` = [E, K, N].
     """
     e, n, k = w_bits.shape
-    flat = w_bits.reshape(e * n, k)
-    splits = [n] * e
+    w = bf16_bits_to_f64(w_bits.reshape(e * n, k)).reshape(e, n, k)
+    q = {"row": [], "colT": []}
+    row, colT = [], []
     if recipe.kind == MXFP8:
-        q = mxfp8_group_quantize(flat, splits, row=True, col=True)
-        row = mxfp8_dequant_rows(q["row_data"], q["row_scale"]).reshape(e, n, k)
-        colT = np.stack([mxfp8_dequant_rows(d, s) for d, s in q["col_groups"]]) if e else np.zeros((0, k, n))
-        return q, {"row": row, "colT": colT}
-    w = bf16_bits_to_f64(flat).reshape(e, n, k)
-    amax = np.array([np.max(np.abs(w[i])) if w[i].size else 0.0 for i in range(e)], dtype=np.float32)
-    q = nvfp4_group_quantize_with_amax(flat, splits, amax, amax, 0, row=True, col=True, rht=False)
-    q["amax"] = amax
-    row = np.stack([nvfp4_dequant_packed(q["row_data"][i * n:(i + 1) * n], q["row_scale"][i * n:(i + 1) * n],
-                                         amax[i]) for i in range(e)])
-    colT = np.stack([nvfp4_dequant_packed(d, s, amax[i]) for i, (d, s) in enumerate(q["col_groups"])])
-    return q, {"row": row, "colT": colT}
+        for i in range(e):
+            qr, sr = mxfp8_quantize_rows(w[i])
+            qc, sc = mxfp8_quantize_rows(np.ascontiguousarray(w[i].T))
+            q["row"].append((qr, sr))
+            q["colT"].append((qc, sc))
+            row.append(mxfp8_dequant_rows(qr, sr))
+            colT.append(mxfp8_dequant_rows(qc, sc))
+    else:
+        q["amax"] = np.array([np.max(np.abs(w[i])) if w[i].size else 0.0 for i in range(e)], dtype=np.float32)
+        for i in range(e):
+            cr, sr = nvfp4_quantize_rows(w[i], q["amax"][i])
+            cc, sc = nvfp4_quantize_rows(np.ascontiguousarray(w[i].T), q["amax"][i])
+            q["row"].append((pack_fp4(cr), sr))
+            q["colT"].append((pack_fp4(cc), sc))
+            row.append(nvfp4_dequant_rows(cr, sr, q["amax"][i]))
+            colT.append(nvfp4_dequant_rows(cc, sc, q["amax"][i]))
+    stack = lambda a, shape: np.stack(a) if a else np.zeros(shape)
+    return q, {"row": stack(row, (0, n, k)), "colT": stack(colT, (0, k, n))}
 
 
 # ----------------------------------------------------------------------------- forward

@@ -30,15 +30,15 @@ Layouts (ours; the pages fix none):
   [R, K/32].  NVFP4 data u8 [R, K/2] (element 2i in the low nibble), E4M3
   scales [R, K/16].
 * column-wise, per group g with m_g rows: the group's [m_g, K] slab transposed
-  to [K, P_g] with P_g = m_g rounded up to 32 (zero padded; 32 for both
-  recipes so one padded offset table serves both), blocks along tokens.
+  to [K, P_g] with P_g = m_g rounded up to 128 (zero padded; a multiple of both
+  block sizes and of the 128-token contraction stage of the wgrad GEMM, so one
+  padded offset table serves both recipes), blocks along tokens.
   Group g's data starts at K * sum_{h<g} P_h elements (bytes for MXFP8, nibbles
   for NVFP4) and its scales at K * sum_{h<g} P_h / B (B = 32 or 16).
 * MFMA-ready MXFP8 scales: a scale matrix [R, nkb] becomes u32 [ceil(nkb/4), R]
   where word (t, r) holds the codes of blocks 4t..4t+3 of row r in bytes 0..3
   (missing blocks = 127).  For column-wise scales each group's [K, P_g/32]
-  matrix is converted on its own and placed at word offset
-  K * sum_{h<g} ceil(P_h / 128).
+  matrix is converted on its own and placed at word offset K * sum_{h<g} P_h / 128.
 """
 import numpy as np
 
@@ -48,7 +48,7 @@ from .rht import RHT_BLOCK, rht16
 
 MX_BLOCK = 32
 NV_BLOCK = 16
-COL_PAD = 32
+COL_PAD = 128
 
 
 def padded(m, to=COL_PAD):

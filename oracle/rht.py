@@ -70,7 +70,7 @@ def col_blocks(x_group, padded_rows):
     return t.reshape(k, padded_rows // RHT_BLOCK, RHT_BLOCK)
 
 
-def group_hadamard_amax(x_bits, m_splits, mask, pad_to=32):
+def group_hadamard_amax(x_bits, m_splits, mask, pad_to=128):
     """Per-group (pre-RHT amax, post-RHT amax), as fp32 values.
 
     pre_g  = max |x| over the rows of group g;

@@ -1,0 +1,71 @@
+"""The C ABI library: it loads, exports every symbol include/gmlp.h declares, and validates
+arguments before touching a device (CPU only: no compute call reaches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_mxfp8_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "gmlp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gmlp_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = g.lib()
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    # and the binding declares a signature for each of them
+    assert set(names) == set(g._SIGS), set(names) ^ set(g._SIGS)
+
+
+def test_support_query_reasons():
+    ok, why, st = g.check_support(8, 4096, 1536, "swiglu", g.recipe("mxfp8"), arch="gfx950")
+    assert ok and st == 0
+    ok, why, st = g.check_support(8, 4096, 1536, "swiglu", g.recipe("mxfp8"), arch="gfx942")
+    assert not ok and why.startswith("system:") and st == 2
+    ok, why, st = g.check_support(8, 4096, 1500, "swiglu", g.recipe("mxfp8"), arch="gfx950")
+    assert not ok and why.startswith("dims:")
+    ok, why, st = g.check_support(8, 4096, 1536, "swiglu", g.Recipe(7, 0), arch="gfx950")
+    assert not ok and why.startswith("recipe:")
+    ok, why, st = g.check_support(8, 4096, 1536, 5, g.recipe("mxfp8"), arch="gfx950")
+    assert not ok and why.startswith("activation:")
+    ok, why, st = g.check_support(0, 4096, 1536, "swiglu", g.recipe("nvfp4", 0x1234), arch="gfx950")
+    assert not ok and st == 1
+
+
+def test_query_sizes_grow_with_recompute_off():
+    on = g.query_sizes(32768, 8, 4096, 1536, "swiglu", g.recipe("mxfp8"), recompute=True)
+    off = g.query_sizes(32768, 8, 4096, 1536, "swiglu", g.recipe("mxfp8"), recompute=False)
+    # without recompute the forward also keeps the column-wise fc2 input
+    assert off["ctx_bytes"] - on["ctx_bytes"] >= 1536 * 32768
+    assert on["ws_bytes"] > 0 and on["quant_ws_bytes"] > 0
+
+
+def test_validation_happens_before_any_launch():
+    """Bad arguments return an error status and a reason with null device pointers."""
+    L = g.lib()
+    q = g.GroupedQ()
+    st = L.gmlp_group_quantize(None, 64, 100, None, 1, g.recipe("mxfp8"), 1, 1, ctypes.byref(q), None, 0, None)
+    assert st == 2 and "multiple of 32" in g.last_error()
+    st = L.gmlp_group_quantize(None, 64, 128, None, 1, g.recipe("mxfp8"), 1, 1, ctypes.byref(q), None, 0, None)
+    assert st == 1 and "null" in g.last_error()
+    st = L.gmlp_group_quantize_with_amax(None, 64, 128, None, 1, g.recipe("mxfp8"), 1, 1, ctypes.byref(q), None, 0,
+                                         None)
+    assert st == 2 and g.last_error().startswith("recipe:")
+    st = L.gmlp_grouped_gemm(0, g.recipe("mxfp8"), ctypes.byref(q), ctypes.byref(q), ctypes.c_void_p(16), 1, 64,
+                             128, 96, ctypes.c_void_p(16), 0, None, 0, None)
+    assert st == 2 and "multiple of 128" in g.last_error()
+    args = g.FwdArgs()
+    args.E, args.M, args.H, args.ffn = 2, 64, 128, 100
+    args.recipe = g.recipe("mxfp8")
+    assert L.gmlp_grouped_mlp_forward(ctypes.byref(args), None) == 2
+    assert "ffn" in g.last_error()

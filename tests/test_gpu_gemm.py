@@ -1,0 +1,100 @@
+"""GPU parity of the grouped GEMMs on identical quantized operands: relative Frobenius error
+<= 1e-3 against the oracle's fp64 product rounded to the output dtype, and bitwise equality
+where the inputs make every product and sum exact."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_mxfp8_amd as g
+from gpu_util import bits16, dev_bf16, dev_splits
+from oracle import formats as F
+from oracle import mlp as O
+from workloads import random_bf16
+
+pytestmark = pytest.mark.gpu
+
+FPROP_CASES = [([0, 37, 300, 129], 256, 384), ([512], 128, 256), ([1, 0, 700], 384, 128), ([257, 3], 640, 512)]
+WGRAD_CASES = [([0, 37, 300, 129], 256, 384), ([5, 0, 600], 128, 256), ([128, 256], 384, 128)]
+
+
+def _fprop_ref(x, w, splits, kind, mask):
+    rec = O.Recipe(kind, mask)
+    _, xd = O.quantize_activation(x, splits, rec, row=True, col=False)
+    _, wd = O.quantize_weight(w, rec)
+    out, off = [], 0
+    for e, m in enumerate(splits):
+        out.append(xd["row"][off:off + m] @ wd["row"][e].T)
+        off += m
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("splits,N,K", FPROP_CASES)
+def test_gemm_fprop(kind, splits, N, K):
+    M, E, mask = sum(splits), len(splits), 0x3C5A
+    print(f"gemm fprop {kind} splits={splits} N={N} K={K}", flush=True)
+    x = random_bf16((M, K), seed=M + N)
+    w = random_bf16((E, N, K), seed=K + N, std=1 / np.sqrt(K))
+    rec = g.recipe(kind, mask)
+    sd = dev_splits(splits)
+    aq = g.group_quantize(dev_bf16(x), sd, rec, True, False)
+    wq = g.weight_quantize(dev_bf16(w.reshape(E * N, K)).view(E, N, K), rec)
+    c = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wq, sd, M, N, K)
+    c32 = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wq, sd, M, N, K, out_dtype=g.OUT_FP32)
+    torch.cuda.synchronize()
+    ref = _fprop_ref(x, w, splits, kind, mask)
+    got = F.bf16_bits_to_f64(bits16(c)).reshape(M, N)
+    assert O.rel_fro(got, F.round_bf16(ref)) <= 1e-3
+    assert O.rel_fro(c32.cpu().double().numpy(), ref) <= 1e-5
+
+
+def _wgrad_ref(a, b, splits, kind, mask):
+    rec = O.Recipe(kind, mask)
+    _, ad = O.quantize_activation(a, splits, rec, row=False, col=True)
+    _, bd = O.quantize_activation(b, splits, rec, row=False, col=True)
+    return np.stack([ad["col"][e] @ bd["col"][e].T for e in range(len(splits))])
+
+
+@pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("splits,Na,Nb", WGRAD_CASES)
+def test_gemm_wgrad(kind, splits, Na, Nb):
+    M, E, mask = sum(splits), len(splits), 0x91E7
+    print(f"gemm wgrad {kind} splits={splits} Na={Na} Nb={Nb}", flush=True)
+    a = random_bf16((M, Na), seed=M + Na)
+    b = random_bf16((M, Nb), seed=M + Nb + 1, dist="srelu")
+    rec = g.recipe(kind, mask)
+    sd = dev_splits(splits)
+    aq = g.group_quantize(dev_bf16(a), sd, rec, False, True)
+    bq = g.group_quantize(dev_bf16(b), sd, rec, False, True)
+    c = g.grouped_gemm(g.GEMM_WGRAD, rec, aq, bq, sd, M, Na, Nb)
+    torch.cuda.synchronize()
+    ref = _wgrad_ref(a, b, splits, kind, mask)
+    got = F.bf16_bits_to_f64(bits16(c)).reshape(E, Na, Nb)
+    assert O.rel_fro(got, F.round_bf16(ref)) <= 1e-3
+    for e, m in enumerate(splits):
+        if m == 0:
+            assert np.all(got[e] == 0), "an empty expert must get a zero weight gradient"
+
+
+def test_gemm_exact_inputs_bitwise():
+    """Small-integer data quantizes exactly to MXFP8 and every fp32 partial sum is exact, so the
+    MFMA result equals the fp64 product and the bf16 outputs must match bit for bit."""
+    rng = np.random.default_rng(5)
+    splits, N, K = [96, 0, 300], 256, 512
+    M, E = sum(splits), len(splits)
+    from workloads import to_bf16_bits
+    x = to_bf16_bits(rng.integers(-4, 5, size=(M, K)).astype(np.float32))
+    w = to_bf16_bits(rng.integers(-4, 5, size=(E, N, K)).astype(np.float32))
+    rec = g.recipe("mxfp8")
+    sd = dev_splits(splits)
+    aq = g.group_quantize(dev_bf16(x), sd, rec, True, True)
+    wq = g.weight_quantize(dev_bf16(w.reshape(E * N, K)).view(E, N, K), rec)
+    c = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wq, sd, M, N, K)
+    torch.cuda.synchronize()
+    ref = _fprop_ref(x, w, splits, "mxfp8", 0)
+    assert np.array_equal(bits16(c).reshape(M, N), F.f64_to_bf16_bits(ref))
+    # wgrad on the same data: exact too
+    c = g.grouped_gemm(g.GEMM_WGRAD, rec, aq, aq, sd, M, K, K)
+    torch.cuda.synchronize()
+    ref = _wgrad_ref(x, x, splits, "mxfp8", 0)
+    assert np.array_equal(bits16(c).reshape(E, K, K), F.f64_to_bf16_bits(ref))

@@ -1,0 +1,116 @@
+"""GPU parity of the fused grouped MLP forward + backward with the oracle (relative Frobenius
+<= 2e-2), recompute on/off bitwise equality, determinism and the launch plan."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_mxfp8_amd as g
+from gpu_util import bits16, dev_bf16, dev_f32, dev_splits
+from oracle import formats as F
+from oracle import mlp as O
+from workloads import make_workload, small_case
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _upload(wl):
+    E, H, ffn = wl.config.experts, wl.config.hidden, wl.config.ffn
+    F1 = wl.config.f1
+    d = {"x": dev_bf16(wl.x), "splits": dev_splits(wl.m_splits), "probs": dev_f32(wl.probs),
+         "w1": dev_bf16(wl.w1.reshape(E * F1, H)).view(E, F1, H),
+         "w2": dev_bf16(wl.w2.reshape(E * H, ffn)).view(E, H, ffn)}
+    if wl.dy is not None:
+        d["dy"] = dev_bf16(wl.dy)
+    return d
+
+
+def _run(wl, d, kind, recompute, backward=True, wgrad_dtype=g.OUT_BF16):
+    rec = g.recipe(kind, wl.sign_mask)
+    w1q = g.weight_quantize(d["w1"], rec)
+    w2q = g.weight_quantize(d["w2"], rec)
+    y, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], wl.config.activation, rec,
+                                   recompute=recompute)
+    out = {"y": y, "fwd_counts": g.last_launch_counts()}
+    if backward:
+        out.update(g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx, wgrad_dtype=wgrad_dtype))
+        out["bwd_counts"] = g.last_launch_counts()
+    torch.cuda.synchronize()
+    return out
+
+
+def _f64(t):
+    return F.bf16_bits_to_f64(bits16(t)) if t.dtype == torch.bfloat16 else t.detach().cpu().double().numpy()
+
+
+def _compare(out, wl, kind, backward=True):
+    rec = O.Recipe(kind, wl.sign_mask)
+    fwd = O.forward(wl.x, wl.m_splits, wl.w1, wl.w2, wl.probs, wl.config.activation, rec)
+    errs = {"y": O.rel_fro(_f64(out["y"]).reshape(fwd["y_f64"].shape), F.round_bf16(fwd["y_f64"]))}
+    if backward:
+        bwd = O.backward(fwd, wl.dy)
+        errs["dx"] = O.rel_fro(_f64(out["dx"]).reshape(bwd["dx_f64"].shape), F.round_bf16(bwd["dx_f64"]))
+        errs["dprobs"] = O.rel_fro(out["dprobs"].cpu().double().numpy(), bwd["dprob"])
+        errs["dw1"] = O.rel_fro(_f64(out["dw1"]).reshape(bwd["dw1_f64"].shape), F.round_bf16(bwd["dw1_f64"]))
+        errs["dw2"] = O.rel_fro(_f64(out["dw2"]).reshape(bwd["dw2_f64"].shape), F.round_bf16(bwd["dw2_f64"]))
+        for e, m in enumerate(wl.m_splits):
+            if m == 0:
+                assert not _f64(out["dw1"])[e].any() and not _f64(out["dw2"])[e].any()
+    print(kind, wl.config.activation, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+    return errs
+
+
+CASES = [("mxfp8", "swiglu"), ("nvfp4", "srelu"), ("mxfp8", "srelu"), ("nvfp4", "swiglu")]
+
+
+@pytest.mark.parametrize("kind,act", CASES)
+def test_mlp_forward_backward_matches_oracle(kind, act):
+    print(f"mlp {kind} {act}", flush=True)
+    wl = small_case([0, 37, 300, 129, 5], 512, 384, activation=act, recipe=kind, seed=1, w_std=0.05)
+    out = _run(wl, _upload(wl), kind, recompute=False)
+    _compare(out, wl, kind)
+
+
+@pytest.mark.parametrize("kind,act", CASES)
+def test_recompute_on_off_bitwise(kind, act):
+    """Rebuilding the fc2 input in backward gives bitwise-equal output and gradients."""
+    print(f"recompute {kind} {act}", flush=True)
+    wl = small_case([64, 0, 200, 300], 256, 256, activation=act, recipe=kind, seed=2, w_std=0.05)
+    d = _upload(wl)
+    a = _run(wl, d, kind, recompute=False)
+    b = _run(wl, d, kind, recompute=True)
+    for k in ("y", "dx", "dprobs", "dw1", "dw2"):
+        assert torch.equal(a[k].view(torch.int16) if a[k].dtype == torch.bfloat16 else a[k].view(torch.int32),
+                           b[k].view(torch.int16) if b[k].dtype == torch.bfloat16 else b[k].view(torch.int32)), k
+    if kind == "nvfp4":
+        # the recompute backward casts the rebuilt input with the forward's amax: no third amax pass
+        assert b["bwd_counts"]["hadamard_amax"] == 2 and a["bwd_counts"]["hadamard_amax"] == 2
+        assert b["bwd_counts"]["nvfp4_quantize"] == 3 and a["bwd_counts"]["nvfp4_quantize"] == 2
+        assert b["fwd_counts"]["hadamard_amax"] == 2
+
+
+def test_deterministic_and_fp32_wgrad():
+    wl = small_case([100, 1, 300], 256, 256, activation="swiglu", recipe="mxfp8", seed=3, w_std=0.05)
+    d = _upload(wl)
+    a = _run(wl, d, "mxfp8", recompute=False)
+    b = _run(wl, d, "mxfp8", recompute=False)
+    for k in ("y", "dx", "dprobs", "dw1", "dw2"):
+        assert torch.equal(a[k], b[k]), k
+    c = _run(wl, d, "mxfp8", recompute=False, wgrad_dtype=g.OUT_FP32)
+    assert c["dw1"].dtype == torch.float32
+    assert O.rel_fro(c["dw1"].double().cpu().numpy(), _f64(a["dw1"])) <= 1e-2
+
+
+def test_tiny_config_forward():
+    """2 experts, hidden 128, ffn 128, m_splits [64, 128], MXFP8 SwiGLU, forward only."""
+    wl = make_workload("tiny")
+    out = _run(wl, _upload(wl), "mxfp8", recompute=False, backward=False)
+    _compare(out, wl, "mxfp8", backward=False)
+
+
+def test_all_tokens_in_one_expert_and_empty_experts():
+    wl = small_case([0, 0, 513, 0], 256, 256, activation="srelu", recipe="nvfp4", seed=4, w_std=0.05)
+    out = _run(wl, _upload(wl), "nvfp4", recompute=True)
+    _compare(out, wl, "nvfp4")

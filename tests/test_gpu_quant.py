@@ -1,0 +1,168 @@
+"""GPU parity of the group-quantize kernels with the CPU oracle: bit-exact on identical bf16 inputs."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_mxfp8_amd as g
+from gpu_util import assert_bytes_equal, bits16, col_total, dev_bf16, dev_f32, dev_splits, f32bits, u32, u8
+from oracle import quant as Q
+from oracle import rht as R
+from workloads import all_bf16_finite, random_bf16
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ([64, 128], 128, "normal"),
+    ([0, 1, 31, 33, 0, 300], 256, "normal"),
+    ([517], 96, "wide"),
+    ([200, 0, 57], 160, "srelu"),
+    ([129, 255, 3], 384, "wide"),
+]
+
+
+def _check_mx(q, ref, splits, M, K, row=True, col=True):
+    if row:
+        assert_bytes_equal(u8(q.bufs["row_data"])[:M * K], ref["row_data"], "row data")
+        assert_bytes_equal(u8(q.bufs["row_scale"])[:M * K // 32], ref["row_scale"], "row scales")
+        assert_bytes_equal(u32(q.bufs["row_scale_mfma"])[:((K + 127) // 128) * M], ref["row_scale_mfma"], "row mfma scales")
+    if col:
+        P = col_total(splits)
+        assert_bytes_equal(u8(q.bufs["col_data"])[:K * P], ref["col_data"], "col data")
+        assert_bytes_equal(u8(q.bufs["col_scale"])[:K * P // 32], ref["col_scale"], "col scales")
+        assert_bytes_equal(u32(q.bufs["col_scale_mfma"])[:K * P // 128], ref["col_scale_mfma"], "col mfma scales")
+
+
+@pytest.mark.parametrize("splits,K,dist", CASES)
+def test_mxfp8_group_quantize(splits, K, dist):
+    M = sum(splits)
+    print(f"mxfp8 group_quantize splits={splits} K={K} dist={dist}", flush=True)
+    x = random_bf16((M, K), seed=M + K, dist=dist)
+    q = g.group_quantize(dev_bf16(x), dev_splits(splits), g.recipe("mxfp8"), True, True)
+    torch.cuda.synchronize()
+    _check_mx(q, Q.mxfp8_group_quantize(x, splits), splits, M, K)
+
+
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
+def test_mxfp8_every_bf16_pattern(order):
+    """All 65280 finite bf16 patterns, in blocks of similar magnitude (many scales) and shuffled."""
+    v = all_bf16_finite()
+    if order == "sorted":
+        mag = v & 0x7FFF
+        v = v[np.argsort(mag, kind="stable")]
+    else:
+        v = np.random.default_rng(0).permutation(v)
+    K = 256
+    M = -(-v.size // K)
+    x = np.zeros(M * K, np.uint16)
+    x[:v.size] = v
+    x = x.reshape(M, K)
+    splits = [100, M - 100]
+    print(f"mxfp8 exhaustive sweep order={order} M={M}", flush=True)
+    q = g.group_quantize(dev_bf16(x), dev_splits(splits), g.recipe("mxfp8"), True, True)
+    torch.cuda.synchronize()
+    _check_mx(q, Q.mxfp8_group_quantize(x, splits), splits, M, K)
+
+
+def test_mxfp8_row_only_and_col_only():
+    splits, K = [70, 0, 190], 256
+    M = sum(splits)
+    x = random_bf16((M, K), seed=11)
+    ref = Q.mxfp8_group_quantize(x, splits)
+    q = g.group_quantize(dev_bf16(x), dev_splits(splits), g.recipe("mxfp8"), True, False)
+    torch.cuda.synchronize()
+    _check_mx(q, ref, splits, M, K, row=True, col=False)
+    q = g.group_quantize(dev_bf16(x), dev_splits(splits), g.recipe("mxfp8"), False, True)
+    torch.cuda.synchronize()
+    _check_mx(q, ref, splits, M, K, row=False, col=True)
+
+
+def test_empty_input_and_clamped_splits():
+    """M = 0 launches nothing harmful; splits that overrun M are clamped on the device and flagged."""
+    q = g.group_quantize(dev_bf16(np.zeros((0, 128), np.uint16)), dev_splits([0, 0]), g.recipe("mxfp8"))
+    torch.cuda.synchronize()
+    splits_dev = dev_splits([100, 100])            # claims 200 rows, x has 150
+    x = random_bf16((150, 128), seed=12)
+    ws = g.quant_workspace(2, "cuda")
+    q = g.group_quantize(dev_bf16(x), splits_dev, g.recipe("mxfp8"), True, True, ws=ws)
+    torch.cuda.synchronize()
+    assert g.read_device_flags(ws) & 2
+    ref = Q.mxfp8_group_quantize(x, [100, 50])
+    _check_mx(q, ref, [100, 50], 150, 128)
+
+
+@pytest.mark.parametrize("splits,K,dist", CASES)
+def test_nvfp4_hadamard_amax(splits, K, dist):
+    M = sum(splits)
+    mask = 0xB5E3
+    print(f"nvfp4 hadamard amax splits={splits} K={K}", flush=True)
+    x = random_bf16((M, K), seed=M * 3 + K, dist=dist)
+    pre, post = g.group_hadamard_amax(dev_bf16(x), dev_splits(splits), mask)
+    torch.cuda.synchronize()
+    rpre, rpost = R.group_hadamard_amax(x, splits, mask)
+    assert_bytes_equal(f32bits(pre), rpre.view(np.uint32), "pre-RHT amax")
+    assert_bytes_equal(f32bits(post), rpost.view(np.uint32), "post-RHT amax")
+
+
+@pytest.mark.parametrize("splits,K,dist", CASES)
+def test_nvfp4_group_quantize(splits, K, dist):
+    """Amax pass + cast (row-wise with the pre-RHT amax, column-wise RHT with the post-RHT amax)."""
+    M = sum(splits)
+    mask = 0x6A0F
+    print(f"nvfp4 group_quantize splits={splits} K={K}", flush=True)
+    x = random_bf16((M, K), seed=M * 5 + K, dist=dist)
+    rec = g.recipe("nvfp4", mask)
+    q = g.group_quantize(dev_bf16(x), dev_splits(splits), rec, True, True)
+    torch.cuda.synchronize()
+    pre, post = R.group_hadamard_amax(x, splits, mask)
+    ref = Q.nvfp4_group_quantize_with_amax(x, splits, pre, post, mask)
+    assert_bytes_equal(f32bits(q.bufs["amax_pre"]), pre.view(np.uint32), "pre amax")
+    assert_bytes_equal(f32bits(q.bufs["amax_post"]), post.view(np.uint32), "post amax")
+    assert_bytes_equal(u8(q.bufs["row_data"])[:M * K // 2], ref["row_data"], "row data")
+    assert_bytes_equal(u8(q.bufs["row_scale"])[:M * K // 16], ref["row_scale"], "row scales")
+    P = col_total(splits)
+    assert_bytes_equal(u8(q.bufs["col_data"])[:K * P // 2], ref["col_data"], "col data")
+    assert_bytes_equal(u8(q.bufs["col_scale"])[:K * P // 16], ref["col_scale"], "col scales")
+
+
+def test_nvfp4_quantize_with_given_amax():
+    """The cast reads the amax it is given (the recompute path re-uses the forward's)."""
+    splits, K, mask = [33, 0, 160], 128, 0x0F0F
+    M = sum(splits)
+    x = random_bf16((M, K), seed=21, dist="srelu")
+    pre = np.array([3.0, 0.0, 1.5], np.float32)        # deliberately not the data's amax
+    post = np.array([2.5, 0.0, 7.0], np.float32)
+    q = g.group_quantize_with_amax(dev_bf16(x), dev_splits(splits), g.recipe("nvfp4", mask), dev_f32(pre),
+                                   dev_f32(post), True, True)
+    torch.cuda.synchronize()
+    ref = Q.nvfp4_group_quantize_with_amax(x, splits, pre, post, mask)
+    assert_bytes_equal(u8(q.bufs["row_data"])[:M * K // 2], ref["row_data"], "row data")
+    assert_bytes_equal(u8(q.bufs["row_scale"])[:M * K // 16], ref["row_scale"], "row scales")
+    P = col_total(splits)
+    assert_bytes_equal(u8(q.bufs["col_data"])[:K * P // 2], ref["col_data"], "col data")
+    assert_bytes_equal(u8(q.bufs["col_scale"])[:K * P // 16], ref["col_scale"], "col scales")
+
+
+@pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
+def test_weight_quantize(kind):
+    """fprop operand (blocks along K) and dgrad operand (W_e^T, blocks along N), stacked and discrete."""
+    from oracle.mlp import Recipe, quantize_weight
+    E, N, K = 3, 256, 384
+    w = random_bf16((E, N, K), seed=31, std=0.05)
+    rec = g.recipe(kind)
+    ref, _ = quantize_weight(w, Recipe(kind))
+    wd = dev_bf16(w.reshape(E * N, K)).view(E, N, K)
+    for q in (g.weight_quantize(wd, rec), g.weight_quantize([wd[e] for e in range(E)], rec)):
+        torch.cuda.synchronize()
+        if kind == "mxfp8":
+            assert_bytes_equal(u8(q.bufs["row_data"]), np.stack([r[0] for r in ref["row"]]), "w row data")
+            want = np.concatenate([Q.mfma_scale_layout(r[1]).reshape(-1) for r in ref["row"]])
+            assert_bytes_equal(u32(q.bufs["row_scale_mfma"]), want, "w row mfma scales")
+            assert_bytes_equal(u8(q.bufs["col_data"]), np.stack([r[0] for r in ref["colT"]]), "w col data")
+            want = np.concatenate([Q.mfma_scale_layout(r[1]).reshape(-1) for r in ref["colT"]])
+            assert_bytes_equal(u32(q.bufs["col_scale_mfma"]), want, "w col mfma scales")
+        else:
+            assert_bytes_equal(f32bits(q.bufs["amax_pre"]), ref["amax"].view(np.uint32), "w amax")
+            assert_bytes_equal(u8(q.bufs["row_data"]), np.stack([r[0] for r in ref["row"]]), "w row data")
+            assert_bytes_equal(u8(q.bufs["row_scale"]), np.stack([r[1] for r in ref["row"]]), "w row scales")
+            assert_bytes_equal(u8(q.bufs["col_data"]), np.stack([r[0] for r in ref["colT"]]), "w col data")
+            assert_bytes_equal(u8(q.bufs["col_scale"]), np.stack([r[1] for r in ref["colT"]]), "w col scales")

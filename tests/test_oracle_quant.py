@@ -87,13 +87,13 @@ def test_mxfp8_nearest_and_error_bound():
 
 
 def test_mxfp8_group_col_layout():
-    """Column-wise data = per-group transpose, zero padded to 32, quantized along tokens."""
+    """Column-wise data = per-group transpose, zero padded to 128, quantized along tokens."""
     splits = [0, 1, 31, 33, 0, 64]
     k = 64
     x = random_bf16((sum(splits), k), seed=4)
     out = Q.mxfp8_group_quantize(x, splits)
     offs = Q.col_offsets(splits)
-    assert offs.tolist() == [0, 0, 32, 64, 128, 128, 192]
+    assert offs.tolist() == [0, 0, 128, 256, 384, 384, 512]
     v = F.bf16_bits_to_f64(x)
     row_off = np.concatenate([[0], np.cumsum(splits)])
     for g, m in enumerate(splits):
@@ -201,13 +201,13 @@ def test_nvfp4_group_quantize_layout_and_rht_choice():
     # row-wise: group 2's rows with pre amax, no transform
     c, qq = Q.nvfp4_quantize_rows(v[5:45], 2.0)
     assert np.array_equal(out["row_nibbles"][5:45], c) and np.array_equal(out["row_scale"][5:45], qq)
-    # column-wise: group 0 padded to 32 tokens, transformed, post amax
-    t = np.zeros((k, 32))
+    # column-wise: group 0 padded to 128 tokens, transformed, post amax
+    t = np.zeros((k, 128))
     t[:, :5] = v[:5].T
     from oracle.rht import rht16
-    y = rht16(t.reshape(k, 2, 16), 0x1234).reshape(k, 32)
+    y = rht16(t.reshape(k, 8, 16), 0x1234).reshape(k, 128)
     c0, q0 = Q.nvfp4_quantize_rows(y, 3.0)
     assert np.array_equal(out["col_groups"][0][0], F.pack_fp4(c0))
     assert np.array_equal(out["col_groups"][0][1], q0)
-    assert out["col_data"].size == k * (32 + 0 + 64) // 2
-    assert out["col_scale"].size == k * (32 + 0 + 64) // 16
+    assert out["col_data"].size == k * (128 + 0 + 128) // 2
+    assert out["col_scale"].size == k * (128 + 0 + 128) // 16

@@ -86,7 +86,7 @@ def test_group_amax_bounds_and_nonnegative_closed_form():
             xg = v[off:off + m]
             assert pre[g] == np.max(np.abs(xg))
             # x >= 0: every |y_i| <= y_0 = sum/4, so the unsigned post amax is the largest block sum / 4
-            p = -(-m // 32) * 32
+            p = -(-m // 128) * 128
             blocks = R.col_blocks(xg, p)
             sums = F.round_bf16(F.f32(np.max(np.sum(blocks, axis=-1)) / 4))
             assert abs(post[g] - sums) <= sums * 2 ** -7
