@@ -1,0 +1,226 @@
+"""Throughput of the fused MoE grouped MLP (MXFP8, SwiGLU) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config mid] [--cpu-sample-rows R]
+
+One step = one forward + backward of the whole path (x and dy group quantize,
+fc1 GEMM + SwiGLU*prob, fc2-input quantize, fc2 GEMM, fc2 dgrad + dSwiGLU +
+dprob, dh quantize, fc2 wgrad, fc1 dgrad, fc1 wgrad) over the synthetic
+workload: 8 experts, hidden 4096, ffn 1536, 16384 tokens routed top-2 = 32768
+rows split by a uniform multinomial.  Inputs are resident in HBM before timing;
+weights are quantized once, outside the timed steps.
+
+Prints one JSON line: TFLOP/s of the step (6 M H (F1 + ffn) flops), the
+roofline of the dominant kernel (the fc1-dgrad-shaped grouped GEMM, timed live
+with HIP events on the stream it runs on), the group-quantize GB/s, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+MXFP8_PEAK_TFLOPS = 5000.0      # MI355X dense MXFP8 / fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="mid")
+    p.add_argument("--recompute", type=int, default=0)
+    p.add_argument("--kernel-reps", type=int, default=20)
+    p.add_argument("--cpu-sample-rows", type=int, default=512, help="rows per sampled expert for the oracle")
+    p.add_argument("--cpu-sample-experts", type=int, default=2)
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              f"(the path shards by expert across GPUs; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import nvfp4_block_scaled_mxfp8_amd as g
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS[args.config]
+    t0 = time.perf_counter()
+    wl = make_workload(cfg)
+    log(f"workload {cfg.name}: generated in {time.perf_counter() - t0:.1f}s; splits={wl.m_splits.tolist()}")
+    E, H, ffn, F1, M = cfg.experts, cfg.hidden, cfg.ffn, cfg.f1, int(wl.m_splits.sum())
+    dev = "cuda"
+
+    def up(bits, shape=None):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+        return t.view(*shape) if shape else t
+
+    x = up(wl.x)
+    dy = up(wl.dy)
+    w1 = up(wl.w1.reshape(E * F1, H), (E, F1, H))
+    w2 = up(wl.w2.reshape(E * H, ffn), (E, H, ffn))
+    probs = torch.from_numpy(wl.probs).to(dev)
+    splits = torch.from_numpy(wl.m_splits.astype(np.int32)).to(dev)
+    kind = cfg.recipe
+    rec = g.recipe(kind, wl.sign_mask)
+    act = cfg.activation
+    w1q = g.weight_quantize(w1, rec)
+    w2q = g.weight_quantize(w2, rec)
+    sizes = g.query_sizes(M, E, H, ffn, act, rec, bool(args.recompute))
+    ws = torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
+    ctxbuf = torch.empty(sizes["ctx_bytes"], dtype=torch.uint8, device=dev)
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    outs = {"dx": torch.empty((M, H), dtype=torch.bfloat16, device=dev),
+            "dprobs": torch.empty(M, dtype=torch.float32, device=dev),
+            "dw1": torch.empty((E, F1, H), dtype=torch.bfloat16, device=dev),
+            "dw2": torch.empty((E, H, ffn), dtype=torch.bfloat16, device=dev)}
+    ctx_holder = {}
+
+    def step():
+        _, ctx = g.grouped_mlp_forward(x, splits, w1q, w2q, probs, act, rec, recompute=bool(args.recompute), ws=ws,
+                                       y=y, ctx=ctx_holder.get("ctx"))
+        ctx_holder["ctx"] = ctx
+        g.grouped_mlp_backward(dy, splits, w1q, w2q, probs, ctx, ws=ws, out=outs)
+
+    ctx_holder["ctx"] = g.MlpContext(ctxbuf, M, E, H, ffn, g.activation_id(act), rec, bool(args.recompute), True, True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = 6.0 * M * H * (F1 + ffn)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"step: {ms:.3f} ms  {tflops:.1f} TFLOP/s  (wall {wall / args.steps * 1e3:.3f} ms/step)")
+
+    # ------------------------------------------------------------------ dominant kernel: fc1-dgrad-shaped GEMM
+    # C [M, H] = Q(dh)[M, F1] . Q(W1 along F1)[E][H, F1]^T -- one of the three largest GEMMs of the step
+    dh = torch.randn((M, F1), device=dev).to(torch.bfloat16)
+    dhq = g.group_quantize(dh, splits, rec, True, False)
+    w1_dgrad = g.QTensor(w1q.kind, {"row_data": w1q.bufs["col_data"], "row_scale_mfma": w1q.bufs.get("col_scale_mfma"),
+                                    "row_scale": w1q.bufs.get("col_scale"), "amax_pre": w1q.bufs.get("amax_pre")})
+    gws = g.quant_workspace(E, dev)
+    gout = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        g.lib().gmlp_grouped_gemm(g.GEMM_FPROP, rec, g.ctypes.byref(dhq.struct()), g.ctypes.byref(w1_dgrad.struct()),
+                                  g._p(splits), E, M, H, F1, g._p(gout), g.OUT_BF16, g._p(gws), gws.numel(),
+                                  g._stream())
+    torch.cuda.synchronize()
+    qa, qb = dhq.struct(), w1_dgrad.struct()
+    ev0.record()
+    for _ in range(args.kernel_reps):
+        st = g.lib().gmlp_grouped_gemm(g.GEMM_FPROP, rec, g.ctypes.byref(qa), g.ctypes.byref(qb), g._p(splits), E, M,
+                                       H, F1, g._p(gout), g.OUT_BF16, g._p(gws), gws.numel(), g._stream())
+        assert st == 0, g.last_error()
+    ev1.record()
+    torch.cuda.synchronize()
+    k_ms = ev0.elapsed_time(ev1) / args.kernel_reps
+    k_flops = 2.0 * M * F1 * H
+    k_tflops = k_flops / (k_ms * 1e-3) / 1e12
+    peak = MXFP8_PEAK_TFLOPS if kind == "mxfp8" else BF16_PEAK_TFLOPS
+    log(f"fc1-dgrad GEMM: {k_ms:.3f} ms  {k_tflops:.1f} TFLOP/s  ({100 * k_tflops / peak:.1f}% of {peak:.0f})")
+
+    # ------------------------------------------------------------------ group quantize GB/s (x, row + column-wise)
+    qout = g.alloc_grouped_q(rec, M, H, E, True, True, dev)
+    for _ in range(3):
+        g.group_quantize(x, splits, rec, True, True, out=qout, ws=gws)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.kernel_reps):
+        g.group_quantize(x, splits, rec, True, True, out=qout, ws=gws)
+    ev1.record()
+    torch.cuda.synchronize()
+    q_ms = ev0.elapsed_time(ev1) / args.kernel_reps
+    q_bytes = (2 + 1 + 1 + 2.0 / 32) * M * H if kind == "mxfp8" else (2 + 0.5 + 1 / 16 + 0.5 + 1 / 16) * M * H
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    log(f"group quantize x: {q_ms * 1e3:.1f} us  {q_gbs:.0f} GB/s ({100 * q_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+
+    # ------------------------------------------------------------------ CPU oracle on a bounded sample
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, args)
+
+    line = {
+        "metric": "grouped-MLP fwd+bwd TFLOP/s at 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-e4m3/e8m0, fp32 accumulate" if kind == "mxfp8" else "nvfp4-e2m1/e4m3, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": cfg.description, "experts": E, "hidden": H, "ffn": ffn, "rows": M,
+                   "activation": act, "recipe": kind, "recompute": bool(args.recompute),
+                   "flops_per_step": flops, "pct_of_mxfp8_peak": round(100 * tflops / MXFP8_PEAK_TFLOPS, 2)},
+        "roofline": {"kernel": "grouped GEMM, fc1-dgrad shape (M=%d, N=%d, K=%d, %d experts)" % (M, H, F1, E),
+                     "bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(k_tflops / peak, 4), "traffic": None, "ms_per_launch": round(k_ms, 4)},
+        "quantize": {"kernel": "MXFP8 group quantize of x, row + column-wise" if kind == "mxfp8" else
+                     "NVFP4 group quantize of x (amax + row + column-wise RHT)",
+                     "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(q_gbs / HBM_PEAK_GBS, 4), "us_per_call": round(q_ms * 1e3, 2),
+                     "algorithmic_bytes": q_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, args):
+    """The oracle (numpy fp64) on a bounded sample: the first R rows of the first few experts, full
+    hidden / ffn, forward + backward, weights pre-quantized outside the timed region."""
+    from oracle import mlp as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    cfg = wl.config
+    ne = min(args.cpu_sample_experts, cfg.experts)
+    off = np.concatenate([[0], np.cumsum(wl.m_splits)])
+    rows, splits = [], []
+    for e in range(ne):
+        r = min(args.cpu_sample_rows, int(wl.m_splits[e]))
+        rows.append(np.arange(off[e], off[e] + r))
+        splits.append(r)
+    idx = np.concatenate(rows)
+    rec = O.Recipe(cfg.recipe, wl.sign_mask)
+    t = time.perf_counter()
+    wq1 = O.quantize_weight(wl.w1[:ne], rec)
+    wq2 = O.quantize_weight(wl.w2[:ne], rec)
+    log(f"cpu baseline: weights of {ne} experts quantized in {time.perf_counter() - t:.1f}s (untimed)")
+    t = time.perf_counter()
+    fwd = O.forward(wl.x[idx], splits, wl.w1[:ne], wl.w2[:ne], wl.probs[idx], cfg.activation, rec, wq1=wq1, wq2=wq2)
+    O.backward(fwd, wl.dy[idx])
+    dt = time.perf_counter() - t
+    m = int(sum(splits))
+    flops = 6.0 * m * cfg.hidden * (cfg.f1 + cfg.ffn)
+    log(f"cpu baseline: {m} rows fwd+bwd in {dt:.1f}s = {flops / dt / 1e12:.4f} TFLOP/s on {threads} threads")
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{m} rows ({splits} from the first {ne} experts), hidden {cfg.hidden}, ffn {cfg.ffn}, "
+                      f"forward + backward, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
