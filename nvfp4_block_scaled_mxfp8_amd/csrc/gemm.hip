@@ -57,7 +57,11 @@ __device__ __forceinline__ int64_t uni(int64_t v) {
 template <class T>
 __device__ __forceinline__ T* uni_ptr(T* p) { return reinterpret_cast<T*>(uni((int64_t)reinterpret_cast<uintptr_t>(p))); }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ (row & 7)) << 4); }
+// Physical 16-byte chunk of logical chunk c in tile row r: c ^ ((r >> 1) & 7).  Rows are 128
+// bytes, so two consecutive rows fill one 256-byte line of the 64 banks; the XOR term then
+// differs between any two rows of the same parity among 16 consecutive rows, which keeps the
+// 16 lanes of each 16-byte LDS access phase on 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // ----------------------------------------------------------------------------- activations
 // Shared by the fc1 epilogue and the fc2-dgrad recompute so that both produce the same bits;
@@ -140,7 +144,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 
 struct DmaPlan {
   __amdgpu_buffer_rsrc_t ra, rb;   // this wave's 64-row bands of A and B
-  uint32_t lane_off;               // (lane / 8) * ld + 16 * ((lane % 8) ^ (lane / 8 % 8))
+  uint32_t lane_off[2];            // even / odd instruction: (lane / 8) * ld + 16 * logical chunk
   uint32_t ld;
 };
 
@@ -149,7 +153,12 @@ __device__ __forceinline__ DmaPlan make_dma_plan(const GemmArgs& A, const Ctx& c
   DmaPlan d;
   d.ld = (uint32_t)c.a_ld;
   const int r8 = lane >> 3;
-  d.lane_off = (uint32_t)r8 * d.ld + 16u * (uint32_t)((lane & 7) ^ (r8 & 7));
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    // tile row = 8 * (8 wave + i) + r8, so (row >> 1) & 7 = (4 (i & 1) + (r8 >> 1)) & 7
+    const int x = (4 * par + (r8 >> 1)) & 7;
+    d.lane_off[par] = (uint32_t)r8 * d.ld + 16u * (uint32_t)((lane & 7) ^ x);
+  }
   const int64_t a_rows = min(64, max(0, c.arows - 64 * wave));
   d.ra = make_rsrc(A.a.data + c.a_base + (c.arow0 + 64 * wave) * c.a_ld, a_rows * c.a_ld);
   int64_t b_first, b_rows;
@@ -171,7 +180,7 @@ __device__ __forceinline__ void mx_dma_stage(const DmaPlan& d, int kt, uint8_t* 
   const uint32_t k = (uint32_t)kt * BKB;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t voff = d.lane_off + (uint32_t)i * 8u * d.ld + k;
+    const uint32_t voff = d.lane_off[i & 1] + (uint32_t)i * 8u * d.ld + k;
     dma16(d.ra, voff, stage + wave * 8192 + i * 1024);
     dma16(d.rb, voff, stage + OPB + wave * 8192 + i * 1024);
   }
@@ -229,50 +238,70 @@ __device__ __forceinline__ void nv_store_stage(uint8_t* stage, int tid, const Nv
 }
 
 // ----------------------------------------------------------------------------- MFMA stage
-template <int S>
-__device__ __forceinline__ void mx_kstep(const uint8_t* stage, int wm, int wn, int lane, const uint32_t* sca,
-                                         const uint32_t* scb, v16f (&acc)[4][4]) {
-  const int m = lane & 31, j = lane >> 5;
-  v8i bf[4];
+// Fragments of one stage for one wave, read from LDS into registers before the next stage's DMA
+// is issued (the compiler cannot prove that the DMA target and the buffer being read differ,
+// so any LDS read after a DMA would wait for the DMA to land).
+struct MxFrags {
+  v8i a[2][4], b[2][4];        // [K-step][tile]
+  uint32_t sa[4], sb[4];       // scale words, shifted for this lane's 32-block
+};
+struct BfFrags {
+  v8bf a[4][4], b[4][4];       // [K-step][tile]
+};
+
+__device__ __forceinline__ v8i ld_frag8(const uint8_t* base, int row, int c0, int c1) {
+  const uint4 x0 = *reinterpret_cast<const uint4*>(base + swz(row, c0));
+  const uint4 x1 = *reinterpret_cast<const uint4*>(base + swz(row, c1));
+  return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+}
+
+__device__ __forceinline__ void mx_read(const uint8_t* stage, int wm, int wn, int lane, MxFrags& f) {
+  const int m = lane & 31, j = lane >> 5, sh = 8 * j;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(stage + SCALE_OFF);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int rb = wn * 128 + t * 32 + m;
-    const uint4 b0 = *reinterpret_cast<const uint4*>(stage + OPB + swz(rb, 4 * S + j));
-    const uint4 b1 = *reinterpret_cast<const uint4*>(stage + OPB + swz(rb, 4 * S + 2 + j));
-    bf[t] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    f.sa[t] = w[wm * 128 + t * 32 + m] >> sh;
+    f.sb[t] = w[256 + wn * 128 + t * 32 + m] >> sh;
   }
+  // lane (m + 32 j) holds K bytes [16 j, 16 j + 16) and [32 + 16 j, 48 + 16 j) of each 64-K step
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm) {
-    const int ra = wm * 128 + tm * 32 + m;
-    const uint4 a0 = *reinterpret_cast<const uint4*>(stage + swz(ra, 4 * S + j));
-    const uint4 a1 = *reinterpret_cast<const uint4*>(stage + swz(ra, 4 * S + 2 + j));
-    const v8i af = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
-      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[tn], acc[tm][tn], 0, 0, 2 * S,
-                                                                     (int)sca[tm], 2 * S, (int)scb[tn]);
-  }
-  // keep the next K-step's fragment reads from being hoisted over this one (register budget)
-  __builtin_amdgcn_sched_barrier(0);
+    for (int t = 0; t < 4; ++t) {
+      f.a[s][t] = ld_frag8(stage, wm * 128 + t * 32 + m, 4 * s + j, 4 * s + 2 + j);
+      f.b[s][t] = ld_frag8(stage + OPB, wn * 128 + t * 32 + m, 4 * s + j, 4 * s + 2 + j);
+    }
 }
 
 template <int S>
-__device__ __forceinline__ void bf_kstep(const uint8_t* stage, int wm, int wn, int lane, v16f (&acc)[4][4]) {
-  const int m = lane & 31, j = lane >> 5;
-  v8bf af[4], bf[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint4 a = *reinterpret_cast<const uint4*>(stage + swz(wm * 128 + t * 32 + m, 2 * S + j));
-    const uint4 b = *reinterpret_cast<const uint4*>(stage + OPB + swz(wn * 128 + t * 32 + m, 2 * S + j));
-    af[t] = __builtin_bit_cast(v8bf, a);
-    bf[t] = __builtin_bit_cast(v8bf, b);
-  }
+__device__ __forceinline__ void mx_mma(const MxFrags& f, v16f (&acc)[4][4]) {
 #pragma unroll
   for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn)
-      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
+      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[S][tm], f.b[S][tn], acc[tm][tn], 0, 0, 2 * S,
+                                                                     (int)f.sa[tm], 2 * S, (int)f.sb[tn]);
+}
+
+__device__ __forceinline__ void bf_read(const uint8_t* stage, int wm, int wn, int lane, BfFrags& f) {
+  const int m = lane & 31, j = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f.a[s][t] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(stage + swz(wm * 128 + t * 32 + m, 2 * s + j)));
+      f.b[s][t] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(stage + OPB + swz(wn * 128 + t * 32 + m, 2 * s + j)));
+    }
+}
+
+__device__ __forceinline__ void bf_mma(const BfFrags& f, v16f (&acc)[4][4]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[s][tm], f.b[s][tn], acc[tm][tn], 0, 0, 0);
 }
 
 // ----------------------------------------------------------------------------- tile mapping
@@ -382,55 +411,8 @@ __device__ __forceinline__ void mx_dma_scales(const GemmArgs& A, const Ctx& c, i
 
 // ----------------------------------------------------------------------------- kernel
 template <int FMT, int MODE, int EPI>
-__device__ __forceinline__ void compute_stage(const uint8_t* stage, int wm, int wn, int lane, v16f (&acc)[4][4]) {
-  if (FMT == FMT_MXFP8) {
-    // this lane's scale words (rows 32 t + m of its wave's A and B sub-tiles), shifted so that
-    // byte 2s holds its 32-block of K-step s
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(stage + SCALE_OFF);
-    const int m = lane & 31, sh = 8 * (lane >> 5);
-    uint32_t sca[4], scb[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sca[t] = w[wm * 128 + t * 32 + m] >> sh;
-      scb[t] = w[256 + wn * 128 + t * 32 + m] >> sh;
-    }
-    mx_kstep<0>(stage, wm, wn, lane, sca, scb, acc);
-    mx_kstep<1>(stage, wm, wn, lane, sca, scb, acc);
-  } else {
-    bf_kstep<0>(stage, wm, wn, lane, acc);
-    bf_kstep<1>(stage, wm, wn, lane, acc);
-    bf_kstep<2>(stage, wm, wn, lane, acc);
-    bf_kstep<3>(stage, wm, wn, lane, acc);
-  }
-}
-
-// Issues the loads of stage kt into `dst` (MXFP8: DMA straight to LDS; NVFP4: to registers).
-template <int FMT, int MODE, int EPI>
-__device__ __forceinline__ void issue_stage(const GemmArgs& A, const Ctx& c, const DmaPlan& d, int kt, uint8_t* dst,
-                                            int tid, NvStage& nv) {
-  if (FMT == FMT_MXFP8) {
-    const int wave = uni(tid >> 6);
-    mx_dma_scales<MODE, EPI>(A, c, kt, dst, wave, tid & 63);
-    mx_dma_stage(d, kt, dst, wave);
-  } else {
-    nv_load_stage<MODE, EPI>(A, c, kt, tid, nv);
-  }
-}
-
-// Completes stage kt in `dst` (NVFP4: expand and store), waits for all of its data, barrier.
-template <int FMT>
-__device__ __forceinline__ void finish_stage(uint8_t* dst, int tid, const NvStage& nv) {
-  if (FMT == FMT_NVFP4) nv_store_stage(dst, tid, nv);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-}
-
-template <int FMT, int MODE, int EPI>
 __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
-  // Two distinct LDS objects (not one array) so that the compiler can tell the buffer being
-  // read from the buffer the DMA is filling when it places its wait counts.
-  __shared__ __align__(16) uint8_t buf0[STAGE];
-  __shared__ __align__(16) uint8_t buf1[STAGE];
+  __shared__ __align__(16) uint8_t smem[2 * STAGE];
   int mt = 0;
   Ctx c;
   if (!make_ctx<FMT, MODE, EPI>(A, mt, c)) return;
@@ -450,30 +432,57 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
 
-  NvStage nv;
-  DmaPlan dp;
-  if (FMT == FMT_MXFP8) dp = make_dma_plan<MODE, EPI>(A, c, wave, lane);
-  if (c.nk > 0) {
-    issue_stage<FMT, MODE, EPI>(A, c, dp, 0, buf0, tid, nv);
-    finish_stage<FMT>(buf0, tid, nv);
+  if (FMT == FMT_MXFP8) {
+    const DmaPlan dp = make_dma_plan<MODE, EPI>(A, c, wave, lane);
+    if (c.nk > 0) {
+      mx_dma_scales<MODE, EPI>(A, c, 0, smem, wave, lane);
+      mx_dma_stage(dp, 0, smem, wave);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < c.nk; ++kt) {
+      const uint8_t* cur = smem + (kt & 1) * STAGE;
+      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+      MxFrags f;
+      mx_read(cur, wm, wn, lane, f);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < c.nk) {
+        mx_dma_scales<MODE, EPI>(A, c, kt + 1, nxt, wave, lane);
+        mx_dma_stage(dp, kt + 1, nxt, wave);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mx_mma<0>(f, acc);
+      mx_mma<1>(f, acc);
+      // keep the MFMAs above the wait for the next stage (they do not touch memory, so the
+      // compiler would otherwise sink them below it and serialize compute behind the DMA)
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    NvStage nv;
+    if (c.nk > 0) {
+      nv_load_stage<MODE, EPI>(A, c, 0, tid, nv);
+      nv_store_stage(smem, tid, nv);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < c.nk; ++kt) {
+      const uint8_t* cur = smem + (kt & 1) * STAGE;
+      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+      const bool more = kt + 1 < c.nk;
+      if (more) nv_load_stage<MODE, EPI>(A, c, kt + 1, tid, nv);
+      BfFrags f;
+      bf_read(cur, wm, wn, lane, f);
+      bf_mma(f, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) nv_store_stage(nxt, tid, nv);
+      __syncthreads();
+    }
   }
-  // stages in pairs (even stage in buf0, odd stage in buf1), one loop exit, odd tail after
-  int kt = 0;
-  for (; kt + 1 < c.nk; kt += 2) {
-    issue_stage<FMT, MODE, EPI>(A, c, dp, kt + 1, buf1, tid, nv);
-    compute_stage<FMT, MODE, EPI>(buf0, wm, wn, lane, acc);
-    finish_stage<FMT>(buf1, tid, nv);
-    const bool more = kt + 2 < c.nk;
-    if (more) issue_stage<FMT, MODE, EPI>(A, c, dp, kt + 2, buf0, tid, nv);
-    compute_stage<FMT, MODE, EPI>(buf1, wm, wn, lane, acc);
-    if (more) finish_stage<FMT>(buf0, tid, nv);
-  }
-  if (kt < c.nk) compute_stage<FMT, MODE, EPI>(buf0, wm, wn, lane, acc);
-  __syncthreads();
 
   // --------------------------------------------------------------------------- epilogues
   const int m = lane & 31, j = lane >> 5;
-  if (EPI == EPI_STORE && A.out_fp32) {
+  if (EPI == EPI_STORE32) {
     // fp32 output (optional wgrad dtype): direct stores
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
@@ -488,27 +497,30 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
           const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + row : (int64_t)c.g * A.N + c.arow0 + row;
           static_cast<float*>(A.c)[orow * ncols + col] = acc[tm][tn][r] * c.alpha;
         }
+        __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 tile at a time (register budget)
       }
     return;
   }
   // Stage the bf16-rounded tile (the C dtype of every fused output) in LDS, then run the
   // epilogue per 8-column chunk with 16-byte loads and stores.
   {
-    uint16_t* st = reinterpret_cast<uint16_t*>(wm == 0 ? buf0 : buf1);
+    uint16_t* st = reinterpret_cast<uint16_t*>(smem + wm * STAGE);
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn)
+      for (int tn = 0; tn < 4; ++tn) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = tm * 32 + 8 * (r >> 2) + 4 * j + (r & 3);      // row within this half
-          st[ep_off(row, wn * 128 + tn * 32 + m)] = (uint16_t)f32_to_bf16_bits(acc[tm][tn][r] * c.alpha);
+          for (int r = 0; r < 16; ++r) {
+            const int row = tm * 32 + 8 * (r >> 2) + 4 * j + (r & 3);      // row within this half
+            st[ep_off(row, wn * 128 + tn * 32 + m)] = (uint16_t)f32_to_bf16_bits(acc[tm][tn][r] * c.alpha);
+          }
+          __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 tile at a time (register budget)
         }
   }
   __syncthreads();
   // staged element (row, col) of the 256 x 256 tile
   auto stg = [&](int row, int col) -> const uint4* {
-    const uint16_t* st = reinterpret_cast<const uint16_t*>(row < 128 ? buf0 : buf1);
+    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem + (row >> 7) * STAGE);
     return reinterpret_cast<const uint4*>(st + ep_off(row & 127, col));
   };
 
@@ -653,8 +665,13 @@ static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.mode == MODE_FPROP && g.M == 0) return hipSuccess;
 #define GMLP_DISPATCH(F, MO, E) \
-  if (g.fmt == F && g.mode == MO && g.epi == E) return launch_one<F, MO, E>(g, s);
+  if (g.fmt == F && g.mode == MO && epi == E) return launch_one<F, MO, E>(g, s);
+  const int epi = (g.epi == EPI_STORE && g.out_fp32) ? (int)EPI_STORE32 : g.epi;
   GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_STORE)
+  GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_STORE32)
+  GMLP_DISPATCH(FMT_MXFP8, MODE_WGRAD, EPI_STORE32)
+  GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_STORE32)
+  GMLP_DISPATCH(FMT_NVFP4, MODE_WGRAD, EPI_STORE32)
   GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_FC1)
   GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_DACT)
   GMLP_DISPATCH(FMT_MXFP8, MODE_WGRAD, EPI_STORE)

@@ -51,7 +51,7 @@ hipError_t launch_gather_weights(const void* const* w_ptrs, int E, int64_t N, in
 // ----------------------------------------------------------------------------- GEMM
 enum GemmFmt { FMT_MXFP8 = 0, FMT_NVFP4 = 1 };
 enum GemmMode { MODE_FPROP = 0, MODE_WGRAD = 1 };
-enum GemmEpi { EPI_STORE = 0, EPI_FC1 = 1, EPI_DACT = 2 };
+enum GemmEpi { EPI_STORE = 0, EPI_FC1 = 1, EPI_DACT = 2, EPI_STORE32 = 3 };   // STORE32: fp32 output
 
 struct GemmOperand {
   const uint8_t* data;        // fp8 / packed fp4
