@@ -7,7 +7,7 @@
 // forward casts fc2_x row-wise only when the backward rebuilds it; the forward
 // keeps the fc2_x (pre, post) amax; the backward casts the rebuilt fc2_x with
 // that amax and runs no second Hadamard-amax pass.
-#include "../../include/gmlp.h"
+#include "gmlp.h"
 #include "kernels.h"
 
 #include <hip/hip_runtime.h>
