@@ -76,10 +76,17 @@ typedef struct {
 /* A group-quantized tensor [MX, Greptile summary: flat 1-D data and scale
  * buffers with per-group offsets].  Every pointer is device memory owned by the
  * caller; a pointer the call does not need may be NULL.
- *   row_data       MXFP8 u8 [M, K];              NVFP4 u8 [M, K/2]
+ * MXFP8 data is stored in 64-byte K panels (the GEMM stages one panel of 256
+ * rows as 16 KB of contiguous memory): for a matrix of R rows and K columns,
+ * panel p holds columns [64p, 64p + w), w = min(64, K - 64p), as R rows of w
+ * bytes starting at byte 64 p R.  Row-wise data is one such [M, K] matrix;
+ * column-wise data is, per group g, the [K, P_g] matrix of the group's columns
+ * (tokens along the panel), starting at byte K * sum_{h<g} P_h.
+ * NVFP4 data is row-major with two E2M1 codes per byte (low nibble first).
+ *   row_data       MXFP8 u8 [M, K] (panels);     NVFP4 u8 [M, K/2]
  *   row_scale      MXFP8 E8M0 u8 [M, K/32];      NVFP4 E4M3 u8 [M, K/16]
  *   row_scale_mfma MXFP8 u32 [ceil(K/128), M]    (unused for NVFP4)
- *   col_data       MXFP8 u8 [K * sum P_g];       NVFP4 u8 [K * sum P_g / 2]
+ *   col_data       MXFP8 u8 [K * sum P_g] (panels); NVFP4 u8 [K * sum P_g / 2]
  *   col_scale      MXFP8 u8 [K * sum P_g / 32];  NVFP4 u8 [K * sum P_g / 16]
  *   col_scale_mfma MXFP8 u32 [K * sum P_g/128]
  *   amax_pre, amax_post  NVFP4 fp32 [G] (per-group pre-/post-RHT amax) */
@@ -96,8 +103,9 @@ typedef struct {
 
 /* Quantized stacked weights for one GroupedLinear, W [E, N, K] (Linear layout
  * [out, in]) [MX, Greptile summary: stacked and discrete weights].
- *   fprop operand: blocks along K  -> row_data [E*N, K(/2)], row scales
- *   dgrad operand: blocks along N  -> col_data [E, K, N(/2)], col scales (W^T per expert)
+ *   fprop operand: blocks along K  -> row_data [E][N, K(/2)], row scales
+ *   dgrad operand: blocks along N  -> col_data [E][K, N(/2)], col scales (W^T per expert)
+ *   MXFP8 data of each expert is one matrix in 64-byte K panels, as above. 
  *   NVFP4: amax [E] (one global scale per expert for both casts; weights get no RHT). */
 typedef gmlp_grouped_q gmlp_weight_q;
 

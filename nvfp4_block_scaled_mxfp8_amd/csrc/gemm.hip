@@ -35,12 +35,22 @@ namespace gmlp {
 constexpr int BM = 256, BN = 256;
 constexpr int BKB = 128;                         // bytes per tile row per stage
 constexpr int NTHREADS = 256;
-constexpr int OPB = BM * BKB;                    // bytes of one operand stage (32 KB)
-constexpr int SCALE_OFF = 2 * OPB;               // MXFP8 scale words of the stage: A [256] then B [256] (u32)
-constexpr int STAGE = 2 * OPB + 2048;            // A + B + scales (66 KB)
+constexpr int OPB = BM * BKB;                    // NVFP4 (bf16 after expansion): one operand stage (32 KB)
+constexpr int STAGE = 2 * OPB;                   // NVFP4 stage: A + B (64 KB), double buffered
+// MXFP8: a ring of 4 stages of 64 K (one MFMA K-step), 3 in flight while one is computed.
+constexpr int MX_BK = 64;
+constexpr int MX_OPB = BM * MX_BK;               // 16 KB per operand
+constexpr int MX_SC_OFF = 2 * MX_OPB;            // scale words: A [256] then B [256] (u32)
+constexpr int MX_STAGE = 2 * MX_OPB + 2048;      // 34 KB
+constexpr int MX_NSTAGE = 4;
+constexpr int MX_DMA_PER_STAGE = 9;              // per wave: 4 A + 4 B data DMAs + 1 scale-word DMA
+constexpr int SMEM_BYTES = (MX_NSTAGE * MX_STAGE > 2 * STAGE) ? MX_NSTAGE * MX_STAGE : 2 * STAGE;
 // Epilogue staging: 128 rows x 256 bf16 (512 bytes) per buffer; the 16-byte chunk index is
 // XORed with bits 2..3 of the row so that the two rows a wave writes at once (r and r + 4)
 // fall in different banks.
+// fp32 staging: 256 rows x 128 floats; rows 4 apart (the two lane halves of an MFMA output
+// register) land 32 banks apart.
+__device__ __forceinline__ int ep32_off(int row, int col) { return row * 128 + (col ^ (((row >> 2) & 1) << 5)); }
 __device__ __forceinline__ int ep_off(int row, int col) {
   return row * 256 + ((((col >> 3) ^ (((row >> 2) & 3) << 2))) << 3) + (col & 7);
 }
@@ -62,6 +72,9 @@ __device__ __forceinline__ T* uni_ptr(T* p) { return reinterpret_cast<T*>(uni((i
 // differs between any two rows of the same parity among 16 consecutive rows, which keeps the
 // 16 lanes of each 16-byte LDS access phase on 16 distinct bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// 64-byte rows (MXFP8 stages): four rows share a 256-byte bank line, so the chunk is XORed
+// with (row >> 2) & 3; 16 consecutive rows then cover all 16 bank groups.
+__device__ __forceinline__ int swz64(int row, int chunk) { return row * MX_BK + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 // ----------------------------------------------------------------------------- activations
 // Shared by the fc1 epilogue and the fc2-dgrad recompute so that both produce the same bits;
@@ -106,6 +119,7 @@ struct Ctx {
   int nk;            // stages
   // operand bases (element offsets of row 0 of the operand matrix for this group)
   int64_t a_base, b_base, a_ld, b_ld;
+  int64_t a_rtot, b_rtot;                           // MXFP8: rows per 64-byte K panel of A and B
   int64_t a_sw_base, b_sw_base, a_sw_ld, b_sw_ld;   // MXFP8 scale words: base + kt * ld + row
   float alpha;
 };
@@ -126,64 +140,119 @@ __device__ __forceinline__ bool b_row(const GemmArgs& A, const Ctx& c, int j, in
 
 // ----------------------------------------------------------------------------- stage loads
 // MXFP8: direct buffer -> LDS DMA (buffer_load_dwordx4 ... lds).  One instruction moves a
-// wave's 64 x 16 bytes into 1 KB of LDS (lane l lands at +16 l), i.e. 8 tile rows; lane l
-// fetches logical chunk (l % 8) ^ (row % 8) of its row so that LDS holds the swizzled layout.
+// wave's 64 x 16 bytes into 1 KB of LDS (lane l lands at +16 l), i.e. 16 rows of a 64-K
+// stage; each lane fetches the logical chunk that the swizzle places at its slot.
 // Wave w loads A rows and B rows [64 w, 64 w + 64) of the tile through one buffer resource
 // each, whose size ends at the last valid row: rows past it read as zero (hardware range
 // check), so partial tiles need no clamping and every lane keeps one 32-bit offset.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9 family)
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int32_t n = uni((int)(bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes)));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uni_ptr(base)), (short)0, n, (int)kRsrcWord3);
-}
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_block) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, 0, 0, 0);
-}
-
-struct DmaPlan {
-  __amdgpu_buffer_rsrc_t ra, rb;   // this wave's 64-row bands of A and B
-  uint32_t lane_off[2];            // even / odd instruction: (lane / 8) * ld + 16 * logical chunk
-  uint32_t ld;
+// Buffer descriptor {base, stride 0, num_records, format}: loads at offsets >= num_records
+// return zero (hardware range check).
+struct Rsrc {
+  v4i w;
 };
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)uni((int64_t)reinterpret_cast<uintptr_t>(base));
+  const int32_t n = (int32_t)(bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes));
+  Rsrc r;
+  r.w = v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), uni(n), (int)kRsrcWord3};
+  return r;
+}
+
+// One buffer -> LDS DMA of 16 bytes per active lane: lane l's bytes land at lds + 16 l.  Issued
+// through inline asm so that the compiler's wait-count pass does not treat it as a pending
+// LDS write (it would otherwise wait for every outstanding DMA before any LDS read); the
+// kernel accounts for these loads itself with explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const Rsrc& r, uint32_t voff, const uint8_t* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds;          // low 32 bits of a shared address = LDS offset
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(r.w), "s"(__builtin_amdgcn_readfirstlane(m0)) : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter: vmcnt <= n (expcnt, lgkmcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// MXFP8 operands are stored in 64-byte K panels: byte (r, k) of an R-row operand sits at
+// ((k / 64) R + r) 64 + k % 64, so one stage of a 64-row band is 4 KB of contiguous memory
+// and every DMA instruction reads 16 whole rows (1 KB, 8 full cache lines).
+struct DmaPlan {
+  const uint8_t* a0;               // this wave's A band, panel 0
+  const uint8_t* b0;               // this wave's B band, panel 0
+  int64_t a_pstride, b_pstride;    // bytes per panel (R x 64)
+  int32_t a_bytes, b_bytes;        // valid rows of the band x 64: the resource range
+  uint32_t lane_off;               // (lane / 4) 64 + 16 x logical chunk
+};
+
+template <int MODE, int EPI>
+__device__ __forceinline__ void b_band(const GemmArgs& A, const Ctx& c, int wave, int64_t& first, int64_t& rows) {
+  if (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
+    // band w = [gate | up][(w & 1)] rows f0 + 64 (w >> 1) .. + 64, f0 = 128 nt
+    const int64_t f = (int64_t)c.nt * 128 + 64 * (wave >> 1);
+    first = ((wave & 1) ? A.ffn : 0) + f;
+    rows = min((int64_t)64, max((int64_t)0, A.ffn - f));
+  } else {
+    const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
+    first = c.nrow0 + 64 * wave;
+    rows = min((int64_t)64, max((int64_t)0, nb - first));
+  }
+}
 
 template <int MODE, int EPI>
 __device__ __forceinline__ DmaPlan make_dma_plan(const GemmArgs& A, const Ctx& c, int wave, int lane) {
   DmaPlan d;
-  d.ld = (uint32_t)c.a_ld;
-  const int r8 = lane >> 3;
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    // tile row = 8 * (8 wave + i) + r8, so (row >> 1) & 7 = (4 (i & 1) + (r8 >> 1)) & 7
-    const int x = (4 * par + (r8 >> 1)) & 7;
-    d.lane_off[par] = (uint32_t)r8 * d.ld + 16u * (uint32_t)((lane & 7) ^ x);
-  }
+  // one instruction = 16 rows of 64 bytes; lane l -> row 16 i + l / 4, physical chunk l % 4,
+  // so it fetches logical chunk (l % 4) ^ ((row >> 2) & 3) = (l % 4) ^ ((l >> 4) & 3)
+  d.lane_off = (uint32_t)(lane >> 2) * 64u + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
   const int64_t a_rows = min(64, max(0, c.arows - 64 * wave));
-  d.ra = make_rsrc(A.a.data + c.a_base + (c.arow0 + 64 * wave) * c.a_ld, a_rows * c.a_ld);
+  d.a0 = A.a.data + c.a_base + (c.arow0 + 64 * wave) * 64;
+  d.a_pstride = c.a_rtot * 64;
+  d.a_bytes = (int32_t)(a_rows * 64);
   int64_t b_first, b_rows;
-  if (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
-    // band w = [gate | up][(w & 1)] rows f0 + 64 (w >> 1) .. + 64, f0 = 128 nt
-    const int64_t f = (int64_t)c.nt * 128 + 64 * (wave >> 1);
-    b_first = ((wave & 1) ? A.ffn : 0) + f;
-    b_rows = min((int64_t)64, max((int64_t)0, A.ffn - f));
-  } else {
-    const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
-    b_first = c.nrow0 + 64 * wave;
-    b_rows = min((int64_t)64, max((int64_t)0, nb - b_first));
-  }
-  d.rb = make_rsrc(A.b.data + c.b_base + b_first * c.b_ld, b_rows * c.b_ld);
+  b_band<MODE, EPI>(A, c, wave, b_first, b_rows);
+  d.b0 = A.b.data + c.b_base + b_first * 64;
+  d.b_pstride = c.b_rtot * 64;
+  d.b_bytes = (int32_t)(b_rows * 64);
   return d;
 }
 
-__device__ __forceinline__ void mx_dma_stage(const DmaPlan& d, int kt, uint8_t* stage, int wave) {
-  const uint32_t k = (uint32_t)kt * BKB;
+// Stage kt (64 K): wave w fetches A and B rows [64 w, 64 w + 64) (4 + 4 DMAs) and one 1 KB DMA
+// of MFMA scale words for the stage's 128-K word: waves 0 and 2 the 256 A rows' words, waves 1
+// and 3 the 256 B rows' words (waves 2 and 3 repeat the same bytes).  Every wave issues the
+// same 9 DMAs per stage, so one vmcnt bound serves all waves; a stage past the end (live ==
+// false) is issued with empty resources so that the count stays the same without a branch.
+template <int MODE, int EPI>
+__device__ __forceinline__ void mx_dma_stage(const GemmArgs& A, const Ctx& c, const DmaPlan& d, int kt, uint8_t* stage,
+                                             int wave, int lane, bool live) {
+  // the stage's band: rows past the valid ones are out of the resource's range and read zero
+  const Rsrc ra = make_rsrc(d.a0 + kt * d.a_pstride, live ? d.a_bytes : 0);
+  const Rsrc rb = make_rsrc(d.b0 + kt * d.b_pstride, live ? d.b_bytes : 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t voff = d.lane_off[i & 1] + (uint32_t)i * 8u * d.ld + k;
-    dma16(d.ra, voff, stage + wave * 8192 + i * 1024);
-    dma16(d.rb, voff, stage + OPB + wave * 8192 + i * 1024);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t voff = d.lane_off + (uint32_t)i * 1024u;
+    dma16(ra, voff, stage + wave * 4096 + i * 1024);
+    dma16(rb, voff, stage + MX_OPB + wave * 4096 + i * 1024);
   }
+  const int64_t kw = kt >> 1;
+  const bool swiglu = MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0;
+  const bool is_b = (wave & 1) != 0;
+  // A rows arow0 .. arow0 + arows of the 128-K word kw
+  const uint32_t* a_w = A.a.scale_mfma + c.a_sw_base + kw * c.a_sw_ld + c.arow0;
+  const int64_t a_n = 4 * (int64_t)c.arows;
+  // B rows: the tile's 256 rows in order, or for SwiGLU fc1 the 64-row bands
+  // [gate f0 | up f0 | gate f0 + 64 | up f0 + 64] of one resource starting at gate row f0
+  const uint32_t* bw = A.b.scale_mfma + c.b_sw_base + kw * c.b_sw_ld;
+  const int64_t f0 = (int64_t)c.nt * 128;
+  const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
+  const uint32_t* b_w = swiglu ? bw + f0 : bw + c.nrow0;
+  const int64_t b_n = swiglu ? 4 * (2 * A.ffn - f0) : 4 * max((int64_t)0, nb - c.nrow0);
+  const int band = lane >> 4;
+  const uint32_t b_voff = swiglu ? 4u * (uint32_t)((band & 1) * A.ffn + (band >> 1) * 64 + 4 * (lane & 15)) : 16u * lane;
+  const Rsrc rs = make_rsrc(is_b ? b_w : a_w, live ? (is_b ? b_n : a_n) : 0);
+  dma16(rs, is_b ? b_voff : 16u * lane, stage + MX_SC_OFF + (is_b ? 1024 : 0));
 }
 
 // NVFP4: thread = tile row; 64 packed E2M1 (32 bytes) + 4 E4M3 block scales per operand,
@@ -242,45 +311,42 @@ __device__ __forceinline__ void nv_store_stage(uint8_t* stage, int tid, const Nv
 // is issued (the compiler cannot prove that the DMA target and the buffer being read differ,
 // so any LDS read after a DMA would wait for the DMA to land).
 struct MxFrags {
-  v8i a[2][4], b[2][4];        // [K-step][tile]
-  uint32_t sa[4], sb[4];       // scale words, shifted for this lane's 32-block
+  v8i a[4], b[4];              // one 64-K step
+  uint32_t sa[4], sb[4];       // E8M0 scale of this lane's 32-block in byte 0
 };
 struct BfFrags {
   v8bf a[4][4], b[4][4];       // [K-step][tile]
 };
 
 __device__ __forceinline__ v8i ld_frag8(const uint8_t* base, int row, int c0, int c1) {
-  const uint4 x0 = *reinterpret_cast<const uint4*>(base + swz(row, c0));
-  const uint4 x1 = *reinterpret_cast<const uint4*>(base + swz(row, c1));
+  const uint4 x0 = *reinterpret_cast<const uint4*>(base + swz64(row, c0));
+  const uint4 x1 = *reinterpret_cast<const uint4*>(base + swz64(row, c1));
   return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 
-__device__ __forceinline__ void mx_read(const uint8_t* stage, int wm, int wn, int lane, MxFrags& f) {
-  const int m = lane & 31, j = lane >> 5, sh = 8 * j;
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(stage + SCALE_OFF);
+// Lane (m + 32 j) holds K bytes [16 j, 16 j + 16) and [32 + 16 j, 48 + 16 j) of the step; its
+// scale is block j of the step, i.e. byte 2 (kt & 1) + j of the stage's 128-K word, read as a
+// single byte so that it lands in byte 0 of the register the MFMA takes it from.
+__device__ __forceinline__ void mx_read(const uint8_t* stage, int wm, int wn, int lane, int kt, MxFrags& f) {
+  const int m = lane & 31, j = lane >> 5;
+  const uint8_t* w = stage + MX_SC_OFF + 2 * (kt & 1) + j;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    f.sa[t] = w[wm * 128 + t * 32 + m] >> sh;
-    f.sb[t] = w[256 + wn * 128 + t * 32 + m] >> sh;
+    f.sa[t] = w[4 * (wm * 128 + t * 32 + m)];
+    f.sb[t] = w[1024 + 4 * (wn * 128 + t * 32 + m)];
+    f.a[t] = ld_frag8(stage, wm * 128 + t * 32 + m, j, 2 + j);
+    f.b[t] = ld_frag8(stage + MX_OPB, wn * 128 + t * 32 + m, j, 2 + j);
   }
-  // lane (m + 32 j) holds K bytes [16 j, 16 j + 16) and [32 + 16 j, 48 + 16 j) of each 64-K step
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f.a[s][t] = ld_frag8(stage, wm * 128 + t * 32 + m, 4 * s + j, 4 * s + 2 + j);
-      f.b[s][t] = ld_frag8(stage + OPB, wn * 128 + t * 32 + m, 4 * s + j, 4 * s + 2 + j);
-    }
 }
 
-template <int S>
+template <int TM0, int TM1>
 __device__ __forceinline__ void mx_mma(const MxFrags& f, v16f (&acc)[4][4]) {
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm)
+  for (int tm = TM0; tm < TM1; ++tm)
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn)
-      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[S][tm], f.b[S][tn], acc[tm][tn], 0, 0, 2 * S,
-                                                                     (int)f.sa[tm], 2 * S, (int)f.sb[tn]);
+      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[tm], f.b[tn], acc[tm][tn], 0, 0, 0,
+                                                                     (int)f.sa[tm], 0, (int)f.sb[tn]);
 }
 
 __device__ __forceinline__ void bf_read(const uint8_t* stage, int wm, int wn, int lane, BfFrags& f) {
@@ -323,8 +389,15 @@ __device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
   } else {
     ntn = (int)((A.K + BN - 1) / BN);
   }
-  const int tile_m = bid / ntn;
-  c.nt = bid % ntn;
+  // Launch order within an XCD's range: groups of group_rows tile rows, column-major inside
+  // a group, so that the workgroups resident together share few A row blocks and B blocks.
+  const int ntm = (int)(gridDim.x / ntn);
+  const int gr = A.group_rows;
+  const int gsz = gr * ntn;
+  const int grp = bid / gsz, rem = bid - grp * gsz;
+  const int rows_here = min(gr, ntm - grp * gr);
+  const int tile_m = grp * gr + rem % rows_here;
+  c.nt = rem / rows_here;
   c.alpha = 1.0f;
   if (MODE == MODE_FPROP) {
     if (A.G <= 0 || tile_m >= A.T.t256_off[A.G]) return false;
@@ -342,6 +415,8 @@ __device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
     const int64_t brows = (EPI == EPI_FC1 && A.act == 0) ? 2 * A.ffn : A.N;
     c.b_base = (int64_t)c.g * brows * A.K;
     c.b_ld = A.K;
+    c.a_rtot = A.M;
+    c.b_rtot = brows;
     c.a_sw_base = 0;
     c.a_sw_ld = A.M;
     c.b_sw_base = (int64_t)c.g * ((A.K + 127) / 128) * brows;
@@ -351,7 +426,7 @@ __device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
       const float sb = nvfp4_global_scale(A.b.amax[c.g]);
       c.alpha = __fmul_rn(__fdiv_rn(1.0f, sa), __fdiv_rn(1.0f, sb));
     }
-    c.nk = (int)((A.K + (FMT == FMT_MXFP8 ? 127 : 63)) / (FMT == FMT_MXFP8 ? 128 : 64));
+    c.nk = (int)((A.K + 63) / 64);              // 64-K stages (both formats)
   } else {
     const int ntm = (int)((A.N + BM - 1) / BM);
     const int per_g = ntm;
@@ -367,6 +442,8 @@ __device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
     c.a_ld = P;
     c.b_base = A.K * (int64_t)A.T.col_off[c.g];
     c.b_ld = P;
+    c.a_rtot = A.N;
+    c.b_rtot = A.K;
     c.a_sw_base = A.N * (int64_t)A.T.colw_off[c.g];
     c.a_sw_ld = A.N;
     c.b_sw_base = A.K * (int64_t)A.T.colw_off[c.g];
@@ -376,49 +453,22 @@ __device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
       const float sb = nvfp4_global_scale(A.b.amax[c.g]);
       c.alpha = __fmul_rn(__fdiv_rn(1.0f, sa), __fdiv_rn(1.0f, sb));
     }
-    c.nk = (int)((P + (FMT == FMT_MXFP8 ? 127 : 63)) / (FMT == FMT_MXFP8 ? 128 : 64));
+    c.nk = (int)((P + 63) / 64);
   }
   return true;
-}
-
-// MFMA-ready scale words of the stage's 256 A rows and 256 B rows, DMAed into LDS next to the
-// data (one 1 KB instruction each: lane l fetches the words of tile rows 4l..4l+3).  Rows past
-// the valid range read 0: their data is zero too, and those outputs are never stored.
-template <int MODE, int EPI>
-__device__ __forceinline__ void mx_dma_scales(const GemmArgs& A, const Ctx& c, int kt, uint8_t* stage, int wave,
-                                              int lane) {
-  if (wave == 0) {
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(A.a.scale_mfma + c.a_sw_base + (int64_t)kt * c.a_sw_ld + c.arow0, 4 * (int64_t)c.arows);
-    dma16(ra, 16u * lane, stage + SCALE_OFF);
-  } else if (wave == 1) {
-    const uint32_t* bw = A.b.scale_mfma + c.b_sw_base + (int64_t)kt * c.b_sw_ld;
-    if (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
-      // tile rows in 64-row bands [gate f0.. | up f0.. | gate f0+64.. | up f0+64..], f0 = 128 nt;
-      // one resource from gate row f0 to the end of the expert's up rows
-      const int64_t f0 = (int64_t)c.nt * 128;
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(bw + f0, 4 * (2 * A.ffn - f0));
-      const int band = lane >> 4;
-      const uint32_t row = (uint32_t)((band & 1) * A.ffn + (band >> 1) * 64 + 4 * (lane & 15));
-      dma16(rb, 4u * row, stage + SCALE_OFF + 1024);
-    } else {
-      const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(bw + c.nrow0, 4 * max((int64_t)0, nb - c.nrow0));
-      dma16(rb, 16u * lane, stage + SCALE_OFF + 1024);
-    }
-  }
 }
 
 // ----------------------------------------------------------------------------- kernel
 template <int FMT, int MODE, int EPI>
 __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
-  __shared__ __align__(16) uint8_t smem[2 * STAGE];
+  __shared__ __align__(16) uint8_t smem[SMEM_BYTES];
   int mt = 0;
   Ctx c;
   if (!make_ctx<FMT, MODE, EPI>(A, mt, c)) return;
   c.g = uni(c.g); c.arows = uni(c.arows); c.nt = uni(c.nt); c.nk = uni(c.nk);
   c.arow0 = uni(c.arow0); c.nrow0 = uni(c.nrow0); c.kvalid = uni(c.kvalid);
   c.a_base = uni(c.a_base); c.b_base = uni(c.b_base); c.a_ld = uni(c.a_ld); c.b_ld = uni(c.b_ld);
+  c.a_rtot = uni(c.a_rtot); c.b_rtot = uni(c.b_rtot);
   c.a_sw_base = uni(c.a_sw_base); c.b_sw_base = uni(c.b_sw_base); c.a_sw_ld = uni(c.a_sw_ld); c.b_sw_ld = uni(c.b_sw_ld);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uni(tid >> 6);
@@ -433,32 +483,43 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
       for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
 
   if (FMT == FMT_MXFP8) {
+    // Ring of 4 stages of 64 K: stage s lives in slot s % 4.  Iteration kt computes stage kt
+    // from registers while stages kt+1..kt+3 are in flight; the fragments of stage kt+1 are
+    // read into the second register set between the two halves of the MFMAs.
+    const int nk = c.nk;                         // 64-K stages
     const DmaPlan dp = make_dma_plan<MODE, EPI>(A, c, wave, lane);
-    if (c.nk > 0) {
-      mx_dma_scales<MODE, EPI>(A, c, 0, smem, wave, lane);
-      mx_dma_stage(dp, 0, smem, wave);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+    auto slot = [&](int st) { return smem + (st & (MX_NSTAGE - 1)) * MX_STAGE; };
+    for (int st = 0; st < 3; ++st) mx_dma_stage<MODE, EPI>(A, c, dp, st, slot(st), wave, lane, st < nk);
+    MxFrags f0, f1;
+    // Every step issues one stage, live or empty, so that stage s has landed once at most the
+    // 2 x 9 DMAs of the two stages issued after it are pending; the loop body then has no
+    // branch for the compiler to move the MFMAs across.
+    wait_vmcnt<2 * MX_DMA_PER_STAGE>();
     __syncthreads();
-    for (int kt = 0; kt < c.nk; ++kt) {
-      const uint8_t* cur = smem + (kt & 1) * STAGE;
-      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
-      MxFrags f;
-      mx_read(cur, wm, wn, lane, f);
+    mx_read(slot(0), wm, wn, lane, 0, f0);
+    auto step = [&](int kt, const MxFrags& cur, MxFrags& nxt) __attribute__((always_inline)) {
+      // the slot of stage kt + 3 held stage kt - 1, whose fragments every wave read before
+      // the barrier of the previous step
+      mx_dma_stage<MODE, EPI>(A, c, dp, kt + 3, slot(kt + 3), wave, lane, kt + 3 < nk);
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < c.nk) {
-        mx_dma_scales<MODE, EPI>(A, c, kt + 1, nxt, wave, lane);
-        mx_dma_stage(dp, kt + 1, nxt, wave);
-      }
+      mx_mma<0, 2>(cur, acc);
       __builtin_amdgcn_sched_barrier(0);
-      mx_mma<0>(f, acc);
-      mx_mma<1>(f, acc);
-      // keep the MFMAs above the wait for the next stage (they do not touch memory, so the
-      // compiler would otherwise sink them below it and serialize compute behind the DMA)
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0);
+      wait_vmcnt<2 * MX_DMA_PER_STAGE>();
       __syncthreads();
+      // on the last step this reads a slot that holds no stage; the values go unused
+      mx_read(slot(kt + 1), wm, wn, lane, kt + 1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_mma<2, 4>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // two steps per trip (the stage count is even: K and every P_g are multiples of 128) so
+    // that the two fragment sets stay in fixed registers
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, f0, f1);
+      step(kt + 1, f1, f0);
     }
+    wait_vmcnt<0>();                 // the empty stages' DMAs, before LDS is reused
+    __syncthreads();
   } else {
     NvStage nv;
     if (c.nk > 0) {
@@ -483,28 +544,49 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
   // --------------------------------------------------------------------------- epilogues
   const int m = lane & 31, j = lane >> 5;
   if (EPI == EPI_STORE32) {
-    // fp32 output (optional wgrad dtype): direct stores
+    // fp32 output (optional wgrad dtype), in two passes over column pairs: pass p stages the
+    // 32-column tiles tn = 2p, 2p + 1 of every wave (256 rows x 128 floats = 128 KB of LDS),
+    // then stores whole row segments with 16-byte stores.
+    float* st = reinterpret_cast<float*>(smem);
+    const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
+    float* C = static_cast<float*>(A.c);
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        const int64_t col = c.nrow0 + wn * 128 + tn * 32 + m;
-        const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
+      for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + tm * 32 + 8 * (r >> 2) + 4 * j + (r & 3);
-          if (row >= c.arows || col >= ncols) continue;
-          const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + row : (int64_t)c.g * A.N + c.arow0 + row;
-          static_cast<float*>(A.c)[orow * ncols + col] = acc[tm][tn][r] * c.alpha;
+        for (int q = 0; q < 2; ++q) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * 128 + tm * 32 + 8 * (r >> 2) + 4 * j + (r & 3);
+            st[ep32_off(row, wn * 64 + q * 32 + m)] = acc[tm][2 * p + q][r] * c.alpha;
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 tile at a time (register budget)
+      __syncthreads();
+      for (int it = 0; it < 32; ++it) {
+        const int row = it * 8 + (tid >> 5);
+        const int lc = 4 * (tid & 31);
+        const int64_t gcol = c.nrow0 + (lc >> 6) * 128 + 64 * p + (lc & 63);
+        if (row < c.arows && gcol < ncols) {
+          const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + row : (int64_t)c.g * A.N + c.arow0 + row;
+          const float4 v = *reinterpret_cast<const float4*>(st + ep32_off(row, lc));
+          if (gcol + 4 <= ncols) {
+            *reinterpret_cast<float4*>(C + orow * ncols + gcol) = v;
+          } else {
+            const float e[4] = {v.x, v.y, v.z, v.w};
+            for (int q = 0; q < 4 && gcol + q < ncols; ++q) C[orow * ncols + gcol + q] = e[q];
+          }
+        }
       }
+      __syncthreads();
+    }
     return;
   }
   // Stage the bf16-rounded tile (the C dtype of every fused output) in LDS, then run the
   // epilogue per 8-column chunk with 16-byte loads and stores.
   {
-    uint16_t* st = reinterpret_cast<uint16_t*>(smem + wm * STAGE);
+    uint16_t* st = reinterpret_cast<uint16_t*>(smem + wm * 65536);
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
@@ -520,7 +602,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
   __syncthreads();
   // staged element (row, col) of the 256 x 256 tile
   auto stg = [&](int row, int col) -> const uint4* {
-    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem + (row >> 7) * STAGE);
+    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem + (row >> 7) * 65536);
     return reinterpret_cast<const uint4*>(st + ep_off(row & 127, col));
   };
 
@@ -658,7 +740,10 @@ static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
     tiles = (int64_t)g.G * ((g.N + BM - 1) / BM) * ((g.K + BN - 1) / BN);
   }
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<FMT, MODE, EPI>), dim3((unsigned)tiles), dim3(NTHREADS), 0, s, g);
+  GemmArgs a = g;
+  a.group_rows = 4;
+  if (const char* e = getenv("GMLP_GROUP_ROWS")) a.group_rows = atoi(e) > 0 ? atoi(e) : 1;
+  hipLaunchKernelGGL((gemm_kernel<FMT, MODE, EPI>), dim3((unsigned)tiles), dim3(NTHREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -79,6 +79,7 @@ struct GemmArgs {
   uint16_t* a_out;   // EPI_FC1: out a [M, ffn]; EPI_DACT: out a' (recompute) or null
   uint16_t* dh;      // EPI_DACT: out dh [M, F1]
   float* dprob_part; // EPI_DACT: [n_tiles, M]
+  int group_rows;    // tile rows per launch-order group (see make_ctx); set by launch_gemm
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);

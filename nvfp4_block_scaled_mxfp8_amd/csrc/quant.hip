@@ -183,7 +183,11 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __rest
       const uint32_t code = mx_block(v, w);
       const bool ok = (r < ti.rows) && (c0 + 32 * b < ti.kcols);
       if (ok) {
-        uint4* dst = reinterpret_cast<uint4*>(o.row_data + grow * K + ti.k0 + c0 + 32 * b);
+        // 64-byte K panels: panel p = k / 64 holds features [64 p, 64 p + w), w = min(64, K - 64 p),
+        // as M rows of w bytes at 64 p M; this thread's (up to) 64 features are one panel row
+        const int64_t pn = (ti.k0 + c0) / 64;
+        const int64_t pw = min((int64_t)64, K - 64 * pn);
+        uint4* dst = reinterpret_cast<uint4*>(o.row_data + 64 * pn * M + grow * pw + 32 * b);
         dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
         dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
         if (o.row_scale) o.row_scale[grow * (K / 32) + (ti.k0 + c0) / 32 + b] = (uint8_t)code;
@@ -216,7 +220,9 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __rest
     const uint32_t code = mx_block(v, w);
     const bool inpad = 32 * cb < rowsP;
     if (inpad && c < ti.kcols) {
-      uint4* dst = reinterpret_cast<uint4*>(o.col_data + colbase + (ti.k0 + c) * P + ti.t0 + 32 * cb);
+      // the group's [K, P] column-wise tensor in 64-byte token panels: byte (f, t) at
+      // ((t / 64) K + f) 64 + t % 64; tokens 64 half .. 64 half + 63 of the tile are one panel row
+      uint4* dst = reinterpret_cast<uint4*>(o.col_data + colbase + (((ti.t0 / 64) + half) * K + ti.k0 + c) * 64 + 32 * j);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
       if (o.col_scale) o.col_scale[colbase / 32 + (ti.k0 + c) * (P / 32) + ti.t0 / 32 + cb] = (uint8_t)code;

@@ -4,7 +4,8 @@ import pytest
 import torch
 
 import nvfp4_block_scaled_mxfp8_amd as g
-from gpu_util import assert_bytes_equal, bits16, col_total, dev_bf16, dev_f32, dev_splits, f32bits, u32, u8
+from gpu_util import (assert_bytes_equal, bits16, col_total, dev_bf16, dev_f32, dev_splits, f32bits, u32, u8,
+                      unpanel, unpanel_groups)
 from oracle import quant as Q
 from oracle import rht as R
 from workloads import all_bf16_finite, random_bf16
@@ -22,12 +23,12 @@ CASES = [
 
 def _check_mx(q, ref, splits, M, K, row=True, col=True):
     if row:
-        assert_bytes_equal(u8(q.bufs["row_data"])[:M * K], ref["row_data"], "row data")
+        assert_bytes_equal(unpanel(u8(q.bufs["row_data"])[:M * K], M, K), ref["row_data"], "row data")
         assert_bytes_equal(u8(q.bufs["row_scale"])[:M * K // 32], ref["row_scale"], "row scales")
         assert_bytes_equal(u32(q.bufs["row_scale_mfma"])[:((K + 127) // 128) * M], ref["row_scale_mfma"], "row mfma scales")
     if col:
         P = col_total(splits)
-        assert_bytes_equal(u8(q.bufs["col_data"])[:K * P], ref["col_data"], "col data")
+        assert_bytes_equal(unpanel_groups(u8(q.bufs["col_data"])[:K * P], K, splits), ref["col_data"], "col data")
         assert_bytes_equal(u8(q.bufs["col_scale"])[:K * P // 32], ref["col_scale"], "col scales")
         assert_bytes_equal(u32(q.bufs["col_scale_mfma"])[:K * P // 128], ref["col_scale_mfma"], "col mfma scales")
 
@@ -154,10 +155,14 @@ def test_weight_quantize(kind):
     for q in (g.weight_quantize(wd, rec), g.weight_quantize([wd[e] for e in range(E)], rec)):
         torch.cuda.synchronize()
         if kind == "mxfp8":
-            assert_bytes_equal(u8(q.bufs["row_data"]), np.stack([r[0] for r in ref["row"]]), "w row data")
+            rows = u8(q.bufs["row_data"]).reshape(E, N * K)
+            got = np.stack([unpanel(rows[e], N, K) for e in range(E)])
+            assert_bytes_equal(got, np.stack([r[0] for r in ref["row"]]), "w row data")
             want = np.concatenate([Q.mfma_scale_layout(r[1]).reshape(-1) for r in ref["row"]])
             assert_bytes_equal(u32(q.bufs["row_scale_mfma"]), want, "w row mfma scales")
-            assert_bytes_equal(u8(q.bufs["col_data"]), np.stack([r[0] for r in ref["colT"]]), "w col data")
+            cols = u8(q.bufs["col_data"]).reshape(E, N * K)
+            got = np.stack([unpanel(cols[e], K, N) for e in range(E)])
+            assert_bytes_equal(got, np.stack([r[0] for r in ref["colT"]]), "w col data")
             want = np.concatenate([Q.mfma_scale_layout(r[1]).reshape(-1) for r in ref["colT"]])
             assert_bytes_equal(u32(q.bufs["col_scale_mfma"]), want, "w col mfma scales")
         else:
