@@ -224,18 +224,21 @@ __device__ __forceinline__ DmaPlan make_dma_plan(const GemmArgs& A, const Ctx& c
 // and 3 the 256 B rows' words (waves 2 and 3 repeat the same bytes).  Every wave issues the
 // same 9 DMAs per stage, so one vmcnt bound serves all waves; a stage past the end (live ==
 // false) is issued with empty resources so that the count stays the same without a branch.
+struct StageDma {
+  Rsrc ra, rb, rs;       // the stage's A band, B band and scale words
+  uint32_t s_voff;
+  uint8_t* lds;          // the stage's slot
+  uint32_t s_lds;        // scale-word destination offset in the slot
+};
+
 template <int MODE, int EPI>
-__device__ __forceinline__ void mx_dma_stage(const GemmArgs& A, const Ctx& c, const DmaPlan& d, int kt, uint8_t* stage,
-                                             int wave, int lane, bool live) {
+__device__ __forceinline__ StageDma mx_stage_plan(const GemmArgs& A, const Ctx& c, const DmaPlan& d, int kt,
+                                                  uint8_t* stage, int wave, int lane, bool live) {
+  StageDma s;
+  s.lds = stage;
   // the stage's band: rows past the valid ones are out of the resource's range and read zero
-  const Rsrc ra = make_rsrc(d.a0 + kt * d.a_pstride, live ? d.a_bytes : 0);
-  const Rsrc rb = make_rsrc(d.b0 + kt * d.b_pstride, live ? d.b_bytes : 0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t voff = d.lane_off + (uint32_t)i * 1024u;
-    dma16(ra, voff, stage + wave * 4096 + i * 1024);
-    dma16(rb, voff, stage + MX_OPB + wave * 4096 + i * 1024);
-  }
+  s.ra = make_rsrc(d.a0 + kt * d.a_pstride, live ? d.a_bytes : 0);
+  s.rb = make_rsrc(d.b0 + kt * d.b_pstride, live ? d.b_bytes : 0);
   const int64_t kw = kt >> 1;
   const bool swiglu = MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0;
   const bool is_b = (wave & 1) != 0;
@@ -251,8 +254,33 @@ __device__ __forceinline__ void mx_dma_stage(const GemmArgs& A, const Ctx& c, co
   const int64_t b_n = swiglu ? 4 * (2 * A.ffn - f0) : 4 * max((int64_t)0, nb - c.nrow0);
   const int band = lane >> 4;
   const uint32_t b_voff = swiglu ? 4u * (uint32_t)((band & 1) * A.ffn + (band >> 1) * 64 + 4 * (lane & 15)) : 16u * lane;
-  const Rsrc rs = make_rsrc(is_b ? b_w : a_w, live ? (is_b ? b_n : a_n) : 0);
-  dma16(rs, is_b ? b_voff : 16u * lane, stage + MX_SC_OFF + (is_b ? 1024 : 0));
+  s.rs = make_rsrc(is_b ? b_w : a_w, live ? (is_b ? b_n : a_n) : 0);
+  s.s_voff = is_b ? b_voff : 16u * lane;
+  s.s_lds = MX_SC_OFF + (is_b ? 1024 : 0);
+  return s;
+}
+
+// DMA number I (0..8) of a stage: even I < 8 an A instruction, odd I < 8 a B instruction, 8 the
+// scale words.
+template <int I>
+__device__ __forceinline__ void mx_dma_one(const StageDma& s, const DmaPlan& d, int wave) {
+  if constexpr (I < 8) {
+    constexpr int i = I >> 1;
+    const uint32_t voff = d.lane_off + (uint32_t)i * 1024u;
+    if constexpr ((I & 1) == 0) dma16(s.ra, voff, s.lds + wave * 4096 + i * 1024);
+    else dma16(s.rb, voff, s.lds + MX_OPB + wave * 4096 + i * 1024);
+  } else {
+    dma16(s.rs, s.s_voff, s.lds + s.s_lds);
+  }
+}
+
+template <int MODE, int EPI>
+__device__ __forceinline__ void mx_dma_stage(const GemmArgs& A, const Ctx& c, const DmaPlan& d, int kt, uint8_t* stage,
+                                             int wave, int lane, bool live) {
+  const StageDma s = mx_stage_plan<MODE, EPI>(A, c, d, kt, stage, wave, lane, live);
+  mx_dma_one<0>(s, d, wave); mx_dma_one<1>(s, d, wave); mx_dma_one<2>(s, d, wave);
+  mx_dma_one<3>(s, d, wave); mx_dma_one<4>(s, d, wave); mx_dma_one<5>(s, d, wave);
+  mx_dma_one<6>(s, d, wave); mx_dma_one<7>(s, d, wave); mx_dma_one<8>(s, d, wave);
 }
 
 // NVFP4: thread = tile row; 64 packed E2M1 (32 bytes) + 4 E4M3 block scales per operand,
@@ -327,16 +355,69 @@ __device__ __forceinline__ v8i ld_frag8(const uint8_t* base, int row, int c0, in
 // Lane (m + 32 j) holds K bytes [16 j, 16 j + 16) and [32 + 16 j, 48 + 16 j) of the step; its
 // scale is block j of the step, i.e. byte 2 (kt & 1) + j of the stage's 128-K word, read as a
 // single byte so that it lands in byte 0 of the register the MFMA takes it from.
-__device__ __forceinline__ void mx_read(const uint8_t* stage, int wm, int wn, int lane, int kt, MxFrags& f) {
+template <int T>
+__device__ __forceinline__ void mx_read_t(const uint8_t* stage, int wm, int wn, int lane, int kt, MxFrags& f) {
   const int m = lane & 31, j = lane >> 5;
   const uint8_t* w = stage + MX_SC_OFF + 2 * (kt & 1) + j;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f.sa[t] = w[4 * (wm * 128 + t * 32 + m)];
-    f.sb[t] = w[1024 + 4 * (wn * 128 + t * 32 + m)];
-    f.a[t] = ld_frag8(stage, wm * 128 + t * 32 + m, j, 2 + j);
-    f.b[t] = ld_frag8(stage + MX_OPB, wn * 128 + t * 32 + m, j, 2 + j);
-  }
+  f.a[T] = ld_frag8(stage, wm * 128 + T * 32 + m, j, 2 + j);
+  f.b[T] = ld_frag8(stage + MX_OPB, wn * 128 + T * 32 + m, j, 2 + j);
+  f.sa[T] = w[4 * (wm * 128 + T * 32 + m)];
+  f.sb[T] = w[1024 + 4 * (wn * 128 + T * 32 + m)];
+}
+
+__device__ __forceinline__ void mx_read(const uint8_t* stage, int wm, int wn, int lane, int kt, MxFrags& f) {
+  mx_read_t<0>(stage, wm, wn, lane, kt, f);
+  mx_read_t<1>(stage, wm, wn, lane, kt, f);
+  mx_read_t<2>(stage, wm, wn, lane, kt, f);
+  mx_read_t<3>(stage, wm, wn, lane, kt, f);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void mx_mma_one(const MxFrags& f, v16f (&acc)[4][4]) {
+  acc[TM][TN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[TM], f.b[TN], acc[TM][TN], 0, 0, 0, (int)f.sa[TM],
+                                                                 0, (int)f.sb[TN]);
+}
+
+#define GMLP_SB() __builtin_amdgcn_sched_barrier(0)
+
+// One step's instruction order.  The 9 DMAs of the stage three ahead are spread over the 16
+// MFMAs (one per 64-cycle MFMA pair at most), so that the address unit's queue, shared by the
+// four waves, is fed at the rate it drains: a wave whose DMA waits for room stalls under a
+// running MFMA instead of holding back a block of them.  The reads of the next stage are
+// spread over the second half.
+//   before the barrier: D0 M00 M01 D1 M02 M03 D2 M10 M11 D3 M12 M13 D4
+//   after the barrier:  R0 M20 D5 R1 M21 M22 D6 R2 M23 M30 D7 R3 M31 M32 D8 M33
+constexpr int MX_DMA_BEFORE_BARRIER = 5;
+
+__device__ __forceinline__ void mx_phase1(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
+                                          int wave) {
+  mx_dma_one<0>(s, d, wave); GMLP_SB();
+  mx_mma_one<0, 0>(f, acc); GMLP_SB(); mx_mma_one<0, 1>(f, acc); GMLP_SB();
+  mx_dma_one<1>(s, d, wave); GMLP_SB();
+  mx_mma_one<0, 2>(f, acc); GMLP_SB(); mx_mma_one<0, 3>(f, acc); GMLP_SB();
+  mx_dma_one<2>(s, d, wave); GMLP_SB();
+  mx_mma_one<1, 0>(f, acc); GMLP_SB(); mx_mma_one<1, 1>(f, acc); GMLP_SB();
+  mx_dma_one<3>(s, d, wave); GMLP_SB();
+  mx_mma_one<1, 2>(f, acc); GMLP_SB(); mx_mma_one<1, 3>(f, acc); GMLP_SB();
+  mx_dma_one<4>(s, d, wave); GMLP_SB();
+}
+
+__device__ __forceinline__ void mx_phase2(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
+                                          int wave, const uint8_t* nstage, int wm, int wn, int lane, int nkt,
+                                          MxFrags& nf) {
+  mx_read_t<0>(nstage, wm, wn, lane, nkt, nf); GMLP_SB();
+  mx_mma_one<2, 0>(f, acc); GMLP_SB();
+  mx_dma_one<5>(s, d, wave); GMLP_SB();
+  mx_read_t<1>(nstage, wm, wn, lane, nkt, nf); GMLP_SB();
+  mx_mma_one<2, 1>(f, acc); GMLP_SB(); mx_mma_one<2, 2>(f, acc); GMLP_SB();
+  mx_dma_one<6>(s, d, wave); GMLP_SB();
+  mx_read_t<2>(nstage, wm, wn, lane, nkt, nf); GMLP_SB();
+  mx_mma_one<2, 3>(f, acc); GMLP_SB(); mx_mma_one<3, 0>(f, acc); GMLP_SB();
+  mx_dma_one<7>(s, d, wave); GMLP_SB();
+  mx_read_t<3>(nstage, wm, wn, lane, nkt, nf); GMLP_SB();
+  mx_mma_one<3, 1>(f, acc); GMLP_SB(); mx_mma_one<3, 2>(f, acc); GMLP_SB();
+  mx_dma_one<8>(s, d, wave); GMLP_SB();
+  mx_mma_one<3, 3>(f, acc); GMLP_SB();
 }
 
 template <int TM0, int TM1>
@@ -500,17 +581,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
     auto step = [&](int kt, const MxFrags& cur, MxFrags& nxt) __attribute__((always_inline)) {
       // the slot of stage kt + 3 held stage kt - 1, whose fragments every wave read before
       // the barrier of the previous step
-      mx_dma_stage<MODE, EPI>(A, c, dp, kt + 3, slot(kt + 3), wave, lane, kt + 3 < nk);
-      __builtin_amdgcn_sched_barrier(0);
-      mx_mma<0, 2>(cur, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<2 * MX_DMA_PER_STAGE>();
+      const StageDma sd = mx_stage_plan<MODE, EPI>(A, c, dp, kt + 3, slot(kt + 3), wave, lane, kt + 3 < nk);
+      GMLP_SB();
+      mx_phase1(cur, acc, sd, dp, wave);
+      // stage kt + 1 has landed once at most the DMAs issued after it are pending: the 9 of
+      // stage kt + 2 and the first ones of stage kt + 3
+      wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
       __syncthreads();
       // on the last step this reads a slot that holds no stage; the values go unused
-      mx_read(slot(kt + 1), wm, wn, lane, kt + 1, nxt);
-      __builtin_amdgcn_sched_barrier(0);
-      mx_mma<2, 4>(cur, acc);
-      __builtin_amdgcn_sched_barrier(0);
+      mx_phase2(cur, acc, sd, dp, wave, slot(kt + 1), wm, wn, lane, kt + 1, nxt);
     };
     // two steps per trip (the stage count is even: K and every P_g are multiples of 128) so
     // that the two fragment sets stay in fixed registers
