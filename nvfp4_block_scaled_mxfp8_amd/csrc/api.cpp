@@ -294,7 +294,9 @@ BwdWs carve_bwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, c
     w.a2 = b.take<uint16_t>(M * ffn);
     w.a2q = carve_q(b, r, M, ffn, E, false, true, false);
   }
-  w.dprob_part = b.take<float>((size_t)dact_ntiles(ffn) * M);
+  // dL/dp partials: per 256-column tile of the NVFP4 fused epilogue, per 128 features of the
+  // MXFP8 fused activation-gradient cast
+  w.dprob_part = b.take<float>((size_t)ceil_div(ffn, 128) * M);
   return w;
 }
 
@@ -638,9 +640,43 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
 
   // 1. dy: row-wise for the fc2 dgrad, column-wise for the fc2 wgrad
   if (!quant(static_cast<const uint16_t*>(A->dy), H, W.dyq, true, wgrad)) return L.st;
-  // 2. fc2 dgrad + dGLU / dSReLU epilogue (+ rebuilt fc2 input when recomputing)
+  // 2-3. MXFP8: fc2 dgrad da = dy W2 (bf16, in the dh buffer), then one pass that forms dh from
+  // da and h, casts it row- and column-wise, sums the dL/dp partials and (recomputing) rebuilds
+  // and casts the fc2 input.  NVFP4: the dgrad GEMM's fused epilogue writes bf16 dh, then dh
+  // is cast like any tensor.
+  if (mx) {
+    uint16_t* da = W.dh;
+    GemmArgs g = gemm_base(MODE_FPROP, r, EPI_STORE, W.T, E);
+    g.M = M;
+    g.N = ffn;
+    g.K = H;
+    g.a = op_row(W.dyq.q, W.dyq.q.amax_pre);
+    g.b = op_col(*A->w2, A->w2->amax_pre);
+    g.c = da;
+    if (!L.check(launch_gemm(g, stream), "fc2 dgrad gemm")) return L.st;
+    g_counts[CNT_GEMM]++;
+    DactArgs d{};
+    d.da = da;
+    d.h = C.h;
+    d.probs = A->probs;
+    d.act = A->activation;
+    d.ffn = ffn;
+    d.dh = MxOut{dgrad ? static_cast<uint8_t*>(W.dhq.q.row_data) : nullptr, nullptr,
+                 dgrad ? static_cast<uint32_t*>(W.dhq.q.row_scale_mfma) : nullptr,
+                 wgrad ? static_cast<uint8_t*>(W.dhq.q.col_data) : nullptr, nullptr,
+                 wgrad ? static_cast<uint32_t*>(W.dhq.q.col_scale_mfma) : nullptr};
+    d.a2 = (rec && wgrad) ? MxOut{nullptr, nullptr, nullptr, static_cast<uint8_t*>(W.a2q.q.col_data), nullptr,
+                                  static_cast<uint32_t*>(W.a2q.q.col_scale_mfma)}
+                          : MxOut{};
+    d.dprob_part = W.dprob_part;
+    if (!L.check(launch_dact_quant(d, W.T, E, M, stream), "activation gradient cast")) return L.st;
+    g_counts[CNT_MXQ]++;
+    if (!L.check(launch_dprob_reduce(W.dprob_part, (int)ceil_div(ffn, 128), M, A->dprobs, stream), "dprob reduce"))
+      return L.st;
+    g_counts[CNT_DPROB]++;
+  }
   const int ntn = dact_ntiles(ffn);
-  {
+  if (!mx) {
     GemmArgs g = gemm_base(MODE_FPROP, r, EPI_DACT, W.T, E);
     g.M = M;
     g.N = ffn;
@@ -657,22 +693,20 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     if (!L.check(launch_gemm(g, stream), "fc2 dgrad gemm")) return L.st;
     g_counts[CNT_GEMM]++;
   }
-  if (!L.check(launch_dprob_reduce(W.dprob_part, ntn, M, A->dprobs, stream), "dprob reduce")) return L.st;
-  g_counts[CNT_DPROB]++;
-  // 3. dh: row-wise for the fc1 dgrad, column-wise for the fc1 wgrad
-  if (dgrad || wgrad)
-    if (!quant(W.dh, F1, W.dhq, dgrad, wgrad)) return L.st;
+  if (!mx) {
+    if (!L.check(launch_dprob_reduce(W.dprob_part, ntn, M, A->dprobs, stream), "dprob reduce")) return L.st;
+    g_counts[CNT_DPROB]++;
+    // 3. dh: row-wise for the fc1 dgrad, column-wise for the fc1 wgrad
+    if (dgrad || wgrad)
+      if (!quant(W.dh, F1, W.dhq, dgrad, wgrad)) return L.st;
+  }
   // 4. fc2 wgrad: column-wise dy and fc2 input (rebuilt and cast with the saved amax when recomputing)
   if (wgrad) {
     const gmlp_grouped_q* aq = &C.aq_col.q;
     const float* a_post = C.a_post;
     if (rec) {
       if (mx) {
-        MxOut o{nullptr, nullptr, nullptr, static_cast<uint8_t*>(W.a2q.q.col_data), nullptr,
-                static_cast<uint32_t*>(W.a2q.q.col_scale_mfma)};
-        if (!L.check(launch_mxfp8_quant(W.a2, M, ffn, W.T, E, false, true, o, stream), "mxfp8 quantize rebuilt fc2 input"))
-          return L.st;
-        g_counts[CNT_MXQ]++;
+        // cast by the activation-gradient pass above
       } else {
         NvOut o{nullptr, nullptr, static_cast<uint8_t*>(W.a2q.q.col_data), static_cast<uint8_t*>(W.a2q.q.col_scale)};
         if (!L.check(launch_nvfp4_quant(W.a2, M, ffn, W.T, E, mask, true, false, true, C.a_pre, C.a_post, o, stream),

@@ -27,6 +27,7 @@
 // V_MFMA_F32_32X32X16_BF16; the per-group global scales multiply the fp32
 // result.  (The block-scaled MFMA takes E8M0 scales per 32 elements; NVFP4's
 // E4M3 scales per 16 cannot be folded into it exactly.)
+#include "activation.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -75,38 +76,6 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((ch
 // 64-byte rows (MXFP8 stages): four rows share a 256-byte bank line, so the chunk is XORed
 // with (row >> 2) & 3; 16 consecutive rows then cover all 16 bank groups.
 __device__ __forceinline__ int swz64(int row, int chunk) { return row * MX_BK + ((chunk ^ ((row >> 2) & 3)) << 4); }
-
-// ----------------------------------------------------------------------------- activations
-// Shared by the fc1 epilogue and the fc2-dgrad recompute so that both produce the same bits;
-// every operation is an explicitly rounded fp32 op (no contraction).
-__device__ __forceinline__ float sigmoid_f(float g) { return __fdiv_rn(1.0f, __fadd_rn(1.0f, expf(-g))); }
-
-__device__ __forceinline__ float act_value(int act, float g, float u) {
-  if (act == 0) return __fmul_rn(__fmul_rn(g, sigmoid_f(g)), u);   // silu(gate) * up
-  const float r = fmaxf(g, 0.0f);
-  return __fmul_rn(r, r);                                            // relu(h)^2
-}
-__device__ __forceinline__ float act_out(int act, float g, float u, float p) {
-  return round_bf16(__fmul_rn(act_value(act, g, u), p));
-}
-// d(act * p)/dh for upstream da: d0 = d/dgate (or d/dh), d1 = d/dup; dp = da * act (dL/dp).
-__device__ __forceinline__ void act_grad(int act, float g, float u, float da, float p, float& d0, float& d1,
-                                         float& dp) {
-  if (act == 0) {
-    const float sg = sigmoid_f(g);
-    const float silu = __fmul_rn(g, sg);
-    const float dap = __fmul_rn(da, p);
-    const float dsilu = __fmul_rn(sg, __fadd_rn(1.0f, __fmul_rn(g, __fsub_rn(1.0f, sg))));
-    d0 = __fmul_rn(__fmul_rn(dap, u), dsilu);
-    d1 = __fmul_rn(dap, silu);
-    dp = __fmul_rn(da, __fmul_rn(silu, u));
-  } else {
-    const float r = fmaxf(g, 0.0f);
-    d0 = __fmul_rn(__fmul_rn(__fmul_rn(da, p), 2.0f), r);
-    d1 = 0.0f;
-    dp = __fmul_rn(da, __fmul_rn(r, r));
-  }
-}
 
 // ----------------------------------------------------------------------------- tile context
 struct Ctx {
@@ -702,7 +671,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
   if (EPI == EPI_FC1) {
     const int64_t F1 = (A.act == 0) ? 2 * A.ffn : A.ffn;
     if (A.act == 0) {
-      // staged columns of wave wn: [gate f0..f0+63 | up f0..f0+63], f0 = nt*128 + wn*64
+      // staged columns of wave wn: [gate f0..f0+63 | up f0..f0+63], f0 = nt*128 + wn*64.
+      // The routing probabilities of this thread's 16 rows are loaded up front (one latency).
+      float pv[16];
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int row = it * 16 + (tid >> 4);
+        pv[it] = row < c.arows ? A.probs[c.arow0 + row] : 0.0f;
+      }
+#pragma unroll
       for (int it = 0; it < 16; ++it) {
         const int row = it * 16 + (tid >> 4);
         const int fl = 8 * (tid & 15);
@@ -714,7 +691,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
         const uint4 uv = *stg(row, scol + 64);
         *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = gv;
         *reinterpret_cast<uint4*>(A.h + grow * F1 + A.ffn + f) = uv;
-        const float p = A.probs[grow];
+        const float p = pv[it];
         const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
         uint32_t ow[4];
         for (int i = 0; i < 4; ++i) {
@@ -725,6 +702,13 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
         *reinterpret_cast<uint4*>(A.a_out + grow * A.ffn + f) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
       }
     } else {
+      float pv[32];
+#pragma unroll
+      for (int it = 0; it < 32; ++it) {
+        const int row = it * 8 + (tid >> 5);
+        pv[it] = row < c.arows ? A.probs[c.arow0 + row] : 0.0f;
+      }
+#pragma unroll
       for (int it = 0; it < 32; ++it) {
         const int row = it * 8 + (tid >> 5);
         const int col = 8 * (tid & 31);
@@ -733,7 +717,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
         const int64_t grow = c.arow0 + row;
         const uint4 hv = *stg(row, col);
         *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = hv;
-        const float p = A.probs[grow];
+        const float p = pv[it];
         const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
         uint32_t ow[4];
         for (int i = 0; i < 4; ++i) {
@@ -748,49 +732,68 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
   }
 
   // EPI_DACT: staged tile = da [rows, f]; writes dh (+ a' when recomputing) and per-row dprob
-  // partials of this n-tile, summed over its 256 columns in a fixed order.
+  // partials of this n-tile, summed over its 256 columns in a fixed order.  The h loads of 8
+  // row-chunks are issued together before any of them is used, so that their memory latency
+  // overlaps instead of adding up chunk by chunk.
   {
     const int64_t F1 = (A.act == 0) ? 2 * A.ffn : A.ffn;
-    for (int it = 0; it < 32; ++it) {
-      const int row = it * 8 + (tid >> 5);
-      const int col = 8 * (tid & 31);
-      const int64_t f = c.nrow0 + col;
-      const bool ok = row < c.arows && f < A.ffn;
-      const int64_t grow = c.arow0 + (row < c.arows ? row : 0);
-      float psum = 0.0f;
-      if (ok) {
-        const float p = A.probs[grow];
-        const uint4 dv = *stg(row, col);
-        const uint4 gv = *reinterpret_cast<const uint4*>(A.h + grow * F1 + f);
-        uint4 uv = make_uint4(0, 0, 0, 0);
-        if (A.act == 0) uv = *reinterpret_cast<const uint4*>(A.h + grow * F1 + A.ffn + f);
-        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w},
-                       uw[4] = {uv.x, uv.y, uv.z, uv.w};
-        uint32_t o0[4], o1[4], oa[4];
-        for (int i = 0; i < 4; ++i) {
-          uint32_t r0 = 0, r1 = 0, ra = 0;
-          for (int hh = 0; hh < 2; ++hh) {
-            const float da = bf16_to_f32((dw[i] >> (16 * hh)) & 0xFFFFu);
-            const float g = bf16_to_f32((gw[i] >> (16 * hh)) & 0xFFFFu);
-            const float u = bf16_to_f32((uw[i] >> (16 * hh)) & 0xFFFFu);
-            float d0, d1, dp;
-            act_grad(A.act, g, u, da, p, d0, d1, dp);
-            psum += dp;
-            r0 |= f32_to_bf16_bits(d0) << (16 * hh);
-            r1 |= f32_to_bf16_bits(d1) << (16 * hh);
-            ra |= (__float_as_uint(act_out(A.act, g, u, p)) >> 16) << (16 * hh);
-          }
-          o0[i] = r0;
-          o1[i] = r1;
-          oa[i] = ra;
+    const int col = 8 * (tid & 31);
+    const int64_t f = c.nrow0 + col;
+    constexpr int BATCH = 8;
+    for (int it0 = 0; it0 < 32; it0 += BATCH) {
+      uint4 gv[BATCH], uv[BATCH];
+      float pv[BATCH];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int row = (it0 + b) * 8 + (tid >> 5);
+        const bool ok = row < c.arows && f < A.ffn;
+        const int64_t grow = c.arow0 + (row < c.arows ? row : 0);
+        gv[b] = make_uint4(0, 0, 0, 0);
+        uv[b] = make_uint4(0, 0, 0, 0);
+        pv[b] = 0.0f;
+        if (ok) {
+          pv[b] = A.probs[grow];
+          gv[b] = *reinterpret_cast<const uint4*>(A.h + grow * F1 + f);
+          if (A.act == 0) uv[b] = *reinterpret_cast<const uint4*>(A.h + grow * F1 + A.ffn + f);
         }
-        *reinterpret_cast<uint4*>(A.dh + grow * F1 + f) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-        if (A.act == 0) *reinterpret_cast<uint4*>(A.dh + grow * F1 + A.ffn + f) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-        if (A.a_out) *reinterpret_cast<uint4*>(A.a_out + grow * A.ffn + f) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
       }
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) psum += __shfl_xor(psum, o, 64);
-      if ((tid & 31) == 0 && row < c.arows) A.dprob_part[(int64_t)c.nt * A.M + grow] = psum;
+      for (int b = 0; b < BATCH; ++b) {
+        const int row = (it0 + b) * 8 + (tid >> 5);
+        const bool ok = row < c.arows && f < A.ffn;
+        const int64_t grow = c.arow0 + (row < c.arows ? row : 0);
+        float psum = 0.0f;
+        if (ok) {
+          const float p = pv[b];
+          const uint4 dv = *stg(row, col);
+          const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv[b].x, gv[b].y, gv[b].z, gv[b].w},
+                         uw[4] = {uv[b].x, uv[b].y, uv[b].z, uv[b].w};
+          uint32_t o0[4], o1[4], oa[4];
+          for (int i = 0; i < 4; ++i) {
+            uint32_t r0 = 0, r1 = 0, ra = 0;
+            for (int hh = 0; hh < 2; ++hh) {
+              const float da = bf16_to_f32((dw[i] >> (16 * hh)) & 0xFFFFu);
+              const float g = bf16_to_f32((gw[i] >> (16 * hh)) & 0xFFFFu);
+              const float u = bf16_to_f32((uw[i] >> (16 * hh)) & 0xFFFFu);
+              float d0, d1, dp;
+              act_grad(A.act, g, u, da, p, d0, d1, dp);
+              psum += dp;
+              r0 |= f32_to_bf16_bits(d0) << (16 * hh);
+              r1 |= f32_to_bf16_bits(d1) << (16 * hh);
+              ra |= (__float_as_uint(act_out(A.act, g, u, p)) >> 16) << (16 * hh);
+            }
+            o0[i] = r0;
+            o1[i] = r1;
+            oa[i] = ra;
+          }
+          *reinterpret_cast<uint4*>(A.dh + grow * F1 + f) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+          if (A.act == 0) *reinterpret_cast<uint4*>(A.dh + grow * F1 + A.ffn + f) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+          if (A.a_out) *reinterpret_cast<uint4*>(A.a_out + grow * A.ffn + f) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+        }
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) psum += __shfl_xor(psum, o, 64);
+        if ((tid & 31) == 0 && row < c.arows) A.dprob_part[(int64_t)c.nt * A.M + grow] = psum;
+      }
     }
   }
 }

@@ -25,6 +25,18 @@ struct MxOut {
   uint32_t* col_scale_mfma;
 };
 
+// Fused activation gradient + MXFP8 cast (backward, between the fc2 dgrad and the fc1 GEMMs).
+struct DactArgs {
+  const uint16_t* da;   // [M, ffn] bf16: dy W2
+  const uint16_t* h;    // [M, F1] bf16: fc1 output ([gate | up] for SwiGLU)
+  const float* probs;   // [M]
+  int act;              // 0 SwiGLU, 1 squared ReLU
+  int64_t ffn;
+  MxOut dh;             // MXFP8 dh [M, F1], row- and/or column-wise (null pointers: not written)
+  MxOut a2;             // column-wise MXFP8 of the rebuilt fc2 input [M, ffn], or all null
+  float* dprob_part;    // [ffn / 128][M]
+};
+
 struct NvOut {
   uint8_t* row_data;
   uint8_t* row_scale;
@@ -36,6 +48,7 @@ hipError_t launch_scan(const int32_t* m_splits, int G, int64_t M, SplitTables T,
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 hipError_t launch_mxfp8_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
                               bool row, bool col, MxOut o, hipStream_t s);
+hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M, hipStream_t s);
 hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
                                 uint32_t mask, float* pre, float* post, hipStream_t s);
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,

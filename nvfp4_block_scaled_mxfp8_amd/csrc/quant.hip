@@ -15,6 +15,7 @@
 // parks them in LDS; the column pass reads one feature column per lane (a wave
 // reads 128 contiguous bytes per token: conflict-free) and writes 64 contiguous
 // tokens per lane.
+#include "activation.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -157,6 +158,48 @@ __device__ __forceinline__ uint32_t mx_block(const float* v, uint32_t* w) {
   return code;
 }
 
+// Column-wise MXFP8 cast of a parked bf16 tile [QT tokens][LDW] whose features are features
+// kf0 .. kf0 + kcols of a K-feature tensor: thread -> (feature c = tid % 128, tokens
+// 64 half .. 64 half + 63 = two 32-token blocks).  The group's [K, P_g] column-wise tensor is
+// stored in 64-byte token panels: byte (f, t) at ((t / 64) K + f) 64 + t % 64, and the tile's
+// 64 tokens of one half are one panel row.  All threads of the block must call it.
+__device__ __forceinline__ void col_cast_tile(const uint16_t* tile, const TileInfo& ti, int64_t K, int64_t kf0,
+                                              int kcols, const SplitTables& T, const MxOut& o, uint32_t* colcodes,
+                                              int tid) {
+  const int c = tid & (QF - 1);
+  const int half = tid >> 7;                       // tokens [64*half, 64*half + 64)
+  const int P = (ti.m + 127) & ~127;
+  const int rowsP = min(QT, P - ti.t0);            // tile tokens inside the group's padding
+  const int64_t colbase = K * (int64_t)T.col_off[ti.g];
+  uint32_t codes[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cb = 2 * half + j;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(tile[(32 * cb + i) * LDW + c]);
+    uint32_t w[8];
+    const uint32_t code = mx_block(v, w);
+    const bool inpad = 32 * cb < rowsP;
+    if (inpad && c < kcols) {
+      uint4* dst = reinterpret_cast<uint4*>(o.col_data + colbase + (((ti.t0 / 64) + half) * K + kf0 + c) * 64 + 32 * j);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      if (o.col_scale) o.col_scale[colbase / 32 + (kf0 + c) * (P / 32) + ti.t0 / 32 + cb] = (uint8_t)code;
+    }
+    codes[j] = inpad ? code : 127u;
+  }
+  if (o.col_scale_mfma) {
+    colcodes[half * QF + c] = codes[0] | (codes[1] << 8);
+    __syncthreads();
+    if (tid < QF && c < kcols) {
+      const uint32_t word = colcodes[c] | (colcodes[QF + c] << 16);
+      o.col_scale_mfma[K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K + kf0 + c] = word;
+    }
+    __syncthreads();                               // colcodes may be reused by the caller
+  }
+}
+
 // ----------------------------------------------------------------------------- MXFP8 cast
 template <bool ROW, bool COL>
 __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
@@ -204,39 +247,129 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __rest
   }
   if (!COL) return;
   __syncthreads();
-  const int c = tid & (QF - 1);
-  const int half = tid >> 7;                       // tokens [64*half, 64*half + 64)
-  const int P = (ti.m + 127) & ~127;
-  const int rowsP = min(QT, P - ti.t0);            // tile tokens inside the group's padding
-  const int64_t colbase = K * (int64_t)T.col_off[ti.g];
-  uint32_t codes[2];
+  col_cast_tile(tile, ti, K, ti.k0, ti.kcols, T, o, colcodes, tid);
+}
+
+// ----------------------------------------------------------------------------- fused activation gradient + MXFP8 cast
+// One pass of the backward between the fc2 dgrad and the fc1 GEMMs: from da = dy W2 (bf16
+// [M, ffn]), h = fc1 output (bf16 [M, F1]) and the routing probabilities, it forms
+// dh = bf16(d(act(h) p)/dh . da) and casts it row-wise (fc1 dgrad) and column-wise (fc1
+// wgrad) to MXFP8 without writing dh itself; the per-row dL/dp partial sums of the tile's 128
+// features go to dprob_part[blockIdx.y][row]; with a2 set it also rebuilds the fc2 input
+// a = bf16(act(h) p) and casts it column-wise (fc2 wgrad with activation recompute).
+// Tile = 128 tokens x 128 of the ffn features; for SwiGLU the gate and up gradients of those
+// features are dh columns f and ffn + f.
+template <bool SWIGLU, bool WANT_A>
+__global__ __launch_bounds__(256, 2) void dact_quant_kernel(DactArgs D, SplitTables T, int G, int64_t M) {
+  constexpr int NT = 1 + (SWIGLU ? 1 : 0) + (WANT_A ? 1 : 0);   // parked tiles: dgate (dh), dup, a
+  __shared__ __align__(16) uint16_t tiles[NT][QT * LDW];
+  __shared__ uint32_t colcodes[2 * QF];
+  const int64_t ffn = D.ffn;
+  const int64_t F1 = SWIGLU ? 2 * ffn : ffn;
+  TileInfo ti;
+  if (!tile_info(T, G, ffn, ti)) return;
+  const int tid = threadIdx.x;
+  // thread -> rows r4 and 64 + r4 of the tile, features 32 q .. 32 q + 31
+  const int r4 = tid >> 2;
+  const int q = tid & 3;
+  uint4 qd[2][4], qg[2][4], qu[2][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int cb = 2 * half + j;
-    float v[32];
+  for (int ps = 0; ps < 2; ++ps) {
+    const int r = 64 * ps + r4;
+    const bool ok = r < ti.rows;
+    const int64_t row = ti.gstart + ti.t0 + r;
+    const uint4* sd = reinterpret_cast<const uint4*>(D.da + row * ffn + ti.k0 + 32 * q);
+    const uint4* sg = reinterpret_cast<const uint4*>(D.h + row * F1 + ti.k0 + 32 * q);
+    const uint4* su = reinterpret_cast<const uint4*>(D.h + row * F1 + ffn + ti.k0 + 32 * q);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(tile[(32 * cb + i) * LDW + c]);
-    uint32_t w[8];
-    const uint32_t code = mx_block(v, w);
-    const bool inpad = 32 * cb < rowsP;
-    if (inpad && c < ti.kcols) {
-      // the group's [K, P] column-wise tensor in 64-byte token panels: byte (f, t) at
-      // ((t / 64) K + f) 64 + t % 64; tokens 64 half .. 64 half + 63 of the tile are one panel row
-      uint4* dst = reinterpret_cast<uint4*>(o.col_data + colbase + (((ti.t0 / 64) + half) * K + ti.k0 + c) * 64 + 32 * j);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      if (o.col_scale) o.col_scale[colbase / 32 + (ti.k0 + c) * (P / 32) + ti.t0 / 32 + cb] = (uint8_t)code;
-    }
-    codes[j] = inpad ? code : 127u;
-  }
-  if (o.col_scale_mfma) {
-    colcodes[half * QF + c] = codes[0] | (codes[1] << 8);
-    __syncthreads();
-    if (tid < QF && c < ti.kcols) {
-      const uint32_t word = colcodes[c] | (colcodes[QF + c] << 16);
-      o.col_scale_mfma[K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K + ti.k0 + c] = word;
+    for (int j = 0; j < 4; ++j) {
+      qd[ps][j] = ok ? sd[j] : make_uint4(0, 0, 0, 0);
+      qg[ps][j] = ok ? sg[j] : make_uint4(0, 0, 0, 0);
+      qu[ps][j] = (SWIGLU && ok) ? su[j] : make_uint4(0, 0, 0, 0);
     }
   }
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    const int r = 64 * ps + r4;
+    const bool ok = r < ti.rows;
+    const int64_t grow = ti.gstart + ti.t0 + (ok ? r : 0);
+    const float p = ok ? D.probs[grow] : 0.0f;
+    // bf16 results, two per word: dgate (or dh), dup, rebuilt a
+    uint32_t p0[16], p1[16], pa[16];
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float vd[8], vg[8], vu[8];
+      unpack8(qd[ps][j], vd);
+      unpack8(qg[ps][j], vg);
+      unpack8(qu[ps][j], vu);
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        uint32_t w0 = 0, w1 = 0, wa = 0;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          float a0, a1, dp, av = 0.0f;
+          const float u = SWIGLU ? vu[i + k] : 0.0f;
+          if (WANT_A) act_grad_out(SWIGLU ? 0 : 1, vg[i + k], u, vd[i + k], p, a0, a1, dp, av);
+          else act_grad(SWIGLU ? 0 : 1, vg[i + k], u, vd[i + k], p, a0, a1, dp);
+          psum += dp;
+          w0 |= f32_to_bf16_bits(a0) << (16 * k);
+          w1 |= f32_to_bf16_bits(a1) << (16 * k);
+          wa |= (__float_as_uint(av) >> 16) << (16 * k);
+        }
+        p0[4 * j + i / 2] = w0;
+        p1[4 * j + i / 2] = w1;
+        pa[4 * j + i / 2] = wa;
+      }
+    }
+    // dL/dp partial of the row over the tile's 128 features (fixed order: pairs, then halves)
+    psum += __shfl_xor(psum, 1, 64);
+    psum += __shfl_xor(psum, 2, 64);
+    if (q == 0 && ok) D.dprob_part[(int64_t)blockIdx.y * M + grow] = psum;
+    // row-wise cast of one 32-block (gate / plain gradient at feature f, up at ffn + f), and
+    // the values parked for the column pass
+    auto row_cast = [&](const uint32_t* pk, int64_t f, uint16_t* tile) {
+      if (D.dh.row_data) {
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          v[2 * i] = bf16_to_f32(pk[i] & 0xFFFFu);
+          v[2 * i + 1] = bf16_to_f32(pk[i] >> 16);
+        }
+        uint32_t w[8];
+        const uint32_t code = mx_block(v, w);
+        if (ok) {
+          uint4* dst = reinterpret_cast<uint4*>(D.dh.row_data + (f / 64) * 64 * M + grow * 64 + 32 * (q & 1));
+          dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+          if (D.dh.row_scale) D.dh.row_scale[grow * (F1 / 32) + f / 32] = (uint8_t)code;
+        }
+        // the 128-feature word: byte q from thread q of the row's four
+        uint32_t word = code << (8 * q);
+        word |= (uint32_t)__shfl_xor((int)word, 1, 64);
+        word |= (uint32_t)__shfl_xor((int)word, 2, 64);
+        if (D.dh.row_scale_mfma && q == 0 && ok) D.dh.row_scale_mfma[(f / 128) * M + grow] = word;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(tile + r * LDW + 32 * q + 8 * j) =
+            make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
+    };
+    row_cast(p0, ti.k0 + 32 * q, tiles[0]);
+    if (SWIGLU) row_cast(p1, ffn + ti.k0 + 32 * q, tiles[1]);
+    if (WANT_A) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(tiles[NT - 1] + r * LDW + 32 * q + 8 * j) =
+            make_uint4(pa[4 * j], pa[4 * j + 1], pa[4 * j + 2], pa[4 * j + 3]);
+    }
+  }
+  __syncthreads();
+  if (D.dh.col_data) {
+    col_cast_tile(tiles[0], ti, F1, ti.k0, QF, T, D.dh, colcodes, tid);
+    if (SWIGLU) col_cast_tile(tiles[1], ti, F1, ffn + ti.k0, QF, T, D.dh, colcodes, tid);
+  }
+  if (WANT_A) col_cast_tile(tiles[NT - 1], ti, ffn, ti.k0, QF, T, D.a2, colcodes, tid);
 }
 
 // ----------------------------------------------------------------------------- signed Hadamard
@@ -434,6 +567,17 @@ hipError_t launch_mxfp8_quant(const uint16_t* x, int64_t M, int64_t K, SplitTabl
   if (row && col) hipLaunchKernelGGL((mxfp8_quant_kernel<true, true>), grid, dim3(256), 0, s, x, M, K, T, G, o);
   else if (row) hipLaunchKernelGGL((mxfp8_quant_kernel<true, false>), grid, dim3(256), 0, s, x, M, K, T, G, o);
   else hipLaunchKernelGGL((mxfp8_quant_kernel<false, true>), grid, dim3(256), 0, s, x, M, K, T, G, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid = tile_grid(M, d.ffn, G);
+  const bool a = d.a2.col_data != nullptr;
+  if (d.act == 0 && !a) hipLaunchKernelGGL((dact_quant_kernel<true, false>), grid, dim3(256), 0, s, d, T, G, M);
+  else if (d.act == 0) hipLaunchKernelGGL((dact_quant_kernel<true, true>), grid, dim3(256), 0, s, d, T, G, M);
+  else if (!a) hipLaunchKernelGGL((dact_quant_kernel<false, false>), grid, dim3(256), 0, s, d, T, G, M);
+  else hipLaunchKernelGGL((dact_quant_kernel<false, true>), grid, dim3(256), 0, s, d, T, G, M);
   return hipGetLastError();
 }
 
