@@ -138,6 +138,9 @@ gmlp_status check_dims(int64_t M, int64_t K, int G) {
   if (M < 0) return fail(GMLP_INVALID_ARG, "dims: M must be >= 0, got %lld", (long long)M);
   if (K <= 0 || K % 32 != 0) return fail(GMLP_UNSUPPORTED, "dims: K must be a positive multiple of 32, got %lld", (long long)K);
   if (M + 127LL * G > (1LL << 30)) return fail(GMLP_UNSUPPORTED, "dims: M = %lld rows is too large", (long long)M);
+  // one launch covers every 128-row tile of every group along the grid's y dimension
+  if ((M + 127) / 128 + G > 65535)
+    return fail(GMLP_UNSUPPORTED, "dims: M = %lld rows in %d groups exceeds one launch's tile range", (long long)M, G);
   return GMLP_OK;
 }
 

@@ -25,6 +25,13 @@ constexpr int QT = 128;          // tokens per tile
 constexpr int QF = 128;          // features per tile
 constexpr int LDW = QF + 8;      // LDS row stride (bf16): +16 bytes keeps the 16-byte writes conflict-free
 
+// Parked MXFP8 tiles: element (token r, feature c) at r LDW + (c ^ 32 ((r / 16) % 4)).  The
+// column pass reads 16-token runs of 16 features with four runs 16 tokens apart in one
+// instruction; 16 rows are a whole number of bank lines, so without the XOR the four runs
+// would share banks.  The XOR moves them to four different 64-byte windows and keeps every
+// 8-feature group (one 16-byte store) contiguous.
+__device__ __forceinline__ int tile_off(int r, int c) { return r * LDW + (c ^ (((r >> 4) & 3) << 5)); }
+
 // ----------------------------------------------------------------------------- split scan
 __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ m_splits, int G, int64_t M,
                                                    SplitTables T) {
@@ -106,14 +113,14 @@ struct TileInfo {
 };
 
 __device__ __forceinline__ bool tile_info(const SplitTables& T, int G, int64_t K, TileInfo& ti) {
-  const int tt = blockIdx.x;
+  const int tt = blockIdx.y;
   if (G <= 0 || tt >= T.t128_off[G]) return false;
   ti.g = find_group(T.t128_off, G, tt);
   ti.gstart = T.row_off[ti.g];
   ti.m = T.row_off[ti.g + 1] - (int)ti.gstart;
   ti.t0 = (tt - T.t128_off[ti.g]) * QT;
   ti.rows = min(QT, ti.m - ti.t0);
-  ti.k0 = (int64_t)blockIdx.y * QF;
+  ti.k0 = (int64_t)blockIdx.x * QF;
   ti.kcols = (int)min((int64_t)QF, K - ti.k0);
   return ti.rows > 0;
 }
@@ -159,95 +166,126 @@ __device__ __forceinline__ uint32_t mx_block(const float* v, uint32_t* w) {
 }
 
 // Column-wise MXFP8 cast of a parked bf16 tile [QT tokens][LDW] whose features are features
-// kf0 .. kf0 + kcols of a K-feature tensor: thread -> (feature c = tid % 128, tokens
-// 64 half .. 64 half + 63 = two 32-token blocks).  The group's [K, P_g] column-wise tensor is
-// stored in 64-byte token panels: byte (f, t) at ((t / 64) K + f) 64 + t % 64, and the tile's
-// 64 tokens of one half are one panel row.  All threads of the block must call it.
+// kf0 .. kf0 + kcols of a K-feature tensor.  The group's [K, P_g] column-wise tensor is stored
+// in 64-byte token panels: byte (f, t) at ((t / 64) K + f) 64 + t % 64, so the tile holds two
+// panel rows (token halves) per feature.  Task u = 256 k + tid (k = 0..3) -> feature
+// c = (u / 4) % 128, token half u / 512, 16-token part p = u % 4: a 32-token block spans the
+// lane pair p = 0, 1 or 2, 3 (amax by one shuffle), and the 64 lanes of a wave store 16 whole
+// panel rows = 1 KB of contiguous memory per instruction.  A thread holds both halves of its
+// features (k and k + 2), so it assembles the MFMA scale word (4 blocks of 128 tokens) with one
+// more shuffle.
 __device__ __forceinline__ void col_cast_tile(const uint16_t* tile, const TileInfo& ti, int64_t K, int64_t kf0,
-                                              int kcols, const SplitTables& T, const MxOut& o, uint32_t* colcodes,
-                                              int tid) {
-  const int c = tid & (QF - 1);
-  const int half = tid >> 7;                       // tokens [64*half, 64*half + 64)
+                                              int kcols, const SplitTables& T, const MxOut& o, int tid) {
+  const int p = tid & 3;
   const int P = (ti.m + 127) & ~127;
   const int rowsP = min(QT, P - ti.t0);            // tile tokens inside the group's padding
   const int64_t colbase = K * (int64_t)T.col_off[ti.g];
-  uint32_t codes[2];
+  uint32_t word[2] = {0, 0};                       // features tid / 4 and 64 + tid / 4
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int cb = 2 * half + j;
-    float v[32];
+  for (int k = 0; k < 4; ++k) {
+    const int c = (64 * k + (tid >> 2)) & (QF - 1);
+    const int half = k >> 1;
+    const int tok0 = 64 * half + 16 * p;
+    float v[16];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(tile[(32 * cb + i) * LDW + c]);
-    uint32_t w[8];
-    const uint32_t code = mx_block(v, w);
-    const bool inpad = 32 * cb < rowsP;
+    for (int i = 0; i < 16; ++i) v[i] = bf16_to_f32(tile[tile_off(tok0 + i, c)]);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    const uint32_t code = e8m0_code(amax);
+    const float inv = e8m0_inv_scale(code);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = cvt_e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
+    const bool inpad = tok0 < rowsP;
     if (inpad && c < kcols) {
-      uint4* dst = reinterpret_cast<uint4*>(o.col_data + colbase + (((ti.t0 / 64) + half) * K + kf0 + c) * 64 + 32 * j);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      if (o.col_scale) o.col_scale[colbase / 32 + (kf0 + c) * (P / 32) + ti.t0 / 32 + cb] = (uint8_t)code;
+      __builtin_nontemporal_store(v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
+                                  reinterpret_cast<v4i*>(o.col_data + colbase + (((ti.t0 / 64) + half) * K + kf0 + c) * 64 + 16 * p));
+      if (o.col_scale && (p & 1) == 0)
+        o.col_scale[colbase / 32 + (kf0 + c) * (P / 32) + ti.t0 / 32 + 2 * half + (p >> 1)] = (uint8_t)code;
     }
-    codes[j] = inpad ? code : 127u;
+    word[k & 1] |= (inpad ? code : 127u) << (8 * (2 * half + (p >> 1)));
   }
   if (o.col_scale_mfma) {
-    colcodes[half * QF + c] = codes[0] | (codes[1] << 8);
-    __syncthreads();
-    if (tid < QF && c < kcols) {
-      const uint32_t word = colcodes[c] | (colcodes[QF + c] << 16);
-      o.col_scale_mfma[K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K + kf0 + c] = word;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t full = word[h] | (uint32_t)__shfl_xor((int)word[h], 2, 64);
+      const int c = 64 * h + (tid >> 2);
+      if (p == 0 && c < kcols)
+        o.col_scale_mfma[K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K + kf0 + c] = full;
     }
-    __syncthreads();                               // colcodes may be reused by the caller
   }
 }
 
 // ----------------------------------------------------------------------------- MXFP8 cast
+// Loads and the row-wise cast: wave w, load i (0..7), lane l -> tile row 32 w + 4 i + l / 16,
+// features 8 (l % 16) .. + 7, so every load instruction reads four whole 256-byte row segments.
+// A 32-feature block is the lane quad l % 16 in {4b .. 4b + 3} (amax by two shuffles); each
+// lane stores its 8 codes into the row's panel, and the 16 lanes of a row assemble its MFMA
+// scale word.
 template <bool ROW, bool COL>
 __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                           SplitTables T, int G, MxOut o) {
   __shared__ __align__(16) uint16_t tile[COL ? QT * LDW : 8];
-  __shared__ uint32_t colcodes[COL ? 2 * QF : 1];
   TileInfo ti;
   if (!tile_info(T, G, K, ti)) return;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ch = lane & 15;
+  const int kc = 8 * ch;
+  const bool kok = kc < ti.kcols;
   uint4 q[8];
-  load_row_chunk(x, K, ti, tid, q, COL ? tile : nullptr);
-
-  if (ROW) {
-    const int r = tid >> 1;
-    const int c0 = 64 * (tid & 1);
-    const int64_t grow = ti.gstart + ti.t0 + r;
-    uint32_t codes[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float v[32];
+  for (int i = 0; i < 8; ++i) {
+    const int r = 32 * wave + 4 * i + (lane >> 4);
+    const bool ok = r < ti.rows && kok;
+    q[i] = ok ? *reinterpret_cast<const uint4*>(x + (ti.gstart + ti.t0 + r) * K + ti.k0 + kc) : make_uint4(0, 0, 0, 0);
+  }
+  if (COL) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) unpack8(q[4 * b + j], v + 8 * j);
-      uint32_t w[8];
-      const uint32_t code = mx_block(v, w);
-      const bool ok = (r < ti.rows) && (c0 + 32 * b < ti.kcols);
-      if (ok) {
-        // 64-byte K panels: panel p = k / 64 holds features [64 p, 64 p + w), w = min(64, K - 64 p),
-        // as M rows of w bytes at 64 p M; this thread's (up to) 64 features are one panel row
-        const int64_t pn = (ti.k0 + c0) / 64;
-        const int64_t pw = min((int64_t)64, K - 64 * pn);
-        uint4* dst = reinterpret_cast<uint4*>(o.row_data + 64 * pn * M + grow * pw + 32 * b);
-        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        if (o.row_scale) o.row_scale[grow * (K / 32) + (ti.k0 + c0) / 32 + b] = (uint8_t)code;
-      }
-      codes[b] = (c0 + 32 * b < ti.kcols) ? code : 127u;
+    for (int i = 0; i < 8; ++i) {
+      const int r = 32 * wave + 4 * i + (lane >> 4);
+      *reinterpret_cast<uint4*>(tile + tile_off(r, kc)) = q[i];
     }
-    if (o.row_scale_mfma) {
-      // word = blocks 0..3 of this row's 128 features: lanes 2r' and 2r'+1 of the wave hold 2 each
-      const uint32_t mine = codes[0] | (codes[1] << 8);
-      const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
-      if ((tid & 1) == 0 && r < ti.rows)
-        o.row_scale_mfma[(ti.k0 / 128) * M + grow] = mine | (other << 16);
+  }
+  if (ROW) {
+    const int64_t f = ti.k0 + kc;
+    const int64_t pn = f / 64;
+    const int64_t pw = min((int64_t)64, K - 64 * pn);    // width of the (last, maybe narrower) panel
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 32 * wave + 4 * i + (lane >> 4);
+      const int64_t grow = ti.gstart + ti.t0 + r;
+      float v[8];
+      unpack8(q[i], v);
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      const uint32_t code = e8m0_code(amax);
+      const float inv = e8m0_inv_scale(code);
+      const uint32_t w0 = cvt_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      const uint32_t w1 = cvt_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+      const bool ok = r < ti.rows && kok;
+      if (ok) {
+        __builtin_nontemporal_store((uint64_t)w0 | ((uint64_t)w1 << 32),
+                                    reinterpret_cast<uint64_t*>(o.row_data + 64 * pn * M + grow * pw + (f - 64 * pn)));
+        if (o.row_scale && (ch & 3) == 0) o.row_scale[grow * (K / 32) + f / 32] = (uint8_t)code;
+      }
+      if (o.row_scale_mfma) {
+        // byte b of the row's word = block b of its 128 features (127 for blocks past K)
+        uint32_t word = (kok ? code : 127u) << (8 * (ch >> 2));
+        word |= (uint32_t)__shfl_xor((int)word, 4, 64);
+        word |= (uint32_t)__shfl_xor((int)word, 8, 64);
+        if (ch == 0 && r < ti.rows) o.row_scale_mfma[(ti.k0 / 128) * M + grow] = word;
+      }
     }
   }
   if (!COL) return;
   __syncthreads();
-  col_cast_tile(tile, ti, K, ti.k0, ti.kcols, T, o, colcodes, tid);
+  col_cast_tile(tile, ti, K, ti.k0, ti.kcols, T, o, tid);
 }
 
 // ----------------------------------------------------------------------------- fused activation gradient + MXFP8 cast
@@ -255,7 +293,7 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __rest
 // [M, ffn]), h = fc1 output (bf16 [M, F1]) and the routing probabilities, it forms
 // dh = bf16(d(act(h) p)/dh . da) and casts it row-wise (fc1 dgrad) and column-wise (fc1
 // wgrad) to MXFP8 without writing dh itself; the per-row dL/dp partial sums of the tile's 128
-// features go to dprob_part[blockIdx.y][row]; with a2 set it also rebuilds the fc2 input
+// features go to dprob_part[feature tile][row]; with a2 set it also rebuilds the fc2 input
 // a = bf16(act(h) p) and casts it column-wise (fc2 wgrad with activation recompute).
 // Tile = 128 tokens x 128 of the ffn features; for SwiGLU the gate and up gradients of those
 // features are dh columns f and ffn + f.
@@ -263,7 +301,6 @@ template <bool SWIGLU, bool WANT_A>
 __global__ __launch_bounds__(256, 2) void dact_quant_kernel(DactArgs D, SplitTables T, int G, int64_t M) {
   constexpr int NT = 1 + (SWIGLU ? 1 : 0) + (WANT_A ? 1 : 0);   // parked tiles: dgate (dh), dup, a
   __shared__ __align__(16) uint16_t tiles[NT][QT * LDW];
-  __shared__ uint32_t colcodes[2 * QF];
   const int64_t ffn = D.ffn;
   const int64_t F1 = SWIGLU ? 2 * ffn : ffn;
   TileInfo ti;
@@ -325,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void dact_quant_kernel(DactArgs D, SplitTab
     // dL/dp partial of the row over the tile's 128 features (fixed order: pairs, then halves)
     psum += __shfl_xor(psum, 1, 64);
     psum += __shfl_xor(psum, 2, 64);
-    if (q == 0 && ok) D.dprob_part[(int64_t)blockIdx.y * M + grow] = psum;
+    if (q == 0 && ok) D.dprob_part[(int64_t)blockIdx.x * M + grow] = psum;
     // row-wise cast of one 32-block (gate / plain gradient at feature f, up at ffn + f), and
     // the values parked for the column pass
     auto row_cast = [&](const uint32_t* pk, int64_t f, uint16_t* tile) {
@@ -352,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void dact_quant_kernel(DactArgs D, SplitTab
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(tile + r * LDW + 32 * q + 8 * j) =
+        *reinterpret_cast<uint4*>(tile + tile_off(r, 32 * q + 8 * j)) =
             make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
     };
     row_cast(p0, ti.k0 + 32 * q, tiles[0]);
@@ -360,16 +397,16 @@ __global__ __launch_bounds__(256, 2) void dact_quant_kernel(DactArgs D, SplitTab
     if (WANT_A) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(tiles[NT - 1] + r * LDW + 32 * q + 8 * j) =
+        *reinterpret_cast<uint4*>(tiles[NT - 1] + tile_off(r, 32 * q + 8 * j)) =
             make_uint4(pa[4 * j], pa[4 * j + 1], pa[4 * j + 2], pa[4 * j + 3]);
     }
   }
   __syncthreads();
   if (D.dh.col_data) {
-    col_cast_tile(tiles[0], ti, F1, ti.k0, QF, T, D.dh, colcodes, tid);
-    if (SWIGLU) col_cast_tile(tiles[1], ti, F1, ffn + ti.k0, QF, T, D.dh, colcodes, tid);
+    col_cast_tile(tiles[0], ti, F1, ti.k0, QF, T, D.dh, tid);
+    if (SWIGLU) col_cast_tile(tiles[1], ti, F1, ffn + ti.k0, QF, T, D.dh, tid);
   }
-  if (WANT_A) col_cast_tile(tiles[NT - 1], ti, ffn, ti.k0, QF, T, D.a2, colcodes, tid);
+  if (WANT_A) col_cast_tile(tiles[NT - 1], ti, ffn, ti.k0, QF, T, D.a2, tid);
 }
 
 // ----------------------------------------------------------------------------- signed Hadamard
@@ -544,8 +581,10 @@ __global__ __launch_bounds__(256) void gather_weights_kernel(const void* const* 
 }
 
 // ----------------------------------------------------------------------------- launchers
+// x: feature tiles (consecutive workgroups write neighbouring panel rows of the column-wise
+// output and read neighbouring 256-byte row segments), y: token tiles.
 static dim3 tile_grid(int64_t M, int64_t K, int G) {
-  return dim3((unsigned)((M + QT - 1) / QT + G), (unsigned)((K + QF - 1) / QF));
+  return dim3((unsigned)((K + QF - 1) / QF), (unsigned)((M + QT - 1) / QT + G));
 }
 
 hipError_t launch_scan(const int32_t* m_splits, int G, int64_t M, SplitTables T, hipStream_t s) {
