@@ -31,6 +31,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace gmlp {
 
 constexpr int BM = 256, BN = 256;
@@ -64,6 +66,13 @@ __device__ __forceinline__ int64_t uni(int64_t v) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
   return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+// A copy of a uniform value that the compiler cannot see through: derived addresses are then
+// computed where they are used instead of being hoisted out of the tile loop (where they
+// would stay live, and spill, across the whole main loop).
+__device__ __forceinline__ int64_t opaque(int64_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
 }
 template <class T>
 __device__ __forceinline__ T* uni_ptr(T* p) { return reinterpret_cast<T*>(uni((int64_t)reinterpret_cast<uintptr_t>(p))); }
@@ -139,6 +148,14 @@ __device__ __forceinline__ void dma16(const Rsrc& r, uint32_t voff, const uint8_
                :: "v"(voff), "s"(r.w), "s"(__builtin_amdgcn_readfirstlane(m0)) : "memory");
 }
 
+// The same with an instruction offset, which moves the global and the LDS address alike: the
+// four 1 KB instructions of one 64-row band share one M0 and one lane offset.
+template <int OFF>
+__device__ __forceinline__ void dma16_at(const Rsrc& r, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds"
+               :: "v"(voff), "s"(r.w), "s"(m0), "i"(OFF) : "memory");
+}
+
 // s_waitcnt with only the vector-memory counter: vmcnt <= n (expcnt, lgkmcnt untouched).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -198,7 +215,14 @@ struct StageDma {
   uint32_t s_voff;
   uint8_t* lds;          // the stage's slot
   uint32_t s_lds;        // scale-word destination offset in the slot
+  uint32_t m0a, m0b, m0s;  // LDS destinations (M0) of this wave's A band, B band and scale words
 };
+__device__ __forceinline__ void stage_m0(StageDma& s, int wave) {
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)s.lds);
+  s.m0a = base + 4096u * (uint32_t)wave;
+  s.m0b = base + MX_OPB + 4096u * (uint32_t)wave;
+  s.m0s = base + s.s_lds;
+}
 
 template <int MODE, int EPI>
 __device__ __forceinline__ StageDma mx_stage_plan(const GemmArgs& A, const Ctx& c, const DmaPlan& d, int kt,
@@ -226,6 +250,138 @@ __device__ __forceinline__ StageDma mx_stage_plan(const GemmArgs& A, const Ctx& 
   s.rs = make_rsrc(is_b ? b_w : a_w, live ? (is_b ? b_n : a_n) : 0);
   s.s_voff = is_b ? b_voff : 16u * lane;
   s.s_lds = MX_SC_OFF + (is_b ? 1024 : 0);
+  stage_m0(s, wave);
+  return s;
+}
+
+// A tile of the persistent kernel, reduced to what fixes its DMA sources and its epilogue.
+struct TileRef {
+  int32_t nk;                // 64-K stages; 0: no tile
+  int32_t arows;             // valid A rows in the tile
+  int64_t arow0;             // FPROP: first global row; WGRAD: first A feature row
+  int32_t g, nt;             // expert / group, n-tile
+  int32_t off, woff;         // WGRAD: the group's padded token offset and 128-token word offset
+};
+
+// Field-wise uniform select (keeps both operands in scalar registers).
+__device__ __forceinline__ TileRef sel_ref(bool c, const TileRef& a, const TileRef& b) {
+  TileRef r;
+  r.nk = c ? a.nk : b.nk;
+  r.arows = c ? a.arows : b.arows;
+  r.arow0 = c ? a.arow0 : b.arow0;
+  r.g = c ? a.g : b.g;
+  r.nt = c ? a.nt : b.nt;
+  r.off = c ? a.off : b.off;
+  r.woff = c ? a.woff : b.woff;
+  return r;
+}
+
+// The per-wave DMA sources of a tile, as 32-bit offsets from the operands' bases (the launch
+// keeps every operand below 4 GB): six scalars, so that three of them fit the scalar registers.
+struct DmaTile {
+  uint32_t a_off, b_off;     // bytes: this wave's A / B band in panel 0
+  uint32_t s_off;            // words: this wave's scale words (A or B rows) of the first 128-K word
+  uint32_t ab_bytes;         // resource ranges of the A and B bands (low / high 16 bits)
+  uint32_t s_bytes;          // resource range of the scale words
+  int32_t nk;                // 64-K stages; 0: no tile
+};
+// Per-launch constants of the DMA sources.
+struct DmaConst {
+  const uint8_t* a;          // operand bases
+  const uint8_t* b;
+  const uint32_t* s;         // this wave's scale-word base (A or B)
+  uint32_t a_ps, b_ps;       // bytes per 64-K panel
+  uint32_t s_ld;             // words per 128-K word
+};
+
+// Field-wise uniform select (scalar selects, no branch).
+__device__ __forceinline__ DmaTile sel_tile(bool c, const DmaTile& a, const DmaTile& b) {
+  DmaTile r;
+  r.a_off = c ? a.a_off : b.a_off;
+  r.b_off = c ? a.b_off : b.b_off;
+  r.s_off = c ? a.s_off : b.s_off;
+  r.ab_bytes = c ? a.ab_bytes : b.ab_bytes;
+  r.s_bytes = c ? a.s_bytes : b.s_bytes;
+  r.nk = c ? a.nk : b.nk;
+  return r;
+}
+
+template <int MODE, int EPI>
+__device__ __forceinline__ DmaConst dma_const(const GemmArgs& A, int wave) {
+  DmaConst k;
+  const bool swiglu = MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0;
+  k.a = A.a.data;
+  k.b = A.b.data;
+  k.s = (wave & 1) ? A.b.scale_mfma : A.a.scale_mfma;
+  if (MODE == MODE_FPROP) {
+    const int64_t brows = swiglu ? 2 * A.ffn : A.N;
+    k.a_ps = (uint32_t)(A.M * 64);
+    k.b_ps = (uint32_t)(brows * 64);
+    k.s_ld = (uint32_t)((wave & 1) ? brows : A.M);
+  } else {
+    k.a_ps = (uint32_t)(A.N * 64);
+    k.b_ps = (uint32_t)(A.K * 64);
+    k.s_ld = (uint32_t)((wave & 1) ? A.K : A.N);
+  }
+  return k;
+}
+
+template <int MODE, int EPI>
+__device__ __forceinline__ DmaTile dma_tile(const GemmArgs& A, const TileRef& r, int wave) {
+  DmaTile t;
+  const bool swiglu = MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0;
+  const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
+  int64_t b_first, b_rows;
+  if (swiglu) {
+    const int64_t f = (int64_t)r.nt * 128 + 64 * (wave >> 1);
+    b_first = ((wave & 1) ? A.ffn : 0) + f;
+    b_rows = min((int64_t)64, max((int64_t)0, A.ffn - f));
+  } else {
+    b_first = (int64_t)r.nt * BN + 64 * wave;
+    b_rows = min((int64_t)64, max((int64_t)0, nb - b_first));
+  }
+  const int64_t a_rows = min(64, max(0, r.arows - 64 * wave));
+  int64_t a_base, b_base, a_sw, b_sw;
+  if (MODE == MODE_FPROP) {
+    const int64_t brows = swiglu ? 2 * A.ffn : A.N;
+    a_base = 0;
+    a_sw = 0;
+    b_base = (int64_t)r.g * brows * A.K;
+    b_sw = (int64_t)r.g * ((A.K + 127) / 128) * brows;
+  } else {
+    a_base = A.N * (int64_t)r.off;
+    a_sw = A.N * (int64_t)r.woff;
+    b_base = A.K * (int64_t)r.off;
+    b_sw = A.K * (int64_t)r.woff;
+  }
+  t.a_off = (uint32_t)(a_base + (r.arow0 + 64 * wave) * 64);
+  t.b_off = (uint32_t)(b_base + b_first * 64);
+  t.ab_bytes = (uint32_t)(a_rows * 64) | ((uint32_t)(b_rows * 64) << 16);
+  if ((wave & 1) == 0) {
+    t.s_off = (uint32_t)(a_sw + r.arow0);
+    t.s_bytes = (uint32_t)(4 * r.arows);
+  } else {
+    const int64_t f0 = (int64_t)r.nt * 128;
+    const int64_t n0 = (int64_t)r.nt * BN;
+    t.s_off = (uint32_t)(b_sw + (swiglu ? f0 : n0));
+    t.s_bytes = (uint32_t)(swiglu ? 4 * (2 * A.ffn - f0) : 4 * max((int64_t)0, nb - n0));
+  }
+  t.nk = r.nk;
+  return t;
+}
+
+// Stage k of tile t into slot `stage` (empty resources when k is past the tile's stages).
+__device__ __forceinline__ StageDma dma_tile_stage(const DmaConst& K, const DmaTile& t, int k, uint8_t* stage,
+                                                   uint32_t s_voff, int wave) {
+  StageDma s;
+  const bool live = k < t.nk;
+  s.lds = stage;
+  s.ra = make_rsrc(K.a + t.a_off + (uint64_t)k * K.a_ps, live ? (t.ab_bytes & 0xFFFFu) : 0);
+  s.rb = make_rsrc(K.b + t.b_off + (uint64_t)k * K.b_ps, live ? (t.ab_bytes >> 16) : 0);
+  s.rs = make_rsrc(K.s + t.s_off + (uint64_t)(k >> 1) * K.s_ld, live ? t.s_bytes : 0);
+  s.s_voff = s_voff;
+  s.s_lds = MX_SC_OFF + ((wave & 1) ? 1024 : 0);
+  stage_m0(s, wave);
   return s;
 }
 
@@ -235,11 +391,10 @@ template <int I>
 __device__ __forceinline__ void mx_dma_one(const StageDma& s, const DmaPlan& d, int wave) {
   if constexpr (I < 8) {
     constexpr int i = I >> 1;
-    const uint32_t voff = d.lane_off + (uint32_t)i * 1024u;
-    if constexpr ((I & 1) == 0) dma16(s.ra, voff, s.lds + wave * 4096 + i * 1024);
-    else dma16(s.rb, voff, s.lds + MX_OPB + wave * 4096 + i * 1024);
+    if constexpr ((I & 1) == 0) dma16_at<1024 * i>(s.ra, d.lane_off, s.m0a);
+    else dma16_at<1024 * i>(s.rb, d.lane_off, s.m0b);
   } else {
-    dma16(s.rs, s.s_voff, s.lds + s.s_lds);
+    dma16_at<0>(s.rs, s.s_voff, s.m0s);
   }
 }
 
@@ -334,6 +489,43 @@ __device__ __forceinline__ void mx_read_t(const uint8_t* stage, int wm, int wn, 
   f.sb[T] = w[1024 + 4 * (wn * 128 + T * 32 + m)];
 }
 
+// Per-lane byte offsets of the fragment reads within a stage slot.  Tile t of a fragment adds
+// the constant 2048 t (32 rows of 64 bytes: the swizzle term (row / 4) % 4 is the same), so
+// each read is one of six per-step bases plus an immediate offset.
+struct ReadPlan {
+  uint32_t a0, a1, b0, b1;   // K bytes [16 j, 16 j + 16) and [32 + 16 j, ...) of A / B row (128 wm|wn + m)
+  uint32_t sa, sb;           // scale bytes j of the row words (the step parity adds 2)
+};
+__device__ __forceinline__ ReadPlan make_read_plan(int wm, int wn, int lane) {
+  const int m = lane & 31, j = lane >> 5;
+  ReadPlan r;
+  r.a0 = (uint32_t)swz64(wm * 128 + m, j);
+  r.a1 = (uint32_t)swz64(wm * 128 + m, 2 + j);
+  r.b0 = (uint32_t)(MX_OPB + swz64(wn * 128 + m, j));
+  r.b1 = (uint32_t)(MX_OPB + swz64(wn * 128 + m, 2 + j));
+  r.sa = (uint32_t)(MX_SC_OFF + j + 4 * (wm * 128 + m));
+  r.sb = (uint32_t)(MX_SC_OFF + 1024 + j + 4 * (wn * 128 + m));
+  return r;
+}
+template <int T, int PAR>
+__device__ __forceinline__ void mx_read_tp(const uint8_t* stage, const ReadPlan& r, MxFrags& f) {
+  const uint4 x0 = *reinterpret_cast<const uint4*>(stage + r.a0 + 2048 * T);
+  const uint4 x1 = *reinterpret_cast<const uint4*>(stage + r.a1 + 2048 * T);
+  const uint4 y0 = *reinterpret_cast<const uint4*>(stage + r.b0 + 2048 * T);
+  const uint4 y1 = *reinterpret_cast<const uint4*>(stage + r.b1 + 2048 * T);
+  f.a[T] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  f.b[T] = v8i{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+  f.sa[T] = stage[r.sa + 2 * PAR + 128 * T];
+  f.sb[T] = stage[r.sb + 2 * PAR + 128 * T];
+}
+template <int PAR>
+__device__ __forceinline__ void mx_read_p(const uint8_t* stage, const ReadPlan& r, MxFrags& f) {
+  mx_read_tp<0, PAR>(stage, r, f);
+  mx_read_tp<1, PAR>(stage, r, f);
+  mx_read_tp<2, PAR>(stage, r, f);
+  mx_read_tp<3, PAR>(stage, r, f);
+}
+
 __device__ __forceinline__ void mx_read(const uint8_t* stage, int wm, int wn, int lane, int kt, MxFrags& f) {
   mx_read_t<0>(stage, wm, wn, lane, kt, f);
   mx_read_t<1>(stage, wm, wn, lane, kt, f);
@@ -369,6 +561,24 @@ __device__ __forceinline__ void mx_phase1(const MxFrags& f, v16f (&acc)[4][4], c
   mx_dma_one<3>(s, d, wave); GMLP_SB();
   mx_mma_one<1, 2>(f, acc); GMLP_SB(); mx_mma_one<1, 3>(f, acc); GMLP_SB();
   mx_dma_one<4>(s, d, wave); GMLP_SB();
+}
+
+template <int PAR>
+__device__ __forceinline__ void mx_phase2p(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
+                                           int wave, const uint8_t* nstage, const ReadPlan& rp, MxFrags& nf) {
+  mx_read_tp<0, PAR>(nstage, rp, nf); GMLP_SB();
+  mx_mma_one<2, 0>(f, acc); GMLP_SB();
+  mx_dma_one<5>(s, d, wave); GMLP_SB();
+  mx_read_tp<1, PAR>(nstage, rp, nf); GMLP_SB();
+  mx_mma_one<2, 1>(f, acc); GMLP_SB(); mx_mma_one<2, 2>(f, acc); GMLP_SB();
+  mx_dma_one<6>(s, d, wave); GMLP_SB();
+  mx_read_tp<2, PAR>(nstage, rp, nf); GMLP_SB();
+  mx_mma_one<2, 3>(f, acc); GMLP_SB(); mx_mma_one<3, 0>(f, acc); GMLP_SB();
+  mx_dma_one<7>(s, d, wave); GMLP_SB();
+  mx_read_tp<3, PAR>(nstage, rp, nf); GMLP_SB();
+  mx_mma_one<3, 1>(f, acc); GMLP_SB(); mx_mma_one<3, 2>(f, acc); GMLP_SB();
+  mx_dma_one<8>(s, d, wave); GMLP_SB();
+  mx_mma_one<3, 3>(f, acc); GMLP_SB();
 }
 
 __device__ __forceinline__ void mx_phase2(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
@@ -430,18 +640,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return (bid % 8) * (nb / 8) + bid / 8;
 }
 
+template <int MODE, int EPI>
+__device__ __forceinline__ int tiles_n(const GemmArgs& A) {
+  if (MODE == MODE_FPROP)
+    return (EPI == EPI_FC1 && A.act == 0) ? (int)((A.ffn + 127) / 128) : (int)((A.N + BN - 1) / BN);
+  return (int)((A.K + BN - 1) / BN);
+}
+
+// Context of tile bid of an ntm x ntn tile grid.
 template <int FMT, int MODE, int EPI>
-__device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  int ntn;
-  if (MODE == MODE_FPROP) {
-    ntn = (EPI == EPI_FC1 && A.act == 0) ? (int)((A.ffn + 127) / 128) : (int)((A.N + BN - 1) / BN);
-  } else {
-    ntn = (int)((A.K + BN - 1) / BN);
-  }
-  // Launch order within an XCD's range: groups of group_rows tile rows, column-major inside
-  // a group, so that the workgroups resident together share few A row blocks and B blocks.
-  const int ntm = (int)(gridDim.x / ntn);
+__device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, int ntn, int& mt, Ctx& c) {
+  // Order: groups of group_rows tile rows, column-major inside a group, so that the
+  // workgroups resident together on one XCD share few A row blocks and B blocks.
   const int gr = A.group_rows;
   const int gsz = gr * ntn;
   const int grp = bid / gsz, rem = bid - grp * gsz;
@@ -506,6 +716,12 @@ __device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
     c.nk = (int)((P + 63) / 64);
   }
   return true;
+}
+
+template <int FMT, int MODE, int EPI>
+__device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
+  const int ntn = tiles_n<MODE, EPI>(A);
+  return tile_ctx<FMT, MODE, EPI>(A, xcd_remap(blockIdx.x, gridDim.x), (int)(gridDim.x / ntn), ntn, mt, c);
 }
 
 // ----------------------------------------------------------------------------- kernel
@@ -799,6 +1015,350 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
 }
 
 // ----------------------------------------------------------------------------- dprob reduce
+// ----------------------------------------------------------------------------- persistent MXFP8 kernel
+// One workgroup per CU walks a list of tiles.  The 64-K stages of its non-empty tiles form one
+// sequence that flows through the 4-slot ring without a break: while a tile's last steps run,
+// the DMAs already fetch the first stages of the next tiles, so neither the pipeline fill nor
+// the epilogue's stores stall the matrix cores between tiles.  The epilogue stages its output
+// through the one ring slot that holds no pending stage (that of the last stage consumed), in
+// row chunks of at most 32 KB.
+//
+// Tile list: XCD x = blockIdx % 8 owns the contiguous tile range [x T / 8, (x + 1) T / 8) of
+// the T valid tiles and its workgroups take them in lockstep (tile lo + l, lo + l + n, ...),
+// so the tiles resident together on an XCD are neighbours in the group order of tile_ctx.
+
+// Epilogue of the persistent kernel: the 256 x 256 fp32 tile leaves the accumulators in 8
+// chunks of 64 rows x 128 columns (32 KB, one ring slot).  Chunk ch holds MFMA tile row
+// tm = ch / 2 of both wave halves (staged row sr -> tile row chunk_row(tm, sr)) and two of each
+// wave's four MFMA column tiles: tn = 2 q, 2 q + 1 (q = ch % 2), or for the SwiGLU fc1
+// tn = q, q + 2 (32 gate and the matching 32 up columns).  The accumulators are written to LDS
+// straight from the accumulator registers (inline ds_write_b32 with an AGPR operand), so
+// they are never copied to vector registers.
+__device__ __forceinline__ int chunk_row(int tm, int sr) { return ((sr >> 5) << 7) + 32 * tm + (sr & 31); }
+constexpr int EPC_LD = 136;        // floats per staged row: rows 4 apart are 32 banks apart
+
+template <int OFF>
+__device__ __forceinline__ void lds_write_acc(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1 offset:%2" :: "v"(addr), "a"(v), "i"(OFF) : "memory");
+}
+__device__ __forceinline__ void lds_writes_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Stage chunk ch: wave (wm, wn) writes acc[tm][tn0 + d tn1] (d = 0, 1) at staged rows
+// 32 wm + (r / 4) 8 + 4 j + r % 4, staged columns 64 wn + 32 d + m.
+template <int TM, int TN0, int TN1>
+__device__ __forceinline__ void stage_chunk(const v16f (&acc)[4][4], uint32_t base) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    constexpr int unused = 0;
+    (void)unused;
+  }
+  // base = LDS byte address of staged (32 wm + 4 j, 64 wn + m)
+#define GMLP_W(D, TN, R) lds_write_acc<((8 * ((R) >> 2) + ((R) & 3)) * EPC_LD + 32 * (D)) * 4>(base, acc[TM][TN][R]);
+#define GMLP_W16(D, TN) GMLP_W(D, TN, 0) GMLP_W(D, TN, 1) GMLP_W(D, TN, 2) GMLP_W(D, TN, 3) GMLP_W(D, TN, 4) \
+  GMLP_W(D, TN, 5) GMLP_W(D, TN, 6) GMLP_W(D, TN, 7) GMLP_W(D, TN, 8) GMLP_W(D, TN, 9) GMLP_W(D, TN, 10)          \
+  GMLP_W(D, TN, 11) GMLP_W(D, TN, 12) GMLP_W(D, TN, 13) GMLP_W(D, TN, 14) GMLP_W(D, TN, 15)
+  GMLP_W16(0, TN0)
+  GMLP_W16(1, TN1)
+#undef GMLP_W16
+#undef GMLP_W
+  lds_writes_done();
+}
+
+template <int MODE, int EPI, int CH>
+__device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
+                                          int tid, int wm, int wn, int lane) {
+  constexpr int TM = CH >> 1, Q = CH & 1;
+  constexpr bool SWIGLU_FC1 = false;
+  const bool swiglu = (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0);
+  const float* st = reinterpret_cast<const float*>(buf);
+  {
+    const int m = lane & 31, j = lane >> 5;
+    const uint32_t base = (uint32_t)(uintptr_t)buf + (uint32_t)(((32 * wm + 4 * j) * EPC_LD + 64 * wn + m) * 4);
+    if (swiglu) stage_chunk<TM, Q, Q + 2>(acc, base);
+    else stage_chunk<TM, 2 * Q, 2 * Q + 1>(acc, base);
+  }
+  (void)SWIGLU_FC1;
+  __syncthreads();
+  if (EPI == EPI_STORE || EPI == EPI_STORE32) {
+    const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
+    constexpr int PER = (EPI == EPI_STORE32) ? 4 : 8;            // output elements per 16-byte store
+    constexpr int NIT = 64 * 128 / PER / NTHREADS;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int task = it * NTHREADS + tid;
+      const int sr = task / (128 / PER);
+      const int sc = (task % (128 / PER)) * PER;
+      const int trow = chunk_row(TM, sr);
+      const int col = 128 * (sc >> 6) + 64 * Q + (sc & 63);
+      const int64_t gcol = c.nrow0 + col;
+      if (trow >= c.arows || gcol >= ncols) continue;
+      const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + trow : (int64_t)c.g * A.N + c.arow0 + trow;
+      const float4 v0 = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc);
+      if (EPI == EPI_STORE32) {
+        float* C = static_cast<float*>(A.c) + orow * ncols + gcol;
+        if (gcol + 4 <= ncols) {
+          *reinterpret_cast<float4*>(C) = v0;
+        } else {
+          const float e[4] = {v0.x, v0.y, v0.z, v0.w};
+          for (int q = 0; q < 4 && gcol + q < ncols; ++q) C[q] = e[q];
+        }
+      } else {
+        const float4 v1 = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 4);
+        const uint4 o = make_uint4(f32_to_bf16_bits(v0.x) | (f32_to_bf16_bits(v0.y) << 16),
+                                   f32_to_bf16_bits(v0.z) | (f32_to_bf16_bits(v0.w) << 16),
+                                   f32_to_bf16_bits(v1.x) | (f32_to_bf16_bits(v1.y) << 16),
+                                   f32_to_bf16_bits(v1.z) | (f32_to_bf16_bits(v1.w) << 16));
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(A.c) + orow * ncols + gcol) = o;
+      }
+    }
+  } else {
+    // EPI_FC1: h = bf16(acc) and a = bf16(act(h) p)
+    const int64_t ffn = A.ffn;
+    const int64_t F1 = (A.act == 0) ? 2 * ffn : ffn;
+    if (A.act == 0) {
+      // staged columns 64 wn + [gate 32 | up 32] hold features f = 128 nt + 64 wn + 32 Q + [0, 32)
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int task = it * NTHREADS + tid;
+        const int sr = task >> 3;
+        const int g8 = task & 7;                       // 8-feature group: wave half g8 / 4
+        const int sc = 64 * (g8 >> 2) + 8 * (g8 & 3);
+        const int trow = chunk_row(TM, sr);
+        const int64_t f = (int64_t)c.nt * 128 + 64 * (g8 >> 2) + 32 * Q + 8 * (g8 & 3);
+        if (trow >= c.arows || f >= ffn) continue;
+        const int64_t grow = c.arow0 + trow;
+        const float p = A.probs[grow];
+        float gv[8], uv[8];
+        *reinterpret_cast<float4*>(gv) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc);
+        *reinterpret_cast<float4*>(gv + 4) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 4);
+        *reinterpret_cast<float4*>(uv) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 32);
+        *reinterpret_cast<float4*>(uv + 4) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 36);
+        uint32_t hg[4], hu[4], ow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t g0 = f32_to_bf16_bits(gv[2 * i]), g1 = f32_to_bf16_bits(gv[2 * i + 1]);
+          const uint32_t u0 = f32_to_bf16_bits(uv[2 * i]), u1 = f32_to_bf16_bits(uv[2 * i + 1]);
+          hg[i] = g0 | (g1 << 16);
+          hu[i] = u0 | (u1 << 16);
+          const float a0 = act_out(0, bf16_to_f32(g0), bf16_to_f32(u0), p);
+          const float a1 = act_out(0, bf16_to_f32(g1), bf16_to_f32(u1), p);
+          ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
+        }
+        *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = make_uint4(hg[0], hg[1], hg[2], hg[3]);
+        *reinterpret_cast<uint4*>(A.h + grow * F1 + ffn + f) = make_uint4(hu[0], hu[1], hu[2], hu[3]);
+        *reinterpret_cast<uint4*>(A.a_out + grow * ffn + f) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int task = it * NTHREADS + tid;
+        const int sr = task >> 4;
+        const int sc = 8 * (task & 15);
+        const int trow = chunk_row(TM, sr);
+        const int64_t f = c.nrow0 + 128 * (sc >> 6) + 64 * Q + (sc & 63);
+        if (trow >= c.arows || f >= ffn) continue;
+        const int64_t grow = c.arow0 + trow;
+        const float p = A.probs[grow];
+        float hv[8];
+        *reinterpret_cast<float4*>(hv) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc);
+        *reinterpret_cast<float4*>(hv + 4) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 4);
+        uint32_t hw[4], ow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t h0 = f32_to_bf16_bits(hv[2 * i]), h1 = f32_to_bf16_bits(hv[2 * i + 1]);
+          hw[i] = h0 | (h1 << 16);
+          const float a0 = act_out(1, bf16_to_f32(h0), 0.0f, p);
+          const float a1 = act_out(1, bf16_to_f32(h1), 0.0f, p);
+          ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
+        }
+        *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(A.a_out + grow * ffn + f) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Output tile of a group with no tokens (weight gradients only): zeros, stored directly.
+template <int MODE, int EPI>
+__device__ __forceinline__ void epi_zero(const GemmArgs& A, const Ctx& c, int tid) {
+  const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
+  const int esz = (EPI == EPI_STORE32) ? 4 : 2;
+  for (int it = 0; it < 32 * esz / 2; ++it) {
+    const int per_row = 256 * esz / 16;             // 16-byte pieces per tile row
+    const int idx = it * NTHREADS + tid;
+    const int row = idx / per_row;
+    const int col = (idx % per_row) * (16 / esz);
+    const int64_t gcol = c.nrow0 + col;
+    if (row >= c.arows || gcol >= ncols) continue;
+    const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + row : (int64_t)c.g * A.N + c.arow0 + row;
+    uint8_t* dst = static_cast<uint8_t*>(A.c) + (orow * ncols + gcol) * esz;
+    if (gcol + 16 / esz <= ncols) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
+    } else {
+      for (int q = 0; q < (int)(ncols - gcol) * esz; ++q) dst[q] = 0;
+    }
+  }
+}
+
+template <int MODE, int EPI>
+__device__ __forceinline__ void mx_epilogue(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
+                                            int tid, int wm, int wn, int lane) {
+  epi_chunk<MODE, EPI, 0>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 1>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 2>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 3>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 4>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 5>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 6>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 7>(A, c, acc, buf, tid, wm, wn, lane);
+}
+
+template <int MODE, int EPI>
+__device__ __forceinline__ TileRef tile_ref(const GemmArgs& A, int t, int ntm, int ntn) {
+  int mt;
+  Ctx c;
+  tile_ctx<FMT_MXFP8, MODE, EPI>(A, t, ntm, ntn, mt, c);
+  TileRef r;
+  r.nk = uni(c.nk);
+  r.arows = uni(c.arows);
+  r.arow0 = uni(c.arow0);
+  r.g = uni(c.g);
+  r.nt = uni(c.nt);
+  r.off = (MODE == MODE_WGRAD) ? uni(A.T.col_off[c.g]) : 0;
+  r.woff = (MODE == MODE_WGRAD) ? uni(A.T.colw_off[c.g]) : 0;
+  return r;
+}
+
+template <int MODE, int EPI>
+__global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
+  __shared__ __align__(16) uint8_t smem[MX_NSTAGE * MX_STAGE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = uni(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  // valid tiles and this workgroup's share
+  const int ntn = tiles_n<MODE, EPI>(A);
+  const int ntm = (MODE == MODE_FPROP) ? (A.G > 0 ? uni(A.T.t256_off[A.G]) : 0) : A.G * (int)((A.N + BM - 1) / BM);
+  const int64_t nt = (int64_t)ntm * ntn;
+  const int nwx = gridDim.x / 8, x = blockIdx.x % 8, lw = blockIdx.x / 8;
+  const int hi = (int)(nt * (x + 1) / 8);
+  int t = (int)(nt * x / 8) + lw;
+  if (t >= hi) return;
+
+  const uint32_t lane_off = (uint32_t)(lane >> 2) * 64u + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+  const DmaPlan dpl{nullptr, nullptr, 0, 0, 0, 0, lane_off};
+  uint32_t s_voff = 16u * lane;
+  if ((wave & 1) && MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
+    const int band = lane >> 4;
+    s_voff = 4u * (uint32_t)((band & 1) * A.ffn + (band >> 1) * 64 + 4 * (lane & 15));
+  }
+  auto slot = [&](uint32_t st) { return smem + (st & (MX_NSTAGE - 1)) * MX_STAGE; };
+
+  // DMA window: the current non-empty tile (R0, and its full sources D0) and the next two
+  int dnext = t;
+  auto next_ref = [&]() -> TileRef {
+    while (dnext < hi) {
+      const TileRef r = tile_ref<MODE, EPI>(A, dnext, ntm, ntn);
+      dnext += nwx;
+      if (r.nk > 0) return r;
+    }
+    TileRef r{};
+    return r;                          // nk = 0: no tile (its stages are issued empty)
+  };
+  const DmaConst KC = dma_const<MODE, EPI>(A, wave);
+  const ReadPlan rp = make_read_plan(wm, wn, lane);
+  DmaTile D0 = dma_tile<MODE, EPI>(A, next_ref(), wave);
+  DmaTile D1 = dma_tile<MODE, EPI>(A, next_ref(), wave);
+  DmaTile D2 = dma_tile<MODE, EPI>(A, next_ref(), wave);
+  // stage `off` positions past the first stage of D0 (selects only: the step has no branch)
+  auto window_stage = [&](int off, uint8_t* dst) -> StageDma {
+    const bool u1 = off >= D0.nk;
+    const int o1 = off - D0.nk;
+    const bool u2 = u1 && o1 >= D1.nk;
+    const int o2 = o1 - D1.nk;
+    return dma_tile_stage(KC, sel_tile(u2, D2, sel_tile(u1, D1, D0)), u2 ? o2 : (u1 ? o1 : off), dst, s_voff, wave);
+  };
+
+  uint32_t gs = 0;                     // sequence number of the next stage to compute
+  for (int o = 0; o < 3; ++o) {
+    const StageDma sd = window_stage(o, slot(o));
+    mx_dma_one<0>(sd, dpl, wave); mx_dma_one<1>(sd, dpl, wave); mx_dma_one<2>(sd, dpl, wave);
+    mx_dma_one<3>(sd, dpl, wave); mx_dma_one<4>(sd, dpl, wave); mx_dma_one<5>(sd, dpl, wave);
+    mx_dma_one<6>(sd, dpl, wave); mx_dma_one<7>(sd, dpl, wave); mx_dma_one<8>(sd, dpl, wave);
+  }
+
+  for (; t < hi; t += nwx) {
+    // every non-empty tile is R0 of the DMA window when the compute reaches it
+    const TileRef cr = tile_ref<MODE, EPI>(A, t, ntm, ntn);
+    Ctx c;
+    c.arows = cr.arows;
+    c.arow0 = cr.arow0;
+    c.g = cr.g;
+    c.nt = cr.nt;
+    c.nrow0 = (int64_t)cr.nt * BN;
+    const int nk = cr.nk;
+    if (nk == 0) {                     // an empty group's weight gradient: zeros
+      int tid_t = tid;
+      asm volatile("" : "+v"(tid_t));
+      epi_zero<MODE, EPI>(A, c, tid_t);
+      continue;
+    }
+    v16f acc[4][4];
+    MxFrags f0, f1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+    {
+      // stage gs (this tile's first) has landed once at most the two stages after it are pending
+      wait_vmcnt<2 * MX_DMA_PER_STAGE>();
+      __syncthreads();
+      mx_read_p<0>(slot(gs), rp, f0);
+      // One step: the DMAs of sequence stage gs + 3 (whose slot held stage gs - 1, read by every
+      // wave before the previous step's barrier), then the MFMAs of stage gs with the reads of
+      // stage gs + 1 in between.  Stage gs + 1 may be the next tile's first (read again after
+      // the epilogue) or no stage at all; such reads go unused.  Two steps per trip keep the two
+      // fragment sets in fixed registers
+      // (stage kt + 1 of an even kt has parity 1, of an odd kt parity 0)
+      int kt = 0;
+      do {                               // nk >= 2 and even
+        {
+          const StageDma sd = window_stage(kt + 3, slot(gs + 3));
+          GMLP_SB();
+          mx_phase1(f0, acc, sd, dpl, wave);
+          wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
+          __syncthreads();
+          mx_phase2p<1>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
+          ++gs;
+        }
+        {
+          const StageDma sd = window_stage(kt + 4, slot(gs + 3));
+          GMLP_SB();
+          mx_phase1(f1, acc, sd, dpl, wave);
+          wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
+          __syncthreads();
+          mx_phase2p<0>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
+          ++gs;
+        }
+        kt += 2;
+      } while (kt < nk);
+      D0 = D1;
+      D1 = D2;
+      D2 = dma_tile<MODE, EPI>(A, next_ref(), wave);
+    }
+    // the slot of the last consumed stage holds nothing pending (the ones after it do).  The
+    // thread index is laundered per tile so that the epilogue's per-thread addresses are
+    // formed here rather than hoisted out of the tile loop (they would stay live, and spill,
+    // across every main loop).
+    int tid_t = tid;
+    asm volatile("" : "+v"(tid_t));
+    mx_epilogue<MODE, EPI>(A, c, acc, slot(gs + 3), tid_t, wm, wn, tid_t & 63);
+  }
+  wait_vmcnt<0>();                     // the DMAs past the last tile (empty) before the LDS is released
+}
+
 __global__ void dprob_reduce_kernel(const float* __restrict__ part, int nparts, int64_t M, float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= M) return;
@@ -811,6 +1371,37 @@ __global__ void dprob_reduce_kernel(const float* __restrict__ part, int nparts, 
 int gemm_fprop_ntiles_n(const GemmArgs& g) {
   if (g.epi == EPI_FC1 && g.act == 0) return (int)((g.ffn + 127) / 128);
   return (int)((g.N + BN - 1) / BN);
+}
+
+static int cu_count() {
+  static int n[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (n[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    n[dev] = v;
+  }
+  return n[dev];
+}
+
+template <int MODE, int EPI>
+static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
+  int64_t tiles;
+  if (MODE == MODE_FPROP) {
+    tiles = ((g.M + BM - 1) / BM + g.G) * (int64_t)gemm_fprop_ntiles_n(g);
+  } else {
+    tiles = (int64_t)g.G * ((g.N + BM - 1) / BM) * ((g.K + BN - 1) / BN);
+  }
+  if (tiles <= 0) return hipSuccess;
+  GemmArgs a = g;
+  a.group_rows = 4;
+  if (const char* e = getenv("GMLP_GROUP_ROWS")) a.group_rows = atoi(e) > 0 ? atoi(e) : 1;
+  // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split
+  int64_t wgs = std::min<int64_t>(cu_count(), tiles);
+  wgs = (wgs + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_mx_kernel<MODE, EPI>), dim3((unsigned)wgs), dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int FMT, int MODE, int EPI>
@@ -834,14 +1425,16 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
 #define GMLP_DISPATCH(F, MO, E) \
   if (g.fmt == F && g.mode == MO && epi == E) return launch_one<F, MO, E>(g, s);
   const int epi = (g.epi == EPI_STORE && g.out_fp32) ? (int)EPI_STORE32 : g.epi;
-  GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_STORE)
-  GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_STORE32)
-  GMLP_DISPATCH(FMT_MXFP8, MODE_WGRAD, EPI_STORE32)
+#define GMLP_DISPATCH_MX(MO, E) \
+  if (g.fmt == FMT_MXFP8 && g.mode == MO && epi == E) return launch_mx<MO, E>(g, s);
+  GMLP_DISPATCH_MX(MODE_FPROP, EPI_STORE)
+  GMLP_DISPATCH_MX(MODE_FPROP, EPI_STORE32)
+  GMLP_DISPATCH_MX(MODE_WGRAD, EPI_STORE32)
+  GMLP_DISPATCH_MX(MODE_FPROP, EPI_FC1)
+  GMLP_DISPATCH_MX(MODE_WGRAD, EPI_STORE)
+#undef GMLP_DISPATCH_MX
   GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_STORE32)
   GMLP_DISPATCH(FMT_NVFP4, MODE_WGRAD, EPI_STORE32)
-  GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_FC1)
-  GMLP_DISPATCH(FMT_MXFP8, MODE_FPROP, EPI_DACT)
-  GMLP_DISPATCH(FMT_MXFP8, MODE_WGRAD, EPI_STORE)
   GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_STORE)
   GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_FC1)
   GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_DACT)
