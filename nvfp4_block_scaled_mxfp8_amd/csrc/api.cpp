@@ -310,6 +310,11 @@ gmlp_status mlp_common_checks(int64_t M, int E, int64_t H, int64_t ffn, int act,
   if ((st = check_dims(M, H, E)) != GMLP_OK) return st;
   if (ffn <= 0 || ffn % 128 != 0) return fail(GMLP_UNSUPPORTED, "dims: ffn must be a positive multiple of 128, got %lld", (long long)ffn);
   if (H % 128 != 0) return fail(GMLP_UNSUPPORTED, "dims: hidden must be a multiple of 128, got %lld", (long long)H);
+  // the GEMMs address every quantized operand with 32-bit offsets
+  const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
+  if ((M + 127LL * E) * std::max(H, F1) >= (1LL << 32) || (int64_t)E * F1 * H >= (1LL << 32))
+    return fail(GMLP_UNSUPPORTED, "dims: a quantized operand would reach 4 GB (M = %lld, hidden %lld, ffn %lld)",
+                (long long)M, (long long)H, (long long)ffn);
   return GMLP_OK;
 }
 

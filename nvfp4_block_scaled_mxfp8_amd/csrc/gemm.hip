@@ -156,6 +156,20 @@ __device__ __forceinline__ void dma16_at(const Rsrc& r, uint32_t voff, uint32_t 
                :: "v"(voff), "s"(r.w), "s"(m0), "i"(OFF) : "memory");
 }
 
+// Persistent kernel DMAs: the per-stage offset can go in SOFFSET, and M0 is written once per band:
+// the A band's four instructions run back to back on one M0, then the B band's, then the scale
+// words' (nothing else in the kernel uses M0).
+template <int OFF>
+__device__ __forceinline__ void dma_set_m0(const Rsrc& r, uint32_t voff, uint32_t soff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%4 lds"
+               :: "v"(voff), "s"(r.w), "s"(soff), "s"(m0), "i"(OFF) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void dma_same_m0(const Rsrc& r, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds" :: "v"(voff), "s"(r.w), "s"(soff), "i"(OFF)
+               : "memory");
+}
+
 // s_waitcnt with only the vector-memory counter: vmcnt <= n (expcnt, lgkmcnt untouched).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -216,6 +230,7 @@ struct StageDma {
   uint8_t* lds;          // the stage's slot
   uint32_t s_lds;        // scale-word destination offset in the slot
   uint32_t m0a, m0b, m0s;  // LDS destinations (M0) of this wave's A band, B band and scale words
+  uint32_t soa, sob, sos;  // SOFFSET of the three resources (0 unless the resource is a tile's)
 };
 __device__ __forceinline__ void stage_m0(StageDma& s, int wave) {
   const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)s.lds);
@@ -250,6 +265,7 @@ __device__ __forceinline__ StageDma mx_stage_plan(const GemmArgs& A, const Ctx& 
   s.rs = make_rsrc(is_b ? b_w : a_w, live ? (is_b ? b_n : a_n) : 0);
   s.s_voff = is_b ? b_voff : 16u * lane;
   s.s_lds = MX_SC_OFF + (is_b ? 1024 : 0);
+  s.soa = s.sob = s.sos = 0;
   stage_m0(s, wave);
   return s;
 }
@@ -292,6 +308,7 @@ struct DmaConst {
   const uint32_t* s;         // this wave's scale-word base (A or B)
   uint32_t a_ps, b_ps;       // bytes per 64-K panel
   uint32_t s_ld;             // words per 128-K word
+  uint32_t a_total, b_total, s_total;   // bytes of the operands and of this wave's scale words
 };
 
 // Field-wise uniform select (scalar selects, no branch).
@@ -315,13 +332,21 @@ __device__ __forceinline__ DmaConst dma_const(const GemmArgs& A, int wave) {
   k.s = (wave & 1) ? A.b.scale_mfma : A.a.scale_mfma;
   if (MODE == MODE_FPROP) {
     const int64_t brows = swiglu ? 2 * A.ffn : A.N;
+    const int64_t kw = (A.K + 127) / 128;
     k.a_ps = (uint32_t)(A.M * 64);
     k.b_ps = (uint32_t)(brows * 64);
     k.s_ld = (uint32_t)((wave & 1) ? brows : A.M);
+    k.a_total = (uint32_t)(A.M * A.K);
+    k.b_total = (uint32_t)(A.G * brows * A.K);
+    k.s_total = (uint32_t)(4 * kw * ((wave & 1) ? A.G * brows : A.M));
   } else {
+    const int64_t P = A.T.col_off[A.G], W = A.T.colw_off[A.G];
     k.a_ps = (uint32_t)(A.N * 64);
     k.b_ps = (uint32_t)(A.K * 64);
     k.s_ld = (uint32_t)((wave & 1) ? A.K : A.N);
+    k.a_total = (uint32_t)(A.N * P);
+    k.b_total = (uint32_t)(A.K * P);
+    k.s_total = (uint32_t)(4 * W * ((wave & 1) ? A.K : A.N));
   }
   return k;
 }
@@ -381,6 +406,46 @@ __device__ __forceinline__ StageDma dma_tile_stage(const DmaConst& K, const DmaT
   s.rs = make_rsrc(K.s + t.s_off + (uint64_t)(k >> 1) * K.s_ld, live ? t.s_bytes : 0);
   s.s_voff = s_voff;
   s.s_lds = MX_SC_OFF + ((wave & 1) ? 1024 : 0);
+  s.soa = s.sob = s.sos = 0;
+  stage_m0(s, wave);
+  return s;
+}
+
+// A stage of the current tile from running source addresses (the common case: no selection).
+// Interior stages of a tile: three resources fixed for the tile (its bands in panel 0) and the
+// stage offset in SOFFSET.  SOFFSET counts in the range check, so these resources reach to the
+// end of the operand: rows past a partial band's valid ones are then read from the neighbouring
+// rows instead of as zeros.  They only feed output rows and columns past the tile's valid
+// range, which are never stored (the MFMA rows and columns are independent); the buffer end
+// still bounds every access.
+struct RunDma {
+  Rsrc ra, rb, rs;
+};
+__device__ __forceinline__ uint32_t rest(uint32_t total, uint32_t off) { return total > off ? total - off : 0u; }
+__device__ __forceinline__ RunDma run_rsrc(const DmaConst& K, const DmaTile& t) {
+  RunDma r;
+  const uint64_t pa = (uint64_t)(uintptr_t)K.a + t.a_off;
+  const uint64_t pb = (uint64_t)(uintptr_t)K.b + t.b_off;
+  const uint64_t ps = (uint64_t)(uintptr_t)(K.s + t.s_off);
+  auto word = [](uint32_t v) { return __builtin_amdgcn_readfirstlane((int)v); };   // uniform: scalar registers
+  r.ra.w = v4i{word((uint32_t)pa), word((uint32_t)(pa >> 32) & 0xFFFFu), word(rest(K.a_total, t.a_off)), (int)kRsrcWord3};
+  r.rb.w = v4i{word((uint32_t)pb), word((uint32_t)(pb >> 32) & 0xFFFFu), word(rest(K.b_total, t.b_off)), (int)kRsrcWord3};
+  r.rs.w = v4i{word((uint32_t)ps), word((uint32_t)(ps >> 32) & 0xFFFFu), word(rest(K.s_total, 4 * t.s_off)),
+               (int)kRsrcWord3};
+  return r;
+}
+__device__ __forceinline__ StageDma run_stage(const RunDma& r, uint32_t soa, uint32_t sob, uint32_t sos, uint8_t* stage,
+                                              uint32_t s_voff, int wave) {
+  StageDma s;
+  s.lds = stage;
+  s.ra = r.ra;
+  s.rb = r.rb;
+  s.rs = r.rs;
+  s.soa = (uint32_t)__builtin_amdgcn_readfirstlane((int)soa);
+  s.sob = (uint32_t)__builtin_amdgcn_readfirstlane((int)sob);
+  s.sos = (uint32_t)__builtin_amdgcn_readfirstlane((int)sos);
+  s.s_voff = s_voff;
+  s.s_lds = MX_SC_OFF + ((wave & 1) ? 1024 : 0);
   stage_m0(s, wave);
   return s;
 }
@@ -389,13 +454,11 @@ __device__ __forceinline__ StageDma dma_tile_stage(const DmaConst& K, const DmaT
 // scale words.
 template <int I>
 __device__ __forceinline__ void mx_dma_one(const StageDma& s, const DmaPlan& d, int wave) {
-  if constexpr (I < 8) {
-    constexpr int i = I >> 1;
-    if constexpr ((I & 1) == 0) dma16_at<1024 * i>(s.ra, d.lane_off, s.m0a);
-    else dma16_at<1024 * i>(s.rb, d.lane_off, s.m0b);
-  } else {
-    dma16_at<0>(s.rs, s.s_voff, s.m0s);
-  }
+  if constexpr (I == 0) dma_set_m0<0>(s.ra, d.lane_off, s.soa, s.m0a);
+  else if constexpr (I < 4) dma_same_m0<1024 * I>(s.ra, d.lane_off, s.soa);
+  else if constexpr (I == 4) dma_set_m0<0>(s.rb, d.lane_off, s.sob, s.m0b);
+  else if constexpr (I < 8) dma_same_m0<1024 * (I - 4)>(s.rb, d.lane_off, s.sob);
+  else dma_set_m0<0>(s.rs, s.s_voff, s.sos, s.m0s);
 }
 
 template <int MODE, int EPI>
@@ -1323,7 +1386,41 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
       // fragment sets in fixed registers
       // (stage kt + 1 of an even kt has parity 1, of an odd kt parity 0)
       int kt = 0;
-      do {                               // nk >= 2 and even
+      if (nk > 4) {
+        // steps whose DMA target (kt + 3, kt + 4) is still in this tile: fixed resources, the
+        // stage in SOFFSET (32-bit: every operand is below 4 GB)
+        const RunDma rr = run_rsrc(KC, D0);
+        uint32_t soa = 3u * KC.a_ps, sob = 3u * KC.b_ps;
+        uint32_t sos = 4u * KC.s_ld;                 // 128-K word (kt + 3) / 2 = 1
+        const uint32_t s_step = 4u * KC.s_ld;
+        do {
+          {
+            const StageDma sd = run_stage(rr, soa, sob, sos, slot(gs + 3), s_voff, wave);
+            GMLP_SB();
+            mx_phase1(f0, acc, sd, dpl, wave);
+            wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
+            __syncthreads();
+            mx_phase2p<1>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
+            ++gs;
+          }
+          soa += KC.a_ps;
+          sob += KC.b_ps;
+          {
+            const StageDma sd = run_stage(rr, soa, sob, sos + s_step, slot(gs + 3), s_voff, wave);
+            GMLP_SB();
+            mx_phase1(f1, acc, sd, dpl, wave);
+            wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
+            __syncthreads();
+            mx_phase2p<0>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
+            ++gs;
+          }
+          soa += KC.a_ps;
+          sob += KC.b_ps;
+          sos += s_step;
+          kt += 2;
+        } while (kt < nk - 4);
+      }
+      do {                               // the last two pairs (or one): DMA targets may be past the tile
         {
           const StageDma sd = window_stage(kt + 3, slot(gs + 3));
           GMLP_SB();
@@ -1394,6 +1491,14 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
     tiles = (int64_t)g.G * ((g.N + BM - 1) / BM) * ((g.K + BN - 1) / BN);
   }
   if (tiles <= 0) return hipSuccess;
+  // the DMA sources are 32-bit offsets: every operand (data and scale words) below 4 GB
+  {
+    const int64_t brows = (MODE == MODE_FPROP && EPI == EPI_FC1 && g.act == 0) ? 2 * g.ffn : g.N;
+    const int64_t rows_bound = g.M + 127LL * g.G;                    // padded tokens of all groups
+    const int64_t big = (MODE == MODE_FPROP) ? std::max(g.M * g.K, (int64_t)g.G * brows * g.K)
+                                             : std::max(g.N, g.K) * rows_bound;
+    if (big >= (1LL << 32)) return hipErrorInvalidValue;
+  }
   GemmArgs a = g;
   a.group_rows = 4;
   if (const char* e = getenv("GMLP_GROUP_ROWS")) a.group_rows = atoi(e) > 0 ? atoi(e) : 1;
