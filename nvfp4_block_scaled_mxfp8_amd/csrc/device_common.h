@@ -24,11 +24,16 @@ constexpr float kFltMax = 3.40282346638528859811704183484516925e+38f;
 // --------------------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// Round to nearest even; inputs are finite.
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two values at once: lo in bits [0, 16), hi in [16, 32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
 }
 __device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f32_to_bf16_bits(f) << 16); }
 

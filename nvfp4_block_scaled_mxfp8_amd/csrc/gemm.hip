@@ -1110,11 +1110,6 @@ __device__ __forceinline__ void lds_writes_done() { asm volatile("s_waitcnt lgkm
 // 32 wm + (r / 4) 8 + 4 j + r % 4, staged columns 64 wn + 32 d + m.
 template <int TM, int TN0, int TN1>
 __device__ __forceinline__ void stage_chunk(const v16f (&acc)[4][4], uint32_t base) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    constexpr int unused = 0;
-    (void)unused;
-  }
   // base = LDS byte address of staged (32 wm + 4 j, 64 wn + m)
 #define GMLP_W(D, TN, R) lds_write_acc<((8 * ((R) >> 2) + ((R) & 3)) * EPC_LD + 32 * (D)) * 4>(base, acc[TM][TN][R]);
 #define GMLP_W16(D, TN) GMLP_W(D, TN, 0) GMLP_W(D, TN, 1) GMLP_W(D, TN, 2) GMLP_W(D, TN, 3) GMLP_W(D, TN, 4) \
@@ -1127,11 +1122,28 @@ __device__ __forceinline__ void stage_chunk(const v16f (&acc)[4][4], uint32_t ba
   lds_writes_done();
 }
 
+// Output stores of the persistent kernel: one buffer resource per output matrix and tile, based
+// at the tile's first row and column and sized to its valid rows, so that the rows past the
+// last token fall outside the range and are dropped by the hardware check; a lane whose columns
+// lie past the matrix gets an offset beyond the range.  The row of each store goes in SOFFSET.
+// Stores stream past the L2 (nontemporal): the output is not read again by this kernel, and
+// keeping it out of the cache leaves the L2 to the operand panels.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kStoreNT = 2;                       // aux bits of a nontemporal buffer store
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, (int)kRsrcWord3);
+}
+__device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t x,
+                                          uint32_t y, uint32_t z, uint32_t w) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128((v4u){x, y, z, w}, r, voff, soff, kStoreNT);
+}
+
 template <int MODE, int EPI, int CH>
 __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
                                           int tid, int wm, int wn, int lane) {
   constexpr int TM = CH >> 1, Q = CH & 1;
-  constexpr bool SWIGLU_FC1 = false;
   const bool swiglu = (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0);
   const float* st = reinterpret_cast<const float*>(buf);
   {
@@ -1140,102 +1152,104 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
     if (swiglu) stage_chunk<TM, Q, Q + 2>(acc, base);
     else stage_chunk<TM, 2 * Q, 2 * Q + 1>(acc, base);
   }
-  (void)SWIGLU_FC1;
   __syncthreads();
   if (EPI == EPI_STORE || EPI == EPI_STORE32) {
+    // lanes [LPR r, LPR r + LPR) store staged row r of each group of RPI rows
+    constexpr int ESZ = (EPI == EPI_STORE32) ? 4 : 2;
+    constexpr int PER = 16 / ESZ;                 // output elements per 16-byte store
+    constexpr int LPR = 128 / PER;
+    constexpr int RPI = NTHREADS / LPR;
+    constexpr int NIT = 64 / RPI;
     const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
-    constexpr int PER = (EPI == EPI_STORE32) ? 4 : 8;            // output elements per 16-byte store
-    constexpr int NIT = 64 * 128 / PER / NTHREADS;
+    const int64_t orow0 = (MODE == MODE_FPROP) ? c.arow0 : (int64_t)c.g * A.N + c.arow0;
+    const uint32_t rowb = (uint32_t)(ncols * ESZ);
+    const __amdgpu_buffer_rsrc_t r =
+        out_rsrc(static_cast<uint8_t*>(A.c) + (orow0 * ncols + c.nrow0) * ESZ, (int64_t)c.arows * rowb);
+    const int lrow = tid / LPR, sc = (tid % LPR) * PER;
+    const int col = 128 * (sc >> 6) + 64 * Q + (sc & 63);
+    const uint32_t voff = (c.nrow0 + col < ncols) ? (uint32_t)lrow * rowb + (uint32_t)(col * ESZ) : kOutOfRange;
+    const float* src = st + lrow * EPC_LD + sc;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int task = it * NTHREADS + tid;
-      const int sr = task / (128 / PER);
-      const int sc = (task % (128 / PER)) * PER;
-      const int trow = chunk_row(TM, sr);
-      const int col = 128 * (sc >> 6) + 64 * Q + (sc & 63);
-      const int64_t gcol = c.nrow0 + col;
-      if (trow >= c.arows || gcol >= ncols) continue;
-      const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + trow : (int64_t)c.g * A.N + c.arow0 + trow;
-      const float4 v0 = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc);
+      const uint32_t ur = (uint32_t)(128 * ((RPI * it) >> 5) + 32 * TM + ((RPI * it) & 31));   // tile row - lrow
+      const float4 v0 = *reinterpret_cast<const float4*>(src + RPI * it * EPC_LD);
       if (EPI == EPI_STORE32) {
-        float* C = static_cast<float*>(A.c) + orow * ncols + gcol;
-        if (gcol + 4 <= ncols) {
-          *reinterpret_cast<float4*>(C) = v0;
-        } else {
-          const float e[4] = {v0.x, v0.y, v0.z, v0.w};
-          for (int q = 0; q < 4 && gcol + q < ncols; ++q) C[q] = e[q];
-        }
+        out_store(r, voff, ur * rowb, __float_as_uint(v0.x), __float_as_uint(v0.y), __float_as_uint(v0.z),
+                  __float_as_uint(v0.w));
       } else {
-        const float4 v1 = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 4);
-        const uint4 o = make_uint4(f32_to_bf16_bits(v0.x) | (f32_to_bf16_bits(v0.y) << 16),
-                                   f32_to_bf16_bits(v0.z) | (f32_to_bf16_bits(v0.w) << 16),
-                                   f32_to_bf16_bits(v1.x) | (f32_to_bf16_bits(v1.y) << 16),
-                                   f32_to_bf16_bits(v1.z) | (f32_to_bf16_bits(v1.w) << 16));
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(A.c) + orow * ncols + gcol) = o;
+        const float4 v1 = *reinterpret_cast<const float4*>(src + RPI * it * EPC_LD + 4);
+        out_store(r, voff, ur * rowb, pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
+                  pack_bf16x2(v1.z, v1.w));
       }
     }
   } else {
     // EPI_FC1: h = bf16(acc) and a = bf16(act(h) p)
     const int64_t ffn = A.ffn;
     const int64_t F1 = (A.act == 0) ? 2 * ffn : ffn;
+    const uint32_t hrow = (uint32_t)(F1 * 2), arow = (uint32_t)(ffn * 2);
     if (A.act == 0) {
-      // staged columns 64 wn + [gate 32 | up 32] hold features f = 128 nt + 64 wn + 32 Q + [0, 32)
+      // staged columns 64 wn + [gate 32 | up 32] hold features f = 128 nt + 64 wn + 32 Q + [0, 32);
+      // lanes [8 r, 8 r + 8) take staged row r + 32 it, 8 features each
+      const int64_t f0 = (int64_t)c.nt * 128;
+      const __amdgpu_buffer_rsrc_t rh = out_rsrc(A.h + c.arow0 * F1 + f0, (int64_t)c.arows * hrow);
+      const __amdgpu_buffer_rsrc_t ra = out_rsrc(A.a_out + c.arow0 * ffn + f0, (int64_t)c.arows * arow);
+      const int lrow = tid >> 3, g8 = tid & 7;
+      const int sc = 64 * (g8 >> 2) + 8 * (g8 & 3);
+      const int fc = 64 * (g8 >> 2) + 32 * Q + 8 * (g8 & 3);
+      const bool fok = f0 + fc < ffn;
+      const uint32_t vh = fok ? (uint32_t)lrow * hrow + (uint32_t)(2 * fc) : kOutOfRange;
+      const uint32_t va = fok ? (uint32_t)lrow * arow + (uint32_t)(2 * fc) : kOutOfRange;
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
-        const int task = it * NTHREADS + tid;
-        const int sr = task >> 3;
-        const int g8 = task & 7;                       // 8-feature group: wave half g8 / 4
-        const int sc = 64 * (g8 >> 2) + 8 * (g8 & 3);
-        const int trow = chunk_row(TM, sr);
-        const int64_t f = (int64_t)c.nt * 128 + 64 * (g8 >> 2) + 32 * Q + 8 * (g8 & 3);
-        if (trow >= c.arows || f >= ffn) continue;
-        const int64_t grow = c.arow0 + trow;
-        const float p = A.probs[grow];
+        const int ur = 128 * it + 32 * TM;
+        const int trow = ur + lrow;
+        const float p = A.probs[c.arow0 + (trow < c.arows ? trow : c.arows - 1)];
+        const float* src = st + (32 * it + lrow) * EPC_LD + sc;
         float gv[8], uv[8];
-        *reinterpret_cast<float4*>(gv) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc);
-        *reinterpret_cast<float4*>(gv + 4) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 4);
-        *reinterpret_cast<float4*>(uv) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 32);
-        *reinterpret_cast<float4*>(uv + 4) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 36);
+        *reinterpret_cast<float4*>(gv) = *reinterpret_cast<const float4*>(src);
+        *reinterpret_cast<float4*>(gv + 4) = *reinterpret_cast<const float4*>(src + 4);
+        *reinterpret_cast<float4*>(uv) = *reinterpret_cast<const float4*>(src + 32);
+        *reinterpret_cast<float4*>(uv + 4) = *reinterpret_cast<const float4*>(src + 36);
         uint32_t hg[4], hu[4], ow[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t g0 = f32_to_bf16_bits(gv[2 * i]), g1 = f32_to_bf16_bits(gv[2 * i + 1]);
-          const uint32_t u0 = f32_to_bf16_bits(uv[2 * i]), u1 = f32_to_bf16_bits(uv[2 * i + 1]);
-          hg[i] = g0 | (g1 << 16);
-          hu[i] = u0 | (u1 << 16);
-          const float a0 = act_out(0, bf16_to_f32(g0), bf16_to_f32(u0), p);
-          const float a1 = act_out(0, bf16_to_f32(g1), bf16_to_f32(u1), p);
+          hg[i] = pack_bf16x2(gv[2 * i], gv[2 * i + 1]);
+          hu[i] = pack_bf16x2(uv[2 * i], uv[2 * i + 1]);
+          const float a0 = act_out(0, bf16_to_f32(hg[i] & 0xFFFFu), bf16_to_f32(hu[i] & 0xFFFFu), p);
+          const float a1 = act_out(0, bf16_to_f32(hg[i] >> 16), bf16_to_f32(hu[i] >> 16), p);
           ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
         }
-        *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = make_uint4(hg[0], hg[1], hg[2], hg[3]);
-        *reinterpret_cast<uint4*>(A.h + grow * F1 + ffn + f) = make_uint4(hu[0], hu[1], hu[2], hu[3]);
-        *reinterpret_cast<uint4*>(A.a_out + grow * ffn + f) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        out_store(rh, vh, (uint32_t)ur * hrow, hg[0], hg[1], hg[2], hg[3]);
+        out_store(rh, vh, (uint32_t)ur * hrow + arow, hu[0], hu[1], hu[2], hu[3]);   // up half: + ffn
+        out_store(ra, va, (uint32_t)ur * arow, ow[0], ow[1], ow[2], ow[3]);
       }
     } else {
+      const __amdgpu_buffer_rsrc_t rh = out_rsrc(A.h + c.arow0 * F1 + c.nrow0, (int64_t)c.arows * hrow);
+      const __amdgpu_buffer_rsrc_t ra = out_rsrc(A.a_out + c.arow0 * ffn + c.nrow0, (int64_t)c.arows * arow);
+      const int lrow = tid >> 4, sc = 8 * (tid & 15);
+      const int col = 128 * (sc >> 6) + 64 * Q + (sc & 63);
+      const bool fok = c.nrow0 + col < ffn;
+      const uint32_t vh = fok ? (uint32_t)lrow * hrow + (uint32_t)(2 * col) : kOutOfRange;
+      const uint32_t va = fok ? (uint32_t)lrow * arow + (uint32_t)(2 * col) : kOutOfRange;
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int task = it * NTHREADS + tid;
-        const int sr = task >> 4;
-        const int sc = 8 * (task & 15);
-        const int trow = chunk_row(TM, sr);
-        const int64_t f = c.nrow0 + 128 * (sc >> 6) + 64 * Q + (sc & 63);
-        if (trow >= c.arows || f >= ffn) continue;
-        const int64_t grow = c.arow0 + trow;
-        const float p = A.probs[grow];
+        const int ur = 128 * (it >> 1) + 32 * TM + 16 * (it & 1);
+        const int trow = ur + lrow;
+        const float p = A.probs[c.arow0 + (trow < c.arows ? trow : c.arows - 1)];
+        const float* src = st + (16 * it + lrow) * EPC_LD + sc;
         float hv[8];
-        *reinterpret_cast<float4*>(hv) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc);
-        *reinterpret_cast<float4*>(hv + 4) = *reinterpret_cast<const float4*>(st + sr * EPC_LD + sc + 4);
+        *reinterpret_cast<float4*>(hv) = *reinterpret_cast<const float4*>(src);
+        *reinterpret_cast<float4*>(hv + 4) = *reinterpret_cast<const float4*>(src + 4);
         uint32_t hw[4], ow[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t h0 = f32_to_bf16_bits(hv[2 * i]), h1 = f32_to_bf16_bits(hv[2 * i + 1]);
-          hw[i] = h0 | (h1 << 16);
-          const float a0 = act_out(1, bf16_to_f32(h0), 0.0f, p);
-          const float a1 = act_out(1, bf16_to_f32(h1), 0.0f, p);
+          hw[i] = pack_bf16x2(hv[2 * i], hv[2 * i + 1]);
+          const float a0 = act_out(1, bf16_to_f32(hw[i] & 0xFFFFu), 0.0f, p);
+          const float a1 = act_out(1, bf16_to_f32(hw[i] >> 16), 0.0f, p);
           ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
         }
-        *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(A.a_out + grow * ffn + f) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        out_store(rh, vh, (uint32_t)ur * hrow, hw[0], hw[1], hw[2], hw[3]);
+        out_store(ra, va, (uint32_t)ur * arow, ow[0], ow[1], ow[2], ow[3]);
       }
     }
   }
@@ -1498,6 +1512,10 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
     const int64_t big = (MODE == MODE_FPROP) ? std::max(g.M * g.K, (int64_t)g.G * brows * g.K)
                                              : std::max(g.N, g.K) * rows_bound;
     if (big >= (1LL << 32)) return hipErrorInvalidValue;
+    // epilogue stores address one tile (256 rows) of an output through one buffer resource,
+    // with kOutOfRange marking a lane's columns as outside it
+    const int64_t orow_bytes = (EPI == EPI_FC1) ? 4 * g.ffn : (MODE == MODE_FPROP ? g.N : g.K) * 4;
+    if (256 * orow_bytes >= (int64_t)kOutOfRange) return hipErrorInvalidValue;
   }
   GemmArgs a = g;
   a.group_rows = 4;
