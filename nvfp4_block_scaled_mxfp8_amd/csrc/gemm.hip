@@ -1093,8 +1093,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
 // Epilogue of the persistent kernel: the 256 x 256 fp32 tile leaves the accumulators in 8
 // chunks of 64 rows x 128 columns (32 KB, one ring slot).  Chunk ch holds MFMA tile row
 // tm = ch / 2 of both wave halves (staged row sr -> tile row chunk_row(tm, sr)) and two of each
-// wave's four MFMA column tiles: tn = 2 q, 2 q + 1 (q = ch % 2), or for the SwiGLU fc1
-// tn = q, q + 2 (32 gate and the matching 32 up columns).  The accumulators are written to LDS
+// wave's four MFMA column tiles: tn = 2 q, 2 q + 1 (q = ch % 2), or for the SwiGLU fc1 all
+// four column tiles of the waves with wn = q (64 gate and the matching 64 up columns), so
+// that every output row segment a chunk stores is a whole 128-byte line (half-line
+// streaming stores cost about twice as much).  The accumulators are written to LDS
 // straight from the accumulator registers (inline ds_write_b32 with an AGPR operand), so
 // they are never copied to vector registers.
 __device__ __forceinline__ int chunk_row(int tm, int sr) { return ((sr >> 5) << 7) + 32 * tm + (sr & 31); }
@@ -1108,19 +1110,30 @@ __device__ __forceinline__ void lds_writes_done() { asm volatile("s_waitcnt lgkm
 
 // Stage chunk ch: wave (wm, wn) writes acc[tm][tn0 + d tn1] (d = 0, 1) at staged rows
 // 32 wm + (r / 4) 8 + 4 j + r % 4, staged columns 64 wn + 32 d + m.
-template <int TM, int TN0, int TN1>
-__device__ __forceinline__ void stage_chunk(const v16f (&acc)[4][4], uint32_t base) {
-  // base = LDS byte address of staged (32 wm + 4 j, 64 wn + m)
 #define GMLP_W(D, TN, R) lds_write_acc<((8 * ((R) >> 2) + ((R) & 3)) * EPC_LD + 32 * (D)) * 4>(base, acc[TM][TN][R]);
 #define GMLP_W16(D, TN) GMLP_W(D, TN, 0) GMLP_W(D, TN, 1) GMLP_W(D, TN, 2) GMLP_W(D, TN, 3) GMLP_W(D, TN, 4) \
   GMLP_W(D, TN, 5) GMLP_W(D, TN, 6) GMLP_W(D, TN, 7) GMLP_W(D, TN, 8) GMLP_W(D, TN, 9) GMLP_W(D, TN, 10)          \
   GMLP_W(D, TN, 11) GMLP_W(D, TN, 12) GMLP_W(D, TN, 13) GMLP_W(D, TN, 14) GMLP_W(D, TN, 15)
+template <int TM, int TN0, int TN1>
+__device__ __forceinline__ void stage_chunk(const v16f (&acc)[4][4], uint32_t base) {
+  // base = LDS byte address of staged (32 wm + 4 j, 64 wn + m)
   GMLP_W16(0, TN0)
   GMLP_W16(1, TN1)
-#undef GMLP_W16
-#undef GMLP_W
   lds_writes_done();
 }
+// SwiGLU fc1: the chunk holds all four column tiles of one wave column wn (gate features
+// 64 wn + [0, 64) at staged columns [0, 64), the matching up features at [64, 128)), so that
+// each output row segment of the chunk is 128 contiguous bytes; base = staged (32 wm + 4 j, m)
+template <int TM>
+__device__ __forceinline__ void stage_chunk4(const v16f (&acc)[4][4], uint32_t base) {
+  GMLP_W16(0, 0)
+  GMLP_W16(1, 1)
+  GMLP_W16(2, 2)
+  GMLP_W16(3, 3)
+  lds_writes_done();
+}
+#undef GMLP_W16
+#undef GMLP_W
 
 // Output stores of the persistent kernel: one buffer resource per output matrix and tile, based
 // at the tile's first row and column and sized to its valid rows, so that the rows past the
@@ -1142,15 +1155,18 @@ __device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t vof
 
 template <int MODE, int EPI, int CH>
 __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
-                                          int tid, int wm, int wn, int lane) {
+                                          int tid, int wm, int wn, int lane, const float (&pr)[16]) {
   constexpr int TM = CH >> 1, Q = CH & 1;
   const bool swiglu = (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0);
   const float* st = reinterpret_cast<const float*>(buf);
   {
     const int m = lane & 31, j = lane >> 5;
-    const uint32_t base = (uint32_t)(uintptr_t)buf + (uint32_t)(((32 * wm + 4 * j) * EPC_LD + 64 * wn + m) * 4);
-    if (swiglu) stage_chunk<TM, Q, Q + 2>(acc, base);
-    else stage_chunk<TM, 2 * Q, 2 * Q + 1>(acc, base);
+    const uint32_t base = (uint32_t)(uintptr_t)buf + (uint32_t)(((32 * wm + 4 * j) * EPC_LD + m) * 4);
+    if (swiglu) {
+      if (wn == Q) stage_chunk4<TM>(acc, base);
+    } else {
+      stage_chunk<TM, 2 * Q, 2 * Q + 1>(acc, base + 256u * (uint32_t)wn);
+    }
   }
   __syncthreads();
   if (EPI == EPI_STORE || EPI == EPI_STORE32) {
@@ -1188,28 +1204,27 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
     const int64_t F1 = (A.act == 0) ? 2 * ffn : ffn;
     const uint32_t hrow = (uint32_t)(F1 * 2), arow = (uint32_t)(ffn * 2);
     if (A.act == 0) {
-      // staged columns 64 wn + [gate 32 | up 32] hold features f = 128 nt + 64 wn + 32 Q + [0, 32);
-      // lanes [8 r, 8 r + 8) take staged row r + 32 it, 8 features each
-      const int64_t f0 = (int64_t)c.nt * 128;
+      // staged columns [gate 64 | up 64] hold features f = 128 nt + 64 Q + [0, 64); lanes
+      // [8 r, 8 r + 8) take staged row r + 32 it, 8 features each (one 128-byte row segment)
+      const int64_t f0 = (int64_t)c.nt * 128 + 64 * Q;
       const __amdgpu_buffer_rsrc_t rh = out_rsrc(A.h + c.arow0 * F1 + f0, (int64_t)c.arows * hrow);
       const __amdgpu_buffer_rsrc_t ra = out_rsrc(A.a_out + c.arow0 * ffn + f0, (int64_t)c.arows * arow);
       const int lrow = tid >> 3, g8 = tid & 7;
-      const int sc = 64 * (g8 >> 2) + 8 * (g8 & 3);
-      const int fc = 64 * (g8 >> 2) + 32 * Q + 8 * (g8 & 3);
+      const int sc = 8 * g8;
+      const int fc = 8 * g8;
       const bool fok = f0 + fc < ffn;
       const uint32_t vh = fok ? (uint32_t)lrow * hrow + (uint32_t)(2 * fc) : kOutOfRange;
       const uint32_t va = fok ? (uint32_t)lrow * arow + (uint32_t)(2 * fc) : kOutOfRange;
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         const int ur = 128 * it + 32 * TM;
-        const int trow = ur + lrow;
-        const float p = A.probs[c.arow0 + (trow < c.arows ? trow : c.arows - 1)];
+        const float p = pr[4 * TM + it];
         const float* src = st + (32 * it + lrow) * EPC_LD + sc;
         float gv[8], uv[8];
         *reinterpret_cast<float4*>(gv) = *reinterpret_cast<const float4*>(src);
         *reinterpret_cast<float4*>(gv + 4) = *reinterpret_cast<const float4*>(src + 4);
-        *reinterpret_cast<float4*>(uv) = *reinterpret_cast<const float4*>(src + 32);
-        *reinterpret_cast<float4*>(uv + 4) = *reinterpret_cast<const float4*>(src + 36);
+        *reinterpret_cast<float4*>(uv) = *reinterpret_cast<const float4*>(src + 64);
+        *reinterpret_cast<float4*>(uv + 4) = *reinterpret_cast<const float4*>(src + 68);
         uint32_t hg[4], hu[4], ow[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1234,8 +1249,7 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int ur = 128 * (it >> 1) + 32 * TM + 16 * (it & 1);
-        const int trow = ur + lrow;
-        const float p = A.probs[c.arow0 + (trow < c.arows ? trow : c.arows - 1)];
+        const float p = pr[4 * TM + it];
         const float* src = st + (16 * it + lrow) * EPC_LD + sc;
         float hv[8];
         *reinterpret_cast<float4*>(hv) = *reinterpret_cast<const float4*>(src);
@@ -1281,14 +1295,30 @@ __device__ __forceinline__ void epi_zero(const GemmArgs& A, const Ctx& c, int ti
 template <int MODE, int EPI>
 __device__ __forceinline__ void mx_epilogue(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
                                             int tid, int wm, int wn, int lane) {
-  epi_chunk<MODE, EPI, 0>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 1>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 2>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 3>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 4>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 5>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 6>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 7>(A, c, acc, buf, tid, wm, wn, lane);
+  // fc1: the routing probabilities of the thread's output rows, all fetched up front (entry
+  // 4 TM + it is the row that epi_chunk's iteration it of MFMA tile row TM stores)
+  float pr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pr[i] = 0.0f;
+  if (EPI == EPI_FC1) {
+    const bool swiglu = A.act == 0;
+#pragma unroll
+    for (int TM = 0; TM < 4; ++TM)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        if (swiglu && it >= 2) continue;
+        const int trow = swiglu ? 128 * it + 32 * TM + (tid >> 3) : 128 * (it >> 1) + 32 * TM + 16 * (it & 1) + (tid >> 4);
+        pr[4 * TM + it] = A.probs[c.arow0 + (trow < c.arows ? trow : c.arows - 1)];
+      }
+  }
+  epi_chunk<MODE, EPI, 0>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 1>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 2>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 3>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 4>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 5>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 6>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 7>(A, c, acc, buf, tid, wm, wn, lane, pr);
 }
 
 template <int MODE, int EPI>
