@@ -235,6 +235,73 @@ def backward(fwd, dy_bits):
     }
 
 
+# ----------------------------------------------------------------------------- sampled evaluation (MXFP8)
+# For MXFP8 every forward step and the dgrad chain are row-local: the row-wise cast blocks run
+# along a row, the GEMMs produce a row from that row, the activation and its derivative act
+# elementwise.  Rows of the full computation can therefore be evaluated on their own, which
+# lets full-size runs be checked on sampled rows.  A weight-gradient entry contracts one
+# feature column of each operand over the group's tokens (column-wise blocks of 32 tokens,
+# zero padded to P_g), so it needs those two columns over all of the group's rows.
+
+def _mx_rows(v):
+    q, s = mxfp8_quantize_rows(v)
+    return mxfp8_dequant_rows(q, s)
+
+
+def mxfp8_rows(x_bits, dy_bits, p, wd1, wd2, activation):
+    """Rows of one expert's MXFP8 forward + backward, exactly as ``forward`` / ``backward``
+    compute them.  ``wd1`` / ``wd2`` are that expert's dequantized weights
+    {"row": [N, K], "colT": [K, N]} (from ``quantize_weight``).  Returns h, a, y (fp64, before
+    its bf16 rounding), da, dh, dprob, dx (fp64, before its bf16 rounding)."""
+    p = np.asarray(p, dtype=np.float32).astype(np.float64)
+    xd = _mx_rows(bf16_bits_to_f64(x_bits))
+    h = round_bf16(xd @ wd1["row"].T)
+    a = round_bf16(act_forward(h, activation) * p[:, None])
+    y = _mx_rows(a) @ wd2["row"].T
+    da = round_bf16(_mx_rows(bf16_bits_to_f64(dy_bits)) @ wd2["colT"].T)
+    dh_raw, dprob = act_backward(h, da, p, activation)
+    dh = round_bf16(dh_raw)
+    dx = _mx_rows(dh) @ wd1["colT"].T
+    return {"h": h, "a": a, "y_f64": y, "da": da, "dh": dh, "dprob": dprob, "dx_f64": dx}
+
+
+def _mx_col(v):
+    """Column-wise MXFP8 cast of one feature over a group's tokens, dequantized (length m)."""
+    m = v.shape[0]
+    t = np.zeros((1, padded(m)))
+    t[0, :m] = v
+    return _mx_rows(t)[0, :m]
+
+
+def mxfp8_wgrad_entries(x_bits, dy_bits, p, wd1, wd2, activation, dw1_idx, dw2_idx):
+    """Entries (f1, k) of dW1_g = Q_col(dh_g)^T Q_col(x_g) and (n, f) of dW2_g = Q_col(dy_g)^T
+    Q_col(a_g) for one expert whose rows are ``x_bits`` / ``dy_bits`` (all of the group's
+    rows), fp64 before the bf16 rounding."""
+    p = np.asarray(p, dtype=np.float32).astype(np.float64)
+    x = bf16_bits_to_f64(x_bits)
+    dy = bf16_bits_to_f64(dy_bits)
+    xd, dyd = _mx_rows(x), _mx_rows(dy)
+    ffn = wd2["row"].shape[1]
+    glu = activation == SWIGLU
+
+    def h_cols(j):
+        cols = [j, ffn + j] if glu else [j]
+        return round_bf16(xd @ wd1["row"][cols].T)                       # [m, 1 or 2]
+
+    def a_col(f):
+        return round_bf16(act_forward(h_cols(f), activation)[:, 0] * p)
+
+    def dh_col(f1):
+        j = f1 % ffn if glu else f1
+        da = round_bf16(dyd @ wd2["colT"][j])
+        dh, _ = act_backward(h_cols(j), da[:, None], p, activation)
+        return round_bf16(dh[:, 1 if (glu and f1 >= ffn) else 0])
+
+    dw1 = np.array([_mx_col(dh_col(f1)) @ _mx_col(x[:, k]) for f1, k in dw1_idx])
+    dw2 = np.array([_mx_col(dy[:, n]) @ _mx_col(a_col(f)) for n, f in dw2_idx])
+    return dw1, dw2
+
+
 def reference_mlp_f64(x, m_splits, w1, w2, probs, activation):
     """Unquantized fp64 grouped MLP forward (no rounding anywhere), for format-error sanity checks."""
     out, off = [], 0
@@ -256,5 +323,6 @@ def rel_fro(a, b):
 
 
 __all__ = ["forward", "backward", "grouped_gemm_nt", "quantize_activation", "quantize_weight",
+           "mxfp8_rows", "mxfp8_wgrad_entries",
            "act_forward", "act_backward", "Recipe", "reference_mlp_f64", "rel_fro",
            "SWIGLU", "SRELU", "MXFP8", "NVFP4", "padded", "mxfp8_quantize_rows"]

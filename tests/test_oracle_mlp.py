@@ -136,3 +136,33 @@ def test_swiglu_halves_and_prob_placement():
     sig = lambda z: 1 / (1 + np.exp(-z))
     assert np.allclose(got, [[1 * sig(1) * 3, -2 * sig(-2) * 0.5]], rtol=1e-15)
     assert np.array_equal(O.act_forward(np.array([[-1.0, 2.0]]), O.SRELU), [[0.0, 4.0]])
+
+
+@pytest.mark.parametrize("act", [O.SWIGLU, O.SRELU])
+def test_sampled_rows_and_wgrad_entries_match_the_full_oracle(act):
+    """The sampled evaluators used at full size (rows on their own, weight-gradient entries from
+    two feature columns over a group's tokens) give the full unfused oracle's values: the same
+    rounded h, a, da, dh and dprob, and y, dx, dW1, dW2 to fp64 summation-order noise."""
+    splits = [70, 0, 161]
+    wl = small_case(splits, 64, 96, activation=act, recipe=O.MXFP8, seed=11)
+    rec = O.Recipe(O.MXFP8)
+    fwd = O.forward(wl.x, splits, wl.w1, wl.w2, wl.probs, act, rec)
+    bwd = O.backward(fwd, wl.dy)
+    F1, ffn, H = wl.w1.shape[1], wl.w2.shape[2], wl.w1.shape[2]
+    off = np.concatenate([[0], np.cumsum(splits)])
+    for e in (0, 2):
+        d1 = {"row": fwd["wq1"][1]["row"][e], "colT": fwd["wq1"][1]["colT"][e]}
+        d2 = {"row": fwd["wq2"][1]["row"][e], "colT": fwd["wq2"][1]["colT"][e]}
+        rows = np.array([off[e], off[e] + 1, off[e] + 33, off[e + 1] - 1])
+        r = O.mxfp8_rows(wl.x[rows], wl.dy[rows], wl.probs[rows], d1, d2, act)
+        for k, full in (("h", fwd["h"]), ("a", fwd["a"]), ("da", bwd["da"]), ("dh", bwd["dh"])):
+            assert np.array_equal(r[k], full[rows]), k
+        np.testing.assert_allclose(r["dprob"], bwd["dprob"][rows], rtol=1e-6, atol=1e-9)
+        np.testing.assert_allclose(r["y_f64"], fwd["y_f64"][rows], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(r["dx_f64"], bwd["dx_f64"][rows], rtol=1e-10, atol=1e-12)
+        i1 = [(0, 0), (F1 - 1, H - 1), (ffn // 2, 7), (F1 // 2 + 3, 40)]
+        i2 = [(0, 0), (H - 1, ffn - 1), (5, 50)]
+        w1e, w2e = O.mxfp8_wgrad_entries(wl.x[off[e]:off[e + 1]], wl.dy[off[e]:off[e + 1]],
+                                         wl.probs[off[e]:off[e + 1]], d1, d2, act, i1, i2)
+        np.testing.assert_allclose(w1e, [bwd["dw1_f64"][e, f, k] for f, k in i1], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(w2e, [bwd["dw2_f64"][e, n, f] for n, f in i2], rtol=1e-10, atol=1e-12)
