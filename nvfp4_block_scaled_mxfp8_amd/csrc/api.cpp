@@ -168,7 +168,6 @@ gmlp_status quant_core(const void* x, int64_t M, int64_t K, const int32_t* m_spl
   SplitTables T = carve_tables(b, G);
   if (!ws || ws_bytes < b.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", b.off);
   Launcher L{stream};
-  if (!L.check(launch_fill_u32(T.flags, 0u, 1, stream), "fill")) return L.st;
   if (!L.check(launch_scan(m_splits, G, M, T, stream), "scan")) return L.st;
   g_counts[CNT_SCAN]++;
   const uint16_t* xx = static_cast<const uint16_t*>(x);
@@ -299,7 +298,7 @@ BwdWs carve_bwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, c
   }
   // dL/dp partials: per 256-column tile of the NVFP4 fused epilogue, per 128 features of the
   // MXFP8 fused activation-gradient cast
-  w.dprob_part = b.take<float>((size_t)ceil_div(ffn, 128) * M);
+  w.dprob_part = b.take<float>((size_t)ceil_div(ffn, 64) * M);
   return w;
 }
 
@@ -423,7 +422,6 @@ gmlp_status gmlp_weight_quantize(const void* w, const void* const* w_ptrs, int32
   if (!ws || ws_bytes < b.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", b.off);
   Launcher L{stream};
   if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(split), (uint32_t)N, 1, stream), "fill")) return L.st;
-  if (!L.check(launch_fill_u32(T.flags, 0u, 1, stream), "fill")) return L.st;
   if (!L.check(launch_scan(split, 1, N, T, stream), "scan")) return L.st;
   const int64_t nkt = ceil_div(K, 128), nkt_t = ceil_div(N, 128);
   for (int e = 0; e < E; ++e) {
@@ -468,7 +466,6 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
   SplitTables T = carve_tables(bb, G);
   if (!ws || ws_bytes < bb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", bb.off);
   Launcher L{stream};
-  if (!L.check(launch_fill_u32(T.flags, 0u, 1, stream), "fill")) return L.st;
   if (!L.check(launch_scan(m_splits, G, M, T, stream), "scan")) return L.st;
   GemmArgs g = gemm_base(layout == GMLP_GEMM_FPROP ? MODE_FPROP : MODE_WGRAD, recipe, EPI_STORE, T, G);
   g.M = M;
@@ -510,7 +507,6 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
   if (!A->ws || A->ws_bytes < wb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", wb.off);
 
   Launcher L{stream};
-  if (!L.check(launch_fill_u32(W.T.flags, 0u, 1, stream), "fill")) return L.st;
   if (!L.check(launch_scan(A->m_splits, E, M, W.T, stream), "scan")) return L.st;
   g_counts[CNT_SCAN]++;
   const uint16_t* x = static_cast<const uint16_t*>(A->x);
@@ -620,7 +616,6 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
   if (!A->ws || A->ws_bytes < wb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", wb.off);
 
   Launcher L{stream};
-  if (!L.check(launch_fill_u32(W.T.flags, 0u, 1, stream), "fill")) return L.st;
   if (!L.check(launch_scan(A->m_splits, E, M, W.T, stream), "scan")) return L.st;
   g_counts[CNT_SCAN]++;
 
@@ -679,7 +674,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     d.dprob_part = W.dprob_part;
     if (!L.check(launch_dact_quant(d, W.T, E, M, stream), "activation gradient cast")) return L.st;
     g_counts[CNT_MXQ]++;
-    if (!L.check(launch_dprob_reduce(W.dprob_part, (int)ceil_div(ffn, 128), M, A->dprobs, stream), "dprob reduce"))
+    if (!L.check(launch_dprob_reduce(W.dprob_part, (int)ceil_div(ffn, 64), M, A->dprobs, stream), "dprob reduce"))
       return L.st;
     g_counts[CNT_DPROB]++;
   }

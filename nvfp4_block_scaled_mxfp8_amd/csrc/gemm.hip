@@ -1500,11 +1500,22 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
   wait_vmcnt<0>();                     // the DMAs past the last tile (empty) before the LDS is released
 }
 
-__global__ void dprob_reduce_kernel(const float* __restrict__ part, int nparts, int64_t M, float* __restrict__ out) {
+// One thread per row sums the partials in tile order; the loads of 8 partials are issued
+// together (small blocks: enough of them to spread over every CU).
+__global__ __launch_bounds__(64) void dprob_reduce_kernel(const float* __restrict__ part, int nparts, int64_t M,
+                                                          float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= M) return;
   float s = 0.0f;
-  for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * M + i];
+  int p = 0;
+  for (; p + 8 <= nparts; p += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = part[(int64_t)(p + k) * M + i];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
+  for (; p < nparts; ++p) s += part[(int64_t)p * M + i];
   out[i] = s;
 }
 
@@ -1598,7 +1609,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_dprob_reduce(const float* part, int nparts, int64_t M, float* out, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(dprob_reduce_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, part, nparts, M, out);
+  hipLaunchKernelGGL(dprob_reduce_kernel, dim3((unsigned)((M + 63) / 64)), dim3(64), 0, s, part, nparts, M, out);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ struct DactArgs {
   int64_t ffn;
   MxOut dh;             // MXFP8 dh [M, F1], row- and/or column-wise (null pointers: not written)
   MxOut a2;             // column-wise MXFP8 of the rebuilt fc2 input [M, ffn], or all null
-  float* dprob_part;    // [ffn / 128][M]
+  float* dprob_part;    // [ffn / 64][M]
 };
 
 struct NvOut {

@@ -39,9 +39,11 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ m
   __shared__ int s_d[4][256];
   __shared__ long long carry_raw;
   __shared__ int carry[5];
+  __shared__ uint32_t s_flags;
   const int t = threadIdx.x;
   if (t == 0) {
     carry_raw = 0;
+    s_flags = 0;
     for (int i = 0; i < 5; ++i) carry[i] = 0;
     T.row_off[0] = T.col_off[0] = T.colw_off[0] = T.t128_off[0] = T.t256_off[0] = 0;
   }
@@ -93,7 +95,9 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ m
     if (carry_raw > M) flags |= 2u;
     if (carry_raw < M) flags |= 4u;
   }
-  if (flags) atomicOr(T.flags, flags);
+  if (flags) atomicOr(&s_flags, flags);
+  __syncthreads();
+  if (t == 0) *T.flags = s_flags;        // the whole word: no clearing launch needed before the scan
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
@@ -292,121 +296,171 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __rest
 // One pass of the backward between the fc2 dgrad and the fc1 GEMMs: from da = dy W2 (bf16
 // [M, ffn]), h = fc1 output (bf16 [M, F1]) and the routing probabilities, it forms
 // dh = bf16(d(act(h) p)/dh . da) and casts it row-wise (fc1 dgrad) and column-wise (fc1
-// wgrad) to MXFP8 without writing dh itself; the per-row dL/dp partial sums of the tile's 128
+// wgrad) to MXFP8 without writing dh itself; the per-row dL/dp partial sums of the tile's 64
 // features go to dprob_part[feature tile][row]; with a2 set it also rebuilds the fc2 input
 // a = bf16(act(h) p) and casts it column-wise (fc2 wgrad with activation recompute).
-// Tile = 128 tokens x 128 of the ffn features; for SwiGLU the gate and up gradients of those
-// features are dh columns f and ffn + f.
+//
+// Tile = 128 tokens x 64 of the ffn features (one 64-byte K panel of each output; for SwiGLU
+// the gate and up gradients of those features are dh columns f and ffn + f).  Thread -> rows
+// 32 j + tid / 8 (j = 0..3), features 8 (tid % 8) .. + 7: every load instruction reads 32 whole
+// 128-byte row segments of each input, the 8 lanes of a row reduce its dL/dp partial, a
+// 32-feature block is a lane quad, and the lanes of a row store one whole 64-byte panel row.
+// Parked tiles (bf16 [128 tokens][DLW]) feed the column pass; a small tile (37 KB of LDS
+// without the rebuild) keeps four workgroups per CU in flight.
+constexpr int DF = 64;                // features per tile
+constexpr int DLW = DF + 8;           // parked row stride (bf16): 144 bytes, 16-byte aligned
+// Element (token r, feature c) of a parked tile: the column pass reads 16 features of four
+// 16-token runs 16 tokens apart in one instruction; 16 rows are a whole number of bank lines,
+// so the XOR moves the four runs to four different 32-byte windows.
+__device__ __forceinline__ int dtile_off(int r, int c) { return r * DLW + (c ^ (((r >> 4) & 3) << 4)); }
+
+// Column-wise MXFP8 cast of a parked [128 tokens][64 features] tile whose features are
+// kf0 .. kf0 + 63 of a K-feature tensor (token panels, as in col_cast_tile).  Task
+// u = 256 k + tid (k = 0, 1) -> feature c = tid / 4, token half k, 16-token part p = tid % 4.
+__device__ __forceinline__ void col_cast_tile64(const uint16_t* tile, const TileInfo& ti, int64_t K, int64_t kf0,
+                                                const SplitTables& T, const MxOut& o, int tid) {
+  const int p = tid & 3;
+  const int c = tid >> 2;
+  const int P = (ti.m + 127) & ~127;
+  const int64_t colbase = K * (int64_t)T.col_off[ti.g];
+  uint32_t word = 0;                               // the 128-token MFMA scale word of feature c
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int tok0 = 64 * half + 16 * p;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = bf16_to_f32(tile[dtile_off(tok0 + i, c)]);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    const uint32_t code = e8m0_code(amax);
+    const float inv = e8m0_inv_scale(code);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = cvt_e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
+    // a valid tile starts below m <= P and P is a multiple of 128: all its tokens are inside P
+    __builtin_nontemporal_store(v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
+                                reinterpret_cast<v4i*>(o.col_data + colbase + (((ti.t0 / 64) + half) * K + kf0 + c) * 64 + 16 * p));
+    if (o.col_scale && (p & 1) == 0)
+      o.col_scale[colbase / 32 + (kf0 + c) * (P / 32) + ti.t0 / 32 + 2 * half + (p >> 1)] = (uint8_t)code;
+    word |= code << (8 * (2 * half + (p >> 1)));
+  }
+  word |= (uint32_t)__shfl_xor((int)word, 2, 64);
+  if (o.col_scale_mfma && p == 0)
+    o.col_scale_mfma[K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K + kf0 + c] = word;
+}
+
 template <bool SWIGLU, bool WANT_A>
-__global__ __launch_bounds__(256, 2) void dact_quant_kernel(DactArgs D, SplitTables T, int G, int64_t M) {
+__global__ __launch_bounds__(256, (SWIGLU && WANT_A) ? 2 : 4) void dact_quant_kernel(DactArgs D, SplitTables T, int G,
+                                                                                    int64_t M) {
   constexpr int NT = 1 + (SWIGLU ? 1 : 0) + (WANT_A ? 1 : 0);   // parked tiles: dgate (dh), dup, a
-  __shared__ __align__(16) uint16_t tiles[NT][QT * LDW];
+  __shared__ __align__(16) uint16_t tiles[NT][QT * DLW];
   const int64_t ffn = D.ffn;
   const int64_t F1 = SWIGLU ? 2 * ffn : ffn;
   TileInfo ti;
-  if (!tile_info(T, G, ffn, ti)) return;
+  {
+    const int tt = blockIdx.y;
+    if (G <= 0 || tt >= T.t128_off[G]) return;
+    ti.g = find_group(T.t128_off, G, tt);
+    ti.gstart = T.row_off[ti.g];
+    ti.m = T.row_off[ti.g + 1] - (int)ti.gstart;
+    ti.t0 = (tt - T.t128_off[ti.g]) * QT;
+    ti.rows = min(QT, ti.m - ti.t0);
+    ti.k0 = (int64_t)blockIdx.x * DF;
+    ti.kcols = DF;                                 // ffn is a multiple of 128
+    if (ti.rows <= 0) return;
+  }
   const int tid = threadIdx.x;
-  // thread -> rows r4 and 64 + r4 of the tile, features 32 q .. 32 q + 31
-  const int r4 = tid >> 2;
-  const int q = tid & 3;
-  uint4 qd[2][4], qg[2][4], qu[2][4];
+  const int rl = tid >> 3, g = tid & 7;
+  uint4 qd[4], qg[4], qu[4];
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    const int r = 64 * ps + r4;
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * j + rl;
     const bool ok = r < ti.rows;
     const int64_t row = ti.gstart + ti.t0 + r;
-    const uint4* sd = reinterpret_cast<const uint4*>(D.da + row * ffn + ti.k0 + 32 * q);
-    const uint4* sg = reinterpret_cast<const uint4*>(D.h + row * F1 + ti.k0 + 32 * q);
-    const uint4* su = reinterpret_cast<const uint4*>(D.h + row * F1 + ffn + ti.k0 + 32 * q);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      qd[ps][j] = ok ? sd[j] : make_uint4(0, 0, 0, 0);
-      qg[ps][j] = ok ? sg[j] : make_uint4(0, 0, 0, 0);
-      qu[ps][j] = (SWIGLU && ok) ? su[j] : make_uint4(0, 0, 0, 0);
-    }
+    qd[j] = ok ? *reinterpret_cast<const uint4*>(D.da + row * ffn + ti.k0 + 8 * g) : make_uint4(0, 0, 0, 0);
+    qg[j] = ok ? *reinterpret_cast<const uint4*>(D.h + row * F1 + ti.k0 + 8 * g) : make_uint4(0, 0, 0, 0);
+    qu[j] = (SWIGLU && ok) ? *reinterpret_cast<const uint4*>(D.h + row * F1 + ffn + ti.k0 + 8 * g)
+                           : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    const int r = 64 * ps + r4;
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * j + rl;
     const bool ok = r < ti.rows;
     const int64_t grow = ti.gstart + ti.t0 + (ok ? r : 0);
     const float p = ok ? D.probs[grow] : 0.0f;
+    float vd[8], vg[8], vu[8];
+    unpack8(qd[j], vd);
+    unpack8(qg[j], vg);
+    unpack8(qu[j], vu);
     // bf16 results, two per word: dgate (or dh), dup, rebuilt a
-    uint32_t p0[16], p1[16], pa[16];
+    uint32_t p0[4], p1[4], pa[4];
     float psum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float vd[8], vg[8], vu[8];
-      unpack8(qd[ps][j], vd);
-      unpack8(qg[ps][j], vg);
-      unpack8(qu[ps][j], vu);
+    for (int i = 0; i < 8; i += 2) {
+      float r0[2], r1[2], ra[2];
 #pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        uint32_t w0 = 0, w1 = 0, wa = 0;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          float a0, a1, dp, av = 0.0f;
-          const float u = SWIGLU ? vu[i + k] : 0.0f;
-          if (WANT_A) act_grad_out(SWIGLU ? 0 : 1, vg[i + k], u, vd[i + k], p, a0, a1, dp, av);
-          else act_grad(SWIGLU ? 0 : 1, vg[i + k], u, vd[i + k], p, a0, a1, dp);
-          psum += dp;
-          w0 |= f32_to_bf16_bits(a0) << (16 * k);
-          w1 |= f32_to_bf16_bits(a1) << (16 * k);
-          wa |= (__float_as_uint(av) >> 16) << (16 * k);
-        }
-        p0[4 * j + i / 2] = w0;
-        p1[4 * j + i / 2] = w1;
-        pa[4 * j + i / 2] = wa;
+      for (int k = 0; k < 2; ++k) {
+        float dp, av = 0.0f;
+        const float u = SWIGLU ? vu[i + k] : 0.0f;
+        if (WANT_A) act_grad_out(SWIGLU ? 0 : 1, vg[i + k], u, vd[i + k], p, r0[k], r1[k], dp, av);
+        else act_grad(SWIGLU ? 0 : 1, vg[i + k], u, vd[i + k], p, r0[k], r1[k], dp);
+        psum += dp;
+        ra[k] = av;
       }
+      p0[i / 2] = pack_bf16x2(r0[0], r0[1]);
+      p1[i / 2] = pack_bf16x2(r1[0], r1[1]);
+      pa[i / 2] = (__float_as_uint(ra[0]) >> 16) | (__float_as_uint(ra[1]) & 0xFFFF0000u);
     }
-    // dL/dp partial of the row over the tile's 128 features (fixed order: pairs, then halves)
+    // dL/dp partial of the row over the tile's 64 features (fixed order: the thread's 8, then
+    // pairs, quads, halves)
     psum += __shfl_xor(psum, 1, 64);
     psum += __shfl_xor(psum, 2, 64);
-    if (q == 0 && ok) D.dprob_part[(int64_t)blockIdx.x * M + grow] = psum;
-    // row-wise cast of one 32-block (gate / plain gradient at feature f, up at ffn + f), and
-    // the values parked for the column pass
+    psum += __shfl_xor(psum, 4, 64);
+    if (g == 0 && ok) D.dprob_part[(int64_t)blockIdx.x * M + grow] = psum;
+    // row-wise cast of the thread's 8 values of one 32-block (gate / plain gradient at feature
+    // f, up at ffn + f), and the values parked for the column pass
     auto row_cast = [&](const uint32_t* pk, int64_t f, uint16_t* tile) {
       if (D.dh.row_data) {
-        float v[32];
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 4; ++i) {
           v[2 * i] = bf16_to_f32(pk[i] & 0xFFFFu);
           v[2 * i + 1] = bf16_to_f32(pk[i] >> 16);
         }
-        uint32_t w[8];
-        const uint32_t code = mx_block(v, w);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        const uint32_t code = e8m0_code(amax);
+        const float inv = e8m0_inv_scale(code);
+        const uint32_t w0 = cvt_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        const uint32_t w1 = cvt_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        // the tile's two blocks are bytes b, b + 1 of the row's 128-feature MFMA word
+        const uint32_t pair = code | ((uint32_t)__shfl_xor((int)code, 4, 64) << 8);
         if (ok) {
-          uint4* dst = reinterpret_cast<uint4*>(D.dh.row_data + (f / 64) * 64 * M + grow * 64 + 32 * (q & 1));
-          dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-          dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-          if (D.dh.row_scale) D.dh.row_scale[grow * (F1 / 32) + f / 32] = (uint8_t)code;
+          __builtin_nontemporal_store((uint64_t)w0 | ((uint64_t)w1 << 32),
+                                      reinterpret_cast<uint64_t*>(D.dh.row_data + (f / 64) * 64 * M + grow * 64 + (f & 63)));
+          if (D.dh.row_scale && (g & 3) == 0) D.dh.row_scale[grow * (F1 / 32) + f / 32] = (uint8_t)code;
+          if (D.dh.row_scale_mfma && g == 0)
+            *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(D.dh.row_scale_mfma) +
+                                         ((f / 128) * M + grow) * 4 + (f & 127) / 32) = (uint16_t)pair;
         }
-        // the 128-feature word: byte q from thread q of the row's four
-        uint32_t word = code << (8 * q);
-        word |= (uint32_t)__shfl_xor((int)word, 1, 64);
-        word |= (uint32_t)__shfl_xor((int)word, 2, 64);
-        if (D.dh.row_scale_mfma && q == 0 && ok) D.dh.row_scale_mfma[(f / 128) * M + grow] = word;
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(tile + tile_off(r, 32 * q + 8 * j)) =
-            make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
+      *reinterpret_cast<uint4*>(tile + dtile_off(r, 8 * g)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     };
-    row_cast(p0, ti.k0 + 32 * q, tiles[0]);
-    if (SWIGLU) row_cast(p1, ffn + ti.k0 + 32 * q, tiles[1]);
-    if (WANT_A) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(tiles[NT - 1] + tile_off(r, 32 * q + 8 * j)) =
-            make_uint4(pa[4 * j], pa[4 * j + 1], pa[4 * j + 2], pa[4 * j + 3]);
-    }
+    row_cast(p0, ti.k0 + 8 * g, tiles[0]);
+    if (SWIGLU) row_cast(p1, ffn + ti.k0 + 8 * g, tiles[1]);
+    if (WANT_A) *reinterpret_cast<uint4*>(tiles[NT - 1] + dtile_off(r, 8 * g)) = make_uint4(pa[0], pa[1], pa[2], pa[3]);
   }
   __syncthreads();
   if (D.dh.col_data) {
-    col_cast_tile(tiles[0], ti, F1, ti.k0, QF, T, D.dh, tid);
-    if (SWIGLU) col_cast_tile(tiles[1], ti, F1, ffn + ti.k0, QF, T, D.dh, tid);
+    col_cast_tile64(tiles[0], ti, F1, ti.k0, T, D.dh, tid);
+    if (SWIGLU) col_cast_tile64(tiles[1], ti, F1, ffn + ti.k0, T, D.dh, tid);
   }
-  if (WANT_A) col_cast_tile(tiles[NT - 1], ti, ffn, ti.k0, QF, T, D.a2, tid);
+  if (WANT_A) col_cast_tile64(tiles[NT - 1], ti, ffn, ti.k0, T, D.a2, tid);
 }
 
 // ----------------------------------------------------------------------------- signed Hadamard
@@ -611,7 +665,7 @@ hipError_t launch_mxfp8_quant(const uint16_t* x, int64_t M, int64_t K, SplitTabl
 
 hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const dim3 grid = tile_grid(M, d.ffn, G);
+  const dim3 grid((unsigned)(d.ffn / DF), (unsigned)((M + QT - 1) / QT + G));
   const bool a = d.a2.col_data != nullptr;
   if (d.act == 0 && !a) hipLaunchKernelGGL((dact_quant_kernel<true, false>), grid, dim3(256), 0, s, d, T, G, M);
   else if (d.act == 0) hipLaunchKernelGGL((dact_quant_kernel<true, true>), grid, dim3(256), 0, s, d, T, G, M);
