@@ -35,11 +35,14 @@ def parse():
     p.add_argument("--config", default="mid")
     p.add_argument("--recompute", type=int, default=0)
     p.add_argument("--kernel-reps", type=int, default=20)
-    p.add_argument("--cpu-sample-rows", type=int, default=512, help="rows per sampled expert for the oracle")
+    p.add_argument("--cpu-sample-rows", type=int, default=2560, help="rows per sampled expert for the oracle")
     p.add_argument("--cpu-sample-experts", type=int, default=2)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--traffic-probe", action="store_true",
                    help="only launch the dominant GEMM and a 1 GiB device copy (for rocprofv3 --pmc runs)")
+    p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarise two rocprofv3 --pmc runs of --traffic-probe (FETCH_SIZE, WRITE_SIZE) into "
+                        "the traffic record used by the bench line; needs no GPU")
     return p.parse_args()
 
 
@@ -106,6 +109,53 @@ def traffic_probe():
     print("traffic probe done", flush=True)
 
 
+TRAFFIC_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+    "-d gpurun_out/traffic/fetch -o p -- python3 bench.py --traffic-probe",
+    "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && rocprofv3 --pmc WRITE_SIZE --output-format csv "
+    "-d gpurun_out/traffic/write -o p -- python3 bench.py --traffic-probe",
+]
+
+
+def _counter_rows(d, counter):
+    """(kernel name, value) per dispatch, in dispatch order, from rocprofv3 counter CSVs under d."""
+    import csv
+    import glob
+    rows = []
+    for fn in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, v) for _, k, v in rows]
+
+
+def write_traffic(fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the probe's GEMM, each scaled by what the counter
+    reads for the 1 GiB copy, stored with the hash of the kernel sources they were taken with."""
+    fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
+    write = _counter_rows(write_dir, "WRITE_SIZE")
+    pick = lambda rows, key: [v for k, v in rows if key in k]
+    cf, cw = pick(fetch, "copyBuffer"), pick(write, "copyBuffer")
+    gf, gw = pick(fetch, "gemm_mx_kernel"), pick(write, "gemm_mx_kernel")
+    assert cf and cw and gf and gw, (len(cf), len(cw), len(gf), len(gw))
+    gib_kib = float(1 << 20)
+    fscale, wscale = gib_kib / cf[-1], gib_kib / cw[-1]
+    fb, wb = gf[-1] * 1024 * fscale, gw[-1] * 1024 * wscale
+    M, H, F1, E = 32768, 4096, 3072, 8
+    rec = {"kernel": "gmlp::gemm_mx_kernel<0, 0> (fc1-dgrad shape: M 32768, N 4096, K 3072, 8 experts)",
+           "source_sha256": kernel_source_hash(),
+           "fetch_kib_per_dispatch": gf, "write_kib_per_dispatch": gw,
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_scale": fscale, "write_scale": wscale,
+           "bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
+           "algorithmic_bytes": M * F1 + H * F1 * E + 4 * (F1 // 128) * M + 4 * (F1 // 128) * H * E + 2 * M * H,
+           "commands": TRAFFIC_COMMANDS}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({k: rec[k] for k in ("fetch_bytes", "write_bytes", "bytes_per_launch", "algorithmic_bytes")}))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -115,17 +165,20 @@ def main():
     if args.traffic_probe:
         traffic_probe()
         return
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               f"(the path shards by expert across GPUs; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
     import torch
     import nvfp4_block_scaled_mxfp8_amd as g
-    from workloads import CONFIGS, make_workload
+    from workloads import CONFIGS, iter_expert_weights, make_workload
 
     cfg = CONFIGS[args.config]
     t0 = time.perf_counter()
-    wl = make_workload(cfg)
+    wl = make_workload(cfg, with_weights=False)
     log(f"workload {cfg.name}: generated in {time.perf_counter() - t0:.1f}s; splits={wl.m_splits.tolist()}")
     E, H, ffn, F1, M = cfg.experts, cfg.hidden, cfg.ffn, cfg.f1, int(wl.m_splits.sum())
     dev = "cuda"
@@ -136,8 +189,13 @@ def main():
 
     x = up(wl.x)
     dy = up(wl.dy)
-    w1 = up(wl.w1.reshape(E * F1, H), (E, F1, H))
-    w2 = up(wl.w2.reshape(E * H, ffn), (E, H, ffn))
+    w1 = torch.empty((E, F1, H), dtype=torch.bfloat16, device=dev)
+    w2 = torch.empty((E, H, ffn), dtype=torch.bfloat16, device=dev)
+    for idx, a, b in iter_expert_weights(cfg, 0):           # drawn per expert, uploaded per chunk
+        n = len(idx)
+        w1[idx[0]:idx[-1] + 1].copy_(up(a.reshape(n * F1, H), (n, F1, H)))
+        w2[idx[0]:idx[-1] + 1].copy_(up(b.reshape(n * H, ffn), (n, H, ffn)))
+    log(f"weights on the device after {time.perf_counter() - t0:.1f}s")
     probs = torch.from_numpy(wl.probs).to(dev)
     splits = torch.from_numpy(wl.m_splits.astype(np.int32)).to(dev)
     kind = cfg.recipe
@@ -260,6 +318,7 @@ def cpu_baseline(wl, args):
     """The oracle (numpy fp64) on a bounded sample: the first R rows of the first few experts, full
     hidden / ffn, forward + backward, weights pre-quantized outside the timed region."""
     from oracle import mlp as O
+    from workloads import expert_weights
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
@@ -275,12 +334,13 @@ def cpu_baseline(wl, args):
         splits.append(r)
     idx = np.concatenate(rows)
     rec = O.Recipe(cfg.recipe, wl.sign_mask)
+    w1, w2 = expert_weights(cfg, 0, range(ne))
     t = time.perf_counter()
-    wq1 = O.quantize_weight(wl.w1[:ne], rec)
-    wq2 = O.quantize_weight(wl.w2[:ne], rec)
+    wq1 = O.quantize_weight(w1, rec)
+    wq2 = O.quantize_weight(w2, rec)
     log(f"cpu baseline: weights of {ne} experts quantized in {time.perf_counter() - t:.1f}s (untimed)")
     t = time.perf_counter()
-    fwd = O.forward(wl.x[idx], splits, wl.w1[:ne], wl.w2[:ne], wl.probs[idx], cfg.activation, rec, wq1=wq1, wq2=wq2)
+    fwd = O.forward(wl.x[idx], splits, w1, w2, wl.probs[idx], cfg.activation, rec, wq1=wq1, wq2=wq2)
     O.backward(fwd, wl.dy[idx])
     dt = time.perf_counter() - t
     m = int(sum(splits))

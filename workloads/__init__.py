@@ -186,6 +186,20 @@ def expert_weights(cfg, seed, experts):
     return w1, w2
 
 
+def iter_expert_weights(cfg, seed=0, chunk=16, threads=8):
+    """Yield (experts, W1 bits [n, F1, H], W2 bits [n, H, ffn]) for consecutive chunks of experts,
+    each expert drawn on a worker thread from its own child stream (identical to the full draw);
+    keeps host memory to one chunk for the largest workloads."""
+    from concurrent.futures import ThreadPoolExecutor
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    with ThreadPoolExecutor(threads) as ex:
+        for e0 in range(0, cfg.experts, chunk):
+            idx = list(range(e0, min(cfg.experts, e0 + chunk)))
+            parts = list(ex.map(lambda e: expert_weights(cfg, seed, [e]), idx))
+            yield idx, np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
 def small_case(m_splits, hidden, ffn, activation=SWIGLU, recipe=MXFP8, seed=0,
                x_std=1.0, w_std=None, backward=True, probs="uniform"):
     """A small ad-hoc case for parity tests (same stream layout as the configs)."""
