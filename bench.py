@@ -243,7 +243,7 @@ def main():
     dhq = g.group_quantize(dh, splits, rec, True, False)
     w1_dgrad = g.QTensor(w1q.kind, {"row_data": w1q.bufs["col_data"], "row_scale_mfma": w1q.bufs.get("col_scale_mfma"),
                                     "row_scale": w1q.bufs.get("col_scale"), "amax_pre": w1q.bufs.get("amax_pre")})
-    gws = g.quant_workspace(E, dev)
+    gws = torch.empty(g.grouped_gemm_ws_bytes(g.GEMM_FPROP, rec, E, M, H, F1), dtype=torch.uint8, device=dev)
     gout = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     for _ in range(3):
         g.lib().gmlp_grouped_gemm(g.GEMM_FPROP, rec, g.ctypes.byref(dhq.struct()), g.ctypes.byref(w1_dgrad.struct()),

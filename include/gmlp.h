@@ -192,7 +192,14 @@ typedef enum {
  * FPROP: a = row-wise quantized [M, K] tensor, b = weight fprop operand
  *        (b->row_*), n = N, k = K; C [M, N].
  * WGRAD: a, b = column-wise quantized tensors with rows N_a = n, N_b = k;
- *        C [G, n, k]; empty groups write zeros. */
+ *        C [G, n, k]; empty groups write zeros.
+ * ws: >= gmlp_grouped_gemm_ws_bytes for the same arguments. */
+/* Workspace bytes of one gmlp_grouped_gemm call with these sizes (host only).  MXFP8 needs
+ * only the split tables; NVFP4 also holds both operands expanded exactly to bf16
+ * (2 bytes per element of A and of B). */
+gmlp_status gmlp_grouped_gemm_ws_bytes(int32_t layout, gmlp_recipe recipe, int32_t G, int64_t M,
+                                       int64_t n, int64_t k, size_t* bytes);
+
 gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_grouped_q* a,
                               const gmlp_grouped_q* b, const int32_t* m_splits, int32_t G,
                               int64_t M, int64_t n, int64_t k, void* c, int32_t out_dtype,

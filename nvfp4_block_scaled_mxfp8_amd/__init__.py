@@ -103,6 +103,8 @@ _SIGS = {
     "gmlp_grouped_mlp_forward": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "gmlp_grouped_mlp_backward": (ctypes.c_int, [ctypes.POINTER(BwdArgs), ctypes.c_void_p]),
     "gmlp_last_launch_counts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]),
+    "gmlp_grouped_gemm_ws_bytes": (ctypes.c_int, [ctypes.c_int32, Recipe, ctypes.c_int32, ctypes.c_int64,
+                                                  ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]),
 }
 
 _lib = None
@@ -312,12 +314,19 @@ def weight_quantize(w, rec, out=None):
     return out
 
 
+def grouped_gemm_ws_bytes(layout, rec, G, M, n, k):
+    v = ctypes.c_size_t(0)
+    _check(lib().gmlp_grouped_gemm_ws_bytes(layout, rec, G, M, n, k, ctypes.byref(v)))
+    return v.value
+
+
 def grouped_gemm(layout, rec, a, b, m_splits, M, n, k, out_dtype=OUT_BF16, ws=None):
     G = m_splits.numel()
     dev = m_splits.device
     dt = torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16
     c = torch.empty((M, n) if layout == GEMM_FPROP else (G, n, k), dtype=dt, device=dev)
-    ws = ws if ws is not None else quant_workspace(G, dev)
+    if ws is None:
+        ws = torch.empty(grouped_gemm_ws_bytes(layout, rec, G, M, n, k), dtype=torch.uint8, device=dev)
     qa, qb = a.struct(), b.struct()
     _check(lib().gmlp_grouped_gemm(layout, rec, ctypes.byref(qa), ctypes.byref(qb), _p(m_splits), G, M, n, k,
                                    _p(c), out_dtype, _p(ws), ws.numel(), _stream(dev)))

@@ -260,18 +260,39 @@ FwdCtx carve_ctx(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, con
   return c;
 }
 
+// NVFP4 GEMM scratch: the two operands of one GEMM expanded to bf16 (see GemmArgs::xa, xb).
+struct NvScratch {
+  uint8_t* xa = nullptr;
+  uint8_t* xb = nullptr;
+};
+NvScratch carve_nv(Bump& b, const gmlp_recipe& r, int64_t a_elems, int64_t b_elems) {
+  NvScratch n;
+  if (is_mx(r)) return n;
+  n.xa = b.take<uint8_t>(2 * a_elems);
+  n.xb = b.take<uint8_t>(2 * b_elems);
+  return n;
+}
+void set_nv(GemmArgs& g, const NvScratch& n) {
+  g.xa = n.xa;
+  g.xb = n.xb;
+}
+
 struct FwdWs {
   SplitTables T;
   QBuf xq_row;
   uint16_t* a;
   QBuf aq_row;
+  NvScratch nv;
 };
-FwdWs carve_fwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, const gmlp_recipe& r) {
+FwdWs carve_fwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, const gmlp_recipe& r) {
+  const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
   FwdWs w;
   w.T = carve_tables(b, E);
   w.xq_row = carve_q(b, r, M, H, E, true, false, false);
   w.a = b.take<uint16_t>(M * ffn);
   w.aq_row = carve_q(b, r, M, ffn, E, true, false, false);
+  // fc1: x [M, H] and W1 [E, F1, H]; fc2: a [M, ffn] and W2 [E, H, ffn]
+  w.nv = carve_nv(b, r, M * std::max(H, ffn), (int64_t)E * H * std::max(F1, ffn));
   return w;
 }
 
@@ -283,6 +304,8 @@ struct BwdWs {
   uint16_t* a2;
   QBuf a2q;
   float* dprob_part;
+  NvScratch nv;
+  uint16_t* da;       // NVFP4: bf16 da between the fc2 dgrad and the activation gradient
 };
 int dact_ntiles(int64_t ffn) { return (int)ceil_div(ffn, 256); }
 BwdWs carve_bwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, const gmlp_recipe& r, bool recompute) {
@@ -299,6 +322,11 @@ BwdWs carve_bwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, c
   // dL/dp partials: per 256-column tile of the NVFP4 fused epilogue, per 128 features of the
   // MXFP8 fused activation-gradient cast
   w.dprob_part = b.take<float>((size_t)ceil_div(ffn, 64) * M);
+  // NVFP4 GEMM operands: A up to [padded tokens, max(H, F1)] (dy, dh row- or column-wise), B up to
+  // the larger of the weights [E, H, F1] and a column-wise [max(H, ffn), padded tokens]
+  const int64_t Pt = M + 127LL * E;
+  w.nv = carve_nv(b, r, Pt * std::max(H, F1), std::max((int64_t)E * H * F1, std::max(H, ffn) * Pt));
+  if (!is_mx(r)) w.da = b.take<uint16_t>(M * ffn);
   return w;
 }
 
@@ -311,7 +339,8 @@ gmlp_status mlp_common_checks(int64_t M, int E, int64_t H, int64_t ffn, int act,
   if (H % 128 != 0) return fail(GMLP_UNSUPPORTED, "dims: hidden must be a multiple of 128, got %lld", (long long)H);
   // the GEMMs address every quantized operand with 32-bit offsets
   const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
-  if ((M + 127LL * E) * std::max(H, F1) >= (1LL << 32) || (int64_t)E * F1 * H >= (1LL << 32))
+  const int64_t eb = is_mx(r) ? 1 : 2;             // NVFP4 operands run expanded to bf16
+  if (eb * (M + 127LL * E) * std::max(H, F1) >= (1LL << 32) || eb * (int64_t)E * F1 * H >= (1LL << 32))
     return fail(GMLP_UNSUPPORTED, "dims: a quantized operand would reach 4 GB (M = %lld, hidden %lld, ffn %lld)",
                 (long long)M, (long long)H, (long long)ffn);
   return GMLP_OK;
@@ -351,7 +380,7 @@ gmlp_status gmlp_query_sizes(int64_t M, int32_t experts, int64_t hidden, int64_t
   Bump c(nullptr);
   carve_ctx(c, M, experts, hidden, ffn, activation, recipe, recompute != 0);
   Bump f(nullptr);
-  carve_fwd_ws(f, M, experts, hidden, ffn, recipe);
+  carve_fwd_ws(f, M, experts, hidden, ffn, activation, recipe);
   Bump b(nullptr);
   carve_bwd_ws(b, M, experts, hidden, ffn, activation, recipe, recompute != 0);
   Bump q(nullptr);
@@ -452,6 +481,22 @@ gmlp_status gmlp_weight_quantize(const void* w, const void* const* w_ptrs, int32
   return ok();
 }
 
+gmlp_status gmlp_grouped_gemm_ws_bytes(int32_t layout, gmlp_recipe recipe, int32_t G, int64_t M, int64_t n, int64_t k,
+                                       size_t* bytes) {
+  if (!bytes) return fail(GMLP_INVALID_ARG, "null output");
+  gmlp_status st;
+  if ((st = check_recipe(recipe)) != GMLP_OK) return st;
+  if (layout != GMLP_GEMM_FPROP && layout != GMLP_GEMM_WGRAD) return fail(GMLP_INVALID_ARG, "unknown GEMM layout %d", layout);
+  if (G < 1 || M < 0 || n <= 0 || k <= 0) return fail(GMLP_INVALID_ARG, "dims: G, n, k must be positive and M >= 0");
+  Bump bb(nullptr);
+  carve_tables(bb, G);
+  const int64_t Pt = M + 127LL * G;
+  if (layout == GMLP_GEMM_FPROP) carve_nv(bb, recipe, M * k, (int64_t)G * n * k);
+  else carve_nv(bb, recipe, n * Pt, k * Pt);
+  *bytes = bb.off + 256;
+  return ok();
+}
+
 gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_grouped_q* a, const gmlp_grouped_q* b,
                               const int32_t* m_splits, int32_t G, int64_t M, int64_t n, int64_t k, void* c,
                               int32_t out_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -462,12 +507,24 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
   if (!a || !b || !m_splits || !c) return fail(GMLP_INVALID_ARG, "null pointer argument");
   if (G < 1 || M < 0 || n <= 0 || k <= 0 || n % 32 || k % 32) return fail(GMLP_UNSUPPORTED, "dims: n, k must be positive multiples of 32");
   if (layout == GMLP_GEMM_FPROP && k % 128) return fail(GMLP_UNSUPPORTED, "dims: the FPROP contraction k must be a multiple of 128");
+  {
+    const bool fp = layout == GMLP_GEMM_FPROP;
+    const GemmOperand oa = fp ? op_row(*a, a->amax_pre) : op_col(*a, a->amax_post);
+    const GemmOperand ob = fp ? op_row(*b, b->amax_pre) : op_col(*b, b->amax_post);
+    if (!oa.data || !ob.data || (is_mx(recipe) ? (!oa.scale_mfma || !ob.scale_mfma)
+                                               : (!oa.scale || !ob.scale || !oa.amax || !ob.amax)))
+      return fail(GMLP_INVALID_ARG, "operand data, scales%s missing", is_mx(recipe) ? "" : " or amax");
+  }
   Bump bb(ws);
   SplitTables T = carve_tables(bb, G);
+  const int64_t Pt = M + 127LL * G;
+  const NvScratch nv = layout == GMLP_GEMM_FPROP ? carve_nv(bb, recipe, M * k, (int64_t)G * n * k)
+                                                 : carve_nv(bb, recipe, n * Pt, k * Pt);
   if (!ws || ws_bytes < bb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", bb.off);
   Launcher L{stream};
   if (!L.check(launch_scan(m_splits, G, M, T, stream), "scan")) return L.st;
   GemmArgs g = gemm_base(layout == GMLP_GEMM_FPROP ? MODE_FPROP : MODE_WGRAD, recipe, EPI_STORE, T, G);
+  set_nv(g, nv);
   g.M = M;
   g.N = n;
   g.K = k;
@@ -480,6 +537,7 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
     g.a = op_col(*a, a->amax_post);
     g.b = op_col(*b, b->amax_post);
   }
+
   if (!L.check(launch_gemm(g, stream), "grouped gemm")) return L.st;
   g_counts[CNT_GEMM]++;
   return ok();
@@ -503,7 +561,7 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
   FwdCtx C = carve_ctx(cb, M, E, H, ffn, A->activation, r, rec);
   if (!A->ctx || A->ctx_bytes < cb.off) return fail(GMLP_WORKSPACE, "ctx too small: need %zu bytes", cb.off);
   Bump wb(A->ws);
-  FwdWs W = carve_fwd_ws(wb, M, E, H, ffn, r);
+  FwdWs W = carve_fwd_ws(wb, M, E, H, ffn, A->activation, r);
   if (!A->ws || A->ws_bytes < wb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", wb.off);
 
   Launcher L{stream};
@@ -546,6 +604,7 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     g.probs = A->probs;
     g.h = C.h;
     g.a_out = W.a;
+    set_nv(g, W.nv);
     if (!L.check(launch_gemm(g, stream), "fc1 gemm")) return L.st;
     g_counts[CNT_GEMM]++;
   }
@@ -583,6 +642,7 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     g.a = op_row(W.aq_row.q, a_pre);
     g.b = op_row(*A->w2, A->w2->amax_pre);
     g.c = A->y;
+    set_nv(g, W.nv);
     if (!L.check(launch_gemm(g, stream), "fc2 gemm")) return L.st;
     g_counts[CNT_GEMM]++;
   }
@@ -693,6 +753,8 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     g.a_out = (rec && wgrad) ? W.a2 : nullptr;
     g.dh = W.dh;
     g.dprob_part = W.dprob_part;
+    set_nv(g, W.nv);
+    g.da_tmp = W.da;
     if (!L.check(launch_gemm(g, stream), "fc2 dgrad gemm")) return L.st;
     g_counts[CNT_GEMM]++;
   }
@@ -727,6 +789,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     g.b = op_col(*aq, a_post);
     g.c = A->dw2;
     g.out_fp32 = A->wgrad_dtype == GMLP_OUT_FP32;
+    set_nv(g, W.nv);
     if (!L.check(launch_gemm(g, stream), "fc2 wgrad gemm")) return L.st;
     g_counts[CNT_GEMM]++;
   }
@@ -739,6 +802,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     g.a = op_row(W.dhq.q, W.dhq.q.amax_pre);
     g.b = op_col(*A->w1, A->w1->amax_pre);
     g.c = A->dx;
+    set_nv(g, W.nv);
     if (!L.check(launch_gemm(g, stream), "fc1 dgrad gemm")) return L.st;
     g_counts[CNT_GEMM]++;
   }
@@ -752,6 +816,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     g.b = op_col(C.xq_col.q, C.xq_col.q.amax_post);
     g.c = A->dw1;
     g.out_fp32 = A->wgrad_dtype == GMLP_OUT_FP32;
+    set_nv(g, W.nv);
     if (!L.check(launch_gemm(g, stream), "fc1 wgrad gemm")) return L.st;
     g_counts[CNT_GEMM]++;
   }

@@ -323,8 +323,11 @@ __device__ __forceinline__ DmaTile sel_tile(bool c, const DmaTile& a, const DmaT
   return r;
 }
 
-template <int MODE, int EPI>
+// BF: bf16 operands (2 bytes per element in the same 64-byte panels, no scale words: their
+// DMA keeps its slot with an empty resource, which reads nothing and lands zeros).
+template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ DmaConst dma_const(const GemmArgs& A, int wave) {
+  constexpr int64_t EB = BF ? 2 : 1;
   DmaConst k;
   const bool swiglu = MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0;
   k.a = A.a.data;
@@ -336,23 +339,24 @@ __device__ __forceinline__ DmaConst dma_const(const GemmArgs& A, int wave) {
     k.a_ps = (uint32_t)(A.M * 64);
     k.b_ps = (uint32_t)(brows * 64);
     k.s_ld = (uint32_t)((wave & 1) ? brows : A.M);
-    k.a_total = (uint32_t)(A.M * A.K);
-    k.b_total = (uint32_t)(A.G * brows * A.K);
-    k.s_total = (uint32_t)(4 * kw * ((wave & 1) ? A.G * brows : A.M));
+    k.a_total = (uint32_t)(EB * A.M * A.K);
+    k.b_total = (uint32_t)(EB * A.G * brows * A.K);
+    k.s_total = BF ? 0u : (uint32_t)(4 * kw * ((wave & 1) ? A.G * brows : A.M));
   } else {
     const int64_t P = A.T.col_off[A.G], W = A.T.colw_off[A.G];
     k.a_ps = (uint32_t)(A.N * 64);
     k.b_ps = (uint32_t)(A.K * 64);
     k.s_ld = (uint32_t)((wave & 1) ? A.K : A.N);
-    k.a_total = (uint32_t)(A.N * P);
-    k.b_total = (uint32_t)(A.K * P);
-    k.s_total = (uint32_t)(4 * W * ((wave & 1) ? A.K : A.N));
+    k.a_total = (uint32_t)(EB * A.N * P);
+    k.b_total = (uint32_t)(EB * A.K * P);
+    k.s_total = BF ? 0u : (uint32_t)(4 * W * ((wave & 1) ? A.K : A.N));
   }
   return k;
 }
 
-template <int MODE, int EPI>
+template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ DmaTile dma_tile(const GemmArgs& A, const TileRef& r, int wave) {
+  constexpr int64_t EB = BF ? 2 : 1;
   DmaTile t;
   const bool swiglu = MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0;
   const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
@@ -371,7 +375,7 @@ __device__ __forceinline__ DmaTile dma_tile(const GemmArgs& A, const TileRef& r,
     const int64_t brows = swiglu ? 2 * A.ffn : A.N;
     a_base = 0;
     a_sw = 0;
-    b_base = (int64_t)r.g * brows * A.K;
+    b_base = EB * (int64_t)r.g * brows * A.K;
     b_sw = (int64_t)r.g * ((A.K + 127) / 128) * brows;
   } else {
     a_base = A.N * (int64_t)r.off;
@@ -391,6 +395,7 @@ __device__ __forceinline__ DmaTile dma_tile(const GemmArgs& A, const TileRef& r,
     t.s_off = (uint32_t)(b_sw + (swiglu ? f0 : n0));
     t.s_bytes = (uint32_t)(swiglu ? 4 * (2 * A.ffn - f0) : 4 * max((int64_t)0, nb - n0));
   }
+  if (BF) t.s_bytes = 0;
   t.nk = r.nk;
   return t;
 }
@@ -570,7 +575,7 @@ __device__ __forceinline__ ReadPlan make_read_plan(int wm, int wn, int lane) {
   r.sb = (uint32_t)(MX_SC_OFF + 1024 + j + 4 * (wn * 128 + m));
   return r;
 }
-template <int T, int PAR>
+template <int T, int PAR, int BF = 0>
 __device__ __forceinline__ void mx_read_tp(const uint8_t* stage, const ReadPlan& r, MxFrags& f) {
   const uint4 x0 = *reinterpret_cast<const uint4*>(stage + r.a0 + 2048 * T);
   const uint4 x1 = *reinterpret_cast<const uint4*>(stage + r.a1 + 2048 * T);
@@ -578,15 +583,17 @@ __device__ __forceinline__ void mx_read_tp(const uint8_t* stage, const ReadPlan&
   const uint4 y1 = *reinterpret_cast<const uint4*>(stage + r.b1 + 2048 * T);
   f.a[T] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
   f.b[T] = v8i{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
-  f.sa[T] = stage[r.sa + 2 * PAR + 128 * T];
-  f.sb[T] = stage[r.sb + 2 * PAR + 128 * T];
+  if constexpr (!BF) {
+    f.sa[T] = stage[r.sa + 2 * PAR + 128 * T];
+    f.sb[T] = stage[r.sb + 2 * PAR + 128 * T];
+  }
 }
-template <int PAR>
+template <int PAR, int BF = 0>
 __device__ __forceinline__ void mx_read_p(const uint8_t* stage, const ReadPlan& r, MxFrags& f) {
-  mx_read_tp<0, PAR>(stage, r, f);
-  mx_read_tp<1, PAR>(stage, r, f);
-  mx_read_tp<2, PAR>(stage, r, f);
-  mx_read_tp<3, PAR>(stage, r, f);
+  mx_read_tp<0, PAR, BF>(stage, r, f);
+  mx_read_tp<1, PAR, BF>(stage, r, f);
+  mx_read_tp<2, PAR, BF>(stage, r, f);
+  mx_read_tp<3, PAR, BF>(stage, r, f);
 }
 
 __device__ __forceinline__ void mx_read(const uint8_t* stage, int wm, int wn, int lane, int kt, MxFrags& f) {
@@ -596,10 +603,21 @@ __device__ __forceinline__ void mx_read(const uint8_t* stage, int wm, int wn, in
   mx_read_t<3>(stage, wm, wn, lane, kt, f);
 }
 
-template <int TM, int TN>
+// bf16 operands (NVFP4 expanded exactly) travel in the same 64-byte stage rows: a lane's 32
+// fragment bytes are K elements [8 j, 8 j + 8) and [16 + 8 j, 24 + 8 j) of the stage's 32, which
+// are exactly its operands of two 32x32x16 bf16 MFMAs (elements 0..15, then 16..31).
+__device__ __forceinline__ v8bf frag_lo(const v8i& v) { return __builtin_bit_cast(v8bf, v4i{v[0], v[1], v[2], v[3]}); }
+__device__ __forceinline__ v8bf frag_hi(const v8i& v) { return __builtin_bit_cast(v8bf, v4i{v[4], v[5], v[6], v[7]}); }
+
+template <int TM, int TN, int BF = 0>
 __device__ __forceinline__ void mx_mma_one(const MxFrags& f, v16f (&acc)[4][4]) {
-  acc[TM][TN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[TM], f.b[TN], acc[TM][TN], 0, 0, 0, (int)f.sa[TM],
-                                                                 0, (int)f.sb[TN]);
+  if constexpr (BF) {
+    acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_lo(f.a[TM]), frag_lo(f.b[TN]), acc[TM][TN], 0, 0, 0);
+    acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_hi(f.a[TM]), frag_hi(f.b[TN]), acc[TM][TN], 0, 0, 0);
+  } else {
+    acc[TM][TN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[TM], f.b[TN], acc[TM][TN], 0, 0, 0,
+                                                                   (int)f.sa[TM], 0, (int)f.sb[TN]);
+  }
 }
 
 #define GMLP_SB() __builtin_amdgcn_sched_barrier(0)
@@ -613,35 +631,36 @@ __device__ __forceinline__ void mx_mma_one(const MxFrags& f, v16f (&acc)[4][4]) 
 //   after the barrier:  R0 M20 D5 R1 M21 M22 D6 R2 M23 M30 D7 R3 M31 M32 D8 M33
 constexpr int MX_DMA_BEFORE_BARRIER = 5;
 
+template <int BF = 0>
 __device__ __forceinline__ void mx_phase1(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
                                           int wave) {
   mx_dma_one<0>(s, d, wave); GMLP_SB();
-  mx_mma_one<0, 0>(f, acc); GMLP_SB(); mx_mma_one<0, 1>(f, acc); GMLP_SB();
+  mx_mma_one<0, 0, BF>(f, acc); GMLP_SB(); mx_mma_one<0, 1, BF>(f, acc); GMLP_SB();
   mx_dma_one<1>(s, d, wave); GMLP_SB();
-  mx_mma_one<0, 2>(f, acc); GMLP_SB(); mx_mma_one<0, 3>(f, acc); GMLP_SB();
+  mx_mma_one<0, 2, BF>(f, acc); GMLP_SB(); mx_mma_one<0, 3, BF>(f, acc); GMLP_SB();
   mx_dma_one<2>(s, d, wave); GMLP_SB();
-  mx_mma_one<1, 0>(f, acc); GMLP_SB(); mx_mma_one<1, 1>(f, acc); GMLP_SB();
+  mx_mma_one<1, 0, BF>(f, acc); GMLP_SB(); mx_mma_one<1, 1, BF>(f, acc); GMLP_SB();
   mx_dma_one<3>(s, d, wave); GMLP_SB();
-  mx_mma_one<1, 2>(f, acc); GMLP_SB(); mx_mma_one<1, 3>(f, acc); GMLP_SB();
+  mx_mma_one<1, 2, BF>(f, acc); GMLP_SB(); mx_mma_one<1, 3, BF>(f, acc); GMLP_SB();
   mx_dma_one<4>(s, d, wave); GMLP_SB();
 }
 
-template <int PAR>
+template <int PAR, int BF = 0>
 __device__ __forceinline__ void mx_phase2p(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
                                            int wave, const uint8_t* nstage, const ReadPlan& rp, MxFrags& nf) {
-  mx_read_tp<0, PAR>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<2, 0>(f, acc); GMLP_SB();
+  mx_read_tp<0, PAR, BF>(nstage, rp, nf); GMLP_SB();
+  mx_mma_one<2, 0, BF>(f, acc); GMLP_SB();
   mx_dma_one<5>(s, d, wave); GMLP_SB();
-  mx_read_tp<1, PAR>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<2, 1>(f, acc); GMLP_SB(); mx_mma_one<2, 2>(f, acc); GMLP_SB();
+  mx_read_tp<1, PAR, BF>(nstage, rp, nf); GMLP_SB();
+  mx_mma_one<2, 1, BF>(f, acc); GMLP_SB(); mx_mma_one<2, 2, BF>(f, acc); GMLP_SB();
   mx_dma_one<6>(s, d, wave); GMLP_SB();
-  mx_read_tp<2, PAR>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<2, 3>(f, acc); GMLP_SB(); mx_mma_one<3, 0>(f, acc); GMLP_SB();
+  mx_read_tp<2, PAR, BF>(nstage, rp, nf); GMLP_SB();
+  mx_mma_one<2, 3, BF>(f, acc); GMLP_SB(); mx_mma_one<3, 0, BF>(f, acc); GMLP_SB();
   mx_dma_one<7>(s, d, wave); GMLP_SB();
-  mx_read_tp<3, PAR>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<3, 1>(f, acc); GMLP_SB(); mx_mma_one<3, 2>(f, acc); GMLP_SB();
+  mx_read_tp<3, PAR, BF>(nstage, rp, nf); GMLP_SB();
+  mx_mma_one<3, 1, BF>(f, acc); GMLP_SB(); mx_mma_one<3, 2, BF>(f, acc); GMLP_SB();
   mx_dma_one<8>(s, d, wave); GMLP_SB();
-  mx_mma_one<3, 3>(f, acc); GMLP_SB();
+  mx_mma_one<3, 3, BF>(f, acc); GMLP_SB();
 }
 
 __device__ __forceinline__ void mx_phase2(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
@@ -1153,7 +1172,20 @@ __device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t vof
   __builtin_amdgcn_raw_buffer_store_b128((v4u){x, y, z, w}, r, voff, soff, kStoreNT);
 }
 
-template <int MODE, int EPI, int CH>
+// A staged fp32 quad, times the group's scale for NVFP4 (bf16-expanded) operands.
+template <int BF>
+__device__ __forceinline__ float4 ld_st4(const float* p, float alpha) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  if constexpr (BF != 0) {
+    v.x = __fmul_rn(v.x, alpha);
+    v.y = __fmul_rn(v.y, alpha);
+    v.z = __fmul_rn(v.z, alpha);
+    v.w = __fmul_rn(v.w, alpha);
+  }
+  return v;
+}
+
+template <int MODE, int EPI, int CH, int BF = 0>
 __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
                                           int tid, int wm, int wn, int lane, const float (&pr)[16]) {
   constexpr int TM = CH >> 1, Q = CH & 1;
@@ -1188,12 +1220,12 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const uint32_t ur = (uint32_t)(128 * ((RPI * it) >> 5) + 32 * TM + ((RPI * it) & 31));   // tile row - lrow
-      const float4 v0 = *reinterpret_cast<const float4*>(src + RPI * it * EPC_LD);
+      const float4 v0 = ld_st4<BF>(src + RPI * it * EPC_LD, c.alpha);
       if (EPI == EPI_STORE32) {
         out_store(r, voff, ur * rowb, __float_as_uint(v0.x), __float_as_uint(v0.y), __float_as_uint(v0.z),
                   __float_as_uint(v0.w));
       } else {
-        const float4 v1 = *reinterpret_cast<const float4*>(src + RPI * it * EPC_LD + 4);
+        const float4 v1 = ld_st4<BF>(src + RPI * it * EPC_LD + 4, c.alpha);
         out_store(r, voff, ur * rowb, pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
                   pack_bf16x2(v1.z, v1.w));
       }
@@ -1221,10 +1253,10 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
         const float p = pr[4 * TM + it];
         const float* src = st + (32 * it + lrow) * EPC_LD + sc;
         float gv[8], uv[8];
-        *reinterpret_cast<float4*>(gv) = *reinterpret_cast<const float4*>(src);
-        *reinterpret_cast<float4*>(gv + 4) = *reinterpret_cast<const float4*>(src + 4);
-        *reinterpret_cast<float4*>(uv) = *reinterpret_cast<const float4*>(src + 64);
-        *reinterpret_cast<float4*>(uv + 4) = *reinterpret_cast<const float4*>(src + 68);
+        *reinterpret_cast<float4*>(gv) = ld_st4<BF>(src, c.alpha);
+        *reinterpret_cast<float4*>(gv + 4) = ld_st4<BF>(src + 4, c.alpha);
+        *reinterpret_cast<float4*>(uv) = ld_st4<BF>(src + 64, c.alpha);
+        *reinterpret_cast<float4*>(uv + 4) = ld_st4<BF>(src + 68, c.alpha);
         uint32_t hg[4], hu[4], ow[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1252,8 +1284,8 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
         const float p = pr[4 * TM + it];
         const float* src = st + (16 * it + lrow) * EPC_LD + sc;
         float hv[8];
-        *reinterpret_cast<float4*>(hv) = *reinterpret_cast<const float4*>(src);
-        *reinterpret_cast<float4*>(hv + 4) = *reinterpret_cast<const float4*>(src + 4);
+        *reinterpret_cast<float4*>(hv) = ld_st4<BF>(src, c.alpha);
+        *reinterpret_cast<float4*>(hv + 4) = ld_st4<BF>(src + 4, c.alpha);
         uint32_t hw[4], ow[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1292,7 +1324,7 @@ __device__ __forceinline__ void epi_zero(const GemmArgs& A, const Ctx& c, int ti
   }
 }
 
-template <int MODE, int EPI>
+template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ void mx_epilogue(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
                                             int tid, int wm, int wn, int lane) {
   // fc1: the routing probabilities of the thread's output rows, all fetched up front (entry
@@ -1311,33 +1343,35 @@ __device__ __forceinline__ void mx_epilogue(const GemmArgs& A, const Ctx& c, con
         pr[4 * TM + it] = A.probs[c.arow0 + (trow < c.arows ? trow : c.arows - 1)];
       }
   }
-  epi_chunk<MODE, EPI, 0>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 1>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 2>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 3>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 4>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 5>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 6>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 7>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 0, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 1, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 2, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 3, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 4, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 5, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 6, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 7, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
 }
 
-template <int MODE, int EPI>
+template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ TileRef tile_ref(const GemmArgs& A, int t, int ntm, int ntn) {
   int mt;
   Ctx c;
   tile_ctx<FMT_MXFP8, MODE, EPI>(A, t, ntm, ntn, mt, c);
   TileRef r;
-  r.nk = uni(c.nk);
+  // bf16: 32 contraction elements per 64-byte stage; token offsets of the column-wise
+  // operands count 2 bytes per token
+  r.nk = uni(BF ? (int)((2 * c.kvalid + 63) / 64) : c.nk);
   r.arows = uni(c.arows);
   r.arow0 = uni(c.arow0);
   r.g = uni(c.g);
   r.nt = uni(c.nt);
-  r.off = (MODE == MODE_WGRAD) ? uni(A.T.col_off[c.g]) : 0;
+  r.off = (MODE == MODE_WGRAD) ? uni((BF ? 2 : 1) * A.T.col_off[c.g]) : 0;
   r.woff = (MODE == MODE_WGRAD) ? uni(A.T.colw_off[c.g]) : 0;
   return r;
 }
 
-template <int MODE, int EPI>
+template <int MODE, int EPI, int BF>
 __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
   __shared__ __align__(16) uint8_t smem[MX_NSTAGE * MX_STAGE];
   const int tid = threadIdx.x;
@@ -1365,18 +1399,18 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
   int dnext = t;
   auto next_ref = [&]() -> TileRef {
     while (dnext < hi) {
-      const TileRef r = tile_ref<MODE, EPI>(A, dnext, ntm, ntn);
+      const TileRef r = tile_ref<MODE, EPI, BF>(A, dnext, ntm, ntn);
       dnext += nwx;
       if (r.nk > 0) return r;
     }
     TileRef r{};
     return r;                          // nk = 0: no tile (its stages are issued empty)
   };
-  const DmaConst KC = dma_const<MODE, EPI>(A, wave);
+  const DmaConst KC = dma_const<MODE, EPI, BF>(A, wave);
   const ReadPlan rp = make_read_plan(wm, wn, lane);
-  DmaTile D0 = dma_tile<MODE, EPI>(A, next_ref(), wave);
-  DmaTile D1 = dma_tile<MODE, EPI>(A, next_ref(), wave);
-  DmaTile D2 = dma_tile<MODE, EPI>(A, next_ref(), wave);
+  DmaTile D0 = dma_tile<MODE, EPI, BF>(A, next_ref(), wave);
+  DmaTile D1 = dma_tile<MODE, EPI, BF>(A, next_ref(), wave);
+  DmaTile D2 = dma_tile<MODE, EPI, BF>(A, next_ref(), wave);
   // stage `off` positions past the first stage of D0 (selects only: the step has no branch)
   auto window_stage = [&](int off, uint8_t* dst) -> StageDma {
     const bool u1 = off >= D0.nk;
@@ -1396,13 +1430,20 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
 
   for (; t < hi; t += nwx) {
     // every non-empty tile is R0 of the DMA window when the compute reaches it
-    const TileRef cr = tile_ref<MODE, EPI>(A, t, ntm, ntn);
+    const TileRef cr = tile_ref<MODE, EPI, BF>(A, t, ntm, ntn);
     Ctx c;
     c.arows = cr.arows;
     c.arow0 = cr.arow0;
     c.g = cr.g;
     c.nt = cr.nt;
     c.nrow0 = (int64_t)cr.nt * BN;
+    c.alpha = 1.0f;
+    if (BF) {
+      // NVFP4 operands carry dec(E2M1) dec(E4M3); the group's global scales divide the product
+      const float sa = nvfp4_global_scale(A.a.amax[cr.g]);
+      const float sb = nvfp4_global_scale(A.b.amax[cr.g]);
+      c.alpha = __fmul_rn(__fdiv_rn(1.0f, sa), __fdiv_rn(1.0f, sb));
+    }
     const int nk = cr.nk;
     if (nk == 0) {                     // an empty group's weight gradient: zeros
       int tid_t = tid;
@@ -1422,7 +1463,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
       // stage gs (this tile's first) has landed once at most the two stages after it are pending
       wait_vmcnt<2 * MX_DMA_PER_STAGE>();
       __syncthreads();
-      mx_read_p<0>(slot(gs), rp, f0);
+      mx_read_p<0, BF>(slot(gs), rp, f0);
       // One step: the DMAs of sequence stage gs + 3 (whose slot held stage gs - 1, read by every
       // wave before the previous step's barrier), then the MFMAs of stage gs with the reads of
       // stage gs + 1 in between.  Stage gs + 1 may be the next tile's first (read again after
@@ -1441,10 +1482,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
           {
             const StageDma sd = run_stage(rr, soa, sob, sos, slot(gs + 3), s_voff, wave);
             GMLP_SB();
-            mx_phase1(f0, acc, sd, dpl, wave);
+            mx_phase1<BF>(f0, acc, sd, dpl, wave);
             wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
             __syncthreads();
-            mx_phase2p<1>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
+            mx_phase2p<1, BF>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
             ++gs;
           }
           soa += KC.a_ps;
@@ -1452,10 +1493,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
           {
             const StageDma sd = run_stage(rr, soa, sob, sos + s_step, slot(gs + 3), s_voff, wave);
             GMLP_SB();
-            mx_phase1(f1, acc, sd, dpl, wave);
+            mx_phase1<BF>(f1, acc, sd, dpl, wave);
             wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
             __syncthreads();
-            mx_phase2p<0>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
+            mx_phase2p<0, BF>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
             ++gs;
           }
           soa += KC.a_ps;
@@ -1468,26 +1509,26 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
         {
           const StageDma sd = window_stage(kt + 3, slot(gs + 3));
           GMLP_SB();
-          mx_phase1(f0, acc, sd, dpl, wave);
+          mx_phase1<BF>(f0, acc, sd, dpl, wave);
           wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
           __syncthreads();
-          mx_phase2p<1>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
+          mx_phase2p<1, BF>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
           ++gs;
         }
         {
           const StageDma sd = window_stage(kt + 4, slot(gs + 3));
           GMLP_SB();
-          mx_phase1(f1, acc, sd, dpl, wave);
+          mx_phase1<BF>(f1, acc, sd, dpl, wave);
           wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
           __syncthreads();
-          mx_phase2p<0>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
+          mx_phase2p<0, BF>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
           ++gs;
         }
         kt += 2;
       } while (kt < nk);
       D0 = D1;
       D1 = D2;
-      D2 = dma_tile<MODE, EPI>(A, next_ref(), wave);
+      D2 = dma_tile<MODE, EPI, BF>(A, next_ref(), wave);
     }
     // the slot of the last consumed stage holds nothing pending (the ones after it do).  The
     // thread index is laundered per tile so that the epilogue's per-thread addresses are
@@ -1495,7 +1536,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
     // across every main loop).
     int tid_t = tid;
     asm volatile("" : "+v"(tid_t));
-    mx_epilogue<MODE, EPI>(A, c, acc, slot(gs + 3), tid_t, wm, wn, tid_t & 63);
+    mx_epilogue<MODE, EPI, BF>(A, c, acc, slot(gs + 3), tid_t, wm, wn, tid_t & 63);
   }
   wait_vmcnt<0>();                     // the DMAs past the last tile (empty) before the LDS is released
 }
@@ -1537,7 +1578,7 @@ static int cu_count() {
   return n[dev];
 }
 
-template <int MODE, int EPI>
+template <int MODE, int EPI, int BF>
 static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
   int64_t tiles;
   if (MODE == MODE_FPROP) {
@@ -1550,8 +1591,9 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
   {
     const int64_t brows = (MODE == MODE_FPROP && EPI == EPI_FC1 && g.act == 0) ? 2 * g.ffn : g.N;
     const int64_t rows_bound = g.M + 127LL * g.G;                    // padded tokens of all groups
-    const int64_t big = (MODE == MODE_FPROP) ? std::max(g.M * g.K, (int64_t)g.G * brows * g.K)
-                                             : std::max(g.N, g.K) * rows_bound;
+    const int64_t eb = BF ? 2 : 1;
+    const int64_t big = eb * ((MODE == MODE_FPROP) ? std::max(g.M * g.K, (int64_t)g.G * brows * g.K)
+                                                   : std::max(g.N, g.K) * rows_bound);
     if (big >= (1LL << 32)) return hipErrorInvalidValue;
     // epilogue stores address one tile (256 rows) of an output through one buffer resource,
     // with kOutOfRange marking a lane's columns as outside it
@@ -1564,7 +1606,7 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
   // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split
   int64_t wgs = std::min<int64_t>(cu_count(), tiles);
   wgs = (wgs + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_mx_kernel<MODE, EPI>), dim3((unsigned)wgs), dim3(NTHREADS), 0, s, a);
+  hipLaunchKernelGGL((gemm_mx_kernel<MODE, EPI, BF>), dim3((unsigned)wgs), dim3(NTHREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1584,26 +1626,54 @@ static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// NVFP4: both operands expanded exactly to bf16 panels in the caller's scratch, then the
+// persistent kernel on the bf16 MFMA with the groups' global scales in the epilogue.  The
+// fc2-dgrad form (EPI_DACT) stores da and runs the activation gradient as its own pass.
+static hipError_t launch_nvfp4(const GemmArgs& g, int epi, hipStream_t s) {
+  if (!g.xa || !g.xb || (epi == EPI_DACT && !g.da_tmp)) return hipErrorInvalidValue;
+  hipError_t e;
+  if (g.mode == MODE_FPROP) {
+    if ((e = launch_nv_expand(g.a.data, g.a.scale, g.xa, g.M, g.K, 1, s)) != hipSuccess) return e;
+    if ((e = launch_nv_expand(g.b.data, g.b.scale, g.xb, g.N, g.K, g.G, s)) != hipSuccess) return e;
+  } else {
+    const int64_t bound = g.M + 127LL * g.G;               // padded tokens of all groups
+    if ((e = launch_nv_expand_groups(g.a.data, g.a.scale, g.xa, g.N, bound, g.T.col_off, g.G, s)) != hipSuccess)
+      return e;
+    if ((e = launch_nv_expand_groups(g.b.data, g.b.scale, g.xb, g.K, bound, g.T.col_off, g.G, s)) != hipSuccess)
+      return e;
+  }
+  GemmArgs a = g;
+  a.fmt = FMT_NVFP4_BF16;
+  a.a.data = g.xa;
+  a.b.data = g.xb;
+  // no scale words: their DMA slot runs with empty resources; give them a real base anyway
+  a.a.scale_mfma = reinterpret_cast<const uint32_t*>(g.xa);
+  a.b.scale_mfma = reinterpret_cast<const uint32_t*>(g.xb);
+  if (g.mode == MODE_WGRAD) return epi == EPI_STORE32 ? launch_mx<MODE_WGRAD, EPI_STORE32, 1>(a, s)
+                                                      : launch_mx<MODE_WGRAD, EPI_STORE, 1>(a, s);
+  if (epi == EPI_FC1) return launch_mx<MODE_FPROP, EPI_FC1, 1>(a, s);
+  if (epi == EPI_STORE32) return launch_mx<MODE_FPROP, EPI_STORE32, 1>(a, s);
+  if (epi == EPI_STORE) return launch_mx<MODE_FPROP, EPI_STORE, 1>(a, s);
+  if (epi != EPI_DACT) return hipErrorInvalidValue;
+  a.epi = EPI_STORE;
+  a.c = g.da_tmp;
+  a.out_fp32 = 0;
+  if ((e = launch_mx<MODE_FPROP, EPI_STORE, 1>(a, s)) != hipSuccess) return e;
+  return launch_dact_bf16(g.da_tmp, g.h, g.probs, g.act, g.ffn, g.M, g.dh, g.a_out, g.dprob_part, s);
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.mode == MODE_FPROP && g.M == 0) return hipSuccess;
-#define GMLP_DISPATCH(F, MO, E) \
-  if (g.fmt == F && g.mode == MO && epi == E) return launch_one<F, MO, E>(g, s);
   const int epi = (g.epi == EPI_STORE && g.out_fp32) ? (int)EPI_STORE32 : g.epi;
+  if (g.fmt == FMT_NVFP4) return launch_nvfp4(g, epi, s);
 #define GMLP_DISPATCH_MX(MO, E) \
-  if (g.fmt == FMT_MXFP8 && g.mode == MO && epi == E) return launch_mx<MO, E>(g, s);
+  if (g.fmt == FMT_MXFP8 && g.mode == MO && epi == E) return launch_mx<MO, E, 0>(g, s);
   GMLP_DISPATCH_MX(MODE_FPROP, EPI_STORE)
   GMLP_DISPATCH_MX(MODE_FPROP, EPI_STORE32)
   GMLP_DISPATCH_MX(MODE_WGRAD, EPI_STORE32)
   GMLP_DISPATCH_MX(MODE_FPROP, EPI_FC1)
   GMLP_DISPATCH_MX(MODE_WGRAD, EPI_STORE)
 #undef GMLP_DISPATCH_MX
-  GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_STORE32)
-  GMLP_DISPATCH(FMT_NVFP4, MODE_WGRAD, EPI_STORE32)
-  GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_STORE)
-  GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_FC1)
-  GMLP_DISPATCH(FMT_NVFP4, MODE_FPROP, EPI_DACT)
-  GMLP_DISPATCH(FMT_NVFP4, MODE_WGRAD, EPI_STORE)
-#undef GMLP_DISPATCH
   return hipErrorInvalidValue;
 }
 

@@ -61,8 +61,22 @@ hipError_t launch_weight_amax(const uint16_t* w, const void* const* w_ptrs, int 
 hipError_t launch_gather_weights(const void* const* w_ptrs, int E, int64_t N, int64_t K,
                                  uint16_t* out, hipStream_t s);
 
+// NVFP4 operands expanded exactly to bf16 in 64-byte K panels (element (r, c) of an R x C matrix
+// at byte ((c / 32) R + r) 64 + 2 (c % 32)): nmat stacked [R, C] matrices, or the column-wise
+// groups [R, P_g] at element offsets R col_off[g] (cols_bound >= col_off[G]).
+hipError_t launch_nv_expand(const uint8_t* data, const uint8_t* scale, uint8_t* out, int64_t R, int64_t C,
+                            int nmat, hipStream_t s);
+hipError_t launch_nv_expand_groups(const uint8_t* data, const uint8_t* scale, uint8_t* out, int64_t R,
+                                   int64_t cols_bound, const int32_t* col_off, int G, hipStream_t s);
+// NVFP4 backward: bf16 dh (and the rebuilt fc2 input a2 when non-null) from bf16 da and h, with
+// the dL/dp partials of each 256-feature tile in dprob_part [ceil(ffn / 256)][M].
+hipError_t launch_dact_bf16(const uint16_t* da, const uint16_t* h, const float* probs, int act, int64_t ffn,
+                            int64_t M, uint16_t* dh, uint16_t* a2, float* dprob_part, hipStream_t s);
+
 // ----------------------------------------------------------------------------- GEMM
-enum GemmFmt { FMT_MXFP8 = 0, FMT_NVFP4 = 1 };
+// FMT_NVFP4_BF16: NVFP4 operands expanded exactly to bf16 (dec(E2M1) dec(E4M3), no global scale) in
+// the 64-byte panel layout of the MXFP8 operands, with the per-group amax for the global scales.
+enum GemmFmt { FMT_MXFP8 = 0, FMT_NVFP4 = 1, FMT_NVFP4_BF16 = 2 };
 enum GemmMode { MODE_FPROP = 0, MODE_WGRAD = 1 };
 enum GemmEpi { EPI_STORE = 0, EPI_FC1 = 1, EPI_DACT = 2, EPI_STORE32 = 3 };   // STORE32: fp32 output
 
@@ -93,6 +107,11 @@ struct GemmArgs {
   uint16_t* dh;      // EPI_DACT: out dh [M, F1]
   float* dprob_part; // EPI_DACT: [n_tiles, M]
   int group_rows;    // tile rows per launch-order group (see make_ctx); set by launch_gemm
+  // NVFP4: scratch for the operands expanded to bf16 (A: 2 x rows x contraction bytes, B: the
+  // same for the weight or column-wise operand) and, for EPI_DACT, da [M, ffn] bf16
+  uint8_t* xa;
+  uint8_t* xb;
+  uint16_t* da_tmp;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);

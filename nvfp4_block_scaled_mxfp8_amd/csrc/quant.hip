@@ -716,4 +716,129 @@ hipError_t launch_gather_weights(const void* const* w_ptrs, int E, int64_t N, in
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------- NVFP4 -> bf16 panels
+// The NVFP4 GEMMs run on the bf16 MFMA: each operand element becomes dec(E2M1) * dec(E4M3), which
+// has at most 6 significant bits and a magnitude in [2^-10, 2688], so bf16 holds it exactly (the
+// per-group global scales are applied to the fp32 result).  The expanded operand uses the MXFP8
+// operands' 64-byte K panels with 2-byte elements: element (r, c) of an R x C matrix at byte
+// ((c / 32) R + r) 64 + 2 (c % 32).
+// A block covers 16 rows x 128 columns; thread -> row 16 by + tid / 16, 32-column chunk
+// (tid / 4) % 4, 8 columns 8 (tid % 4) of it: it reads one packed word and writes 16 bytes, and
+// the four lanes of a chunk-row write one whole 64-byte panel row.
+// Dense batch (col_off == null): matrix blockIdx.z of nmat equal [R, C] matrices, stored one
+// after the other.  Grouped (column-wise activations): the groups' [R, P_g] matrices at element
+// offsets R * col_off[g]; blockIdx.x walks 128-column units of their concatenation (P_g is a
+// multiple of 128, so a unit never straddles two groups).
+__global__ __launch_bounds__(256) void nv_expand_kernel(const uint8_t* __restrict__ data,
+                                                        const uint8_t* __restrict__ scale, uint8_t* __restrict__ out,
+                                                        int64_t R, int64_t C, const int32_t* __restrict__ col_off,
+                                                        int G) {
+  const int tid = threadIdx.x;
+  const int64_t r = (int64_t)blockIdx.y * 16 + (tid >> 4);
+  if (r >= R) return;
+  int64_t base, c0, cols;
+  if (col_off) {
+    const int u = (int)blockIdx.x * 128;
+    if (u >= col_off[G]) return;
+    const int g = find_group(col_off, G, u);
+    base = R * (int64_t)col_off[g];
+    cols = col_off[g + 1] - col_off[g];
+    c0 = u - col_off[g];
+  } else {
+    base = (int64_t)blockIdx.z * R * C;
+    cols = C;
+    c0 = (int64_t)blockIdx.x * 128;
+  }
+  const int j = (tid >> 2) & 3, q = tid & 3;
+  const int64_t c = c0 + 32 * j + 8 * q;
+  if (c >= cols) return;
+  const int64_t e = base + r * cols + c;                   // element index (a multiple of 8)
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(data + e / 2);
+  const float sc = e4m3_decode_pos(scale[e / 16]);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = e2m1_decode((w >> (8 * i)) & 0xFu) * sc;
+    const float hi = e2m1_decode((w >> (8 * i + 4)) & 0xFu) * sc;
+    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);   // exact: truncation drops zeros
+  }
+  uint8_t* dst = out + 2 * base + (((c / 32) * R + r) * 64 + 2 * (c % 32));
+  __builtin_nontemporal_store(v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]}, reinterpret_cast<v4i*>(dst));
+}
+
+hipError_t launch_nv_expand(const uint8_t* data, const uint8_t* scale, uint8_t* out, int64_t R, int64_t C, int nmat,
+                            hipStream_t s) {
+  if (R == 0 || C == 0 || nmat == 0) return hipSuccess;
+  hipLaunchKernelGGL(nv_expand_kernel, dim3((unsigned)((C + 127) / 128), (unsigned)((R + 15) / 16), (unsigned)nmat),
+                     dim3(256), 0, s, data, scale, out, R, C, (const int32_t*)nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_nv_expand_groups(const uint8_t* data, const uint8_t* scale, uint8_t* out, int64_t R,
+                                   int64_t cols_bound, const int32_t* col_off, int G, hipStream_t s) {
+  if (R == 0 || cols_bound == 0 || G == 0) return hipSuccess;
+  hipLaunchKernelGGL(nv_expand_kernel, dim3((unsigned)((cols_bound + 127) / 128), (unsigned)((R + 15) / 16), 1u),
+                     dim3(256), 0, s, data, scale, out, R, (int64_t)0, col_off, G);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- activation gradient (bf16)
+// NVFP4 backward between the fc2 dgrad (bf16 da [M, ffn]) and the dh casts: dh = bf16(d(act(h) p)/dh
+// . da) written as bf16 [M, F1] (SwiGLU: the gate gradient at feature f, the up gradient at
+// ffn + f), the rebuilt fc2 input a' = bf16(act(h) p) when a2 is set, and per-row dL/dp partials of
+// each 256-feature tile (summed over its features in a fixed lane order) in dprob_part[tile][row].
+// Block = 8 rows x 256 features; thread -> row 8 by + tid / 32, features 8 (tid % 32) .. + 7.
+__global__ __launch_bounds__(256) void dact_bf16_kernel(const uint16_t* __restrict__ da, const uint16_t* __restrict__ h,
+                                                        const float* __restrict__ probs, int act, int64_t ffn,
+                                                        int64_t M, uint16_t* __restrict__ dh, uint16_t* __restrict__ a2,
+                                                        float* __restrict__ dprob_part) {
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.y * 8 + (tid >> 5);
+  if (row >= M) return;                                    // whole 32-lane row groups leave together
+  const int64_t F1 = act == 0 ? 2 * ffn : ffn;
+  const int64_t f = (int64_t)blockIdx.x * 256 + 8 * (tid & 31);
+  float psum = 0.0f;
+  if (f < ffn) {
+    const float p = probs[row];
+    const uint4 dv = *reinterpret_cast<const uint4*>(da + row * ffn + f);
+    const uint4 gv = *reinterpret_cast<const uint4*>(h + row * F1 + f);
+    const uint4 uv = act == 0 ? *reinterpret_cast<const uint4*>(h + row * F1 + ffn + f) : make_uint4(0, 0, 0, 0);
+    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    uint32_t o0[4], o1[4], oa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t r0 = 0, r1 = 0, ra = 0;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float dav = bf16_to_f32((dw[i] >> (16 * hh)) & 0xFFFFu);
+        const float g = bf16_to_f32((gw[i] >> (16 * hh)) & 0xFFFFu);
+        const float u = bf16_to_f32((uw[i] >> (16 * hh)) & 0xFFFFu);
+        float d0, d1, dp, av;
+        act_grad_out(act, g, u, dav, p, d0, d1, dp, av);
+        psum += dp;
+        r0 |= f32_to_bf16_bits(d0) << (16 * hh);
+        r1 |= f32_to_bf16_bits(d1) << (16 * hh);
+        ra |= (__float_as_uint(av) >> 16) << (16 * hh);
+      }
+      o0[i] = r0;
+      o1[i] = r1;
+      oa[i] = ra;
+    }
+    *reinterpret_cast<uint4*>(dh + row * F1 + f) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+    if (act == 0) *reinterpret_cast<uint4*>(dh + row * F1 + ffn + f) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    if (a2) *reinterpret_cast<uint4*>(a2 + row * ffn + f) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+  }
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) psum += __shfl_xor(psum, o, 64);
+  if ((tid & 31) == 0) dprob_part[(int64_t)blockIdx.x * M + row] = psum;
+}
+
+hipError_t launch_dact_bf16(const uint16_t* da, const uint16_t* h, const float* probs, int act, int64_t ffn, int64_t M,
+                            uint16_t* dh, uint16_t* a2, float* dprob_part, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(dact_bf16_kernel, dim3((unsigned)((ffn + 255) / 256), (unsigned)((M + 7) / 8)), dim3(256), 0, s,
+                     da, h, probs, act, ffn, M, dh, a2, dprob_part);
+  return hipGetLastError();
+}
+
 }  // namespace gmlp
