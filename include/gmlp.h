@@ -89,7 +89,17 @@ typedef struct {
  *   col_data       MXFP8 u8 [K * sum P_g] (panels); NVFP4 u8 [K * sum P_g / 2]
  *   col_scale      MXFP8 u8 [K * sum P_g / 32];  NVFP4 u8 [K * sum P_g / 16]
  *   col_scale_mfma MXFP8 u32 [K * sum P_g/128]
- *   amax_pre, amax_post  NVFP4 fp32 [G] (per-group pre-/post-RHT amax) */
+ *   amax_pre, amax_post  NVFP4 fp32 [G] (per-group pre-/post-RHT amax)
+ *   row_bf16, col_bf16   NVFP4 only, optional: the same casts as the values
+ *                  dec(E2M1) * dec(E4M3) (exact in bf16; the global scale is not
+ *                  applied), laid out like MXFP8 data with 2-byte elements: element
+ *                  (r, c) of an R x C matrix at byte ((c / 32) R + r) 64 + 2 (c % 32);
+ *                  row-wise one [M, K] matrix (2 M K bytes), column-wise group g's
+ *                  [K, P_g] at byte 2 K sum_{h<g} P_h.  The NVFP4 GEMMs run on the bf16
+ *                  matrix cores: an operand given in this form is read directly,
+ *                  otherwise the GEMM expands the packed form into its workspace.
+ *                  Written by the quantize calls when non-NULL; either form (or
+ *                  both) may be requested. */
 typedef struct {
   void* row_data;
   void* row_scale;
@@ -99,6 +109,8 @@ typedef struct {
   void* col_scale_mfma;
   float* amax_pre;
   float* amax_post;
+  void* row_bf16;
+  void* col_bf16;
 } gmlp_grouped_q;
 
 /* Quantized stacked weights for one GroupedLinear, W [E, N, K] (Linear layout
@@ -106,7 +118,9 @@ typedef struct {
  *   fprop operand: blocks along K  -> row_data [E][N, K(/2)], row scales
  *   dgrad operand: blocks along N  -> col_data [E][K, N(/2)], col scales (W^T per expert)
  *   MXFP8 data of each expert is one matrix in 64-byte K panels, as above. 
- *   NVFP4: amax [E] (one global scale per expert for both casts; weights get no RHT). */
+ *   NVFP4: amax [E] (one global scale per expert for both casts; weights get no RHT);
+ *   row_bf16 [E][N, K] and col_bf16 [E][K, N] panels (2 N K bytes per expert each),
+ *   optional, written once here so that the GEMMs of every step read them directly. */
 typedef gmlp_grouped_q gmlp_weight_q;
 
 /* ------------------------------------------------------------------ queries */

@@ -40,7 +40,7 @@ class Recipe(ctypes.Structure):
 
 
 _Q_FIELDS = ("row_data", "row_scale", "row_scale_mfma", "col_data", "col_scale", "col_scale_mfma",
-             "amax_pre", "amax_post")
+             "amax_pre", "amax_post", "row_bf16", "col_bf16")
 
 
 class GroupedQ(ctypes.Structure):
@@ -272,7 +272,7 @@ def group_quantize_with_amax(x, m_splits, rec, amax_pre, amax_post, want_row=Tru
     return out
 
 
-def alloc_weight_q(rec, E, N, K, device="cuda"):
+def alloc_weight_q(rec, E, N, K, device="cuda", bf16_panels=True):
     u8 = dict(dtype=torch.uint8, device=device)
     b = {}
     if rec.kind == MXFP8:
@@ -288,6 +288,9 @@ def alloc_weight_q(rec, E, N, K, device="cuda"):
         b["col_data"] = torch.empty(E * K * N // 2, **u8)
         b["col_scale"] = torch.empty(E * K * N // 16, **u8)
         b["amax_pre"] = torch.empty(E, dtype=torch.float32, device=device)
+        if bf16_panels:               # the operands the GEMMs read, expanded once here
+            b["row_bf16"] = torch.empty(2 * E * N * K, **u8)
+            b["col_bf16"] = torch.empty(2 * E * K * N, **u8)
     return QTensor(rec.kind, b)
 
 

@@ -97,19 +97,24 @@ QBuf carve_q(Bump& b, const gmlp_recipe& r, int64_t M, int64_t K, int G, bool ro
       o.q.col_scale_mfma = b.take<uint32_t>(K * pad_words_bound(M, G));
     }
   } else {
-    if (row) {
-      o.q.row_data = b.take<uint8_t>(M * K / 2);
-      o.q.row_scale = b.take<uint8_t>(M * K / 16);
-    }
-    if (col) {
-      o.q.col_data = b.take<uint8_t>(K * PR / 2);
-      o.q.col_scale = b.take<uint8_t>(K * PR / 16);
-    }
+    // NVFP4 inside the fused MLP: only the GEMMs read these casts, so they are kept as the
+    // bf16 panels the GEMMs take (the packed E2M1 / E4M3 form is not written)
+    if (row) o.q.row_bf16 = b.take<uint8_t>(2 * M * K);
+    if (col) o.q.col_bf16 = b.take<uint8_t>(2 * K * PR);
     if (amax) {
       o.q.amax_pre = b.take<float>(G);
       o.q.amax_post = b.take<float>(G);
     }
   }
+  return o;
+}
+
+// NVFP4 cast outputs of q (direction not wanted: null).
+NvOut nv_out(const gmlp_grouped_q& q, bool row, bool col) {
+  NvOut o{row ? static_cast<uint8_t*>(q.row_data) : nullptr, row ? static_cast<uint8_t*>(q.row_scale) : nullptr,
+          col ? static_cast<uint8_t*>(q.col_data) : nullptr, col ? static_cast<uint8_t*>(q.col_scale) : nullptr};
+  o.row_bf16 = row ? static_cast<uint8_t*>(q.row_bf16) : nullptr;
+  o.col_bf16 = col ? static_cast<uint8_t*>(q.col_bf16) : nullptr;
   return o;
 }
 
@@ -159,9 +164,11 @@ gmlp_status quant_core(const void* x, int64_t M, int64_t K, const int32_t* m_spl
     if (col && (!out->col_data || (!out->col_scale && !out->col_scale_mfma)))
       return fail(GMLP_INVALID_ARG, "column-wise output buffers missing");
   } else {
-    if (rows_exist && row && (!out->row_data || !out->row_scale))
+    // packed data needs its scales; the bf16 panels may stand alone
+    if (rows_exist && row && ((!out->row_data && !out->row_bf16) || (out->row_data && !out->row_scale)))
       return fail(GMLP_INVALID_ARG, "row-wise output buffers missing");
-    if (col && (!out->col_data || !out->col_scale)) return fail(GMLP_INVALID_ARG, "column-wise output buffers missing");
+    if (col && ((!out->col_data && !out->col_bf16) || (out->col_data && !out->col_scale)))
+      return fail(GMLP_INVALID_ARG, "column-wise output buffers missing");
     if (!out->amax_pre || !out->amax_post) return fail(GMLP_INVALID_ARG, "NVFP4 needs amax_pre and amax_post");
   }
   Bump b(ws);
@@ -189,8 +196,7 @@ gmlp_status quant_core(const void* x, int64_t M, int64_t K, const int32_t* m_spl
     g_counts[CNT_HAMAX]++;
   }
   if (row || col) {
-    NvOut o{static_cast<uint8_t*>(out->row_data), static_cast<uint8_t*>(out->row_scale),
-            static_cast<uint8_t*>(out->col_data), static_cast<uint8_t*>(out->col_scale)};
+    const NvOut o = nv_out(*out, row, col);
     if (!L.check(launch_nvfp4_quant(xx, M, K, T, G, r.rht_sign_mask & 0xFFFFu, true, row, col, out->amax_pre,
                                     out->amax_post, o, stream), "nvfp4 quantize"))
       return L.st;
@@ -206,6 +212,7 @@ GemmOperand op_row(const gmlp_grouped_q& q, const float* amax) {
   o.scale_mfma = static_cast<const uint32_t*>(q.row_scale_mfma);
   o.scale = static_cast<const uint8_t*>(q.row_scale);
   o.amax = amax;
+  o.bf16 = static_cast<const uint8_t*>(q.row_bf16);
   return o;
 }
 GemmOperand op_col(const gmlp_grouped_q& q, const float* amax) {
@@ -214,6 +221,7 @@ GemmOperand op_col(const gmlp_grouped_q& q, const float* amax) {
   o.scale_mfma = static_cast<const uint32_t*>(q.col_scale_mfma);
   o.scale = static_cast<const uint8_t*>(q.col_scale);
   o.amax = amax;
+  o.bf16 = static_cast<const uint8_t*>(q.col_bf16);
   return o;
 }
 
@@ -230,10 +238,10 @@ GemmArgs gemm_base(int mode, const gmlp_recipe& r, int epi, SplitTables T, int G
 
 gmlp_status weight_ok(const gmlp_weight_q* w, const gmlp_recipe& r, bool fprop, bool dgrad) {
   if (!w) return fail(GMLP_INVALID_ARG, "null weight descriptor");
-  if (fprop && (!w->row_data || (is_mx(r) ? !w->row_scale_mfma : !w->row_scale)))
-    return fail(GMLP_INVALID_ARG, "weight fprop operand (row-wise data and scales) missing");
-  if (dgrad && (!w->col_data || (is_mx(r) ? !w->col_scale_mfma : !w->col_scale)))
-    return fail(GMLP_INVALID_ARG, "weight dgrad operand (column-wise data and scales) missing");
+  const bool f_ok = is_mx(r) ? (w->row_data && w->row_scale_mfma) : (w->row_bf16 || (w->row_data && w->row_scale));
+  const bool d_ok = is_mx(r) ? (w->col_data && w->col_scale_mfma) : (w->col_bf16 || (w->col_data && w->col_scale));
+  if (fprop && !f_ok) return fail(GMLP_INVALID_ARG, "weight fprop operand (row-wise data and scales) missing");
+  if (dgrad && !d_ok) return fail(GMLP_INVALID_ARG, "weight dgrad operand (column-wise data and scales) missing");
   if (!is_mx(r) && !w->amax_pre) return fail(GMLP_INVALID_ARG, "NVFP4 weights need their per-expert amax (amax_pre)");
   return GMLP_OK;
 }
@@ -445,6 +453,8 @@ gmlp_status gmlp_weight_quantize(const void* w, const void* const* w_ptrs, int32
   if (!out->row_data || !out->col_data) return fail(GMLP_INVALID_ARG, "weight output data buffers missing");
   if (is_mx(recipe) ? (!out->row_scale_mfma || !out->col_scale_mfma) : (!out->row_scale || !out->col_scale || !out->amax_pre))
     return fail(GMLP_INVALID_ARG, "weight output scale buffers missing");
+  if (is_mx(recipe) && (out->row_bf16 || out->col_bf16))
+    return fail(GMLP_INVALID_ARG, "bf16 operand panels apply to the NVFP4 recipe only");
   Bump b(ws);
   SplitTables T = carve_tables(b, 1);
   int32_t* split = b.take<int32_t>(1);
@@ -472,6 +482,9 @@ gmlp_status gmlp_weight_quantize(const void* w, const void* const* w_ptrs, int32
               static_cast<uint8_t*>(out->row_scale) + (int64_t)e * N * K / 16,
               static_cast<uint8_t*>(out->col_data) + (int64_t)e * N * K / 2,
               static_cast<uint8_t*>(out->col_scale) + (int64_t)e * N * K / 16};
+      // expert e's panels: fprop [N rows, K], dgrad [K rows, N] (the one group's column-wise cast)
+      o.row_bf16 = out->row_bf16 ? static_cast<uint8_t*>(out->row_bf16) + 2 * (int64_t)e * N * K : nullptr;
+      o.col_bf16 = out->col_bf16 ? static_cast<uint8_t*>(out->col_bf16) + 2 * (int64_t)e * N * K : nullptr;
       if (!L.check(launch_nvfp4_quant(src, N, K, T, 1, 0u, false, true, true, amax, amax, o, stream),
                    "nvfp4 weight quantize"))
         return L.st;
@@ -511,8 +524,9 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
     const bool fp = layout == GMLP_GEMM_FPROP;
     const GemmOperand oa = fp ? op_row(*a, a->amax_pre) : op_col(*a, a->amax_post);
     const GemmOperand ob = fp ? op_row(*b, b->amax_pre) : op_col(*b, b->amax_post);
-    if (!oa.data || !ob.data || (is_mx(recipe) ? (!oa.scale_mfma || !ob.scale_mfma)
-                                               : (!oa.scale || !ob.scale || !oa.amax || !ob.amax)))
+    const bool nv_a = oa.bf16 || (oa.data && oa.scale), nv_b = ob.bf16 || (ob.data && ob.scale);
+    if (is_mx(recipe) ? (!oa.data || !ob.data || !oa.scale_mfma || !ob.scale_mfma)
+                      : (!nv_a || !nv_b || !oa.amax || !ob.amax))
       return fail(GMLP_INVALID_ARG, "operand data, scales%s missing", is_mx(recipe) ? "" : " or amax");
   }
   Bump bb(ws);
@@ -583,8 +597,8 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(post), 0u, E, stream), "fill")) return L.st;
     if (!L.check(launch_hadamard_amax(x, M, H, W.T, E, r.rht_sign_mask & 0xFFFF, pre, post, stream), "amax x")) return L.st;
     g_counts[CNT_HAMAX]++;
-    NvOut o{static_cast<uint8_t*>(W.xq_row.q.row_data), static_cast<uint8_t*>(W.xq_row.q.row_scale),
-            static_cast<uint8_t*>(C.xq_col.q.col_data), static_cast<uint8_t*>(C.xq_col.q.col_scale)};
+    NvOut o = nv_out(W.xq_row.q, true, false);
+    o.col_bf16 = wgrad ? static_cast<uint8_t*>(C.xq_col.q.col_bf16) : nullptr;
     if (!L.check(launch_nvfp4_quant(x, M, H, W.T, E, r.rht_sign_mask & 0xFFFF, true, true, wgrad, pre, post, o, stream),
                  "nvfp4 quantize x"))
       return L.st;
@@ -624,9 +638,8 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
                  "amax fc2 input"))
       return L.st;
     g_counts[CNT_HAMAX]++;
-    NvOut o{static_cast<uint8_t*>(W.aq_row.q.row_data), static_cast<uint8_t*>(W.aq_row.q.row_scale),
-            a_col ? static_cast<uint8_t*>(C.aq_col.q.col_data) : nullptr,
-            a_col ? static_cast<uint8_t*>(C.aq_col.q.col_scale) : nullptr};
+    NvOut o = nv_out(W.aq_row.q, true, false);
+    o.col_bf16 = a_col ? static_cast<uint8_t*>(C.aq_col.q.col_bf16) : nullptr;
     if (!L.check(launch_nvfp4_quant(W.a, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, true, true, a_col, C.a_pre,
                                     C.a_post, o, stream), "nvfp4 quantize fc2 input"))
       return L.st;
@@ -692,8 +705,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(q.q.amax_post), 0u, E, stream), "fill")) return false;
     if (!L.check(launch_hadamard_amax(t, M, K, W.T, E, mask, q.q.amax_pre, q.q.amax_post, stream), "amax")) return false;
     g_counts[CNT_HAMAX]++;
-    NvOut o{static_cast<uint8_t*>(q.q.row_data), static_cast<uint8_t*>(q.q.row_scale),
-            static_cast<uint8_t*>(q.q.col_data), static_cast<uint8_t*>(q.q.col_scale)};
+    const NvOut o = nv_out(q.q, row, col);
     if (!L.check(launch_nvfp4_quant(t, M, K, W.T, E, mask, true, row, col, q.q.amax_pre, q.q.amax_post, o, stream),
                  "nvfp4 quantize"))
       return false;
@@ -773,7 +785,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
       if (mx) {
         // cast by the activation-gradient pass above
       } else {
-        NvOut o{nullptr, nullptr, static_cast<uint8_t*>(W.a2q.q.col_data), static_cast<uint8_t*>(W.a2q.q.col_scale)};
+        const NvOut o = nv_out(W.a2q.q, false, true);
         if (!L.check(launch_nvfp4_quant(W.a2, M, ffn, W.T, E, mask, true, false, true, C.a_pre, C.a_post, o, stream),
                      "nvfp4 quantize rebuilt fc2 input"))
           return L.st;

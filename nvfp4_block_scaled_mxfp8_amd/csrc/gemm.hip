@@ -12,10 +12,10 @@
 //   FPROP  A = row-wise [rows of group g, K], B = expert g's [N, K]      (fc1, fc2, both dgrads)
 //   WGRAD  A = column-wise [N_a, P_g], B = column-wise [N_b, P_g]        (both wgrads, K = tokens)
 //
-// Workgroup tile 256 x 256, 4 waves of 128 x 128 (4 x 4 tiles of 32 x 32), K staged
-// through LDS in 128-byte rows (128 fp8, or 64 bf16 after NVFP4 dequantization),
-// double buffered, 16-byte chunks XOR-swizzled by row so that both the 16-byte
-// stores and the MFMA fragment reads are bank-conflict-free.
+// One persistent kernel: workgroup tile 256 x 256, 4 waves of 128 x 128 (4 x 4 tiles of
+// 32 x 32), K staged through a 4-slot LDS ring of 64-byte rows (64 fp8, or 32 bf16 for
+// NVFP4) filled by buffer-to-LDS DMA, 16-byte chunks XOR-swizzled by row so that the MFMA
+// fragment reads are bank-conflict-free.
 //
 // MXFP8: V_MFMA_SCALE_F32_32X32X64_F8F6F4 with E8M0 block scales.  Lane (m + 32j)
 // holds row m, K bytes [16j, 16j+16) and [32+16j, 48+16j) of the 64-K step, and
@@ -23,10 +23,10 @@
 // holds the 4 blocks of a 128-K stage, so lane group j shifts it by 8j bytes and
 // selects byte 2s for K-step s.
 // NVFP4: E2M1 x E4M3 products have at most 6 significant bits and exponents in
-// [2^-10, 2688], so the loader expands them exactly to bf16 and the GEMM runs on
-// V_MFMA_F32_32X32X16_BF16; the per-group global scales multiply the fp32
-// result.  (The block-scaled MFMA takes E8M0 scales per 32 elements; NVFP4's
-// E4M3 scales per 16 cannot be folded into it exactly.)
+// [2^-10, 2688], so a pass before the GEMM expands both operands exactly to bf16 in the
+// same 64-byte panels and the GEMM runs on V_MFMA_F32_32X32X16_BF16; the per-group global
+// scales multiply the fp32 result.  (The block-scaled MFMA takes E8M0 scales per 32
+// elements; NVFP4's E4M3 scales per 16 cannot be folded into it exactly.)
 #include "activation.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -36,18 +36,14 @@
 namespace gmlp {
 
 constexpr int BM = 256, BN = 256;
-constexpr int BKB = 128;                         // bytes per tile row per stage
 constexpr int NTHREADS = 256;
-constexpr int OPB = BM * BKB;                    // NVFP4 (bf16 after expansion): one operand stage (32 KB)
-constexpr int STAGE = 2 * OPB;                   // NVFP4 stage: A + B (64 KB), double buffered
-// MXFP8: a ring of 4 stages of 64 K (one MFMA K-step), 3 in flight while one is computed.
+// A ring of 4 stages of 64 K (one MFMA K-step), 3 in flight while one is computed.
 constexpr int MX_BK = 64;
 constexpr int MX_OPB = BM * MX_BK;               // 16 KB per operand
 constexpr int MX_SC_OFF = 2 * MX_OPB;            // scale words: A [256] then B [256] (u32)
 constexpr int MX_STAGE = 2 * MX_OPB + 2048;      // 34 KB
 constexpr int MX_NSTAGE = 4;
 constexpr int MX_DMA_PER_STAGE = 9;              // per wave: 4 A + 4 B data DMAs + 1 scale-word DMA
-constexpr int SMEM_BYTES = (MX_NSTAGE * MX_STAGE > 2 * STAGE) ? MX_NSTAGE * MX_STAGE : 2 * STAGE;
 // Epilogue staging: 128 rows x 256 bf16 (512 bytes) per buffer; the 16-byte chunk index is
 // XORed with bits 2..3 of the row so that the two rows a wave writes at once (r and r + 4)
 // fall in different banks.
@@ -76,12 +72,6 @@ __device__ __forceinline__ int64_t opaque(int64_t v) {
 }
 template <class T>
 __device__ __forceinline__ T* uni_ptr(T* p) { return reinterpret_cast<T*>(uni((int64_t)reinterpret_cast<uintptr_t>(p))); }
-
-// Physical 16-byte chunk of logical chunk c in tile row r: c ^ ((r >> 1) & 7).  Rows are 128
-// bytes, so two consecutive rows fill one 256-byte line of the 64 banks; the XOR term then
-// differs between any two rows of the same parity among 16 consecutive rows, which keeps the
-// 16 lanes of each 16-byte LDS access phase on 16 distinct bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ ((row >> 1) & 7)) << 4); }
 // 64-byte rows (MXFP8 stages): four rows share a 256-byte bank line, so the chunk is XORed
 // with (row >> 2) & 3; 16 consecutive rows then cover all 16 bank groups.
 __device__ __forceinline__ int swz64(int row, int chunk) { return row * MX_BK + ((chunk ^ ((row >> 2) & 3)) << 4); }
@@ -101,20 +91,6 @@ struct Ctx {
   int64_t a_sw_base, b_sw_base, a_sw_ld, b_sw_ld;   // MXFP8 scale words: base + kt * ld + row
   float alpha;
 };
-
-// Row of B (in the weight/feature matrix) held by tile row j, and whether it exists.
-template <int MODE, int EPI>
-__device__ __forceinline__ bool b_row(const GemmArgs& A, const Ctx& c, int j, int64_t& row) {
-  if (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
-    // SwiGLU fc1: wave wn's 128 columns are [gate f..f+63 | up f..f+63], f = nt*128 + wn*64
-    const int wn = j >> 7, q = j & 127;
-    const int64_t f = (int64_t)c.nt * 128 + wn * 64 + (q & 63);
-    row = (q < 64) ? f : A.ffn + f;
-    return f < A.ffn;
-  }
-  row = c.nrow0 + j;
-  return row < (MODE == MODE_FPROP ? A.N : A.K);
-}
 
 // ----------------------------------------------------------------------------- stage loads
 // MXFP8: direct buffer -> LDS DMA (buffer_load_dwordx4 ... lds).  One instruction moves a
@@ -187,38 +163,6 @@ struct DmaPlan {
   uint32_t lane_off;               // (lane / 4) 64 + 16 x logical chunk
 };
 
-template <int MODE, int EPI>
-__device__ __forceinline__ void b_band(const GemmArgs& A, const Ctx& c, int wave, int64_t& first, int64_t& rows) {
-  if (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
-    // band w = [gate | up][(w & 1)] rows f0 + 64 (w >> 1) .. + 64, f0 = 128 nt
-    const int64_t f = (int64_t)c.nt * 128 + 64 * (wave >> 1);
-    first = ((wave & 1) ? A.ffn : 0) + f;
-    rows = min((int64_t)64, max((int64_t)0, A.ffn - f));
-  } else {
-    const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
-    first = c.nrow0 + 64 * wave;
-    rows = min((int64_t)64, max((int64_t)0, nb - first));
-  }
-}
-
-template <int MODE, int EPI>
-__device__ __forceinline__ DmaPlan make_dma_plan(const GemmArgs& A, const Ctx& c, int wave, int lane) {
-  DmaPlan d;
-  // one instruction = 16 rows of 64 bytes; lane l -> row 16 i + l / 4, physical chunk l % 4,
-  // so it fetches logical chunk (l % 4) ^ ((row >> 2) & 3) = (l % 4) ^ ((l >> 4) & 3)
-  d.lane_off = (uint32_t)(lane >> 2) * 64u + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-  const int64_t a_rows = min(64, max(0, c.arows - 64 * wave));
-  d.a0 = A.a.data + c.a_base + (c.arow0 + 64 * wave) * 64;
-  d.a_pstride = c.a_rtot * 64;
-  d.a_bytes = (int32_t)(a_rows * 64);
-  int64_t b_first, b_rows;
-  b_band<MODE, EPI>(A, c, wave, b_first, b_rows);
-  d.b0 = A.b.data + c.b_base + b_first * 64;
-  d.b_pstride = c.b_rtot * 64;
-  d.b_bytes = (int32_t)(b_rows * 64);
-  return d;
-}
-
 // Stage kt (64 K): wave w fetches A and B rows [64 w, 64 w + 64) (4 + 4 DMAs) and one 1 KB DMA
 // of MFMA scale words for the stage's 128-K word: waves 0 and 2 the 256 A rows' words, waves 1
 // and 3 the 256 B rows' words (waves 2 and 3 repeat the same bytes).  Every wave issues the
@@ -237,37 +181,6 @@ __device__ __forceinline__ void stage_m0(StageDma& s, int wave) {
   s.m0a = base + 4096u * (uint32_t)wave;
   s.m0b = base + MX_OPB + 4096u * (uint32_t)wave;
   s.m0s = base + s.s_lds;
-}
-
-template <int MODE, int EPI>
-__device__ __forceinline__ StageDma mx_stage_plan(const GemmArgs& A, const Ctx& c, const DmaPlan& d, int kt,
-                                                  uint8_t* stage, int wave, int lane, bool live) {
-  StageDma s;
-  s.lds = stage;
-  // the stage's band: rows past the valid ones are out of the resource's range and read zero
-  s.ra = make_rsrc(d.a0 + kt * d.a_pstride, live ? d.a_bytes : 0);
-  s.rb = make_rsrc(d.b0 + kt * d.b_pstride, live ? d.b_bytes : 0);
-  const int64_t kw = kt >> 1;
-  const bool swiglu = MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0;
-  const bool is_b = (wave & 1) != 0;
-  // A rows arow0 .. arow0 + arows of the 128-K word kw
-  const uint32_t* a_w = A.a.scale_mfma + c.a_sw_base + kw * c.a_sw_ld + c.arow0;
-  const int64_t a_n = 4 * (int64_t)c.arows;
-  // B rows: the tile's 256 rows in order, or for SwiGLU fc1 the 64-row bands
-  // [gate f0 | up f0 | gate f0 + 64 | up f0 + 64] of one resource starting at gate row f0
-  const uint32_t* bw = A.b.scale_mfma + c.b_sw_base + kw * c.b_sw_ld;
-  const int64_t f0 = (int64_t)c.nt * 128;
-  const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
-  const uint32_t* b_w = swiglu ? bw + f0 : bw + c.nrow0;
-  const int64_t b_n = swiglu ? 4 * (2 * A.ffn - f0) : 4 * max((int64_t)0, nb - c.nrow0);
-  const int band = lane >> 4;
-  const uint32_t b_voff = swiglu ? 4u * (uint32_t)((band & 1) * A.ffn + (band >> 1) * 64 + 4 * (lane & 15)) : 16u * lane;
-  s.rs = make_rsrc(is_b ? b_w : a_w, live ? (is_b ? b_n : a_n) : 0);
-  s.s_voff = is_b ? b_voff : 16u * lane;
-  s.s_lds = MX_SC_OFF + (is_b ? 1024 : 0);
-  s.soa = s.sob = s.sos = 0;
-  stage_m0(s, wave);
-  return s;
 }
 
 // A tile of the persistent kernel, reduced to what fixes its DMA sources and its epilogue.
@@ -466,66 +379,6 @@ __device__ __forceinline__ void mx_dma_one(const StageDma& s, const DmaPlan& d, 
   else dma_set_m0<0>(s.rs, s.s_voff, s.sos, s.m0s);
 }
 
-template <int MODE, int EPI>
-__device__ __forceinline__ void mx_dma_stage(const GemmArgs& A, const Ctx& c, const DmaPlan& d, int kt, uint8_t* stage,
-                                             int wave, int lane, bool live) {
-  const StageDma s = mx_stage_plan<MODE, EPI>(A, c, d, kt, stage, wave, lane, live);
-  mx_dma_one<0>(s, d, wave); mx_dma_one<1>(s, d, wave); mx_dma_one<2>(s, d, wave);
-  mx_dma_one<3>(s, d, wave); mx_dma_one<4>(s, d, wave); mx_dma_one<5>(s, d, wave);
-  mx_dma_one<6>(s, d, wave); mx_dma_one<7>(s, d, wave); mx_dma_one<8>(s, d, wave);
-}
-
-// NVFP4: thread = tile row; 64 packed E2M1 (32 bytes) + 4 E4M3 block scales per operand,
-// expanded exactly to bf16 and written to LDS by the thread.
-struct NvStage {
-  uint4 ra[2], rb[2];
-  uint32_t sa[4], sb[4];
-};
-
-template <int MODE, int EPI>
-__device__ __forceinline__ void nv_load_stage(const GemmArgs& A, const Ctx& c, int kt, int tid, NvStage& s) {
-  const int64_t k = (int64_t)kt * 64;
-  const int row = tid;
-  {
-    const int ar = min(row, c.arows - 1);
-    const int64_t e = c.a_base + (c.arow0 + ar) * c.a_ld + k;
-    s.ra[0] = *reinterpret_cast<const uint4*>(A.a.data + e / 2);
-    s.ra[1] = *reinterpret_cast<const uint4*>(A.a.data + e / 2 + 16);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s.sa[q] = A.a.scale[e / 16 + q];
-  }
-  {
-    int64_t br = 0;
-    if (!b_row<MODE, EPI>(A, c, row, br)) br = (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) ? 0 : c.nrow0;
-    const int64_t e = c.b_base + br * c.b_ld + k;
-    s.rb[0] = *reinterpret_cast<const uint4*>(A.b.data + e / 2);
-    s.rb[1] = *reinterpret_cast<const uint4*>(A.b.data + e / 2 + 16);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s.sb[q] = A.b.scale[e / 16 + q];
-  }
-}
-
-__device__ __forceinline__ void nv_store_row(uint8_t* base, int row, const uint4* r, const uint32_t* s) {
-  const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
-#pragma unroll
-  for (int ch = 0; ch < 8; ++ch) {              // 8 bf16 per chunk = one packed word
-    const float sc = e4m3_decode_pos(s[ch >> 1]);
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = e2m1_decode((w[ch] >> (8 * i)) & 0xFu) * sc;
-      const float hi = e2m1_decode((w[ch] >> (8 * i + 4)) & 0xFu) * sc;
-      o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-    }
-    *reinterpret_cast<uint4*>(base + swz(row, ch)) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
-__device__ __forceinline__ void nv_store_stage(uint8_t* stage, int tid, const NvStage& s) {
-  nv_store_row(stage, tid, s.ra, s.sa);
-  nv_store_row(stage + OPB, tid, s.rb, s.sb);
-}
-
 // ----------------------------------------------------------------------------- MFMA stage
 // Fragments of one stage for one wave, read from LDS into registers before the next stage's DMA
 // is issued (the compiler cannot prove that the DMA target and the buffer being read differ,
@@ -534,28 +387,6 @@ struct MxFrags {
   v8i a[4], b[4];              // one 64-K step
   uint32_t sa[4], sb[4];       // E8M0 scale of this lane's 32-block in byte 0
 };
-struct BfFrags {
-  v8bf a[4][4], b[4][4];       // [K-step][tile]
-};
-
-__device__ __forceinline__ v8i ld_frag8(const uint8_t* base, int row, int c0, int c1) {
-  const uint4 x0 = *reinterpret_cast<const uint4*>(base + swz64(row, c0));
-  const uint4 x1 = *reinterpret_cast<const uint4*>(base + swz64(row, c1));
-  return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-}
-
-// Lane (m + 32 j) holds K bytes [16 j, 16 j + 16) and [32 + 16 j, 48 + 16 j) of the step; its
-// scale is block j of the step, i.e. byte 2 (kt & 1) + j of the stage's 128-K word, read as a
-// single byte so that it lands in byte 0 of the register the MFMA takes it from.
-template <int T>
-__device__ __forceinline__ void mx_read_t(const uint8_t* stage, int wm, int wn, int lane, int kt, MxFrags& f) {
-  const int m = lane & 31, j = lane >> 5;
-  const uint8_t* w = stage + MX_SC_OFF + 2 * (kt & 1) + j;
-  f.a[T] = ld_frag8(stage, wm * 128 + T * 32 + m, j, 2 + j);
-  f.b[T] = ld_frag8(stage + MX_OPB, wn * 128 + T * 32 + m, j, 2 + j);
-  f.sa[T] = w[4 * (wm * 128 + T * 32 + m)];
-  f.sb[T] = w[1024 + 4 * (wn * 128 + T * 32 + m)];
-}
 
 // Per-lane byte offsets of the fragment reads within a stage slot.  Tile t of a fragment adds
 // the constant 2048 t (32 rows of 64 bytes: the swizzle term (row / 4) % 4 is the same), so
@@ -594,13 +425,6 @@ __device__ __forceinline__ void mx_read_p(const uint8_t* stage, const ReadPlan& 
   mx_read_tp<1, PAR, BF>(stage, r, f);
   mx_read_tp<2, PAR, BF>(stage, r, f);
   mx_read_tp<3, PAR, BF>(stage, r, f);
-}
-
-__device__ __forceinline__ void mx_read(const uint8_t* stage, int wm, int wn, int lane, int kt, MxFrags& f) {
-  mx_read_t<0>(stage, wm, wn, lane, kt, f);
-  mx_read_t<1>(stage, wm, wn, lane, kt, f);
-  mx_read_t<2>(stage, wm, wn, lane, kt, f);
-  mx_read_t<3>(stage, wm, wn, lane, kt, f);
 }
 
 // bf16 operands (NVFP4 expanded exactly) travel in the same 64-byte stage rows: a lane's 32
@@ -663,65 +487,7 @@ __device__ __forceinline__ void mx_phase2p(const MxFrags& f, v16f (&acc)[4][4], 
   mx_mma_one<3, 3, BF>(f, acc); GMLP_SB();
 }
 
-__device__ __forceinline__ void mx_phase2(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
-                                          int wave, const uint8_t* nstage, int wm, int wn, int lane, int nkt,
-                                          MxFrags& nf) {
-  mx_read_t<0>(nstage, wm, wn, lane, nkt, nf); GMLP_SB();
-  mx_mma_one<2, 0>(f, acc); GMLP_SB();
-  mx_dma_one<5>(s, d, wave); GMLP_SB();
-  mx_read_t<1>(nstage, wm, wn, lane, nkt, nf); GMLP_SB();
-  mx_mma_one<2, 1>(f, acc); GMLP_SB(); mx_mma_one<2, 2>(f, acc); GMLP_SB();
-  mx_dma_one<6>(s, d, wave); GMLP_SB();
-  mx_read_t<2>(nstage, wm, wn, lane, nkt, nf); GMLP_SB();
-  mx_mma_one<2, 3>(f, acc); GMLP_SB(); mx_mma_one<3, 0>(f, acc); GMLP_SB();
-  mx_dma_one<7>(s, d, wave); GMLP_SB();
-  mx_read_t<3>(nstage, wm, wn, lane, nkt, nf); GMLP_SB();
-  mx_mma_one<3, 1>(f, acc); GMLP_SB(); mx_mma_one<3, 2>(f, acc); GMLP_SB();
-  mx_dma_one<8>(s, d, wave); GMLP_SB();
-  mx_mma_one<3, 3>(f, acc); GMLP_SB();
-}
-
-template <int TM0, int TM1>
-__device__ __forceinline__ void mx_mma(const MxFrags& f, v16f (&acc)[4][4]) {
-#pragma unroll
-  for (int tm = TM0; tm < TM1; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
-      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[tm], f.b[tn], acc[tm][tn], 0, 0, 0,
-                                                                     (int)f.sa[tm], 0, (int)f.sb[tn]);
-}
-
-__device__ __forceinline__ void bf_read(const uint8_t* stage, int wm, int wn, int lane, BfFrags& f) {
-  const int m = lane & 31, j = lane >> 5;
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f.a[s][t] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(stage + swz(wm * 128 + t * 32 + m, 2 * s + j)));
-      f.b[s][t] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(stage + OPB + swz(wn * 128 + t * 32 + m, 2 * s + j)));
-    }
-}
-
-__device__ __forceinline__ void bf_mma(const BfFrags& f, v16f (&acc)[4][4]) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[s][tm], f.b[s][tn], acc[tm][tn], 0, 0, 0);
-}
-
 // ----------------------------------------------------------------------------- tile mapping
-// Workgroups are dealt round-robin to the 8 XCDs; renumber so that each XCD runs a
-// contiguous range of tiles (neighbouring tiles share A rows or the expert's B tile
-// in that XCD's L2).
-__device__ __forceinline__ int xcd_remap(int bid, int nb) {
-  const int full = (nb / 8) * 8;
-  if (bid >= full) return bid;
-  return (bid % 8) * (nb / 8) + bid / 8;
-}
-
 template <int MODE, int EPI>
 __device__ __forceinline__ int tiles_n(const GemmArgs& A) {
   if (MODE == MODE_FPROP)
@@ -730,7 +496,7 @@ __device__ __forceinline__ int tiles_n(const GemmArgs& A) {
 }
 
 // Context of tile bid of an ntm x ntn tile grid.
-template <int FMT, int MODE, int EPI>
+template <int MODE, int EPI>
 __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, int ntn, int& mt, Ctx& c) {
   // Order: groups of group_rows tile rows, column-major inside a group, so that the
   // workgroups resident together on one XCD share few A row blocks and B blocks.
@@ -763,11 +529,6 @@ __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, in
     c.a_sw_ld = A.M;
     c.b_sw_base = (int64_t)c.g * ((A.K + 127) / 128) * brows;
     c.b_sw_ld = brows;
-    if (FMT == FMT_NVFP4) {
-      const float sa = nvfp4_global_scale(A.a.amax[c.g]);
-      const float sb = nvfp4_global_scale(A.b.amax[c.g]);
-      c.alpha = __fmul_rn(__fdiv_rn(1.0f, sa), __fdiv_rn(1.0f, sb));
-    }
     c.nk = (int)((A.K + 63) / 64);              // 64-K stages (both formats)
   } else {
     const int ntm = (int)((A.N + BM - 1) / BM);
@@ -790,310 +551,9 @@ __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, in
     c.a_sw_ld = A.N;
     c.b_sw_base = A.K * (int64_t)A.T.colw_off[c.g];
     c.b_sw_ld = A.K;
-    if (FMT == FMT_NVFP4) {
-      const float sa = nvfp4_global_scale(A.a.amax[c.g]);
-      const float sb = nvfp4_global_scale(A.b.amax[c.g]);
-      c.alpha = __fmul_rn(__fdiv_rn(1.0f, sa), __fdiv_rn(1.0f, sb));
-    }
     c.nk = (int)((P + 63) / 64);
   }
   return true;
-}
-
-template <int FMT, int MODE, int EPI>
-__device__ __forceinline__ bool make_ctx(const GemmArgs& A, int& mt, Ctx& c) {
-  const int ntn = tiles_n<MODE, EPI>(A);
-  return tile_ctx<FMT, MODE, EPI>(A, xcd_remap(blockIdx.x, gridDim.x), (int)(gridDim.x / ntn), ntn, mt, c);
-}
-
-// ----------------------------------------------------------------------------- kernel
-template <int FMT, int MODE, int EPI>
-__global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs A) {
-  __shared__ __align__(16) uint8_t smem[SMEM_BYTES];
-  int mt = 0;
-  Ctx c;
-  if (!make_ctx<FMT, MODE, EPI>(A, mt, c)) return;
-  c.g = uni(c.g); c.arows = uni(c.arows); c.nt = uni(c.nt); c.nk = uni(c.nk);
-  c.arow0 = uni(c.arow0); c.nrow0 = uni(c.nrow0); c.kvalid = uni(c.kvalid);
-  c.a_base = uni(c.a_base); c.b_base = uni(c.b_base); c.a_ld = uni(c.a_ld); c.b_ld = uni(c.b_ld);
-  c.a_rtot = uni(c.a_rtot); c.b_rtot = uni(c.b_rtot);
-  c.a_sw_base = uni(c.a_sw_base); c.b_sw_base = uni(c.b_sw_base); c.a_sw_ld = uni(c.a_sw_ld); c.b_sw_ld = uni(c.b_sw_ld);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = uni(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
-
-  if (FMT == FMT_MXFP8) {
-    // Ring of 4 stages of 64 K: stage s lives in slot s % 4.  Iteration kt computes stage kt
-    // from registers while stages kt+1..kt+3 are in flight; the fragments of stage kt+1 are
-    // read into the second register set between the two halves of the MFMAs.
-    const int nk = c.nk;                         // 64-K stages
-    const DmaPlan dp = make_dma_plan<MODE, EPI>(A, c, wave, lane);
-    auto slot = [&](int st) { return smem + (st & (MX_NSTAGE - 1)) * MX_STAGE; };
-    for (int st = 0; st < 3; ++st) mx_dma_stage<MODE, EPI>(A, c, dp, st, slot(st), wave, lane, st < nk);
-    MxFrags f0, f1;
-    // Every step issues one stage, live or empty, so that stage s has landed once at most the
-    // 2 x 9 DMAs of the two stages issued after it are pending; the loop body then has no
-    // branch for the compiler to move the MFMAs across.
-    wait_vmcnt<2 * MX_DMA_PER_STAGE>();
-    __syncthreads();
-    mx_read(slot(0), wm, wn, lane, 0, f0);
-    auto step = [&](int kt, const MxFrags& cur, MxFrags& nxt) __attribute__((always_inline)) {
-      // the slot of stage kt + 3 held stage kt - 1, whose fragments every wave read before
-      // the barrier of the previous step
-      const StageDma sd = mx_stage_plan<MODE, EPI>(A, c, dp, kt + 3, slot(kt + 3), wave, lane, kt + 3 < nk);
-      GMLP_SB();
-      mx_phase1(cur, acc, sd, dp, wave);
-      // stage kt + 1 has landed once at most the DMAs issued after it are pending: the 9 of
-      // stage kt + 2 and the first ones of stage kt + 3
-      wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
-      __syncthreads();
-      // on the last step this reads a slot that holds no stage; the values go unused
-      mx_phase2(cur, acc, sd, dp, wave, slot(kt + 1), wm, wn, lane, kt + 1, nxt);
-    };
-    // two steps per trip (the stage count is even: K and every P_g are multiples of 128) so
-    // that the two fragment sets stay in fixed registers
-    for (int kt = 0; kt < nk; kt += 2) {
-      step(kt, f0, f1);
-      step(kt + 1, f1, f0);
-    }
-    wait_vmcnt<0>();                 // the empty stages' DMAs, before LDS is reused
-    __syncthreads();
-  } else {
-    NvStage nv;
-    if (c.nk > 0) {
-      nv_load_stage<MODE, EPI>(A, c, 0, tid, nv);
-      nv_store_stage(smem, tid, nv);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < c.nk; ++kt) {
-      const uint8_t* cur = smem + (kt & 1) * STAGE;
-      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
-      const bool more = kt + 1 < c.nk;
-      if (more) nv_load_stage<MODE, EPI>(A, c, kt + 1, tid, nv);
-      BfFrags f;
-      bf_read(cur, wm, wn, lane, f);
-      bf_mma(f, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) nv_store_stage(nxt, tid, nv);
-      __syncthreads();
-    }
-  }
-
-  // --------------------------------------------------------------------------- epilogues
-  const int m = lane & 31, j = lane >> 5;
-  if (EPI == EPI_STORE32) {
-    // fp32 output (optional wgrad dtype), in two passes over column pairs: pass p stages the
-    // 32-column tiles tn = 2p, 2p + 1 of every wave (256 rows x 128 floats = 128 KB of LDS),
-    // then stores whole row segments with 16-byte stores.
-    float* st = reinterpret_cast<float*>(smem);
-    const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
-    float* C = static_cast<float*>(A.c);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-#pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = wm * 128 + tm * 32 + 8 * (r >> 2) + 4 * j + (r & 3);
-            st[ep32_off(row, wn * 64 + q * 32 + m)] = acc[tm][2 * p + q][r] * c.alpha;
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      __syncthreads();
-      for (int it = 0; it < 32; ++it) {
-        const int row = it * 8 + (tid >> 5);
-        const int lc = 4 * (tid & 31);
-        const int64_t gcol = c.nrow0 + (lc >> 6) * 128 + 64 * p + (lc & 63);
-        if (row < c.arows && gcol < ncols) {
-          const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + row : (int64_t)c.g * A.N + c.arow0 + row;
-          const float4 v = *reinterpret_cast<const float4*>(st + ep32_off(row, lc));
-          if (gcol + 4 <= ncols) {
-            *reinterpret_cast<float4*>(C + orow * ncols + gcol) = v;
-          } else {
-            const float e[4] = {v.x, v.y, v.z, v.w};
-            for (int q = 0; q < 4 && gcol + q < ncols; ++q) C[orow * ncols + gcol + q] = e[q];
-          }
-        }
-      }
-      __syncthreads();
-    }
-    return;
-  }
-  // Stage the bf16-rounded tile (the C dtype of every fused output) in LDS, then run the
-  // epilogue per 8-column chunk with 16-byte loads and stores.
-  {
-    uint16_t* st = reinterpret_cast<uint16_t*>(smem + wm * 65536);
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = tm * 32 + 8 * (r >> 2) + 4 * j + (r & 3);      // row within this half
-            st[ep_off(row, wn * 128 + tn * 32 + m)] = (uint16_t)f32_to_bf16_bits(acc[tm][tn][r] * c.alpha);
-          }
-          __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 tile at a time (register budget)
-        }
-  }
-  __syncthreads();
-  // staged element (row, col) of the 256 x 256 tile
-  auto stg = [&](int row, int col) -> const uint4* {
-    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem + (row >> 7) * 65536);
-    return reinterpret_cast<const uint4*>(st + ep_off(row & 127, col));
-  };
-
-  if (EPI == EPI_STORE) {
-    const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
-    uint16_t* C = static_cast<uint16_t*>(A.c);
-    for (int it = 0; it < 32; ++it) {
-      const int row = it * 8 + (tid >> 5);
-      const int col = 8 * (tid & 31);
-      const int64_t gcol = c.nrow0 + col;
-      if (row >= c.arows || gcol >= ncols) continue;
-      const int64_t orow = (MODE == MODE_FPROP) ? c.arow0 + row : (int64_t)c.g * A.N + c.arow0 + row;
-      *reinterpret_cast<uint4*>(C + orow * ncols + gcol) = *stg(row, col);
-    }
-    return;
-  }
-
-  if (EPI == EPI_FC1) {
-    const int64_t F1 = (A.act == 0) ? 2 * A.ffn : A.ffn;
-    if (A.act == 0) {
-      // staged columns of wave wn: [gate f0..f0+63 | up f0..f0+63], f0 = nt*128 + wn*64.
-      // The routing probabilities of this thread's 16 rows are loaded up front (one latency).
-      float pv[16];
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int row = it * 16 + (tid >> 4);
-        pv[it] = row < c.arows ? A.probs[c.arow0 + row] : 0.0f;
-      }
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int row = it * 16 + (tid >> 4);
-        const int fl = 8 * (tid & 15);
-        const int64_t f = (int64_t)c.nt * 128 + fl;
-        if (row >= c.arows || f >= A.ffn) continue;
-        const int64_t grow = c.arow0 + row;
-        const int scol = (fl >> 6) * 128 + (fl & 63);
-        const uint4 gv = *stg(row, scol);
-        const uint4 uv = *stg(row, scol + 64);
-        *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = gv;
-        *reinterpret_cast<uint4*>(A.h + grow * F1 + A.ffn + f) = uv;
-        const float p = pv[it];
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
-        uint32_t ow[4];
-        for (int i = 0; i < 4; ++i) {
-          const float a0 = act_out(0, bf16_to_f32(gw[i] & 0xFFFFu), bf16_to_f32(uw[i] & 0xFFFFu), p);
-          const float a1 = act_out(0, bf16_to_f32(gw[i] >> 16), bf16_to_f32(uw[i] >> 16), p);
-          ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
-        }
-        *reinterpret_cast<uint4*>(A.a_out + grow * A.ffn + f) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-      }
-    } else {
-      float pv[32];
-#pragma unroll
-      for (int it = 0; it < 32; ++it) {
-        const int row = it * 8 + (tid >> 5);
-        pv[it] = row < c.arows ? A.probs[c.arow0 + row] : 0.0f;
-      }
-#pragma unroll
-      for (int it = 0; it < 32; ++it) {
-        const int row = it * 8 + (tid >> 5);
-        const int col = 8 * (tid & 31);
-        const int64_t f = c.nrow0 + col;
-        if (row >= c.arows || f >= A.ffn) continue;
-        const int64_t grow = c.arow0 + row;
-        const uint4 hv = *stg(row, col);
-        *reinterpret_cast<uint4*>(A.h + grow * F1 + f) = hv;
-        const float p = pv[it];
-        const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
-        uint32_t ow[4];
-        for (int i = 0; i < 4; ++i) {
-          const float a0 = act_out(1, bf16_to_f32(hw[i] & 0xFFFFu), 0.0f, p);
-          const float a1 = act_out(1, bf16_to_f32(hw[i] >> 16), 0.0f, p);
-          ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
-        }
-        *reinterpret_cast<uint4*>(A.a_out + grow * A.ffn + f) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-      }
-    }
-    return;
-  }
-
-  // EPI_DACT: staged tile = da [rows, f]; writes dh (+ a' when recomputing) and per-row dprob
-  // partials of this n-tile, summed over its 256 columns in a fixed order.  The h loads of 8
-  // row-chunks are issued together before any of them is used, so that their memory latency
-  // overlaps instead of adding up chunk by chunk.
-  {
-    const int64_t F1 = (A.act == 0) ? 2 * A.ffn : A.ffn;
-    const int col = 8 * (tid & 31);
-    const int64_t f = c.nrow0 + col;
-    constexpr int BATCH = 8;
-    for (int it0 = 0; it0 < 32; it0 += BATCH) {
-      uint4 gv[BATCH], uv[BATCH];
-      float pv[BATCH];
-#pragma unroll
-      for (int b = 0; b < BATCH; ++b) {
-        const int row = (it0 + b) * 8 + (tid >> 5);
-        const bool ok = row < c.arows && f < A.ffn;
-        const int64_t grow = c.arow0 + (row < c.arows ? row : 0);
-        gv[b] = make_uint4(0, 0, 0, 0);
-        uv[b] = make_uint4(0, 0, 0, 0);
-        pv[b] = 0.0f;
-        if (ok) {
-          pv[b] = A.probs[grow];
-          gv[b] = *reinterpret_cast<const uint4*>(A.h + grow * F1 + f);
-          if (A.act == 0) uv[b] = *reinterpret_cast<const uint4*>(A.h + grow * F1 + A.ffn + f);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < BATCH; ++b) {
-        const int row = (it0 + b) * 8 + (tid >> 5);
-        const bool ok = row < c.arows && f < A.ffn;
-        const int64_t grow = c.arow0 + (row < c.arows ? row : 0);
-        float psum = 0.0f;
-        if (ok) {
-          const float p = pv[b];
-          const uint4 dv = *stg(row, col);
-          const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv[b].x, gv[b].y, gv[b].z, gv[b].w},
-                         uw[4] = {uv[b].x, uv[b].y, uv[b].z, uv[b].w};
-          uint32_t o0[4], o1[4], oa[4];
-          for (int i = 0; i < 4; ++i) {
-            uint32_t r0 = 0, r1 = 0, ra = 0;
-            for (int hh = 0; hh < 2; ++hh) {
-              const float da = bf16_to_f32((dw[i] >> (16 * hh)) & 0xFFFFu);
-              const float g = bf16_to_f32((gw[i] >> (16 * hh)) & 0xFFFFu);
-              const float u = bf16_to_f32((uw[i] >> (16 * hh)) & 0xFFFFu);
-              float d0, d1, dp;
-              act_grad(A.act, g, u, da, p, d0, d1, dp);
-              psum += dp;
-              r0 |= f32_to_bf16_bits(d0) << (16 * hh);
-              r1 |= f32_to_bf16_bits(d1) << (16 * hh);
-              ra |= (__float_as_uint(act_out(A.act, g, u, p)) >> 16) << (16 * hh);
-            }
-            o0[i] = r0;
-            o1[i] = r1;
-            oa[i] = ra;
-          }
-          *reinterpret_cast<uint4*>(A.dh + grow * F1 + f) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-          if (A.act == 0) *reinterpret_cast<uint4*>(A.dh + grow * F1 + A.ffn + f) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-          if (A.a_out) *reinterpret_cast<uint4*>(A.a_out + grow * A.ffn + f) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
-        }
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) psum += __shfl_xor(psum, o, 64);
-        if ((tid & 31) == 0 && row < c.arows) A.dprob_part[(int64_t)c.nt * A.M + grow] = psum;
-      }
-    }
-  }
 }
 
 // ----------------------------------------------------------------------------- dprob reduce
@@ -1357,7 +817,7 @@ template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ TileRef tile_ref(const GemmArgs& A, int t, int ntm, int ntn) {
   int mt;
   Ctx c;
-  tile_ctx<FMT_MXFP8, MODE, EPI>(A, t, ntm, ntn, mt, c);
+  tile_ctx<MODE, EPI>(A, t, ntm, ntn, mt, c);
   TileRef r;
   // bf16: 32 contraction elements per 64-byte stage; token offsets of the column-wise
   // operands count 2 bytes per token
@@ -1610,45 +1070,30 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, int MODE, int EPI>
-static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
-  int64_t tiles;
-  if (MODE == MODE_FPROP) {
-    tiles = ((g.M + BM - 1) / BM + g.G) * (int64_t)gemm_fprop_ntiles_n(g);
-  } else {
-    tiles = (int64_t)g.G * ((g.N + BM - 1) / BM) * ((g.K + BN - 1) / BN);
-  }
-  if (tiles <= 0) return hipSuccess;
-  GemmArgs a = g;
-  a.group_rows = 4;
-  if (const char* e = getenv("GMLP_GROUP_ROWS")) a.group_rows = atoi(e) > 0 ? atoi(e) : 1;
-  hipLaunchKernelGGL((gemm_kernel<FMT, MODE, EPI>), dim3((unsigned)tiles), dim3(NTHREADS), 0, s, a);
-  return hipGetLastError();
-}
-
 // NVFP4: both operands expanded exactly to bf16 panels in the caller's scratch, then the
 // persistent kernel on the bf16 MFMA with the groups' global scales in the epilogue.  The
 // fc2-dgrad form (EPI_DACT) stores da and runs the activation gradient as its own pass.
 static hipError_t launch_nvfp4(const GemmArgs& g, int epi, hipStream_t s) {
-  if (!g.xa || !g.xb || (epi == EPI_DACT && !g.da_tmp)) return hipErrorInvalidValue;
+  if ((!g.a.bf16 && !g.xa) || (!g.b.bf16 && !g.xb) || (epi == EPI_DACT && !g.da_tmp)) return hipErrorInvalidValue;
   hipError_t e;
-  if (g.mode == MODE_FPROP) {
-    if ((e = launch_nv_expand(g.a.data, g.a.scale, g.xa, g.M, g.K, 1, s)) != hipSuccess) return e;
-    if ((e = launch_nv_expand(g.b.data, g.b.scale, g.xb, g.N, g.K, g.G, s)) != hipSuccess) return e;
-  } else {
-    const int64_t bound = g.M + 127LL * g.G;               // padded tokens of all groups
-    if ((e = launch_nv_expand_groups(g.a.data, g.a.scale, g.xa, g.N, bound, g.T.col_off, g.G, s)) != hipSuccess)
-      return e;
-    if ((e = launch_nv_expand_groups(g.b.data, g.b.scale, g.xb, g.K, bound, g.T.col_off, g.G, s)) != hipSuccess)
-      return e;
+  const int64_t bound = g.M + 127LL * g.G;                 // padded tokens of all groups
+  if (!g.a.bf16) {
+    e = g.mode == MODE_FPROP ? launch_nv_expand(g.a.data, g.a.scale, g.xa, g.M, g.K, 1, s)
+                             : launch_nv_expand_groups(g.a.data, g.a.scale, g.xa, g.N, bound, g.T.col_off, g.G, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!g.b.bf16) {
+    e = g.mode == MODE_FPROP ? launch_nv_expand(g.b.data, g.b.scale, g.xb, g.N, g.K, g.G, s)
+                             : launch_nv_expand_groups(g.b.data, g.b.scale, g.xb, g.K, bound, g.T.col_off, g.G, s);
+    if (e != hipSuccess) return e;
   }
   GemmArgs a = g;
   a.fmt = FMT_NVFP4_BF16;
-  a.a.data = g.xa;
-  a.b.data = g.xb;
+  a.a.data = g.a.bf16 ? g.a.bf16 : g.xa;
+  a.b.data = g.b.bf16 ? g.b.bf16 : g.xb;
   // no scale words: their DMA slot runs with empty resources; give them a real base anyway
-  a.a.scale_mfma = reinterpret_cast<const uint32_t*>(g.xa);
-  a.b.scale_mfma = reinterpret_cast<const uint32_t*>(g.xb);
+  a.a.scale_mfma = reinterpret_cast<const uint32_t*>(a.a.data);
+  a.b.scale_mfma = reinterpret_cast<const uint32_t*>(a.b.data);
   if (g.mode == MODE_WGRAD) return epi == EPI_STORE32 ? launch_mx<MODE_WGRAD, EPI_STORE32, 1>(a, s)
                                                       : launch_mx<MODE_WGRAD, EPI_STORE, 1>(a, s);
   if (epi == EPI_FC1) return launch_mx<MODE_FPROP, EPI_FC1, 1>(a, s);

@@ -37,11 +37,17 @@ struct DactArgs {
   float* dprob_part;    // [ffn / 64][M]
 };
 
+// NVFP4 cast outputs; any null pointer is not written.  row_bf16 / col_bf16: the quantized
+// values dec(E2M1) dec(E4M3) (exact in bf16, no global scale) in the GEMMs' 64-byte panels:
+// row-wise element (r, k) at byte ((k / 32) M + r) 64 + 2 (k % 32); column-wise group g's
+// element (f, t) at 2 K col_off[g] + ((t / 32) K + f) 64 + 2 (t % 32).
 struct NvOut {
   uint8_t* row_data;
   uint8_t* row_scale;
   uint8_t* col_data;
   uint8_t* col_scale;
+  uint8_t* row_bf16 = nullptr;
+  uint8_t* col_bf16 = nullptr;
 };
 
 hipError_t launch_scan(const int32_t* m_splits, int G, int64_t M, SplitTables T, hipStream_t s);
@@ -85,6 +91,7 @@ struct GemmOperand {
   const uint32_t* scale_mfma; // MXFP8: MFMA-ready words
   const uint8_t* scale;       // NVFP4: E4M3 block scales (canonical)
   const float* amax;          // NVFP4: per-group (or per-expert) amax for the global scale
+  const uint8_t* bf16 = nullptr;  // NVFP4: the operand already expanded to bf16 panels (else expanded here)
 };
 
 struct GemmArgs {

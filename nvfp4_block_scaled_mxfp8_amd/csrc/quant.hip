@@ -10,11 +10,10 @@
 // Tiling: one 256-thread workgroup per (128-token tile of one group, 128-feature
 // tile).  Token tiles never straddle groups, so every 32-token (MXFP8) or
 // 16-token (NVFP4) column block starts at a group-relative multiple of its size.
-// Each thread streams 64 contiguous bf16 of one row (8 x 16-byte loads, a wave
-// covers 32 full 256-byte row segments), casts them row-wise in registers and
-// parks them in LDS; the column pass reads one feature column per lane (a wave
-// reads 128 contiguous bytes per token: conflict-free) and writes 64 contiguous
-// tokens per lane.
+// Each load instruction of a wave reads four whole 256-byte row segments (16 lanes
+// per row, 8 bf16 each); the values are cast row-wise in registers (a block spans a
+// lane pair or quad) and parked in LDS, from where the column pass reads one feature
+// column per lane.
 #include "activation.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -129,22 +128,23 @@ __device__ __forceinline__ bool tile_info(const SplitTables& T, int G, int64_t K
   return ti.rows > 0;
 }
 
-// Thread -> (row r = tid/2, 64 features at 64*(tid&1)).  Loads 64 bf16 (zero outside the
-// tile's valid rows/features) and optionally parks them in the LDS tile.
+// Load i of a thread covers tile row r = 32 wave + 4 i + lane / 16 and features 8 (lane % 16)
+// .. + 7, so that every load instruction reads four whole 256-byte row segments.  Values
+// outside the tile's valid rows / features are zero; with lds set they are also parked in the
+// unswizzled LDS tile [QT][LDW].
+__device__ __forceinline__ int chunk_row(int tid, int i) { return 32 * (tid >> 6) + 4 * i + ((tid & 63) >> 4); }
 __device__ __forceinline__ void load_row_chunk(const uint16_t* __restrict__ x, int64_t K, const TileInfo& ti,
                                                int tid, uint4 (&q)[8], uint16_t* lds) {
-  const int r = tid >> 1;
-  const int c0 = 64 * (tid & 1);
-  const uint4* src = reinterpret_cast<const uint4*>(x + (ti.gstart + ti.t0 + r) * K + ti.k0 + c0);
+  const int kc = 8 * (tid & 15);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const bool ok = (r < ti.rows) && (c0 + 8 * j < ti.kcols);
-    q[j] = ok ? src[j] : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < 8; ++i) {
+    const int r = chunk_row(tid, i);
+    const bool ok = (r < ti.rows) && (kc < ti.kcols);
+    q[i] = ok ? *reinterpret_cast<const uint4*>(x + (ti.gstart + ti.t0 + r) * K + ti.k0 + kc) : make_uint4(0, 0, 0, 0);
   }
   if (lds) {
-    uint4* dst = reinterpret_cast<uint4*>(lds + r * LDW + c0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dst[j] = q[j];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(lds + chunk_row(tid, i) * LDW + kc) = q[i];
   }
 }
 
@@ -550,6 +550,56 @@ __device__ __forceinline__ uint32_t nv_block(const float* v, float S, uint32_t& 
   return code;
 }
 
+// The 16 quantized values of a block as bf16 dec(E2M1) dec(E4M3) (exact: at most 6 significant
+// bits), written as 32 contiguous bytes of a GEMM operand panel: half of a 64-byte panel row,
+// whose other half the same lane writes for the neighbouring block.  Plain (write-back) stores,
+// so that the two halves meet in L2 before the line goes to HBM.
+__device__ __forceinline__ void nv_bf16_store(uint8_t* dst, uint32_t lo, uint32_t hi, uint32_t code) {
+  const float sc = e4m3_decode_pos(code);
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = i < 4 ? lo : hi;
+    const int sh = 8 * (i & 3);
+    const float a = e2m1_decode((w >> sh) & 0xFu) * sc;
+    const float b = e2m1_decode((w >> (sh + 4)) & 0xFu) * sc;
+    o[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+  }
+  *reinterpret_cast<v4i*>(dst) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+  *reinterpret_cast<v4i*>(dst + 16) = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+}
+
+// Half (8 values) of a 16-value block whose other half lane ^ 1 holds: the same steps as
+// nv_block, with the block maximum taken across the lane pair.  Returns the E4M3 code and the
+// 8 packed E2M1 codes (one word).
+__device__ __forceinline__ uint32_t nv_half_block(const float* v, float S, uint32_t& word) {
+  float b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b = fmaxf(b, fabsf(v[i]));
+  b = fmaxf(b, __shfl_xor(b, 1, 64));
+  const float s = __fmul_rn(__fdiv_rn(b, 6.0f), S);
+  const uint32_t code = cvt_e4m3(s);
+  const float r = (code == 0) ? 0.0f : __fdiv_rn(S, e4m3_decode_pos(code));
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = __fmul_rn(v[i], r);
+  word = cvt_e2m1x8(t);
+  return code;
+}
+
+// The 8 values of one lane's half block as bf16 dec(E2M1) dec(E4M3): 16 bytes of a panel row.
+__device__ __forceinline__ uint4 nv_bf16_half(uint32_t w, uint32_t code) {
+  const float sc = e4m3_decode_pos(code);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = e2m1_decode((w >> (8 * i)) & 0xFu) * sc;
+    const float b = e2m1_decode((w >> (8 * i + 4)) & 0xFu) * sc;
+    o[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 template <bool ROW, bool COL>
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                           SplitTables T, int G, uint32_t mask, int rht,
@@ -562,21 +612,27 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __rest
   uint4 q[8];
   load_row_chunk(x, K, ti, tid, q, COL ? tile : nullptr);
   if (ROW) {
+    // a 16-value block is a lane pair; the 16 lanes of a row write 64 contiguous packed bytes and
+    // four whole 64-byte bf16 panel rows per instruction
     const float S = nvfp4_global_scale(pre[ti.g]);
-    const int r = tid >> 1;
-    const int c0 = 64 * (tid & 1);
-    const int64_t grow = ti.gstart + ti.t0 + r;
+    const int kc = 8 * (tid & 15);
+    const int64_t k = ti.k0 + kc;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float v[16];
-      unpack8(q[2 * b], v);
-      unpack8(q[2 * b + 1], v + 8);
-      uint32_t lo, hi;
-      const uint32_t code = nv_block(v, S, lo, hi);
-      if (r < ti.rows && c0 + 16 * b < ti.kcols) {
-        const int64_t e = grow * K + ti.k0 + c0 + 16 * b;       // element index
-        *reinterpret_cast<uint2*>(o.row_data + e / 2) = make_uint2(lo, hi);
-        o.row_scale[e / 16] = (uint8_t)code;
+    for (int i = 0; i < 8; ++i) {
+      const int r = chunk_row(tid, i);
+      const int64_t grow = ti.gstart + ti.t0 + r;
+      float v[8];
+      unpack8(q[i], v);
+      uint32_t w;
+      const uint32_t code = nv_half_block(v, S, w);
+      if (r < ti.rows && kc < ti.kcols) {
+        const int64_t e = grow * K + k;                          // element index
+        if (o.row_data) {
+          *reinterpret_cast<uint32_t*>(o.row_data + e / 2) = w;
+          if ((tid & 1) == 0) o.row_scale[e / 16] = (uint8_t)code;
+        }
+        if (o.row_bf16)
+          *reinterpret_cast<uint4*>(o.row_bf16 + ((k / 32) * M + grow) * 64 + 2 * (k % 32)) = nv_bf16_half(w, code);
       }
     }
   }
@@ -602,9 +658,14 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __rest
     }
     uint32_t lo, hi;
     const uint32_t code = nv_block(v, S, lo, hi);
-    const int64_t e = colbase + (ti.k0 + c) * P + ti.t0 + 16 * tb;
-    *reinterpret_cast<uint2*>(o.col_data + e / 2) = make_uint2(lo, hi);
-    o.col_scale[e / 16] = (uint8_t)code;
+    const int64_t t = ti.t0 + 16 * tb;                          // token within the group
+    const int64_t e = colbase + (ti.k0 + c) * P + t;
+    if (o.col_data) {
+      *reinterpret_cast<uint2*>(o.col_data + e / 2) = make_uint2(lo, hi);
+      o.col_scale[e / 16] = (uint8_t)code;
+    }
+    if (o.col_bf16)
+      nv_bf16_store(o.col_bf16 + 2 * colbase + ((t / 32) * K + ti.k0 + c) * 64 + 2 * (t % 32), lo, hi, code);
   }
 }
 

@@ -114,3 +114,25 @@ def test_all_tokens_in_one_expert_and_empty_experts():
     wl = small_case([0, 0, 513, 0], 256, 256, activation="srelu", recipe="nvfp4", seed=4, w_std=0.05)
     out = _run(wl, _upload(wl), "nvfp4", recompute=True)
     _compare(out, wl, "nvfp4")
+
+
+def test_nvfp4_weights_with_or_without_bf16_panels_bitwise():
+    """Weights given as packed NVFP4 only (the GEMMs expand them into their workspace) or with the
+    bf16 panels written at quantize time give bitwise-equal outputs and gradients."""
+    wl = small_case([37, 0, 200, 64], 256, 384, activation="swiglu", recipe="nvfp4", seed=6, w_std=0.05)
+    d = _upload(wl)
+    rec = g.recipe("nvfp4", wl.sign_mask)
+    E, H, ffn, F1 = 4, 256, 384, 768
+    res = []
+    for panels in (True, False):
+        w1q = g.weight_quantize(d["w1"], rec, out=g.alloc_weight_q(rec, E, F1, H, bf16_panels=panels))
+        w2q = g.weight_quantize(d["w2"], rec, out=g.alloc_weight_q(rec, E, H, ffn, bf16_panels=panels))
+        y, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], "swiglu", rec)
+        out = g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx)
+        out["y"] = y
+        torch.cuda.synchronize()
+        res.append(out)
+    for k in ("y", "dx", "dprobs", "dw1", "dw2"):
+        a, b = res[0][k], res[1][k]
+        view = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(a.view(view), b.view(view)), k

@@ -6,6 +6,7 @@ import torch
 import nvfp4_block_scaled_mxfp8_amd as g
 from gpu_util import (assert_bytes_equal, bits16, col_total, dev_bf16, dev_f32, dev_splits, f32bits, u32, u8,
                       unpanel, unpanel_groups)
+from oracle import formats as F
 from oracle import quant as Q
 from oracle import rht as R
 from workloads import all_bf16_finite, random_bf16
@@ -143,6 +144,47 @@ def test_nvfp4_quantize_with_given_amax():
     assert_bytes_equal(u8(q.bufs["col_scale"])[:K * P // 16], ref["col_scale"], "col scales")
 
 
+def _nv_values_bf16(packed, scales):
+    """bf16 bits of dec(E2M1) * dec(E4M3) for the oracle's packed codes [R, C/2] and scales [R, C/16]."""
+    nib = F.unpack_fp4(packed)
+    vals = F.e2m1_decode(nib) * np.repeat(F.e4m3_decode(scales), 16, axis=-1)
+    return F.f64_to_bf16_bits(vals)
+
+
+def _unpanel16(buf, R, C):
+    """bf16 operand panels (2-byte elements, 32 per 64-byte row) -> [R, C] uint16."""
+    return np.ascontiguousarray(unpanel(np.asarray(buf).reshape(-1)[:2 * R * C], R, 2 * C)).view(np.uint16)
+
+
+def test_nvfp4_bf16_panels():
+    """The cast's bf16 GEMM panels hold exactly dec(E2M1) dec(E4M3) of the oracle's codes, row-wise and
+    per group column-wise (RHT), next to the packed form."""
+    splits, K, mask = [33, 0, 160, 200], 256, 0x2D4B
+    M, G = sum(splits), len(splits)
+    print(f"nvfp4 bf16 panels splits={splits} K={K}", flush=True)
+    x = random_bf16((M, K), seed=41, dist="wide")
+    rec = g.recipe("nvfp4", mask)
+    q = g.alloc_grouped_q(rec, M, K, G, True, True)
+    PR = g.col_rows_bound(M, G)
+    q.bufs["row_bf16"] = torch.empty(2 * M * K, dtype=torch.uint8, device="cuda")
+    q.bufs["col_bf16"] = torch.empty(2 * K * PR, dtype=torch.uint8, device="cuda")
+    g.group_quantize(dev_bf16(x), dev_splits(splits), rec, True, True, out=q)
+    torch.cuda.synchronize()
+    pre, post = R.group_hadamard_amax(x, splits, mask)
+    ref = Q.nvfp4_group_quantize_with_amax(x, splits, pre, post, mask)
+    assert_bytes_equal(u8(q.bufs["row_data"])[:M * K // 2], ref["row_data"], "row data")
+    assert_bytes_equal(_unpanel16(u8(q.bufs["row_bf16"]), M, K), _nv_values_bf16(ref["row_data"].reshape(M, K // 2),
+                                                                               ref["row_scale"]), "row bf16 panels")
+    col = u8(q.bufs["col_bf16"])
+    off = 0
+    for gi, (packed, sc) in enumerate(ref["col_groups"]):
+        P = -(-splits[gi] // 128) * 128
+        if P:
+            assert_bytes_equal(_unpanel16(col[2 * off:2 * (off + K * P)], K, P), _nv_values_bf16(packed, sc),
+                               f"col bf16 panels of group {gi}")
+        off += K * P
+
+
 @pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
 def test_weight_quantize(kind):
     """fprop operand (blocks along K) and dgrad operand (W_e^T, blocks along N), stacked and discrete."""
@@ -171,3 +213,10 @@ def test_weight_quantize(kind):
             assert_bytes_equal(u8(q.bufs["row_scale"]), np.stack([r[1] for r in ref["row"]]), "w row scales")
             assert_bytes_equal(u8(q.bufs["col_data"]), np.stack([r[0] for r in ref["colT"]]), "w col data")
             assert_bytes_equal(u8(q.bufs["col_scale"]), np.stack([r[1] for r in ref["colT"]]), "w col scales")
+            rb, cb = u8(q.bufs["row_bf16"]), u8(q.bufs["col_bf16"])
+            for e in range(E):
+                n2 = 2 * N * K
+                assert_bytes_equal(_unpanel16(rb[e * n2:(e + 1) * n2], N, K), _nv_values_bf16(*ref["row"][e]),
+                                   f"w row bf16 panels, expert {e}")
+                assert_bytes_equal(_unpanel16(cb[e * n2:(e + 1) * n2], K, N), _nv_values_bf16(*ref["colT"][e]),
+                                   f"w col bf16 panels, expert {e}")
