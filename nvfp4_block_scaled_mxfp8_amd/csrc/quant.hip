@@ -169,27 +169,45 @@ __device__ __forceinline__ uint32_t mx_block(const float* v, uint32_t* w) {
   return code;
 }
 
-// Column-wise MXFP8 cast of a parked bf16 tile [QT tokens][LDW] whose features are features
-// kf0 .. kf0 + kcols of a K-feature tensor.  The group's [K, P_g] column-wise tensor is stored
-// in 64-byte token panels: byte (f, t) at ((t / 64) K + f) 64 + t % 64, so the tile holds two
-// panel rows (token halves) per feature.  Task u = 256 k + tid (k = 0..3) -> feature
-// c = (u / 4) % 128, token half u / 512, 16-token part p = u % 4: a 32-token block spans the
-// lane pair p = 0, 1 or 2, 3 (amax by one shuffle), and the 64 lanes of a wave store 16 whole
-// panel rows = 1 KB of contiguous memory per instruction.  A thread holds both halves of its
-// features (k and k + 2), so it assembles the MFMA scale word (4 blocks of 128 tokens) with one
-// more shuffle.
-__device__ __forceinline__ void col_cast_tile(const uint16_t* tile, const TileInfo& ti, int64_t K, int64_t kf0,
+// MXFP8 group quantize works on half tiles: 64 tokens (one column-wise token panel) x 128
+// features (one row-wise MFMA scale word), parked in 17 KB of LDS so that eight workgroups per
+// CU keep loads, row casts and column casts of different tiles overlapping.
+constexpr int MQT = 64;
+
+// Token half-tile blockIdx.y (the halves of the groups' 128-row tiles) and feature tile
+// blockIdx.x.  A half past the group's rows but inside its 128-token padding is valid: its
+// column-wise output is the padding (zero data, code 127).
+__device__ __forceinline__ bool half_tile_info(const SplitTables& T, int G, int64_t K, TileInfo& ti) {
+  const int tt = blockIdx.y >> 1;
+  if (G <= 0 || tt >= T.t128_off[G]) return false;
+  ti.g = find_group(T.t128_off, G, tt);
+  ti.gstart = T.row_off[ti.g];
+  ti.m = T.row_off[ti.g + 1] - (int)ti.gstart;
+  ti.t0 = (tt - T.t128_off[ti.g]) * QT + MQT * (int)(blockIdx.y & 1);
+  ti.rows = max(0, min(MQT, ti.m - ti.t0));
+  ti.k0 = (int64_t)blockIdx.x * QF;
+  ti.kcols = (int)min((int64_t)QF, K - ti.k0);
+  return ti.m > 0;
+}
+
+// Column-wise MXFP8 cast of a parked half tile [64 tokens][LDW] whose features are kf0 ..
+// kf0 + kcols of a K-feature tensor.  The group's [K, P_g] column-wise tensor is stored in
+// 64-byte token panels: byte (f, t) at ((t / 64) K + f) 64 + t % 64, so the half tile is one
+// panel row per feature.  Task u = 256 k + tid (k = 0, 1) -> feature c = u / 4, 16-token part
+// p = u % 4: a 32-token block spans the lane pair p = 0, 1 or 2, 3 (amax by one shuffle), and
+// the 64 lanes of a wave store 16 whole panel rows = 1 KB of contiguous memory per instruction.
+// The half tile owns bytes 2 h and 2 h + 1 (h = its half of the 128-token tile) of each
+// feature's MFMA scale word.
+__device__ __forceinline__ void col_cast_half(const uint16_t* tile, const TileInfo& ti, int64_t K, int64_t kf0,
                                               int kcols, const SplitTables& T, const MxOut& o, int tid) {
   const int p = tid & 3;
   const int P = (ti.m + 127) & ~127;
-  const int rowsP = min(QT, P - ti.t0);            // tile tokens inside the group's padding
   const int64_t colbase = K * (int64_t)T.col_off[ti.g];
-  uint32_t word[2] = {0, 0};                       // features tid / 4 and 64 + tid / 4
+  const int h = (ti.t0 / MQT) & 1;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = (64 * k + (tid >> 2)) & (QF - 1);
-    const int half = k >> 1;
-    const int tok0 = 64 * half + 16 * p;
+  for (int k = 0; k < 2; ++k) {
+    const int c = 64 * k + (tid >> 2);
+    const int tok0 = 16 * p;
     float v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = bf16_to_f32(tile[tile_off(tok0 + i, c)]);
@@ -202,28 +220,23 @@ __device__ __forceinline__ void col_cast_tile(const uint16_t* tile, const TileIn
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = cvt_e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
-    const bool inpad = tok0 < rowsP;
-    if (inpad && c < kcols) {
+    if (c < kcols) {
+      // every token of the half tile lies inside the group's padded range P
       __builtin_nontemporal_store(v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
-                                  reinterpret_cast<v4i*>(o.col_data + colbase + (((ti.t0 / 64) + half) * K + kf0 + c) * 64 + 16 * p));
+                                  reinterpret_cast<v4i*>(o.col_data + colbase + ((ti.t0 / 64) * K + kf0 + c) * 64 + 16 * p));
       if (o.col_scale && (p & 1) == 0)
-        o.col_scale[colbase / 32 + (kf0 + c) * (P / 32) + ti.t0 / 32 + 2 * half + (p >> 1)] = (uint8_t)code;
+        o.col_scale[colbase / 32 + (kf0 + c) * (P / 32) + ti.t0 / 32 + (p >> 1)] = (uint8_t)code;
     }
-    word[k & 1] |= (inpad ? code : 127u) << (8 * (2 * half + (p >> 1)));
-  }
-  if (o.col_scale_mfma) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t full = word[h] | (uint32_t)__shfl_xor((int)word[h], 2, 64);
-      const int c = 64 * h + (tid >> 2);
-      if (p == 0 && c < kcols)
-        o.col_scale_mfma[K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K + kf0 + c] = full;
-    }
+    // bytes 2 h + (p >> 1) of the word: the lane pair p = 0 and 2 holds both
+    const uint32_t pair = (code << (8 * (p >> 1))) | ((uint32_t)__shfl_xor((int)code, 2, 64) << (8 * (1 - (p >> 1))));
+    if (o.col_scale_mfma && p == 0 && c < kcols)
+      reinterpret_cast<uint16_t*>(o.col_scale_mfma)[2 * (K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K +
+                                                          kf0 + c) + h] = (uint16_t)pair;
   }
 }
 
 // ----------------------------------------------------------------------------- MXFP8 cast
-// Loads and the row-wise cast: wave w, load i (0..7), lane l -> tile row 32 w + 4 i + l / 16,
+// Loads and the row-wise cast: wave w, load i (0..3), lane l -> tile row 16 w + 4 i + l / 16,
 // features 8 (l % 16) .. + 7, so every load instruction reads four whole 256-byte row segments.
 // A 32-feature block is the lane quad l % 16 in {4b .. 4b + 3} (amax by two shuffles); each
 // lane stores its 8 codes into the row's panel, and the 16 lanes of a row assemble its MFMA
@@ -231,25 +244,26 @@ __device__ __forceinline__ void col_cast_tile(const uint16_t* tile, const TileIn
 template <bool ROW, bool COL>
 __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                           SplitTables T, int G, MxOut o) {
-  __shared__ __align__(16) uint16_t tile[COL ? QT * LDW : 8];
+  __shared__ __align__(16) uint16_t tile[COL ? MQT * LDW : 8];
   TileInfo ti;
-  if (!tile_info(T, G, K, ti)) return;
+  if (!half_tile_info(T, G, K, ti)) return;
+  if (!COL && ti.rows == 0) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int ch = lane & 15;
   const int kc = 8 * ch;
   const bool kok = kc < ti.kcols;
-  uint4 q[8];
+  uint4 q[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 32 * wave + 4 * i + (lane >> 4);
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wave + 4 * i + (lane >> 4);
     const bool ok = r < ti.rows && kok;
     q[i] = ok ? *reinterpret_cast<const uint4*>(x + (ti.gstart + ti.t0 + r) * K + ti.k0 + kc) : make_uint4(0, 0, 0, 0);
   }
   if (COL) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 32 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + (lane >> 4);
       *reinterpret_cast<uint4*>(tile + tile_off(r, kc)) = q[i];
     }
   }
@@ -258,8 +272,8 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __rest
     const int64_t pn = f / 64;
     const int64_t pw = min((int64_t)64, K - 64 * pn);    // width of the (last, maybe narrower) panel
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 32 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + (lane >> 4);
       const int64_t grow = ti.gstart + ti.t0 + r;
       float v[8];
       unpack8(q[i], v);
@@ -289,7 +303,7 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __rest
   }
   if (!COL) return;
   __syncthreads();
-  col_cast_tile(tile, ti, K, ti.k0, ti.kcols, T, o, tid);
+  col_cast_half(tile, ti, K, ti.k0, ti.kcols, T, o, tid);
 }
 
 // ----------------------------------------------------------------------------- fused activation gradient + MXFP8 cast
@@ -315,7 +329,7 @@ constexpr int DLW = DF + 8;           // parked row stride (bf16): 144 bytes, 16
 __device__ __forceinline__ int dtile_off(int r, int c) { return r * DLW + (c ^ (((r >> 4) & 3) << 4)); }
 
 // Column-wise MXFP8 cast of a parked [128 tokens][64 features] tile whose features are
-// kf0 .. kf0 + 63 of a K-feature tensor (token panels, as in col_cast_tile).  Task
+// kf0 .. kf0 + 63 of a K-feature tensor (token panels, as in col_cast_half).  Task
 // u = 256 k + tid (k = 0, 1) -> feature c = tid / 4, token half k, 16-token part p = tid % 4.
 __device__ __forceinline__ void col_cast_tile64(const uint16_t* tile, const TileInfo& ti, int64_t K, int64_t kf0,
                                                 const SplitTables& T, const MxOut& o, int tid) {
@@ -717,7 +731,7 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
 hipError_t launch_mxfp8_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G, bool row, bool col,
                               MxOut o, hipStream_t s) {
   if (M == 0 || (!row && !col)) return hipSuccess;
-  const dim3 grid = tile_grid(M, K, G);
+  const dim3 grid((unsigned)((K + QF - 1) / QF), (unsigned)(2 * ((M + QT - 1) / QT + G)));   // half tiles
   if (row && col) hipLaunchKernelGGL((mxfp8_quant_kernel<true, true>), grid, dim3(256), 0, s, x, M, K, T, G, o);
   else if (row) hipLaunchKernelGGL((mxfp8_quant_kernel<true, false>), grid, dim3(256), 0, s, x, M, K, T, G, o);
   else hipLaunchKernelGGL((mxfp8_quant_kernel<false, true>), grid, dim3(256), 0, s, x, M, K, T, G, o);
