@@ -70,6 +70,7 @@ SplitTables carve_tables(Bump& b, int G) {
   T.colw_off = b.take<int32_t>(G + 1);
   T.t128_off = b.take<int32_t>(G + 1);
   T.t256_off = b.take<int32_t>(G + 1);
+  T.amax_slots = b.take<uint32_t>(2 * (size_t)G * kAmaxSlots);
   return T;
 }
 
@@ -188,8 +189,6 @@ gmlp_status quant_core(const void* x, int64_t M, int64_t K, const int32_t* m_spl
     return ok();
   }
   if (compute_amax) {
-    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(out->amax_pre), 0u, G, stream), "fill")) return L.st;
-    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(out->amax_post), 0u, G, stream), "fill")) return L.st;
     if (!L.check(launch_hadamard_amax(xx, M, K, T, G, r.rht_sign_mask & 0xFFFFu, out->amax_pre, out->amax_post,
                                       stream), "hadamard amax"))
       return L.st;
@@ -593,8 +592,6 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
   } else {
     float* pre = C.xq_col.q.amax_pre;
     float* post = C.xq_col.q.amax_post;
-    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(pre), 0u, E, stream), "fill")) return L.st;
-    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(post), 0u, E, stream), "fill")) return L.st;
     if (!L.check(launch_hadamard_amax(x, M, H, W.T, E, r.rht_sign_mask & 0xFFFF, pre, post, stream), "amax x")) return L.st;
     g_counts[CNT_HAMAX]++;
     NvOut o = nv_out(W.xq_row.q, true, false);
@@ -632,8 +629,6 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     if (!L.check(launch_mxfp8_quant(W.a, M, ffn, W.T, E, true, a_col, o, stream), "mxfp8 quantize fc2 input")) return L.st;
     g_counts[CNT_MXQ]++;
   } else {
-    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(C.a_pre), 0u, E, stream), "fill")) return L.st;
-    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(C.a_post), 0u, E, stream), "fill")) return L.st;
     if (!L.check(launch_hadamard_amax(W.a, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, C.a_pre, C.a_post, stream),
                  "amax fc2 input"))
       return L.st;
@@ -701,8 +696,6 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
       g_counts[CNT_MXQ]++;
       return true;
     }
-    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(q.q.amax_pre), 0u, E, stream), "fill")) return false;
-    if (!L.check(launch_fill_u32(reinterpret_cast<uint32_t*>(q.q.amax_post), 0u, E, stream), "fill")) return false;
     if (!L.check(launch_hadamard_amax(t, M, K, W.T, E, mask, q.q.amax_pre, q.q.amax_post, stream), "amax")) return false;
     g_counts[CNT_HAMAX]++;
     const NvOut o = nv_out(q.q, row, col);

@@ -14,7 +14,12 @@ struct SplitTables {
   int32_t* colw_off;   // P_g / 128 (MFMA-ready column-wise scale words)
   int32_t* t128_off;   // ceil(m_g / 128)  (128-row tiles)
   int32_t* t256_off;   // ceil(m_g / 256)  (256-row tiles)
+  // NVFP4 amax partials [2 (pre, post)][G][kAmaxSlots] (non-negative floats as bits): the scan
+  // clears them, the Hadamard-amax kernel maxes into them (a workgroup picks one slot, so that
+  // few atomics meet on one address), and its finalize pass reduces and clears them again.
+  uint32_t* amax_slots;
 };
+constexpr int kAmaxSlots = 32;
 
 struct MxOut {
   uint8_t* row_data;

@@ -47,6 +47,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ m
     T.row_off[0] = T.col_off[0] = T.colw_off[0] = T.t128_off[0] = T.t256_off[0] = 0;
   }
   uint32_t flags = 0;
+  for (int i = t; i < 2 * G * kAmaxSlots; i += 256) T.amax_slots[i] = 0u;
   __syncthreads();
   for (int base = 0; base < G; base += 256) {
     const int g = base + t;
@@ -497,8 +498,7 @@ __device__ __forceinline__ void signed_fwht16(float* v, uint32_t mask) {
 }
 
 __global__ __launch_bounds__(256) void hadamard_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                            SplitTables T, int G, uint32_t mask,
-                                                            float* __restrict__ pre, float* __restrict__ post) {
+                                                            SplitTables T, int G, uint32_t mask) {
   __shared__ __align__(16) uint16_t tile[QT * LDW];
   __shared__ float red[2][4];
   TileInfo ti;
@@ -540,10 +540,26 @@ __global__ __launch_bounds__(256) void hadamard_amax_kernel(const uint16_t* __re
   if (tid == 0) {
     float a = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     float b = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-    // non-negative floats order like their bit patterns
-    atomicMax(reinterpret_cast<unsigned int*>(pre + ti.g), __float_as_uint(a));
-    atomicMax(reinterpret_cast<unsigned int*>(post + ti.g), __float_as_uint(b));
+    // non-negative floats order like their bit patterns; one of the group's slots per workgroup
+    const int slot = (int)((blockIdx.x + 7u * blockIdx.y) % (unsigned)kAmaxSlots);
+    atomicMax(T.amax_slots + ((int64_t)ti.g * kAmaxSlots + slot), __float_as_uint(a));
+    atomicMax(T.amax_slots + ((int64_t)(G + ti.g) * kAmaxSlots + slot), __float_as_uint(b));
   }
+}
+
+// pre[g] / post[g] = the max over the group's slots, which are cleared for the next amax pass.
+__global__ __launch_bounds__(256) void amax_finalize_kernel(SplitTables T, int G, float* __restrict__ pre,
+                                                            float* __restrict__ post) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);     // (direction, group)
+  if (i >= 2 * G) return;
+  uint32_t* s = T.amax_slots + (int64_t)i * kAmaxSlots;
+  uint32_t m = 0;
+#pragma unroll 8
+  for (int j = 0; j < kAmaxSlots; ++j) {
+    m = max(m, s[j]);
+    s[j] = 0u;
+  }
+  (i < G ? pre : post)[i < G ? i : i - G] = __uint_as_float(m);
 }
 
 // ----------------------------------------------------------------------------- NVFP4 cast
@@ -751,8 +767,9 @@ hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M,
 
 hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G, uint32_t mask,
                                 float* pre, float* post, hipStream_t s) {
-  if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(hadamard_amax_kernel, tile_grid(M, K, G), dim3(256), 0, s, x, M, K, T, G, mask, pre, post);
+  // with no rows the finalize still writes the (zero) amax of every group
+  if (M > 0) hipLaunchKernelGGL(hadamard_amax_kernel, tile_grid(M, K, G), dim3(256), 0, s, x, M, K, T, G, mask);
+  hipLaunchKernelGGL(amax_finalize_kernel, dim3((unsigned)((2 * G + 255) / 256)), dim3(256), 0, s, T, G, pre, post);
   return hipGetLastError();
 }
 
