@@ -69,3 +69,31 @@ def test_validation_happens_before_any_launch():
     args.recipe = g.recipe("mxfp8")
     assert L.gmlp_grouped_mlp_forward(ctypes.byref(args), None) == 2
     assert "ffn" in g.last_error()
+
+
+def test_grouped_gemm_workspace_query():
+    """MXFP8 GEMMs need only the split tables; NVFP4 ones also hold both operands expanded to bf16."""
+    mx = g.grouped_gemm_ws_bytes(g.GEMM_FPROP, g.recipe("mxfp8"), 8, 32768, 4096, 3072)
+    assert 0 < mx < 1 << 20
+    nv = g.grouped_gemm_ws_bytes(g.GEMM_FPROP, g.recipe("nvfp4", 1), 8, 32768, 4096, 3072)
+    assert nv >= 2 * (32768 * 3072 + 8 * 4096 * 3072)
+    wg = g.grouped_gemm_ws_bytes(g.GEMM_WGRAD, g.recipe("nvfp4", 1), 8, 32768, 4096, 1536)
+    assert wg >= 2 * (4096 + 1536) * (32768 + 127 * 8)
+    with pytest.raises(g.GmlpError):
+        g.grouped_gemm_ws_bytes(5, g.recipe("mxfp8"), 8, 32768, 4096, 3072)
+
+
+def test_nvfp4_sizes_hold_bf16_operand_panels():
+    """Inside the fused MLP the NVFP4 casts are kept as bf16 GEMM panels (2 bytes per element)."""
+    M, E, H, ffn = 24576, 8, 5120, 2048
+    nv = g.query_sizes(M, E, H, ffn, "srelu", g.recipe("nvfp4", 3), recompute=False)
+    assert nv["ctx_bytes"] >= 2 * H * M + 2 * ffn * M           # column-wise x and fc2 input panels
+    assert nv["ws_bytes"] >= 2 * M * H                          # row-wise dy (or x) panels
+
+
+def test_nvfp4_gemm_operand_validation():
+    L = g.lib()
+    q = g.GroupedQ()                                            # no data, scales or amax
+    st = L.gmlp_grouped_gemm(0, g.recipe("nvfp4", 1), ctypes.byref(q), ctypes.byref(q), ctypes.c_void_p(16), 1, 64,
+                             128, 128, ctypes.c_void_p(16), 0, None, 0, None)
+    assert st == 1 and "amax" in g.last_error()
