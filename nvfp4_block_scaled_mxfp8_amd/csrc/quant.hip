@@ -635,12 +635,28 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __rest
                                                           SplitTables T, int G, uint32_t mask, int rht,
                                                           const float* __restrict__ pre,
                                                           const float* __restrict__ post, NvOut o) {
-  __shared__ __align__(16) uint16_t tile[COL ? QT * LDW : 8];
+  // 64-token half tiles, as the MXFP8 cast: load i of a thread covers half-tile row
+  // 16 wave + 4 i + lane / 16, features 8 (lane % 16) .. + 7
+  __shared__ __align__(16) uint16_t tile[COL ? MQT * LDW : 8];
   TileInfo ti;
-  if (!tile_info(T, G, K, ti)) return;
+  if (!half_tile_info(T, G, K, ti)) return;
+  if (!COL && ti.rows == 0) return;
   const int tid = threadIdx.x;
-  uint4 q[8];
-  load_row_chunk(x, K, ti, tid, q, COL ? tile : nullptr);
+  auto hrow = [&](int i) { return 16 * (tid >> 6) + 4 * i + ((tid & 63) >> 4); };
+  uint4 q[4];
+  {
+    const int kc = 8 * (tid & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = hrow(i);
+      const bool ok = (r < ti.rows) && (kc < ti.kcols);
+      q[i] = ok ? *reinterpret_cast<const uint4*>(x + (ti.gstart + ti.t0 + r) * K + ti.k0 + kc) : make_uint4(0, 0, 0, 0);
+    }
+    if (COL) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(tile + hrow(i) * LDW + kc) = q[i];
+    }
+  }
   if (ROW) {
     // a 16-value block is a lane pair; the 16 lanes of a row write 64 contiguous packed bytes and
     // four whole 64-byte bf16 panel rows per instruction
@@ -648,8 +664,8 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __rest
     const int kc = 8 * (tid & 15);
     const int64_t k = ti.k0 + kc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = chunk_row(tid, i);
+    for (int i = 0; i < 4; ++i) {
+      const int r = hrow(i);
       const int64_t grow = ti.gstart + ti.t0 + r;
       float v[8];
       unpack8(q[i], v);
@@ -675,8 +691,8 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __rest
   const int64_t colbase = K * (int64_t)T.col_off[ti.g];
   if (c >= ti.kcols) return;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tb = 4 * half + j;
+  for (int j = 0; j < 2; ++j) {
+    const int tb = 2 * half + j;                               // a half tile lies inside the padding P
     if (ti.t0 + 16 * tb >= P) break;
     float v[16];
 #pragma unroll
@@ -777,7 +793,7 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, SplitTabl
                               bool rht, bool row, bool col, const float* pre, const float* post, NvOut o,
                               hipStream_t s) {
   if (M == 0 || (!row && !col)) return hipSuccess;
-  const dim3 grid = tile_grid(M, K, G);
+  const dim3 grid((unsigned)((K + QF - 1) / QF), (unsigned)(2 * ((M + QT - 1) / QT + G)));   // half tiles
   const int r = rht ? 1 : 0;
   if (row && col)
     hipLaunchKernelGGL((nvfp4_quant_kernel<true, true>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o);
