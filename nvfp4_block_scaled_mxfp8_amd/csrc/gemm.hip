@@ -499,13 +499,26 @@ __device__ __forceinline__ int tiles_n(const GemmArgs& A) {
 template <int MODE, int EPI>
 __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, int ntn, int& mt, Ctx& c) {
   // Order: groups of group_rows tile rows, column-major inside a group, so that the
-  // workgroups resident together on one XCD share few A row blocks and B blocks.
+  // workgroups resident together on one XCD share few A row blocks and B blocks.  WGRAD tiles
+  // are ordered expert by expert (the row groups stay inside one expert), so that an expert's
+  // tiles are one contiguous range of the sequence.
   const int gr = A.group_rows;
   const int gsz = gr * ntn;
-  const int grp = bid / gsz, rem = bid - grp * gsz;
-  const int rows_here = min(gr, ntm - grp * gr);
-  const int tile_m = grp * gr + rem % rows_here;
-  c.nt = rem / rows_here;
+  int tile_m;
+  if (MODE == MODE_WGRAD) {
+    const int per_g = (int)((A.N + BM - 1) / BM);
+    const int tpg = per_g * ntn;
+    const int e = bid / tpg, loc = bid - e * tpg;
+    const int grp = loc / gsz, rem = loc - grp * gsz;
+    const int rows_here = min(gr, per_g - grp * gr);
+    tile_m = e * per_g + grp * gr + rem % rows_here;
+    c.nt = rem / rows_here;
+  } else {
+    const int grp = bid / gsz, rem = bid - grp * gsz;
+    const int rows_here = min(gr, ntm - grp * gr);
+    tile_m = grp * gr + rem % rows_here;
+    c.nt = rem / rows_here;
+  }
   c.alpha = 1.0f;
   if (MODE == MODE_FPROP) {
     if (A.G <= 0 || tile_m >= A.T.t256_off[A.G]) return false;
@@ -831,6 +844,48 @@ __device__ __forceinline__ TileRef tile_ref(const GemmArgs& A, int t, int ntm, i
   return r;
 }
 
+// WGRAD: the XCD ranges [lo, hi) of the tile sequence hold equal shares of the work rather than
+// equal numbers of tiles, because experts' token counts (each tile's contraction length) can
+// differ by orders of magnitude.  A tile of expert g costs its stages plus an epilogue's worth
+// (kEpiStages); expert g's tiles are the contiguous range [g tpg, (g + 1) tpg).  The boundary
+// for cost c is the first tile whose preceding tiles cost at least c, so the ranges of the 8
+// XCDs tile the sequence exactly.
+constexpr int64_t kEpiStages = 8;
+template <int BF>
+__device__ __forceinline__ int64_t wgrad_tile_cost(const GemmArgs& A, int g) {
+  const int64_t P = A.T.col_off[g + 1] - A.T.col_off[g];
+  return ((BF ? 2 : 1) * P + 63) / 64 + kEpiStages;
+}
+// Only when the costs are skewed (the dearest tile above twice the mean): with near-equal costs
+// the equal-count ranges are whole rounds of the XCD's workgroups, which cost-cut ranges break.
+template <int BF>
+__device__ __forceinline__ void wgrad_xcd_range(const GemmArgs& A, int tpg, int x, int& lo, int& hi) {
+  int64_t W = 0, wmax = 0;
+  for (int g = 0; g < A.G; ++g) {
+    const int64_t w = wgrad_tile_cost<BF>(A, g);
+    W += tpg * w;
+    wmax = w > wmax ? w : wmax;
+  }
+  if (wmax * A.G * tpg <= 2 * W) return;
+  const int64_t c0 = W * x / 8, c1 = W * (x + 1) / 8;
+  lo = hi = A.G * tpg;
+  bool have_lo = false;
+  int64_t pre = 0;
+  for (int g = 0; g < A.G; ++g) {
+    const int64_t w = wgrad_tile_cost<BF>(A, g);
+    const int64_t end = pre + tpg * w;
+    if (!have_lo && end > c0) {
+      lo = g * tpg + (int)((c0 - pre + w - 1) / w);
+      have_lo = true;
+    }
+    if (end > c1) {
+      hi = g * tpg + (int)((c1 - pre + w - 1) / w);
+      break;
+    }
+    pre = end;
+  }
+}
+
 template <int MODE, int EPI, int BF>
 __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
   __shared__ __align__(16) uint8_t smem[MX_NSTAGE * MX_STAGE];
@@ -842,8 +897,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
   const int ntm = (MODE == MODE_FPROP) ? (A.G > 0 ? uni(A.T.t256_off[A.G]) : 0) : A.G * (int)((A.N + BM - 1) / BM);
   const int64_t nt = (int64_t)ntm * ntn;
   const int nwx = gridDim.x / 8, x = blockIdx.x % 8, lw = blockIdx.x / 8;
-  const int hi = (int)(nt * (x + 1) / 8);
-  int t = (int)(nt * x / 8) + lw;
+  int lo = (int)(nt * x / 8), hi = (int)(nt * (x + 1) / 8);
+  if (MODE == MODE_WGRAD) wgrad_xcd_range<BF>(A, ntm / A.G * ntn, x, lo, hi);
+  lo = uni(lo);
+  hi = uni(hi);
+  int t = lo + lw;
   if (t >= hi) return;
 
   const uint32_t lane_off = (uint32_t)(lane >> 2) * 64u + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
