@@ -315,13 +315,13 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __rest
 // features go to dprob_part[feature tile][row]; with a2 set it also rebuilds the fc2 input
 // a = bf16(act(h) p) and casts it column-wise (fc2 wgrad with activation recompute).
 //
-// Tile = 128 tokens x 64 of the ffn features (one 64-byte K panel of each output; for SwiGLU
+// Tile = 64 tokens x 64 of the ffn features (one 64-byte K panel of each output; for SwiGLU
 // the gate and up gradients of those features are dh columns f and ffn + f).  Thread -> rows
-// 32 j + tid / 8 (j = 0..3), features 8 (tid % 8) .. + 7: every load instruction reads 32 whole
+// 32 j + tid / 8 (j = 0, 1), features 8 (tid % 8) .. + 7: every load instruction reads 32 whole
 // 128-byte row segments of each input, the 8 lanes of a row reduce its dL/dp partial, a
 // 32-feature block is a lane quad, and the lanes of a row store one whole 64-byte panel row.
-// Parked tiles (bf16 [128 tokens][DLW]) feed the column pass; a small tile (37 KB of LDS
-// without the rebuild) keeps four workgroups per CU in flight.
+// Parked tiles (bf16 [64 tokens][DLW]) feed the column pass; the small tiles (18 KB of LDS
+// without the rebuild) keep eight workgroups per CU in flight.
 constexpr int DF = 64;                // features per tile
 constexpr int DLW = DF + 8;           // parked row stride (bf16): 144 bytes, 16-byte aligned
 // Element (token r, feature c) of a parked tile: the column pass reads 16 features of four
@@ -329,19 +329,19 @@ constexpr int DLW = DF + 8;           // parked row stride (bf16): 144 bytes, 16
 // so the XOR moves the four runs to four different 32-byte windows.
 __device__ __forceinline__ int dtile_off(int r, int c) { return r * DLW + (c ^ (((r >> 4) & 3) << 4)); }
 
-// Column-wise MXFP8 cast of a parked [128 tokens][64 features] tile whose features are
-// kf0 .. kf0 + 63 of a K-feature tensor (token panels, as in col_cast_half).  Task
-// u = 256 k + tid (k = 0, 1) -> feature c = tid / 4, token half k, 16-token part p = tid % 4.
+// Column-wise MXFP8 cast of a parked [64 tokens][64 features] half tile whose features are
+// kf0 .. kf0 + 63 of a K-feature tensor (token panels, as in col_cast_half): thread -> feature
+// c = tid / 4, 16-token part p = tid % 4, so the tile is one panel row per feature; the half
+// tile owns bytes 2 h, 2 h + 1 of each feature's 128-token MFMA scale word.
 __device__ __forceinline__ void col_cast_tile64(const uint16_t* tile, const TileInfo& ti, int64_t K, int64_t kf0,
                                                 const SplitTables& T, const MxOut& o, int tid) {
   const int p = tid & 3;
   const int c = tid >> 2;
   const int P = (ti.m + 127) & ~127;
   const int64_t colbase = K * (int64_t)T.col_off[ti.g];
-  uint32_t word = 0;                               // the 128-token MFMA scale word of feature c
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int tok0 = 64 * half + 16 * p;
+  const int h = (ti.t0 / MQT) & 1;
+  {
+    const int tok0 = 16 * p;
     float v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = bf16_to_f32(tile[dtile_off(tok0 + i, c)]);
@@ -354,43 +354,44 @@ __device__ __forceinline__ void col_cast_tile64(const uint16_t* tile, const Tile
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = cvt_e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
-    // a valid tile starts below m <= P and P is a multiple of 128: all its tokens are inside P
+    // a half tile lies inside the group's padded range P (a multiple of 128)
     __builtin_nontemporal_store(v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
-                                reinterpret_cast<v4i*>(o.col_data + colbase + (((ti.t0 / 64) + half) * K + kf0 + c) * 64 + 16 * p));
+                                reinterpret_cast<v4i*>(o.col_data + colbase + ((ti.t0 / 64) * K + kf0 + c) * 64 + 16 * p));
     if (o.col_scale && (p & 1) == 0)
-      o.col_scale[colbase / 32 + (kf0 + c) * (P / 32) + ti.t0 / 32 + 2 * half + (p >> 1)] = (uint8_t)code;
-    word |= code << (8 * (2 * half + (p >> 1)));
+      o.col_scale[colbase / 32 + (kf0 + c) * (P / 32) + ti.t0 / 32 + (p >> 1)] = (uint8_t)code;
+    const uint32_t pair = (code << (8 * (p >> 1))) | ((uint32_t)__shfl_xor((int)code, 2, 64) << (8 * (1 - (p >> 1))));
+    if (o.col_scale_mfma && p == 0)
+      reinterpret_cast<uint16_t*>(o.col_scale_mfma)[2 * (K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K +
+                                                          kf0 + c) + h] = (uint16_t)pair;
   }
-  word |= (uint32_t)__shfl_xor((int)word, 2, 64);
-  if (o.col_scale_mfma && p == 0)
-    o.col_scale_mfma[K * (int64_t)T.colw_off[ti.g] + (int64_t)(ti.t0 / 128) * K + kf0 + c] = word;
 }
 
 template <bool SWIGLU, bool WANT_A>
-__global__ __launch_bounds__(256, (SWIGLU && WANT_A) ? 2 : 4) void dact_quant_kernel(DactArgs D, SplitTables T, int G,
-                                                                                    int64_t M) {
+__global__ __launch_bounds__(256) void dact_quant_kernel(DactArgs D, SplitTables T, int G, int64_t M) {
   constexpr int NT = 1 + (SWIGLU ? 1 : 0) + (WANT_A ? 1 : 0);   // parked tiles: dgate (dh), dup, a
-  __shared__ __align__(16) uint16_t tiles[NT][QT * DLW];
+  __shared__ __align__(16) uint16_t tiles[NT][MQT * DLW];
   const int64_t ffn = D.ffn;
   const int64_t F1 = SWIGLU ? 2 * ffn : ffn;
+  // 64-token half tiles (as the MXFP8 cast); a half past the group's rows still writes its
+  // column-wise padding
   TileInfo ti;
   {
-    const int tt = blockIdx.y;
+    const int tt = blockIdx.y >> 1;
     if (G <= 0 || tt >= T.t128_off[G]) return;
     ti.g = find_group(T.t128_off, G, tt);
     ti.gstart = T.row_off[ti.g];
     ti.m = T.row_off[ti.g + 1] - (int)ti.gstart;
-    ti.t0 = (tt - T.t128_off[ti.g]) * QT;
-    ti.rows = min(QT, ti.m - ti.t0);
+    ti.t0 = (tt - T.t128_off[ti.g]) * QT + MQT * (int)(blockIdx.y & 1);
+    ti.rows = max(0, min(MQT, ti.m - ti.t0));
     ti.k0 = (int64_t)blockIdx.x * DF;
     ti.kcols = DF;                                 // ffn is a multiple of 128
-    if (ti.rows <= 0) return;
+    if (ti.m <= 0) return;
   }
   const int tid = threadIdx.x;
   const int rl = tid >> 3, g = tid & 7;
-  uint4 qd[4], qg[4], qu[4];
+  uint4 qd[2], qg[2], qu[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int r = 32 * j + rl;
     const bool ok = r < ti.rows;
     const int64_t row = ti.gstart + ti.t0 + r;
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(256, (SWIGLU && WANT_A) ? 2 : 4) void dact_quant_ke
                            : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int r = 32 * j + rl;
     const bool ok = r < ti.rows;
     const int64_t grow = ti.gstart + ti.t0 + (ok ? r : 0);
@@ -772,7 +773,7 @@ hipError_t launch_mxfp8_quant(const uint16_t* x, int64_t M, int64_t K, SplitTabl
 
 hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const dim3 grid((unsigned)(d.ffn / DF), (unsigned)((M + QT - 1) / QT + G));
+  const dim3 grid((unsigned)(d.ffn / DF), (unsigned)(2 * ((M + QT - 1) / QT + G)));   // half tiles
   const bool a = d.a2.col_data != nullptr;
   if (d.act == 0 && !a) hipLaunchKernelGGL((dact_quant_kernel<true, false>), grid, dim3(256), 0, s, d, T, G, M);
   else if (d.act == 0) hipLaunchKernelGGL((dact_quant_kernel<true, true>), grid, dim3(256), 0, s, d, T, G, M);
