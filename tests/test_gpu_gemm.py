@@ -14,7 +14,10 @@ from workloads import random_bf16
 pytestmark = pytest.mark.gpu
 
 FPROP_CASES = [([0, 37, 300, 129], 256, 384), ([512], 128, 256), ([1, 0, 700], 384, 128), ([257, 3], 640, 512)]
-WGRAD_CASES = [([0, 37, 300, 129], 256, 384), ([5, 0, 600], 128, 256), ([128, 256], 384, 128)]
+WGRAD_CASES = [([0, 37, 300, 129], 256, 384), ([5, 0, 600], 128, 256), ([128, 256], 384, 128),
+               # skewed experts: the XCD tile ranges are cut by work (one big expert, empty and
+               # one-row experts; with 14 tiles some XCDs get none)
+               ([3000, 1, 0, 40], 256, 128), ([2500, 3, 0, 7, 90, 0, 1], 384, 256)]
 
 
 def _fprop_ref(x, w, splits, kind, mask):

@@ -105,6 +105,24 @@ def test_nvfp4_hadamard_amax(splits, K, dist):
     assert_bytes_equal(f32bits(post), rpost.view(np.uint32), "post-RHT amax")
 
 
+def test_nvfp4_hadamard_amax_many_groups():
+    """300 groups (many empty or tiny): the per-group slots span several finalize blocks, and two
+    passes in a row start from cleared slots."""
+    rng = np.random.default_rng(5)
+    splits = [int(v) for v in rng.choice([0, 0, 1, 3, 17, 40, 130], size=300)]
+    M, K, mask = sum(splits), 128, 0x5A5A
+    print(f"nvfp4 amax, {len(splits)} groups, M={M}", flush=True)
+    x = random_bf16((M, K), seed=77, dist="normal")
+    rpre, rpost = R.group_hadamard_amax(x, splits, mask)
+    dx, ds = dev_bf16(x), dev_splits(splits)
+    ws = g.quant_workspace(len(splits), "cuda")
+    for _ in range(2):
+        pre, post = g.group_hadamard_amax(dx, ds, mask, ws=ws)
+        torch.cuda.synchronize()
+        assert_bytes_equal(f32bits(pre), rpre.view(np.uint32), "pre-RHT amax")
+        assert_bytes_equal(f32bits(post), rpost.view(np.uint32), "post-RHT amax")
+
+
 @pytest.mark.parametrize("splits,K,dist", CASES)
 def test_nvfp4_group_quantize(splits, K, dist):
     """Amax pass + cast (row-wise with the pre-RHT amax, column-wise RHT with the post-RHT amax)."""
