@@ -296,7 +296,7 @@ FwdWs carve_fwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, c
   FwdWs w;
   w.T = carve_tables(b, E);
   w.xq_row = carve_q(b, r, M, H, E, true, false, false);
-  w.a = b.take<uint16_t>(M * ffn);
+  w.a = is_mx(r) ? nullptr : b.take<uint16_t>(M * ffn);       // NVFP4: the bf16 fc2 input
   w.aq_row = carve_q(b, r, M, ffn, E, true, false, false);
   // fc1: x [M, H] and W1 [E, F1, H]; fc2: a [M, ffn] and W2 [E, H, ffn]
   w.nv = carve_nv(b, r, M * std::max(H, ffn), (int64_t)E * H * std::max(F1, ffn));
@@ -602,8 +602,20 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     g_counts[CNT_NVQ]++;
     x_pre = pre;
   }
-  // 2. fc1 grouped GEMM + activation * prob epilogue: h (saved) and the bf16 fc2 input
-  {
+  // 2. fc1 grouped GEMM.  MXFP8: it stores h (saved) and one pass forms the fc2 input from h and
+  // casts it (step 3).  NVFP4: its activation * prob epilogue also writes the bf16 fc2 input,
+  // which the amax pass and the cast read.
+  if (mx) {
+    GemmArgs g = gemm_base(MODE_FPROP, r, EPI_STORE, W.T, E);
+    g.M = M;
+    g.N = A->activation == GMLP_SWIGLU ? 2 * ffn : ffn;
+    g.K = H;
+    g.a = op_row(W.xq_row.q, x_pre);
+    g.b = op_row(*A->w1, A->w1->amax_pre);
+    g.c = C.h;
+    if (!L.check(launch_gemm(g, stream), "fc1 gemm")) return L.st;
+    g_counts[CNT_GEMM]++;
+  } else {
     GemmArgs g = gemm_base(MODE_FPROP, r, EPI_FC1, W.T, E);
     g.M = M;
     g.N = A->activation == GMLP_SWIGLU ? 2 * ffn : ffn;
@@ -626,7 +638,8 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     MxOut o{static_cast<uint8_t*>(W.aq_row.q.row_data), nullptr, static_cast<uint32_t*>(W.aq_row.q.row_scale_mfma),
             a_col ? static_cast<uint8_t*>(C.aq_col.q.col_data) : nullptr, nullptr,
             a_col ? static_cast<uint32_t*>(C.aq_col.q.col_scale_mfma) : nullptr};
-    if (!L.check(launch_mxfp8_quant(W.a, M, ffn, W.T, E, true, a_col, o, stream), "mxfp8 quantize fc2 input")) return L.st;
+    if (!L.check(launch_act_quant(C.h, A->probs, A->activation, ffn, W.T, E, M, o, stream), "fc2 input cast"))
+      return L.st;
     g_counts[CNT_MXQ]++;
   } else {
     if (!L.check(launch_hadamard_amax(W.a, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, C.a_pre, C.a_post, stream),

@@ -1174,7 +1174,6 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   GMLP_DISPATCH_MX(MODE_FPROP, EPI_STORE)
   GMLP_DISPATCH_MX(MODE_FPROP, EPI_STORE32)
   GMLP_DISPATCH_MX(MODE_WGRAD, EPI_STORE32)
-  GMLP_DISPATCH_MX(MODE_FPROP, EPI_FC1)
   GMLP_DISPATCH_MX(MODE_WGRAD, EPI_STORE)
 #undef GMLP_DISPATCH_MX
   return hipErrorInvalidValue;

@@ -60,6 +60,10 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 hipError_t launch_mxfp8_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
                               bool row, bool col, MxOut o, hipStream_t s);
 hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M, hipStream_t s);
+// MXFP8 forward: the fc2 input a = bf16(act(h) p) from the fc1 output h [M, F1], cast row-wise
+// (and column-wise when o.col_data is set) without writing a.
+hipError_t launch_act_quant(const uint16_t* h, const float* probs, int act, int64_t ffn, SplitTables T, int G,
+                            int64_t M, MxOut o, hipStream_t s);
 hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
                                 uint32_t mask, float* pre, float* post, hipStream_t s);
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,

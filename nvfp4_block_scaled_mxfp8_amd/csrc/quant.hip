@@ -479,6 +479,83 @@ __global__ __launch_bounds__(256) void dact_quant_kernel(DactArgs D, SplitTables
   if (WANT_A) col_cast_tile64(tiles[NT - 1], ti, ffn, ti.k0, T, D.a2, tid);
 }
 
+// ----------------------------------------------------------------------------- activation + MXFP8 cast (forward)
+// The MXFP8 forward's fc2 input: from h = fc1 output (bf16 [M, F1]) and the routing
+// probabilities, a = bf16(act(h) p) (the same function as the backward's rebuild, so the bits
+// match) is cast row-wise for the fc2 GEMM and, when o.col_data is set, column-wise for the fc2
+// wgrad; a itself is never written.  Half tiles and thread layout as in dact_quant_kernel:
+// 64 tokens x 64 features of a (SwiGLU: gate feature f and up feature ffn + f of h).
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ h, const float* __restrict__ probs,
+                                                        int64_t ffn, SplitTables T, int G, int64_t M, MxOut o) {
+  __shared__ __align__(16) uint16_t tile[MQT * DLW];
+  const int64_t F1 = SWIGLU ? 2 * ffn : ffn;
+  TileInfo ti;
+  {
+    const int tt = blockIdx.y >> 1;
+    if (G <= 0 || tt >= T.t128_off[G]) return;
+    ti.g = find_group(T.t128_off, G, tt);
+    ti.gstart = T.row_off[ti.g];
+    ti.m = T.row_off[ti.g + 1] - (int)ti.gstart;
+    ti.t0 = (tt - T.t128_off[ti.g]) * QT + MQT * (int)(blockIdx.y & 1);
+    ti.rows = max(0, min(MQT, ti.m - ti.t0));
+    ti.k0 = (int64_t)blockIdx.x * DF;
+    ti.kcols = DF;                                 // ffn is a multiple of 128
+    if (ti.m <= 0) return;
+  }
+  const int tid = threadIdx.x;
+  const int rl = tid >> 3, g = tid & 7;
+  uint4 qg[2], qu[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 32 * j + rl;
+    const bool ok = r < ti.rows;
+    const int64_t row = ti.gstart + ti.t0 + r;
+    qg[j] = ok ? *reinterpret_cast<const uint4*>(h + row * F1 + ti.k0 + 8 * g) : make_uint4(0, 0, 0, 0);
+    qu[j] = (SWIGLU && ok) ? *reinterpret_cast<const uint4*>(h + row * F1 + ffn + ti.k0 + 8 * g) : make_uint4(0, 0, 0, 0);
+  }
+  const int64_t f = ti.k0 + 8 * g;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 32 * j + rl;
+    const bool ok = r < ti.rows;
+    const int64_t grow = ti.gstart + ti.t0 + (ok ? r : 0);
+    const float p = ok ? probs[grow] : 0.0f;
+    float vg[8], vu[8], v[8];
+    unpack8(qg[j], vg);
+    unpack8(qu[j], vu);
+    uint32_t pa[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = act_out(SWIGLU ? 0 : 1, vg[i], SWIGLU ? vu[i] : 0.0f, p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pa[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
+    // row-wise cast: a 32-feature block is a lane quad; the tile's two blocks are bytes b, b + 1
+    // of the row's 128-feature MFMA word
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const uint32_t code = e8m0_code(amax);
+    const float inv = e8m0_inv_scale(code);
+    const uint32_t w0 = cvt_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    const uint32_t w1 = cvt_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    const uint32_t pair = code | ((uint32_t)__shfl_xor((int)code, 4, 64) << 8);
+    if (ok) {
+      __builtin_nontemporal_store((uint64_t)w0 | ((uint64_t)w1 << 32),
+                                  reinterpret_cast<uint64_t*>(o.row_data + (f / 64) * 64 * M + grow * 64 + (f & 63)));
+      if (o.row_scale && (g & 3) == 0) o.row_scale[grow * (ffn / 32) + f / 32] = (uint8_t)code;
+      if (o.row_scale_mfma && g == 0)
+        *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(o.row_scale_mfma) + ((f / 128) * M + grow) * 4 +
+                                     (f & 127) / 32) = (uint16_t)pair;
+    }
+    *reinterpret_cast<uint4*>(tile + dtile_off(r, 8 * g)) = make_uint4(pa[0], pa[1], pa[2], pa[3]);
+  }
+  if (!o.col_data) return;
+  __syncthreads();
+  col_cast_tile64(tile, ti, ffn, ti.k0, T, o, tid);
+}
+
 // ----------------------------------------------------------------------------- signed Hadamard
 // y = H16 (s * x) with H16[i][j] = (-1)^popcount(i & j): the fp32 butterfly over strides
 // 1, 2, 4, 8 (each stage maps (v[i], v[i+h]) -> (v[i] + v[i+h], v[i] - v[i+h])); the caller
@@ -779,6 +856,15 @@ hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M,
   else if (d.act == 0) hipLaunchKernelGGL((dact_quant_kernel<true, true>), grid, dim3(256), 0, s, d, T, G, M);
   else if (!a) hipLaunchKernelGGL((dact_quant_kernel<false, false>), grid, dim3(256), 0, s, d, T, G, M);
   else hipLaunchKernelGGL((dact_quant_kernel<false, true>), grid, dim3(256), 0, s, d, T, G, M);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant(const uint16_t* h, const float* probs, int act, int64_t ffn, SplitTables T, int G,
+                            int64_t M, MxOut o, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid((unsigned)(ffn / DF), (unsigned)(2 * ((M + QT - 1) / QT + G)));   // half tiles
+  if (act == 0) hipLaunchKernelGGL((act_quant_kernel<true>), grid, dim3(256), 0, s, h, probs, ffn, T, G, M, o);
+  else hipLaunchKernelGGL((act_quant_kernel<false>), grid, dim3(256), 0, s, h, probs, ffn, T, G, M, o);
   return hipGetLastError();
 }
 
