@@ -144,8 +144,9 @@ gmlp_status check_dims(int64_t M, int64_t K, int G) {
   if (M < 0) return fail(GMLP_INVALID_ARG, "dims: M must be >= 0, got %lld", (long long)M);
   if (K <= 0 || K % 32 != 0) return fail(GMLP_UNSUPPORTED, "dims: K must be a positive multiple of 32, got %lld", (long long)K);
   if (M + 127LL * G > (1LL << 30)) return fail(GMLP_UNSUPPORTED, "dims: M = %lld rows is too large", (long long)M);
-  // one launch covers every 128-row tile of every group along the grid's y dimension
-  if ((M + 127) / 128 + G > 65535)
+  // one launch covers both 64-row halves of every 128-row tile of every group along the grid's
+  // y dimension (at most 65535)
+  if (2 * ((M + 127) / 128 + G) > 65535)
     return fail(GMLP_UNSUPPORTED, "dims: M = %lld rows in %d groups exceeds one launch's tile range", (long long)M, G);
   return GMLP_OK;
 }
@@ -344,6 +345,9 @@ gmlp_status mlp_common_checks(int64_t M, int E, int64_t H, int64_t ffn, int act,
   if ((st = check_dims(M, H, E)) != GMLP_OK) return st;
   if (ffn <= 0 || ffn % 128 != 0) return fail(GMLP_UNSUPPORTED, "dims: ffn must be a positive multiple of 128, got %lld", (long long)ffn);
   if (H % 128 != 0) return fail(GMLP_UNSUPPORTED, "dims: hidden must be a multiple of 128, got %lld", (long long)H);
+  // the NVFP4 activation-gradient pass covers 8 rows per workgroup along the grid's y dimension
+  if (!is_mx(r) && (M + 7) / 8 > 65535)
+    return fail(GMLP_UNSUPPORTED, "dims: M = %lld rows exceeds one launch's row range", (long long)M);
   // the GEMMs address every quantized operand with 32-bit offsets
   const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
   const int64_t eb = is_mx(r) ? 1 : 2;             // NVFP4 operands run expanded to bf16
@@ -527,6 +531,10 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
     if (is_mx(recipe) ? (!oa.data || !ob.data || !oa.scale_mfma || !ob.scale_mfma)
                       : (!nv_a || !nv_b || !oa.amax || !ob.amax))
       return fail(GMLP_INVALID_ARG, "operand data, scales%s missing", is_mx(recipe) ? "" : " or amax");
+    // a packed NVFP4 row-wise operand is expanded 16 rows per workgroup along the grid's y dimension
+    if (!is_mx(recipe) && fp && !oa.bf16 && (M + 15) / 16 > 65535)
+      return fail(GMLP_UNSUPPORTED, "dims: a packed NVFP4 operand of %lld rows exceeds one expansion launch",
+                  (long long)M);
   }
   Bump bb(ws);
   SplitTables T = carve_tables(bb, G);

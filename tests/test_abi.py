@@ -97,3 +97,18 @@ def test_nvfp4_gemm_operand_validation():
     st = L.gmlp_grouped_gemm(0, g.recipe("nvfp4", 1), ctypes.byref(q), ctypes.byref(q), ctypes.c_void_p(16), 1, 64,
                              128, 128, ctypes.c_void_p(16), 0, None, 0, None)
     assert st == 1 and "amax" in g.last_error()
+
+
+def test_launch_range_limits_are_reported():
+    """Inputs too large for one launch's grid are rejected on the host with a dims reason."""
+    L = g.lib()
+    q = g.GroupedQ()
+    # 2 x (M / 128 + G) half tiles must fit the grid's y dimension
+    st = L.gmlp_group_quantize(None, 128 * 33000, 128, None, 1, g.recipe("mxfp8"), 1, 1, ctypes.byref(q), None, 0,
+                               None)
+    assert st == 2 and "tile range" in g.last_error()
+    args = g.FwdArgs()
+    args.E, args.M, args.H, args.ffn = 8, 600000, 128, 128
+    args.recipe = g.recipe("nvfp4", 1)
+    assert L.gmlp_grouped_mlp_forward(ctypes.byref(args), None) == 2
+    assert "row range" in g.last_error()
