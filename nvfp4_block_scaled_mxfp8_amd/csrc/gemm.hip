@@ -1,4 +1,6 @@
-// Grouped GEMMs of the MoE MLP on CDNA4 matrix cores, with the fused fc1 and fc2-dgrad epilogues.
+// Grouped GEMMs of the MoE MLP on CDNA4 matrix cores: bf16 / fp32 store epilogues and, for NVFP4,
+// the fc1 epilogue that also writes the activation (the MXFP8 activation and every activation
+// gradient run as memory-bound passes of their own, see quant.hip).
 //
 // Sources: "GEMM + Swiglu fused Grouped MLP for MXFP8" (sequence diagram: the FC1
 // GLU kernel writes the bf16 pre-activation and the activation; the FC2 dGLU
