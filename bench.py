@@ -1,13 +1,14 @@
-"""Throughput of the fused MoE grouped MLP (MXFP8, SwiGLU) on one MI355X.
+"""Throughput of the fused MoE grouped MLP on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config mid] [--cpu-sample-rows R]
+    python bench.py [--steps K] [--warmup W] [--config mid|nvfp4|zipf|large] [--cpu-sample-rows R]
 
-One step = one forward + backward of the whole path (x and dy group quantize,
-fc1 GEMM + SwiGLU*prob, fc2-input quantize, fc2 GEMM, fc2 dgrad + dSwiGLU +
-dprob, dh quantize, fc2 wgrad, fc1 dgrad, fc1 wgrad) over the synthetic
-workload: 8 experts, hidden 4096, ffn 1536, 16384 tokens routed top-2 = 32768
-rows split by a uniform multinomial.  Inputs are resident in HBM before timing;
-weights are quantized once, outside the timed steps.
+One step = one forward + backward of the whole path (x group quantize, fc1 GEMM,
+SwiGLU * prob with the fc2-input cast, fc2 GEMM, dy group quantize, fc2 dgrad,
+activation gradient + dprob + dh casts, fc2 wgrad, fc1 dgrad, fc1 wgrad) over a
+synthetic workload; the default (mid) is 8 experts, hidden 4096, ffn 1536, 16384
+tokens routed top-2 = 32768 rows split by a uniform multinomial, MXFP8 SwiGLU.
+Inputs are resident in HBM before timing; weights are quantized once, outside
+the timed steps.
 
 Prints one JSON line: TFLOP/s of the step (6 M H (F1 + ffn) flops), the
 roofline of the dominant kernel (the fc1-dgrad-shaped grouped GEMM, timed live
