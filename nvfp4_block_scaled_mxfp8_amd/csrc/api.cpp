@@ -288,7 +288,6 @@ void set_nv(GemmArgs& g, const NvScratch& n) {
 struct FwdWs {
   SplitTables T;
   QBuf xq_row;
-  uint16_t* a;
   QBuf aq_row;
   NvScratch nv;
 };
@@ -297,7 +296,6 @@ FwdWs carve_fwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, c
   FwdWs w;
   w.T = carve_tables(b, E);
   w.xq_row = carve_q(b, r, M, H, E, true, false, false);
-  w.a = is_mx(r) ? nullptr : b.take<uint16_t>(M * ffn);       // NVFP4: the bf16 fc2 input
   w.aq_row = carve_q(b, r, M, ffn, E, true, false, false);
   // fc1: x [M, H] and W1 [E, F1, H]; fc2: a [M, ffn] and W2 [E, H, ffn]
   w.nv = carve_nv(b, r, M * std::max(H, ffn), (int64_t)E * H * std::max(F1, ffn));
@@ -610,10 +608,10 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     g_counts[CNT_NVQ]++;
     x_pre = pre;
   }
-  // 2. fc1 grouped GEMM.  MXFP8: it stores h (saved) and one pass forms the fc2 input from h and
-  // casts it (step 3).  NVFP4: its activation * prob epilogue also writes the bf16 fc2 input,
-  // which the amax pass and the cast read.
-  if (mx) {
+  // 2. fc1 grouped GEMM: it stores h (saved); the fc2 input a = bf16(act(h) p) is formed from h by
+  // the pass that casts it (MXFP8) or by the amax pass and the cast that read it (NVFP4), so a
+  // itself is never written.
+  {
     GemmArgs g = gemm_base(MODE_FPROP, r, EPI_STORE, W.T, E);
     g.M = M;
     g.N = A->activation == GMLP_SWIGLU ? 2 * ffn : ffn;
@@ -621,20 +619,6 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     g.a = op_row(W.xq_row.q, x_pre);
     g.b = op_row(*A->w1, A->w1->amax_pre);
     g.c = C.h;
-    if (!L.check(launch_gemm(g, stream), "fc1 gemm")) return L.st;
-    g_counts[CNT_GEMM]++;
-  } else {
-    GemmArgs g = gemm_base(MODE_FPROP, r, EPI_FC1, W.T, E);
-    g.M = M;
-    g.N = A->activation == GMLP_SWIGLU ? 2 * ffn : ffn;
-    g.K = H;
-    g.a = op_row(W.xq_row.q, x_pre);
-    g.b = op_row(*A->w1, A->w1->amax_pre);
-    g.act = A->activation;
-    g.ffn = ffn;
-    g.probs = A->probs;
-    g.h = C.h;
-    g.a_out = W.a;
     set_nv(g, W.nv);
     if (!L.check(launch_gemm(g, stream), "fc1 gemm")) return L.st;
     g_counts[CNT_GEMM]++;
@@ -650,14 +634,19 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
       return L.st;
     g_counts[CNT_MXQ]++;
   } else {
-    if (!L.check(launch_hadamard_amax(W.a, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, C.a_pre, C.a_post, stream),
+    ActSrc src;
+    src.h = C.h;
+    src.probs = A->probs;
+    src.act = A->activation;
+    src.ffn = ffn;
+    if (!L.check(launch_hadamard_amax(C.h, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, C.a_pre, C.a_post, stream, src),
                  "amax fc2 input"))
       return L.st;
     g_counts[CNT_HAMAX]++;
     NvOut o = nv_out(W.aq_row.q, true, false);
     o.col_bf16 = a_col ? static_cast<uint8_t*>(C.aq_col.q.col_bf16) : nullptr;
-    if (!L.check(launch_nvfp4_quant(W.a, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, true, true, a_col, C.a_pre,
-                                    C.a_post, o, stream), "nvfp4 quantize fc2 input"))
+    if (!L.check(launch_nvfp4_quant(C.h, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, true, true, a_col, C.a_pre,
+                                    C.a_post, o, stream, src), "nvfp4 quantize fc2 input"))
       return L.st;
     g_counts[CNT_NVQ]++;
     a_pre = C.a_pre;

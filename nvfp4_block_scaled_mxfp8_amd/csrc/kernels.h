@@ -64,11 +64,20 @@ hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M,
 // (and column-wise when o.col_data is set) without writing a.
 hipError_t launch_act_quant(const uint16_t* h, const float* probs, int act, int64_t ffn, SplitTables T, int G,
                             int64_t M, MxOut o, hipStream_t s);
+// The input of an NVFP4 amax pass or cast: x itself (h == nullptr) or the fc2 input
+// a = bf16(act(h) p) [M, ffn], formed on the fly from the fc1 output h [M, F1] (F1 = 2 ffn for
+// SwiGLU: gate | up) with the same function as the backward's rebuild.
+struct ActSrc {
+  const uint16_t* h = nullptr;
+  const float* probs = nullptr;
+  int act = 0;          // 0 SwiGLU, 1 squared ReLU
+  int64_t ffn = 0;
+};
 hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
-                                uint32_t mask, float* pre, float* post, hipStream_t s);
+                                uint32_t mask, float* pre, float* post, hipStream_t s, ActSrc act = ActSrc());
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
                               uint32_t mask, bool rht, bool row, bool col, const float* pre,
-                              const float* post, NvOut o, hipStream_t s);
+                              const float* post, NvOut o, hipStream_t s, ActSrc act = ActSrc());
 // Per-expert amax of stacked weights [E, N, K] (one group per expert, no transform).
 hipError_t launch_weight_amax(const uint16_t* w, const void* const* w_ptrs, int E, int64_t N,
                               int64_t K, float* amax, hipStream_t s);

@@ -129,19 +129,44 @@ __device__ __forceinline__ bool tile_info(const SplitTables& T, int G, int64_t K
   return ti.rows > 0;
 }
 
+__device__ __forceinline__ void unpack8(const uint4& q, float* v);
+
+// 8 bf16 of row `row`, features k .. k + 7, of an NVFP4 pass's input: x itself, or the fc2
+// input a = bf16(act(h) p) formed from the fc1 output (the same function as every other
+// producer of a, so the bits agree).
+__device__ __forceinline__ uint4 load_in8(const uint16_t* __restrict__ x, int64_t K, const ActSrc& A, int64_t row,
+                                          int64_t k) {
+  if (!A.h) return *reinterpret_cast<const uint4*>(x + row * K + k);
+  const int64_t F1 = A.act == 0 ? 2 * A.ffn : A.ffn;
+  const uint4 gq = *reinterpret_cast<const uint4*>(A.h + row * F1 + k);
+  const uint4 uq = A.act == 0 ? *reinterpret_cast<const uint4*>(A.h + row * F1 + A.ffn + k) : make_uint4(0, 0, 0, 0);
+  const float p = A.probs[row];
+  float g[8], u[8];
+  unpack8(gq, g);
+  unpack8(uq, u);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = act_out(A.act, g[2 * i], u[2 * i], p);
+    const float hi = act_out(A.act, g[2 * i + 1], u[2 * i + 1], p);
+    w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Load i of a thread covers tile row r = 32 wave + 4 i + lane / 16 and features 8 (lane % 16)
 // .. + 7, so that every load instruction reads four whole 256-byte row segments.  Values
 // outside the tile's valid rows / features are zero; with lds set they are also parked in the
 // unswizzled LDS tile [QT][LDW].
 __device__ __forceinline__ int chunk_row(int tid, int i) { return 32 * (tid >> 6) + 4 * i + ((tid & 63) >> 4); }
 __device__ __forceinline__ void load_row_chunk(const uint16_t* __restrict__ x, int64_t K, const TileInfo& ti,
-                                               int tid, uint4 (&q)[8], uint16_t* lds) {
+                                               int tid, uint4 (&q)[8], uint16_t* lds, const ActSrc& A = ActSrc()) {
   const int kc = 8 * (tid & 15);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = chunk_row(tid, i);
     const bool ok = (r < ti.rows) && (kc < ti.kcols);
-    q[i] = ok ? *reinterpret_cast<const uint4*>(x + (ti.gstart + ti.t0 + r) * K + ti.k0 + kc) : make_uint4(0, 0, 0, 0);
+    q[i] = ok ? load_in8(x, K, A, ti.gstart + ti.t0 + r, ti.k0 + kc) : make_uint4(0, 0, 0, 0);
   }
   if (lds) {
 #pragma unroll
@@ -576,14 +601,14 @@ __device__ __forceinline__ void signed_fwht16(float* v, uint32_t mask) {
 }
 
 __global__ __launch_bounds__(256) void hadamard_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                            SplitTables T, int G, uint32_t mask) {
+                                                            SplitTables T, int G, uint32_t mask, ActSrc A) {
   __shared__ __align__(16) uint16_t tile[QT * LDW];
   __shared__ float red[2][4];
   TileInfo ti;
   if (!tile_info(T, G, K, ti)) return;
   const int tid = threadIdx.x;
   uint4 q[8];
-  load_row_chunk(x, K, ti, tid, q, tile);
+  load_row_chunk(x, K, ti, tid, q, tile, A);
   float amax_pre = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -712,7 +737,7 @@ template <bool ROW, bool COL>
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                           SplitTables T, int G, uint32_t mask, int rht,
                                                           const float* __restrict__ pre,
-                                                          const float* __restrict__ post, NvOut o) {
+                                                          const float* __restrict__ post, NvOut o, ActSrc A) {
   // 64-token half tiles, as the MXFP8 cast: load i of a thread covers half-tile row
   // 16 wave + 4 i + lane / 16, features 8 (lane % 16) .. + 7
   __shared__ __align__(16) uint16_t tile[COL ? MQT * LDW : 8];
@@ -728,7 +753,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __rest
     for (int i = 0; i < 4; ++i) {
       const int r = hrow(i);
       const bool ok = (r < ti.rows) && (kc < ti.kcols);
-      q[i] = ok ? *reinterpret_cast<const uint4*>(x + (ti.gstart + ti.t0 + r) * K + ti.k0 + kc) : make_uint4(0, 0, 0, 0);
+      q[i] = ok ? load_in8(x, K, A, ti.gstart + ti.t0 + r, ti.k0 + kc) : make_uint4(0, 0, 0, 0);
     }
     if (COL) {
 #pragma unroll
@@ -869,25 +894,28 @@ hipError_t launch_act_quant(const uint16_t* h, const float* probs, int act, int6
 }
 
 hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G, uint32_t mask,
-                                float* pre, float* post, hipStream_t s) {
+                                float* pre, float* post, hipStream_t s, ActSrc act) {
   // with no rows the finalize still writes the (zero) amax of every group
-  if (M > 0) hipLaunchKernelGGL(hadamard_amax_kernel, tile_grid(M, K, G), dim3(256), 0, s, x, M, K, T, G, mask);
+  if (M > 0) hipLaunchKernelGGL(hadamard_amax_kernel, tile_grid(M, K, G), dim3(256), 0, s, x, M, K, T, G, mask, act);
   hipLaunchKernelGGL(amax_finalize_kernel, dim3((unsigned)((2 * G + 255) / 256)), dim3(256), 0, s, T, G, pre, post);
   return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G, uint32_t mask,
                               bool rht, bool row, bool col, const float* pre, const float* post, NvOut o,
-                              hipStream_t s) {
+                              hipStream_t s, ActSrc act) {
   if (M == 0 || (!row && !col)) return hipSuccess;
   const dim3 grid((unsigned)((K + QF - 1) / QF), (unsigned)(2 * ((M + QT - 1) / QT + G)));   // half tiles
   const int r = rht ? 1 : 0;
   if (row && col)
-    hipLaunchKernelGGL((nvfp4_quant_kernel<true, true>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o);
+    hipLaunchKernelGGL((nvfp4_quant_kernel<true, true>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o,
+                       act);
   else if (row)
-    hipLaunchKernelGGL((nvfp4_quant_kernel<true, false>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o);
+    hipLaunchKernelGGL((nvfp4_quant_kernel<true, false>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o,
+                       act);
   else
-    hipLaunchKernelGGL((nvfp4_quant_kernel<false, true>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o);
+    hipLaunchKernelGGL((nvfp4_quant_kernel<false, true>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o,
+                       act);
   return hipGetLastError();
 }
 
