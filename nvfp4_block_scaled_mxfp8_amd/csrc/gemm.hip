@@ -29,7 +29,6 @@
 // same 64-byte panels and the GEMM runs on V_MFMA_F32_32X32X16_BF16; the per-group global
 // scales multiply the fp32 result.  (The block-scaled MFMA takes E8M0 scales per 32
 // elements; NVFP4's E4M3 scales per 16 cannot be folded into it exactly.)
-#include "activation.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -244,12 +243,11 @@ template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ DmaConst dma_const(const GemmArgs& A, int wave) {
   constexpr int64_t EB = BF ? 2 : 1;
   DmaConst k;
-  const bool swiglu = MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0;
   k.a = A.a.data;
   k.b = A.b.data;
   k.s = (wave & 1) ? A.b.scale_mfma : A.a.scale_mfma;
   if (MODE == MODE_FPROP) {
-    const int64_t brows = swiglu ? 2 * A.ffn : A.N;
+    const int64_t brows = A.N;
     const int64_t kw = (A.K + 127) / 128;
     k.a_ps = (uint32_t)(A.M * 64);
     k.b_ps = (uint32_t)(brows * 64);
@@ -273,21 +271,13 @@ template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ DmaTile dma_tile(const GemmArgs& A, const TileRef& r, int wave) {
   constexpr int64_t EB = BF ? 2 : 1;
   DmaTile t;
-  const bool swiglu = MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0;
   const int64_t nb = (MODE == MODE_FPROP) ? A.N : A.K;
-  int64_t b_first, b_rows;
-  if (swiglu) {
-    const int64_t f = (int64_t)r.nt * 128 + 64 * (wave >> 1);
-    b_first = ((wave & 1) ? A.ffn : 0) + f;
-    b_rows = min((int64_t)64, max((int64_t)0, A.ffn - f));
-  } else {
-    b_first = (int64_t)r.nt * BN + 64 * wave;
-    b_rows = min((int64_t)64, max((int64_t)0, nb - b_first));
-  }
+  const int64_t b_first = (int64_t)r.nt * BN + 64 * wave;
+  const int64_t b_rows = min((int64_t)64, max((int64_t)0, nb - b_first));
   const int64_t a_rows = min(64, max(0, r.arows - 64 * wave));
   int64_t a_base, b_base, a_sw, b_sw;
   if (MODE == MODE_FPROP) {
-    const int64_t brows = swiglu ? 2 * A.ffn : A.N;
+    const int64_t brows = A.N;
     a_base = 0;
     a_sw = 0;
     b_base = EB * (int64_t)r.g * brows * A.K;
@@ -305,10 +295,9 @@ __device__ __forceinline__ DmaTile dma_tile(const GemmArgs& A, const TileRef& r,
     t.s_off = (uint32_t)(a_sw + r.arow0);
     t.s_bytes = (uint32_t)(4 * r.arows);
   } else {
-    const int64_t f0 = (int64_t)r.nt * 128;
     const int64_t n0 = (int64_t)r.nt * BN;
-    t.s_off = (uint32_t)(b_sw + (swiglu ? f0 : n0));
-    t.s_bytes = (uint32_t)(swiglu ? 4 * (2 * A.ffn - f0) : 4 * max((int64_t)0, nb - n0));
+    t.s_off = (uint32_t)(b_sw + n0);
+    t.s_bytes = (uint32_t)(4 * max((int64_t)0, nb - n0));
   }
   if (BF) t.s_bytes = 0;
   t.nk = r.nk;
@@ -493,7 +482,7 @@ __device__ __forceinline__ void mx_phase2p(const MxFrags& f, v16f (&acc)[4][4], 
 template <int MODE, int EPI>
 __device__ __forceinline__ int tiles_n(const GemmArgs& A) {
   if (MODE == MODE_FPROP)
-    return (EPI == EPI_FC1 && A.act == 0) ? (int)((A.ffn + 127) / 128) : (int)((A.N + BN - 1) / BN);
+    return (int)((A.N + BN - 1) / BN);
   return (int)((A.K + BN - 1) / BN);
 }
 
@@ -535,7 +524,7 @@ __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, in
     c.a_base = 0;
     c.a_ld = A.K;
     // B rows per expert; weight scale words are per expert: [E][ceil(K/128)][brows]
-    const int64_t brows = (EPI == EPI_FC1 && A.act == 0) ? 2 * A.ffn : A.N;
+    const int64_t brows = A.N;
     c.b_base = (int64_t)c.g * brows * A.K;
     c.b_ld = A.K;
     c.a_rtot = A.M;
@@ -615,17 +604,6 @@ __device__ __forceinline__ void stage_chunk(const v16f (&acc)[4][4], uint32_t ba
   GMLP_W16(1, TN1)
   lds_writes_done();
 }
-// SwiGLU fc1: the chunk holds all four column tiles of one wave column wn (gate features
-// 64 wn + [0, 64) at staged columns [0, 64), the matching up features at [64, 128)), so that
-// each output row segment of the chunk is 128 contiguous bytes; base = staged (32 wm + 4 j, m)
-template <int TM>
-__device__ __forceinline__ void stage_chunk4(const v16f (&acc)[4][4], uint32_t base) {
-  GMLP_W16(0, 0)
-  GMLP_W16(1, 1)
-  GMLP_W16(2, 2)
-  GMLP_W16(3, 3)
-  lds_writes_done();
-}
 #undef GMLP_W16
 #undef GMLP_W
 
@@ -662,21 +640,16 @@ __device__ __forceinline__ float4 ld_st4(const float* p, float alpha) {
 
 template <int MODE, int EPI, int CH, int BF = 0>
 __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
-                                          int tid, int wm, int wn, int lane, const float (&pr)[16]) {
+                                          int tid, int wm, int wn, int lane) {
   constexpr int TM = CH >> 1, Q = CH & 1;
-  const bool swiglu = (MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0);
   const float* st = reinterpret_cast<const float*>(buf);
   {
     const int m = lane & 31, j = lane >> 5;
     const uint32_t base = (uint32_t)(uintptr_t)buf + (uint32_t)(((32 * wm + 4 * j) * EPC_LD + m) * 4);
-    if (swiglu) {
-      if (wn == Q) stage_chunk4<TM>(acc, base);
-    } else {
-      stage_chunk<TM, 2 * Q, 2 * Q + 1>(acc, base + 256u * (uint32_t)wn);
-    }
+    stage_chunk<TM, 2 * Q, 2 * Q + 1>(acc, base + 256u * (uint32_t)wn);
   }
   __syncthreads();
-  if (EPI == EPI_STORE || EPI == EPI_STORE32) {
+  {
     // lanes [LPR r, LPR r + LPR) store staged row r of each group of RPI rows
     constexpr int ESZ = (EPI == EPI_STORE32) ? 4 : 2;
     constexpr int PER = 16 / ESZ;                 // output elements per 16-byte store
@@ -703,74 +676,6 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
         const float4 v1 = ld_st4<BF>(src + RPI * it * EPC_LD + 4, c.alpha);
         out_store(r, voff, ur * rowb, pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
                   pack_bf16x2(v1.z, v1.w));
-      }
-    }
-  } else {
-    // EPI_FC1: h = bf16(acc) and a = bf16(act(h) p)
-    const int64_t ffn = A.ffn;
-    const int64_t F1 = (A.act == 0) ? 2 * ffn : ffn;
-    const uint32_t hrow = (uint32_t)(F1 * 2), arow = (uint32_t)(ffn * 2);
-    if (A.act == 0) {
-      // staged columns [gate 64 | up 64] hold features f = 128 nt + 64 Q + [0, 64); lanes
-      // [8 r, 8 r + 8) take staged row r + 32 it, 8 features each (one 128-byte row segment)
-      const int64_t f0 = (int64_t)c.nt * 128 + 64 * Q;
-      const __amdgpu_buffer_rsrc_t rh = out_rsrc(A.h + c.arow0 * F1 + f0, (int64_t)c.arows * hrow);
-      const __amdgpu_buffer_rsrc_t ra = out_rsrc(A.a_out + c.arow0 * ffn + f0, (int64_t)c.arows * arow);
-      const int lrow = tid >> 3, g8 = tid & 7;
-      const int sc = 8 * g8;
-      const int fc = 8 * g8;
-      const bool fok = f0 + fc < ffn;
-      const uint32_t vh = fok ? (uint32_t)lrow * hrow + (uint32_t)(2 * fc) : kOutOfRange;
-      const uint32_t va = fok ? (uint32_t)lrow * arow + (uint32_t)(2 * fc) : kOutOfRange;
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int ur = 128 * it + 32 * TM;
-        const float p = pr[4 * TM + it];
-        const float* src = st + (32 * it + lrow) * EPC_LD + sc;
-        float gv[8], uv[8];
-        *reinterpret_cast<float4*>(gv) = ld_st4<BF>(src, c.alpha);
-        *reinterpret_cast<float4*>(gv + 4) = ld_st4<BF>(src + 4, c.alpha);
-        *reinterpret_cast<float4*>(uv) = ld_st4<BF>(src + 64, c.alpha);
-        *reinterpret_cast<float4*>(uv + 4) = ld_st4<BF>(src + 68, c.alpha);
-        uint32_t hg[4], hu[4], ow[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hg[i] = pack_bf16x2(gv[2 * i], gv[2 * i + 1]);
-          hu[i] = pack_bf16x2(uv[2 * i], uv[2 * i + 1]);
-          const float a0 = act_out(0, bf16_to_f32(hg[i] & 0xFFFFu), bf16_to_f32(hu[i] & 0xFFFFu), p);
-          const float a1 = act_out(0, bf16_to_f32(hg[i] >> 16), bf16_to_f32(hu[i] >> 16), p);
-          ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
-        }
-        out_store(rh, vh, (uint32_t)ur * hrow, hg[0], hg[1], hg[2], hg[3]);
-        out_store(rh, vh, (uint32_t)ur * hrow + arow, hu[0], hu[1], hu[2], hu[3]);   // up half: + ffn
-        out_store(ra, va, (uint32_t)ur * arow, ow[0], ow[1], ow[2], ow[3]);
-      }
-    } else {
-      const __amdgpu_buffer_rsrc_t rh = out_rsrc(A.h + c.arow0 * F1 + c.nrow0, (int64_t)c.arows * hrow);
-      const __amdgpu_buffer_rsrc_t ra = out_rsrc(A.a_out + c.arow0 * ffn + c.nrow0, (int64_t)c.arows * arow);
-      const int lrow = tid >> 4, sc = 8 * (tid & 15);
-      const int col = 128 * (sc >> 6) + 64 * Q + (sc & 63);
-      const bool fok = c.nrow0 + col < ffn;
-      const uint32_t vh = fok ? (uint32_t)lrow * hrow + (uint32_t)(2 * col) : kOutOfRange;
-      const uint32_t va = fok ? (uint32_t)lrow * arow + (uint32_t)(2 * col) : kOutOfRange;
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int ur = 128 * (it >> 1) + 32 * TM + 16 * (it & 1);
-        const float p = pr[4 * TM + it];
-        const float* src = st + (16 * it + lrow) * EPC_LD + sc;
-        float hv[8];
-        *reinterpret_cast<float4*>(hv) = ld_st4<BF>(src, c.alpha);
-        *reinterpret_cast<float4*>(hv + 4) = ld_st4<BF>(src + 4, c.alpha);
-        uint32_t hw[4], ow[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hw[i] = pack_bf16x2(hv[2 * i], hv[2 * i + 1]);
-          const float a0 = act_out(1, bf16_to_f32(hw[i] & 0xFFFFu), 0.0f, p);
-          const float a1 = act_out(1, bf16_to_f32(hw[i] >> 16), 0.0f, p);
-          ow[i] = (__float_as_uint(a0) >> 16) | (__float_as_uint(a1) & 0xFFFF0000u);
-        }
-        out_store(rh, vh, (uint32_t)ur * hrow, hw[0], hw[1], hw[2], hw[3]);
-        out_store(ra, va, (uint32_t)ur * arow, ow[0], ow[1], ow[2], ow[3]);
       }
     }
   }
@@ -802,30 +707,14 @@ __device__ __forceinline__ void epi_zero(const GemmArgs& A, const Ctx& c, int ti
 template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ void mx_epilogue(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
                                             int tid, int wm, int wn, int lane) {
-  // fc1: the routing probabilities of the thread's output rows, all fetched up front (entry
-  // 4 TM + it is the row that epi_chunk's iteration it of MFMA tile row TM stores)
-  float pr[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) pr[i] = 0.0f;
-  if (EPI == EPI_FC1) {
-    const bool swiglu = A.act == 0;
-#pragma unroll
-    for (int TM = 0; TM < 4; ++TM)
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        if (swiglu && it >= 2) continue;
-        const int trow = swiglu ? 128 * it + 32 * TM + (tid >> 3) : 128 * (it >> 1) + 32 * TM + 16 * (it & 1) + (tid >> 4);
-        pr[4 * TM + it] = A.probs[c.arow0 + (trow < c.arows ? trow : c.arows - 1)];
-      }
-  }
-  epi_chunk<MODE, EPI, 0, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 1, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 2, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 3, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 4, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 5, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 6, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
-  epi_chunk<MODE, EPI, 7, BF>(A, c, acc, buf, tid, wm, wn, lane, pr);
+  epi_chunk<MODE, EPI, 0, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 1, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 2, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 3, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 4, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 5, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 6, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk<MODE, EPI, 7, BF>(A, c, acc, buf, tid, wm, wn, lane);
 }
 
 template <int MODE, int EPI, int BF = 0>
@@ -908,11 +797,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
 
   const uint32_t lane_off = (uint32_t)(lane >> 2) * 64u + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
   const DmaPlan dpl{nullptr, nullptr, 0, 0, 0, 0, lane_off};
-  uint32_t s_voff = 16u * lane;
-  if ((wave & 1) && MODE == MODE_FPROP && EPI == EPI_FC1 && A.act == 0) {
-    const int band = lane >> 4;
-    s_voff = 4u * (uint32_t)((band & 1) * A.ffn + (band >> 1) * 64 + 4 * (lane & 15));
-  }
+  const uint32_t s_voff = 16u * lane;
   auto slot = [&](uint32_t st) { return smem + (st & (MX_NSTAGE - 1)) * MX_STAGE; };
 
   // DMA window: the current non-empty tile (R0, and its full sources D0) and the next two
@@ -1082,7 +967,6 @@ __global__ __launch_bounds__(64) void dprob_reduce_kernel(const float* __restric
 
 // ----------------------------------------------------------------------------- launchers
 int gemm_fprop_ntiles_n(const GemmArgs& g) {
-  if (g.epi == EPI_FC1 && g.act == 0) return (int)((g.ffn + 127) / 128);
   return (int)((g.N + BN - 1) / BN);
 }
 
@@ -1109,7 +993,7 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   // the DMA sources are 32-bit offsets: every operand (data and scale words) below 4 GB
   {
-    const int64_t brows = (MODE == MODE_FPROP && EPI == EPI_FC1 && g.act == 0) ? 2 * g.ffn : g.N;
+    const int64_t brows = g.N;
     const int64_t rows_bound = g.M + 127LL * g.G;                    // padded tokens of all groups
     const int64_t eb = BF ? 2 : 1;
     const int64_t big = eb * ((MODE == MODE_FPROP) ? std::max(g.M * g.K, (int64_t)g.G * brows * g.K)
@@ -1117,7 +1001,7 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
     if (big >= (1LL << 32)) return hipErrorInvalidValue;
     // epilogue stores address one tile (256 rows) of an output through one buffer resource,
     // with kOutOfRange marking a lane's columns as outside it
-    const int64_t orow_bytes = (EPI == EPI_FC1) ? 4 * g.ffn : (MODE == MODE_FPROP ? g.N : g.K) * 4;
+    const int64_t orow_bytes = (MODE == MODE_FPROP ? g.N : g.K) * 4;
     if (256 * orow_bytes >= (int64_t)kOutOfRange) return hipErrorInvalidValue;
   }
   GemmArgs a = g;
@@ -1156,7 +1040,6 @@ static hipError_t launch_nvfp4(const GemmArgs& g, int epi, hipStream_t s) {
   a.b.scale_mfma = reinterpret_cast<const uint32_t*>(a.b.data);
   if (g.mode == MODE_WGRAD) return epi == EPI_STORE32 ? launch_mx<MODE_WGRAD, EPI_STORE32, 1>(a, s)
                                                       : launch_mx<MODE_WGRAD, EPI_STORE, 1>(a, s);
-  if (epi == EPI_FC1) return launch_mx<MODE_FPROP, EPI_FC1, 1>(a, s);
   if (epi == EPI_STORE32) return launch_mx<MODE_FPROP, EPI_STORE32, 1>(a, s);
   if (epi == EPI_STORE) return launch_mx<MODE_FPROP, EPI_STORE, 1>(a, s);
   if (epi != EPI_DACT) return hipErrorInvalidValue;

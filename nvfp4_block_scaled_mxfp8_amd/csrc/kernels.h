@@ -102,7 +102,8 @@ hipError_t launch_dact_bf16(const uint16_t* da, const uint16_t* h, const float* 
 // the 64-byte panel layout of the MXFP8 operands, with the per-group amax for the global scales.
 enum GemmFmt { FMT_MXFP8 = 0, FMT_NVFP4 = 1, FMT_NVFP4_BF16 = 2 };
 enum GemmMode { MODE_FPROP = 0, MODE_WGRAD = 1 };
-enum GemmEpi { EPI_STORE = 0, EPI_FC1 = 1, EPI_DACT = 2, EPI_STORE32 = 3 };   // STORE32: fp32 output
+// STORE32: fp32 output.  DACT (NVFP4 fc2 dgrad): da is stored, then the activation-gradient pass.
+enum GemmEpi { EPI_STORE = 0, EPI_DACT = 2, EPI_STORE32 = 3 };
 
 struct GemmOperand {
   const uint8_t* data;        // fp8 / packed fp4
@@ -125,10 +126,10 @@ struct GemmArgs {
   int out_fp32;
   // fused epilogue operands
   int act;           // 0 SwiGLU, 1 SReLU
-  int64_t ffn;       // EPI_FC1 / EPI_DACT: ffn (output a width); SwiGLU F1 = 2 ffn
+  int64_t ffn;       // EPI_DACT: ffn (width of da and a'); SwiGLU F1 = 2 ffn
   const float* probs;
-  uint16_t* h;       // EPI_FC1: out h [M, F1]; EPI_DACT: in h
-  uint16_t* a_out;   // EPI_FC1: out a [M, ffn]; EPI_DACT: out a' (recompute) or null
+  uint16_t* h;       // EPI_DACT: in h [M, F1]
+  uint16_t* a_out;   // EPI_DACT: out a' (recompute) or null
   uint16_t* dh;      // EPI_DACT: out dh [M, F1]
   float* dprob_part; // EPI_DACT: [n_tiles, M]
   int group_rows;    // tile rows per launch-order group (see make_ctx); set by launch_gemm
