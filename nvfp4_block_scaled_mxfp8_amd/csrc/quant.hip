@@ -7,9 +7,12 @@
 // post-RHT amax in one pass; nvfp4_group_quantize_with_amax casts from given
 // amax; the RHT carries the quantizer's sign mask).
 //
-// Tiling: one 256-thread workgroup per (128-token tile of one group, 128-feature
-// tile).  Token tiles never straddle groups, so every 32-token (MXFP8) or
-// 16-token (NVFP4) column block starts at a group-relative multiple of its size.
+// Tiling: the split tables count 128-token tiles per group; tiles never straddle
+// groups, so every 32-token (MXFP8) or 16-token (NVFP4) column block starts at a
+// group-relative multiple of its size.  The casts run one 256-thread workgroup per
+// 64-token half of such a tile and 128 features (64 for the activation passes), so
+// 17 KB of LDS keeps eight workgroups per CU in flight; the NVFP4 amax pass keeps
+// whole 128-token tiles, which measured faster for it.
 // Each load instruction of a wave reads four whole 256-byte row segments (16 lanes
 // per row, 8 bf16 each); the values are cast row-wise in registers (a block spans a
 // lane pair or quad) and parked in LDS, from where the column pass reads one feature
