@@ -62,7 +62,13 @@ typedef enum {
 
 typedef enum { GMLP_MXFP8 = 0, GMLP_NVFP4_RHT = 1 } gmlp_recipe_kind;
 typedef enum { GMLP_SWIGLU = 0, GMLP_SRELU = 1 } gmlp_activation;
-typedef enum { GMLP_OUT_BF16 = 0, GMLP_OUT_FP32 = 1 } gmlp_out_dtype;
+/* Output of a GEMM: bf16 or fp32 (round to nearest even), or fp32 added to what the output
+ * buffer holds: C = fp32(C + product), the weight gradient accumulated into a persistent fp32
+ * main_grad [MX, review comments on overwrite_main_grad: the grouped wgrad either overwrites
+ * main_grad or accumulates into it].  Accumulation
+ * is for weight gradients only (WGRAD layout, the backward's dw1 / dw2); an empty expert
+ * leaves its slice unchanged. */
+typedef enum { GMLP_OUT_BF16 = 0, GMLP_OUT_FP32 = 1, GMLP_OUT_FP32_ACCUMULATE = 2 } gmlp_out_dtype;
 
 /* Recipe [FB, Changes]: MXFP8 (E4M3 data for activations and gradients alike),
  * or NVFP4 with the randomized Hadamard transform (NVFP4 without RHT is not
@@ -206,7 +212,9 @@ typedef enum {
  * FPROP: a = row-wise quantized [M, K] tensor, b = weight fprop operand
  *        (b->row_*), n = N, k = K; C [M, N].
  * WGRAD: a, b = column-wise quantized tensors with rows N_a = n, N_b = k;
- *        C [G, n, k]; empty groups write zeros.
+ *        C [G, n, k]; empty groups write zeros (accumulating: leave C_g as it is).
+ * out_dtype: gmlp_out_dtype; an unknown value is INVALID_ARG, accumulation with FPROP
+ * UNSUPPORTED.
  * ws: >= gmlp_grouped_gemm_ws_bytes for the same arguments. */
 /* Workspace bytes of one gmlp_grouped_gemm call with these sizes (host only).  MXFP8 needs
  * only the split tables; NVFP4 also holds both operands expanded exactly to bf16
@@ -268,7 +276,7 @@ typedef struct {
   float* dprobs;              /* fp32 [M] */
   void* dw1;                  /* [E, F1, H] in wgrad_dtype (NULL if !weight_requires_grad) */
   void* dw2;                  /* [E, H, ffn] */
-  int32_t wgrad_dtype;        /* gmlp_out_dtype */
+  int32_t wgrad_dtype;        /* gmlp_out_dtype; FP32_ACCUMULATE: dw1, dw2 are fp32 main_grads, added to */
   const void* ctx; size_t ctx_bytes;
   void* ws; size_t ws_bytes;
 } gmlp_bwd_args;

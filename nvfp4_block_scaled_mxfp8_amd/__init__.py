@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libgmlp.so")
 
 MXFP8, NVFP4_RHT = 0, 1
 SWIGLU, SRELU = 0, 1
-OUT_BF16, OUT_FP32 = 0, 1
+OUT_BF16, OUT_FP32, OUT_FP32_ACCUMULATE = 0, 1, 2
 GEMM_FPROP, GEMM_WGRAD = 0, 1
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP_ERROR"}
 COL_PAD = 128
@@ -323,11 +323,22 @@ def grouped_gemm_ws_bytes(layout, rec, G, M, n, k):
     return v.value
 
 
-def grouped_gemm(layout, rec, a, b, m_splits, M, n, k, out_dtype=OUT_BF16, ws=None):
+def _check_out(t, shape, dtype, name):
+    if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: an existing contiguous {dtype} tensor of shape {tuple(shape)} is required")
+
+
+def grouped_gemm(layout, rec, a, b, m_splits, M, n, k, out_dtype=OUT_BF16, ws=None, out=None):
+    """out: the output tensor (required for OUT_FP32_ACCUMULATE, whose product is added to it)."""
     G = m_splits.numel()
     dev = m_splits.device
-    dt = torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16
-    c = torch.empty((M, n) if layout == GEMM_FPROP else (G, n, k), dtype=dt, device=dev)
+    dt = torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32
+    shape = (M, n) if layout == GEMM_FPROP else (G, n, k)
+    if out is not None or out_dtype == OUT_FP32_ACCUMULATE:
+        _check_out(out, shape, dt, "grouped_gemm out")
+        c = out
+    else:
+        c = torch.empty(shape, dtype=dt, device=dev)
     if ws is None:
         ws = torch.empty(grouped_gemm_ws_bytes(layout, rec, G, M, n, k), dtype=torch.uint8, device=dev)
     qa, qb = a.struct(), b.struct()
@@ -376,6 +387,9 @@ def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute
 
 
 def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF16, ws=None, out=None):
+    """out: optional {"dx", "dprobs", "dw1", "dw2"} tensors to write; with wgrad_dtype
+    OUT_FP32_ACCUMULATE, "dw1" and "dw2" are required: the fp32 main_grads the weight
+    gradients are added to."""
     dy = _bits(dy)
     M, H = dy.shape
     E, ffn, act = ctx.E, ctx.ffn, ctx.activation
@@ -383,7 +397,7 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
     dev = dy.device
     sizes = query_sizes(M, E, H, ffn, act, ctx.rec, ctx.recompute)
     ws = ws if ws is not None else torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
-    wdt = torch.float32 if wgrad_dtype == OUT_FP32 else torch.bfloat16
+    wdt = torch.bfloat16 if wgrad_dtype == OUT_BF16 else torch.float32
     o = out or {}
     dx = o.get("dx") if ctx.input_requires_grad else None
     if ctx.input_requires_grad and dx is None:
@@ -391,8 +405,13 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
     dprobs = o.get("dprobs", torch.empty(M, dtype=torch.float32, device=dev))
     dw1 = dw2 = None
     if ctx.weight_requires_grad:
-        dw1 = o.get("dw1", torch.empty((E, F1, H), dtype=wdt, device=dev))
-        dw2 = o.get("dw2", torch.empty((E, H, ffn), dtype=wdt, device=dev))
+        if wgrad_dtype == OUT_FP32_ACCUMULATE:
+            dw1, dw2 = o.get("dw1"), o.get("dw2")
+            _check_out(dw1, (E, F1, H), wdt, "dw1 main_grad")
+            _check_out(dw2, (E, H, ffn), wdt, "dw2 main_grad")
+        else:
+            dw1 = o.get("dw1", torch.empty((E, F1, H), dtype=wdt, device=dev))
+            dw2 = o.get("dw2", torch.empty((E, H, ffn), dtype=wdt, device=dev))
     s1, s2 = w1q.struct(), w2q.struct()
     a = BwdArgs(dy.data_ptr(), m_splits.data_ptr(), M, E, H, ffn, ctypes.pointer(s1), ctypes.pointer(s2),
                 probs.data_ptr() if M else None, act, ctx.rec, int(ctx.recompute), int(ctx.input_requires_grad),

@@ -521,6 +521,10 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
   if (!a || !b || !m_splits || !c) return fail(GMLP_INVALID_ARG, "null pointer argument");
   if (G < 1 || M < 0 || n <= 0 || k <= 0 || n % 32 || k % 32) return fail(GMLP_UNSUPPORTED, "dims: n, k must be positive multiples of 32");
   if (layout == GMLP_GEMM_FPROP && k % 128) return fail(GMLP_UNSUPPORTED, "dims: the FPROP contraction k must be a multiple of 128");
+  if (out_dtype != GMLP_OUT_BF16 && out_dtype != GMLP_OUT_FP32 && out_dtype != GMLP_OUT_FP32_ACCUMULATE)
+    return fail(GMLP_INVALID_ARG, "unknown output dtype %d", out_dtype);
+  if (out_dtype == GMLP_OUT_FP32_ACCUMULATE && layout != GMLP_GEMM_WGRAD)
+    return fail(GMLP_UNSUPPORTED, "accumulating output: WGRAD layout only");
   {
     const bool fp = layout == GMLP_GEMM_FPROP;
     const GemmOperand oa = fp ? op_row(*a, a->amax_pre) : op_col(*a, a->amax_post);
@@ -548,7 +552,7 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
   g.N = n;
   g.K = k;
   g.c = c;
-  g.out_fp32 = out_dtype == GMLP_OUT_FP32;
+  g.out_fp32 = out_dtype;   // 0 bf16, 1 fp32, 2 fp32 added to c
   if (layout == GMLP_GEMM_FPROP) {
     g.a = op_row(*a, a->amax_pre);
     g.b = op_row(*b, b->amax_pre);
@@ -677,6 +681,9 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
   if (!A->m_splits || (A->M > 0 && (!A->dy || !A->probs || !A->dprobs)) || (dgrad && A->M > 0 && !A->dx) ||
       (wgrad && (!A->dw1 || !A->dw2)))
     return fail(GMLP_INVALID_ARG, "null pointer argument");
+  if (wgrad && A->wgrad_dtype != GMLP_OUT_BF16 && A->wgrad_dtype != GMLP_OUT_FP32 &&
+      A->wgrad_dtype != GMLP_OUT_FP32_ACCUMULATE)
+    return fail(GMLP_INVALID_ARG, "unknown wgrad dtype %d", A->wgrad_dtype);
   if ((st = weight_ok(A->w2, A->recipe, false, true)) != GMLP_OK) return st;
   if (dgrad && (st = weight_ok(A->w1, A->recipe, false, true)) != GMLP_OK) return st;
   const bool mx = is_mx(A->recipe);
@@ -803,7 +810,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     g.a = op_col(W.dyq.q, W.dyq.q.amax_post);
     g.b = op_col(*aq, a_post);
     g.c = A->dw2;
-    g.out_fp32 = A->wgrad_dtype == GMLP_OUT_FP32;
+    g.out_fp32 = A->wgrad_dtype;
     set_nv(g, W.nv);
     if (!L.check(launch_gemm(g, stream), "fc2 wgrad gemm")) return L.st;
     g_counts[CNT_GEMM]++;
@@ -830,7 +837,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     g.a = op_col(W.dhq.q, W.dhq.q.amax_post);
     g.b = op_col(C.xq_col.q, C.xq_col.q.amax_post);
     g.c = A->dw1;
-    g.out_fp32 = A->wgrad_dtype == GMLP_OUT_FP32;
+    g.out_fp32 = A->wgrad_dtype;
     set_nv(g, W.nv);
     if (!L.check(launch_gemm(g, stream), "fc1 wgrad gemm")) return L.st;
     g_counts[CNT_GEMM]++;

@@ -619,6 +619,11 @@ constexpr int kStoreNT = 2;                       // aux bits of a nontemporal b
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, (int)kRsrcWord3);
 }
+__device__ __forceinline__ uint4 out_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t x,
                                           uint32_t y, uint32_t z, uint32_t w) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -651,7 +656,7 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
   __syncthreads();
   {
     // lanes [LPR r, LPR r + LPR) store staged row r of each group of RPI rows
-    constexpr int ESZ = (EPI == EPI_STORE32) ? 4 : 2;
+    constexpr int ESZ = (EPI == EPI_STORE32 || EPI == EPI_ACC32) ? 4 : 2;
     constexpr int PER = 16 / ESZ;                 // output elements per 16-byte store
     constexpr int LPR = 128 / PER;
     constexpr int RPI = NTHREADS / LPR;
@@ -665,6 +670,25 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
     const int col = 128 * (sc >> 6) + 64 * Q + (sc & 63);
     const uint32_t voff = (c.nrow0 + col < ncols) ? (uint32_t)lrow * rowb + (uint32_t)(col * ESZ) : kOutOfRange;
     const float* src = st + lrow * EPC_LD + sc;
+    if constexpr (EPI == EPI_ACC32) {
+      // C += tile: the chunk's old fp32 values are fetched together (one 16-byte load per
+      // store, same offsets, so the range check drops the same lanes), then added in fp32
+      uint4 old[NIT];
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const uint32_t ur = (uint32_t)(128 * ((RPI * it) >> 5) + 32 * TM + ((RPI * it) & 31));
+        old[it] = out_load(r, voff, ur * rowb);
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const uint32_t ur = (uint32_t)(128 * ((RPI * it) >> 5) + 32 * TM + ((RPI * it) & 31));
+        const float4 v = ld_st4<BF>(src + RPI * it * EPC_LD, c.alpha);
+        out_store(r, voff, ur * rowb, __float_as_uint(__fadd_rn(__uint_as_float(old[it].x), v.x)),
+                  __float_as_uint(__fadd_rn(__uint_as_float(old[it].y), v.y)),
+                  __float_as_uint(__fadd_rn(__uint_as_float(old[it].z), v.z)),
+                  __float_as_uint(__fadd_rn(__uint_as_float(old[it].w), v.w)));
+      }
+    } else {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const uint32_t ur = (uint32_t)(128 * ((RPI * it) >> 5) + 32 * TM + ((RPI * it) & 31));   // tile row - lrow
@@ -678,13 +702,16 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
                   pack_bf16x2(v1.z, v1.w));
       }
     }
+    }
   }
   __syncthreads();
 }
 
-// Output tile of a group with no tokens (weight gradients only): zeros, stored directly.
+// Output tile of a group with no tokens (weight gradients only): zeros, stored directly (an
+// accumulated gradient is left as it is).
 template <int MODE, int EPI>
 __device__ __forceinline__ void epi_zero(const GemmArgs& A, const Ctx& c, int tid) {
+  if constexpr (EPI == EPI_ACC32) return;
   const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
   const int esz = (EPI == EPI_STORE32) ? 4 : 2;
   for (int it = 0; it < 32 * esz / 2; ++it) {
@@ -1038,8 +1065,10 @@ static hipError_t launch_nvfp4(const GemmArgs& g, int epi, hipStream_t s) {
   // no scale words: their DMA slot runs with empty resources; give them a real base anyway
   a.a.scale_mfma = reinterpret_cast<const uint32_t*>(a.a.data);
   a.b.scale_mfma = reinterpret_cast<const uint32_t*>(a.b.data);
-  if (g.mode == MODE_WGRAD) return epi == EPI_STORE32 ? launch_mx<MODE_WGRAD, EPI_STORE32, 1>(a, s)
-                                                      : launch_mx<MODE_WGRAD, EPI_STORE, 1>(a, s);
+  if (g.mode == MODE_WGRAD) {
+    if (epi == EPI_ACC32) return launch_mx<MODE_WGRAD, EPI_ACC32, 1>(a, s);
+    return epi == EPI_STORE32 ? launch_mx<MODE_WGRAD, EPI_STORE32, 1>(a, s) : launch_mx<MODE_WGRAD, EPI_STORE, 1>(a, s);
+  }
   if (epi == EPI_STORE32) return launch_mx<MODE_FPROP, EPI_STORE32, 1>(a, s);
   if (epi == EPI_STORE) return launch_mx<MODE_FPROP, EPI_STORE, 1>(a, s);
   if (epi != EPI_DACT) return hipErrorInvalidValue;
@@ -1052,7 +1081,8 @@ static hipError_t launch_nvfp4(const GemmArgs& g, int epi, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.mode == MODE_FPROP && g.M == 0) return hipSuccess;
-  const int epi = (g.epi == EPI_STORE && g.out_fp32) ? (int)EPI_STORE32 : g.epi;
+  const int epi = (g.epi != EPI_STORE || !g.out_fp32) ? g.epi : (g.out_fp32 == 2 ? (int)EPI_ACC32 : (int)EPI_STORE32);
+  if (epi == EPI_ACC32 && g.mode != MODE_WGRAD) return hipErrorInvalidValue;
   if (g.fmt == FMT_NVFP4) return launch_nvfp4(g, epi, s);
 #define GMLP_DISPATCH_MX(MO, E) \
   if (g.fmt == FMT_MXFP8 && g.mode == MO && epi == E) return launch_mx<MO, E, 0>(g, s);
@@ -1060,6 +1090,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   GMLP_DISPATCH_MX(MODE_FPROP, EPI_STORE32)
   GMLP_DISPATCH_MX(MODE_WGRAD, EPI_STORE32)
   GMLP_DISPATCH_MX(MODE_WGRAD, EPI_STORE)
+  GMLP_DISPATCH_MX(MODE_WGRAD, EPI_ACC32)
 #undef GMLP_DISPATCH_MX
   return hipErrorInvalidValue;
 }

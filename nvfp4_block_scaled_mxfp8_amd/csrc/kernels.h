@@ -102,8 +102,9 @@ hipError_t launch_dact_bf16(const uint16_t* da, const uint16_t* h, const float* 
 // the 64-byte panel layout of the MXFP8 operands, with the per-group amax for the global scales.
 enum GemmFmt { FMT_MXFP8 = 0, FMT_NVFP4 = 1, FMT_NVFP4_BF16 = 2 };
 enum GemmMode { MODE_FPROP = 0, MODE_WGRAD = 1 };
-// STORE32: fp32 output.  DACT (NVFP4 fc2 dgrad): da is stored, then the activation-gradient pass.
-enum GemmEpi { EPI_STORE = 0, EPI_DACT = 2, EPI_STORE32 = 3 };
+// STORE32: fp32 output.  ACC32: fp32 output added to what C holds (weight gradients into an fp32
+// main_grad).  DACT (NVFP4 fc2 dgrad): da is stored, then the activation-gradient pass.
+enum GemmEpi { EPI_STORE = 0, EPI_DACT = 2, EPI_STORE32 = 3, EPI_ACC32 = 4 };
 
 struct GemmOperand {
   const uint8_t* data;        // fp8 / packed fp4
@@ -123,7 +124,7 @@ struct GemmArgs {
   int64_t K;         // FPROP: contraction; WGRAD: rows of B per group
   // outputs
   void* c;           // EPI_STORE: C (bf16 or fp32)
-  int out_fp32;
+  int out_fp32;      // 0 bf16, 1 fp32, 2 fp32 added to C (WGRAD)
   // fused epilogue operands
   int act;           // 0 SwiGLU, 1 SReLU
   int64_t ffn;       // EPI_DACT: ffn (width of da and a'); SwiGLU F1 = 2 ffn

@@ -36,10 +36,12 @@ Readings (the pages are silent on these):
   the post-RHT amax for column-wise casts; per expert (amax of the whole
   weight matrix) for weights.
 * Empty experts contribute no rows and a zero weight gradient.
+* A weight gradient accumulated into an fp32 main_grad is the exact gradient
+  added to the stored fp32 value, rounded once to fp32 (no bf16 step).
 """
 import numpy as np
 
-from .formats import bf16_bits_to_f64, f64_to_bf16_bits, round_bf16
+from .formats import bf16_bits_to_f64, f32, f64_to_bf16_bits, round_bf16
 from .formats import pack_fp4
 from .quant import (mxfp8_dequant_rows, mxfp8_group_quantize, mxfp8_quantize_rows,
                     nvfp4_dequant_packed, nvfp4_dequant_rows, nvfp4_group_quantize_with_amax,
@@ -233,6 +235,18 @@ def backward(fwd, dy_bits):
         "dw1_f64": dw1, "dw1_bits": f64_to_bf16_bits(dw1),
         "dw2_f64": dw2, "dw2_bits": f64_to_bf16_bits(dw2),
     }
+
+
+def accumulate_main_grad(main_grad, dw):
+    """fp32 main_grad after the weight gradient is added to it: fp32(main_grad + dW).
+
+    "GEMM + Swiglu fused Grouped MLP for MXFP8", review comments on overwrite_main_grad: the
+    grouped wgrad either overwrites the parameter's fp32 main_grad or accumulates into it.
+    main_grad holds fp32 values; dw is the fp64 gradient (``dw1_f64`` / ``dw2_f64``).  The sum
+    is formed in fp64 and rounded once to fp32; for an fp32-representable dw that is exactly
+    IEEE fp32 addition (53 >= 2 * 24 + 2).  An empty expert's zero gradient leaves it as it is.
+    """
+    return f32(np.asarray(main_grad, dtype=np.float64) + np.asarray(dw, dtype=np.float64))
 
 
 # ----------------------------------------------------------------------------- sampled evaluation (MXFP8)

@@ -112,3 +112,23 @@ def test_launch_range_limits_are_reported():
     args.recipe = g.recipe("nvfp4", 1)
     assert L.gmlp_grouped_mlp_forward(ctypes.byref(args), None) == 2
     assert "row range" in g.last_error()
+
+
+def test_output_dtype_validation():
+    """Unknown output dtypes are rejected, and accumulation is for weight gradients only."""
+    L = g.lib()
+    q = g.GroupedQ()
+    dummy = ctypes.c_void_p(16)
+    st = L.gmlp_grouped_gemm(1, g.recipe("mxfp8"), ctypes.byref(q), ctypes.byref(q), dummy, 1, 64, 128, 128, dummy,
+                             7, None, 0, None)
+    assert st == 1 and "output dtype" in g.last_error()
+    st = L.gmlp_grouped_gemm(0, g.recipe("mxfp8"), ctypes.byref(q), ctypes.byref(q), dummy, 1, 64, 128, 128, dummy,
+                             g.OUT_FP32_ACCUMULATE, None, 0, None)
+    assert st == 2 and "WGRAD" in g.last_error()
+    args = g.BwdArgs()
+    args.E, args.M, args.H, args.ffn = 2, 64, 128, 128
+    args.recipe = g.recipe("mxfp8")
+    args.m_splits = args.dy = args.probs = args.dprobs = args.dw1 = args.dw2 = 16
+    args.weight_requires_grad, args.wgrad_dtype = 1, 9
+    assert L.gmlp_grouped_mlp_backward(ctypes.byref(args), None) == 1
+    assert "wgrad dtype" in g.last_error()

@@ -80,6 +80,39 @@ def test_gemm_wgrad(kind, splits, Na, Nb):
             assert np.all(got[e] == 0), "an empty expert must get a zero weight gradient"
 
 
+@pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
+def test_gemm_wgrad_accumulates_into_fp32(kind):
+    """WGRAD with OUT_FP32_ACCUMULATE adds the product to the fp32 tensor given, twice in a row:
+    each result is bit for bit the fp32 sum of the previous contents and the plain fp32 output
+    (an empty expert's slice stays as it was), and within the GEMM tolerance of the oracle's
+    fp32(main_grad + dW)."""
+    splits, Na, Nb = [300, 0, 37, 129], 256, 384
+    M, E, mask = sum(splits), len(splits), 0x91E7
+    print(f"gemm wgrad accumulate {kind} splits={splits} Na={Na} Nb={Nb}", flush=True)
+    a = random_bf16((M, Na), seed=11)
+    b = random_bf16((M, Nb), seed=12, dist="srelu")
+    rec = g.recipe(kind, mask)
+    sd = dev_splits(splits)
+    aq = g.group_quantize(dev_bf16(a), sd, rec, False, True)
+    bq = g.group_quantize(dev_bf16(b), sd, rec, False, True)
+    c32 = g.grouped_gemm(g.GEMM_WGRAD, rec, aq, bq, sd, M, Na, Nb, out_dtype=g.OUT_FP32)
+    torch.cuda.synchronize()
+    c = c32.cpu().numpy()
+    main0 = (np.random.default_rng(13).standard_normal((E, Na, Nb)) * c.std()).astype(np.float32)
+    main = torch.from_numpy(main0).to("cuda")
+    want = main0
+    for _ in range(2):
+        out = g.grouped_gemm(g.GEMM_WGRAD, rec, aq, bq, sd, M, Na, Nb, out_dtype=g.OUT_FP32_ACCUMULATE, out=main)
+        assert out is main
+        torch.cuda.synchronize()
+        want = want + c
+        assert np.array_equal(main.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    got = main.cpu().numpy()
+    assert np.array_equal(got[1].view(np.uint32), main0[1].view(np.uint32)), "empty expert changed"
+    ref = _wgrad_ref(a, b, splits, kind, mask)
+    assert O.rel_fro(got.astype(np.float64), O.accumulate_main_grad(O.accumulate_main_grad(main0, ref), ref)) <= 5e-5
+
+
 def test_gemm_exact_inputs_bitwise():
     """Small-integer data quantizes exactly to MXFP8 and every fp32 partial sum is exact, so the
     MFMA result equals the fp64 product and the bf16 outputs must match bit for bit."""

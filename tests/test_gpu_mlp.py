@@ -25,18 +25,19 @@ def _upload(wl):
     return d
 
 
-def _run(wl, d, kind, recompute, backward=True, wgrad_dtype=g.OUT_BF16):
+def _run(wl, d, kind, recompute, backward=True, wgrad_dtype=g.OUT_BF16, out=None):
     rec = g.recipe(kind, wl.sign_mask)
     w1q = g.weight_quantize(d["w1"], rec)
     w2q = g.weight_quantize(d["w2"], rec)
     y, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], wl.config.activation, rec,
                                    recompute=recompute)
-    out = {"y": y, "fwd_counts": g.last_launch_counts()}
+    res = {"y": y, "fwd_counts": g.last_launch_counts()}
     if backward:
-        out.update(g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx, wgrad_dtype=wgrad_dtype))
-        out["bwd_counts"] = g.last_launch_counts()
+        res.update(g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx,
+                                          wgrad_dtype=wgrad_dtype, out=out))
+        res["bwd_counts"] = g.last_launch_counts()
     torch.cuda.synchronize()
-    return out
+    return res
 
 
 def _f64(t):
@@ -101,6 +102,35 @@ def test_deterministic_and_fp32_wgrad():
     c = _run(wl, d, "mxfp8", recompute=False, wgrad_dtype=g.OUT_FP32)
     assert c["dw1"].dtype == torch.float32
     assert O.rel_fro(c["dw1"].double().cpu().numpy(), _f64(a["dw1"])) <= 1e-2
+
+
+@pytest.mark.parametrize("kind,act", [("mxfp8", "swiglu"), ("nvfp4", "srelu")])
+def test_backward_accumulates_weight_gradients_into_fp32_main_grad(kind, act):
+    """wgrad_dtype OUT_FP32_ACCUMULATE adds the weight gradients to the fp32 main_grads passed in:
+    bit for bit the fp32 sum of the stored values and the plain fp32 gradients (an empty expert's
+    slices unchanged), dx and dprobs as without it, and within tolerance of the oracle's
+    fp32(main_grad + dW)."""
+    wl = small_case([100, 0, 300, 41], 256, 256, activation=act, recipe=kind, seed=9, w_std=0.05)
+    d = _upload(wl)
+    plain = _run(wl, d, kind, recompute=True, wgrad_dtype=g.OUT_FP32)
+    rng = np.random.default_rng(10)
+    m0 = {k: (rng.standard_normal(tuple(plain[k].shape)) * plain[k].std().item()).astype(np.float32)
+          for k in ("dw1", "dw2")}
+    main = {k: torch.from_numpy(v).to("cuda") for k, v in m0.items()}
+    acc = _run(wl, d, kind, recompute=True, wgrad_dtype=g.OUT_FP32_ACCUMULATE, out=dict(main))
+    rec = O.Recipe(kind, wl.sign_mask)
+    bwd = O.backward(O.forward(wl.x, wl.m_splits, wl.w1, wl.w2, wl.probs, act, rec), wl.dy)
+    for k in ("dw1", "dw2"):
+        assert acc[k].data_ptr() == main[k].data_ptr(), "the main_grad is updated in place"
+        got = acc[k].cpu().numpy()
+        want = m0[k] + plain[k].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), k
+        assert np.array_equal(got[1].view(np.uint32), m0[k][1].view(np.uint32)), "empty expert changed"
+        err = O.rel_fro(got.astype(np.float64), O.accumulate_main_grad(m0[k], bwd[k + "_f64"]))
+        print(kind, act, k, f"{err:.2e}", flush=True)
+        assert err <= TOL, (k, err)
+    for k in ("y", "dx", "dprobs"):
+        assert torch.equal(acc[k], plain[k]), k
 
 
 def test_tiny_config_forward():

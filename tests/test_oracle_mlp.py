@@ -166,3 +166,24 @@ def test_sampled_rows_and_wgrad_entries_match_the_full_oracle(act):
                                          wl.probs[off[e]:off[e + 1]], d1, d2, act, i1, i2)
         np.testing.assert_allclose(w1e, [bwd["dw1_f64"][e, f, k] for f, k in i1], rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(w2e, [bwd["dw2_f64"][e, n, f] for n, f in i2], rtol=1e-10, atol=1e-12)
+
+
+def test_main_grad_accumulation_is_one_fp32_rounding():
+    """fp32(main_grad + dW): for fp32 gradients it is IEEE fp32 addition (numpy's float32 add),
+    bit for bit, across wide exponent ranges and cancellation; an fp64 gradient is rounded once,
+    with ties to even, and never through bf16."""
+    rng = np.random.default_rng(21)
+    n = 20000
+    main = (rng.standard_normal(n) * np.exp2(rng.integers(-40, 41, n))).astype(np.float32)
+    dw = (rng.standard_normal(n) * np.exp2(rng.integers(-40, 41, n))).astype(np.float32)
+    dw[:1000] = -main[:1000]                                    # exact cancellation
+    dw[1000:2000] = 0.0                                         # an empty expert's zero gradient
+    got = O.accumulate_main_grad(main, dw).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32)[1000:], (main + dw).view(np.uint32)[1000:])
+    assert np.all(got[:1000] == 0.0)
+    assert np.array_equal(got[1000:2000], main[1000:2000])
+    # one rounding of the exact sum: 1 + 2^-24 is a tie (to even: 1), a hair above it rounds up
+    assert O.accumulate_main_grad(1.0, 2.0 ** -24) == 1.0
+    assert O.accumulate_main_grad(1.0, 2.0 ** -24 + 2.0 ** -40) == 1.0 + 2.0 ** -23
+    # no bf16 step: 1 + 2^-20 survives (bf16 would make it 1)
+    assert O.accumulate_main_grad(0.0, 1.0 + 2.0 ** -20) == 1.0 + 2.0 ** -20
