@@ -279,10 +279,23 @@ typedef struct {
   int32_t wgrad_dtype;        /* gmlp_out_dtype; FP32_ACCUMULATE: dw1, dw2 are fp32 main_grads, added to */
   const void* ctx; size_t ctx_bytes;
   void* ws; size_t ws_bytes;
+  int32_t defer_wgrad;        /* != 0 (with weight_requires_grad): cast the weight-gradient operands into
+                                 ws but leave dw1, dw2 to a later gmlp_grouped_mlp_wgrad */
 } gmlp_bwd_args;
 
 gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* args, hipStream_t stream);
 gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* args, hipStream_t stream);
+
+/* Deferred weight gradients [MX, Greptile summary, Important Files Changed: the grouped linear
+ * op's delay_wgrad hooks]:
+ * dW2_g and dW1_g from the operands a backward with defer_wgrad != 0 left in ws (and the
+ * forward's ctx).  args: the same sizes, recipe, activation, recompute, m_splits, ctx and ws as
+ * that backward, with dw1, dw2 and wgrad_dtype for this call (dy, dx, dprobs, w1, w2 are not
+ * read).  Stream-ordered after that backward; ctx and ws must be untouched in between,
+ * otherwise the gradients are unspecified (the split tables are rebuilt from m_splits, so
+ * every address stays inside the buffers).  May be called once or several times (e.g.
+ * accumulating into main_grad). */
+gmlp_status gmlp_grouped_mlp_wgrad(const gmlp_bwd_args* args, hipStream_t stream);
 
 /* Launch counts of the last forward / backward on this thread, by kernel kind
  * (0 scan, 1 mxfp8 quantize, 2 hadamard amax, 3 nvfp4 cast, 4 gemm, 5 dprob

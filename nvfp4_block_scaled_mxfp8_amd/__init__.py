@@ -72,7 +72,8 @@ class BwdArgs(ctypes.Structure):
                 ("weight_requires_grad", ctypes.c_int32), ("dx", ctypes.c_void_p),
                 ("dprobs", ctypes.c_void_p), ("dw1", ctypes.c_void_p), ("dw2", ctypes.c_void_p),
                 ("wgrad_dtype", ctypes.c_int32), ("ctx", ctypes.c_void_p),
-                ("ctx_bytes", ctypes.c_size_t), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+                ("ctx_bytes", ctypes.c_size_t), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+                ("defer_wgrad", ctypes.c_int32)]
 
 
 _SIGS = {
@@ -102,6 +103,7 @@ _SIGS = {
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "gmlp_grouped_mlp_forward": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "gmlp_grouped_mlp_backward": (ctypes.c_int, [ctypes.POINTER(BwdArgs), ctypes.c_void_p]),
+    "gmlp_grouped_mlp_wgrad": (ctypes.c_int, [ctypes.POINTER(BwdArgs), ctypes.c_void_p]),
     "gmlp_last_launch_counts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]),
     "gmlp_grouped_gemm_ws_bytes": (ctypes.c_int, [ctypes.c_int32, Recipe, ctypes.c_int32, ctypes.c_int64,
                                                   ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]),
@@ -386,10 +388,12 @@ def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute
     return y, c
 
 
-def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF16, ws=None, out=None):
+def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF16, ws=None, out=None,
+                         defer_wgrad=False):
     """out: optional {"dx", "dprobs", "dw1", "dw2"} tensors to write; with wgrad_dtype
     OUT_FP32_ACCUMULATE, "dw1" and "dw2" are required: the fp32 main_grads the weight
-    gradients are added to."""
+    gradients are added to.  defer_wgrad: dw1 and dw2 are left to grouped_mlp_wgrad, which
+    takes the returned "deferred" handle (it holds the workspace with the cast operands)."""
     dy = _bits(dy)
     M, H = dy.shape
     E, ffn, act = ctx.E, ctx.ffn, ctx.activation
@@ -404,7 +408,7 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
         dx = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     dprobs = o.get("dprobs", torch.empty(M, dtype=torch.float32, device=dev))
     dw1 = dw2 = None
-    if ctx.weight_requires_grad:
+    if ctx.weight_requires_grad and not defer_wgrad:
         if wgrad_dtype == OUT_FP32_ACCUMULATE:
             dw1, dw2 = o.get("dw1"), o.get("dw2")
             _check_out(dw1, (E, F1, H), wdt, "dw1 main_grad")
@@ -418,9 +422,47 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
                 int(ctx.weight_requires_grad), dx.data_ptr() if (dx is not None and M) else None,
                 dprobs.data_ptr() if M else None, dw1.data_ptr() if dw1 is not None else None,
                 dw2.data_ptr() if dw2 is not None else None, wgrad_dtype, ctx.buf.data_ptr(), ctx.buf.numel(),
-                ws.data_ptr(), ws.numel())
+                ws.data_ptr(), ws.numel(), int(bool(defer_wgrad)))
     _check(lib().gmlp_grouped_mlp_backward(ctypes.byref(a), _stream(dev)))
-    return {"dx": dx, "dprobs": dprobs, "dw1": dw1, "dw2": dw2}
+    res = {"dx": dx, "dprobs": dprobs, "dw1": dw1, "dw2": dw2}
+    if defer_wgrad and ctx.weight_requires_grad:
+        res["deferred"] = DeferredWgrad(m_splits, ctx, ws)
+    return res
+
+
+@dataclass
+class DeferredWgrad:
+    """What a deferring backward leaves for grouped_mlp_wgrad: the splits, the forward's context
+    and the workspace holding the cast weight-gradient operands (keep both untouched)."""
+    m_splits: torch.Tensor
+    ctx: MlpContext
+    ws: torch.Tensor
+
+
+def grouped_mlp_wgrad(deferred, wgrad_dtype=OUT_BF16, out=None):
+    """The weight gradients of a backward called with defer_wgrad; out as in grouped_mlp_backward
+    ("dw1", "dw2")."""
+    ctx, ws = deferred.ctx, deferred.ws
+    E, H, ffn, act = ctx.E, ctx.H, ctx.ffn, ctx.activation
+    F1 = 2 * ffn if act == SWIGLU else ffn
+    dev = ws.device
+    wdt = torch.bfloat16 if wgrad_dtype == OUT_BF16 else torch.float32
+    o = out or {}
+    if wgrad_dtype == OUT_FP32_ACCUMULATE:
+        dw1, dw2 = o.get("dw1"), o.get("dw2")
+        _check_out(dw1, (E, F1, H), wdt, "dw1 main_grad")
+        _check_out(dw2, (E, H, ffn), wdt, "dw2 main_grad")
+    else:
+        dw1 = o.get("dw1", torch.empty((E, F1, H), dtype=wdt, device=dev))
+        dw2 = o.get("dw2", torch.empty((E, H, ffn), dtype=wdt, device=dev))
+    a = BwdArgs()
+    a.m_splits, a.M, a.E, a.H, a.ffn = deferred.m_splits.data_ptr(), ctx.M, E, H, ffn
+    a.activation, a.recipe, a.recompute = act, ctx.rec, int(ctx.recompute)
+    a.input_requires_grad, a.weight_requires_grad = int(ctx.input_requires_grad), 1
+    a.dw1, a.dw2, a.wgrad_dtype = dw1.data_ptr(), dw2.data_ptr(), wgrad_dtype
+    a.ctx, a.ctx_bytes, a.ws, a.ws_bytes = ctx.buf.data_ptr(), ctx.buf.numel(), ws.data_ptr(), ws.numel()
+    _check(lib().gmlp_grouped_mlp_wgrad(ctypes.byref(a), _stream(dev)))
+    return {"dw1": dw1, "dw2": dw2}
 
 
 def ffn_from_w2(w2q, rec, E, H):

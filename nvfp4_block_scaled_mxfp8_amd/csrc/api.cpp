@@ -671,6 +671,56 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+gmlp_status check_wgrad_dtype(int32_t d) {
+  if (d != GMLP_OUT_BF16 && d != GMLP_OUT_FP32 && d != GMLP_OUT_FP32_ACCUMULATE)
+    return fail(GMLP_INVALID_ARG, "unknown wgrad dtype %d", d);
+  return GMLP_OK;
+}
+
+// fc2 wgrad: dW2_g = Qc(dy_g)^T Qc(a_g), with the fc2 input rebuilt and cast in the backward when
+// recomputing (its column-wise cast then lives in the backward's workspace, cast with the saved
+// amax), else the forward's column-wise cast in ctx.
+bool fc2_wgrad(const gmlp_bwd_args* A, const FwdCtx& C, const BwdWs& W, Launcher& L, hipStream_t stream) {
+  const bool rec = A->recompute != 0;
+  GemmArgs g = gemm_base(MODE_WGRAD, A->recipe, EPI_STORE, W.T, A->E);
+  g.M = A->M;
+  g.N = A->H;
+  g.K = A->ffn;
+  g.a = op_col(W.dyq.q, W.dyq.q.amax_post);
+  g.b = rec ? op_col(W.a2q.q, C.a_post) : op_col(C.aq_col.q, C.a_post);
+  g.c = A->dw2;
+  g.out_fp32 = A->wgrad_dtype;
+  set_nv(g, W.nv);
+  if (!L.check(launch_gemm(g, stream), "fc2 wgrad gemm")) return false;
+  g_counts[CNT_GEMM]++;
+  return true;
+}
+
+// fc1 wgrad: dW1_g = Qc(dh_g)^T Qc(x_g).
+bool fc1_wgrad(const gmlp_bwd_args* A, const FwdCtx& C, const BwdWs& W, Launcher& L, hipStream_t stream) {
+  const int64_t F1 = A->activation == GMLP_SWIGLU ? 2 * A->ffn : A->ffn;
+  GemmArgs g = gemm_base(MODE_WGRAD, A->recipe, EPI_STORE, W.T, A->E);
+  g.M = A->M;
+  g.N = F1;
+  g.K = A->H;
+  g.a = op_col(W.dhq.q, W.dhq.q.amax_post);
+  g.b = op_col(C.xq_col.q, C.xq_col.q.amax_post);
+  g.c = A->dw1;
+  g.out_fp32 = A->wgrad_dtype;
+  set_nv(g, W.nv);
+  if (!L.check(launch_gemm(g, stream), "fc1 wgrad gemm")) return false;
+  g_counts[CNT_GEMM]++;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
 gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream) {
   memset(g_counts, 0, sizeof(g_counts));
   if (!A) return fail(GMLP_INVALID_ARG, "null args");
@@ -678,12 +728,11 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
   if (st != GMLP_OK) return st;
   const bool dgrad = A->input_requires_grad != 0;
   const bool wgrad = A->weight_requires_grad != 0;
+  const bool defer = wgrad && A->defer_wgrad != 0;
   if (!A->m_splits || (A->M > 0 && (!A->dy || !A->probs || !A->dprobs)) || (dgrad && A->M > 0 && !A->dx) ||
-      (wgrad && (!A->dw1 || !A->dw2)))
+      (wgrad && !defer && (!A->dw1 || !A->dw2)))
     return fail(GMLP_INVALID_ARG, "null pointer argument");
-  if (wgrad && A->wgrad_dtype != GMLP_OUT_BF16 && A->wgrad_dtype != GMLP_OUT_FP32 &&
-      A->wgrad_dtype != GMLP_OUT_FP32_ACCUMULATE)
-    return fail(GMLP_INVALID_ARG, "unknown wgrad dtype %d", A->wgrad_dtype);
+  if (wgrad && !defer && (st = check_wgrad_dtype(A->wgrad_dtype)) != GMLP_OK) return st;
   if ((st = weight_ok(A->w2, A->recipe, false, true)) != GMLP_OK) return st;
   if (dgrad && (st = weight_ok(A->w1, A->recipe, false, true)) != GMLP_OK) return st;
   const bool mx = is_mx(A->recipe);
@@ -787,33 +836,18 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     if (dgrad || wgrad)
       if (!quant(W.dh, F1, W.dhq, dgrad, wgrad)) return L.st;
   }
-  // 4. fc2 wgrad: column-wise dy and fc2 input (rebuilt and cast with the saved amax when recomputing)
+  // 4. fc2 wgrad: column-wise dy and fc2 input (rebuilt and cast with the saved amax when
+  // recomputing; the MXFP8 rebuild was cast by the activation-gradient pass above).  Deferred:
+  // the operands stay in the workspace for gmlp_grouped_mlp_wgrad.
   if (wgrad) {
-    const gmlp_grouped_q* aq = &C.aq_col.q;
-    const float* a_post = C.a_post;
-    if (rec) {
-      if (mx) {
-        // cast by the activation-gradient pass above
-      } else {
-        const NvOut o = nv_out(W.a2q.q, false, true);
-        if (!L.check(launch_nvfp4_quant(W.a2, M, ffn, W.T, E, mask, true, false, true, C.a_pre, C.a_post, o, stream),
-                     "nvfp4 quantize rebuilt fc2 input"))
-          return L.st;
-        g_counts[CNT_NVQ]++;
-      }
-      aq = &W.a2q.q;
+    if (rec && !mx) {
+      const NvOut o = nv_out(W.a2q.q, false, true);
+      if (!L.check(launch_nvfp4_quant(W.a2, M, ffn, W.T, E, mask, true, false, true, C.a_pre, C.a_post, o, stream),
+                   "nvfp4 quantize rebuilt fc2 input"))
+        return L.st;
+      g_counts[CNT_NVQ]++;
     }
-    GemmArgs g = gemm_base(MODE_WGRAD, r, EPI_STORE, W.T, E);
-    g.M = M;
-    g.N = H;
-    g.K = ffn;
-    g.a = op_col(W.dyq.q, W.dyq.q.amax_post);
-    g.b = op_col(*aq, a_post);
-    g.c = A->dw2;
-    g.out_fp32 = A->wgrad_dtype;
-    set_nv(g, W.nv);
-    if (!L.check(launch_gemm(g, stream), "fc2 wgrad gemm")) return L.st;
-    g_counts[CNT_GEMM]++;
+    if (!defer && !fc2_wgrad(A, C, W, L, stream)) return L.st;
   }
   // 5. fc1 dgrad
   if (dgrad) {
@@ -829,19 +863,29 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     g_counts[CNT_GEMM]++;
   }
   // 6. fc1 wgrad
-  if (wgrad) {
-    GemmArgs g = gemm_base(MODE_WGRAD, r, EPI_STORE, W.T, E);
-    g.M = M;
-    g.N = F1;
-    g.K = H;
-    g.a = op_col(W.dhq.q, W.dhq.q.amax_post);
-    g.b = op_col(C.xq_col.q, C.xq_col.q.amax_post);
-    g.c = A->dw1;
-    g.out_fp32 = A->wgrad_dtype;
-    set_nv(g, W.nv);
-    if (!L.check(launch_gemm(g, stream), "fc1 wgrad gemm")) return L.st;
-    g_counts[CNT_GEMM]++;
-  }
+  if (wgrad && !defer && !fc1_wgrad(A, C, W, L, stream)) return L.st;
+  return ok();
+}
+
+gmlp_status gmlp_grouped_mlp_wgrad(const gmlp_bwd_args* A, hipStream_t stream) {
+  memset(g_counts, 0, sizeof(g_counts));
+  if (!A) return fail(GMLP_INVALID_ARG, "null args");
+  gmlp_status st = mlp_common_checks(A->M, A->E, A->H, A->ffn, A->activation, A->recipe);
+  if (st != GMLP_OK) return st;
+  if (!A->weight_requires_grad) return fail(GMLP_INVALID_ARG, "the deferred weight gradients need weight_requires_grad");
+  if (!A->m_splits || !A->dw1 || !A->dw2) return fail(GMLP_INVALID_ARG, "null pointer argument");
+  if ((st = check_wgrad_dtype(A->wgrad_dtype)) != GMLP_OK) return st;
+  Bump cb(const_cast<void*>(A->ctx));
+  FwdCtx C = carve_ctx(cb, A->M, A->E, A->H, A->ffn, A->activation, A->recipe, A->recompute != 0);
+  if (!A->ctx || A->ctx_bytes < cb.off) return fail(GMLP_WORKSPACE, "ctx too small: need %zu bytes", cb.off);
+  Bump wb(A->ws);
+  BwdWs W = carve_bwd_ws(wb, A->M, A->E, A->H, A->ffn, A->activation, A->recipe, A->recompute != 0);
+  if (!A->ws || A->ws_bytes < wb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", wb.off);
+  Launcher L{stream};
+  // the split tables are rebuilt from m_splits: only the operands come from the deferring call
+  if (!L.check(launch_scan(A->m_splits, A->E, A->M, W.T, stream), "scan")) return L.st;
+  g_counts[CNT_SCAN]++;
+  if (!fc2_wgrad(A, C, W, L, stream) || !fc1_wgrad(A, C, W, L, stream)) return L.st;
   return ok();
 }
 

@@ -132,3 +132,20 @@ def test_output_dtype_validation():
     args.weight_requires_grad, args.wgrad_dtype = 1, 9
     assert L.gmlp_grouped_mlp_backward(ctypes.byref(args), None) == 1
     assert "wgrad dtype" in g.last_error()
+
+
+def test_deferred_wgrad_validation():
+    """The deferred weight-gradient call checks its arguments like the backward, before any launch."""
+    L = g.lib()
+    args = g.BwdArgs()
+    args.E, args.M, args.H, args.ffn = 2, 64, 128, 128
+    args.recipe = g.recipe("mxfp8")
+    args.m_splits = args.dw1 = args.dw2 = 16
+    assert L.gmlp_grouped_mlp_wgrad(ctypes.byref(args), None) == 1
+    assert "weight_requires_grad" in g.last_error()
+    args.weight_requires_grad = 1
+    assert L.gmlp_grouped_mlp_wgrad(ctypes.byref(args), None) == 3          # no ctx / workspace
+    assert "ctx too small" in g.last_error()
+    args.wgrad_dtype = 4
+    assert L.gmlp_grouped_mlp_wgrad(ctypes.byref(args), None) == 1
+    assert "wgrad dtype" in g.last_error()

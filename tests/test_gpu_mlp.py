@@ -133,6 +133,41 @@ def test_backward_accumulates_weight_gradients_into_fp32_main_grad(kind, act):
         assert torch.equal(acc[k], plain[k]), k
 
 
+@pytest.mark.parametrize("kind,act,recompute", [("mxfp8", "swiglu", True), ("mxfp8", "srelu", False),
+                                                ("nvfp4", "srelu", True), ("nvfp4", "swiglu", False)])
+def test_deferred_wgrad_matches_one_backward_bitwise(kind, act, recompute):
+    """A backward with defer_wgrad leaves dw1, dw2 to a later grouped_mlp_wgrad call: dx and dprobs
+    as from one backward with two fewer GEMM launches; the later call (split scan + the two wgrad
+    GEMMs), made after other work on the stream, gives bitwise the same weight gradients, and
+    can be repeated, in fp32 or accumulated into an fp32 main_grad."""
+    wl = small_case([100, 0, 300, 41], 256, 256, activation=act, recipe=kind, seed=12, w_std=0.05)
+    d = _upload(wl)
+    rec = g.recipe(kind, wl.sign_mask)
+    w1q, w2q = g.weight_quantize(d["w1"], rec), g.weight_quantize(d["w2"], rec)
+    _, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], act, rec, recompute=recompute)
+    full = g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx)
+    full_counts = g.last_launch_counts()
+    part = g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx, defer_wgrad=True)
+    part_counts = g.last_launch_counts()
+    assert part["dw1"] is None and part["dw2"] is None
+    assert part_counts["gemm"] == full_counts["gemm"] - 2
+    # other work in between: a forward with buffers of its own
+    g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], act, rec, recompute=recompute)
+    late = g.grouped_mlp_wgrad(part["deferred"])
+    wg_counts = g.last_launch_counts()
+    assert wg_counts["gemm"] == 2 and wg_counts["scan"] == 1 and sum(wg_counts.values()) == 3
+    fp = g.grouped_mlp_wgrad(part["deferred"], wgrad_dtype=g.OUT_FP32)
+    main = {k: torch.full(tuple(full[k].shape), 0.5, dtype=torch.float32, device="cuda") for k in ("dw1", "dw2")}
+    acc = g.grouped_mlp_wgrad(part["deferred"], wgrad_dtype=g.OUT_FP32_ACCUMULATE, out=dict(main))
+    torch.cuda.synchronize()
+    for k in ("dx", "dprobs"):
+        assert torch.equal(part[k], full[k]), k
+    for k in ("dw1", "dw2"):
+        assert torch.equal(late[k].view(torch.int16), full[k].view(torch.int16)), k
+        assert torch.equal(acc[k], 0.5 + fp[k]), k
+        assert torch.equal(fp[k].to(torch.bfloat16).view(torch.int16), full[k].view(torch.int16)), k
+
+
 def test_tiny_config_forward():
     """2 experts, hidden 128, ffn 128, m_splits [64, 128], MXFP8 SwiGLU, forward only."""
     wl = make_workload("tiny")
