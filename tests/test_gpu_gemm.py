@@ -81,6 +81,33 @@ def test_gemm_wgrad(kind, splits, Na, Nb):
 
 
 @pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
+def test_gemm_fprop_more_tiles_than_workgroups(kind):
+    """287 tiles of 256 x 256 for one workgroup per CU: every workgroup takes a second tile and
+    the last round is short (ragged and empty experts).  Within the GEMM tolerance of the oracle
+    (bf16 and fp32 outputs), bitwise repeatable, and the bf16 output is the fp32 one rounded."""
+    splits, N, K = [5000, 0, 3000, 2240], 1792, 2048
+    M, E, mask = sum(splits), len(splits), 0x5A3C
+    print(f"gemm fprop {kind} splits={splits} N={N} K={K}", flush=True)
+    x = random_bf16((M, K), seed=31)
+    w = random_bf16((E, N, K), seed=32, std=1 / np.sqrt(K))
+    rec = g.recipe(kind, mask)
+    sd = dev_splits(splits)
+    aq = g.group_quantize(dev_bf16(x), sd, rec, True, False)
+    wq = g.weight_quantize(dev_bf16(w.reshape(E * N, K)).view(E, N, K), rec)
+    c = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wq, sd, M, N, K)
+    c2 = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wq, sd, M, N, K)
+    c32 = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wq, sd, M, N, K, out_dtype=g.OUT_FP32)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), c2.view(torch.int16)), "not repeatable"
+    ref = _fprop_ref(x, w, splits, kind, mask)
+    got = F.bf16_bits_to_f64(bits16(c)).reshape(M, N)
+    assert O.rel_fro(got, F.round_bf16(ref)) <= 1e-3
+    assert O.rel_fro(c32.cpu().double().numpy(), ref) <= 5e-5
+    # bf16 output = the fp32 output rounded (the same sum, converted once)
+    assert torch.equal(c32.to(torch.bfloat16).view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
 def test_gemm_wgrad_accumulates_into_fp32(kind):
     """WGRAD with OUT_FP32_ACCUMULATE adds the product to the fp32 tensor given, twice in a row:
     each result is bit for bit the fp32 sum of the previous contents and the plain fp32 output
