@@ -149,3 +149,22 @@ def test_deferred_wgrad_validation():
     args.wgrad_dtype = 4
     assert L.gmlp_grouped_mlp_wgrad(ctypes.byref(args), None) == 1
     assert "wgrad dtype" in g.last_error()
+
+
+def test_accumulating_gradients_need_the_callers_main_grads():
+    """The binding refuses OUT_FP32_ACCUMULATE without existing fp32 main_grads of the right shape
+    (host check, before any launch), in the backward and in the deferred weight-gradient call."""
+    import torch
+    E, M, H, ffn = 2, 64, 128, 128
+    rec = g.recipe("mxfp8")
+    ctx = g.MlpContext(torch.empty(0, dtype=torch.uint8), M, E, H, ffn, g.SWIGLU, rec, False, True, True)
+    dy = torch.zeros(M, H, dtype=torch.bfloat16)
+    splits = torch.tensor([M // 2, M // 2], dtype=torch.int32)
+    with pytest.raises(ValueError, match="main_grad"):
+        g.grouped_mlp_backward(dy, splits, None, None, None, ctx, wgrad_dtype=g.OUT_FP32_ACCUMULATE)
+    bad = {"dw1": torch.zeros(E, 2 * ffn, H, dtype=torch.bfloat16), "dw2": torch.zeros(E, H, ffn)}
+    with pytest.raises(ValueError, match="dw1 main_grad"):
+        g.grouped_mlp_backward(dy, splits, None, None, None, ctx, wgrad_dtype=g.OUT_FP32_ACCUMULATE, out=bad)
+    deferred = g.DeferredWgrad(splits, ctx, torch.empty(0, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="main_grad"):
+        g.grouped_mlp_wgrad(deferred, wgrad_dtype=g.OUT_FP32_ACCUMULATE)
