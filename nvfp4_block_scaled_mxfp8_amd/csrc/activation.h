@@ -1,5 +1,6 @@
-// Activations of the grouped MLP and their gradients, shared by the fc1 epilogue, the fused
-// activation-gradient cast and the fc2-input rebuild, so that all of them produce the same bits.
+// Activations of the grouped MLP and their gradients, shared by the passes that form the fc2
+// input from h (forward casts and amax), the activation-gradient passes and the fc2-input
+// rebuild of the backward, so that all of them produce the same bits.
 //
 // Sources: "GEMM + Swiglu fused Grouped MLP for MXFP8" (SwiGLU: silu(gate) * up over the
 // [gate | up] halves of the fc1 output, scaled by the token's routing probability);

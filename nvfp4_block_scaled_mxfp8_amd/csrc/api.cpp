@@ -325,8 +325,8 @@ BwdWs carve_bwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, c
     w.a2 = b.take<uint16_t>(M * ffn);
     w.a2q = carve_q(b, r, M, ffn, E, false, true, false);
   }
-  // dL/dp partials: per 256-column tile of the NVFP4 fused epilogue, per 128 features of the
-  // MXFP8 fused activation-gradient cast
+  // dL/dp partials: per 256-feature tile of the NVFP4 activation-gradient pass, per 64 features
+  // of the MXFP8 activation-gradient cast
   w.dprob_part = b.take<float>((size_t)ceil_div(ffn, 64) * M);
   // NVFP4 GEMM operands: A up to [padded tokens, max(H, F1)] (dy, dh row- or column-wise), B up to
   // the larger of the weights [E, H, F1] and a column-wise [max(H, ffn), padded tokens]
@@ -776,8 +776,8 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
   if (!quant(static_cast<const uint16_t*>(A->dy), H, W.dyq, true, wgrad)) return L.st;
   // 2-3. MXFP8: fc2 dgrad da = dy W2 (bf16, in the dh buffer), then one pass that forms dh from
   // da and h, casts it row- and column-wise, sums the dL/dp partials and (recomputing) rebuilds
-  // and casts the fc2 input.  NVFP4: the dgrad GEMM's fused epilogue writes bf16 dh, then dh
-  // is cast like any tensor.
+  // and casts the fc2 input.  NVFP4: the dgrad GEMM stores bf16 da, the activation-gradient
+  // pass writes bf16 dh (and the rebuilt fc2 input), then dh is cast like any tensor.
   if (mx) {
     uint16_t* da = W.dh;
     GemmArgs g = gemm_base(MODE_FPROP, r, EPI_STORE, W.T, E);

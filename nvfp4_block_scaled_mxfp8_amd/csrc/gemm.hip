@@ -1,14 +1,12 @@
-// Grouped GEMMs of the MoE MLP on CDNA4 matrix cores: bf16 / fp32 store epilogues and, for NVFP4,
-// the fc1 epilogue that also writes the activation (the MXFP8 activation and every activation
-// gradient run as memory-bound passes of their own, see quant.hip).
+// Grouped GEMMs of the MoE MLP on CDNA4 matrix cores.  Every GEMM stores its result as it is:
+// bf16 or fp32, or (weight gradients) added in fp32 to what the output holds.  The activation,
+// its gradient and dprob run as memory-bound passes of their own over the stored h and da
+// (quant.hip), unlike the pages' kernels, which fuse them into the fc1 and fc2-dgrad GEMMs.
 //
-// Sources: "GEMM + Swiglu fused Grouped MLP for MXFP8" (sequence diagram: the FC1
-// GLU kernel writes the bf16 pre-activation and the activation; the FC2 dGLU
-// kernel consumes dy, the saved pre-activation and the fc2 weight and emits the
-// fc1 grad and dprob; FC1 dgrad; wgrad grouped GEMMs) and "Reduce NVFP4
-// quantization work ..." (Description and commits: the accumulator is rounded
-// through the bf16 C dtype before the activation; the backward activation
-// kernel regenerates the fc2 input bit-exactly).
+// Sources: "GEMM + Swiglu fused Grouped MLP for MXFP8" (sequence diagram: the fc1 GEMM
+// with the bf16 pre-activation, the fc2 GEMM, the fc2 dgrad, the fc1 dgrad and the wgrad
+// grouped GEMMs) and "Reduce NVFP4 quantization work ..." (Description and commits: the
+// accumulator is rounded through the bf16 C dtype before the activation).
 //
 // Every GEMM here is C = A . B^T with both operands K-contiguous:
 //   FPROP  A = row-wise [rows of group g, K], B = expert g's [N, K]      (fc1, fc2, both dgrads)

@@ -125,7 +125,7 @@ struct GemmArgs {
   // outputs
   void* c;           // EPI_STORE: C (bf16 or fp32)
   int out_fp32;      // 0 bf16, 1 fp32, 2 fp32 added to C (WGRAD)
-  // fused epilogue operands
+  // EPI_DACT (NVFP4 fc2 dgrad): operands of the activation-gradient pass run after the GEMM
   int act;           // 0 SwiGLU, 1 SReLU
   int64_t ffn;       // EPI_DACT: ffn (width of da and a'); SwiGLU F1 = 2 ffn
   const float* probs;
@@ -133,7 +133,7 @@ struct GemmArgs {
   uint16_t* a_out;   // EPI_DACT: out a' (recompute) or null
   uint16_t* dh;      // EPI_DACT: out dh [M, F1]
   float* dprob_part; // EPI_DACT: [n_tiles, M]
-  int group_rows;    // tile rows per launch-order group (see make_ctx); set by launch_gemm
+  int group_rows;    // tile rows per launch-order group (see tile_ctx); set by the launcher
   // NVFP4: scratch for the operands expanded to bf16 (A: 2 x rows x contraction bytes, B: the
   // same for the weight or column-wise operand) and, for EPI_DACT, da [M, ffn] bf16
   uint8_t* xa;
