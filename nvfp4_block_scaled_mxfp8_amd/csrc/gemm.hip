@@ -335,8 +335,11 @@ __device__ __forceinline__ RunDma run_rsrc(const DmaConst& K, const DmaTile& t) 
   const uint64_t pb = (uint64_t)(uintptr_t)K.b + t.b_off;
   const uint64_t ps = (uint64_t)(uintptr_t)(K.s + t.s_off);
   auto word = [](uint32_t v) { return __builtin_amdgcn_readfirstlane((int)v); };   // uniform: scalar registers
-  r.ra.w = v4i{word((uint32_t)pa), word((uint32_t)(pa >> 32) & 0xFFFFu), word(rest(K.a_total, t.a_off)), (int)kRsrcWord3};
-  r.rb.w = v4i{word((uint32_t)pb), word((uint32_t)(pb >> 32) & 0xFFFFu), word(rest(K.b_total, t.b_off)), (int)kRsrcWord3};
+  // a band with no valid row (past a partial tile's rows or columns) reads nothing
+  const uint32_t na = (t.ab_bytes & 0xFFFFu) ? rest(K.a_total, t.a_off) : 0u;
+  const uint32_t nbb = (t.ab_bytes >> 16) ? rest(K.b_total, t.b_off) : 0u;
+  r.ra.w = v4i{word((uint32_t)pa), word((uint32_t)(pa >> 32) & 0xFFFFu), word(na), (int)kRsrcWord3};
+  r.rb.w = v4i{word((uint32_t)pb), word((uint32_t)(pb >> 32) & 0xFFFFu), word(nbb), (int)kRsrcWord3};
   r.rs.w = v4i{word((uint32_t)ps), word((uint32_t)(ps >> 32) & 0xFFFFu), word(rest(K.s_total, 4 * t.s_off)),
                (int)kRsrcWord3};
   return r;
