@@ -670,14 +670,16 @@ __global__ __launch_bounds__(256) void amax_finalize_kernel(SplitTables T, int G
 
 // ----------------------------------------------------------------------------- NVFP4 cast
 // One 16-value block with global scale S: writes 8 packed bytes (two words), returns the E4M3 code.
-//   s = fp32(fp32(b / 6) * S); q = E4M3(s); r = fp32(S / dec(q)) (0 if q == 0); c_i = E2M1(fp32(v_i * r))
+//   s = fp32(fp32(b / 6) * S); q = E4M3(s); r = min(fp32(S / dec(q)), FLT_MAX) (0 if q == 0);
+//   c_i = E2M1(fp32(v_i * r)).  r is clipped like S, so a zero element casts to zero even when S
+//   itself was clipped (S / dec(q) would overflow and 0 * inf is no number).
 __device__ __forceinline__ uint32_t nv_block(const float* v, float S, uint32_t& lo, uint32_t& hi) {
   float b = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) b = fmaxf(b, fabsf(v[i]));
   const float s = __fmul_rn(__fdiv_rn(b, 6.0f), S);
   const uint32_t code = cvt_e4m3(s);
-  const float r = (code == 0) ? 0.0f : __fdiv_rn(S, e4m3_decode_pos(code));
+  const float r = (code == 0) ? 0.0f : fminf(__fdiv_rn(S, e4m3_decode_pos(code)), kFltMax);
   float t[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) t[i] = __fmul_rn(v[i], r);
@@ -715,7 +717,7 @@ __device__ __forceinline__ uint32_t nv_half_block(const float* v, float S, uint3
   b = fmaxf(b, __shfl_xor(b, 1, 64));
   const float s = __fmul_rn(__fdiv_rn(b, 6.0f), S);
   const uint32_t code = cvt_e4m3(s);
-  const float r = (code == 0) ? 0.0f : __fdiv_rn(S, e4m3_decode_pos(code));
+  const float r = (code == 0) ? 0.0f : fminf(__fdiv_rn(S, e4m3_decode_pos(code)), kFltMax);
   float t[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) t[i] = __fmul_rn(v[i], r);

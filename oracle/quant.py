@@ -22,7 +22,7 @@ NVFP4 block of 16 values v with group amax A (pre-RHT amax for row-wise casts,
 post-RHT amax for column-wise casts), every step in fp32 (readings S5, S6):
   S = 2688 / A (A > 0; clipped to FLT_MAX), S = 1 when A == 0; 2688 = 6 * 448
   b = max|v_i|;  s = (b / 6) * S;  q = E4M3(s) (saturating)
-  r = S / dec(q)  (r = 0 when q == 0);  c_i = E2M1(v_i * r)
+  r = S / dec(q), clipped to FLT_MAX like S  (r = 0 when q == 0);  c_i = E2M1(v_i * r)
   dequantized value: dec(c_i) * dec(q) / S.
 
 Layouts (ours; the pages fix none):
@@ -156,7 +156,8 @@ def nvfp4_quantize_rows(v, amax):
     q = e4m3_encode(s)
     dq = e4m3_decode(q)
     with np.errstate(divide="ignore"):
-        rr = np.where(q == 0, 0.0, f32(S / np.where(q == 0, 1.0, dq)))
+        with np.errstate(over="ignore"):
+            rr = np.where(q == 0, 0.0, np.minimum(f32(S / np.where(q == 0, 1.0, dq)), FLT_MAX))
     c = e2m1_encode(f32(blk * rr[..., None]))
     return c.reshape(r, k), q
 

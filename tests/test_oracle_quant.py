@@ -135,6 +135,51 @@ def test_nvfp4_hand_worked_blocks():
         assert c[0].tolist() == blk["codes"], (c[0].tolist(), blk["codes"])
 
 
+def _nvfp4_block_alt(v, amax, s_order="ours", r_order="ours"):
+    """The NVFP4 block cast of one row with one step done in another order (planted mistakes for
+    the fixture test below; "ours" everywhere is the oracle's reading)."""
+    S = Q.nvfp4_global_scale(amax)
+    b = float(np.max(np.abs(v)))
+    s = {"ours": F.f32(F.f32(b / 6) * S), "exact": F.f32(b * S / 6), "bS/6": F.f32(F.f32(b * S) / 6),
+         "S/6": F.f32(b * F.f32(S / 6))}[s_order]
+    q = int(F.e4m3_encode(s))
+    d = float(F.e4m3_decode(q))
+    if q == 0:
+        return q, [int(c) for c in F.e2m1_encode(v * 0.0)]
+    x = {"ours": F.f32(v * F.f32(S / d)), "exact": v * S / d, "dec/S": F.f32(v / F.f32(d / S)),
+         "1/dec": F.f32(v * F.f32(S * F.f32(1 / d)))}[r_order]
+    return q, [int(c) for c in F.e2m1_encode(x)]
+
+
+def test_nvfp4_hand_worked_blocks_inexact_global_scale():
+    """Blocks at group amaxes 5, 7.25 and 13 (global scales 537.59998, 370.75861, 206.76923) worked
+    by hand with exact arithmetic: scale codes and nibbles, and S itself."""
+    blocks = _blocks("nvfp4_blocks_inexact.txt", 3)
+    assert len(blocks) == 8
+    for blk in blocks:
+        amax, S = float(blk["hdr"][0]), float(blk["hdr"][1])
+        assert Q.nvfp4_global_scale(amax) == S
+        v = F.bf16_bits_to_f64(_bf16(blk["vals"]))[None, :]
+        assert np.array_equal(v[0], np.array(blk["vals"])), "fixture values must be bf16"
+        c, q = Q.nvfp4_quantize_rows(v, amax)
+        assert int(q[0, 0]) == int(blk["hdr"][2], 16), (hex(int(q[0, 0])), blk["hdr"])
+        assert c[0].tolist() == blk["codes"], (c[0].tolist(), blk["codes"])
+        assert _nvfp4_block_alt(v[0], amax) == (int(q[0, 0]), c[0].tolist())
+
+
+@pytest.mark.parametrize("s_order,r_order", [("exact", "ours"), ("bS/6", "ours"), ("S/6", "ours"),
+                                             ("ours", "exact"), ("ours", "dec/S"), ("ours", "1/dec")])
+def test_nvfp4_inexact_blocks_catch_other_step_orders(s_order, r_order):
+    """Planted mistake: one fp32 step of the block cast in another order.  At least one hand-worked
+    block must then disagree with the fixture."""
+    diffs = 0
+    for blk in _blocks("nvfp4_blocks_inexact.txt", 3):
+        v = F.bf16_bits_to_f64(_bf16(blk["vals"]))
+        q, c = _nvfp4_block_alt(v, float(blk["hdr"][0]), s_order, r_order)
+        diffs += (q != int(blk["hdr"][2], 16)) or (c != blk["codes"])
+    assert diffs > 0
+
+
 def test_nvfp4_global_scale_edges():
     assert Q.nvfp4_global_scale(0.0) == 1.0
     assert Q.nvfp4_global_scale(6.0) == 448.0
@@ -174,6 +219,25 @@ def test_nvfp4_nearest_element():
                 best = np.flatnonzero(d == d.min())
                 want = best[0] if len(best) == 1 else [k for k in best if k % 2 == 0][0]
                 assert int(c[r, b * 16 + j]) & 7 == want
+
+
+def test_nvfp4_zero_elements_cast_to_signed_zero():
+    """A zero element encodes as +0 (nibble 0x0) and -0 as 0x8 at any global scale, including one
+    clipped to FLT_MAX (amax 1e-36), where S / dec(q) overflows for blocks below 6 / FLT_MAX and the
+    reading clips it the same way; every other element encodes a finite E2M1 value."""
+    rng = np.random.default_rng(9)
+    tiny = [2.0 ** -127, 2.0 ** -130, 2.0 ** -133, 1e-38, 3e-39]
+    for amax in (1e-36, 1e-30, 5.0, 1e30, 3e38):
+        v = np.zeros((64, 16))
+        v[:, 0] = rng.choice(tiny + [1e-3, 1.0, 100.0], size=64) * rng.choice([-1, 1], size=64)
+        v[:, 1] = rng.choice(tiny, size=64)
+        v[::2, 2:8] = -0.0
+        v = F.round_bf16(v)
+        c, q = Q.nvfp4_quantize_rows(v, amax)
+        zero = v == 0
+        assert np.all(c[zero & ~np.signbit(v)] == 0x0), amax
+        assert np.all(c[zero & np.signbit(v)] == 0x8), amax
+        assert np.all(np.isfinite(F.e2m1_decode(c))), amax
 
 
 def test_nvfp4_zero_group_and_dequant_error():
