@@ -187,3 +187,112 @@ def test_main_grad_accumulation_is_one_fp32_rounding():
     assert O.accumulate_main_grad(1.0, 2.0 ** -24 + 2.0 ** -40) == 1.0 + 2.0 ** -23
     # no bf16 step: 1 + 2^-20 survives (bf16 would make it 1)
     assert O.accumulate_main_grad(0.0, 1.0 + 2.0 ** -20) == 1.0 + 2.0 ** -20
+
+
+# ----------------------------------------------------------------------------- hand-worked one-token cases
+def _single_token_cases():
+    """Cases of tests/golden/mlp_single_token.txt as (header, inputs, expected outputs)."""
+    from conftest import read_golden
+    cases, cur = [], None
+    for line in read_golden("mlp_single_token.txt"):
+        p = line.split()
+        if p[0] == "case":
+            kv = dict(zip(p[3::2], p[4::2]))
+            cur = {"name": p[1], "act": p[2], "H": int(kv["H"]), "ffn": int(kv["ffn"]), "p": float(kv["p"]),
+                   "in": [], "out": []}
+            cases.append(cur)
+        else:
+            cur[p[0]].append((p[1], tuple(int(v) for v in p[2:-1]), float(p[-1])))
+    return cases
+
+
+def _run_single_token(case, skip_first_rounding=None):
+    """The oracle's forward + backward of one case.  skip_first_rounding = "forward" / "backward"
+    plants a mistake: that pass's first bf16 rounding (h, respectively da) is left out."""
+    H, ffn = case["H"], case["ffn"]
+    f1 = 2 * ffn if case["act"] == O.SWIGLU else ffn
+    t = {"x": np.zeros((1, H)), "w1": np.zeros((1, f1, H)), "w2": np.zeros((1, H, ffn)), "dy": np.zeros((1, H))}
+    for name, idx, v in case["in"]:
+        t[name][idx] = v
+    bits = {k: F.f64_to_bf16_bits(v) for k, v in t.items()}
+    for k, v in t.items():
+        assert np.array_equal(F.bf16_bits_to_f64(bits[k]), v), f"{k} must hold bf16 values"
+    real = O.round_bf16
+
+    def plant(phase):
+        calls = []
+
+        def rounding(x):
+            calls.append(1)
+            return np.asarray(x, np.float64) if (phase == skip_first_rounding and len(calls) == 1) else real(x)
+        O.round_bf16 = rounding
+
+    try:
+        plant("forward")
+        fwd = O.forward(bits["x"], [1], bits["w1"], bits["w2"], np.array([case["p"]], np.float32), case["act"],
+                        O.Recipe(O.MXFP8))
+        plant("backward")
+        bwd = O.backward(fwd, bits["dy"])
+    finally:
+        O.round_bf16 = real
+    got = {"y": F.round_bf16(fwd["y_f64"]), "dx": F.round_bf16(bwd["dx_f64"]), "dprob": bwd["dprob"],
+           "dw1": F.round_bf16(bwd["dw1_f64"]), "dw2": F.round_bf16(bwd["dw2_f64"])}
+    want = {k: np.zeros(v.shape) for k, v in got.items()}
+    for name, idx, v in case["out"]:
+        want[name][idx] = v
+    return got, want
+
+
+def _single_token_mismatches(**kw):
+    bad = []
+    for case in _single_token_cases():
+        got, want = _run_single_token(case, **kw)
+        bad += [(case["name"], k) for k in got if not np.array_equal(np.asarray(got[k], np.float64), want[k])]
+    return bad
+
+
+def test_single_token_hand_worked_cases():
+    """Every output of the one-token cases equals the hand derivation exactly."""
+    assert len(_single_token_cases()) == 3
+    assert _single_token_mismatches() == []
+
+
+@pytest.mark.parametrize("phase", ["forward", "backward"])
+def test_single_token_cases_catch_a_missing_bf16_rounding(phase):
+    """Planted mistake: h (forward) or da (backward) is used unrounded, where it feeds the activation
+    or its gradient in fp64.  (a and dh reach the quantizer as bf16 bit patterns, so the oracle
+    cannot skip their rounding; the GPU test of these cases pins those two on the kernels.)"""
+    bad = _single_token_mismatches(skip_first_rounding=phase)
+    assert bad, f"the first {phase} rounding left out, yet every hand-worked output still matches"
+    assert any(name == "srelu_rounding" for name, _ in bad)
+
+
+def test_single_token_cases_catch_prob_inside_the_activation(monkeypatch):
+    """Planted mistake: the prob scales h before the activation instead of the activation's value."""
+    real_fwd = O.act_forward
+
+    def planted(h, activation):
+        return real_fwd(h * 1.0625, activation) / 1.0625 if activation == O.SRELU else real_fwd(h, activation)
+
+    monkeypatch.setattr(O, "act_forward", planted)
+    assert _single_token_mismatches()
+
+
+def test_single_token_cases_catch_swapped_gate_and_up(monkeypatch):
+    """Planted mistake: SwiGLU takes the gate from the second half of h and the up from the first."""
+    real_fwd, real_bwd = O.act_forward, O.act_backward
+
+    def swap(h):
+        f = h.shape[1] // 2
+        return np.concatenate([h[:, f:], h[:, :f]], axis=1)
+
+    monkeypatch.setattr(O, "act_forward", lambda h, a: real_fwd(swap(h), a) if a == O.SWIGLU else real_fwd(h, a))
+
+    def bwd(h, da, p, a):
+        if a != O.SWIGLU:
+            return real_bwd(h, da, p, a)
+        dh, dp = real_bwd(swap(h), da, p, a)
+        return swap(dh), dp
+
+    monkeypatch.setattr(O, "act_backward", bwd)
+    assert ("swiglu_order", "dw1") in _single_token_mismatches()
