@@ -1,19 +1,20 @@
 """Throughput of the fused MoE grouped MLP on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config mid|nvfp4|zipf|large] [--cpu-sample-rows R]
+    python bench.py [--steps K] [--warmup W] [--config large|mid|nvfp4|zipf] [--recompute 0|1]
 
 One step = one forward + backward of the whole path (x group quantize, fc1 GEMM,
-SwiGLU * prob with the fc2-input cast, fc2 GEMM, dy group quantize, fc2 dgrad,
+activation * prob with the fc2-input cast, fc2 GEMM, dy group quantize, fc2 dgrad,
 activation gradient + dprob + dh casts, fc2 wgrad, fc1 dgrad, fc1 wgrad) over a
-synthetic workload; the default (mid) is 8 experts, hidden 4096, ffn 1536, 16384
-tokens routed top-2 = 32768 rows split by a uniform multinomial, MXFP8 SwiGLU.
-Inputs are resident in HBM before timing; weights are quantized once, outside
-the timed steps.
+synthetic workload.  The default is the largest one-GPU workload: 128 experts,
+hidden 7168, ffn 2048, 8192 tokens routed top-8 = 65536 rows with Dirichlet(0.5)
+expert counts, stacked weights, MXFP8 SwiGLU.  Inputs are resident in HBM before
+timing; weights are quantized once, outside the timed steps.
 
 Prints one JSON line: TFLOP/s of the step (6 M H (F1 + ffn) flops), the
-roofline of the dominant kernel (the fc1-dgrad-shaped grouped GEMM, timed live
-with HIP events on the stream it runs on), the group-quantize GB/s, and the CPU
-oracle timed on a bounded sample of the same workload.
+roofline of the dominant kernel (the fc1-dgrad-shaped grouped GEMM of the same
+workload, timed live with HIP events on the stream it runs on, the 256 MB MALL
+flushed before every launch), the group-quantize GB/s of x (flushed likewise),
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -33,14 +34,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="mid")
+    p.add_argument("--config", default="large")
     p.add_argument("--recompute", type=int, default=0)
     p.add_argument("--kernel-reps", type=int, default=20)
-    p.add_argument("--cpu-sample-rows", type=int, default=2560, help="rows per sampled expert for the oracle")
-    p.add_argument("--cpu-sample-experts", type=int, default=2)
+    p.add_argument("--cpu-sample-rows", type=int, default=0,
+                   help="rows per sampled expert for the oracle (0: the workload's default)")
+    p.add_argument("--cpu-sample-experts", type=int, default=0, help="largest experts sampled (0: default)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--traffic-probe", action="store_true",
-                   help="only launch the dominant GEMM and a 1 GiB device copy (for rocprofv3 --pmc runs)")
+                   help="only launch the dominant GEMM of --config and a 1 GiB device copy (rocprofv3 --pmc runs)")
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs of --traffic-probe (FETCH_SIZE, WRITE_SIZE) into "
                         "the traffic record used by the bench line; needs no GPU")
@@ -50,9 +52,17 @@ def parse():
 # HBM traffic of the dominant kernel comes from rocprofv3 counter runs of --traffic-probe
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for the 1 GiB copy); the
 # summary records the hash of the kernel sources it was taken with and is used only while they
-# are unchanged.
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "gemm_mx_fc1_dgrad_32768x4096x3072_traffic.json")
+# are unchanged.  One record per workload shape.
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def dominant_shape(cfg, splits):
+    """The fc1-dgrad-shaped grouped GEMM of a workload: C [M, H] = Q(dh) [M, F1] . Q(W1 along F1)^T."""
+    return {"E": cfg.experts, "M": int(sum(splits)), "N": cfg.hidden, "K": cfg.f1}
+
+
+def traffic_file(shape):
+    return os.path.join(PROFILES, "gemm_mx_fc1_dgrad_%dx%dx%d_traffic.json" % (shape["M"], shape["N"], shape["K"]))
 
 
 def kernel_source_hash():
@@ -65,9 +75,9 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(shape):
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(shape)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -76,46 +86,75 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def traffic_probe():
-    """The dominant GEMM (fc1-dgrad shape: C [32768, 4096] = Q(dh) [32768, 3072] Q(W1)^T, 8 experts
-    of 4096 rows) launched 3 times after a 1 GiB device-to-device copy launched twice."""
+def config_splits(cfg):
+    """The workload's expert counts alone (the same draw as the full workload)."""
+    from workloads import _streams, draw_splits
+    return draw_splits(cfg, _streams(0)["splits"])
+
+
+class DominantGemm:
+    """The dominant kernel's call: gmlp_grouped_gemm in the FPROP layout with the weight's dgrad
+    operand (W1 along F1) as B, on a quantized random dh, exactly as the fc1 dgrad of the step runs."""
+
+    def __init__(self, g, torch, rec, w1q, splits_dev, shape, dev):
+        E, M, N, K = shape["E"], shape["M"], shape["N"], shape["K"]
+        self.g, self.shape, self.rec, self.splits = g, shape, rec, splits_dev
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1)
+        dh = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
+        self.dhq = g.group_quantize(dh, splits_dev, rec, True, False)
+        del dh
+        self.wd = g.QTensor(w1q.kind, {"row_data": w1q.bufs["col_data"],
+                                       "row_scale_mfma": w1q.bufs.get("col_scale_mfma"),
+                                       "row_scale": w1q.bufs.get("col_scale"), "amax_pre": w1q.bufs.get("amax_pre"),
+                                       "row_bf16": w1q.bufs.get("col_bf16")})
+        self.ws = torch.empty(g.grouped_gemm_ws_bytes(g.GEMM_FPROP, rec, E, M, N, K), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.qa, self.qb = self.dhq.struct(), self.wd.struct()
+
+    def __call__(self):
+        g, sh = self.g, self.shape
+        st = g.lib().gmlp_grouped_gemm(g.GEMM_FPROP, self.rec, g.ctypes.byref(self.qa), g.ctypes.byref(self.qb),
+                                       g._p(self.splits), sh["E"], sh["M"], sh["N"], sh["K"], g._p(self.out),
+                                       g.OUT_BF16, g._p(self.ws), self.ws.numel(), g._stream())
+        assert st == 0, g.last_error()
+
+
+def traffic_probe(args):
+    """The dominant GEMM of the workload launched 3 times after a 1 GiB device-to-device copy launched
+    twice (the copy calibrates the counters).  Weights and dh are random (the traffic does not depend
+    on the values); the expert counts are the workload's."""
     import torch
     import nvfp4_block_scaled_mxfp8_amd as g
-    E, M, H, F1 = 8, 32768, 4096, 3072
+    from workloads import CONFIGS
+    cfg = CONFIGS[args.config]
+    splits = config_splits(cfg)
+    shape = dominant_shape(cfg, splits)
     dev = "cuda"
-    torch.manual_seed(0)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(2):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    rec = g.recipe("mxfp8")
-    splits = torch.full((E,), M // E, dtype=torch.int32, device=dev)
-    w1 = (torch.randn((E, F1, H), device=dev) * 0.02).to(torch.bfloat16)
+    rec = g.recipe(cfg.recipe)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    w1 = (torch.randn((cfg.experts, cfg.f1, cfg.hidden), device=dev, generator=gen) * cfg.w1_std).to(torch.bfloat16)
     w1q = g.weight_quantize(w1, rec)
-    dh = torch.randn((M, F1), device=dev).to(torch.bfloat16)
-    dhq = g.group_quantize(dh, splits, rec, True, False)
-    wd = g.QTensor(w1q.kind, {"row_data": w1q.bufs["col_data"], "row_scale_mfma": w1q.bufs.get("col_scale_mfma"),
-                              "row_scale": w1q.bufs.get("col_scale"), "amax_pre": w1q.bufs.get("amax_pre")})
-    gws = g.quant_workspace(E, dev)
-    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    del w1
+    call = DominantGemm(g, torch, rec, w1q, torch.from_numpy(splits.astype(np.int32)).to(dev), shape, dev)
     torch.cuda.synchronize()
     for _ in range(3):
-        st = g.lib().gmlp_grouped_gemm(g.GEMM_FPROP, rec, g.ctypes.byref(dhq.struct()), g.ctypes.byref(wd.struct()),
-                                       g._p(splits), E, M, H, F1, g._p(out), g.OUT_BF16, g._p(gws), gws.numel(),
-                                       g._stream())
-        assert st == 0, g.last_error()
+        call()
     torch.cuda.synchronize()
-    print("traffic probe done", flush=True)
+    print("traffic probe done: %s" % shape, flush=True)
 
 
-TRAFFIC_COMMANDS = [
-    "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && rocprofv3 --pmc FETCH_SIZE --output-format csv "
-    "-d gpurun_out/traffic/fetch -o p -- python3 bench.py --traffic-probe",
-    "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && rocprofv3 --pmc WRITE_SIZE --output-format csv "
-    "-d gpurun_out/traffic/write -o p -- python3 bench.py --traffic-probe",
-]
+def traffic_commands(config):
+    return ["cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && rocprofv3 --pmc %s --output-format csv "
+            "-d gpurun_out/traffic/%s -o p -- python3 bench.py --config %s --traffic-probe" % (c, d, config)
+            for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
 
 
 def _counter_rows(d, counter):
@@ -132,9 +171,12 @@ def _counter_rows(d, counter):
     return [(k, v) for _, k, v in rows]
 
 
-def write_traffic(fetch_dir, write_dir):
+def write_traffic(args, fetch_dir, write_dir):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the probe's GEMM, each scaled by what the counter
     reads for the 1 GiB copy, stored with the hash of the kernel sources they were taken with."""
+    from workloads import CONFIGS
+    cfg = CONFIGS[args.config]
+    shape = dominant_shape(cfg, config_splits(cfg))
     fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
     write = _counter_rows(write_dir, "WRITE_SIZE")
     pick = lambda rows, key: [v for k, v in rows if key in k]
@@ -144,30 +186,53 @@ def write_traffic(fetch_dir, write_dir):
     gib_kib = float(1 << 20)
     fscale, wscale = gib_kib / cf[-1], gib_kib / cw[-1]
     fb, wb = gf[-1] * 1024 * fscale, gw[-1] * 1024 * wscale
-    M, H, F1, E = 32768, 4096, 3072, 8
-    rec = {"kernel": "gmlp::gemm_mx_kernel<0, 0> (fc1-dgrad shape: M 32768, N 4096, K 3072, 8 experts)",
-           "source_sha256": kernel_source_hash(),
+    E, M, N, K = shape["E"], shape["M"], shape["N"], shape["K"]
+    rec = {"kernel": "gmlp::gemm_mx_kernel<0, 0, 0> (fc1-dgrad shape: M %d, N %d, K %d, %d experts)" % (M, N, K, E),
+           "workload": args.config, "source_sha256": kernel_source_hash(),
            "fetch_kib_per_dispatch": gf, "write_kib_per_dispatch": gw,
            "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_scale": fscale, "write_scale": wscale,
            "bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
-           "algorithmic_bytes": M * F1 + H * F1 * E + 4 * (F1 // 128) * M + 4 * (F1 // 128) * H * E + 2 * M * H,
-           "commands": TRAFFIC_COMMANDS}
-    with open(TRAFFIC_FILE, "w") as f:
+           "algorithmic_bytes": gemm_algorithmic_bytes(shape), "commands": traffic_commands(args.config)}
+    with open(traffic_file(shape), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps({k: rec[k] for k in ("fetch_bytes", "write_bytes", "bytes_per_launch", "algorithmic_bytes")}))
+
+
+def gemm_algorithmic_bytes(shape):
+    """E4M3 operands read once (A [M, K], B [E, N, K]), their MFMA scale words (one u32 per row and
+    128 contraction elements) and the bf16 output written once."""
+    E, M, N, K = shape["E"], shape["M"], shape["N"], shape["K"]
+    return M * K + E * N * K + 4 * (K // 128) * (M + E * N) + 2 * M * N
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def timed_flushed(torch, fn, reps, flush):
+    """Mean device time of fn (HIP events on torch's current stream, which is the stream the library
+    launches on), with a 512 MB write between launches so that the 256 MB MALL holds none of fn's
+    operands when it starts."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        flush.fill_(i & 0x7F)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+CPU_SAMPLE = {"large": (1, 2048), "mid": (2, 2560), "zipf": (2, 2560), "nvfp4": (1, 1536)}
+
+
 def main():
     args = parse()
     if args.traffic_probe:
-        traffic_probe()
+        traffic_probe(args)
         return
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(args, *args.write_traffic)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -204,6 +269,7 @@ def main():
     act = cfg.activation
     w1q = g.weight_quantize(w1, rec)
     w2q = g.weight_quantize(w2, rec)
+    del w1, w2
     sizes = g.query_sizes(M, E, H, ffn, act, rec, bool(args.recompute))
     ws = torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
     ctxbuf = torch.empty(sizes["ctx_bytes"], dtype=torch.uint8, device=dev)
@@ -237,48 +303,34 @@ def main():
     flops = 6.0 * M * H * (F1 + ffn)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"step: {ms:.3f} ms  {tflops:.1f} TFLOP/s  (wall {wall / args.steps * 1e3:.3f} ms/step)")
+    del ws, ctxbuf, ctx_holder["ctx"]
 
     # ------------------------------------------------------------------ dominant kernel: fc1-dgrad-shaped GEMM
-    # C [M, H] = Q(dh)[M, F1] . Q(W1 along F1)[E][H, F1]^T -- one of the three largest GEMMs of the step
-    dh = torch.randn((M, F1), device=dev).to(torch.bfloat16)
-    dhq = g.group_quantize(dh, splits, rec, True, False)
-    w1_dgrad = g.QTensor(w1q.kind, {"row_data": w1q.bufs["col_data"], "row_scale_mfma": w1q.bufs.get("col_scale_mfma"),
-                                    "row_scale": w1q.bufs.get("col_scale"), "amax_pre": w1q.bufs.get("amax_pre")})
-    gws = torch.empty(g.grouped_gemm_ws_bytes(g.GEMM_FPROP, rec, E, M, H, F1), dtype=torch.uint8, device=dev)
-    gout = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    shape = dominant_shape(cfg, wl.m_splits)
+    call = DominantGemm(g, torch, rec, w1q, splits, shape, dev)
     for _ in range(3):
-        g.lib().gmlp_grouped_gemm(g.GEMM_FPROP, rec, g.ctypes.byref(dhq.struct()), g.ctypes.byref(w1_dgrad.struct()),
-                                  g._p(splits), E, M, H, F1, g._p(gout), g.OUT_BF16, g._p(gws), gws.numel(),
-                                  g._stream())
+        call()
     torch.cuda.synchronize()
-    qa, qb = dhq.struct(), w1_dgrad.struct()
-    ev0.record()
-    for _ in range(args.kernel_reps):
-        st = g.lib().gmlp_grouped_gemm(g.GEMM_FPROP, rec, g.ctypes.byref(qa), g.ctypes.byref(qb), g._p(splits), E, M,
-                                       H, F1, g._p(gout), g.OUT_BF16, g._p(gws), gws.numel(), g._stream())
-        assert st == 0, g.last_error()
-    ev1.record()
-    torch.cuda.synchronize()
-    k_ms = ev0.elapsed_time(ev1) / args.kernel_reps
+    k_ms = timed_flushed(torch, call, args.kernel_reps, flush)
     k_flops = 2.0 * M * F1 * H
     k_tflops = k_flops / (k_ms * 1e-3) / 1e12
     peak = MXFP8_PEAK_TFLOPS if kind == "mxfp8" else BF16_PEAK_TFLOPS
     log(f"fc1-dgrad GEMM: {k_ms:.3f} ms  {k_tflops:.1f} TFLOP/s  ({100 * k_tflops / peak:.1f}% of {peak:.0f})")
+    del call
 
     # ------------------------------------------------------------------ group quantize GB/s (x, row + column-wise)
     qout = g.alloc_grouped_q(rec, M, H, E, True, True, dev)
+    qws = g.quant_workspace(E, dev)
+    quant = lambda: g.group_quantize(x, splits, rec, True, True, out=qout, ws=qws)
     for _ in range(3):
-        g.group_quantize(x, splits, rec, True, True, out=qout, ws=gws)
+        quant()
     torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.kernel_reps):
-        g.group_quantize(x, splits, rec, True, True, out=qout, ws=gws)
-    ev1.record()
-    torch.cuda.synchronize()
-    q_ms = ev0.elapsed_time(ev1) / args.kernel_reps
+    q_ms = timed_flushed(torch, quant, args.kernel_reps, flush)
     q_bytes = (2 + 1 + 1 + 2.0 / 32) * M * H if kind == "mxfp8" else (2 + 0.5 + 1 / 16 + 0.5 + 1 / 16) * M * H
     q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     log(f"group quantize x: {q_ms * 1e3:.1f} us  {q_gbs:.0f} GB/s ({100 * q_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+    del flush, qout
 
     # ------------------------------------------------------------------ CPU oracle on a bounded sample
     cpu = None
@@ -303,8 +355,8 @@ def main():
                    "flops_per_step": flops, "pct_of_mxfp8_peak": round(100 * tflops / MXFP8_PEAK_TFLOPS, 2)},
         "roofline": {"kernel": "grouped GEMM, fc1-dgrad shape (M=%d, N=%d, K=%d, %d experts)" % (M, H, F1, E),
                      "bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(k_tflops / peak, 4), "traffic": measured_traffic(),
-                     "ms_per_launch": round(k_ms, 4)},
+                     "frac": round(k_tflops / peak, 4), "traffic": measured_traffic(shape),
+                     "algorithmic_bytes": gemm_algorithmic_bytes(shape), "ms_per_launch": round(k_ms, 4)},
         "quantize": {"kernel": "MXFP8 group quantize of x, row + column-wise" if kind == "mxfp8" else
                      "NVFP4 group quantize of x (amax + row + column-wise RHT)",
                      "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -316,7 +368,7 @@ def main():
 
 
 def cpu_baseline(wl, args):
-    """The oracle (numpy fp64) on a bounded sample: the first R rows of the first few experts, full
+    """The oracle (numpy fp64) on a bounded sample: the first R rows of the largest experts, full
     hidden / ffn, forward + backward, weights pre-quantized outside the timed region."""
     from oracle import mlp as O
     from workloads import expert_weights
@@ -326,20 +378,23 @@ def cpu_baseline(wl, args):
     except Exception:
         threads = os.cpu_count()
     cfg = wl.config
-    ne = min(args.cpu_sample_experts, cfg.experts)
+    ne_def, rows_def = CPU_SAMPLE.get(cfg.name, (1, 1024))
+    ne = min(args.cpu_sample_experts or ne_def, cfg.experts)
+    nrows = args.cpu_sample_rows or rows_def
+    experts = sorted(sorted(range(cfg.experts), key=lambda e: (-int(wl.m_splits[e]), e))[:ne])
     off = np.concatenate([[0], np.cumsum(wl.m_splits)])
     rows, splits = [], []
-    for e in range(ne):
-        r = min(args.cpu_sample_rows, int(wl.m_splits[e]))
+    for e in experts:
+        r = min(nrows, int(wl.m_splits[e]))
         rows.append(np.arange(off[e], off[e] + r))
         splits.append(r)
     idx = np.concatenate(rows)
     rec = O.Recipe(cfg.recipe, wl.sign_mask)
-    w1, w2 = expert_weights(cfg, 0, range(ne))
+    w1, w2 = expert_weights(cfg, 0, experts)
     t = time.perf_counter()
     wq1 = O.quantize_weight(w1, rec)
     wq2 = O.quantize_weight(w2, rec)
-    log(f"cpu baseline: weights of {ne} experts quantized in {time.perf_counter() - t:.1f}s (untimed)")
+    log(f"cpu baseline: weights of experts {experts} quantized in {time.perf_counter() - t:.1f}s (untimed)")
     t = time.perf_counter()
     fwd = O.forward(wl.x[idx], splits, w1, w2, wl.probs[idx], cfg.activation, rec, wq1=wq1, wq2=wq2)
     O.backward(fwd, wl.dy[idx])
@@ -348,8 +403,8 @@ def cpu_baseline(wl, args):
     flops = 6.0 * m * cfg.hidden * (cfg.f1 + cfg.ffn)
     log(f"cpu baseline: {m} rows fwd+bwd in {dt:.1f}s = {flops / dt / 1e12:.4f} TFLOP/s on {threads} threads")
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{m} rows ({splits} from the first {ne} experts), hidden {cfg.hidden}, ffn {cfg.ffn}, "
-                      f"forward + backward, {dt:.1f} s"}
+            "sample": f"{m} rows (the first {splits} rows of experts {experts}, the largest), hidden {cfg.hidden}, "
+                      f"ffn {cfg.ffn}, forward + backward, {dt:.1f} s"}
 
 
 if __name__ == "__main__":

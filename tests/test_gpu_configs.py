@@ -27,11 +27,13 @@ from oracle import formats as F
 from oracle import mlp as O
 from oracle import quant as Q
 from oracle import rht as R
-from workloads import CONFIGS, expert_weights, iter_expert_weights, make_workload
+from workloads import CONFIGS, expert_weights, iter_expert_weights, make_workload, random_bf16
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2              # end-to-end relative Frobenius error (fused output and gradients)
 ROW_TOL = 1e-2          # sampled rows / entries of MXFP8 (fp32 vs fp64 accumulation only)
+GEMM_TOL = 1e-3         # grouped GEMM on identical quantized operands vs the fp64 product rounded to bf16
+LARGE_WGRAD_A_SEED = 777
 
 _STATE = {}
 
@@ -94,8 +96,20 @@ def state(name):
         del ctx
         print(f"{name}: forward + backward done (recompute={recompute})", flush=True)
     xq = g.group_quantize(x, splits, rec, True, True)
+    wgrad = {}
+    if name == "large":
+        # whole-output check of an fc1-wgrad-shaped GEMM (A [M, F1] with x, contraction over each
+        # expert's tokens) on the three largest experts, in the launch shape of the step
+        order = sorted(range(E), key=lambda e: (-int(wl.m_splits[e]), e))[:3]
+        a_bits = random_bf16((M, F1), seed=LARGE_WGRAD_A_SEED)
+        aq = g.group_quantize(dev_bf16(a_bits), splits, rec, False, True)
+        c = g.grouped_gemm(g.GEMM_WGRAD, rec, aq, xq, splits, M, F1, H)
+        torch.cuda.synchronize()
+        wgrad = {"experts": order, "a_bits": a_bits, "c": {e: bits16(c[e]) for e in order}}
+        del aq, c
+        print(f"{name}: fc1-shaped WGRAD done; checking experts {order}", flush=True)
     torch.cuda.synchronize()
-    _STATE.update(name=name, wl=wl, cfg=cfg, E=E, H=H, ffn=ffn, F1=F1, M=M, runs=runs, rec=rec,
+    _STATE.update(wgrad=wgrad, name=name, wl=wl, cfg=cfg, E=E, H=H, ffn=ffn, F1=F1, M=M, runs=runs, rec=rec,
                   off=np.concatenate([[0], np.cumsum(wl.m_splits)]).astype(np.int64),
                   xq={k: u8(v) if k not in ("amax_pre", "amax_post") else f32bits(v) for k, v in xq.bufs.items()
                       if k in ("row_data", "row_scale", "col_data", "col_scale", "amax_pre", "amax_post")},
@@ -195,6 +209,12 @@ def _by_size(wl):
     return order[0], order[-1]
 
 
+def _median_expert(wl):
+    nz = [e for e in range(len(wl.m_splits)) if wl.m_splits[e] > 0]
+    order = sorted(nz, key=lambda e: (int(wl.m_splits[e]), e))
+    return order[len(order) // 2]
+
+
 # ----------------------------------------------------------------------------- NVFP4 + RHT, SReLU
 def test_nvfp4_recompute_on_off_bitwise():
     s = state("nvfp4")
@@ -273,3 +293,29 @@ def test_large_largest_expert_sampled():
     _, big = _by_size(s["wl"])
     _mx_x_casts(s, big)
     _sampled_rows(s, big)
+
+
+def test_large_median_expert_matches_oracle():
+    """The median-size non-empty expert, whole: y, dx, dprob and both weight gradients."""
+    s = state("large")
+    e = _median_expert(s["wl"])
+    _mx_x_casts(s, e)
+    _expert_full(s, e)
+
+
+@pytest.mark.parametrize("rank", [0, 1, 2])
+def test_large_fc1_wgrad_largest_experts_whole(rank):
+    """Every element of the rank-th largest expert's [F1, H] = [4096, 7168] slice of an
+    fc1-wgrad-shaped grouped GEMM against the oracle's fp64 product of the column-wise operands."""
+    s = state("large")
+    wl, w = s["wl"], s["wgrad"]
+    e = w["experts"][rank]
+    o, m = int(s["off"][e]), int(wl.m_splits[e])
+    print(f"large: WGRAD of expert {e} over {m} tokens", flush=True)
+    rec = O.Recipe("mxfp8")
+    _, ad = O.quantize_activation(w["a_bits"][o:o + m], [m], rec, row=False, col=True)
+    _, xd = O.quantize_activation(wl.x[o:o + m], [m], rec, row=False, col=True)
+    ref = ad["col"][0] @ xd["col"][0].T
+    err = O.rel_fro(F.bf16_bits_to_f64(w["c"][e]).reshape(ref.shape), F.round_bf16(ref))
+    print(f"large: expert {e} WGRAD relative Frobenius error {err:.2e}", flush=True)
+    assert err <= GEMM_TOL

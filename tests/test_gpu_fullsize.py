@@ -16,10 +16,12 @@ from gpu_util import assert_bytes_equal, bits16, dev_bf16, dev_f32, dev_splits, 
 from oracle import formats as F
 from oracle import mlp as O
 from oracle import quant as Q
-from workloads import CONFIGS, make_workload
+from workloads import CONFIGS, make_workload, random_bf16
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2          # relative Frobenius error over the sampled values (fp32 vs fp64 accumulation)
+GEMM_TOL = 1e-3     # grouped GEMM on identical quantized operands vs the fp64 product rounded to bf16
+WGRAD_A_SEED = 4242
 
 
 @pytest.fixture(scope="module")
@@ -38,8 +40,16 @@ def run():
     y, ctx = g.grouped_mlp_forward(x, splits, w1q, w2q, probs, cfg.activation, rec, recompute=False)
     out = g.grouped_mlp_backward(dy, splits, w1q, w2q, probs, ctx)
     xq = g.group_quantize(x, splits, rec, True, True)
+    # whole-output GEMM checks in the launch shapes of the step: fc1 FPROP (x . W1^T, 7 rounds of
+    # 256 workgroups) and a WGRAD of the fc1-wgrad shape (A [M, F1] with x, contraction over tokens)
+    c_fprop = g.grouped_gemm(g.GEMM_FPROP, rec, xq, w1q, splits, M, F1, H)
+    a_bits = random_bf16((M, F1), seed=WGRAD_A_SEED)
+    aq = g.group_quantize(dev_bf16(a_bits), splits, rec, False, True)
+    c_wgrad = g.grouped_gemm(g.GEMM_WGRAD, rec, aq, xq, splits, M, F1, H)
     torch.cuda.synchronize()
-    r = {"wl": wl, "E": E, "H": H, "ffn": ffn, "F1": F1, "M": M,
+    print("full-size mid workload: fused step and the two GEMMs done", flush=True)
+    r = {"wl": wl, "E": E, "H": H, "ffn": ffn, "F1": F1, "M": M, "a_bits": a_bits, "wq": {},
+         "c_fprop": bits16(c_fprop).reshape(M, F1), "c_wgrad": bits16(c_wgrad).reshape(E, F1, H),
          "off": np.concatenate([[0], np.cumsum(wl.m_splits)]).astype(np.int64),
          "w1_row": u8(w1q.bufs["row_data"]), "w2_row": u8(w2q.bufs["row_data"]),
          "w1_col": u8(w1q.bufs["col_data"]), "xq_row": u8(xq.bufs["row_data"]), "xq_col": u8(xq.bufs["col_data"]),
@@ -50,12 +60,15 @@ def run():
 
 
 def _expert(r, e):
-    """Oracle-quantized weights of expert e (codes and dequantized values)."""
-    wl = r["wl"]
-    rec = O.Recipe("mxfp8")
-    q1, d1 = O.quantize_weight(wl.w1[e:e + 1], rec)
-    q2, d2 = O.quantize_weight(wl.w2[e:e + 1], rec)
-    return q1, q2, {"row": d1["row"][0], "colT": d1["colT"][0]}, {"row": d2["row"][0], "colT": d2["colT"][0]}
+    """Oracle-quantized weights of expert e (codes and dequantized values), computed once."""
+    if e not in r["wq"]:
+        wl = r["wl"]
+        rec = O.Recipe("mxfp8")
+        q1, d1 = O.quantize_weight(wl.w1[e:e + 1], rec)
+        q2, d2 = O.quantize_weight(wl.w2[e:e + 1], rec)
+        r["wq"][e] = (q1, q2, {"row": d1["row"][0], "colT": d1["colT"][0]},
+                      {"row": d2["row"][0], "colT": d2["colT"][0]})
+    return r["wq"][e]
 
 
 def _rows(r, e):
@@ -126,3 +139,37 @@ def test_fullsize_sampled_weight_gradients(run, e):
     for got, ref in ((got1, ref1), (got2, ref2)):
         scale = np.sqrt(np.mean(ref * ref))
         assert np.all(np.abs(got - ref) <= 2.0 ** -6 * np.abs(ref) + 1e-2 * scale), (got, ref)
+
+
+@pytest.mark.parametrize("e", range(8))
+def test_fullsize_fc1_fprop_whole_output(run, e):
+    """Every element of expert e's rows of h = Q(x) Q(W1)^T from gmlp_grouped_gemm (the fc1 launch of
+    the step: 8 experts of ~4096 rows, 12 x 128 tile pairs per expert, 7 rounds of 256 workgroups)
+    against the fp64 product of the oracle's dequantized operands, rounded to bf16."""
+    r = run
+    wl = r["wl"]
+    o, m = int(r["off"][e]), int(wl.m_splits[e])
+    _, _, d1, _ = _expert(r, e)
+    print(f"expert {e}: fc1 FPROP, {m} rows", flush=True)
+    xd = Q.mxfp8_dequant_rows(*Q.mxfp8_quantize_rows(F.bf16_bits_to_f64(wl.x[o:o + m])))
+    ref = xd @ d1["row"].T
+    err = O.rel_fro(F.bf16_bits_to_f64(r["c_fprop"][o:o + m]), F.round_bf16(ref))
+    print(f"expert {e}: fc1 FPROP relative Frobenius error {err:.2e}", flush=True)
+    assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("e", range(8))
+def test_fullsize_fc1_wgrad_whole_output(run, e):
+    """Every element of expert e's [F1, H] slice of Qc(A)^T Qc(x) (contraction over the expert's
+    tokens, column-wise operands zero padded to 128 tokens) against the oracle's fp64 product."""
+    r = run
+    wl = r["wl"]
+    o, m = int(r["off"][e]), int(wl.m_splits[e])
+    print(f"expert {e}: fc1-shaped WGRAD over {m} tokens", flush=True)
+    rec = O.Recipe("mxfp8")
+    _, ad = O.quantize_activation(r["a_bits"][o:o + m], [m], rec, row=False, col=True)
+    _, xd = O.quantize_activation(wl.x[o:o + m], [m], rec, row=False, col=True)
+    ref = ad["col"][0] @ xd["col"][0].T
+    err = O.rel_fro(F.bf16_bits_to_f64(r["c_wgrad"][e]), F.round_bf16(ref))
+    print(f"expert {e}: WGRAD relative Frobenius error {err:.2e}", flush=True)
+    assert err <= GEMM_TOL
