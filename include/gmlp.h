@@ -172,6 +172,19 @@ gmlp_status gmlp_group_quantize(const void* x, int64_t M, int64_t K, const int32
                                 const gmlp_grouped_q* out, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): gmlp_group_quantize with no workspace argument.  Its
+ * workspace (split tables, NVFP4 amax slots) is a fixed 288 KiB device array of the library, one
+ * copy per GPU, held until the process ends; the call allocates nothing.  1 <= G <= 1024, else
+ * GMLP_UNSUPPORTED and nothing is enqueued.  Every call rewrites that workspace from scratch
+ * (no state carries over between calls); calls that overlap on one GPU (unordered streams)
+ * share it and race.  The first call on a device looks up the array's address on that device
+ * (hipGetSymbolAddress, with the device current); make it outside graph capture.  Arguments,
+ * outputs and errors otherwise as gmlp_group_quantize. */
+gmlp_status gmlp_group_quantize_noalloc(const void* x, int64_t M, int64_t K, const int32_t* m_splits,
+                                        int32_t G, gmlp_recipe recipe, int32_t want_row, int32_t want_col,
+                                        const gmlp_grouped_q* out, hipStream_t stream);
+
 /* Per-group pre-RHT amax (max |x| over the group's rows) and post-RHT amax (max
  * |bf16(H S x)| over every 16-token block of every column of the group, padded
  * with zeros), both in one read of x [NV, Changes: nvfp4_group_hadamard_amax].

@@ -6,7 +6,7 @@ memory and supplies the stream.  The library must be built (python -m
 nvfp4_block_scaled_mxfp8_amd.build); nothing here falls back to another
 implementation when it is missing.
 
-Names follow the C ABI: group_quantize, group_hadamard_amax,
+Names follow the C ABI: group_quantize (and group_quantize_noalloc), group_hadamard_amax,
 group_quantize_with_amax, weight_quantize, grouped_gemm, grouped_mlp_forward,
 grouped_mlp_backward.
 """
@@ -87,6 +87,9 @@ _SIGS = {
                                            ctypes.c_int32, Recipe, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.POINTER(GroupedQ), ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p]),
+    "gmlp_group_quantize_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                   ctypes.c_void_p, ctypes.c_int32, Recipe, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.POINTER(GroupedQ), ctypes.c_void_p]),
     "gmlp_group_hadamard_amax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                                 ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -244,6 +247,19 @@ def group_quantize(x, m_splits, rec, want_row=True, want_col=True, out=None, ws=
     q = out.struct()
     _check(lib().gmlp_group_quantize(_p(x), M, K, _p(m_splits), G, rec, int(want_row), int(want_col),
                                      ctypes.byref(q), _p(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+def group_quantize_noalloc(x, m_splits, rec, want_row=True, want_col=True, out=None):
+    """group_quantize with the library's fixed device workspace (no workspace argument; at most
+    1024 groups).  out must be given by callers that cannot allocate."""
+    x = _bits(x)
+    M, K = x.shape
+    G = m_splits.numel()
+    out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
+    q = out.struct()
+    _check(lib().gmlp_group_quantize_noalloc(_p(x), M, K, _p(m_splits), G, rec, int(want_row), int(want_col),
+                                             ctypes.byref(q), _stream(x.device)))
     return out
 
 

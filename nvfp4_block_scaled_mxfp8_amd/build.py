@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgmlp.so")
-SOURCES = ["quant.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "static_ws.hip", "api.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

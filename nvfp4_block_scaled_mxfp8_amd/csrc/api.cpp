@@ -9,6 +9,7 @@
 // that amax and runs no second Hadamard-amax pass.
 #include "gmlp.h"
 #include "kernels.h"
+#include "planner.h"
 
 #include <hip/hip_runtime.h>
 
@@ -357,6 +358,34 @@ gmlp_status mlp_common_checks(int64_t M, int E, int64_t H, int64_t ffn, int act,
 
 }  // namespace
 
+namespace gmlp {
+
+gmlp_status set_error(gmlp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+size_t group_quantize_ws_need(int G) {
+  Bump b(nullptr);
+  carve_tables(b, G);
+  return b.off;
+}
+
+gmlp_status group_quantize_on(const void* x, int64_t M, int64_t K, const int32_t* m_splits, int32_t G,
+                              gmlp_recipe recipe, int32_t want_row, int32_t want_col, const gmlp_grouped_q* out,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  memset(g_counts, 0, sizeof(g_counts));
+  return quant_core(x, M, K, m_splits, G, recipe, want_row != 0, want_col != 0, out, ws, ws_bytes, stream,
+                    !is_mx(recipe));
+}
+
+}  // namespace gmlp
+
 // =============================================================================== C ABI
 extern "C" {
 
@@ -416,9 +445,7 @@ gmlp_status gmlp_last_launch_counts(int32_t* counts, int32_t n) {
 gmlp_status gmlp_group_quantize(const void* x, int64_t M, int64_t K, const int32_t* m_splits, int32_t G,
                                 gmlp_recipe recipe, int32_t want_row, int32_t want_col, const gmlp_grouped_q* out,
                                 void* ws, size_t ws_bytes, hipStream_t stream) {
-  memset(g_counts, 0, sizeof(g_counts));
-  return quant_core(x, M, K, m_splits, G, recipe, want_row != 0, want_col != 0, out, ws, ws_bytes, stream,
-                    !is_mx(recipe));
+  return gmlp::group_quantize_on(x, M, K, m_splits, G, recipe, want_row, want_col, out, ws, ws_bytes, stream);
 }
 
 gmlp_status gmlp_group_hadamard_amax(const void* x, int64_t M, int64_t K, const int32_t* m_splits, int32_t G,
