@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 Source: "Reduce NVFP4 quantization work for the fused GroupedMLP fc2 input with
 activation recompute" -- Changes (the quantizer's ``rht_sign_mask``; a post-RHT
 amax computed for the plain transform leaves the global scale off by the sign
-pattern) and the commit "Pass the RHT sign mask to the Hadamard-fused GEMM
-kernel" (the fused kernel "rounds its amax values like the quantizer does";
+pattern) and the commit on passing the RHT sign mask to the Hadamard-fused GEMM
+kernel (the fused kernel's amax values are rounded the same way the quantizer
+rounds its data, so they agree with the standalone pass bit for bit;
 ``nvfp4_group_hadamard_amax`` returns the pre- and post-RHT amax of each group).
 
 The pages fix neither the matrix nor where the signs go.  Readings:
@@ -23,7 +24,7 @@ The pages fix neither the matrix nor where the signs go.  Readings:
   (v[i], v[i+h]) by (v[i] + v[i+h], v[i] - v[i+h]) for i with (i & h) == 0,
   then the exact multiply by 0.25.
 * The result is rounded to bf16 (round to nearest even) -- the reading of the
-  amax being rounded "like the quantizer does": the quantizer sees bf16 data.
+  amax being rounded the way the quantizer rounds: the quantizer sees bf16 data.
 """
 import numpy as np
 
