@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs of --traffic-probe (FETCH_SIZE, WRITE_SIZE) into "
                         "the traffic record used by the bench line; needs no GPU")
+    p.add_argument("--write-counters", metavar="COUNTER_DIR",
+                   help="summarise the rocprofv3 --pmc runs of --traffic-probe listed in COUNTER_PASSES (one "
+                        "subdirectory per pass) into the counter record under profiles/; needs no GPU")
     return p.parse_args()
 
 
@@ -143,10 +146,19 @@ def traffic_probe(args):
     w1 = (torch.randn((cfg.experts, cfg.f1, cfg.hidden), device=dev, generator=gen) * cfg.w1_std).to(torch.bfloat16)
     w1q = g.weight_quantize(w1, rec)
     del w1
-    call = DominantGemm(g, torch, rec, w1q, torch.from_numpy(splits.astype(np.int32)).to(dev), shape, dev)
+    splits_dev = torch.from_numpy(splits.astype(np.int32)).to(dev)
+    call = DominantGemm(g, torch, rec, w1q, splits_dev, shape, dev)
     torch.cuda.synchronize()
     for _ in range(3):
         call()
+    torch.cuda.synchronize()
+    del call, w1q
+    # the group quantize of an x-shaped tensor, row- and column-wise, twice
+    x = torch.randn((shape["M"], cfg.hidden), device=dev, generator=gen).to(torch.bfloat16)
+    q = g.alloc_grouped_q(rec, shape["M"], cfg.hidden, cfg.experts, True, True, dev)
+    qws = g.quant_workspace(cfg.experts, dev)
+    for _ in range(2):
+        g.group_quantize(x, splits_dev, rec, True, True, out=q, ws=qws)
     torch.cuda.synchronize()
     print("traffic probe done: %s" % shape, flush=True)
 
@@ -171,6 +183,74 @@ def _counter_rows(d, counter):
     return [(k, v) for _, k, v in rows]
 
 
+# Counter passes over --traffic-probe, each within one pass's hardware limits (at most 8 SQ, 4 TCC
+# and 2 GRBM counters).  MFMA busy cycles against the SIMDs' active cycles give the matrix cores'
+# utilisation; LDS bank conflicts and L2 hits name the other limits of the GEMM's main loop.
+COUNTER_PASSES = {
+    "mfma": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_MFMA",
+             "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+             "GRBM_GUI_ACTIVE"],
+    "lds": ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_DATA_FIFO_FULL",
+            "SQ_VMEM_TA_ADDR_FIFO_FULL", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VMEM", "GRBM_GUI_ACTIVE"],
+    "l2": ["TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_WRREQ_sum", "GRBM_GUI_ACTIVE"],
+}
+SIMDS = 1024            # MI355X: 256 compute units x 4 SIMDs
+
+
+def counter_commands(config):
+    return ["cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc %s "
+            "--output-format csv -d gpurun_out/counters/%s -o p -- python3 bench.py --config %s --traffic-probe"
+            % (" ".join(c), name, config) for name, c in COUNTER_PASSES.items()]
+
+
+def _dispatch_counters(d):
+    """{dispatch id: (kernel name, {counter: value})} from the counter CSVs under d."""
+    import csv
+    import glob
+    out = {}
+    for fn in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                k = int(r["Dispatch_Id"])
+                name, vals = out.setdefault(k, (r["Kernel_Name"], {}))
+                vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def write_counters(args, root):
+    """Per-kernel ratios from the counter passes: the last dispatch of the dominant GEMM and of the x
+    quantize in each pass."""
+    from workloads import CONFIGS
+    cfg = CONFIGS[args.config]
+    shape = dominant_shape(cfg, config_splits(cfg))
+    kernels = {"gemm": "gemm_mx_kernel<0, 0, 0>", "quantize": "mxfp8_quant_kernel<true, true>"}
+    raw = {k: {} for k in kernels}
+    for name in COUNTER_PASSES:
+        disp = _dispatch_counters(os.path.join(root, name))
+        for k, key in kernels.items():
+            hits = [v for _, (kn, v) in sorted(disp.items()) if key in kn]
+            if hits:
+                raw[k].update({c: v for c, v in hits[-1].items()})
+    rec = {"workload": args.config, "shape": shape, "source_sha256": kernel_source_hash(),
+           "commands": counter_commands(args.config), "raw": raw, "derived": {}}
+    for k, v in raw.items():
+        d = {}
+        gui = v.get("GRBM_GUI_ACTIVE")
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+            d["mfma_busy_pct_of_simd_cycles"] = 100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS)
+        if "SQ_LDS_BANK_CONFLICT" in v and v.get("SQ_LDS_IDX_ACTIVE"):
+            d["lds_bank_conflict_pct_of_lds_active"] = 100.0 * v["SQ_LDS_BANK_CONFLICT"] / v["SQ_LDS_IDX_ACTIVE"]
+        if v.get("TCC_HIT_sum") is not None and v.get("TCC_MISS_sum") is not None:
+            d["l2_hit_pct"] = 100.0 * v["TCC_HIT_sum"] / max(1.0, v["TCC_HIT_sum"] + v["TCC_MISS_sum"])
+        if gui:
+            d["gpu_active_cycles"] = gui
+        rec["derived"][k] = d
+    path = os.path.join(PROFILES, "counters_%s_%dx%dx%d.json" % (args.config, shape["M"], shape["N"], shape["K"]))
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec["derived"], indent=1))
+
+
 def write_traffic(args, fetch_dir, write_dir):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the probe's GEMM, each scaled by what the counter
     reads for the 1 GiB copy, stored with the hash of the kernel sources they were taken with."""
@@ -182,9 +262,11 @@ def write_traffic(args, fetch_dir, write_dir):
     pick = lambda rows, key: [v for k, v in rows if key in k]
     cf, cw = pick(fetch, "copyBuffer"), pick(write, "copyBuffer")
     gf, gw = pick(fetch, "gemm_mx_kernel"), pick(write, "gemm_mx_kernel")
+    qf, qw = pick(fetch, "mxfp8_quant_kernel<true, true>"), pick(write, "mxfp8_quant_kernel<true, true>")
     assert cf and cw and gf and gw, (len(cf), len(cw), len(gf), len(gw))
+    # the 1 GiB copies are the probe's largest (other copies move the split sizes and such)
     gib_kib = float(1 << 20)
-    fscale, wscale = gib_kib / cf[-1], gib_kib / cw[-1]
+    fscale, wscale = gib_kib / max(cf), gib_kib / max(cw)
     fb, wb = gf[-1] * 1024 * fscale, gw[-1] * 1024 * wscale
     E, M, N, K = shape["E"], shape["M"], shape["N"], shape["K"]
     rec = {"kernel": "gmlp::gemm_mx_kernel<0, 0, 0> (fc1-dgrad shape: M %d, N %d, K %d, %d experts)" % (M, N, K, E),
@@ -193,6 +275,14 @@ def write_traffic(args, fetch_dir, write_dir):
            "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_scale": fscale, "write_scale": wscale,
            "bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
            "algorithmic_bytes": gemm_algorithmic_bytes(shape), "commands": traffic_commands(args.config)}
+    if qf and qw:
+        # the x-shaped group quantize of the probe (row- and column-wise): read 2 B, write 2 B + 2/32 B
+        # of scales per element
+        rec["quantize"] = {"kernel": "gmlp::mxfp8_quant_kernel<true, true> ([%d, %d], %d groups)"
+                                     % (shape["M"], cfg.hidden, cfg.experts),
+                           "fetch_bytes": int(round(qf[-1] * 1024 * fscale)),
+                           "write_bytes": int(round(qw[-1] * 1024 * wscale)),
+                           "algorithmic_bytes": int((2 + 1 + 1 + 2.0 / 32) * shape["M"] * cfg.hidden)}
     with open(traffic_file(shape), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps({k: rec[k] for k in ("fetch_bytes", "write_bytes", "bytes_per_launch", "algorithmic_bytes")}))
@@ -233,6 +323,9 @@ def main():
         return
     if args.write_traffic:
         write_traffic(args, *args.write_traffic)
+        return
+    if args.write_counters:
+        write_counters(args, args.write_counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "

@@ -265,6 +265,10 @@ typedef struct {
   void* y;                    /* bf16 [M, H] out */
   void* ctx; size_t ctx_bytes;
   void* ws;  size_t ws_bytes;
+  int32_t fc2_amax_in_fc1;    /* NVFP4 with squared ReLU only (else GMLP_UNSUPPORTED): != 0 takes the fc2
+                                 input's pre- and post-RHT amax in the fc1 GEMM's epilogue [NV, Changes:
+                                 the Hadamard-fused fc1 kernel] instead of a pass over h after it; the
+                                 same values either way (the separate pass is the faster one here) */
 } gmlp_fwd_args;
 
 /* Backward [MX, sequence diagram; NV, commits]:
@@ -297,6 +301,15 @@ typedef struct {
 } gmlp_bwd_args;
 
 gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* args, hipStream_t stream);
+
+/* Device addresses, inside a forward's ctx, of two things it saves for the backward: h [M, F1]
+ * bf16 (the fc1 output, the bf16 pre-activation of [MX, sequence diagram]) and, for NVFP4, the
+ * fc2 input's per-group pre- and post-RHT amax (fp32 [E] each; the forward keeps them for the
+ * recompute cast [NV, Changes]; NULL for MXFP8), whether the forward took them in a pass over h
+ * or in the fc1 GEMM's epilogue (fc2_amax_in_fc1).  args: the forward's M, E, H, ffn, activation,
+ * recipe, recompute, ctx and ctx_bytes (nothing else is read).  Host only: computes addresses,
+ * enqueues nothing. */
+gmlp_status gmlp_forward_saved(const gmlp_fwd_args* args, void** h, float** fc2_amax_pre, float** fc2_amax_post);
 gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* args, hipStream_t stream);
 
 /* Deferred weight gradients [MX, Greptile summary, Important Files Changed: the grouped linear

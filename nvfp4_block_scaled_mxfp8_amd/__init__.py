@@ -60,7 +60,7 @@ class FwdArgs(ctypes.Structure):
                 ("recompute", ctypes.c_int32), ("input_requires_grad", ctypes.c_int32),
                 ("weight_requires_grad", ctypes.c_int32), ("y", ctypes.c_void_p),
                 ("ctx", ctypes.c_void_p), ("ctx_bytes", ctypes.c_size_t),
-                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("fc2_amax_in_fc1", ctypes.c_int32)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -106,6 +106,8 @@ _SIGS = {
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "gmlp_grouped_mlp_forward": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.c_void_p]),
     "gmlp_grouped_mlp_backward": (ctypes.c_int, [ctypes.POINTER(BwdArgs), ctypes.c_void_p]),
+    "gmlp_forward_saved": (ctypes.c_int, [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_void_p),
+                                          ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p)]),
     "gmlp_grouped_mlp_wgrad": (ctypes.c_int, [ctypes.POINTER(BwdArgs), ctypes.c_void_p]),
     "gmlp_last_launch_counts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]),
     "gmlp_grouped_gemm_ws_bytes": (ctypes.c_int, [ctypes.c_int32, Recipe, ctypes.c_int32, ctypes.c_int64,
@@ -382,7 +384,10 @@ class MlpContext:
 
 
 def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute=False,
-                        input_requires_grad=True, weight_requires_grad=True, ws=None, y=None, ctx=None):
+                        input_requires_grad=True, weight_requires_grad=True, ws=None, y=None, ctx=None,
+                        fc2_amax_in_fc1=False):
+    """fc2_amax_in_fc1 (NVFP4, squared ReLU): take the fc2 input's amax in the fc1 GEMM's epilogue
+    instead of a pass over h (the same values)."""
     x = _bits(x)
     M, H = x.shape
     E = m_splits.numel()
@@ -397,11 +402,34 @@ def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute
     a = FwdArgs(x.data_ptr(), m_splits.data_ptr(), M, E, H, ffn, ctypes.pointer(s1), ctypes.pointer(s2),
                 probs.data_ptr() if M else None, act, rec, int(recompute), int(input_requires_grad),
                 int(weight_requires_grad), y.data_ptr() if M else None, cbuf.data_ptr(), cbuf.numel(),
-                ws.data_ptr(), ws.numel())
+                ws.data_ptr(), ws.numel(), int(bool(fc2_amax_in_fc1)))
     _check(lib().gmlp_grouped_mlp_forward(ctypes.byref(a), _stream(dev)))
     c = MlpContext(cbuf, M, E, H, ffn, act, rec, bool(recompute), bool(input_requires_grad),
                    bool(weight_requires_grad))
     return y, c
+
+
+def forward_saved(ctx):
+    """Views into a forward's context: h [M, F1] bf16 and (NVFP4) the fc2 input's per-group pre- and
+    post-RHT amax (fp32 [E]; None for MXFP8)."""
+    a = FwdArgs()
+    a.M, a.E, a.H, a.ffn, a.activation, a.recipe = ctx.M, ctx.E, ctx.H, ctx.ffn, ctx.activation, ctx.rec
+    a.recompute, a.ctx, a.ctx_bytes = int(ctx.recompute), ctx.buf.data_ptr(), ctx.buf.numel()
+    h, pre, post = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib().gmlp_forward_saved(ctypes.byref(a), ctypes.byref(h), ctypes.byref(pre), ctypes.byref(post)))
+    base = ctx.buf.data_ptr()
+    F1 = 2 * ctx.ffn if ctx.activation == SWIGLU else ctx.ffn
+
+    def view(ptr, n, dtype):
+        if not ptr.value:
+            return None
+        off = ptr.value - base
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        return ctx.buf[off:off + nbytes].view(dtype)
+
+    hv = view(h, ctx.M * F1, torch.bfloat16)
+    return (hv.view(ctx.M, F1) if hv is not None else None, view(pre, ctx.E, torch.float32),
+            view(post, ctx.E, torch.float32))
 
 
 def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF16, ws=None, out=None,

@@ -11,7 +11,7 @@
 #include "kernels.h"
 #include "planner.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cstdarg>
@@ -601,6 +601,9 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
   if ((A->M > 0 && (!A->x || !A->probs || !A->y)) || !A->m_splits) return fail(GMLP_INVALID_ARG, "null pointer argument");
   if ((st = weight_ok(A->w1, A->recipe, true, false)) != GMLP_OK) return st;
   if ((st = weight_ok(A->w2, A->recipe, true, false)) != GMLP_OK) return st;
+  if (A->fc2_amax_in_fc1 && !(A->recipe.kind == GMLP_NVFP4_RHT && A->activation == GMLP_SRELU))
+    return fail(GMLP_UNSUPPORTED, "%s: the fc2-input amax in the fc1 epilogue needs the NVFP4 recipe and squared ReLU",
+                A->recipe.kind == GMLP_NVFP4_RHT ? "activation" : "recipe");
   const bool mx = is_mx(A->recipe);
   const bool wgrad = A->weight_requires_grad != 0;
   const bool rec = A->recompute != 0;
@@ -641,15 +644,26 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
   }
   // 2. fc1 grouped GEMM: it stores h (saved); the fc2 input a = bf16(act(h) p) is formed from h by
   // the pass that casts it (MXFP8) or by the amax pass and the cast that read it (NVFP4), so a
-  // itself is never written.
+  // itself is never written.  With fc2_amax_in_fc1 (NVFP4, squared ReLU) the GEMM's epilogue forms
+  // a for its tile and takes the fc2 input's pre- and post-RHT amax there ([NV] Changes: the
+  // Hadamard-fused fc1 kernel returns both amax values), and no amax pass reads h.
+  const bool fused_amax = A->fc2_amax_in_fc1 != 0;
   {
-    GemmArgs g = gemm_base(MODE_FPROP, r, EPI_STORE, W.T, E);
+    GemmArgs g = gemm_base(MODE_FPROP, r, fused_amax ? EPI_STORE_AMAX : EPI_STORE, W.T, E);
     g.M = M;
     g.N = A->activation == GMLP_SWIGLU ? 2 * ffn : ffn;
     g.K = H;
     g.a = op_row(W.xq_row.q, x_pre);
     g.b = op_row(*A->w1, A->w1->amax_pre);
     g.c = C.h;
+    if (fused_amax) {
+      g.act = GMLP_SRELU;
+      g.ffn = ffn;
+      g.probs = A->probs;
+      g.rht_mask = r.rht_sign_mask & 0xFFFF;
+      g.amax_pre_out = C.a_pre;
+      g.amax_post_out = C.a_post;
+    }
     set_nv(g, W.nv);
     if (!L.check(launch_gemm(g, stream), "fc1 gemm")) return L.st;
     g_counts[CNT_GEMM]++;
@@ -670,10 +684,12 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     src.probs = A->probs;
     src.act = A->activation;
     src.ffn = ffn;
-    if (!L.check(launch_hadamard_amax(C.h, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, C.a_pre, C.a_post, stream, src),
-                 "amax fc2 input"))
-      return L.st;
-    g_counts[CNT_HAMAX]++;
+    if (!fused_amax) {
+      if (!L.check(launch_hadamard_amax(C.h, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, C.a_pre, C.a_post, stream,
+                                        src), "amax fc2 input"))
+        return L.st;
+      g_counts[CNT_HAMAX]++;
+    }
     NvOut o = nv_out(W.aq_row.q, true, false);
     o.col_bf16 = a_col ? static_cast<uint8_t*>(C.aq_col.q.col_bf16) : nullptr;
     if (!L.check(launch_nvfp4_quant(C.h, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, true, true, a_col, C.a_pre,
@@ -695,6 +711,19 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     if (!L.check(launch_gemm(g, stream), "fc2 gemm")) return L.st;
     g_counts[CNT_GEMM]++;
   }
+  return ok();
+}
+
+gmlp_status gmlp_forward_saved(const gmlp_fwd_args* A, void** h, float** fc2_amax_pre, float** fc2_amax_post) {
+  if (!A || !h || !fc2_amax_pre || !fc2_amax_post) return fail(GMLP_INVALID_ARG, "null pointer argument");
+  gmlp_status st = mlp_common_checks(A->M, A->E, A->H, A->ffn, A->activation, A->recipe);
+  if (st != GMLP_OK) return st;
+  Bump cb(A->ctx);
+  FwdCtx C = carve_ctx(cb, A->M, A->E, A->H, A->ffn, A->activation, A->recipe, A->recompute != 0);
+  if (!A->ctx || A->ctx_bytes < cb.off) return fail(GMLP_WORKSPACE, "ctx too small: need %zu bytes", cb.off);
+  *h = C.h;
+  *fc2_amax_pre = C.a_pre;
+  *fc2_amax_post = C.a_post;
   return ok();
 }
 

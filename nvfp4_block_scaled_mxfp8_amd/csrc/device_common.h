@@ -102,6 +102,28 @@ __device__ __forceinline__ float nvfp4_global_scale(float amax) {
   return fminf(s, kFltMax);
 }
 
+// --------------------------------------------------------------------------- signed Hadamard
+// The NVFP4 recipe's 16x16 randomized Hadamard transform ("Reduce NVFP4 quantization work ...",
+// Changes: the quantizer's rht_sign_mask): y = H16 (s * x) with s_j = -1 where bit j of the mask
+// is set and H16[i][j] = (-1)^popcount(i & j), as the fp32 butterfly over strides 1, 2, 4, 8
+// (each stage maps (v[i], v[i+h]) -> (v[i] + v[i+h], v[i] - v[i+h])); the caller applies the
+// exact factor 1/4.  Every pass that transforms or takes the post-transform amax uses this one
+// function, so that they agree bit for bit.
+__device__ __forceinline__ void signed_fwht16(float* v, uint32_t mask) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = ((mask >> j) & 1u) ? -v[j] : v[j];
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+}
+
 // --------------------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

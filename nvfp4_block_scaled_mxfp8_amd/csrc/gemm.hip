@@ -27,6 +27,7 @@
 // same 64-byte panels and the GEMM runs on V_MFMA_F32_32X32X16_BF16; the per-group global
 // scales multiply the fp32 result.  (The block-scaled MFMA takes E8M0 scales per 32
 // elements; NVFP4's E4M3 scales per 16 cannot be folded into it exactly.)
+#include "activation.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -644,9 +645,55 @@ __device__ __forceinline__ float4 ld_st4(const float* p, float alpha) {
   return v;
 }
 
+// A kernel argument read where it is used (a volatile load of the argument), so that the compiler
+// does not keep it in a register across the main loop: the epilogue-only arguments would otherwise
+// add to the main loop's scalar-register pressure.
+template <class T>
+__device__ __forceinline__ T* late_ptr(T* const& arg) {
+  return *reinterpret_cast<T* const volatile*>(&arg);
+}
+
+// EPI_STORE_AMAX: the fc2-input amax of a staged chunk, read after the store loop (which only
+// reads the staged values too, so no barrier is needed in between).  The chunk holds tile rows
+// 32 TM + [0, 32) and 128 + 32 TM + [0, 32) (staged rows [0, 32) and [32, 64)): four whole
+// 16-token blocks of the group, since tiles start at multiples of 256 rows from the group's first
+// row; and 128 columns.  Thread tid takes the (block, column) pairs tid and tid + 256 (a wave's 64
+// pairs share the block, so the token probabilities it reads from LDS are one address per wave):
+// the column's 16 values as the stored bf16 h (the same fp32 product and rounding as the store),
+// a = bf16(relu(h)^2 p) of each token with the function the standalone amax pass and the casts
+// use, zeros for the rows past the group's end and the columns past N (the zero padding of the
+// column-wise cast), then the signed Hadamard of the block.  pre / post: running maxima of |a|
+// and of the unscaled |H16 (s * a)|.
+template <int TM, int Q>
+__device__ __forceinline__ void epi_chunk_amax(const GemmArgs& A, const Ctx& c, const float* st, const float* probs,
+                                               int tid, uint32_t mask, float& pre, float& post) {
+#pragma unroll 1
+  for (int k = 0; k < 2; ++k) {
+    const int p = tid + 256 * k;
+    const int blk = p >> 7, sc = p & 127;
+    const int col = 128 * (sc >> 6) + 64 * Q + (sc & 63);
+    const bool col_ok = c.nrow0 + col < A.N;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sr = 16 * blk + i;
+      const int tr = chunk_row(TM, sr);
+      const bool ok = col_ok && tr < c.arows;
+      const float h = round_bf16(__fmul_rn(st[sr * EPC_LD + sc], c.alpha));
+      const float a = ok ? act_out(1, h, 0.0f, probs[tr]) : 0.0f;
+      pre = fmaxf(pre, fabsf(a));
+      v[i] = a;
+    }
+    signed_fwht16(v, mask);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) post = fmaxf(post, fabsf(v[i]));
+  }
+}
+
 template <int MODE, int EPI, int CH, int BF = 0>
 __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
-                                          int tid, int wm, int wn, int lane) {
+                                          int tid, int wm, int wn, int lane, const float* probs, uint32_t mask,
+                                          float& pre, float& post) {
   constexpr int TM = CH >> 1, Q = CH & 1;
   const float* st = reinterpret_cast<const float*>(buf);
   {
@@ -705,6 +752,7 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
     }
     }
   }
+  if constexpr (EPI == EPI_STORE_AMAX) epi_chunk_amax<TM, Q>(A, c, st, probs, tid, mask, pre, post);
   __syncthreads();
 }
 
@@ -732,17 +780,48 @@ __device__ __forceinline__ void epi_zero(const GemmArgs& A, const Ctx& c, int ti
   }
 }
 
+// red: 8 floats of LDS for the workgroup's amax reduction (EPI_STORE_AMAX); tile: the tile's index
+// in the launch's sequence (its amax slot).
+// probs: 256 floats of LDS for the tile's token probabilities (EPI_STORE_AMAX).  They are loaded
+// once, before the first chunk's stores: a vector load waits for every memory operation issued
+// before it (the wait counter retires in order), so a load after the stores would wait for them.
 template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ void mx_epilogue(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
-                                            int tid, int wm, int wn, int lane) {
-  epi_chunk<MODE, EPI, 0, BF>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 1, BF>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 2, BF>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 3, BF>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 4, BF>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 5, BF>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 6, BF>(A, c, acc, buf, tid, wm, wn, lane);
-  epi_chunk<MODE, EPI, 7, BF>(A, c, acc, buf, tid, wm, wn, lane);
+                                            int tid, int wm, int wn, int lane, int tile, float* red, float* probs) {
+  float pre = 0.0f, post = 0.0f;
+  uint32_t mask = 0;
+  if constexpr (EPI == EPI_STORE_AMAX) {
+    probs[tid] = tid < c.arows ? late_ptr(A.probs)[c.arow0 + tid] : 0.0f;   // visible after chunk 0's barrier
+    mask = *reinterpret_cast<const volatile uint32_t*>(&A.rht_mask);
+  }
+  epi_chunk<MODE, EPI, 0, BF>(A, c, acc, buf, tid, wm, wn, lane, probs, mask, pre, post);
+  epi_chunk<MODE, EPI, 1, BF>(A, c, acc, buf, tid, wm, wn, lane, probs, mask, pre, post);
+  epi_chunk<MODE, EPI, 2, BF>(A, c, acc, buf, tid, wm, wn, lane, probs, mask, pre, post);
+  epi_chunk<MODE, EPI, 3, BF>(A, c, acc, buf, tid, wm, wn, lane, probs, mask, pre, post);
+  epi_chunk<MODE, EPI, 4, BF>(A, c, acc, buf, tid, wm, wn, lane, probs, mask, pre, post);
+  epi_chunk<MODE, EPI, 5, BF>(A, c, acc, buf, tid, wm, wn, lane, probs, mask, pre, post);
+  epi_chunk<MODE, EPI, 6, BF>(A, c, acc, buf, tid, wm, wn, lane, probs, mask, pre, post);
+  epi_chunk<MODE, EPI, 7, BF>(A, c, acc, buf, tid, wm, wn, lane, probs, mask, pre, post);
+  if constexpr (EPI == EPI_STORE_AMAX) {
+    // the tile's maxima into one of its group's slots, as the standalone pass does: the
+    // post-transform amax is bf16(max |y| / 4) (the factor is exact and rounding is monotone)
+    post = wave_max(round_bf16(post * 0.25f));
+    pre = wave_max(pre);
+    const int wave = tid >> 6;
+    if (lane == 0) {
+      red[wave] = pre;
+      red[4 + wave] = post;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      const float b = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+      const int slot = tile % kAmaxSlots;
+      uint32_t* slots = late_ptr(A.T.amax_slots);
+      atomicMax(slots + ((int64_t)c.g * kAmaxSlots + slot), __float_as_uint(a));
+      atomicMax(slots + ((int64_t)(A.G + c.g) * kAmaxSlots + slot), __float_as_uint(b));
+    }
+  }
 }
 
 template <int MODE, int EPI, int BF = 0>
@@ -808,6 +887,8 @@ __device__ __forceinline__ void wgrad_xcd_range(const GemmArgs& A, int tpg, int 
 template <int MODE, int EPI, int BF>
 __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
   __shared__ __align__(16) uint8_t smem[MX_NSTAGE * MX_STAGE];
+  __shared__ float red[8];
+  __shared__ float tile_probs[(EPI == EPI_STORE_AMAX) ? 256 : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uni(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -969,7 +1050,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
     // across every main loop).
     int tid_t = tid;
     asm volatile("" : "+v"(tid_t));
-    mx_epilogue<MODE, EPI, BF>(A, c, acc, slot(gs + 3), tid_t, wm, wn, tid_t & 63);
+    mx_epilogue<MODE, EPI, BF>(A, c, acc, slot(gs + 3), tid_t, wm, wn, tid_t & 63, t, red, tile_probs);
   }
   wait_vmcnt<0>();                     // the DMAs past the last tile (empty) before the LDS is released
 }
@@ -1073,6 +1154,10 @@ static hipError_t launch_nvfp4(const GemmArgs& g, int epi, hipStream_t s) {
   }
   if (epi == EPI_STORE32) return launch_mx<MODE_FPROP, EPI_STORE32, 1>(a, s);
   if (epi == EPI_STORE) return launch_mx<MODE_FPROP, EPI_STORE, 1>(a, s);
+  if (epi == EPI_STORE_AMAX) {
+    if ((e = launch_mx<MODE_FPROP, EPI_STORE_AMAX, 1>(a, s)) != hipSuccess) return e;
+    return launch_amax_finalize(g.T, g.G, g.amax_pre_out, g.amax_post_out, s);
+  }
   if (epi != EPI_DACT) return hipErrorInvalidValue;
   a.epi = EPI_STORE;
   a.c = g.da_tmp;
@@ -1082,7 +1167,13 @@ static hipError_t launch_nvfp4(const GemmArgs& g, int epi, hipStream_t s) {
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if (g.mode == MODE_FPROP && g.M == 0) return hipSuccess;
+  if (g.epi == EPI_STORE_AMAX &&
+      (g.mode != MODE_FPROP || g.fmt != FMT_NVFP4 || !g.probs || !g.amax_pre_out || !g.amax_post_out))
+    return hipErrorInvalidValue;
+  if (g.mode == MODE_FPROP && g.M == 0) {
+    // no rows: every group's fc2-input amax is zero
+    return g.epi == EPI_STORE_AMAX ? launch_amax_finalize(g.T, g.G, g.amax_pre_out, g.amax_post_out, s) : hipSuccess;
+  }
   const int epi = (g.epi != EPI_STORE || !g.out_fp32) ? g.epi : (g.out_fp32 == 2 ? (int)EPI_ACC32 : (int)EPI_STORE32);
   if (epi == EPI_ACC32 && g.mode != MODE_WGRAD) return hipErrorInvalidValue;
   if (g.fmt == FMT_NVFP4) return launch_nvfp4(g, epi, s);

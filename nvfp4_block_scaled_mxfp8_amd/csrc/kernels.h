@@ -1,6 +1,6 @@
 // Private interface between the host planner (api.cpp) and the kernel files.
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace gmlp {
@@ -75,6 +75,8 @@ struct ActSrc {
 };
 hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
                                 uint32_t mask, float* pre, float* post, hipStream_t s, ActSrc act = ActSrc());
+// pre[g] / post[g] = the max over group g's amax slots (T.amax_slots), which it clears again.
+hipError_t launch_amax_finalize(SplitTables T, int G, float* pre, float* post, hipStream_t s);
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
                               uint32_t mask, bool rht, bool row, bool col, const float* pre,
                               const float* post, NvOut o, hipStream_t s, ActSrc act = ActSrc());
@@ -104,7 +106,10 @@ enum GemmFmt { FMT_MXFP8 = 0, FMT_NVFP4 = 1, FMT_NVFP4_BF16 = 2 };
 enum GemmMode { MODE_FPROP = 0, MODE_WGRAD = 1 };
 // STORE32: fp32 output.  ACC32: fp32 output added to what C holds (weight gradients into an fp32
 // main_grad).  DACT (NVFP4 fc2 dgrad): da is stored, then the activation-gradient pass.
-enum GemmEpi { EPI_STORE = 0, EPI_DACT = 2, EPI_STORE32 = 3, EPI_ACC32 = 4 };
+// STORE_AMAX (NVFP4 fc1 with squared ReLU): h is stored as by STORE, and the epilogue also forms
+// the fc2 input a = bf16(relu(h)^2 p) of its tile and maxes the tile's pre- and post-RHT amax of a
+// into the group's amax slots; a finalize pass after the GEMM writes amax_pre_out / amax_post_out.
+enum GemmEpi { EPI_STORE = 0, EPI_DACT = 2, EPI_STORE32 = 3, EPI_ACC32 = 4, EPI_STORE_AMAX = 5 };
 
 struct GemmOperand {
   const uint8_t* data;        // fp8 / packed fp4
@@ -139,6 +144,10 @@ struct GemmArgs {
   uint8_t* xa;
   uint8_t* xb;
   uint16_t* da_tmp;
+  // EPI_STORE_AMAX: the recipe's sign mask (probs above) and the per-group fc2-input amax outputs
+  uint32_t rht_mask;
+  float* amax_pre_out;
+  float* amax_post_out;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);

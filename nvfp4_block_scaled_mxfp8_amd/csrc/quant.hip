@@ -584,25 +584,6 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   col_cast_tile64(tile, ti, ffn, ti.k0, T, o, tid);
 }
 
-// ----------------------------------------------------------------------------- signed Hadamard
-// y = H16 (s * x) with H16[i][j] = (-1)^popcount(i & j): the fp32 butterfly over strides
-// 1, 2, 4, 8 (each stage maps (v[i], v[i+h]) -> (v[i] + v[i+h], v[i] - v[i+h])); the caller
-// applies the exact factor 1/4.
-__device__ __forceinline__ void signed_fwht16(float* v, uint32_t mask) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = ((mask >> j) & 1u) ? -v[j] : v[j];
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i & h) continue;
-      const float a = v[i], b = v[i + h];
-      v[i] = a + b;
-      v[i + h] = a - b;
-    }
-  }
-}
-
 __global__ __launch_bounds__(256) void hadamard_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                             SplitTables T, int G, uint32_t mask, ActSrc A) {
   __shared__ __align__(16) uint16_t tile[QT * LDW];
@@ -895,6 +876,11 @@ hipError_t launch_act_quant(const uint16_t* h, const float* probs, int act, int6
   const dim3 grid((unsigned)(ffn / DF), (unsigned)(2 * ((M + QT - 1) / QT + G)));   // half tiles
   if (act == 0) hipLaunchKernelGGL((act_quant_kernel<true>), grid, dim3(256), 0, s, h, probs, ffn, T, G, M, o);
   else hipLaunchKernelGGL((act_quant_kernel<false>), grid, dim3(256), 0, s, h, probs, ffn, T, G, M, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_finalize(SplitTables T, int G, float* pre, float* post, hipStream_t s) {
+  hipLaunchKernelGGL(amax_finalize_kernel, dim3((unsigned)((2 * G + 255) / 256)), dim3(256), 0, s, T, G, pre, post);
   return hipGetLastError();
 }
 

@@ -79,8 +79,23 @@ def state(name):
     del w1, w2
     runs = {}
     for recompute in ([False, True] if cfg.recipe == "nvfp4" else [False]):
-        y, ctx = g.grouped_mlp_forward(x, splits, w1q, w2q, probs, cfg.activation, rec, recompute=recompute)
+        # NVFP4: the recompute run takes the fc2-input amax in the fc1 epilogue (fc2_amax_in_fc1), the
+        # other in a pass over h; the two runs are compared bitwise below
+        fused = cfg.recipe == "nvfp4" and recompute
+        y, ctx = g.grouped_mlp_forward(x, splits, w1q, w2q, probs, cfg.activation, rec, recompute=recompute,
+                                       fc2_amax_in_fc1=fused)
         fwd_counts = g.last_launch_counts()
+        fused_amax_ok = None
+        if fused:
+            # the fc2 input's amax from the fc1 GEMM's epilogue vs the standalone pass on the same a
+            h, pre, post = g.forward_saved(ctx)
+            r_ = torch.relu(h.float())
+            a_ = (r_ * r_ * probs[:, None]).to(torch.bfloat16)
+            del r_
+            rpre, rpost = g.group_hadamard_amax(a_, splits, wl.sign_mask)
+            fused_amax_ok = (torch.equal(pre.view(torch.int32), rpre.view(torch.int32)) and
+                             torch.equal(post.view(torch.int32), rpost.view(torch.int32)))
+            del a_
         out = g.grouped_mlp_backward(dy, splits, w1q, w2q, probs, ctx)
         bwd_counts = g.last_launch_counts()
         torch.cuda.synchronize()
@@ -90,7 +105,8 @@ def state(name):
         empty_zero = all(not bool(out["dw1"][e].any()) and not bool(out["dw2"][e].any()) for e in empty)
         host = {"y": _host(y).reshape(M, H), "dx": _host(out["dx"]).reshape(M, H), "dprobs": _host(out["dprobs"]),
                 "finite": finite, "empty": empty, "empty_zero": empty_zero,
-                "fwd_counts": fwd_counts, "bwd_counts": bwd_counts, "dev": {k: out[k] for k in ("dw1", "dw2")}}
+                "fwd_counts": fwd_counts, "bwd_counts": bwd_counts, "dev": {k: out[k] for k in ("dw1", "dw2")},
+                "fused_amax_ok": fused_amax_ok}
         host["dev"]["y"], host["dev"]["dx"], host["dev"]["dprobs"] = y, out["dx"], out["dprobs"]
         runs[recompute] = host
         del ctx
@@ -226,6 +242,10 @@ def test_nvfp4_recompute_on_off_bitwise():
         assert torch.equal(ta.view(view), tb.view(view)), k
     # recompute casts the rebuilt fc2 input with the forward's amax: no extra Hadamard-amax pass
     assert a["bwd_counts"]["hadamard_amax"] == b["bwd_counts"]["hadamard_amax"] == 2
+    # the recompute run took the fc2-input amax in the fc1 GEMM's epilogue: bit for bit the
+    # standalone pass's, and only x got an amax pass of its own
+    assert b["fused_amax_ok"]
+    assert a["fwd_counts"]["hadamard_amax"] == 2 and b["fwd_counts"]["hadamard_amax"] == 1
     assert b["bwd_counts"]["nvfp4_quantize"] == a["bwd_counts"]["nvfp4_quantize"] + 1
 
 

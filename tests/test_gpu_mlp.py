@@ -89,7 +89,58 @@ def test_recompute_on_off_bitwise(kind, act):
         # the recompute backward casts the rebuilt input with the forward's amax: no third amax pass
         assert b["bwd_counts"]["hadamard_amax"] == 2 and a["bwd_counts"]["hadamard_amax"] == 2
         assert b["bwd_counts"]["nvfp4_quantize"] == 3 and a["bwd_counts"]["nvfp4_quantize"] == 2
-        assert b["fwd_counts"]["hadamard_amax"] == 2
+        # forward: x's amax pass and the fc2 input's
+        assert a["fwd_counts"]["hadamard_amax"] == b["fwd_counts"]["hadamard_amax"] == 2
+
+
+def _fc2_input_amax_reference(ctx, probs, splits, sign_mask):
+    """gmlp_group_hadamard_amax on the fc2 input a = bf16(relu(h)^2 p), formed by torch from the h
+    the forward saved (fp32 products, round to nearest even, as the kernels form it)."""
+    h, pre, post = g.forward_saved(ctx)
+    r = torch.relu(h.float())
+    a = (r * r * probs[:, None]).to(torch.bfloat16)
+    rpre, rpost = g.group_hadamard_amax(a, splits, sign_mask)
+    return pre, post, rpre, rpost
+
+
+@pytest.mark.parametrize("recompute", [False, True])
+@pytest.mark.parametrize("splits", [[0, 37, 300, 129, 5], [512, 256, 1]])
+def test_nvfp4_fused_fc2_amax_matches_standalone_pass(splits, recompute):
+    """NVFP4 with squared ReLU and fc2_amax_in_fc1: the fc1 GEMM's epilogue takes the fc2 input's
+    per-group pre- and post-RHT amax ("Reduce NVFP4 quantization work ...", Changes: the
+    Hadamard-fused fc1 kernel returns both); they equal, bit for bit, the standalone Hadamard-amax
+    pass on the same fc2 input, the forward launches only x's amax pass, and y is bitwise the
+    default forward's (which takes the amax in a pass over h).  (ffn 384: the second column tile
+    of each row band is half empty.)"""
+    print(f"fused fc2 amax splits={splits} recompute={recompute}", flush=True)
+    wl = small_case(splits, 256, 384, activation="srelu", recipe="nvfp4", seed=9, w_std=0.05)
+    d = _upload(wl)
+    rec = g.recipe("nvfp4", wl.sign_mask)
+    w1q, w2q = g.weight_quantize(d["w1"], rec), g.weight_quantize(d["w2"], rec)
+    y0, ctx0 = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], "srelu", rec, recompute=recompute)
+    counts0 = g.last_launch_counts()
+    y, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], "srelu", rec, recompute=recompute,
+                                   fc2_amax_in_fc1=True)
+    counts = g.last_launch_counts()
+    pre, post, rpre, rpost = _fc2_input_amax_reference(ctx, d["probs"], d["splits"], wl.sign_mask)
+    _, pre0, post0 = g.forward_saved(ctx0)
+    torch.cuda.synchronize()
+    assert counts["hadamard_amax"] == 1 and counts0["hadamard_amax"] == 2, (counts, counts0)
+    assert torch.equal(pre.view(torch.int32), rpre.view(torch.int32)), (pre, rpre)
+    assert torch.equal(post.view(torch.int32), rpost.view(torch.int32)), (post, rpost)
+    assert torch.equal(pre0.view(torch.int32), pre.view(torch.int32))
+    assert torch.equal(post0.view(torch.int32), post.view(torch.int32))
+    assert torch.equal(y0.view(torch.int16), y.view(torch.int16))
+    assert float(post.max()) > 0 and all(float(pre[e]) == 0 for e in range(len(splits)) if splits[e] == 0)
+
+
+def test_fc2_amax_in_fc1_needs_nvfp4_srelu():
+    wl = small_case([64, 64], 128, 128, activation="swiglu", recipe="nvfp4", seed=9, w_std=0.05)
+    d = _upload(wl)
+    rec = g.recipe("nvfp4", 1)
+    w1q, w2q = g.weight_quantize(d["w1"], rec), g.weight_quantize(d["w2"], rec)
+    with pytest.raises(g.GmlpError, match="squared ReLU"):
+        g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], "swiglu", rec, fc2_amax_in_fc1=True)
 
 
 def test_deterministic_and_fp32_wgrad():
