@@ -426,13 +426,16 @@ __device__ __forceinline__ void mx_read_p(const uint8_t* stage, const ReadPlan& 
 __device__ __forceinline__ v8bf frag_lo(const v8i& v) { return __builtin_bit_cast(v8bf, v4i{v[0], v[1], v[2], v[3]}); }
 __device__ __forceinline__ v8bf frag_hi(const v8i& v) { return __builtin_bit_cast(v8bf, v4i{v[4], v[5], v[6], v[7]}); }
 
-template <int TM, int TN, int BF = 0>
+// Z: the tile's first step, which starts the accumulators from zero (the MFMA's C operand is the
+// constant 0, so no register has to be cleared between tiles).
+template <int TM, int TN, int BF = 0, bool Z = false>
 __device__ __forceinline__ void mx_mma_one(const MxFrags& f, v16f (&acc)[4][4]) {
+  const v16f c = Z ? v16f{} : acc[TM][TN];
   if constexpr (BF) {
-    acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_lo(f.a[TM]), frag_lo(f.b[TN]), acc[TM][TN], 0, 0, 0);
+    acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_lo(f.a[TM]), frag_lo(f.b[TN]), c, 0, 0, 0);
     acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_hi(f.a[TM]), frag_hi(f.b[TN]), acc[TM][TN], 0, 0, 0);
   } else {
-    acc[TM][TN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[TM], f.b[TN], acc[TM][TN], 0, 0, 0,
+    acc[TM][TN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[TM], f.b[TN], c, 0, 0, 0,
                                                                    (int)f.sa[TM], 0, (int)f.sb[TN]);
   }
 }
@@ -448,36 +451,36 @@ __device__ __forceinline__ void mx_mma_one(const MxFrags& f, v16f (&acc)[4][4]) 
 //   after the barrier:  R0 M20 D5 R1 M21 M22 D6 R2 M23 M30 D7 R3 M31 M32 D8 M33
 constexpr int MX_DMA_BEFORE_BARRIER = 5;
 
-template <int BF = 0>
+template <int BF = 0, bool Z = false>
 __device__ __forceinline__ void mx_phase1(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
                                           int wave) {
   mx_dma_one<0>(s, d, wave); GMLP_SB();
-  mx_mma_one<0, 0, BF>(f, acc); GMLP_SB(); mx_mma_one<0, 1, BF>(f, acc); GMLP_SB();
+  mx_mma_one<0, 0, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<0, 1, BF, Z>(f, acc); GMLP_SB();
   mx_dma_one<1>(s, d, wave); GMLP_SB();
-  mx_mma_one<0, 2, BF>(f, acc); GMLP_SB(); mx_mma_one<0, 3, BF>(f, acc); GMLP_SB();
+  mx_mma_one<0, 2, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<0, 3, BF, Z>(f, acc); GMLP_SB();
   mx_dma_one<2>(s, d, wave); GMLP_SB();
-  mx_mma_one<1, 0, BF>(f, acc); GMLP_SB(); mx_mma_one<1, 1, BF>(f, acc); GMLP_SB();
+  mx_mma_one<1, 0, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<1, 1, BF, Z>(f, acc); GMLP_SB();
   mx_dma_one<3>(s, d, wave); GMLP_SB();
-  mx_mma_one<1, 2, BF>(f, acc); GMLP_SB(); mx_mma_one<1, 3, BF>(f, acc); GMLP_SB();
+  mx_mma_one<1, 2, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<1, 3, BF, Z>(f, acc); GMLP_SB();
   mx_dma_one<4>(s, d, wave); GMLP_SB();
 }
 
-template <int PAR, int BF = 0>
+template <int PAR, int BF = 0, bool Z = false>
 __device__ __forceinline__ void mx_phase2p(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
                                            int wave, const uint8_t* nstage, const ReadPlan& rp, MxFrags& nf) {
   mx_read_tp<0, PAR, BF>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<2, 0, BF>(f, acc); GMLP_SB();
+  mx_mma_one<2, 0, BF, Z>(f, acc); GMLP_SB();
   mx_dma_one<5>(s, d, wave); GMLP_SB();
   mx_read_tp<1, PAR, BF>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<2, 1, BF>(f, acc); GMLP_SB(); mx_mma_one<2, 2, BF>(f, acc); GMLP_SB();
+  mx_mma_one<2, 1, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<2, 2, BF, Z>(f, acc); GMLP_SB();
   mx_dma_one<6>(s, d, wave); GMLP_SB();
   mx_read_tp<2, PAR, BF>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<2, 3, BF>(f, acc); GMLP_SB(); mx_mma_one<3, 0, BF>(f, acc); GMLP_SB();
+  mx_mma_one<2, 3, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<3, 0, BF, Z>(f, acc); GMLP_SB();
   mx_dma_one<7>(s, d, wave); GMLP_SB();
   mx_read_tp<3, PAR, BF>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<3, 1, BF>(f, acc); GMLP_SB(); mx_mma_one<3, 2, BF>(f, acc); GMLP_SB();
+  mx_mma_one<3, 1, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<3, 2, BF, Z>(f, acc); GMLP_SB();
   mx_dma_one<8>(s, d, wave); GMLP_SB();
-  mx_mma_one<3, 3, BF>(f, acc); GMLP_SB();
+  mx_mma_one<3, 3, BF, Z>(f, acc); GMLP_SB();
 }
 
 // ----------------------------------------------------------------------------- tile mapping
@@ -965,14 +968,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
       epi_zero<MODE, EPI>(A, c, tid_t);
       continue;
     }
-    v16f acc[4][4];
+    v16f acc[4][4];                    // set by the first step (MFMAs onto zero)
     MxFrags f0, f1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
     {
       // stage gs (this tile's first) has landed once at most the two stages after it are pending
       wait_vmcnt<2 * MX_DMA_PER_STAGE>();
@@ -983,15 +980,35 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
       // stage gs + 1 in between.  Stage gs + 1 may be the next tile's first (read again after
       // the epilogue) or no stage at all; such reads go unused.  Two steps per trip keep the two
       // fragment sets in fixed registers
-      // (stage kt + 1 of an even kt has parity 1, of an odd kt parity 0)
-      int kt = 0;
-      if (nk > 4) {
+      // (stage kt + 1 of an even kt has parity 1, of an odd kt parity 0).  nk is even.
+      // The first pair: its first step starts the accumulators (DMA targets 3 and 4 may be past
+      // the tile).
+      {
+        const StageDma sd = window_stage(3, slot(gs + 3));
+        GMLP_SB();
+        mx_phase1<BF, true>(f0, acc, sd, dpl, wave);
+        wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
+        __syncthreads();
+        mx_phase2p<1, BF, true>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
+        ++gs;
+      }
+      {
+        const StageDma sd = window_stage(4, slot(gs + 3));
+        GMLP_SB();
+        mx_phase1<BF>(f1, acc, sd, dpl, wave);
+        wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
+        __syncthreads();
+        mx_phase2p<0, BF>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
+        ++gs;
+      }
+      int kt = 2;
+      if (nk > 6) {
         // steps whose DMA target (kt + 3, kt + 4) is still in this tile: fixed resources, the
         // stage in SOFFSET (32-bit: every operand is below 4 GB)
         const RunDma rr = run_rsrc(KC, D0);
-        uint32_t soa = 3u * KC.a_ps, sob = 3u * KC.b_ps;
-        uint32_t sos = 4u * KC.s_ld;                 // 128-K word (kt + 3) / 2 = 1
+        uint32_t soa = 5u * KC.a_ps, sob = 5u * KC.b_ps;
         const uint32_t s_step = 4u * KC.s_ld;
+        uint32_t sos = 2u * s_step;                  // 128-K word (kt + 3) / 2 = 2
         do {
           {
             const StageDma sd = run_stage(rr, soa, sob, sos, slot(gs + 3), s_voff, wave);
@@ -1019,7 +1036,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
           kt += 2;
         } while (kt < nk - 4);
       }
-      do {                               // the last two pairs (or one): DMA targets may be past the tile
+      while (kt < nk) {                  // the last two pairs (or one): DMA targets may be past the tile
         {
           const StageDma sd = window_stage(kt + 3, slot(gs + 3));
           GMLP_SB();
@@ -1039,7 +1056,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
           ++gs;
         }
         kt += 2;
-      } while (kt < nk);
+      }
       D0 = D1;
       D1 = D2;
       D2 = dma_tile<MODE, EPI, BF>(A, next_ref(), wave);
