@@ -721,19 +721,30 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
     const int col = 128 * (sc >> 6) + 64 * Q + (sc & 63);
     const uint32_t voff = (c.nrow0 + col < ncols) ? (uint32_t)lrow * rowb + (uint32_t)(col * ESZ) : kOutOfRange;
     const float* src = st + lrow * EPC_LD + sc;
+    // The staged values are all read before the first store: a buffer store may alias LDS as far
+    // as the compiler knows, so a read placed after a store would wait for it and for its own
+    // LDS latency, once per store.
+    // EPI_ACC32 (C += tile): the chunk's old fp32 values are fetched first (one 16-byte load per
+    // store, same offsets, so the range check drops the same lanes), then added in fp32.
+    uint4 old[NIT];
     if constexpr (EPI == EPI_ACC32) {
-      // C += tile: the chunk's old fp32 values are fetched together (one 16-byte load per
-      // store, same offsets, so the range check drops the same lanes), then added in fp32
-      uint4 old[NIT];
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const uint32_t ur = (uint32_t)(128 * ((RPI * it) >> 5) + 32 * TM + ((RPI * it) & 31));
         old[it] = out_load(r, voff, ur * rowb);
       }
+    }
+    float4 v0[NIT], v1[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      v0[it] = ld_st4<BF>(src + RPI * it * EPC_LD, c.alpha);
+      if constexpr (ESZ == 2) v1[it] = ld_st4<BF>(src + RPI * it * EPC_LD + 4, c.alpha);
+    }
+    if constexpr (EPI == EPI_ACC32) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const uint32_t ur = (uint32_t)(128 * ((RPI * it) >> 5) + 32 * TM + ((RPI * it) & 31));
-        const float4 v = ld_st4<BF>(src + RPI * it * EPC_LD, c.alpha);
+        const float4 v = v0[it];
         out_store(r, voff, ur * rowb, __float_as_uint(__fadd_rn(__uint_as_float(old[it].x), v.x)),
                   __float_as_uint(__fadd_rn(__uint_as_float(old[it].y), v.y)),
                   __float_as_uint(__fadd_rn(__uint_as_float(old[it].z), v.z)),
@@ -741,18 +752,18 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& A, const Ctx& c, const
       }
     } else {
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const uint32_t ur = (uint32_t)(128 * ((RPI * it) >> 5) + 32 * TM + ((RPI * it) & 31));   // tile row - lrow
-      const float4 v0 = ld_st4<BF>(src + RPI * it * EPC_LD, c.alpha);
-      if (EPI == EPI_STORE32) {
-        out_store(r, voff, ur * rowb, __float_as_uint(v0.x), __float_as_uint(v0.y), __float_as_uint(v0.z),
-                  __float_as_uint(v0.w));
-      } else {
-        const float4 v1 = ld_st4<BF>(src + RPI * it * EPC_LD + 4, c.alpha);
-        out_store(r, voff, ur * rowb, pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
-                  pack_bf16x2(v1.z, v1.w));
+      for (int it = 0; it < NIT; ++it) {
+        const uint32_t ur = (uint32_t)(128 * ((RPI * it) >> 5) + 32 * TM + ((RPI * it) & 31));   // tile row - lrow
+        const float4 a = v0[it];
+        if (EPI == EPI_STORE32) {
+          out_store(r, voff, ur * rowb, __float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
+                    __float_as_uint(a.w));
+        } else {
+          const float4 b = v1[it];
+          out_store(r, voff, ur * rowb, pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                    pack_bf16x2(b.z, b.w));
+        }
       }
-    }
     }
   }
   if constexpr (EPI == EPI_STORE_AMAX) epi_chunk_amax<TM, Q>(A, c, st, probs, tid, mask, pre, post);
