@@ -61,7 +61,16 @@ typedef enum {
 } gmlp_status;
 
 typedef enum { GMLP_MXFP8 = 0, GMLP_NVFP4_RHT = 1 } gmlp_recipe_kind;
-typedef enum { GMLP_SWIGLU = 0, GMLP_SRELU = 1 } gmlp_activation;
+/* Activation of the fc2 input, scaled by the token's routing probability p:
+ *   GMLP_SWIGLU      silu(gate) * up over h = [gate | up] (F1 = 2 ffn)        [MX, sequence diagram]
+ *   GMLP_SRELU       relu(h)^2 (F1 = ffn)                                      [NV, Description]
+ *   GMLP_TANH_SRELU  c * tanh(relu(h)^2 / c), c = tanh_clamp_scale > 0: the squared ReLU with the tanh
+ *                    soft clamp [NV, Changes and commits: ScaledTanhSReLU, tanh_clamp_scale; the pages
+ *                    give no formula, this is the library's reading]           (F1 = ffn)
+ *   GMLP_QGEGLU      gate * sigmoid(1.702 gate) * up, the GLU with the quick-GELU gate [FB, review: QGeGLU,
+ *                    named without a formula; the gate is the sigmoid approximation of GELU from
+ *                    Hendrycks and Gimpel, "Gaussian Error Linear Units", section 2] (F1 = 2 ffn) */
+typedef enum { GMLP_SWIGLU = 0, GMLP_SRELU = 1, GMLP_TANH_SRELU = 2, GMLP_QGEGLU = 3 } gmlp_activation;
 /* Output of a GEMM: bf16 or fp32 (round to nearest even), or fp32 added to what the output
  * buffer holds: C = fp32(C + product), the weight gradient accumulated into a persistent fp32
  * main_grad [MX, review comments on overwrite_main_grad: the grouped wgrad either overwrites
@@ -244,7 +253,7 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
 
 /* Forward [MX, sequence diagram; NV, Description and Changes]:
  *   h = bf16(Q(x) Q(W1)^T)   a = bf16(act(h) * prob)   y = bf16(Q(a) Q(W2)^T)
- * act = SwiGLU (h = [gate | up], F1 = 2 ffn) or squared ReLU (F1 = ffn).
+ * act: one of gmlp_activation (F1 = 2 ffn for the gated kinds, ffn otherwise).
  * recompute != 0: the forward casts the fc2 input row-wise only and the
  * backward rebuilds it from h (NVFP4: with the amax saved here).
  * ctx must stay untouched between this call and the matching backward. */
@@ -265,10 +274,12 @@ typedef struct {
   void* y;                    /* bf16 [M, H] out */
   void* ctx; size_t ctx_bytes;
   void* ws;  size_t ws_bytes;
-  int32_t fc2_amax_in_fc1;    /* NVFP4 with squared ReLU only (else GMLP_UNSUPPORTED): != 0 takes the fc2
-                                 input's pre- and post-RHT amax in the fc1 GEMM's epilogue [NV, Changes:
-                                 the Hadamard-fused fc1 kernel] instead of a pass over h after it; the
-                                 same values either way (the separate pass is the faster one here) */
+  int32_t fc2_amax_in_fc1;    /* NVFP4 with a squared-ReLU activation (GMLP_SRELU, GMLP_TANH_SRELU) only (else
+                                 GMLP_UNSUPPORTED): != 0 takes the fc2 input's pre- and post-RHT amax in the
+                                 fc1 GEMM's epilogue [NV, Changes: the Hadamard-fused fc1 kernel] instead of
+                                 a pass over h after it; the same values either way (the separate pass is the
+                                 faster one here) */
+  float tanh_clamp_scale;     /* GMLP_TANH_SRELU: c > 0 and finite (else GMLP_INVALID_ARG); ignored otherwise */
 } gmlp_fwd_args;
 
 /* Backward [MX, sequence diagram; NV, commits]:
@@ -298,6 +309,7 @@ typedef struct {
   void* ws; size_t ws_bytes;
   int32_t defer_wgrad;        /* != 0 (with weight_requires_grad): cast the weight-gradient operands into
                                  ws but leave dw1, dw2 to a later gmlp_grouped_mlp_wgrad */
+  float tanh_clamp_scale;     /* GMLP_TANH_SRELU: the forward's c (else GMLP_INVALID_ARG); ignored otherwise */
 } gmlp_bwd_args;
 
 gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* args, hipStream_t stream);

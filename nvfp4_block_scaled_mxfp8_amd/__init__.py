@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgmlp.so")
 
 MXFP8, NVFP4_RHT = 0, 1
-SWIGLU, SRELU = 0, 1
+SWIGLU, SRELU, TANH_SRELU, QGEGLU = 0, 1, 2, 3
 OUT_BF16, OUT_FP32, OUT_FP32_ACCUMULATE = 0, 1, 2
 GEMM_FPROP, GEMM_WGRAD = 0, 1
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP_ERROR"}
@@ -60,7 +60,8 @@ class FwdArgs(ctypes.Structure):
                 ("recompute", ctypes.c_int32), ("input_requires_grad", ctypes.c_int32),
                 ("weight_requires_grad", ctypes.c_int32), ("y", ctypes.c_void_p),
                 ("ctx", ctypes.c_void_p), ("ctx_bytes", ctypes.c_size_t),
-                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("fc2_amax_in_fc1", ctypes.c_int32)]
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("fc2_amax_in_fc1", ctypes.c_int32),
+                ("tanh_clamp_scale", ctypes.c_float)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -73,7 +74,7 @@ class BwdArgs(ctypes.Structure):
                 ("dprobs", ctypes.c_void_p), ("dw1", ctypes.c_void_p), ("dw2", ctypes.c_void_p),
                 ("wgrad_dtype", ctypes.c_int32), ("ctx", ctypes.c_void_p),
                 ("ctx_bytes", ctypes.c_size_t), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
-                ("defer_wgrad", ctypes.c_int32)]
+                ("defer_wgrad", ctypes.c_int32), ("tanh_clamp_scale", ctypes.c_float)]
 
 
 _SIGS = {
@@ -150,9 +151,25 @@ def recipe(kind="mxfp8", sign_mask=0):
     return Recipe(k, int(sign_mask) & 0xFFFF)
 
 
+_ACT_NAMES = {"swiglu": SWIGLU, "srelu": SRELU, "tanh_srelu": TANH_SRELU, "qgeglu": QGEGLU}
+
+
+def activation_spec(act):
+    """An activation as (C enum, tanh clamp scale): 'swiglu', 'srelu', 'qgeglu', or
+    ('tanh_srelu', c); integers (or (int, c)) pass through (the library validates them)."""
+    if isinstance(act, tuple):
+        name, c = act
+        return (name if isinstance(name, int) else _ACT_NAMES[name]), float(c)
+    return (act if isinstance(act, int) else _ACT_NAMES[act]), 0.0
+
+
 def activation_id(act):
-    """'swiglu' / 'srelu' -> the C enum; integers pass through (the library validates them)."""
-    return act if isinstance(act, int) else {"swiglu": SWIGLU, "srelu": SRELU}[act]
+    return activation_spec(act)[0]
+
+
+def is_glu(act):
+    """Gated activations read h = [gate | up] (F1 = 2 ffn)."""
+    return activation_id(act) in (SWIGLU, QGEGLU)
 
 
 def last_error():
@@ -381,17 +398,18 @@ class MlpContext:
     recompute: bool
     input_requires_grad: bool
     weight_requires_grad: bool
+    clamp: float = 0.0             # tanh clamp scale (tanh-clamped squared ReLU)
 
 
 def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute=False,
                         input_requires_grad=True, weight_requires_grad=True, ws=None, y=None, ctx=None,
                         fc2_amax_in_fc1=False):
-    """fc2_amax_in_fc1 (NVFP4, squared ReLU): take the fc2 input's amax in the fc1 GEMM's epilogue
-    instead of a pass over h (the same values)."""
+    """activation: as activation_spec.  fc2_amax_in_fc1 (NVFP4, squared-ReLU activations): take the
+    fc2 input's amax in the fc1 GEMM's epilogue instead of a pass over h (the same values)."""
     x = _bits(x)
     M, H = x.shape
     E = m_splits.numel()
-    act = activation_id(activation)
+    act, clamp = activation_spec(activation)
     ffn = ffn_from_w2(w2q, rec, E, H)
     sizes = query_sizes(M, E, H, ffn, act, rec, recompute)
     dev = x.device
@@ -402,10 +420,10 @@ def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute
     a = FwdArgs(x.data_ptr(), m_splits.data_ptr(), M, E, H, ffn, ctypes.pointer(s1), ctypes.pointer(s2),
                 probs.data_ptr() if M else None, act, rec, int(recompute), int(input_requires_grad),
                 int(weight_requires_grad), y.data_ptr() if M else None, cbuf.data_ptr(), cbuf.numel(),
-                ws.data_ptr(), ws.numel(), int(bool(fc2_amax_in_fc1)))
+                ws.data_ptr(), ws.numel(), int(bool(fc2_amax_in_fc1)), clamp)
     _check(lib().gmlp_grouped_mlp_forward(ctypes.byref(a), _stream(dev)))
     c = MlpContext(cbuf, M, E, H, ffn, act, rec, bool(recompute), bool(input_requires_grad),
-                   bool(weight_requires_grad))
+                   bool(weight_requires_grad), clamp)
     return y, c
 
 
@@ -418,7 +436,7 @@ def forward_saved(ctx):
     h, pre, post = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
     _check(lib().gmlp_forward_saved(ctypes.byref(a), ctypes.byref(h), ctypes.byref(pre), ctypes.byref(post)))
     base = ctx.buf.data_ptr()
-    F1 = 2 * ctx.ffn if ctx.activation == SWIGLU else ctx.ffn
+    F1 = 2 * ctx.ffn if is_glu(ctx.activation) else ctx.ffn
 
     def view(ptr, n, dtype):
         if not ptr.value:
@@ -441,7 +459,7 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
     dy = _bits(dy)
     M, H = dy.shape
     E, ffn, act = ctx.E, ctx.ffn, ctx.activation
-    F1 = 2 * ffn if act == SWIGLU else ffn
+    F1 = 2 * ffn if is_glu(act) else ffn
     dev = dy.device
     sizes = query_sizes(M, E, H, ffn, act, ctx.rec, ctx.recompute)
     ws = ws if ws is not None else torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
@@ -466,7 +484,7 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
                 int(ctx.weight_requires_grad), dx.data_ptr() if (dx is not None and M) else None,
                 dprobs.data_ptr() if M else None, dw1.data_ptr() if dw1 is not None else None,
                 dw2.data_ptr() if dw2 is not None else None, wgrad_dtype, ctx.buf.data_ptr(), ctx.buf.numel(),
-                ws.data_ptr(), ws.numel(), int(bool(defer_wgrad)))
+                ws.data_ptr(), ws.numel(), int(bool(defer_wgrad)), ctx.clamp)
     _check(lib().gmlp_grouped_mlp_backward(ctypes.byref(a), _stream(dev)))
     res = {"dx": dx, "dprobs": dprobs, "dw1": dw1, "dw2": dw2}
     if defer_wgrad and ctx.weight_requires_grad:
@@ -488,7 +506,7 @@ def grouped_mlp_wgrad(deferred, wgrad_dtype=OUT_BF16, out=None):
     ("dw1", "dw2")."""
     ctx, ws = deferred.ctx, deferred.ws
     E, H, ffn, act = ctx.E, ctx.H, ctx.ffn, ctx.activation
-    F1 = 2 * ffn if act == SWIGLU else ffn
+    F1 = 2 * ffn if is_glu(act) else ffn
     dev = ws.device
     wdt = torch.bfloat16 if wgrad_dtype == OUT_BF16 else torch.float32
     o = out or {}
@@ -501,7 +519,7 @@ def grouped_mlp_wgrad(deferred, wgrad_dtype=OUT_BF16, out=None):
         dw2 = o.get("dw2", torch.empty((E, H, ffn), dtype=wdt, device=dev))
     a = BwdArgs()
     a.m_splits, a.M, a.E, a.H, a.ffn = deferred.m_splits.data_ptr(), ctx.M, E, H, ffn
-    a.activation, a.recipe, a.recompute = act, ctx.rec, int(ctx.recompute)
+    a.activation, a.recipe, a.recompute, a.tanh_clamp_scale = act, ctx.rec, int(ctx.recompute), ctx.clamp
     a.input_requires_grad, a.weight_requires_grad = int(ctx.input_requires_grad), 1
     a.dw1, a.dw2, a.wgrad_dtype = dw1.data_ptr(), dw2.data_ptr(), wgrad_dtype
     a.ctx, a.ctx_bytes, a.ws, a.ws_bytes = ctx.buf.data_ptr(), ctx.buf.numel(), ws.data_ptr(), ws.numel()

@@ -248,6 +248,22 @@ gmlp_status weight_ok(const gmlp_weight_q* w, const gmlp_recipe& r, bool fprop, 
 }
 
 // ----------------------------------------------------------------------------- MLP plan
+// Width of h: the gated activations (SwiGLU, QGeGLU) read [gate | up].
+int64_t f1_of(int act, int64_t ffn) { return (act == GMLP_SWIGLU || act == GMLP_QGEGLU) ? 2 * ffn : ffn; }
+// The activation as the kernels take it; its parameter is checked by check_act.
+Act act_of(int act, float tanh_clamp_scale) {
+  Act a;
+  a.kind = act;
+  a.c = act == GMLP_TANH_SRELU ? tanh_clamp_scale : 0.0f;
+  return a;
+}
+gmlp_status check_act(int act, float tanh_clamp_scale) {
+  if (act == GMLP_TANH_SRELU && !(tanh_clamp_scale > 0.0f && tanh_clamp_scale <= 3.0e38f))
+    return fail(GMLP_INVALID_ARG, "activation: the tanh clamp scale must be a positive finite number, got %g",
+                (double)tanh_clamp_scale);
+  return GMLP_OK;
+}
+
 struct FwdCtx {     // saved tensors (in ctx)
   uint16_t* h;
   QBuf xq_col;      // column-wise x (+ NVFP4 amax)
@@ -257,7 +273,7 @@ struct FwdCtx {     // saved tensors (in ctx)
 };
 
 FwdCtx carve_ctx(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, const gmlp_recipe& r, bool recompute) {
-  const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
+  const int64_t F1 = f1_of(act, ffn);
   FwdCtx c{};
   c.h = b.take<uint16_t>(M * F1);
   c.xq_col = carve_q(b, r, M, H, E, false, true, true);
@@ -293,7 +309,7 @@ struct FwdWs {
   NvScratch nv;
 };
 FwdWs carve_fwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, const gmlp_recipe& r) {
-  const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
+  const int64_t F1 = f1_of(act, ffn);
   FwdWs w;
   w.T = carve_tables(b, E);
   w.xq_row = carve_q(b, r, M, H, E, true, false, false);
@@ -316,7 +332,7 @@ struct BwdWs {
 };
 int dact_ntiles(int64_t ffn) { return (int)ceil_div(ffn, 256); }
 BwdWs carve_bwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, const gmlp_recipe& r, bool recompute) {
-  const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
+  const int64_t F1 = f1_of(act, ffn);
   BwdWs w{};
   w.T = carve_tables(b, E);
   w.dyq = carve_q(b, r, M, H, E, true, true, true);
@@ -340,7 +356,8 @@ BwdWs carve_bwd_ws(Bump& b, int64_t M, int E, int64_t H, int64_t ffn, int act, c
 gmlp_status mlp_common_checks(int64_t M, int E, int64_t H, int64_t ffn, int act, const gmlp_recipe& r) {
   gmlp_status st;
   if ((st = check_recipe(r)) != GMLP_OK) return st;
-  if (act != GMLP_SWIGLU && act != GMLP_SRELU) return fail(GMLP_UNSUPPORTED, "activation: unsupported activation %d", act);
+  if (act != GMLP_SWIGLU && act != GMLP_SRELU && act != GMLP_TANH_SRELU && act != GMLP_QGEGLU)
+    return fail(GMLP_UNSUPPORTED, "activation: unsupported activation %d", act);
   if ((st = check_dims(M, H, E)) != GMLP_OK) return st;
   if (ffn <= 0 || ffn % 128 != 0) return fail(GMLP_UNSUPPORTED, "dims: ffn must be a positive multiple of 128, got %lld", (long long)ffn);
   if (H % 128 != 0) return fail(GMLP_UNSUPPORTED, "dims: hidden must be a multiple of 128, got %lld", (long long)H);
@@ -348,7 +365,7 @@ gmlp_status mlp_common_checks(int64_t M, int E, int64_t H, int64_t ffn, int act,
   if (!is_mx(r) && (M + 7) / 8 > 65535)
     return fail(GMLP_UNSUPPORTED, "dims: M = %lld rows exceeds one launch's row range", (long long)M);
   // the GEMMs address every quantized operand with 32-bit offsets
-  const int64_t F1 = act == GMLP_SWIGLU ? 2 * ffn : ffn;
+  const int64_t F1 = f1_of(act, ffn);
   const int64_t eb = is_mx(r) ? 1 : 2;             // NVFP4 operands run expanded to bf16
   if (eb * (M + 127LL * E) * std::max(H, F1) >= (1LL << 32) || eb * (int64_t)E * F1 * H >= (1LL << 32))
     return fail(GMLP_UNSUPPORTED, "dims: a quantized operand would reach 4 GB (M = %lld, hidden %lld, ffn %lld)",
@@ -601,9 +618,13 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
   if ((A->M > 0 && (!A->x || !A->probs || !A->y)) || !A->m_splits) return fail(GMLP_INVALID_ARG, "null pointer argument");
   if ((st = weight_ok(A->w1, A->recipe, true, false)) != GMLP_OK) return st;
   if ((st = weight_ok(A->w2, A->recipe, true, false)) != GMLP_OK) return st;
-  if (A->fc2_amax_in_fc1 && !(A->recipe.kind == GMLP_NVFP4_RHT && A->activation == GMLP_SRELU))
-    return fail(GMLP_UNSUPPORTED, "%s: the fc2-input amax in the fc1 epilogue needs the NVFP4 recipe and squared ReLU",
+  if ((st = check_act(A->activation, A->tanh_clamp_scale)) != GMLP_OK) return st;
+  if (A->fc2_amax_in_fc1 &&
+      !(A->recipe.kind == GMLP_NVFP4_RHT && (A->activation == GMLP_SRELU || A->activation == GMLP_TANH_SRELU)))
+    return fail(GMLP_UNSUPPORTED,
+                "%s: the fc2-input amax in the fc1 epilogue needs the NVFP4 recipe and a squared-ReLU activation",
                 A->recipe.kind == GMLP_NVFP4_RHT ? "activation" : "recipe");
+  const Act act = act_of(A->activation, A->tanh_clamp_scale);
   const bool mx = is_mx(A->recipe);
   const bool wgrad = A->weight_requires_grad != 0;
   const bool rec = A->recompute != 0;
@@ -651,13 +672,13 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
   {
     GemmArgs g = gemm_base(MODE_FPROP, r, fused_amax ? EPI_STORE_AMAX : EPI_STORE, W.T, E);
     g.M = M;
-    g.N = A->activation == GMLP_SWIGLU ? 2 * ffn : ffn;
+    g.N = f1_of(A->activation, ffn);
     g.K = H;
     g.a = op_row(W.xq_row.q, x_pre);
     g.b = op_row(*A->w1, A->w1->amax_pre);
     g.c = C.h;
     if (fused_amax) {
-      g.act = GMLP_SRELU;
+      g.act = act;
       g.ffn = ffn;
       g.probs = A->probs;
       g.rht_mask = r.rht_sign_mask & 0xFFFF;
@@ -675,14 +696,14 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     MxOut o{static_cast<uint8_t*>(W.aq_row.q.row_data), nullptr, static_cast<uint32_t*>(W.aq_row.q.row_scale_mfma),
             a_col ? static_cast<uint8_t*>(C.aq_col.q.col_data) : nullptr, nullptr,
             a_col ? static_cast<uint32_t*>(C.aq_col.q.col_scale_mfma) : nullptr};
-    if (!L.check(launch_act_quant(C.h, A->probs, A->activation, ffn, W.T, E, M, o, stream), "fc2 input cast"))
+    if (!L.check(launch_act_quant(C.h, A->probs, act, ffn, W.T, E, M, o, stream), "fc2 input cast"))
       return L.st;
     g_counts[CNT_MXQ]++;
   } else {
     ActSrc src;
     src.h = C.h;
     src.probs = A->probs;
-    src.act = A->activation;
+    src.act = act;
     src.ffn = ffn;
     if (!fused_amax) {
       if (!L.check(launch_hadamard_amax(C.h, M, ffn, W.T, E, r.rht_sign_mask & 0xFFFF, C.a_pre, C.a_post, stream,
@@ -758,7 +779,7 @@ bool fc2_wgrad(const gmlp_bwd_args* A, const FwdCtx& C, const BwdWs& W, Launcher
 
 // fc1 wgrad: dW1_g = Qc(dh_g)^T Qc(x_g).
 bool fc1_wgrad(const gmlp_bwd_args* A, const FwdCtx& C, const BwdWs& W, Launcher& L, hipStream_t stream) {
-  const int64_t F1 = A->activation == GMLP_SWIGLU ? 2 * A->ffn : A->ffn;
+  const int64_t F1 = f1_of(A->activation, A->ffn);
   GemmArgs g = gemm_base(MODE_WGRAD, A->recipe, EPI_STORE, W.T, A->E);
   g.M = A->M;
   g.N = F1;
@@ -782,6 +803,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
   if (!A) return fail(GMLP_INVALID_ARG, "null args");
   gmlp_status st = mlp_common_checks(A->M, A->E, A->H, A->ffn, A->activation, A->recipe);
   if (st != GMLP_OK) return st;
+  if ((st = check_act(A->activation, A->tanh_clamp_scale)) != GMLP_OK) return st;
   const bool dgrad = A->input_requires_grad != 0;
   const bool wgrad = A->weight_requires_grad != 0;
   const bool defer = wgrad && A->defer_wgrad != 0;
@@ -795,7 +817,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
   const bool rec = A->recompute != 0;
   const int E = A->E;
   const int64_t M = A->M, H = A->H, ffn = A->ffn;
-  const int64_t F1 = A->activation == GMLP_SWIGLU ? 2 * ffn : ffn;
+  const int64_t F1 = f1_of(A->activation, ffn);
   const gmlp_recipe& r = A->recipe;
   const uint32_t mask = r.rht_sign_mask & 0xFFFF;
   Bump cb(const_cast<void*>(A->ctx));
@@ -849,7 +871,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     d.da = da;
     d.h = C.h;
     d.probs = A->probs;
-    d.act = A->activation;
+    d.act = act_of(A->activation, A->tanh_clamp_scale);
     d.ffn = ffn;
     d.dh = MxOut{dgrad ? static_cast<uint8_t*>(W.dhq.q.row_data) : nullptr, nullptr,
                  dgrad ? static_cast<uint32_t*>(W.dhq.q.row_scale_mfma) : nullptr,
@@ -873,7 +895,7 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
     g.K = H;
     g.a = op_row(W.dyq.q, W.dyq.q.amax_pre);
     g.b = op_col(*A->w2, A->w2->amax_pre);
-    g.act = A->activation;
+    g.act = act_of(A->activation, A->tanh_clamp_scale);
     g.ffn = ffn;
     g.probs = A->probs;
     g.h = C.h;

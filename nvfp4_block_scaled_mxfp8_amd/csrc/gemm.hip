@@ -683,7 +683,9 @@ __device__ __forceinline__ void epi_chunk_amax(const GemmArgs& A, const Ctx& c, 
       const int tr = chunk_row(TM, sr);
       const bool ok = col_ok && tr < c.arows;
       const float h = round_bf16(__fmul_rn(st[sr * EPC_LD + sc], c.alpha));
-      const float a = ok ? act_out(1, h, 0.0f, probs[tr]) : 0.0f;
+      const float a = !ok ? 0.0f
+                          : A.act.kind == ACT_TANH_SRELU ? act_out<ACT_TANH_SRELU>(h, 0.0f, probs[tr], A.act.c)
+                                                         : act_out<ACT_SRELU>(h, 0.0f, probs[tr], A.act.c);
       pre = fmaxf(pre, fabsf(a));
       v[i] = a;
     }

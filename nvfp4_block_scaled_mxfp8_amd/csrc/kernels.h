@@ -5,6 +5,13 @@
 
 namespace gmlp {
 
+// Activation of the fc2 input: kind (0 SwiGLU, 1 squared ReLU, 2 tanh-clamped squared ReLU,
+// 3 QGeGLU; the C ABI's gmlp_activation) and the clamp scale c of kind 2.
+struct Act {
+  int kind = 0;
+  float c = 0.0f;
+};
+
 // Per-call split tables, computed on the device from m_splits (all int32, length G+1,
 // exclusive prefix sums; row counts clamped so that row_off[G] <= M).
 struct SplitTables {
@@ -35,7 +42,7 @@ struct DactArgs {
   const uint16_t* da;   // [M, ffn] bf16: dy W2
   const uint16_t* h;    // [M, F1] bf16: fc1 output ([gate | up] for SwiGLU)
   const float* probs;   // [M]
-  int act;              // 0 SwiGLU, 1 squared ReLU
+  Act act;
   int64_t ffn;
   MxOut dh;             // MXFP8 dh [M, F1], row- and/or column-wise (null pointers: not written)
   MxOut a2;             // column-wise MXFP8 of the rebuilt fc2 input [M, ffn], or all null
@@ -62,7 +69,7 @@ hipError_t launch_mxfp8_quant(const uint16_t* x, int64_t M, int64_t K, SplitTabl
 hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M, hipStream_t s);
 // MXFP8 forward: the fc2 input a = bf16(act(h) p) from the fc1 output h [M, F1], cast row-wise
 // (and column-wise when o.col_data is set) without writing a.
-hipError_t launch_act_quant(const uint16_t* h, const float* probs, int act, int64_t ffn, SplitTables T, int G,
+hipError_t launch_act_quant(const uint16_t* h, const float* probs, Act act, int64_t ffn, SplitTables T, int G,
                             int64_t M, MxOut o, hipStream_t s);
 // The input of an NVFP4 amax pass or cast: x itself (h == nullptr) or the fc2 input
 // a = bf16(act(h) p) [M, ffn], formed on the fly from the fc1 output h [M, F1] (F1 = 2 ffn for
@@ -70,7 +77,7 @@ hipError_t launch_act_quant(const uint16_t* h, const float* probs, int act, int6
 struct ActSrc {
   const uint16_t* h = nullptr;
   const float* probs = nullptr;
-  int act = 0;          // 0 SwiGLU, 1 squared ReLU
+  Act act;
   int64_t ffn = 0;
 };
 hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G,
@@ -96,7 +103,7 @@ hipError_t launch_nv_expand_groups(const uint8_t* data, const uint8_t* scale, ui
                                    int64_t cols_bound, const int32_t* col_off, int G, hipStream_t s);
 // NVFP4 backward: bf16 dh (and the rebuilt fc2 input a2 when non-null) from bf16 da and h, with
 // the dL/dp partials of each 256-feature tile in dprob_part [ceil(ffn / 256)][M].
-hipError_t launch_dact_bf16(const uint16_t* da, const uint16_t* h, const float* probs, int act, int64_t ffn,
+hipError_t launch_dact_bf16(const uint16_t* da, const uint16_t* h, const float* probs, Act act, int64_t ffn,
                             int64_t M, uint16_t* dh, uint16_t* a2, float* dprob_part, hipStream_t s);
 
 // ----------------------------------------------------------------------------- GEMM
@@ -131,8 +138,8 @@ struct GemmArgs {
   void* c;           // EPI_STORE: C (bf16 or fp32)
   int out_fp32;      // 0 bf16, 1 fp32, 2 fp32 added to C (WGRAD)
   // EPI_DACT (NVFP4 fc2 dgrad): operands of the activation-gradient pass run after the GEMM
-  int act;           // 0 SwiGLU, 1 SReLU
-  int64_t ffn;       // EPI_DACT: ffn (width of da and a'); SwiGLU F1 = 2 ffn
+  Act act;
+  int64_t ffn;       // EPI_DACT: ffn (width of da and a'); gated kinds F1 = 2 ffn
   const float* probs;
   uint16_t* h;       // EPI_DACT: in h [M, F1]
   uint16_t* a_out;   // EPI_DACT: out a' (recompute) or null

@@ -140,9 +140,10 @@ __device__ __forceinline__ void unpack8(const uint4& q, float* v);
 __device__ __forceinline__ uint4 load_in8(const uint16_t* __restrict__ x, int64_t K, const ActSrc& A, int64_t row,
                                           int64_t k) {
   if (!A.h) return *reinterpret_cast<const uint4*>(x + row * K + k);
-  const int64_t F1 = A.act == 0 ? 2 * A.ffn : A.ffn;
+  const bool glu = act_is_glu(A.act.kind);
+  const int64_t F1 = glu ? 2 * A.ffn : A.ffn;
   const uint4 gq = *reinterpret_cast<const uint4*>(A.h + row * F1 + k);
-  const uint4 uq = A.act == 0 ? *reinterpret_cast<const uint4*>(A.h + row * F1 + A.ffn + k) : make_uint4(0, 0, 0, 0);
+  const uint4 uq = glu ? *reinterpret_cast<const uint4*>(A.h + row * F1 + A.ffn + k) : make_uint4(0, 0, 0, 0);
   const float p = A.probs[row];
   float g[8], u[8];
   unpack8(gq, g);
@@ -150,8 +151,8 @@ __device__ __forceinline__ uint4 load_in8(const uint16_t* __restrict__ x, int64_
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float lo = act_out(A.act, g[2 * i], u[2 * i], p);
-    const float hi = act_out(A.act, g[2 * i + 1], u[2 * i + 1], p);
+    const float lo = act_out_rt(A.act, g[2 * i], u[2 * i], p);
+    const float hi = act_out_rt(A.act, g[2 * i + 1], u[2 * i + 1], p);
     w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
@@ -394,12 +395,13 @@ __device__ __forceinline__ void col_cast_tile64(const uint16_t* tile, const Tile
   }
 }
 
-template <bool SWIGLU, bool WANT_A>
+template <int KIND, bool WANT_A>
 __global__ __launch_bounds__(256) void dact_quant_kernel(DactArgs D, SplitTables T, int G, int64_t M) {
-  constexpr int NT = 1 + (SWIGLU ? 1 : 0) + (WANT_A ? 1 : 0);   // parked tiles: dgate (dh), dup, a
+  constexpr bool GLU = act_is_glu(KIND);      // [gate | up] layout (SwiGLU, QGeGLU)
+  constexpr int NT = 1 + (GLU ? 1 : 0) + (WANT_A ? 1 : 0);   // parked tiles: dgate (dh), dup, a
   __shared__ __align__(16) uint16_t tiles[NT][MQT * DLW];
   const int64_t ffn = D.ffn;
-  const int64_t F1 = SWIGLU ? 2 * ffn : ffn;
+  const int64_t F1 = GLU ? 2 * ffn : ffn;
   // 64-token half tiles (as the MXFP8 cast); a half past the group's rows still writes its
   // column-wise padding
   TileInfo ti;
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(256) void dact_quant_kernel(DactArgs D, SplitTables
     const int64_t row = ti.gstart + ti.t0 + r;
     qd[j] = ok ? *reinterpret_cast<const uint4*>(D.da + row * ffn + ti.k0 + 8 * g) : make_uint4(0, 0, 0, 0);
     qg[j] = ok ? *reinterpret_cast<const uint4*>(D.h + row * F1 + ti.k0 + 8 * g) : make_uint4(0, 0, 0, 0);
-    qu[j] = (SWIGLU && ok) ? *reinterpret_cast<const uint4*>(D.h + row * F1 + ffn + ti.k0 + 8 * g)
+    qu[j] = (GLU && ok) ? *reinterpret_cast<const uint4*>(D.h + row * F1 + ffn + ti.k0 + 8 * g)
                            : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
@@ -447,9 +449,9 @@ __global__ __launch_bounds__(256) void dact_quant_kernel(DactArgs D, SplitTables
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         float dp, av = 0.0f;
-        const float u = SWIGLU ? vu[i + k] : 0.0f;
-        if (WANT_A) act_grad_out(SWIGLU ? 0 : 1, vg[i + k], u, vd[i + k], p, r0[k], r1[k], dp, av);
-        else act_grad(SWIGLU ? 0 : 1, vg[i + k], u, vd[i + k], p, r0[k], r1[k], dp);
+        const float u = GLU ? vu[i + k] : 0.0f;
+        if (WANT_A) act_grad_out<KIND>(vg[i + k], u, vd[i + k], p, D.act.c, r0[k], r1[k], dp, av);
+        else act_grad<KIND>(vg[i + k], u, vd[i + k], p, D.act.c, r0[k], r1[k], dp);
         psum += dp;
         ra[k] = av;
       }
@@ -496,13 +498,13 @@ __global__ __launch_bounds__(256) void dact_quant_kernel(DactArgs D, SplitTables
       *reinterpret_cast<uint4*>(tile + dtile_off(r, 8 * g)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     };
     row_cast(p0, ti.k0 + 8 * g, tiles[0]);
-    if (SWIGLU) row_cast(p1, ffn + ti.k0 + 8 * g, tiles[1]);
+    if (GLU) row_cast(p1, ffn + ti.k0 + 8 * g, tiles[1]);
     if (WANT_A) *reinterpret_cast<uint4*>(tiles[NT - 1] + dtile_off(r, 8 * g)) = make_uint4(pa[0], pa[1], pa[2], pa[3]);
   }
   __syncthreads();
   if (D.dh.col_data) {
     col_cast_tile64(tiles[0], ti, F1, ti.k0, T, D.dh, tid);
-    if (SWIGLU) col_cast_tile64(tiles[1], ti, F1, ffn + ti.k0, T, D.dh, tid);
+    if (GLU) col_cast_tile64(tiles[1], ti, F1, ffn + ti.k0, T, D.dh, tid);
   }
   if (WANT_A) col_cast_tile64(tiles[NT - 1], ti, ffn, ti.k0, T, D.a2, tid);
 }
@@ -513,11 +515,13 @@ __global__ __launch_bounds__(256) void dact_quant_kernel(DactArgs D, SplitTables
 // match) is cast row-wise for the fc2 GEMM and, when o.col_data is set, column-wise for the fc2
 // wgrad; a itself is never written.  Half tiles and thread layout as in dact_quant_kernel:
 // 64 tokens x 64 features of a (SwiGLU: gate feature f and up feature ffn + f of h).
-template <bool SWIGLU>
+template <int KIND>
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ h, const float* __restrict__ probs,
-                                                        int64_t ffn, SplitTables T, int G, int64_t M, MxOut o) {
+                                                        float act_c, int64_t ffn, SplitTables T, int G, int64_t M,
+                                                        MxOut o) {
+  constexpr bool GLU = act_is_glu(KIND);      // [gate | up] layout (SwiGLU, QGeGLU)
   __shared__ __align__(16) uint16_t tile[MQT * DLW];
-  const int64_t F1 = SWIGLU ? 2 * ffn : ffn;
+  const int64_t F1 = GLU ? 2 * ffn : ffn;
   TileInfo ti;
   {
     const int tt = blockIdx.y >> 1;
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
     const bool ok = r < ti.rows;
     const int64_t row = ti.gstart + ti.t0 + r;
     qg[j] = ok ? *reinterpret_cast<const uint4*>(h + row * F1 + ti.k0 + 8 * g) : make_uint4(0, 0, 0, 0);
-    qu[j] = (SWIGLU && ok) ? *reinterpret_cast<const uint4*>(h + row * F1 + ffn + ti.k0 + 8 * g) : make_uint4(0, 0, 0, 0);
+    qu[j] = (GLU && ok) ? *reinterpret_cast<const uint4*>(h + row * F1 + ffn + ti.k0 + 8 * g) : make_uint4(0, 0, 0, 0);
   }
   const int64_t f = ti.k0 + 8 * g;
 #pragma unroll
@@ -554,7 +558,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
     unpack8(qu[j], vu);
     uint32_t pa[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = act_out(SWIGLU ? 0 : 1, vg[i], SWIGLU ? vu[i] : 0.0f, p);
+    for (int i = 0; i < 8; ++i) v[i] = act_out<KIND>(vg[i], GLU ? vu[i] : 0.0f, p, act_c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pa[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
     // row-wise cast: a 32-feature block is a lane quad; the tile's two blocks are bytes b, b + 1
@@ -863,19 +867,39 @@ hipError_t launch_dact_quant(const DactArgs& d, SplitTables T, int G, int64_t M,
   if (M == 0) return hipSuccess;
   const dim3 grid((unsigned)(d.ffn / DF), (unsigned)(2 * ((M + QT - 1) / QT + G)));   // half tiles
   const bool a = d.a2.col_data != nullptr;
-  if (d.act == 0 && !a) hipLaunchKernelGGL((dact_quant_kernel<true, false>), grid, dim3(256), 0, s, d, T, G, M);
-  else if (d.act == 0) hipLaunchKernelGGL((dact_quant_kernel<true, true>), grid, dim3(256), 0, s, d, T, G, M);
-  else if (!a) hipLaunchKernelGGL((dact_quant_kernel<false, false>), grid, dim3(256), 0, s, d, T, G, M);
-  else hipLaunchKernelGGL((dact_quant_kernel<false, true>), grid, dim3(256), 0, s, d, T, G, M);
+#define GMLP_DACT(K)                                                                                  \
+  if (a) hipLaunchKernelGGL((dact_quant_kernel<K, true>), grid, dim3(256), 0, s, d, T, G, M);        \
+  else hipLaunchKernelGGL((dact_quant_kernel<K, false>), grid, dim3(256), 0, s, d, T, G, M);
+  switch (d.act.kind) {
+    case ACT_SWIGLU: GMLP_DACT(ACT_SWIGLU) break;
+    case ACT_SRELU: GMLP_DACT(ACT_SRELU) break;
+    case ACT_TANH_SRELU: GMLP_DACT(ACT_TANH_SRELU) break;
+    case ACT_QGEGLU: GMLP_DACT(ACT_QGEGLU) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef GMLP_DACT
   return hipGetLastError();
 }
 
-hipError_t launch_act_quant(const uint16_t* h, const float* probs, int act, int64_t ffn, SplitTables T, int G,
+hipError_t launch_act_quant(const uint16_t* h, const float* probs, Act act, int64_t ffn, SplitTables T, int G,
                             int64_t M, MxOut o, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const dim3 grid((unsigned)(ffn / DF), (unsigned)(2 * ((M + QT - 1) / QT + G)));   // half tiles
-  if (act == 0) hipLaunchKernelGGL((act_quant_kernel<true>), grid, dim3(256), 0, s, h, probs, ffn, T, G, M, o);
-  else hipLaunchKernelGGL((act_quant_kernel<false>), grid, dim3(256), 0, s, h, probs, ffn, T, G, M, o);
+  switch (act.kind) {
+    case ACT_SWIGLU:
+      hipLaunchKernelGGL((act_quant_kernel<ACT_SWIGLU>), grid, dim3(256), 0, s, h, probs, act.c, ffn, T, G, M, o);
+      break;
+    case ACT_SRELU:
+      hipLaunchKernelGGL((act_quant_kernel<ACT_SRELU>), grid, dim3(256), 0, s, h, probs, act.c, ffn, T, G, M, o);
+      break;
+    case ACT_TANH_SRELU:
+      hipLaunchKernelGGL((act_quant_kernel<ACT_TANH_SRELU>), grid, dim3(256), 0, s, h, probs, act.c, ffn, T, G, M, o);
+      break;
+    case ACT_QGEGLU:
+      hipLaunchKernelGGL((act_quant_kernel<ACT_QGEGLU>), grid, dim3(256), 0, s, h, probs, act.c, ffn, T, G, M, o);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1003,20 +1027,21 @@ hipError_t launch_nv_expand_groups(const uint8_t* data, const uint8_t* scale, ui
 // each 256-feature tile (summed over its features in a fixed lane order) in dprob_part[tile][row].
 // Block = 8 rows x 256 features; thread -> row 8 by + tid / 32, features 8 (tid % 32) .. + 7.
 __global__ __launch_bounds__(256) void dact_bf16_kernel(const uint16_t* __restrict__ da, const uint16_t* __restrict__ h,
-                                                        const float* __restrict__ probs, int act, int64_t ffn,
+                                                        const float* __restrict__ probs, Act act, int64_t ffn,
                                                         int64_t M, uint16_t* __restrict__ dh, uint16_t* __restrict__ a2,
                                                         float* __restrict__ dprob_part) {
   const int tid = threadIdx.x;
   const int64_t row = (int64_t)blockIdx.y * 8 + (tid >> 5);
   if (row >= M) return;                                    // whole 32-lane row groups leave together
-  const int64_t F1 = act == 0 ? 2 * ffn : ffn;
+  const bool glu = act_is_glu(act.kind);
+  const int64_t F1 = glu ? 2 * ffn : ffn;
   const int64_t f = (int64_t)blockIdx.x * 256 + 8 * (tid & 31);
   float psum = 0.0f;
   if (f < ffn) {
     const float p = probs[row];
     const uint4 dv = *reinterpret_cast<const uint4*>(da + row * ffn + f);
     const uint4 gv = *reinterpret_cast<const uint4*>(h + row * F1 + f);
-    const uint4 uv = act == 0 ? *reinterpret_cast<const uint4*>(h + row * F1 + ffn + f) : make_uint4(0, 0, 0, 0);
+    const uint4 uv = glu ? *reinterpret_cast<const uint4*>(h + row * F1 + ffn + f) : make_uint4(0, 0, 0, 0);
     const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
     uint32_t o0[4], o1[4], oa[4];
 #pragma unroll
@@ -1028,7 +1053,7 @@ __global__ __launch_bounds__(256) void dact_bf16_kernel(const uint16_t* __restri
         const float g = bf16_to_f32((gw[i] >> (16 * hh)) & 0xFFFFu);
         const float u = bf16_to_f32((uw[i] >> (16 * hh)) & 0xFFFFu);
         float d0, d1, dp, av;
-        act_grad_out(act, g, u, dav, p, d0, d1, dp, av);
+        act_grad_out_rt(act, g, u, dav, p, d0, d1, dp, av);
         psum += dp;
         r0 |= f32_to_bf16_bits(d0) << (16 * hh);
         r1 |= f32_to_bf16_bits(d1) << (16 * hh);
@@ -1039,7 +1064,7 @@ __global__ __launch_bounds__(256) void dact_bf16_kernel(const uint16_t* __restri
       oa[i] = ra;
     }
     *reinterpret_cast<uint4*>(dh + row * F1 + f) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-    if (act == 0) *reinterpret_cast<uint4*>(dh + row * F1 + ffn + f) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    if (glu) *reinterpret_cast<uint4*>(dh + row * F1 + ffn + f) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
     if (a2) *reinterpret_cast<uint4*>(a2 + row * ffn + f) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
   }
 #pragma unroll
@@ -1047,7 +1072,7 @@ __global__ __launch_bounds__(256) void dact_bf16_kernel(const uint16_t* __restri
   if ((tid & 31) == 0) dprob_part[(int64_t)blockIdx.x * M + row] = psum;
 }
 
-hipError_t launch_dact_bf16(const uint16_t* da, const uint16_t* h, const float* probs, int act, int64_t ffn, int64_t M,
+hipError_t launch_dact_bf16(const uint16_t* da, const uint16_t* h, const float* probs, Act act, int64_t ffn, int64_t M,
                             uint16_t* dh, uint16_t* a2, float* dprob_part, hipStream_t s) {
   if (M == 0) return hipSuccess;
   hipLaunchKernelGGL(dact_bf16_kernel, dim3((unsigned)((ffn + 255) / 256), (unsigned)((M + 7) / 8)), dim3(256), 0, s,

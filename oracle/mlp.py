@@ -24,6 +24,15 @@ Readings (the pages are silent on these):
 * SwiGLU: h = [gate | up] along F1 = 2 * ffn; a = silu(gate) * up * p.
   SReLU: F1 = ffn; a = max(h, 0)^2 * p.  p multiplies after the activation,
   before the bf16 rounding.
+* The tanh-clamped SReLU ("Reduce NVFP4 quantization work ...", Changes and
+  commits: ScaledTanhSReLU, its soft clamp and tanh_clamp_scale; no formula on
+  the pages): F1 = ffn; a = c * tanh(max(h, 0)^2 / c) * p with c the clamp
+  scale, i.e. the squared ReLU softly clamped to (0, c).  Written
+  ("tanh_srelu", c).
+* QGeGLU ("Add NVTE_CUTEDSL_FUSED_GROUPED_MLP_WARN_FALLBACK ...", review: named
+  only): the GLU with the quick-GELU gate, h = [gate | up], a = gate *
+  sigmoid(1.702 gate) * up * p (the sigmoid approximation of GELU, Hendrycks and
+  Gimpel, "Gaussian Error Linear Units", section 2).
 * h, a, y, da, dh, dx and the weight gradients are bf16 (round to nearest
   even); dprob is fp32.  Activations are evaluated in fp64 from bf16 h.
 * Backward operands: dy row-wise (blocks along H) times W2 quantized along H
@@ -50,36 +59,68 @@ from .rht import group_hadamard_amax
 
 SWIGLU = "swiglu"
 SRELU = "srelu"
+TANH_SRELU = "tanh_srelu"
+QGEGLU = "qgeglu"
+QUICK_GELU_K = 1.702
 MXFP8 = "mxfp8"
 NVFP4 = "nvfp4"
+
+
+def act_kind(activation):
+    """(name, clamp scale or None): an activation is a name or ("tanh_srelu", c)."""
+    if isinstance(activation, tuple):
+        name, c = activation
+        return name, float(c)
+    return activation, None
+
+
+def is_glu(activation):
+    """The gated activations read h = [gate | up]."""
+    return act_kind(activation)[0] in (SWIGLU, QGEGLU)
 
 
 def _sigmoid(x):
     return 1.0 / (1.0 + np.exp(-x))
 
 
+def _gate(g, kind):
+    """The gate's value g s(k g) and its derivative s (1 + k g (1 - s)) (k = 1 for SwiGLU)."""
+    k = QUICK_GELU_K if kind == QGEGLU else 1.0
+    s = _sigmoid(k * g)
+    return g * s, s * (1.0 + k * g * (1.0 - s))
+
+
 def act_forward(h, activation):
     """Activation value without the prob, from bf16 h (fp64)."""
-    if activation == SWIGLU:
+    kind, c = act_kind(activation)
+    if kind in (SWIGLU, QGEGLU):
         f = h.shape[1] // 2
         g, u = h[:, :f], h[:, f:]
-        return g * _sigmoid(g) * u
+        return _gate(g, kind)[0] * u
     r = np.maximum(h, 0.0)
+    if kind == TANH_SRELU:
+        return c * np.tanh(r * r / c)
+    assert kind == SRELU, kind
     return r * r
 
 
 def act_backward(h, da, p, activation):
     """(dh, dprob) for a = act(h) * p given da = dL/da; dh unrounded fp64, dprob fp64."""
-    if activation == SWIGLU:
+    kind, c = act_kind(activation)
+    if kind in (SWIGLU, QGEGLU):
         f = h.shape[1] // 2
         g, u = h[:, :f], h[:, f:]
-        sg = _sigmoid(g)
-        silu = g * sg
-        dgate = da * p[:, None] * u * sg * (1.0 + g * (1.0 - sg))
-        dup = da * p[:, None] * silu
-        dprob = np.sum(da * silu * u, axis=1)
+        gs, dgs = _gate(g, kind)
+        dgate = da * p[:, None] * u * dgs
+        dup = da * p[:, None] * gs
+        dprob = np.sum(da * gs * u, axis=1)
         return np.concatenate([dgate, dup], axis=1), dprob
     r = np.maximum(h, 0.0)
+    if kind == TANH_SRELU:
+        t = np.tanh(r * r / c)
+        dh = da * p[:, None] * (1.0 - t * t) * 2.0 * r
+        dprob = np.sum(da * c * t, axis=1)
+        return dh, dprob
     dh = da * p[:, None] * 2.0 * r
     dprob = np.sum(da * r * r, axis=1)
     return dh, dprob
@@ -296,7 +337,7 @@ def mxfp8_wgrad_entries(x_bits, dy_bits, p, wd1, wd2, activation, dw1_idx, dw2_i
     dy = bf16_bits_to_f64(dy_bits)
     xd, dyd = _mx_rows(x), _mx_rows(dy)
     ffn = wd2["row"].shape[1]
-    glu = activation == SWIGLU
+    glu = is_glu(activation)
 
     def h_cols(j):
         cols = [j, ffn + j] if glu else [j]
@@ -339,4 +380,5 @@ def rel_fro(a, b):
 __all__ = ["forward", "backward", "grouped_gemm_nt", "quantize_activation", "quantize_weight",
            "mxfp8_rows", "mxfp8_wgrad_entries",
            "act_forward", "act_backward", "Recipe", "reference_mlp_f64", "rel_fro",
-           "SWIGLU", "SRELU", "MXFP8", "NVFP4", "padded", "mxfp8_quantize_rows"]
+           "SWIGLU", "SRELU", "TANH_SRELU", "QGEGLU", "MXFP8", "NVFP4", "padded", "mxfp8_quantize_rows",
+           "act_kind", "is_glu"]

@@ -120,7 +120,7 @@ int main() {
 
   // ---------------------------------------------------------------- fused MLP
   for (int kind = 0; kind < 2; ++kind) {
-    for (int act = 0; act < 2; ++act) {
+    for (int act = 0; act < 4; ++act) {
       for (int rec = 0; rec < 2; ++rec) {
         const gmlp_recipe r = kind ? nv : mx;
         const int64_t M = 3000, H = 512, ffn = 384;
@@ -140,6 +140,7 @@ int main() {
         f.w2 = &w2;
         f.probs = static_cast<const float*>(fake(0xB0000000));
         f.activation = act;
+        f.tanh_clamp_scale = act == GMLP_TANH_SRELU ? 8.0f : 0.0f;
         f.recipe = r;
         f.recompute = rec;
         f.input_requires_grad = f.weight_requires_grad = 1;
@@ -150,8 +151,16 @@ int main() {
         f.ws_bytes = sz.ws_bytes;
         EXPECT(gmlp_grouped_mlp_forward(&f, nullptr), GMLP_OK);
         f.fc2_amax_in_fc1 = 1;
-        EXPECT(gmlp_grouped_mlp_forward(&f, nullptr), (kind == 1 && act == GMLP_SRELU) ? GMLP_OK : GMLP_UNSUPPORTED);
+        EXPECT(gmlp_grouped_mlp_forward(&f, nullptr),
+               (kind == 1 && (act == GMLP_SRELU || act == GMLP_TANH_SRELU)) ? GMLP_OK : GMLP_UNSUPPORTED);
         f.fc2_amax_in_fc1 = 0;
+        if (act == GMLP_TANH_SRELU) {        // the clamp scale must be positive and finite
+          f.tanh_clamp_scale = 0.0f;
+          EXPECT(gmlp_grouped_mlp_forward(&f, nullptr), GMLP_INVALID_ARG);
+          f.tanh_clamp_scale = -1.0f;
+          EXPECT(gmlp_grouped_mlp_forward(&f, nullptr), GMLP_INVALID_ARG);
+          f.tanh_clamp_scale = 8.0f;
+        }
         void* h = nullptr;
         float *pre = nullptr, *post = nullptr;
         EXPECT(gmlp_forward_saved(&f, &h, &pre, &post), GMLP_OK);
@@ -172,6 +181,7 @@ int main() {
         b.w2 = &w2;
         b.probs = f.probs;
         b.activation = act;
+        b.tanh_clamp_scale = f.tanh_clamp_scale;
         b.recipe = r;
         b.recompute = rec;
         b.input_requires_grad = b.weight_requires_grad = 1;
@@ -185,6 +195,11 @@ int main() {
         b.ws = f.ws;
         b.ws_bytes = sz.ws_bytes;
         EXPECT(gmlp_grouped_mlp_backward(&b, nullptr), GMLP_OK);
+        if (act == GMLP_TANH_SRELU) {
+          b.tanh_clamp_scale = 0.0f;
+          EXPECT(gmlp_grouped_mlp_backward(&b, nullptr), GMLP_INVALID_ARG);
+          b.tanh_clamp_scale = f.tanh_clamp_scale;
+        }
         b.defer_wgrad = 1;
         EXPECT(gmlp_grouped_mlp_backward(&b, nullptr), GMLP_OK);
         EXPECT(gmlp_grouped_mlp_wgrad(&b, nullptr), GMLP_OK);

@@ -13,7 +13,7 @@ hipError_t launch_mxfp8_quant(const uint16_t*, int64_t, int64_t, SplitTables, in
   return hipSuccess;
 }
 hipError_t launch_dact_quant(const DactArgs&, SplitTables, int, int64_t, hipStream_t) { return hipSuccess; }
-hipError_t launch_act_quant(const uint16_t*, const float*, int, int64_t, SplitTables, int, int64_t, MxOut,
+hipError_t launch_act_quant(const uint16_t*, const float*, Act, int64_t, SplitTables, int, int64_t, MxOut,
                             hipStream_t) {
   return hipSuccess;
 }
@@ -39,7 +39,7 @@ hipError_t launch_nv_expand_groups(const uint8_t*, const uint8_t*, uint8_t*, int
                                    hipStream_t) {
   return hipSuccess;
 }
-hipError_t launch_dact_bf16(const uint16_t*, const uint16_t*, const float*, int, int64_t, int64_t, uint16_t*,
+hipError_t launch_dact_bf16(const uint16_t*, const uint16_t*, const float*, Act, int64_t, int64_t, uint16_t*,
                             uint16_t*, float*, hipStream_t) {
   return hipSuccess;
 }

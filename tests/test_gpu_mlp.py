@@ -63,10 +63,15 @@ def _compare(out, wl, kind, backward=True):
     return errs
 
 
-CASES = [("mxfp8", "swiglu"), ("nvfp4", "srelu"), ("mxfp8", "srelu"), ("nvfp4", "swiglu")]
+# The tanh-clamped squared ReLU with clamp scale 2 (h has a standard deviation near 1 here, so the
+# clamp bends a fair share of the values without flattening them) and QGeGLU.
+TANH_SRELU = ("tanh_srelu", 2.0)
+CASES = [("mxfp8", "swiglu"), ("nvfp4", "srelu"), ("mxfp8", "srelu"), ("nvfp4", "swiglu"),
+         ("mxfp8", TANH_SRELU), ("nvfp4", TANH_SRELU), ("mxfp8", "qgeglu"), ("nvfp4", "qgeglu")]
+CASE_IDS = [f"{k}-{a if isinstance(a, str) else a[0]}" for k, a in CASES]
 
 
-@pytest.mark.parametrize("kind,act", CASES)
+@pytest.mark.parametrize("kind,act", CASES, ids=CASE_IDS)
 def test_mlp_forward_backward_matches_oracle(kind, act):
     print(f"mlp {kind} {act}", flush=True)
     wl = small_case([0, 37, 300, 129, 5], 512, 384, activation=act, recipe=kind, seed=1, w_std=0.05)
@@ -74,7 +79,7 @@ def test_mlp_forward_backward_matches_oracle(kind, act):
     _compare(out, wl, kind)
 
 
-@pytest.mark.parametrize("kind,act", CASES)
+@pytest.mark.parametrize("kind,act", CASES, ids=CASE_IDS)
 def test_recompute_on_off_bitwise(kind, act):
     """Rebuilding the fc2 input in backward gives bitwise-equal output and gradients."""
     print(f"recompute {kind} {act}", flush=True)
@@ -134,12 +139,82 @@ def test_nvfp4_fused_fc2_amax_matches_standalone_pass(splits, recompute):
     assert float(post.max()) > 0 and all(float(pre[e]) == 0 for e in range(len(splits)) if splits[e] == 0)
 
 
+@pytest.mark.parametrize("recompute", [False, True])
+def test_nvfp4_fused_fc2_amax_tanh_srelu(recompute):
+    """The tanh-clamped squared ReLU takes the same fused route ("Reduce NVFP4 quantization work ...",
+    Changes: ScaledTanhSReLU through the Hadamard-fused fc1 kernel with tanh_clamp_scale): the fc1
+    epilogue's pre- and post-RHT amax equal, bit for bit, those of the default forward's pass over h
+    (the same activation function), with one amax launch fewer, and y and the gradients are bitwise
+    the default forward's."""
+    print(f"fused fc2 amax tanh_srelu recompute={recompute}", flush=True)
+    wl = small_case([0, 37, 300, 129, 5], 256, 384, activation=TANH_SRELU, recipe="nvfp4", seed=9, w_std=0.05)
+    d = _upload(wl)
+    rec = g.recipe("nvfp4", wl.sign_mask)
+    w1q, w2q = g.weight_quantize(d["w1"], rec), g.weight_quantize(d["w2"], rec)
+    y0, ctx0 = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], TANH_SRELU, rec, recompute=recompute)
+    counts0 = g.last_launch_counts()
+    y, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], TANH_SRELU, rec, recompute=recompute,
+                                   fc2_amax_in_fc1=True)
+    counts = g.last_launch_counts()
+    _, pre0, post0 = g.forward_saved(ctx0)
+    _, pre, post = g.forward_saved(ctx)
+    b0 = g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx0)
+    b1 = g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx)
+    torch.cuda.synchronize()
+    assert counts["hadamard_amax"] == 1 and counts0["hadamard_amax"] == 2, (counts, counts0)
+    assert torch.equal(pre0.view(torch.int32), pre.view(torch.int32)), (pre0, pre)
+    assert torch.equal(post0.view(torch.int32), post.view(torch.int32)), (post0, post)
+    assert torch.equal(y0.view(torch.int16), y.view(torch.int16))
+    for k in ("dx", "dprobs", "dw1", "dw2"):
+        view = torch.int16 if b0[k].dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(b0[k].view(view), b1[k].view(view)), k
+    assert float(post.max()) > 0 and float(pre[0]) == 0
+
+
+@pytest.mark.parametrize("act", ["srelu", TANH_SRELU, "swiglu", "qgeglu"],
+                         ids=["srelu", "tanh_srelu", "swiglu", "qgeglu"])
+def test_nvfp4_fc2_input_amax_matches_the_oracle_activation(act):
+    """The NVFP4 forward keeps the fc2 input's per-group amax for the recompute cast.  Against the
+    oracle's activation of the same saved h (fp64, then p, then bf16): the pre-RHT amax, which is
+    one of the a values, within one bf16 ulp (the kernels evaluate the activation in fp32 with the
+    hardware exp2, reciprocal and the library tanh), the post-RHT amax within 2^-5."""
+    from oracle.rht import group_hadamard_amax
+    print(f"fc2 input amax {act}", flush=True)
+    wl = small_case([0, 37, 300, 129, 5], 256, 384, activation=act, recipe="nvfp4", seed=13, w_std=0.05)
+    d = _upload(wl)
+    rec = g.recipe("nvfp4", wl.sign_mask)
+    w1q, w2q = g.weight_quantize(d["w1"], rec), g.weight_quantize(d["w2"], rec)
+    _, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], act, rec, recompute=True)
+    h, pre, post = g.forward_saved(ctx)
+    torch.cuda.synchronize()
+    hv = F.bf16_bits_to_f64(bits16(h))
+    a = F.round_bf16(O.act_forward(hv, act) * wl.probs.astype(np.float64)[:, None])
+    rpre, rpost = group_hadamard_amax(F.f64_to_bf16_bits(a), wl.m_splits, wl.sign_mask)
+    pre, post = pre.cpu().numpy(), post.cpu().numpy()
+    for e, m in enumerate(wl.m_splits):
+        if m == 0:
+            assert pre[e] == 0 and post[e] == 0 and rpre[e] == 0
+            continue
+        assert abs(pre[e] - rpre[e]) <= 2.0 ** -7 * rpre[e], (e, pre[e], rpre[e])
+        assert abs(post[e] - rpost[e]) <= 2.0 ** -5 * rpost[e], (e, post[e], rpost[e])
+
+
+def test_tanh_srelu_needs_a_positive_clamp_scale():
+    wl = small_case([64, 64], 128, 128, activation="srelu", recipe="mxfp8", seed=9, w_std=0.05)
+    d = _upload(wl)
+    rec = g.recipe("mxfp8")
+    w1q, w2q = g.weight_quantize(d["w1"], rec), g.weight_quantize(d["w2"], rec)
+    for c in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(g.GmlpError, match="clamp scale"):
+            g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], ("tanh_srelu", c), rec)
+
+
 def test_fc2_amax_in_fc1_needs_nvfp4_srelu():
     wl = small_case([64, 64], 128, 128, activation="swiglu", recipe="nvfp4", seed=9, w_std=0.05)
     d = _upload(wl)
     rec = g.recipe("nvfp4", 1)
     w1q, w2q = g.weight_quantize(d["w1"], rec), g.weight_quantize(d["w2"], rec)
-    with pytest.raises(g.GmlpError, match="squared ReLU"):
+    with pytest.raises(g.GmlpError, match="squared-ReLU"):
         g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], "swiglu", rec, fc2_amax_in_fc1=True)
 
 

@@ -37,11 +37,16 @@ def test_one_expert_is_a_dense_gemm():
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("act", [O.SWIGLU, O.SRELU])
+TANH_SRELU_3 = (O.TANH_SRELU, 3.0)
+
+
+@pytest.mark.parametrize("act", [O.SWIGLU, O.SRELU, TANH_SRELU_3, O.QGEGLU], ids=["swiglu", "srelu", "tanh_srelu",
+                                                                                    "qgeglu"])
 def test_activation_derivatives_by_central_differences(act):
     rng = np.random.default_rng(22)
     f = 6
-    n1 = 2 * f if act == O.SWIGLU else f
+    n1 = 2 * f if O.is_glu(act) else f
+    relu_kind = O.act_kind(act)[0] in (O.SRELU, O.TANH_SRELU)
     h = rng.standard_normal((4, n1)) * 2
     h[0, 0] = 0.0
     h[1, 1] = -1.5
@@ -55,7 +60,7 @@ def test_activation_derivatives_by_central_differences(act):
 
     for i in range(4):
         for j in range(n1):
-            if act == O.SRELU and abs(h[i, j]) < 1e-3:
+            if relu_kind and abs(h[i, j]) < 1e-3:
                 continue
             hp, hm = h.copy(), h.copy()
             hp[i, j] += eps
@@ -67,8 +72,49 @@ def test_activation_derivatives_by_central_differences(act):
         pm[i] -= eps
         num = (loss(h, pp) - loss(h, pm)) / (2 * eps)
         assert abs(num - dprob[i]) < 1e-6 * max(1, abs(num))
-    if act == O.SRELU:
+    if relu_kind:
         assert dh[1, 1] == 0.0 and dh[0, 0] == 0.0
+
+
+def test_tanh_srelu_closed_forms():
+    """c tanh(relu(h)^2 / c): tanh(ln(3) / 2) = 1/2 exactly, so relu(h)^2 = c ln(3) / 2 gives c / 2;
+    no output for h <= 0; the clamp c for large h; the plain squared ReLU as c grows (tanh(x) = x to
+    fp64 precision for x below 2^-27, and c a power of two makes (s / c) c exact)."""
+    c = 2.0 / np.log(3.0)                          # relu(1)^2 / c = ln(3) / 2
+    h = np.array([[1.0, 0.0, -2.0, 10.0]])
+    got = O.act_forward(h, (O.TANH_SRELU, c))
+    assert abs(got[0, 0] - c / 2) < 1e-15
+    assert got[0, 1] == 0.0 and got[0, 2] == 0.0
+    assert got[0, 3] == c                          # tanh(100 / c) rounds to 1
+    big = 2.0 ** 80
+    hh = np.random.default_rng(5).standard_normal((3, 8)) * 4
+    assert np.array_equal(O.act_forward(hh, (O.TANH_SRELU, big)), O.act_forward(hh, O.SRELU))
+    # dprob is the activation itself, da = 1
+    _, dprob = O.act_backward(h, np.ones_like(h), np.ones(1), (O.TANH_SRELU, c))
+    assert abs(dprob[0] - (c / 2 + c)) < 1e-14
+
+
+def test_qgeglu_closed_forms_and_the_gelu_it_approximates():
+    """gate sigmoid(1.702 gate) up: sigmoid(ln 3) = 3/4 exactly; gate 0 gives 0; it is SwiGLU at
+    1.702 gate divided by 1.702; and g sigmoid(1.702 g) stays within 0.021 of the exact GELU
+    g Phi(g) (Phi from scipy), which the constants 1 and 2 miss by twice that or more."""
+    from scipy.special import ndtr
+    g0 = np.log(3.0) / O.QUICK_GELU_K
+    h = np.array([[g0, 0.0, 2.0, 5.0]])            # gate = [g0, 0], up = [2, 5]
+    got = O.act_forward(h, O.QGEGLU)
+    assert abs(got[0, 0] - g0 * 0.75 * 2.0) < 1e-15
+    assert got[0, 1] == 0.0
+    hh = np.random.default_rng(6).standard_normal((4, 10)) * 3
+    sw = np.concatenate([hh[:, :5] * O.QUICK_GELU_K, hh[:, 5:]], axis=1)
+    assert np.allclose(O.act_forward(hh, O.QGEGLU), O.act_forward(sw, O.SWIGLU) / O.QUICK_GELU_K,
+                       rtol=1e-13, atol=1e-15)
+    g = np.linspace(-8, 8, 4001)
+    ones = np.ones_like(g)
+    quick = O.act_forward(np.stack([g, ones], axis=1), O.QGEGLU)[:, 0]
+    err = np.max(np.abs(quick - g * ndtr(g)))
+    assert 0.015 < err < 0.021
+    for k in (1.0, 2.0):
+        assert np.max(np.abs(g / (1 + np.exp(-k * g)) - g * ndtr(g))) > 0.035
 
 
 def _torch_reference(wl, act):
@@ -80,9 +126,15 @@ def _torch_reference(wl, act):
     ys, off = [], 0
     for g, m in enumerate(wl.m_splits.tolist()):
         h = x[off:off + m] @ w1[g].T
-        if act == O.SWIGLU:
+        kind, c = O.act_kind(act)
+        if kind == O.SWIGLU:
             f = h.shape[1] // 2
             a = torch.nn.functional.silu(h[:, :f]) * h[:, f:]
+        elif kind == O.QGEGLU:
+            f = h.shape[1] // 2
+            a = h[:, :f] * torch.sigmoid(1.702 * h[:, :f]) * h[:, f:]
+        elif kind == O.TANH_SRELU:
+            a = c * torch.tanh(torch.relu(h) ** 2 / c)
         else:
             a = torch.relu(h) ** 2
         ys.append((a * p[off:off + m, None]) @ w2[g].T)
@@ -94,7 +146,9 @@ def _torch_reference(wl, act):
 
 
 @pytest.mark.parametrize("recipe,act,tol", [(O.MXFP8, O.SWIGLU, 0.12), (O.NVFP4, O.SRELU, 0.35),
-                                             (O.MXFP8, O.SRELU, 0.12), (O.NVFP4, O.SWIGLU, 0.35)])
+                                             (O.MXFP8, O.SRELU, 0.12), (O.NVFP4, O.SWIGLU, 0.35),
+                                             (O.MXFP8, (O.TANH_SRELU, 2.0), 0.12), (O.NVFP4, O.QGEGLU, 0.35),
+                                             (O.NVFP4, (O.TANH_SRELU, 2.0), 0.35), (O.MXFP8, O.QGEGLU, 0.12)])
 def test_forward_backward_close_to_unquantized_autograd(recipe, act, tol):
     """Within the quantization-format error of torch fp64 autograd of the same MLP.
 

@@ -18,6 +18,8 @@ import torch
 
 SWIGLU = "swiglu"
 SRELU = "srelu"
+TANH_SRELU = "tanh_srelu"
+QGEGLU = "qgeglu"
 MXFP8 = "mxfp8"
 NVFP4 = "nvfp4"
 
@@ -36,7 +38,7 @@ class Config:
     experts: int
     hidden: int
     ffn: int
-    activation: str
+    activation: object               # a name, or ("tanh_srelu", clamp scale)
     recipe: str
     rows: int
     splits: str                      # "fixed" | "uniform" | "equal" | "zipf" | "dirichlet"
@@ -56,7 +58,10 @@ class Config:
 
     @property
     def f1(self):
-        return 2 * self.ffn if self.activation == SWIGLU else self.ffn
+        # gated activations (SwiGLU, QGeGLU) read [gate | up]; an activation is a name or
+        # ("tanh_srelu", clamp scale)
+        name = self.activation[0] if isinstance(self.activation, tuple) else self.activation
+        return 2 * self.ffn if name in (SWIGLU, QGEGLU) else self.ffn
 
 
 CONFIGS = {
