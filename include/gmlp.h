@@ -3,7 +3,11 @@
  *
  * C ABI of libgmlp.so.  Every entry point is stream-ordered on the caller's
  * hipStream_t, performs no host synchronisation and no device allocation, and
- * keeps no pointer beyond the call.  All tensors are caller-owned device
+ * dereferences no pointer beyond the call (the MLP calls remember the addresses of
+ * their ctx and ws buffers, with the settings they were written with, so that a
+ * backward or a deferred wgrad call whose settings differ from those of the call
+ * that wrote the buffer fails with GMLP_INVALID_ARG instead of reading it in
+ * another layout; a buffer with no record is taken as it is).  All tensors are caller-owned device
  * buffers passed as plain pointers; sizes are host integers.
  *
  * Errors: every argument is validated before anything is enqueued.  On error
@@ -297,7 +301,7 @@ typedef struct {
   const float* probs;
   int32_t activation;
   gmlp_recipe recipe;
-  int32_t recompute;          /* must match the forward */
+  int32_t recompute;          /* must match the forward (checked, as are the sizes, activation and recipe) */
   int32_t input_requires_grad;
   int32_t weight_requires_grad;
   void* dx;                   /* bf16 [M, H] (may be NULL if !input_requires_grad) */

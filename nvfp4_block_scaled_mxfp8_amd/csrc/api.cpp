@@ -17,6 +17,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 using namespace gmlp;
@@ -244,6 +245,87 @@ gmlp_status weight_ok(const gmlp_weight_q* w, const gmlp_recipe& r, bool fprop, 
   if (fprop && !f_ok) return fail(GMLP_INVALID_ARG, "weight fprop operand (row-wise data and scales) missing");
   if (dgrad && !d_ok) return fail(GMLP_INVALID_ARG, "weight dgrad operand (column-wise data and scales) missing");
   if (!is_mx(r) && !w->amax_pre) return fail(GMLP_INVALID_ARG, "NVFP4 weights need their per-expert amax (amax_pre)");
+  return GMLP_OK;
+}
+
+// ----------------------------------------------------------------------------- saved-plan records
+// What a forward wrote into a ctx buffer, and what a backward left in its workspace, keyed by the
+// buffer's address (an address only: never dereferenced).  The backward and the deferred wgrad
+// call check their own settings against the record and reject a mismatch, with which they would
+// read the buffer in another layout (different offsets, or operands never written).  The records
+// are process-wide and bounded (the oldest is dropped); a buffer with no record (written by
+// another process, or dropped) is taken as it is.
+struct SavedPlan {
+  const void* key = nullptr;
+  uint64_t stamp = 0;
+  int64_t M = 0, H = 0, ffn = 0;
+  int E = 0, act = 0, kind = 0, recompute = 0, wgrad = 0, deferred = 0;
+  uint32_t mask = 0;
+  float clamp = 0.0f;
+};
+constexpr int kSavedPlans = 512;
+std::mutex g_plans_mu;
+SavedPlan g_plans[kSavedPlans];
+uint64_t g_plan_stamp = 0;
+
+SavedPlan plan_of(const void* key, int64_t M, int E, int64_t H, int64_t ffn, int act, float clamp,
+                  const gmlp_recipe& r, int recompute, int wgrad, int deferred) {
+  SavedPlan p;
+  p.key = key;
+  p.M = M;
+  p.E = E;
+  p.H = H;
+  p.ffn = ffn;
+  p.act = act;
+  p.clamp = act == GMLP_TANH_SRELU ? clamp : 0.0f;
+  p.kind = r.kind;
+  p.mask = r.kind == GMLP_NVFP4_RHT ? (r.rht_sign_mask & 0xFFFF) : 0u;
+  p.recompute = recompute != 0;
+  p.wgrad = wgrad != 0;
+  p.deferred = deferred != 0;
+  return p;
+}
+void remember_plan(const SavedPlan& p) {
+  std::lock_guard<std::mutex> lock(g_plans_mu);
+  int slot = 0;
+  for (int i = 0; i < kSavedPlans; ++i) {
+    if (g_plans[i].key == p.key) { slot = i; break; }
+    if (g_plans[i].stamp < g_plans[slot].stamp) slot = i;
+  }
+  g_plans[slot] = p;
+  g_plans[slot].stamp = ++g_plan_stamp;
+}
+bool recall_plan(const void* key, SavedPlan* out) {
+  std::lock_guard<std::mutex> lock(g_plans_mu);
+  for (int i = 0; i < kSavedPlans; ++i)
+    if (g_plans[i].key == key && g_plans[i].stamp) {
+      *out = g_plans[i];
+      return true;
+    }
+  return false;
+}
+// The first setting in which `want` differs from the record (nullptr: none).
+const char* plan_mismatch(const SavedPlan& have, const SavedPlan& want) {
+  if (have.M != want.M) return "M";
+  if (have.E != want.E) return "E";
+  if (have.H != want.H) return "hidden";
+  if (have.ffn != want.ffn) return "ffn";
+  if (have.act != want.act) return "activation";
+  if (have.clamp != want.clamp) return "tanh_clamp_scale";
+  if (have.kind != want.kind) return "recipe";
+  if (have.mask != want.mask) return "rht_sign_mask";
+  if (have.recompute != want.recompute) return "recompute";
+  return nullptr;
+}
+// ctx: written by a forward with these settings (and, when the caller needs the weight-gradient
+// operands, one that saved them).
+gmlp_status check_ctx_plan(const SavedPlan& want) {
+  SavedPlan have;
+  if (!recall_plan(want.key, &have)) return GMLP_OK;
+  if (const char* f = plan_mismatch(have, want))
+    return fail(GMLP_INVALID_ARG, "ctx: written by a forward with a different %s", f);
+  if (want.wgrad && !have.wgrad)
+    return fail(GMLP_INVALID_ARG, "ctx: the forward saved no weight-gradient operands (weight_requires_grad 0)");
   return GMLP_OK;
 }
 
@@ -732,6 +814,9 @@ gmlp_status gmlp_grouped_mlp_forward(const gmlp_fwd_args* A, hipStream_t stream)
     if (!L.check(launch_gemm(g, stream), "fc2 gemm")) return L.st;
     g_counts[CNT_GEMM]++;
   }
+  remember_plan(plan_of(A->ctx, M, E, H, ffn, A->activation, A->tanh_clamp_scale, r, rec, wgrad, 0));
+  // the forward's workspace holds no deferred weight-gradient operands any more
+  remember_plan(plan_of(A->ws, M, E, H, ffn, A->activation, A->tanh_clamp_scale, r, rec, wgrad, 0));
   return ok();
 }
 
@@ -826,6 +911,8 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
   Bump wb(A->ws);
   BwdWs W = carve_bwd_ws(wb, M, E, H, ffn, A->activation, r, rec);
   if (!A->ws || A->ws_bytes < wb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", wb.off);
+  const SavedPlan plan = plan_of(A->ctx, M, E, H, ffn, A->activation, A->tanh_clamp_scale, r, rec, wgrad, defer);
+  if ((st = check_ctx_plan(plan)) != GMLP_OK) return st;
 
   Launcher L{stream};
   if (!L.check(launch_scan(A->m_splits, E, M, W.T, stream), "scan")) return L.st;
@@ -942,6 +1029,9 @@ gmlp_status gmlp_grouped_mlp_backward(const gmlp_bwd_args* A, hipStream_t stream
   }
   // 6. fc1 wgrad
   if (wgrad && !defer && !fc1_wgrad(A, C, W, L, stream)) return L.st;
+  SavedPlan ws_plan = plan;
+  ws_plan.key = A->ws;
+  remember_plan(ws_plan);
   return ok();
 }
 
@@ -959,6 +1049,20 @@ gmlp_status gmlp_grouped_mlp_wgrad(const gmlp_bwd_args* A, hipStream_t stream) {
   Bump wb(A->ws);
   BwdWs W = carve_bwd_ws(wb, A->M, A->E, A->H, A->ffn, A->activation, A->recipe, A->recompute != 0);
   if (!A->ws || A->ws_bytes < wb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", wb.off);
+  SavedPlan want = plan_of(A->ctx, A->M, A->E, A->H, A->ffn, A->activation, A->tanh_clamp_scale, A->recipe,
+                           A->recompute, 1, 1);
+  if ((st = check_ctx_plan(want)) != GMLP_OK) return st;
+  {
+    // ws: left by a backward with the same settings that deferred its weight gradients
+    SavedPlan have;
+    want.key = A->ws;
+    if (recall_plan(A->ws, &have)) {
+      if (const char* f = plan_mismatch(have, want))
+        return fail(GMLP_INVALID_ARG, "ws: written by a backward with a different %s", f);
+      if (!have.deferred)
+        return fail(GMLP_INVALID_ARG, "ws: last written by a call that left no deferred weight-gradient operands");
+    }
+  }
   Launcher L{stream};
   // the split tables are rebuilt from m_splits: only the operands come from the deferring call
   if (!L.check(launch_scan(A->m_splits, A->E, A->M, W.T, stream), "scan")) return L.st;

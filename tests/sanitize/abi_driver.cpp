@@ -195,6 +195,21 @@ int main() {
         b.ws = f.ws;
         b.ws_bytes = sz.ws_bytes;
         EXPECT(gmlp_grouped_mlp_backward(&b, nullptr), GMLP_OK);
+        // a deferred wgrad on a workspace whose last backward did not defer, and a backward whose
+        // settings differ from the forward that wrote ctx, are rejected
+        EXPECT(gmlp_grouped_mlp_wgrad(&b, nullptr), GMLP_INVALID_ARG);
+        if (!rec) {                          // (the recompute plan needs a larger workspace)
+          b.recompute = 1;
+          b.ws_bytes = 4 * sz.ws_bytes;
+          EXPECT(gmlp_grouped_mlp_backward(&b, nullptr), GMLP_INVALID_ARG);
+          b.recompute = 0;
+          b.ws_bytes = sz.ws_bytes;
+        }
+        if (act == GMLP_TANH_SRELU) {
+          b.tanh_clamp_scale = 4.0f;
+          EXPECT(gmlp_grouped_mlp_backward(&b, nullptr), GMLP_INVALID_ARG);
+          b.tanh_clamp_scale = f.tanh_clamp_scale;
+        }
         if (act == GMLP_TANH_SRELU) {
           b.tanh_clamp_scale = 0.0f;
           EXPECT(gmlp_grouped_mlp_backward(&b, nullptr), GMLP_INVALID_ARG);

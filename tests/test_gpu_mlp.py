@@ -199,6 +199,31 @@ def test_nvfp4_fc2_input_amax_matches_the_oracle_activation(act):
         assert abs(post[e] - rpost[e]) <= 2.0 ** -5 * rpost[e], (e, post[e], rpost[e])
 
 
+def test_backward_rejects_a_ctx_written_with_other_settings():
+    """The backward and the deferred wgrad call check their settings against those the forward
+    (and the deferring backward) wrote their buffers with: a recompute flag, a weight-gradient flag
+    or a workspace that does not match is an error, not a read of the buffer in another layout."""
+    import dataclasses
+    wl = small_case([64, 0, 100], 128, 128, activation="srelu", recipe="nvfp4", seed=9, w_std=0.05)
+    d = _upload(wl)
+    rec = g.recipe("nvfp4", wl.sign_mask)
+    w1q, w2q = g.weight_quantize(d["w1"], rec), g.weight_quantize(d["w2"], rec)
+    _, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], "srelu", rec, recompute=False)
+    with pytest.raises(g.GmlpError, match="ctx: written by a forward with a different recompute"):
+        g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], dataclasses.replace(ctx, recompute=True))
+    _, ctx2 = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], "srelu", rec,
+                                    weight_requires_grad=False)
+    with pytest.raises(g.GmlpError, match="saved no weight-gradient operands"):
+        g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"],
+                               dataclasses.replace(ctx2, weight_requires_grad=True))
+    part = g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx, defer_wgrad=True)
+    # the deferred operands are in part's workspace; a backward that does not defer reuses it
+    g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx, ws=part["deferred"].ws)
+    with pytest.raises(g.GmlpError, match="ws: last written by a call that left no deferred"):
+        g.grouped_mlp_wgrad(part["deferred"])
+    torch.cuda.synchronize()
+
+
 def test_tanh_srelu_needs_a_positive_clamp_scale():
     wl = small_case([64, 64], 128, 128, activation="srelu", recipe="mxfp8", seed=9, w_std=0.05)
     d = _upload(wl)
