@@ -1144,9 +1144,10 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
     if (256 * orow_bytes >= (int64_t)kOutOfRange) return hipErrorInvalidValue;
   }
   GemmArgs a = g;
-  // 4 row tiles per launch-order group: 4 x 8 tiles are one XCD's round of 32 workgroups (2, 8
-  // and 16 measured 0.5-1.5% slower on the bench workload)
-  a.group_rows = 4;
+  // Row tiles per launch-order group.  FPROP: 4, so that 4 x 8 tiles are one XCD's round of 32
+  // workgroups (2, 8 and 16 measured 0.5-2% slower on the 8- and 128-expert workloads).  WGRAD: 2
+  // (3% faster than 4 on the 128-expert workload's fc1 weight gradient, 8 is 6% slower).
+  a.group_rows = MODE == MODE_WGRAD ? 2 : 4;
   // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split
   int64_t wgs = std::min<int64_t>(cu_count(), tiles);
   wgs = (wgs + 7) / 8 * 8;
