@@ -157,6 +157,8 @@ def traffic_probe(args):
     # the group quantize of an x-shaped tensor, row- and column-wise, twice
     x = torch.randn((shape["M"], cfg.hidden), device=dev, generator=gen).to(torch.bfloat16)
     q = g.alloc_grouped_q(rec, shape["M"], cfg.hidden, cfg.experts, True, True, dev)
+    if rec.kind == g.MXFP8:           # the outputs the step writes (no canonical scale bytes)
+        q = g.QTensor(q.kind, {k: v for k, v in q.bufs.items() if k not in ("row_scale", "col_scale")})
     qws = g.quant_workspace(cfg.experts, dev)
     for _ in range(2):
         g.group_quantize(x, splits_dev, rec, True, True, out=q, ws=qws)
@@ -196,6 +198,7 @@ COUNTER_PASSES = {
     "l2": ["TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_WRREQ_sum", "GRBM_GUI_ACTIVE"],
 }
 SIMDS = 1024            # MI355X: 256 compute units x 4 SIMDs
+XCDS = 8                # GRBM_GUI_ACTIVE is summed over the 8 XCDs
 
 
 def counter_commands(config):
@@ -205,7 +208,8 @@ def counter_commands(config):
 
 
 def _dispatch_counters(d):
-    """{dispatch id: (kernel name, {counter: value})} from the counter CSVs under d."""
+    """{dispatch id: (kernel name, {counter: value, "duration_ns": end - start})} from the counter
+    CSVs under d."""
     import csv
     import glob
     out = {}
@@ -215,6 +219,8 @@ def _dispatch_counters(d):
                 k = int(r["Dispatch_Id"])
                 name, vals = out.setdefault(k, (r["Kernel_Name"], {}))
                 vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                    vals["duration_ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     return out
 
 
@@ -226,25 +232,40 @@ def write_counters(args, root):
     shape = dominant_shape(cfg, config_splits(cfg))
     kernels = {"gemm": "gemm_mx_kernel<0, 0, 0>", "quantize": "mxfp8_quant_kernel<true, true>"}
     raw = {k: {} for k in kernels}
+    # the MFMA pass's own dispatch gives the cycles and the duration the busy fraction and the clock
+    # are taken from (every pass counts GRBM_GUI_ACTIVE of its own dispatch)
+    mfma_pass = {k: (0.0, 0.0) for k in kernels}
     for name in COUNTER_PASSES:
         disp = _dispatch_counters(os.path.join(root, name))
         for k, key in kernels.items():
             hits = [v for _, (kn, v) in sorted(disp.items()) if key in kn]
             if hits:
+                dur = hits[-1].pop("duration_ns", 0.0)
+                if name == "mfma":
+                    mfma_pass[k] = (hits[-1].get("GRBM_GUI_ACTIVE", 0.0), dur)
                 raw[k].update({c: v for c, v in hits[-1].items()})
     rec = {"workload": args.config, "shape": shape, "source_sha256": kernel_source_hash(),
            "commands": counter_commands(args.config), "raw": raw, "derived": {}}
     for k, v in raw.items():
         d = {}
-        gui = v.get("GRBM_GUI_ACTIVE")
-        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
-            d["mfma_busy_pct_of_simd_cycles"] = 100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS)
+        gui, dur = mfma_pass[k]
+        cycles = gui / XCDS if gui else None          # the dispatch's cycles (per XCD)
+        if cycles and dur:
+            d["duration_us_under_counters"] = dur / 1e3
+            d["clock_ghz"] = cycles / dur
+        if cycles and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+            d["mfma_busy_pct_of_simd_cycles"] = 100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS)
+        if k == "gemm" and v.get("SQ_INSTS_VALU_MFMA_MOPS_F8"):
+            # a MOP is 512 flops; the useful flops of the launch are 2 M N K
+            issued = 512.0 * v["SQ_INSTS_VALU_MFMA_MOPS_F8"]
+            d["mfma_flops_issued"] = issued
+            d["mfma_useful_pct_of_issued"] = 100.0 * 2.0 * shape["M"] * shape["N"] * shape["K"] / issued
         if "SQ_LDS_BANK_CONFLICT" in v and v.get("SQ_LDS_IDX_ACTIVE"):
             d["lds_bank_conflict_pct_of_lds_active"] = 100.0 * v["SQ_LDS_BANK_CONFLICT"] / v["SQ_LDS_IDX_ACTIVE"]
         if v.get("TCC_HIT_sum") is not None and v.get("TCC_MISS_sum") is not None:
             d["l2_hit_pct"] = 100.0 * v["TCC_HIT_sum"] / max(1.0, v["TCC_HIT_sum"] + v["TCC_MISS_sum"])
         if gui:
-            d["gpu_active_cycles"] = gui
+            d["gpu_active_cycles_sum_over_xcds"] = gui
         rec["derived"][k] = d
     path = os.path.join(PROFILES, "counters_%s_%dx%dx%d.json" % (args.config, shape["M"], shape["N"], shape["K"]))
     with open(path, "w") as f:
@@ -433,7 +454,8 @@ def main():
     torch.cuda.synchronize()
     q_ms = timed_flushed(torch, quant, args.kernel_reps, flush)
     c_ms = timed_flushed(torch, copy, args.kernel_reps, flush)
-    q_bytes = (2 + 1 + 1 + 2.0 / 32) * M * H if kind == "mxfp8" else (2 + 0.5 + 1 / 16 + 0.5 + 1 / 16) * M * H
+    # NVFP4: the amax pass reads x, then the cast reads it again (the pages' two-pass method)
+    q_bytes = (2 + 1 + 1 + 2.0 / 32) * M * H if kind == "mxfp8" else (2 + 2 + 0.5 + 1 / 16 + 0.5 + 1 / 16) * M * H
     q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     c_gbs = 4.0 * M * H / (c_ms * 1e-3) / 1e9
     log(f"group quantize x: {q_ms * 1e3:.1f} us  {q_gbs:.0f} GB/s ({100 * q_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); "
