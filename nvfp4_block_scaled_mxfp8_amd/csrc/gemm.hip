@@ -495,9 +495,10 @@ __device__ __forceinline__ int tiles_n(const GemmArgs& A) {
 template <int MODE, int EPI>
 __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, int ntn, int& mt, Ctx& c) {
   // Order: groups of group_rows tile rows, column-major inside a group, so that the
-  // workgroups resident together on one XCD share few A row blocks and B blocks.  WGRAD tiles
-  // are ordered expert by expert (the row groups stay inside one expert), so that an expert's
-  // tiles are one contiguous range of the sequence.
+  // workgroups resident together on one XCD share few A row blocks and B blocks.  WGRAD tiles,
+  // and FPROP tiles when expert_groups is set, are ordered expert by expert (the row groups stay
+  // inside one expert), so that an expert's tiles are one contiguous range of the sequence and
+  // a group's column tiles share one weight panel.
   const int gr = A.group_rows;
   const int gsz = gr * ntn;
   int tile_m;
@@ -508,6 +509,16 @@ __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, in
     const int grp = loc / gsz, rem = loc - grp * gsz;
     const int rows_here = min(gr, per_g - grp * gr);
     tile_m = e * per_g + grp * gr + rem % rows_here;
+    c.nt = rem / rows_here;
+  } else if (A.expert_groups) {
+    // expert e's tiles: [t256_off[e] ntn, t256_off[e + 1] ntn) of the sequence
+    if (A.G <= 0 || bid >= ntm * ntn) return false;
+    const int e = find_group(A.T.t256_off, A.G, bid / ntn);
+    const int r0 = A.T.t256_off[e], r = A.T.t256_off[e + 1] - r0;
+    const int loc = bid - r0 * ntn;
+    const int grp = loc / gsz, rem = loc - grp * gsz;
+    const int rows_here = min(gr, r - grp * gr);
+    tile_m = r0 + grp * gr + rem % rows_here;
     c.nt = rem / rows_here;
   } else {
     const int grp = bid / gsz, rem = bid - grp * gsz;
@@ -1145,9 +1156,14 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
   }
   GemmArgs a = g;
   // Row tiles per launch-order group.  FPROP: 4, so that 4 x 8 tiles are one XCD's round of 32
-  // workgroups (2, 8 and 16 measured 0.5-2% slower on the 8- and 128-expert workloads).  WGRAD: 2
-  // (3% faster than 4 on the 128-expert workload's fc1 weight gradient, 8 is 6% slower).
-  a.group_rows = MODE == MODE_WGRAD ? 2 : 4;
+  // workgroups (2, 8 and 16 measured 0.5-2% slower on the 8- and 128-expert workloads).  When
+  // the groups average at most two 256-row tiles, most 4-row groups would straddle experts and
+  // fetch several weight panels per column tile: then groups of 8 rows inside one expert
+  // (the 128-expert workload: 19-26% fewer bytes fetched by its forward-shaped GEMMs, 1% off
+  // the step; with 8 experts of 3-4K rows the same order was 1-2% slower).  WGRAD: 2 (3% faster
+  // than 4 on the 128-expert workload's fc1 weight gradient, 8 is 6% slower).
+  a.expert_groups = (MODE == MODE_FPROP && g.G > 0 && g.M <= 512LL * g.G) ? 1 : 0;
+  a.group_rows = MODE == MODE_WGRAD ? 2 : (a.expert_groups ? 8 : 4);
   // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split
   int64_t wgs = std::min<int64_t>(cu_count(), tiles);
   wgs = (wgs + 7) / 8 * 8;

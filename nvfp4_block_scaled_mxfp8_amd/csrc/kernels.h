@@ -146,6 +146,7 @@ struct GemmArgs {
   uint16_t* dh;      // EPI_DACT: out dh [M, F1]
   float* dprob_part; // EPI_DACT: [n_tiles, M]
   int group_rows;    // tile rows per launch-order group (see tile_ctx); set by the launcher
+  int expert_groups; // FPROP: 1 when the launch-order groups stay inside one expert; set by the launcher
   // NVFP4: scratch for the operands expanded to bf16 (A: 2 x rows x contraction bytes, B: the
   // same for the weight or column-wise operand) and, for EPI_DACT, da [M, ffn] bf16
   uint8_t* xa;
