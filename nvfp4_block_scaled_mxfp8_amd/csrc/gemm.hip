@@ -83,7 +83,7 @@ struct Ctx {
   int arows;         // valid A rows in the tile
   int64_t nrow0;     // first output column (FPROP) / B feature row (WGRAD)
   int nt;            // n-tile index
-  int64_t kvalid;    // contraction length (K, or P_g)
+  int64_t kvalid;    // contraction length (K, or the group's tokens)
   int nk;            // stages
   // operand bases (element offsets of row 0 of the operand matrix for this group)
   int64_t a_base, b_base, a_ld, b_ld;
@@ -428,12 +428,22 @@ __device__ __forceinline__ v8bf frag_hi(const v8i& v) { return __builtin_bit_cas
 
 // Z: the tile's first step, which starts the accumulators from zero (the MFMA's C operand is the
 // constant 0, so no register has to be cleared between tiles).
-template <int TM, int TN, int BF = 0, bool Z = false>
+// TR: the transposed product (B fragments as the MFMA's first operand, with their scales), so that
+// a lane's accumulators hold consecutive output columns of one row (see mx_epilogue_tr).
+template <int TM, int TN, int BF = 0, bool Z = false, int TR = 0>
 __device__ __forceinline__ void mx_mma_one(const MxFrags& f, v16f (&acc)[4][4]) {
   const v16f c = Z ? v16f{} : acc[TM][TN];
   if constexpr (BF) {
-    acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_lo(f.a[TM]), frag_lo(f.b[TN]), c, 0, 0, 0);
-    acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_hi(f.a[TM]), frag_hi(f.b[TN]), acc[TM][TN], 0, 0, 0);
+    if constexpr (TR) {
+      acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_lo(f.b[TN]), frag_lo(f.a[TM]), c, 0, 0, 0);
+      acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_hi(f.b[TN]), frag_hi(f.a[TM]), acc[TM][TN], 0, 0, 0);
+    } else {
+      acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_lo(f.a[TM]), frag_lo(f.b[TN]), c, 0, 0, 0);
+      acc[TM][TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_hi(f.a[TM]), frag_hi(f.b[TN]), acc[TM][TN], 0, 0, 0);
+    }
+  } else if constexpr (TR) {
+    acc[TM][TN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[TN], f.a[TM], c, 0, 0, 0,
+                                                                   (int)f.sb[TN], 0, (int)f.sa[TM]);
   } else {
     acc[TM][TN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[TM], f.b[TN], c, 0, 0, 0,
                                                                    (int)f.sa[TM], 0, (int)f.sb[TN]);
@@ -451,36 +461,36 @@ __device__ __forceinline__ void mx_mma_one(const MxFrags& f, v16f (&acc)[4][4]) 
 //   after the barrier:  R0 M20 D5 R1 M21 M22 D6 R2 M23 M30 D7 R3 M31 M32 D8 M33
 constexpr int MX_DMA_BEFORE_BARRIER = 5;
 
-template <int BF = 0, bool Z = false>
+template <int BF = 0, bool Z = false, int TR = 0>
 __device__ __forceinline__ void mx_phase1(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
                                           int wave) {
   mx_dma_one<0>(s, d, wave); GMLP_SB();
-  mx_mma_one<0, 0, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<0, 1, BF, Z>(f, acc); GMLP_SB();
+  mx_mma_one<0, 0, BF, Z, TR>(f, acc); GMLP_SB(); mx_mma_one<0, 1, BF, Z, TR>(f, acc); GMLP_SB();
   mx_dma_one<1>(s, d, wave); GMLP_SB();
-  mx_mma_one<0, 2, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<0, 3, BF, Z>(f, acc); GMLP_SB();
+  mx_mma_one<0, 2, BF, Z, TR>(f, acc); GMLP_SB(); mx_mma_one<0, 3, BF, Z, TR>(f, acc); GMLP_SB();
   mx_dma_one<2>(s, d, wave); GMLP_SB();
-  mx_mma_one<1, 0, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<1, 1, BF, Z>(f, acc); GMLP_SB();
+  mx_mma_one<1, 0, BF, Z, TR>(f, acc); GMLP_SB(); mx_mma_one<1, 1, BF, Z, TR>(f, acc); GMLP_SB();
   mx_dma_one<3>(s, d, wave); GMLP_SB();
-  mx_mma_one<1, 2, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<1, 3, BF, Z>(f, acc); GMLP_SB();
+  mx_mma_one<1, 2, BF, Z, TR>(f, acc); GMLP_SB(); mx_mma_one<1, 3, BF, Z, TR>(f, acc); GMLP_SB();
   mx_dma_one<4>(s, d, wave); GMLP_SB();
 }
 
-template <int PAR, int BF = 0, bool Z = false>
+template <int PAR, int BF = 0, bool Z = false, int TR = 0>
 __device__ __forceinline__ void mx_phase2p(const MxFrags& f, v16f (&acc)[4][4], const StageDma& s, const DmaPlan& d,
                                            int wave, const uint8_t* nstage, const ReadPlan& rp, MxFrags& nf) {
   mx_read_tp<0, PAR, BF>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<2, 0, BF, Z>(f, acc); GMLP_SB();
+  mx_mma_one<2, 0, BF, Z, TR>(f, acc); GMLP_SB();
   mx_dma_one<5>(s, d, wave); GMLP_SB();
   mx_read_tp<1, PAR, BF>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<2, 1, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<2, 2, BF, Z>(f, acc); GMLP_SB();
+  mx_mma_one<2, 1, BF, Z, TR>(f, acc); GMLP_SB(); mx_mma_one<2, 2, BF, Z, TR>(f, acc); GMLP_SB();
   mx_dma_one<6>(s, d, wave); GMLP_SB();
   mx_read_tp<2, PAR, BF>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<2, 3, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<3, 0, BF, Z>(f, acc); GMLP_SB();
+  mx_mma_one<2, 3, BF, Z, TR>(f, acc); GMLP_SB(); mx_mma_one<3, 0, BF, Z, TR>(f, acc); GMLP_SB();
   mx_dma_one<7>(s, d, wave); GMLP_SB();
   mx_read_tp<3, PAR, BF>(nstage, rp, nf); GMLP_SB();
-  mx_mma_one<3, 1, BF, Z>(f, acc); GMLP_SB(); mx_mma_one<3, 2, BF, Z>(f, acc); GMLP_SB();
+  mx_mma_one<3, 1, BF, Z, TR>(f, acc); GMLP_SB(); mx_mma_one<3, 2, BF, Z, TR>(f, acc); GMLP_SB();
   mx_dma_one<8>(s, d, wave); GMLP_SB();
-  mx_mma_one<3, 3, BF, Z>(f, acc); GMLP_SB();
+  mx_mma_one<3, 3, BF, Z, TR>(f, acc); GMLP_SB();
 }
 
 // ----------------------------------------------------------------------------- tile mapping
@@ -489,6 +499,13 @@ __device__ __forceinline__ int tiles_n(const GemmArgs& A) {
   if (MODE == MODE_FPROP)
     return (int)((A.N + BN - 1) / BN);
   return (int)((A.K + BN - 1) / BN);
+}
+
+// Stages of a weight-gradient tile over `tokens` tokens at `eb` bytes per token (64-byte stage
+// rows): the stages that hold a token, at least 2 for a non-empty group (the persistent kernel's
+// DMA window of three tiles needs every tile to span two stages), 0 for an empty one.
+__device__ __forceinline__ int wgrad_stages(int64_t tokens, int eb) {
+  return tokens > 0 ? (int)max((int64_t)2, (eb * tokens + 63) / 64) : 0;
 }
 
 // Context of tile bid of an ntm x ntn tile grid.
@@ -556,11 +573,15 @@ __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, in
     c.g = tile_m / per_g;
     if (c.g >= A.G) return false;
     mt = tile_m % per_g;
+    // the column-wise operands hold P tokens per group (the group's tokens padded with zeros to
+    // a multiple of 128); the stages stop at the last 64 (32 for bf16) that hold a token, but a
+    // tile keeps at least 2 (wgrad_stages)
     const int64_t P = A.T.col_off[c.g + 1] - A.T.col_off[c.g];
+    const int64_t tokens = min((int64_t)(A.T.row_off[c.g + 1] - A.T.row_off[c.g]), P);
     c.arow0 = (int64_t)mt * BM;
     c.arows = (int)min((int64_t)BM, A.N - c.arow0);
     c.nrow0 = (int64_t)c.nt * BN;
-    c.kvalid = P;
+    c.kvalid = tokens;
     c.a_base = A.N * (int64_t)A.T.col_off[c.g];
     c.a_ld = P;
     c.b_base = A.K * (int64_t)A.T.col_off[c.g];
@@ -571,7 +592,7 @@ __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, in
     c.a_sw_ld = A.N;
     c.b_sw_base = A.K * (int64_t)A.T.colw_off[c.g];
     c.b_sw_ld = A.K;
-    c.nk = (int)((P + 63) / 64);
+    c.nk = wgrad_stages(tokens, 1);
   }
   return true;
 }
@@ -851,6 +872,82 @@ __device__ __forceinline__ void mx_epilogue(const GemmArgs& A, const Ctx& c, con
   }
 }
 
+// bf16 epilogue of the transposed accumulators (EPI_STORE): lane (m + 32 j) of wave (wm, wn)
+// holds in acc[tm][tn][4 q + t] the output at tile row 128 wm + 32 tm + m and tile column
+// 128 wn + 32 tn + 8 q + 4 j + t, so four consecutive columns of one row are rounded to bf16 in
+// registers (the same product by the group scale and the same rounding as the fp32-staged
+// epilogue) and staged with one 8-byte LDS write.  Chunk tm (4 per tile) stages tile rows
+// 32 tm + [0, 32) and 128 + 32 tm + [0, 32) (staged row sr: tile row chunk_row(tm, sr)) across
+// all 256 columns: 64 rows of 512 bytes, one 32 KB ring slot.  The 16-byte column chunk c of
+// staged row sr sits at chunk c ^ (sr & 31), so that the 32 rows one write instruction covers
+// spread over the banks; each read instruction takes two whole rows.
+__device__ __forceinline__ uint32_t trs_off(int sr, int c) { return (uint32_t)(sr * 512 + ((c ^ (sr & 31)) << 4)); }
+
+// One accumulator register read where it is used (element access to the accumulator vectors
+// would have the compiler copy all of them to vector registers at once).
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+template <int MODE, int TM, int BF>
+__device__ __forceinline__ void epi_chunk_tr(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
+                                             int tid, int wm, int wn, int lane) {
+  {
+    const int m = lane & 31, j = lane >> 5;
+    const int sr = 32 * wm + m;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v0 = acc_read(acc[TM][tn][4 * q]), v1 = acc_read(acc[TM][tn][4 * q + 1]);
+        float v2 = acc_read(acc[TM][tn][4 * q + 2]), v3 = acc_read(acc[TM][tn][4 * q + 3]);
+        if constexpr (BF != 0) {
+          v0 = __fmul_rn(v0, c.alpha);
+          v1 = __fmul_rn(v1, c.alpha);
+          v2 = __fmul_rn(v2, c.alpha);
+          v3 = __fmul_rn(v3, c.alpha);
+        }
+        *reinterpret_cast<uint2*>(buf + trs_off(sr, 16 * wn + 4 * tn + q) + 8 * j) =
+            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+      }
+      GMLP_SB();   // a column tile at a time: few accumulators in vector registers at once
+    }
+  }
+  __syncthreads();
+  {
+    // thread tid stores 16-byte column chunk cc of staged rows 8 it + r0 (it = 0..7): one wave
+    // instruction covers two whole 512-byte rows
+    const int64_t ncols = (MODE == MODE_FPROP) ? A.N : A.K;
+    const int64_t orow0 = (MODE == MODE_FPROP) ? c.arow0 : (int64_t)c.g * A.N + c.arow0;
+    const uint32_t rowb = (uint32_t)(ncols * 2);
+    const __amdgpu_buffer_rsrc_t r =
+        out_rsrc(static_cast<uint8_t*>(A.c) + (orow0 * ncols + c.nrow0) * 2, (int64_t)c.arows * rowb);
+    const int cc = tid & 31, r0 = tid >> 5;
+    const uint32_t voff = (c.nrow0 + 8 * cc < ncols) ? (uint32_t)r0 * rowb + (uint32_t)(16 * cc) : kOutOfRange;
+    uint4 v[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) v[it] = *reinterpret_cast<const uint4*>(buf + trs_off(8 * it + r0, cc));
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      // tile row of staged row 8 it + r0 = 128 (it / 4) + 32 TM + 8 (it % 4) + r0; r0 goes in voff
+      const uint32_t ur = (uint32_t)(128 * (it >> 2) + 32 * TM + 8 * (it & 3));
+      out_store(r, voff, ur * rowb, v[it].x, v[it].y, v[it].z, v[it].w);
+    }
+  }
+  __syncthreads();
+}
+
+template <int MODE, int BF>
+__device__ __forceinline__ void mx_epilogue_tr(const GemmArgs& A, const Ctx& c, const v16f (&acc)[4][4], uint8_t* buf,
+                                               int tid, int wm, int wn, int lane) {
+  epi_chunk_tr<MODE, 0, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk_tr<MODE, 1, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk_tr<MODE, 2, BF>(A, c, acc, buf, tid, wm, wn, lane);
+  epi_chunk_tr<MODE, 3, BF>(A, c, acc, buf, tid, wm, wn, lane);
+}
+
 template <int MODE, int EPI, int BF = 0>
 __device__ __forceinline__ TileRef tile_ref(const GemmArgs& A, int t, int ntm, int ntn) {
   int mt;
@@ -859,7 +956,7 @@ __device__ __forceinline__ TileRef tile_ref(const GemmArgs& A, int t, int ntm, i
   TileRef r;
   // bf16: 32 contraction elements per 64-byte stage; token offsets of the column-wise
   // operands count 2 bytes per token
-  r.nk = uni(BF ? (int)((2 * c.kvalid + 63) / 64) : c.nk);
+  r.nk = uni((MODE == MODE_WGRAD && BF) ? wgrad_stages(c.kvalid, 2) : BF ? (int)((2 * c.kvalid + 63) / 64) : c.nk);
   r.arows = uni(c.arows);
   r.arow0 = uni(c.arow0);
   r.g = uni(c.g);
@@ -879,7 +976,8 @@ constexpr int64_t kEpiStages = 8;
 template <int BF>
 __device__ __forceinline__ int64_t wgrad_tile_cost(const GemmArgs& A, int g) {
   const int64_t P = A.T.col_off[g + 1] - A.T.col_off[g];
-  return ((BF ? 2 : 1) * P + 63) / 64 + kEpiStages;
+  const int64_t tokens = min((int64_t)(A.T.row_off[g + 1] - A.T.row_off[g]), P);
+  return wgrad_stages(tokens, BF ? 2 : 1) + kEpiStages;
 }
 // Only when the costs are skewed (the dearest tile above twice the mean): with near-equal costs
 // the equal-count ranges are whole rounds of the XCD's workgroups, which cost-cut ranges break.
@@ -919,6 +1017,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uni(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  // the bf16-store epilogue takes the transposed accumulators
+  constexpr int TR = (EPI == EPI_STORE) ? 1 : 0;
   // valid tiles and this workgroup's share
   const int ntn = tiles_n<MODE, EPI>(A);
   const int ntm = (MODE == MODE_FPROP) ? (A.G > 0 ? uni(A.T.t256_off[A.G]) : 0) : A.G * (int)((A.N + BM - 1) / BM);
@@ -1004,25 +1104,27 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
       // stage gs + 1 in between.  Stage gs + 1 may be the next tile's first (read again after
       // the epilogue) or no stage at all; such reads go unused.  Two steps per trip keep the two
       // fragment sets in fixed registers
-      // (stage kt + 1 of an even kt has parity 1, of an odd kt parity 0).  nk is even.
+      // (stage kt + 1 of an even kt has parity 1, of an odd kt parity 0).  A weight gradient's
+      // nk may be odd: its last trip runs the first step only.  Every tile has at least 2
+      // stages, so the stage three ahead always lies in the window's three tiles.
       // The first pair: its first step starts the accumulators (DMA targets 3 and 4 may be past
       // the tile).
       {
         const StageDma sd = window_stage(3, slot(gs + 3));
         GMLP_SB();
-        mx_phase1<BF, true>(f0, acc, sd, dpl, wave);
+        mx_phase1<BF, true, TR>(f0, acc, sd, dpl, wave);
         wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
         __syncthreads();
-        mx_phase2p<1, BF, true>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
+        mx_phase2p<1, BF, true, TR>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
         ++gs;
       }
       {
         const StageDma sd = window_stage(4, slot(gs + 3));
         GMLP_SB();
-        mx_phase1<BF>(f1, acc, sd, dpl, wave);
+        mx_phase1<BF, false, TR>(f1, acc, sd, dpl, wave);
         wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
         __syncthreads();
-        mx_phase2p<0, BF>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
+        mx_phase2p<0, BF, false, TR>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
         ++gs;
       }
       int kt = 2;
@@ -1037,10 +1139,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
           {
             const StageDma sd = run_stage(rr, soa, sob, sos, slot(gs + 3), s_voff, wave);
             GMLP_SB();
-            mx_phase1<BF>(f0, acc, sd, dpl, wave);
+            mx_phase1<BF, false, TR>(f0, acc, sd, dpl, wave);
             wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
             __syncthreads();
-            mx_phase2p<1, BF>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
+            mx_phase2p<1, BF, false, TR>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
             ++gs;
           }
           soa += KC.a_ps;
@@ -1048,10 +1150,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
           {
             const StageDma sd = run_stage(rr, soa, sob, sos + s_step, slot(gs + 3), s_voff, wave);
             GMLP_SB();
-            mx_phase1<BF>(f1, acc, sd, dpl, wave);
+            mx_phase1<BF, false, TR>(f1, acc, sd, dpl, wave);
             wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
             __syncthreads();
-            mx_phase2p<0, BF>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
+            mx_phase2p<0, BF, false, TR>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
             ++gs;
           }
           soa += KC.a_ps;
@@ -1064,19 +1166,19 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
         {
           const StageDma sd = window_stage(kt + 3, slot(gs + 3));
           GMLP_SB();
-          mx_phase1<BF>(f0, acc, sd, dpl, wave);
+          mx_phase1<BF, false, TR>(f0, acc, sd, dpl, wave);
           wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
           __syncthreads();
-          mx_phase2p<1, BF>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
+          mx_phase2p<1, BF, false, TR>(f0, acc, sd, dpl, wave, slot(gs + 1), rp, f1);
           ++gs;
         }
-        {
+        if (kt + 1 < nk) {
           const StageDma sd = window_stage(kt + 4, slot(gs + 3));
           GMLP_SB();
-          mx_phase1<BF>(f1, acc, sd, dpl, wave);
+          mx_phase1<BF, false, TR>(f1, acc, sd, dpl, wave);
           wait_vmcnt<MX_DMA_PER_STAGE + MX_DMA_BEFORE_BARRIER>();
           __syncthreads();
-          mx_phase2p<0, BF>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
+          mx_phase2p<0, BF, false, TR>(f1, acc, sd, dpl, wave, slot(gs + 1), rp, f0);
           ++gs;
         }
         kt += 2;
@@ -1091,7 +1193,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_mx_kernel(GemmArgs A) {
     // across every main loop).
     int tid_t = tid;
     asm volatile("" : "+v"(tid_t));
-    mx_epilogue<MODE, EPI, BF>(A, c, acc, slot(gs + 3), tid_t, wm, wn, tid_t & 63, t, red, tile_probs);
+    if constexpr (TR) {
+      mx_epilogue_tr<MODE, BF>(A, c, acc, slot(gs + 3), tid_t, wm, wn, tid_t & 63);
+    } else {
+      mx_epilogue<MODE, EPI, BF>(A, c, acc, slot(gs + 3), tid_t, wm, wn, tid_t & 63, t, red, tile_probs);
+    }
   }
   wait_vmcnt<0>();                     // the DMAs past the last tile (empty) before the LDS is released
 }

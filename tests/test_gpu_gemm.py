@@ -80,6 +80,45 @@ def test_gemm_wgrad(kind, splits, Na, Nb):
             assert np.all(got[e] == 0), "an empty expert must get a zero weight gradient"
 
 
+def _tiny_expert_splits():
+    """512 experts, most with one token, every 37th with 65, 129, 130 or 200 (odd stage counts),
+    a few empty: 2 tiles per expert at Na = 256, Nb = 512, so each workgroup runs 4 tiles in a row,
+    most of them of the shortest kind."""
+    splits = [1] * 512
+    for i, e in enumerate(range(5, 512, 37)):
+        splits[e] = (65, 129, 130, 200)[i % 4]
+    for e in (3, 200, 201, 450):
+        splits[e] = 0
+    return splits
+
+
+@pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
+def test_gemm_wgrad_runs_of_tiny_experts(kind):
+    """Weight gradients stop at the last 64-token stage (32 for bf16) that holds a token, so a
+    tile may span an odd number of stages, but never fewer than two: the persistent kernel
+    prefetches three stages ahead through a window of three tiles.  Sampled experts (a run of
+    one-token experts, every larger one, an empty one) against the oracle."""
+    splits, Na, Nb = _tiny_expert_splits(), 256, 512
+    M, E, mask = sum(splits), len(splits), 0x2D4B
+    print(f"gemm wgrad {kind} {E} tiny experts, M={M} Na={Na} Nb={Nb}", flush=True)
+    a = random_bf16((M, Na), seed=41)
+    b = random_bf16((M, Nb), seed=42, dist="srelu")
+    rec = g.recipe(kind, mask)
+    sd = dev_splits(splits)
+    aq = g.group_quantize(dev_bf16(a), sd, rec, False, True)
+    bq = g.group_quantize(dev_bf16(b), sd, rec, False, True)
+    c = g.grouped_gemm(g.GEMM_WGRAD, rec, aq, bq, sd, M, Na, Nb)
+    torch.cuda.synchronize()
+    got = F.bf16_bits_to_f64(bits16(c)).reshape(E, Na, Nb)
+    orec = O.Recipe(kind, mask)
+    _, ad = O.quantize_activation(a, splits, orec, row=False, col=True)
+    _, bd = O.quantize_activation(b, splits, orec, row=False, col=True)
+    sample = sorted(set(range(100, 140)) | {e for e in range(E) if splits[e] > 1} | {200})
+    ref = np.stack([ad["col"][e] @ bd["col"][e].T for e in sample])
+    assert O.rel_fro(got[sample], F.round_bf16(ref)) <= 1e-3
+    assert np.all(got[200] == 0), "an empty expert must get a zero weight gradient"
+
+
 @pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
 def test_gemm_fprop_more_tiles_than_workgroups(kind):
     """287 tiles of 256 x 256 for one workgroup per CU: every workgroup takes a second tile and
