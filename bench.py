@@ -13,9 +13,10 @@ timing; weights are quantized once, outside the timed steps.
 Prints one JSON line: TFLOP/s of the step (6 M H (F1 + ffn) flops), the
 roofline of the dominant kernel (the fc1-dgrad-shaped grouped GEMM of the same
 workload, timed live with HIP events on the stream it runs on, the 256 MB MALL
-flushed before every launch), the group-quantize GB/s of x (the outputs the step
-uses, flushed likewise) next to a device copy of the same input, and the CPU
-oracle timed on a bounded sample of the same workload.
+flushed before every launch) next to the vendor's dense FP8 GEMM at the same
+M, N, K, the group-quantize GB/s of x (the outputs the step uses, flushed
+likewise) next to a device copy of the same input, and the CPU oracle timed on
+a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -321,6 +322,33 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def dense_fp8_reference(torch, shape, flush, reps, dev):
+    """The vendor's dense FP8 GEMM at the dominant kernel's M, N, K: torch._scaled_mm (the ROCm
+    build's hipBLASLt path) with E4M3 operands, per-tensor scales and one weight matrix.  It does
+    the same MFMA work without grouping, padding or per-32 block scales, so its rate is a measured
+    ceiling for the matrix cores at the clock this load holds (the datasheet peak assumes 2.4 GHz).
+    None when the build lacks it."""
+    M, N, K = shape["M"], shape["N"], shape["K"]
+    try:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        a = torch.randn((M, K), device=dev, generator=gen).to(torch.float8_e4m3fn)
+        b = torch.randn((N, K), device=dev, generator=gen).to(torch.float8_e4m3fn)
+        one = torch.ones((), device=dev)
+        fn = lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = timed_flushed(torch, fn, reps, flush)
+    except (RuntimeError, AttributeError, TypeError) as ex:
+        log(f"dense FP8 reference unavailable: {type(ex).__name__}: {ex}")
+        return None
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    log(f"dense FP8 GEMM (torch._scaled_mm) {M}x{N}x{K}: {ms:.3f} ms  {tflops:.1f} TFLOP/s")
+    return {"kernel": "torch._scaled_mm dense E4M3, per-tensor scales, one weight matrix, same M, N, K",
+            "ms_per_launch": round(ms, 4), "tflops": round(tflops, 1)}
+
+
 def timed_flushed(torch, fn, reps, flush):
     """Mean device time of fn (HIP events on torch's current stream, which is the stream the library
     launches on), with a pass that reads a 512 MB buffer between launches so that the 256 MB MALL
@@ -435,6 +463,9 @@ def main():
     peak = MXFP8_PEAK_TFLOPS if kind == "mxfp8" else BF16_PEAK_TFLOPS
     log(f"fc1-dgrad GEMM: {k_ms:.3f} ms  {k_tflops:.1f} TFLOP/s  ({100 * k_tflops / peak:.1f}% of {peak:.0f})")
     del call
+    dense = dense_fp8_reference(torch, shape, flush, args.kernel_reps, dev) if kind == "mxfp8" else None
+    if dense is not None:
+        dense["frac"] = round(k_tflops / dense["tflops"], 4)
 
     # ------------------------------------------------------------------ group quantize GB/s (x, row + column-wise)
     # the outputs the step writes (MXFP8: data and MFMA scale words; NVFP4: data, E4M3 scales and
@@ -486,7 +517,8 @@ def main():
         "roofline": {"kernel": "grouped GEMM, fc1-dgrad shape (M=%d, N=%d, K=%d, %d experts)" % (M, H, F1, E),
                      "bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(k_tflops / peak, 4), "traffic": measured_traffic(shape),
-                     "algorithmic_bytes": gemm_algorithmic_bytes(shape), "ms_per_launch": round(k_ms, 4)},
+                     "algorithmic_bytes": gemm_algorithmic_bytes(shape), "ms_per_launch": round(k_ms, 4),
+                     "dense_fp8_reference": dense},
         "quantize": {"kernel": "MXFP8 group quantize of x, row + column-wise" if kind == "mxfp8" else
                      "NVFP4 group quantize of x (amax + row + column-wise RHT)",
                      "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
