@@ -15,7 +15,9 @@
 // One persistent kernel: workgroup tile 256 x 256, 4 waves of 128 x 128 (4 x 4 tiles of
 // 32 x 32), K staged through a 4-slot LDS ring of 64-byte rows (64 fp8, or 32 bf16 for
 // NVFP4) filled by buffer-to-LDS DMA, 16-byte chunks XOR-swizzled by row so that the MFMA
-// fragment reads are bank-conflict-free.
+// fragment reads are bank-conflict-free.  bf16 outputs take the transposed product and a
+// bf16-staged epilogue (mx_epilogue_tr); fp32 outputs and the fused amax stage fp32
+// (mx_epilogue).
 //
 // MXFP8: V_MFMA_SCALE_F32_32X32X64_F8F6F4 with E8M0 block scales.  Lane (m + 32j)
 // holds row m, K bytes [16j, 16j+16) and [32+16j, 48+16j) of the 64-K step, and
@@ -44,15 +46,6 @@ constexpr int MX_SC_OFF = 2 * MX_OPB;            // scale words: A [256] then B 
 constexpr int MX_STAGE = 2 * MX_OPB + 2048;      // 34 KB
 constexpr int MX_NSTAGE = 4;
 constexpr int MX_DMA_PER_STAGE = 9;              // per wave: 4 A + 4 B data DMAs + 1 scale-word DMA
-// Epilogue staging: 128 rows x 256 bf16 (512 bytes) per buffer; the 16-byte chunk index is
-// XORed with bits 2..3 of the row so that the two rows a wave writes at once (r and r + 4)
-// fall in different banks.
-// fp32 staging: 256 rows x 128 floats; rows 4 apart (the two lane halves of an MFMA output
-// register) land 32 banks apart.
-__device__ __forceinline__ int ep32_off(int row, int col) { return row * 128 + (col ^ (((row >> 2) & 1) << 5)); }
-__device__ __forceinline__ int ep_off(int row, int col) {
-  return row * 256 + ((((col >> 3) ^ (((row >> 2) & 3) << 2))) << 3) + (col & 7);
-}
 
 // Wave-uniform copies (the values are uniform by construction; this tells the compiler so
 // that descriptors and bases live in SGPRs).
@@ -610,15 +603,14 @@ __device__ __forceinline__ bool tile_ctx(const GemmArgs& A, int bid, int ntm, in
 // the T valid tiles and its workgroups take them in lockstep (tile lo + l, lo + l + n, ...),
 // so the tiles resident together on an XCD are neighbours in the group order of tile_ctx.
 
-// Epilogue of the persistent kernel: the 256 x 256 fp32 tile leaves the accumulators in 8
-// chunks of 64 rows x 128 columns (32 KB, one ring slot).  Chunk ch holds MFMA tile row
-// tm = ch / 2 of both wave halves (staged row sr -> tile row chunk_row(tm, sr)) and two of each
-// wave's four MFMA column tiles: tn = 2 q, 2 q + 1 (q = ch % 2), or for the SwiGLU fc1 all
-// four column tiles of the waves with wn = q (64 gate and the matching 64 up columns), so
-// that every output row segment a chunk stores is a whole 128-byte line (half-line
-// streaming stores cost about twice as much).  The accumulators are written to LDS
-// straight from the accumulator registers (inline ds_write_b32 with an AGPR operand), so
-// they are never copied to vector registers.
+// fp32-staged epilogue (fp32 outputs, the fused amax): the 256 x 256 fp32 tile leaves the
+// accumulators in 8 chunks of 64 rows x 128 columns (32 KB, one ring slot).  Chunk ch holds
+// MFMA tile row tm = ch / 2 of both wave halves (staged row sr -> tile row chunk_row(tm, sr))
+// and two of each wave's four MFMA column tiles: tn = 2 q, 2 q + 1 (q = ch % 2), so that every
+// output row segment a chunk stores is a whole 128-byte line (half-line streaming stores cost
+// about twice as much).  The accumulators are written to LDS straight from the accumulator
+// registers (inline ds_write_b32 with an AGPR operand), so they are never copied to vector
+// registers.
 __device__ __forceinline__ int chunk_row(int tm, int sr) { return ((sr >> 5) << 7) + 32 * tm + (sr & 31); }
 constexpr int EPC_LD = 136;        // floats per staged row: rows 4 apart are 32 banks apart
 
