@@ -21,6 +21,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace gmlp {
 
 constexpr int QT = 128;          // tokens per tile
@@ -134,44 +136,73 @@ __device__ __forceinline__ bool tile_info(const SplitTables& T, int G, int64_t K
 
 __device__ __forceinline__ void unpack8(const uint4& q, float* v);
 
-// 8 bf16 of row `row`, features k .. k + 7, of an NVFP4 pass's input: x itself, or the fc2
-// input a = bf16(act(h) p) formed from the fc1 output (the same function as every other
-// producer of a, so the bits agree).
-__device__ __forceinline__ uint4 load_in8(const uint16_t* __restrict__ x, int64_t K, const ActSrc& A, int64_t row,
-                                          int64_t k) {
-  if (!A.h) return *reinterpret_cast<const uint4*>(x + row * K + k);
-  const bool glu = act_is_glu(A.act.kind);
-  const int64_t F1 = glu ? 2 * A.ffn : A.ffn;
-  const uint4 gq = *reinterpret_cast<const uint4*>(A.h + row * F1 + k);
-  const uint4 uq = glu ? *reinterpret_cast<const uint4*>(A.h + row * F1 + A.ffn + k) : make_uint4(0, 0, 0, 0);
-  const float p = A.probs[row];
-  float g[8], u[8];
-  unpack8(gq, g);
-  unpack8(uq, u);
-  uint32_t w[4];
+// 8 bf16 of rows row[i], features k .. k + 7, of an NVFP4 pass's input (zeros where !ok[i]):
+// x itself, or the fc2 input a = bf16(act(h) p) formed from the fc1 output with the same
+// function as every other producer of a, so the bits agree.  Every read is issued before any
+// activation, so that the reads of the N rows are in flight together.
+template <int KIND, int N>
+__device__ __forceinline__ void load_act8(const ActSrc& A, const int64_t (&row)[N], const bool (&ok)[N], int64_t k,
+                                          uint4 (&q)[N]) {
+  constexpr bool GLU = act_is_glu(KIND);
+  const int64_t F1 = GLU ? 2 * A.ffn : A.ffn;
+  uint4 gq[N], uq[N];
+  float p[N];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = act_out_rt(A.act, g[2 * i], u[2 * i], p);
-    const float hi = act_out_rt(A.act, g[2 * i + 1], u[2 * i + 1], p);
-    w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  for (int i = 0; i < N; ++i) {
+    const uint16_t* h = A.h + row[i] * F1 + k;
+    gq[i] = ok[i] ? *reinterpret_cast<const uint4*>(h) : make_uint4(0, 0, 0, 0);
+    uq[i] = (GLU && ok[i]) ? *reinterpret_cast<const uint4*>(h + A.ffn) : make_uint4(0, 0, 0, 0);
+    p[i] = ok[i] ? A.probs[row[i]] : 0.0f;
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float g[8], u[8];
+    unpack8(gq[i], g);
+    unpack8(uq[i], u);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = act_out<KIND>(g[2 * j], u[2 * j], p[i], A.act.c);
+      const float hi = act_out<KIND>(g[2 * j + 1], u[2 * j + 1], p[i], A.act.c);
+      w[j] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    }
+    q[i] = ok[i] ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0, 0, 0, 0);
+  }
 }
+// IN: the input the pass reads, fixed per kernel instantiation so that each keeps its own register
+// budget: kInX for x itself, else the activation kind of the fc2 input formed from h.
+constexpr int kInX = -1;
+template <int IN, int N>
+__device__ __forceinline__ void load_in8(const uint16_t* __restrict__ x, int64_t K, const ActSrc& A,
+                                         const int64_t (&row)[N], const bool (&ok)[N], int64_t k, uint4 (&q)[N]) {
+  if constexpr (IN == kInX) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) q[i] = ok[i] ? *reinterpret_cast<const uint4*>(x + row[i] * K + k) : make_uint4(0, 0, 0, 0);
+  } else {
+    load_act8<IN, N>(A, row, ok, k, q);
+  }
+}
+// The input kind of a pass: kInX, or the activation kind when it reads h.
+inline int input_kind(const ActSrc& A) { return A.h ? A.act.kind : kInX; }
 
 // Load i of a thread covers tile row r = 32 wave + 4 i + lane / 16 and features 8 (lane % 16)
 // .. + 7, so that every load instruction reads four whole 256-byte row segments.  Values
 // outside the tile's valid rows / features are zero; with lds set they are also parked in the
 // unswizzled LDS tile [QT][LDW].
 __device__ __forceinline__ int chunk_row(int tid, int i) { return 32 * (tid >> 6) + 4 * i + ((tid & 63) >> 4); }
+template <int IN>
 __device__ __forceinline__ void load_row_chunk(const uint16_t* __restrict__ x, int64_t K, const TileInfo& ti,
                                                int tid, uint4 (&q)[8], uint16_t* lds, const ActSrc& A = ActSrc()) {
   const int kc = 8 * (tid & 15);
+  int64_t row[8];
+  bool ok[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = chunk_row(tid, i);
-    const bool ok = (r < ti.rows) && (kc < ti.kcols);
-    q[i] = ok ? load_in8(x, K, A, ti.gstart + ti.t0 + r, ti.k0 + kc) : make_uint4(0, 0, 0, 0);
+    ok[i] = (r < ti.rows) && (kc < ti.kcols);
+    row[i] = ti.gstart + ti.t0 + r;
   }
+  load_in8<IN>(x, K, A, row, ok, ti.k0 + kc, q);
   if (lds) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(lds + chunk_row(tid, i) * LDW + kc) = q[i];
@@ -588,6 +619,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   col_cast_tile64(tile, ti, ffn, ti.k0, T, o, tid);
 }
 
+template <int IN>
 __global__ __launch_bounds__(256) void hadamard_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                             SplitTables T, int G, uint32_t mask, ActSrc A) {
   __shared__ __align__(16) uint16_t tile[QT * LDW];
@@ -596,7 +628,7 @@ __global__ __launch_bounds__(256) void hadamard_amax_kernel(const uint16_t* __re
   if (!tile_info(T, G, K, ti)) return;
   const int tid = threadIdx.x;
   uint4 q[8];
-  load_row_chunk(x, K, ti, tid, q, tile, A);
+  load_row_chunk<IN>(x, K, ti, tid, q, tile, A);
   float amax_pre = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -723,7 +755,7 @@ __device__ __forceinline__ uint4 nv_bf16_half(uint32_t w, uint32_t code) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-template <bool ROW, bool COL>
+template <bool ROW, bool COL, int IN>
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                           SplitTables T, int G, uint32_t mask, int rht,
                                                           const float* __restrict__ pre,
@@ -739,12 +771,15 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __rest
   uint4 q[4];
   {
     const int kc = 8 * (tid & 15);
+    int64_t row[4];
+    bool ok[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = hrow(i);
-      const bool ok = (r < ti.rows) && (kc < ti.kcols);
-      q[i] = ok ? load_in8(x, K, A, ti.gstart + ti.t0 + r, ti.k0 + kc) : make_uint4(0, 0, 0, 0);
+      ok[i] = (r < ti.rows) && (kc < ti.kcols);
+      row[i] = ti.gstart + ti.t0 + r;
     }
+    load_in8<IN>(x, K, A, row, ok, ti.k0 + kc, q);
     if (COL) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(tile + hrow(i) * LDW + kc) = q[i];
@@ -911,7 +946,16 @@ hipError_t launch_amax_finalize(SplitTables T, int G, float* pre, float* post, h
 hipError_t launch_hadamard_amax(const uint16_t* x, int64_t M, int64_t K, SplitTables T, int G, uint32_t mask,
                                 float* pre, float* post, hipStream_t s, ActSrc act) {
   // with no rows the finalize still writes the (zero) amax of every group
-  if (M > 0) hipLaunchKernelGGL(hadamard_amax_kernel, tile_grid(M, K, G), dim3(256), 0, s, x, M, K, T, G, mask, act);
+  if (M > 0) {
+    const dim3 grid = tile_grid(M, K, G);
+    switch (input_kind(act)) {
+      case kInX: hipLaunchKernelGGL(hadamard_amax_kernel<kInX>, grid, dim3(256), 0, s, x, M, K, T, G, mask, act); break;
+      case ACT_SWIGLU: hipLaunchKernelGGL(hadamard_amax_kernel<ACT_SWIGLU>, grid, dim3(256), 0, s, x, M, K, T, G, mask, act); break;
+      case ACT_SRELU: hipLaunchKernelGGL(hadamard_amax_kernel<ACT_SRELU>, grid, dim3(256), 0, s, x, M, K, T, G, mask, act); break;
+      case ACT_TANH_SRELU: hipLaunchKernelGGL(hadamard_amax_kernel<ACT_TANH_SRELU>, grid, dim3(256), 0, s, x, M, K, T, G, mask, act); break;
+      default: hipLaunchKernelGGL(hadamard_amax_kernel<ACT_QGEGLU>, grid, dim3(256), 0, s, x, M, K, T, G, mask, act); break;
+    }
+  }
   hipLaunchKernelGGL(amax_finalize_kernel, dim3((unsigned)((2 * G + 255) / 256)), dim3(256), 0, s, T, G, pre, post);
   return hipGetLastError();
 }
@@ -922,15 +966,25 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, SplitTabl
   if (M == 0 || (!row && !col)) return hipSuccess;
   const dim3 grid((unsigned)((K + QF - 1) / QF), (unsigned)(2 * ((M + QT - 1) / QT + G)));   // half tiles
   const int r = rht ? 1 : 0;
-  if (row && col)
-    hipLaunchKernelGGL((nvfp4_quant_kernel<true, true>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o,
-                       act);
-  else if (row)
-    hipLaunchKernelGGL((nvfp4_quant_kernel<true, false>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o,
-                       act);
-  else
-    hipLaunchKernelGGL((nvfp4_quant_kernel<false, true>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post, o,
-                       act);
+  auto go = [&](auto in) {
+    constexpr int IN = decltype(in)::value;
+    if (row && col)
+      hipLaunchKernelGGL((nvfp4_quant_kernel<true, true, IN>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post,
+                         o, act);
+    else if (row)
+      hipLaunchKernelGGL((nvfp4_quant_kernel<true, false, IN>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post,
+                         o, act);
+    else
+      hipLaunchKernelGGL((nvfp4_quant_kernel<false, true, IN>), grid, dim3(256), 0, s, x, M, K, T, G, mask, r, pre, post,
+                         o, act);
+  };
+  switch (input_kind(act)) {
+    case kInX: go(std::integral_constant<int, kInX>()); break;
+    case ACT_SWIGLU: go(std::integral_constant<int, ACT_SWIGLU>()); break;
+    case ACT_SRELU: go(std::integral_constant<int, ACT_SRELU>()); break;
+    case ACT_TANH_SRELU: go(std::integral_constant<int, ACT_TANH_SRELU>()); break;
+    default: go(std::integral_constant<int, ACT_QGEGLU>()); break;
+  }
   return hipGetLastError();
 }
 
