@@ -229,7 +229,9 @@ gmlp_status gmlp_weight_quantize(const void* w, const void* const* w_ptrs, int32
 
 typedef enum {
   GMLP_GEMM_FPROP = 0,  /* C[rows of group g, N] = A_g [m_g, K] . B_g [N, K]^T   (A row-wise, B = weight) */
-  GMLP_GEMM_WGRAD = 1   /* C_g [N_a, N_b] = A_g [N_a, P_g] . B_g [N_b, P_g]^T       (both column-wise)   */
+  GMLP_GEMM_WGRAD = 1,  /* C_g [N_a, N_b] = A_g [N_a, P_g] . B_g [N_b, P_g]^T       (both column-wise)   */
+  GMLP_GEMM_DGRAD = 2   /* C[rows of group g, K_w] = A_g [m_g, N_w] . W_g [N_w, K_w] (A row-wise, B = the weight's
+                         * dgrad operand b->col_*: FPROP on W^T)                                          */
 } gmlp_gemm_layout;
 
 /* One grouped GEMM on already-quantized operands, fp32 accumulation, output
@@ -239,6 +241,8 @@ typedef enum {
  *        (b->row_*), n = N, k = K; C [M, N].
  * WGRAD: a, b = column-wise quantized tensors with rows N_a = n, N_b = k;
  *        C [G, n, k]; empty groups write zeros (accumulating: leave C_g as it is).
+ * DGRAD: a = row-wise quantized [M, k] gradient (k = the weight's N), b = weight whose
+ *        dgrad operand (b->col_*, blocks along N) is used, n = the weight's K; C [M, n].
  * out_dtype: gmlp_out_dtype; an unknown value is INVALID_ARG, accumulation with FPROP
  * UNSUPPORTED.
  * ws: >= gmlp_grouped_gemm_ws_bytes for the same arguments. */

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libgmlp.so")
 MXFP8, NVFP4_RHT = 0, 1
 SWIGLU, SRELU, TANH_SRELU, QGEGLU = 0, 1, 2, 3
 OUT_BF16, OUT_FP32, OUT_FP32_ACCUMULATE = 0, 1, 2
-GEMM_FPROP, GEMM_WGRAD = 0, 1
+GEMM_FPROP, GEMM_WGRAD, GEMM_DGRAD = 0, 1, 2
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP_ERROR"}
 COL_PAD = 128
 LAUNCH_KINDS = ("scan", "mxfp8_quantize", "hadamard_amax", "nvfp4_quantize", "gemm", "dprob_reduce", "fill")
@@ -370,7 +370,7 @@ def grouped_gemm(layout, rec, a, b, m_splits, M, n, k, out_dtype=OUT_BF16, ws=No
     G = m_splits.numel()
     dev = m_splits.device
     dt = torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32
-    shape = (M, n) if layout == GEMM_FPROP else (G, n, k)
+    shape = (G, n, k) if layout == GEMM_WGRAD else (M, n)
     if out is not None or out_dtype == OUT_FP32_ACCUMULATE:
         _check_out(out, shape, dt, "grouped_gemm out")
         c = out

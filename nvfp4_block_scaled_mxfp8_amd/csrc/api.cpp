@@ -626,12 +626,13 @@ gmlp_status gmlp_grouped_gemm_ws_bytes(int32_t layout, gmlp_recipe recipe, int32
   if (!bytes) return fail(GMLP_INVALID_ARG, "null output");
   gmlp_status st;
   if ((st = check_recipe(recipe)) != GMLP_OK) return st;
-  if (layout != GMLP_GEMM_FPROP && layout != GMLP_GEMM_WGRAD) return fail(GMLP_INVALID_ARG, "unknown GEMM layout %d", layout);
+  if (layout != GMLP_GEMM_FPROP && layout != GMLP_GEMM_WGRAD && layout != GMLP_GEMM_DGRAD)
+    return fail(GMLP_INVALID_ARG, "unknown GEMM layout %d", layout);
   if (G < 1 || M < 0 || n <= 0 || k <= 0) return fail(GMLP_INVALID_ARG, "dims: G, n, k must be positive and M >= 0");
   Bump bb(nullptr);
   carve_tables(bb, G);
   const int64_t Pt = M + 127LL * G;
-  if (layout == GMLP_GEMM_FPROP) carve_nv(bb, recipe, M * k, (int64_t)G * n * k);
+  if (layout != GMLP_GEMM_WGRAD) carve_nv(bb, recipe, M * k, (int64_t)G * n * k);
   else carve_nv(bb, recipe, n * Pt, k * Pt);
   *bytes = bb.off + 256;
   return ok();
@@ -643,18 +644,22 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
   memset(g_counts, 0, sizeof(g_counts));
   gmlp_status st;
   if ((st = check_recipe(recipe)) != GMLP_OK) return st;
-  if (layout != GMLP_GEMM_FPROP && layout != GMLP_GEMM_WGRAD) return fail(GMLP_INVALID_ARG, "unknown GEMM layout %d", layout);
+  if (layout != GMLP_GEMM_FPROP && layout != GMLP_GEMM_WGRAD && layout != GMLP_GEMM_DGRAD)
+    return fail(GMLP_INVALID_ARG, "unknown GEMM layout %d", layout);
   if (!a || !b || !m_splits || !c) return fail(GMLP_INVALID_ARG, "null pointer argument");
   if (G < 1 || M < 0 || n <= 0 || k <= 0 || n % 32 || k % 32) return fail(GMLP_UNSUPPORTED, "dims: n, k must be positive multiples of 32");
-  if (layout == GMLP_GEMM_FPROP && k % 128) return fail(GMLP_UNSUPPORTED, "dims: the FPROP contraction k must be a multiple of 128");
+  // DGRAD is FPROP on the weight's dgrad operand (W^T per expert, blocks along the weight's N)
+  const bool fp = layout != GMLP_GEMM_WGRAD;
+  if (fp && k % 128) return fail(GMLP_UNSUPPORTED, "dims: the FPROP / DGRAD contraction k must be a multiple of 128");
   if (out_dtype != GMLP_OUT_BF16 && out_dtype != GMLP_OUT_FP32 && out_dtype != GMLP_OUT_FP32_ACCUMULATE)
     return fail(GMLP_INVALID_ARG, "unknown output dtype %d", out_dtype);
   if (out_dtype == GMLP_OUT_FP32_ACCUMULATE && layout != GMLP_GEMM_WGRAD)
     return fail(GMLP_UNSUPPORTED, "accumulating output: WGRAD layout only");
+  const GemmOperand oa = fp ? op_row(*a, a->amax_pre) : op_col(*a, a->amax_post);
+  const GemmOperand ob = layout == GMLP_GEMM_FPROP ? op_row(*b, b->amax_pre)
+                         : layout == GMLP_GEMM_DGRAD ? op_col(*b, b->amax_pre)
+                                                     : op_col(*b, b->amax_post);
   {
-    const bool fp = layout == GMLP_GEMM_FPROP;
-    const GemmOperand oa = fp ? op_row(*a, a->amax_pre) : op_col(*a, a->amax_post);
-    const GemmOperand ob = fp ? op_row(*b, b->amax_pre) : op_col(*b, b->amax_post);
     const bool nv_a = oa.bf16 || (oa.data && oa.scale), nv_b = ob.bf16 || (ob.data && ob.scale);
     if (is_mx(recipe) ? (!oa.data || !ob.data || !oa.scale_mfma || !ob.scale_mfma)
                       : (!nv_a || !nv_b || !oa.amax || !ob.amax))
@@ -667,25 +672,19 @@ gmlp_status gmlp_grouped_gemm(int32_t layout, gmlp_recipe recipe, const gmlp_gro
   Bump bb(ws);
   SplitTables T = carve_tables(bb, G);
   const int64_t Pt = M + 127LL * G;
-  const NvScratch nv = layout == GMLP_GEMM_FPROP ? carve_nv(bb, recipe, M * k, (int64_t)G * n * k)
-                                                 : carve_nv(bb, recipe, n * Pt, k * Pt);
+  const NvScratch nv = fp ? carve_nv(bb, recipe, M * k, (int64_t)G * n * k) : carve_nv(bb, recipe, n * Pt, k * Pt);
   if (!ws || ws_bytes < bb.off) return fail(GMLP_WORKSPACE, "workspace too small: need %zu bytes", bb.off);
   Launcher L{stream};
   if (!L.check(launch_scan(m_splits, G, M, T, stream), "scan")) return L.st;
-  GemmArgs g = gemm_base(layout == GMLP_GEMM_FPROP ? MODE_FPROP : MODE_WGRAD, recipe, EPI_STORE, T, G);
+  GemmArgs g = gemm_base(fp ? MODE_FPROP : MODE_WGRAD, recipe, EPI_STORE, T, G);
   set_nv(g, nv);
   g.M = M;
   g.N = n;
   g.K = k;
   g.c = c;
   g.out_fp32 = out_dtype;   // 0 bf16, 1 fp32, 2 fp32 added to c
-  if (layout == GMLP_GEMM_FPROP) {
-    g.a = op_row(*a, a->amax_pre);
-    g.b = op_row(*b, b->amax_pre);
-  } else {
-    g.a = op_col(*a, a->amax_post);
-    g.b = op_col(*b, b->amax_post);
-  }
+  g.a = oa;
+  g.b = ob;
 
   if (!L.check(launch_gemm(g, stream), "grouped gemm")) return L.st;
   g_counts[CNT_GEMM]++;

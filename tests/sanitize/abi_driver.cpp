@@ -117,6 +117,16 @@ int main() {
                            fake(0x80000000), GMLP_OUT_FP32_ACCUMULATE, ws, 1 << 20, nullptr), GMLP_UNSUPPORTED);
   EXPECT(gmlp_grouped_gemm(GMLP_GEMM_FPROP, mx, &qm, &wm, static_cast<const int32_t*>(splits), 8, 32768, 4096, 3000,
                            fake(0x80000000), GMLP_OUT_BF16, ws, 1 << 20, nullptr), GMLP_UNSUPPORTED);
+  // DGRAD: the weight's dgrad operand as B (n = the weight's K, k = its N)
+  EXPECT(gmlp_grouped_gemm_ws_bytes(GMLP_GEMM_DGRAD, nv, 8, 32768, 4096, 3072, &gws), GMLP_OK);
+  EXPECT(gmlp_grouped_gemm(GMLP_GEMM_DGRAD, mx, &qm, &wm, static_cast<const int32_t*>(splits), 8, 32768, 4096, 3072,
+                           fake(0x80000000), GMLP_OUT_BF16, ws, 1 << 20, nullptr), GMLP_OK);
+  EXPECT(gmlp_grouped_gemm(GMLP_GEMM_DGRAD, mx, &qm, &wm, static_cast<const int32_t*>(splits), 8, 32768, 4096, 3000,
+                           fake(0x80000000), GMLP_OUT_BF16, ws, 1 << 20, nullptr), GMLP_UNSUPPORTED);
+  EXPECT(gmlp_grouped_gemm(GMLP_GEMM_DGRAD, mx, &qm, &wm, static_cast<const int32_t*>(splits), 8, 32768, 4096, 3072,
+                           fake(0x80000000), GMLP_OUT_FP32_ACCUMULATE, ws, 1 << 20, nullptr), GMLP_UNSUPPORTED);
+  EXPECT(gmlp_grouped_gemm(3, mx, &qm, &wm, static_cast<const int32_t*>(splits), 8, 32768, 4096, 3072,
+                           fake(0x80000000), GMLP_OUT_BF16, ws, 1 << 20, nullptr), GMLP_INVALID_ARG);
 
   // ---------------------------------------------------------------- fused MLP
   for (int kind = 0; kind < 2; ++kind) {

@@ -294,7 +294,8 @@ def test_gemm_nvfp4_wgrad_exact_inputs_bitwise():
 @pytest.mark.parametrize("splits,N,K", [([0, 37, 300, 129], 256, 384), ([700, 1, 0], 384, 640)])
 def test_gemm_dgrad_orientation(kind, splits, N, K):
     """C [M, K] = A [M, N] . W^T, the fc1 / fc2 dgrad: A row-wise with blocks along N, and the
-    weight's dgrad operand (W_e^T [K, N] per expert, blocks along N) as B."""
+    weight's dgrad operand (W_e^T [K, N] per expert, blocks along N) as B, passed as an FPROP
+    operand and through the DGRAD layout."""
     M, E, mask = sum(splits), len(splits), 0x1D2B
     print(f"gemm dgrad {kind} splits={splits} N={N} K={K}", flush=True)
     a = random_bf16((M, N), seed=M + 3 * N)
@@ -307,7 +308,10 @@ def test_gemm_dgrad_orientation(kind, splits, N, K):
                              "row_scale_mfma": wq.bufs.get("col_scale_mfma"), "amax_pre": wq.bufs.get("amax_pre"),
                              "row_bf16": wq.bufs.get("col_bf16")})
     c = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wd, sd, M, K, N)
+    # the DGRAD layout takes the weight as quantized (its dgrad operand) and must give the same bits
+    c2 = g.grouped_gemm(g.GEMM_DGRAD, rec, aq, wq, sd, M, K, N)
     torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), c2.view(torch.int16)), "DGRAD layout differs from FPROP on W^T"
     orec = O.Recipe(kind, mask)
     _, ad = O.quantize_activation(a, splits, orec, row=True, col=False)
     _, wdq = O.quantize_weight(w, orec)
