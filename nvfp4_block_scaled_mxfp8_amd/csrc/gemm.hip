@@ -876,7 +876,10 @@ __device__ __forceinline__ void mx_epilogue(const GemmArgs& A, const Ctx& c, con
 __device__ __forceinline__ uint32_t trs_off(int sr, int c) { return (uint32_t)(sr * 512 + ((c ^ (sr & 31)) << 4)); }
 
 // One accumulator register read where it is used (element access to the accumulator vectors
-// would have the compiler copy all of them to vector registers at once).
+// would have the compiler copy all of them to vector registers at once).  The epilogue reads the
+// MFMA tile rows in the order the last step computed them (tm = 0 first, whose MFMAs issue
+// first), so every read comes at least eight MFMAs (about 500 cycles) after the MFMA that wrote
+// its register, far past the MFMA-to-read wait the hardware requires.
 __device__ __forceinline__ float acc_read(float a) {
   float v;
   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
