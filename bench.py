@@ -71,12 +71,18 @@ def traffic_file(shape):
 
 
 def kernel_source_hash():
+    """sha256 of the GEMM kernel's sources with comments and whitespace runs removed: the code a
+    traffic or counter record was taken with (a comment edit leaves the records valid)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_block_scaled_mxfp8_amd", "csrc")
     for name in ("gemm.hip", "kernels.h", "device_common.h"):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
     return h.hexdigest()
 
 
