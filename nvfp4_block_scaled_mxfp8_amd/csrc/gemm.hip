@@ -354,7 +354,7 @@ __device__ __forceinline__ StageDma run_stage(const RunDma& r, uint32_t soa, uin
   return s;
 }
 
-// DMA number I (0..8) of a stage: even I < 8 an A instruction, odd I < 8 a B instruction, 8 the
+// DMA number I (0..8) of a stage: I < 4 an A instruction, 4 <= I < 8 a B instruction, 8 the
 // scale words.
 template <int I>
 __device__ __forceinline__ void mx_dma_one(const StageDma& s, const DmaPlan& d, int wave) {

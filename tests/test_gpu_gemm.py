@@ -146,6 +146,48 @@ def test_gemm_fprop_more_tiles_than_workgroups(kind):
     assert torch.equal(c32.to(torch.bfloat16).view(torch.int16), c.view(torch.int16))
 
 
+def _many_small_expert_splits():
+    """64 experts of 0..500 rows (seeded), with the row counts at the 64-, 128- and 256-row
+    boundaries spelled out: full and partial 256-row tiles (down to one valid row, and 64-row
+    bands with none), in the expert-by-expert launch order (at most 512 rows per expert on
+    average)."""
+    rng = np.random.default_rng(77)
+    s = list(rng.integers(0, 501, size=52))
+    return s + [0, 1, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384]
+
+
+@pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
+def test_gemm_fprop_many_small_experts(kind):
+    """More tiles than workgroups (540 tiles, three rounds) over 64 small experts, ordered
+    expert by expert.  Within the GEMM tolerance of the oracle, every expert on its own too,
+    bitwise repeatable, and the bf16 output is the fp32 one rounded."""
+    splits, N, K = _many_small_expert_splits(), 1536, 256
+    M, E, mask = sum(splits), len(splits), 0x1D2B
+    print(f"gemm fprop many small experts {kind} M={M} E={E} N={N} K={K}", flush=True)
+    x = random_bf16((M, K), seed=41)
+    w = random_bf16((E, N, K), seed=42, std=1 / np.sqrt(K))
+    rec = g.recipe(kind, mask)
+    sd = dev_splits(splits)
+    aq = g.group_quantize(dev_bf16(x), sd, rec, True, False)
+    wq = g.weight_quantize(dev_bf16(w.reshape(E * N, K)).view(E, N, K), rec)
+    c = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wq, sd, M, N, K)
+    c2 = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wq, sd, M, N, K)
+    c32 = g.grouped_gemm(g.GEMM_FPROP, rec, aq, wq, sd, M, N, K, out_dtype=g.OUT_FP32)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), c2.view(torch.int16)), "not repeatable"
+    ref = _fprop_ref(x, w, splits, kind, mask)
+    got = F.bf16_bits_to_f64(bits16(c)).reshape(M, N)
+    assert O.rel_fro(got, F.round_bf16(ref)) <= 1e-3
+    # every expert on its own (a wrong row mapping of one small tile would hide in the total)
+    off = 0
+    for e, m in enumerate(splits):
+        if m:
+            assert O.rel_fro(got[off:off + m], F.round_bf16(ref[off:off + m])) <= 2e-3, (e, m)
+        off += m
+    assert O.rel_fro(c32.cpu().double().numpy(), ref) <= 5e-5
+    assert torch.equal(c32.to(torch.bfloat16).view(torch.int16), c.view(torch.int16))
+
+
 @pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
 def test_gemm_wgrad_accumulates_into_fp32(kind):
     """WGRAD with OUT_FP32_ACCUMULATE adds the product to the fp32 tensor given, twice in a row:
