@@ -85,13 +85,14 @@ __device__ __forceinline__ float e4m3_decode_pos(uint32_t c) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// E2M1 nibble -> fp32 value (exact): magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.
-__device__ __forceinline__ float e2m1_decode(uint32_t n) {
-  const uint32_t mag = n & 7u;
-  // 0.5 * {0,1,2,3,4,6,8,12}
-  const uint32_t twice = (mag < 4u) ? mag : (mag == 4u ? 4u : (mag == 5u ? 6u : (mag == 6u ? 8u : 12u)));
-  float v = (float)twice * 0.5f;
-  return (n & 8u) ? -v : v;
+// The two E2M1 values of byte I of w (low nibble first) times sc, as one bf16 pair (the low
+// nibble's value in bits [0, 16)).  The hardware converter gives each E2M1 value exactly
+// (magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}, the sign from bit 3); a product with an E4M3 block
+// scale has at most 6 significant bits, so its bf16 bits are the high half of its fp32 bits.
+template <int I>
+__device__ __forceinline__ uint32_t e2m1x2_scaled_bf16(uint32_t w, float sc) {
+  const v2f p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, I);
+  return (__float_as_uint(p.x * sc) >> 16) | (__float_as_uint(p.y * sc) & 0xFFFF0000u);
 }
 
 // --------------------------------------------------------------------------- NVFP4 global scale

@@ -705,23 +705,19 @@ __device__ __forceinline__ uint32_t nv_block(const float* v, float S, uint32_t& 
   return code;
 }
 
+// Eight packed E2M1 codes (one word) with block scale sc as eight bf16 dec(E2M1) dec(E4M3).
+__device__ __forceinline__ v4i nv_bf16x8(uint32_t w, float sc) {
+  return v4i{(int)e2m1x2_scaled_bf16<0>(w, sc), (int)e2m1x2_scaled_bf16<1>(w, sc), (int)e2m1x2_scaled_bf16<2>(w, sc),
+             (int)e2m1x2_scaled_bf16<3>(w, sc)};
+}
 // The 16 quantized values of a block as bf16 dec(E2M1) dec(E4M3) (exact: at most 6 significant
 // bits), written as 32 contiguous bytes of a GEMM operand panel: half of a 64-byte panel row,
 // whose other half the same lane writes for the neighbouring block.  Plain (write-back) stores,
 // so that the two halves meet in L2 before the line goes to HBM.
 __device__ __forceinline__ void nv_bf16_store(uint8_t* dst, uint32_t lo, uint32_t hi, uint32_t code) {
   const float sc = e4m3_decode_pos(code);
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t w = i < 4 ? lo : hi;
-    const int sh = 8 * (i & 3);
-    const float a = e2m1_decode((w >> sh) & 0xFu) * sc;
-    const float b = e2m1_decode((w >> (sh + 4)) & 0xFu) * sc;
-    o[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-  }
-  *reinterpret_cast<v4i*>(dst) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-  *reinterpret_cast<v4i*>(dst + 16) = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+  *reinterpret_cast<v4i*>(dst) = nv_bf16x8(lo, sc);
+  *reinterpret_cast<v4i*>(dst + 16) = nv_bf16x8(hi, sc);
 }
 
 // Half (8 values) of a 16-value block whose other half lane ^ 1 holds: the same steps as
@@ -744,15 +740,8 @@ __device__ __forceinline__ uint32_t nv_half_block(const float* v, float S, uint3
 
 // The 8 values of one lane's half block as bf16 dec(E2M1) dec(E4M3): 16 bytes of a panel row.
 __device__ __forceinline__ uint4 nv_bf16_half(uint32_t w, uint32_t code) {
-  const float sc = e4m3_decode_pos(code);
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = e2m1_decode((w >> (8 * i)) & 0xFu) * sc;
-    const float b = e2m1_decode((w >> (8 * i + 4)) & 0xFu) * sc;
-    o[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  const v4i o = nv_bf16x8(w, e4m3_decode_pos(code));
+  return make_uint4((uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]);
 }
 
 template <bool ROW, bool COL, int IN>
@@ -1046,16 +1035,8 @@ __global__ __launch_bounds__(256) void nv_expand_kernel(const uint8_t* __restric
   if (c >= cols) return;
   const int64_t e = base + r * cols + c;                   // element index (a multiple of 8)
   const uint32_t w = *reinterpret_cast<const uint32_t*>(data + e / 2);
-  const float sc = e4m3_decode_pos(scale[e / 16]);
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = e2m1_decode((w >> (8 * i)) & 0xFu) * sc;
-    const float hi = e2m1_decode((w >> (8 * i + 4)) & 0xFu) * sc;
-    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);   // exact: truncation drops zeros
-  }
   uint8_t* dst = out + 2 * base + (((c / 32) * R + r) * 64 + 2 * (c % 32));
-  __builtin_nontemporal_store(v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]}, reinterpret_cast<v4i*>(dst));
+  __builtin_nontemporal_store(nv_bf16x8(w, e4m3_decode_pos(scale[e / 16])), reinterpret_cast<v4i*>(dst));
 }
 
 hipError_t launch_nv_expand(const uint8_t* data, const uint8_t* scale, uint8_t* out, int64_t R, int64_t C, int nmat,
