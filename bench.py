@@ -474,13 +474,18 @@ def main():
         dense["frac"] = round(k_tflops / dense["tflops"], 4)
 
     # ------------------------------------------------------------------ group quantize GB/s (x, row + column-wise)
-    # the outputs the step writes (MXFP8: data and MFMA scale words; NVFP4: data, E4M3 scales and
-    # bf16 panels of the column-wise operand are not asked for here), next to a device-to-device
-    # copy of x: the read + write stream the quantize is (the copy's rate is the practical ceiling
-    # of such a stream on this device, below the 8 TB/s datasheet figure)
+    # the outputs the step writes (MXFP8: data and MFMA scale words; NVFP4: the bf16 GEMM panels,
+    # row- and column-wise, which the step's GEMMs read instead of the packed form), next to a
+    # device-to-device copy of x: the read + write stream the quantize is (the copy's rate is the
+    # practical ceiling of such a stream on this device, below the 8 TB/s datasheet figure)
     qout = g.alloc_grouped_q(rec, M, H, E, True, True, dev)
     if kind == "mxfp8":
         qout = g.QTensor(qout.kind, {k: v for k, v in qout.bufs.items() if k not in ("row_scale", "col_scale")})
+    else:
+        u8 = dict(dtype=torch.uint8, device=dev)
+        qout = g.QTensor(qout.kind, {"amax_pre": qout.bufs["amax_pre"], "amax_post": qout.bufs["amax_post"],
+                                     "row_bf16": torch.empty(2 * M * H, **u8),
+                                     "col_bf16": torch.empty(2 * H * g.col_rows_bound(M, E), **u8)})
     qws = g.quant_workspace(E, dev)
     quant = lambda: g.group_quantize(x, splits, rec, True, True, out=qout, ws=qws)
     xcopy = torch.empty_like(x)
@@ -491,8 +496,9 @@ def main():
     torch.cuda.synchronize()
     q_ms = timed_flushed(torch, quant, args.kernel_reps, flush)
     c_ms = timed_flushed(torch, copy, args.kernel_reps, flush)
-    # NVFP4: the amax pass reads x, then the cast reads it again (the pages' two-pass method)
-    q_bytes = (2 + 1 + 1 + 2.0 / 32) * M * H if kind == "mxfp8" else (2 + 2 + 0.5 + 1 / 16 + 0.5 + 1 / 16) * M * H
+    # NVFP4: the amax pass reads x, then the cast reads it again (the pages' two-pass method) and
+    # writes 2-byte panel elements both ways
+    q_bytes = (2 + 1 + 1 + 2.0 / 32) * M * H if kind == "mxfp8" else (2 + 2 + 2 + 2) * M * H
     q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     c_gbs = 4.0 * M * H / (c_ms * 1e-3) / 1e9
     log(f"group quantize x: {q_ms * 1e3:.1f} us  {q_gbs:.0f} GB/s ({100 * q_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); "
@@ -526,7 +532,7 @@ def main():
                      "algorithmic_bytes": gemm_algorithmic_bytes(shape), "ms_per_launch": round(k_ms, 4),
                      "dense_fp8_reference": dense},
         "quantize": {"kernel": "MXFP8 group quantize of x, row + column-wise" if kind == "mxfp8" else
-                     "NVFP4 group quantize of x (amax + row + column-wise RHT)",
+                     "NVFP4 group quantize of x (amax + row + column-wise RHT, bf16 GEMM panels)",
                      "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(q_gbs / HBM_PEAK_GBS, 4), "us_per_call": round(q_ms * 1e3, 2),
                      "algorithmic_bytes": q_bytes, "device_copy_gbs": round(c_gbs, 1),
