@@ -19,7 +19,7 @@ import torch
 
 import nvfp4_block_scaled_mxfp8_amd as g
 from conftest import read_golden
-from gpu_util import assert_bytes_equal, bits16, col_total, dev_bf16, dev_f32, dev_splits, f32bits, u8
+from gpu_util import assert_bytes_equal, bits16, col_total, dev_bf16, dev_f32, dev_splits, f32bits, u8, unpanel
 from oracle import formats as F
 from oracle import mlp as O
 from oracle import quant as Q
@@ -140,6 +140,18 @@ def _sweep_input(order, seed, limit_bits=None):
     return x.reshape(M, K)
 
 
+def _nv_values_bf16(packed, scales):
+    """bf16 bits of dec(E2M1) * dec(E4M3) for the oracle's packed codes [R, C/2] and scales [R, C/16]."""
+    nib = F.unpack_fp4(packed)
+    vals = F.e2m1_decode(nib) * np.repeat(F.e4m3_decode(scales), 16, axis=-1)
+    return F.f64_to_bf16_bits(vals)
+
+
+def _unpanel16(buf, R, C):
+    """bf16 operand panels (2-byte elements, 32 per 64-byte row) -> [R, C] uint16."""
+    return np.ascontiguousarray(unpanel(np.asarray(buf).reshape(-1)[:2 * R * C], R, 2 * C)).view(np.uint16)
+
+
 # The Hadamard transform sums 16 values: inputs of magnitude 2^124 and above can overflow fp32 in
 # it, which is outside the casts' domain (finite inputs with a finite transform), so the
 # column-wise sweep takes the patterns below 2^120 (bf16 bits 0x7B80).
@@ -163,17 +175,31 @@ def test_nvfp4_every_bf16_pattern_activation_casts(order, direction):
     amax = np.array([own[i] if a is None else a for i, a in enumerate(AMAXES)], np.float32)
     print(f"nvfp4 exhaustive sweep {direction} order={order}: M={M} K={K} groups={splits} amax={amax}", flush=True)
     rec = g.recipe("nvfp4", mask)
+    # the bf16 GEMM panels too (the form the fused MLP's GEMMs read): every scale code and nibble
+    # the sweep produces goes through the hardware E2M1 expansion
+    q = g.alloc_grouped_q(rec, M, K, len(splits), not col, col)
+    key = "col_bf16" if col else "row_bf16"
+    q.bufs[key] = torch.zeros(2 * K * (g.col_rows_bound(M, len(splits)) if col else M), dtype=torch.uint8,
+                              device="cuda")
     q = g.group_quantize_with_amax(dev_bf16(x), dev_splits(splits), rec, dev_f32(amax), dev_f32(amax),
-                                   not col, col)
+                                   not col, col, out=q)
     torch.cuda.synchronize()
     ref = Q.nvfp4_group_quantize_with_amax(x, splits, amax, amax, mask, row=not col, col=col)
     if col:
         P = col_total(splits)
         assert_bytes_equal(u8(q.bufs["col_data"])[:K * P // 2], ref["col_data"], "col data")
         assert_bytes_equal(u8(q.bufs["col_scale"])[:K * P // 16], ref["col_scale"], "col scales")
+        panels, off = u8(q.bufs[key]), 0
+        for gi, (packed, sc) in enumerate(ref["col_groups"]):
+            Pg = -(-splits[gi] // 128) * 128
+            assert_bytes_equal(_unpanel16(panels[2 * off:2 * (off + K * Pg)], K, Pg), _nv_values_bf16(packed, sc),
+                               f"col bf16 panels of group {gi}")
+            off += K * Pg
     else:
         assert_bytes_equal(u8(q.bufs["row_data"])[:M * K // 2], ref["row_data"], "row data")
         assert_bytes_equal(u8(q.bufs["row_scale"])[:M * K // 16], ref["row_scale"], "row scales")
+        assert_bytes_equal(_unpanel16(u8(q.bufs[key]), M, K),
+                           _nv_values_bf16(ref["row_data"].reshape(M, K // 2), ref["row_scale"]), "row bf16 panels")
 
 
 def test_nvfp4_every_bf16_pattern_weight_casts():
