@@ -70,14 +70,19 @@ def traffic_file(shape):
     return os.path.join(PROFILES, "gemm_mx_fc1_dgrad_%dx%dx%d_traffic.json" % (shape["M"], shape["N"], shape["K"]))
 
 
-def kernel_source_hash():
-    """sha256 of the GEMM kernel's sources with comments and whitespace runs removed: the code a
-    traffic or counter record was taken with (a comment edit leaves the records valid)."""
+KERNEL_SOURCES = ("gemm.hip", "kernels.h", "device_common.h")
+
+
+def kernel_source_hash(csrc=None):
+    """sha256 of the GEMM kernel's sources (under csrc, by default the package's) with comments and
+    whitespace runs removed: the code a traffic or counter record was taken with (a comment edit
+    leaves the records valid)."""
     import hashlib
     import re
     h = hashlib.sha256()
-    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_block_scaled_mxfp8_amd", "csrc")
-    for name in ("gemm.hip", "kernels.h", "device_common.h"):
+    if csrc is None:
+        csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_block_scaled_mxfp8_amd", "csrc")
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
