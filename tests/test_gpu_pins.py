@@ -280,6 +280,31 @@ def test_gemm_nvfp4_fprop_exact_inputs_bitwise():
     assert np.array_equal(bits16(c).reshape(M, N), F.f64_to_bf16_bits(ref))
 
 
+def test_gemm_nvfp4_expands_every_code_exactly():
+    """Every E2M1 code under every finite E4M3 block scale (codes 0..126, one per row of A) through
+    the GEMM's expansion of packed operands, read back exactly: B is the identity (E2M1 1.0 under
+    scale 1.0) and both group amaxes are 2688 (global scales 1), so the fp32 output is
+    dec(E2M1) dec(E4M3) of each element of A (zeros compared by value)."""
+    codes = np.arange(127, dtype=np.uint8)
+    M, N, K = codes.size, 256, 256
+    nib = (np.arange(M * K, dtype=np.int64).reshape(M, K) + np.arange(M)[:, None]) % 16
+    nib = nib.astype(np.uint8)
+    asc = np.repeat(codes[:, None], K // 16, axis=1)
+    bn = np.zeros((N, K), np.uint8)
+    bn[np.arange(N), np.arange(N)] = 2                       # E2M1 code 2 = 1.0
+    bsc = np.full((N, K // 16), 0x38, np.uint8)              # E4M3 1.0
+    amax = np.array([2688.0], np.float32)
+    rec = g.recipe("nvfp4", 0)
+    A = g.QTensor(g.NVFP4_RHT, {"row_data": torch.from_numpy(F.pack_fp4(nib)).cuda(),
+                                "row_scale": torch.from_numpy(asc).cuda(), "amax_pre": dev_f32(amax)})
+    B = g.QTensor(g.NVFP4_RHT, {"row_data": torch.from_numpy(F.pack_fp4(bn)[None]).cuda(),
+                                "row_scale": torch.from_numpy(bsc[None]).cuda(), "amax_pre": dev_f32(amax)})
+    c32 = g.grouped_gemm(g.GEMM_FPROP, rec, A, B, dev_splits([M]), M, N, K, out_dtype=g.OUT_FP32)
+    torch.cuda.synchronize()
+    want = F.e2m1_decode(nib) * F.e4m3_decode(asc).repeat(16, axis=1)
+    assert np.array_equal(c32.cpu().numpy().astype(np.float64), want)
+
+
 def test_gemm_nvfp4_wgrad_exact_inputs_bitwise():
     rng = np.random.default_rng(4)
     splits, Na, Nb = [40, 0, 300, 128], 256, 128
