@@ -280,6 +280,47 @@ def test_gemm_nvfp4_fprop_exact_inputs_bitwise():
     assert np.array_equal(bits16(c).reshape(M, N), F.f64_to_bf16_bits(ref))
 
 
+def _panel(a):
+    """[R, K] bytes (K a multiple of 64) -> the 64-byte K-panel layout of the GEMM operands."""
+    R, K = a.shape
+    return np.ascontiguousarray(a.reshape(R, K // 64, 64).transpose(1, 0, 2)).reshape(-1)
+
+
+def _scale_words(codes):
+    """E8M0 codes [R, K / 32] -> MFMA scale words [K / 128, R] (byte j: 32-block 4 w + j)."""
+    R, nb = codes.shape
+    c = codes.astype(np.uint32).reshape(R, nb // 4, 4)
+    return np.ascontiguousarray((c[..., 0] | (c[..., 1] << 8) | (c[..., 2] << 16) | (c[..., 3] << 24)).T)
+
+
+def test_gemm_mxfp8_every_code_exactly():
+    """Every finite E4M3 code (each row of A cycles through all 254) under E8M0 block scales
+    2^-24 .. 2^23 through the scaled MFMA, read back exactly: B is the identity (E4M3 1.0 under
+    scale 2^0), so the fp32 output is dec(E4M3) 2^(X - 127) of each element of A (zeros compared
+    by value) and the bf16 output its rounding."""
+    M, N, K = 96, 256, 256
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    idx = (np.arange(K)[None, :] + 7 * np.arange(M)[:, None]) % finite.size
+    a = finite[idx]
+    a_codes = (103 + (np.arange(M)[:, None] + 5 * np.arange(K // 32)[None, :]) % 48).astype(np.uint8)
+    b = np.zeros((N, K), np.uint8)
+    b[np.arange(N), np.arange(N)] = 0x38                       # E4M3 1.0
+    b_codes = np.full((N, K // 32), 127, np.uint8)             # 2^0
+    rec = g.recipe("mxfp8")
+    A = g.QTensor(g.MXFP8, {"row_data": torch.from_numpy(_panel(a)).cuda(),
+                            "row_scale_mfma": torch.from_numpy(_scale_words(a_codes).view(np.int32)).cuda()})
+    B = g.QTensor(g.MXFP8, {"row_data": torch.from_numpy(_panel(b)).cuda(),
+                            "row_scale_mfma": torch.from_numpy(_scale_words(b_codes).view(np.int32)).cuda()})
+    sd = dev_splits([M])
+    c32 = g.grouped_gemm(g.GEMM_FPROP, rec, A, B, sd, M, N, K, out_dtype=g.OUT_FP32)
+    c16 = g.grouped_gemm(g.GEMM_FPROP, rec, A, B, sd, M, N, K)
+    torch.cuda.synchronize()
+    want = F.e4m3_decode(a) * np.exp2(np.repeat(a_codes.astype(np.float64) - 127.0, 32, axis=1))
+    assert np.array_equal(c32.cpu().numpy().astype(np.float64), want)
+    assert np.array_equal(bits16(c16).reshape(M, N) & 0x7FFF, F.f64_to_bf16_bits(want) & 0x7FFF)
+    assert np.array_equal(np.sign(c16.float().cpu().numpy()), np.sign(want))
+
+
 def test_gemm_nvfp4_expands_every_code_exactly():
     """Every E2M1 code under every finite E4M3 block scale (codes 0..126, one per row of A) through
     the GEMM's expansion of packed operands, read back exactly: B is the identity (E2M1 1.0 under
