@@ -1262,7 +1262,7 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
   // fetch several weight panels per column tile: then groups of 8 rows inside one expert
   // (the 128-expert workload: 19-26% fewer bytes fetched by its forward-shaped GEMMs, 1% off
   // the step; with 8 experts of 3-4K rows the same order was 1-2% slower).  WGRAD: 2 (3% faster
-  // than 4 on the 128-expert workload's fc1 weight gradient, 8 is 6% slower).
+  // than 4 on the 128-expert workload's fc1 weight gradient, 8 is 6% slower, 1 is 1% slower).
   a.expert_groups = (MODE == MODE_FPROP && g.G > 0 && g.M <= 512LL * g.G) ? 1 : 0;
   a.group_rows = MODE == MODE_WGRAD ? 2 : (a.expert_groups ? 8 : 4);
   // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split
