@@ -1261,7 +1261,8 @@ static hipError_t launch_mx(const GemmArgs& g, hipStream_t s) {
   // the groups average at most two 256-row tiles, most 4-row groups would straddle experts and
   // fetch several weight panels per column tile: then groups of 8 rows inside one expert
   // (the 128-expert workload: 19-26% fewer bytes fetched by its forward-shaped GEMMs, 1% off
-  // the step; with 8 experts of 3-4K rows the same order was 1-2% slower).  WGRAD: 2 (3% faster
+  // the step; with 8 experts of 3-4K rows the same order was 1-2% slower, with the 64 Zipf-sized
+  // experts of 768 rows on average 2-4%).  WGRAD: 2 (3% faster
   // than 4 on the 128-expert workload's fc1 weight gradient, 8 is 6% slower, 1 is 1% slower).
   a.expert_groups = (MODE == MODE_FPROP && g.G > 0 && g.M <= 512LL * g.G) ? 1 : 0;
   a.group_rows = MODE == MODE_WGRAD ? 2 : (a.expert_groups ? 8 : 4);
