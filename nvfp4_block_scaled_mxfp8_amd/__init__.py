@@ -8,7 +8,8 @@ implementation when it is missing.
 
 Names follow the C ABI: group_quantize (and group_quantize_noalloc), group_hadamard_amax,
 group_quantize_with_amax, weight_quantize, grouped_gemm, grouped_mlp_forward,
-grouped_mlp_backward.
+grouped_mlp_backward.  grouped_mlp (GroupedMLPFunction) puts the fused forward and backward
+under torch.autograd.
 """
 import ctypes
 import os
@@ -530,3 +531,44 @@ def grouped_mlp_wgrad(deferred, wgrad_dtype=OUT_BF16, out=None):
 def ffn_from_w2(w2q, rec, E, H):
     n = w2q.bufs["row_data"].numel()
     return (n // (E * H)) if rec.kind == MXFP8 else (2 * n // (E * H))
+
+
+# ----------------------------------------------------------------------------- torch autograd
+class GroupedMLPFunction(torch.autograd.Function):
+    """torch.autograd over grouped_mlp_forward / grouped_mlp_backward, so that the fused MLP sits
+    in a training step like the pages' fused op ("GEMM + Swiglu fused Grouped MLP for MXFP8",
+    sequence diagram: one forward call that saves its context, one backward call).
+
+    Inputs: x [M, H] bf16, probs [M] fp32, w1 [E, F1, H] and w2 [E, H, ffn] bf16 (the parameters
+    the weight gradients flow to), m_splits [E] int32 on the device, w1q / w2q the weights'
+    quantized forms (weight_quantize of w1 and w2, made by the caller once per weight update),
+    then activation, recipe and recompute as in grouped_mlp_forward.  The backward computes dx
+    only when x requires grad and dw1, dw2 (bf16) only when w1 or w2 does; dprobs always."""
+
+    @staticmethod
+    def forward(fctx, x, probs, w1, w2, m_splits, w1q, w2q, activation, rec, recompute=False):
+        need = fctx.needs_input_grad
+        y, c = grouped_mlp_forward(x, m_splits, w1q, w2q, probs.contiguous(), activation, rec,
+                                   recompute=recompute, input_requires_grad=need[0],
+                                   weight_requires_grad=need[2] or need[3])
+        fctx.mlp = (c, w1q, w2q)
+        fctx.save_for_backward(probs, m_splits)
+        return y
+
+    @staticmethod
+    def backward(fctx, dy):
+        probs, m_splits = fctx.saved_tensors
+        c, w1q, w2q = fctx.mlp
+        r = grouped_mlp_backward(dy.to(torch.bfloat16).contiguous(), m_splits, w1q, w2q, probs.contiguous(), c)
+        need = fctx.needs_input_grad
+        return (r["dx"] if need[0] else None, r["dprobs"] if need[1] else None,
+                r["dw1"] if need[2] else None, r["dw2"] if need[3] else None,
+                None, None, None, None, None, None)
+
+
+def grouped_mlp(x, probs, w1, w2, m_splits, activation, rec, w1q=None, w2q=None, recompute=False):
+    """y = the fused grouped MLP of x, differentiable in x, probs, w1 and w2 (GroupedMLPFunction).
+    w1q / w2q default to weight_quantize(w1 / w2, rec) made in this call."""
+    w1q = w1q if w1q is not None else weight_quantize(w1.detach(), rec)
+    w2q = w2q if w2q is not None else weight_quantize(w2.detach(), rec)
+    return GroupedMLPFunction.apply(x, probs, w1, w2, m_splits, w1q, w2q, activation, rec, recompute)
