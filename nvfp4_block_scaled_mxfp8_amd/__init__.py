@@ -543,11 +543,16 @@ class GroupedMLPFunction(torch.autograd.Function):
     the weight gradients flow to), m_splits [E] int32 on the device, w1q / w2q the weights'
     quantized forms (weight_quantize of w1 and w2, made by the caller once per weight update),
     then activation, recipe and recompute as in grouped_mlp_forward.  The backward computes dx
-    only when x requires grad and dw1, dw2 (bf16) only when w1 or w2 does; dprobs always."""
+    only when x requires grad and dw1, dw2 (bf16) only when w1 or w2 does; dprobs always.
+    accumulate_main_grad: the weight gradients are added in fp32 to w1.main_grad and w2.main_grad
+    (fp32 tensors of the weights' shapes, as in the pages' main_grad accumulation: review comments
+    on overwrite_main_grad) and autograd receives no gradient for w1 and w2."""
 
     @staticmethod
-    def forward(fctx, x, probs, w1, w2, m_splits, w1q, w2q, activation, rec, recompute=False):
+    def forward(fctx, x, probs, w1, w2, m_splits, w1q, w2q, activation, rec, recompute=False,
+                accumulate_main_grad=False):
         need = fctx.needs_input_grad
+        fctx.main_grads = (w1.main_grad, w2.main_grad) if accumulate_main_grad else None
         y, c = grouped_mlp_forward(x, m_splits, w1q, w2q, probs.contiguous(), activation, rec,
                                    recompute=recompute, input_requires_grad=need[0],
                                    weight_requires_grad=need[2] or need[3])
@@ -559,16 +564,26 @@ class GroupedMLPFunction(torch.autograd.Function):
     def backward(fctx, dy):
         probs, m_splits = fctx.saved_tensors
         c, w1q, w2q = fctx.mlp
-        r = grouped_mlp_backward(dy.to(torch.bfloat16).contiguous(), m_splits, w1q, w2q, probs.contiguous(), c)
         need = fctx.needs_input_grad
+        acc = fctx.main_grads is not None and c.weight_requires_grad
+        kw = {"wgrad_dtype": OUT_FP32_ACCUMULATE,
+              "out": {"dw1": fctx.main_grads[0], "dw2": fctx.main_grads[1]}} if acc else {}
+        r = grouped_mlp_backward(dy.to(torch.bfloat16).contiguous(), m_splits, w1q, w2q, probs.contiguous(), c,
+                                 **kw)
         return (r["dx"] if need[0] else None, r["dprobs"] if need[1] else None,
-                r["dw1"] if need[2] else None, r["dw2"] if need[3] else None,
-                None, None, None, None, None, None)
+                r["dw1"] if need[2] and not acc else None, r["dw2"] if need[3] and not acc else None,
+                None, None, None, None, None, None, None)
 
 
-def grouped_mlp(x, probs, w1, w2, m_splits, activation, rec, w1q=None, w2q=None, recompute=False):
+def grouped_mlp(x, probs, w1, w2, m_splits, activation, rec, w1q=None, w2q=None, recompute=False,
+                accumulate_main_grad=False):
     """y = the fused grouped MLP of x, differentiable in x, probs, w1 and w2 (GroupedMLPFunction).
     w1q / w2q default to weight_quantize(w1 / w2, rec) made in this call."""
+    if accumulate_main_grad:
+        for w, name in ((w1, "w1"), (w2, "w2")):
+            mg = getattr(w, "main_grad", None)
+            _check_out(mg, tuple(w.shape), torch.float32, f"{name}.main_grad")
     w1q = w1q if w1q is not None else weight_quantize(w1.detach(), rec)
     w2q = w2q if w2q is not None else weight_quantize(w2.detach(), rec)
-    return GroupedMLPFunction.apply(x, probs, w1, w2, m_splits, w1q, w2q, activation, rec, recompute)
+    return GroupedMLPFunction.apply(x, probs, w1, w2, m_splits, w1q, w2q, activation, rec, recompute,
+                                    accumulate_main_grad)

@@ -1,6 +1,7 @@
 """torch.autograd over the fused grouped MLP (GroupedMLPFunction, grouped_mlp): the gradients that
 autograd delivers are bit for bit those of the direct forward + backward calls on the same
-operands, and a frozen input or frozen weights get no gradient."""
+operands, a frozen input or frozen weights get no gradient, and with accumulate_main_grad the weight
+gradients are added to the weights' fp32 main_grad exactly as the backward's accumulate output adds them."""
 import pytest
 import torch
 
@@ -83,3 +84,30 @@ def test_autograd_quantizes_the_weights_itself_and_respects_frozen_tensors():
     _same(probs.grad, ref["dprobs"], "dprobs")
     _same(w1.grad, ref["dw1"], "dw1")
     _same(w2.grad, ref["dw2"], "dw2")
+
+
+@pytest.mark.parametrize("kind,act", CASES, ids=[f"{k}-{a}" for k, a in CASES])
+def test_autograd_accumulates_into_main_grad(kind, act):
+    print(f"autograd main_grad {kind} {act}", flush=True)
+    wl, d, rec, w1q, w2q = _case(kind, act)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    mg1 = torch.randn(d["w1"].shape, device="cuda", generator=gen)
+    mg2 = torch.randn(d["w2"].shape, device="cuda", generator=gen)
+    ref1, ref2 = mg1.clone(), mg2.clone()
+    w1 = d["w1"].clone().requires_grad_(True)
+    w2 = d["w2"].clone().requires_grad_(True)
+    w1.main_grad, w2.main_grad = mg1, mg2
+    for step in range(2):                         # two steps: the second adds to the first's sums
+        _, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], act, rec)
+        ref = g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx,
+                                     wgrad_dtype=g.OUT_FP32_ACCUMULATE, out={"dw1": ref1, "dw2": ref2})
+        x = d["x"].clone().requires_grad_(True)
+        y = g.grouped_mlp(x, d["probs"], w1, w2, d["splits"], act, rec, w1q=w1q, w2q=w2q,
+                          accumulate_main_grad=True)
+        y.backward(d["dy"])
+        torch.cuda.synchronize()
+        _same(x.grad, ref["dx"], f"dx step {step}")
+        _same(w1.main_grad, ref1, f"w1.main_grad step {step}")
+        _same(w2.main_grad, ref2, f"w2.main_grad step {step}")
+        assert w1.grad is None and w2.grad is None
