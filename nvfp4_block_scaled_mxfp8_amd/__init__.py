@@ -139,8 +139,19 @@ def _check(status):
         raise GmlpError(status, lib().gmlp_last_error().decode())
 
 
-def _p(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+def _dev_ptr(t, name="tensor"):
+    """The device address of a GPU tensor (None for None).  Every pointer the library receives
+    goes through here: a host tensor would reach a kernel as a host address, so it is refused."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        where = t.device if isinstance(t, torch.Tensor) else type(t).__name__
+        raise ValueError(f"{name}: a GPU tensor is required, got {where}")
+    return t.data_ptr()
+
+
+def _p(t, name="tensor"):
+    return ctypes.c_void_p(_dev_ptr(t, name) or 0)
 
 
 def _stream(device=None):
@@ -218,7 +229,7 @@ class QTensor:
     bufs: dict = field(default_factory=dict)
 
     def struct(self):
-        return GroupedQ(*[self.bufs[n].data_ptr() if self.bufs.get(n) is not None else None for n in _Q_FIELDS])
+        return GroupedQ(*[_dev_ptr(self.bufs.get(n), n) for n in _Q_FIELDS])
 
 
 def col_rows_bound(M, G):
@@ -339,7 +350,7 @@ def weight_quantize(w, rec, out=None):
         E = len(ws_list)
         N, K = ws_list[0].shape
         dev = ws_list[0].device
-        ptrs = (ctypes.c_void_p * E)(*[t.data_ptr() for t in ws_list])
+        ptrs = (ctypes.c_void_p * E)(*[_dev_ptr(t, f"w[{i}]") for i, t in enumerate(ws_list)])
         base = ctypes.c_void_p(0)
     else:
         w = _bits(w)
@@ -418,10 +429,10 @@ def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute
     cbuf = ctx.buf if ctx is not None else torch.empty(sizes["ctx_bytes"], dtype=torch.uint8, device=dev)
     y = y if y is not None else torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     s1, s2 = w1q.struct(), w2q.struct()
-    a = FwdArgs(x.data_ptr(), m_splits.data_ptr(), M, E, H, ffn, ctypes.pointer(s1), ctypes.pointer(s2),
-                probs.data_ptr() if M else None, act, rec, int(recompute), int(input_requires_grad),
-                int(weight_requires_grad), y.data_ptr() if M else None, cbuf.data_ptr(), cbuf.numel(),
-                ws.data_ptr(), ws.numel(), int(bool(fc2_amax_in_fc1)), clamp)
+    a = FwdArgs(_dev_ptr(x, "x"), _dev_ptr(m_splits, "m_splits"), M, E, H, ffn, ctypes.pointer(s1),
+                ctypes.pointer(s2), _dev_ptr(probs, "probs") if M else None, act, rec, int(recompute), int(input_requires_grad),
+                int(weight_requires_grad), _dev_ptr(y, "y") if M else None, _dev_ptr(cbuf, "ctx"), cbuf.numel(),
+                _dev_ptr(ws, "ws"), ws.numel(), int(bool(fc2_amax_in_fc1)), clamp)
     _check(lib().gmlp_grouped_mlp_forward(ctypes.byref(a), _stream(dev)))
     c = MlpContext(cbuf, M, E, H, ffn, act, rec, bool(recompute), bool(input_requires_grad),
                    bool(weight_requires_grad), clamp)
@@ -433,7 +444,7 @@ def forward_saved(ctx):
     post-RHT amax (fp32 [E]; None for MXFP8)."""
     a = FwdArgs()
     a.M, a.E, a.H, a.ffn, a.activation, a.recipe = ctx.M, ctx.E, ctx.H, ctx.ffn, ctx.activation, ctx.rec
-    a.recompute, a.ctx, a.ctx_bytes = int(ctx.recompute), ctx.buf.data_ptr(), ctx.buf.numel()
+    a.recompute, a.ctx, a.ctx_bytes = int(ctx.recompute), _dev_ptr(ctx.buf, "ctx"), ctx.buf.numel()
     h, pre, post = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
     _check(lib().gmlp_forward_saved(ctypes.byref(a), ctypes.byref(h), ctypes.byref(pre), ctypes.byref(post)))
     base = ctx.buf.data_ptr()
@@ -480,12 +491,11 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
             dw1 = o.get("dw1", torch.empty((E, F1, H), dtype=wdt, device=dev))
             dw2 = o.get("dw2", torch.empty((E, H, ffn), dtype=wdt, device=dev))
     s1, s2 = w1q.struct(), w2q.struct()
-    a = BwdArgs(dy.data_ptr(), m_splits.data_ptr(), M, E, H, ffn, ctypes.pointer(s1), ctypes.pointer(s2),
-                probs.data_ptr() if M else None, act, ctx.rec, int(ctx.recompute), int(ctx.input_requires_grad),
-                int(ctx.weight_requires_grad), dx.data_ptr() if (dx is not None and M) else None,
-                dprobs.data_ptr() if M else None, dw1.data_ptr() if dw1 is not None else None,
-                dw2.data_ptr() if dw2 is not None else None, wgrad_dtype, ctx.buf.data_ptr(), ctx.buf.numel(),
-                ws.data_ptr(), ws.numel(), int(bool(defer_wgrad)), ctx.clamp)
+    a = BwdArgs(_dev_ptr(dy, "dy"), _dev_ptr(m_splits, "m_splits"), M, E, H, ffn, ctypes.pointer(s1),
+                ctypes.pointer(s2), _dev_ptr(probs, "probs") if M else None, act, ctx.rec, int(ctx.recompute), int(ctx.input_requires_grad),
+                int(ctx.weight_requires_grad), _dev_ptr(dx, "dx") if M else None,
+                _dev_ptr(dprobs, "dprobs") if M else None, _dev_ptr(dw1, "dw1"), _dev_ptr(dw2, "dw2"),
+                wgrad_dtype, _dev_ptr(ctx.buf, "ctx"), ctx.buf.numel(), _dev_ptr(ws, "ws"), ws.numel(), int(bool(defer_wgrad)), ctx.clamp)
     _check(lib().gmlp_grouped_mlp_backward(ctypes.byref(a), _stream(dev)))
     res = {"dx": dx, "dprobs": dprobs, "dw1": dw1, "dw2": dw2}
     if defer_wgrad and ctx.weight_requires_grad:
@@ -519,11 +529,11 @@ def grouped_mlp_wgrad(deferred, wgrad_dtype=OUT_BF16, out=None):
         dw1 = o.get("dw1", torch.empty((E, F1, H), dtype=wdt, device=dev))
         dw2 = o.get("dw2", torch.empty((E, H, ffn), dtype=wdt, device=dev))
     a = BwdArgs()
-    a.m_splits, a.M, a.E, a.H, a.ffn = deferred.m_splits.data_ptr(), ctx.M, E, H, ffn
+    a.m_splits, a.M, a.E, a.H, a.ffn = _dev_ptr(deferred.m_splits, "m_splits"), ctx.M, E, H, ffn
     a.activation, a.recipe, a.recompute, a.tanh_clamp_scale = act, ctx.rec, int(ctx.recompute), ctx.clamp
     a.input_requires_grad, a.weight_requires_grad = int(ctx.input_requires_grad), 1
-    a.dw1, a.dw2, a.wgrad_dtype = dw1.data_ptr(), dw2.data_ptr(), wgrad_dtype
-    a.ctx, a.ctx_bytes, a.ws, a.ws_bytes = ctx.buf.data_ptr(), ctx.buf.numel(), ws.data_ptr(), ws.numel()
+    a.dw1, a.dw2, a.wgrad_dtype = _dev_ptr(dw1, "dw1"), _dev_ptr(dw2, "dw2"), wgrad_dtype
+    a.ctx, a.ctx_bytes, a.ws, a.ws_bytes = _dev_ptr(ctx.buf, "ctx"), ctx.buf.numel(), _dev_ptr(ws, "ws"), ws.numel()
     _check(lib().gmlp_grouped_mlp_wgrad(ctypes.byref(a), _stream(dev)))
     return {"dw1": dw1, "dw2": dw2}
 

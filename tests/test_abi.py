@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import nvfp4_block_scaled_mxfp8_amd as g
 
@@ -168,3 +169,24 @@ def test_accumulating_gradients_need_the_callers_main_grads():
     deferred = g.DeferredWgrad(splits, ctx, torch.empty(0, dtype=torch.uint8))
     with pytest.raises(ValueError, match="main_grad"):
         g.grouped_mlp_wgrad(deferred, wgrad_dtype=g.OUT_FP32_ACCUMULATE)
+
+
+def test_binding_refuses_host_tensors():
+    """The Python binding hands the library device addresses only: a host tensor among the
+    arguments is refused (ValueError naming it) before any library call that launches work."""
+    rec = g.recipe("mxfp8")
+    x = torch.zeros((64, 128), dtype=torch.bfloat16)
+    splits = torch.tensor([64], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        g.group_quantize(x, splits, rec)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        g.group_hadamard_amax(x, splits, 0x5A5A)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        g.weight_quantize(torch.zeros((2, 128, 128), dtype=torch.bfloat16), rec)
+    with pytest.raises(ValueError, match=r"w\[0\]"):
+        g.weight_quantize([torch.zeros((128, 128), dtype=torch.bfloat16)] * 2, rec)
+    q = g.alloc_grouped_q(rec, 64, 128, 1, device="cpu")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        g.grouped_gemm(g.GEMM_FPROP, rec, q, q, splits, 64, 128, 128)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        g.read_device_flags(torch.zeros(16, dtype=torch.uint8))
