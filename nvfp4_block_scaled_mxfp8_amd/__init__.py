@@ -269,8 +269,27 @@ def _bits(x):
     return x.contiguous()
 
 
+def _splits(m_splits, G=None):
+    """m_splits as the library reads it: int32 [G] on the device, contiguous."""
+    if not isinstance(m_splits, torch.Tensor) or m_splits.dtype != torch.int32 or m_splits.dim() != 1:
+        raise TypeError("m_splits: a 1-D int32 tensor is required")
+    if G is not None and m_splits.numel() != G:
+        raise ValueError(f"m_splits: {G} groups expected, got {m_splits.numel()}")
+    return m_splits.contiguous()
+
+
+def _probs(probs, M):
+    """probs as the library reads it: fp32 [M] (read as M consecutive floats)."""
+    if M == 0:
+        return probs
+    if not isinstance(probs, torch.Tensor) or probs.dtype != torch.float32 or probs.numel() != M:
+        raise TypeError(f"probs: an fp32 tensor of {M} elements is required")
+    return probs.contiguous()
+
+
 def group_quantize(x, m_splits, rec, want_row=True, want_col=True, out=None, ws=None):
     x = _bits(x)
+    m_splits = _splits(m_splits)
     M, K = x.shape
     G = m_splits.numel()
     out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
@@ -285,6 +304,7 @@ def group_quantize_noalloc(x, m_splits, rec, want_row=True, want_col=True, out=N
     """group_quantize with the library's fixed device workspace (no workspace argument; at most
     1024 groups).  out must be given by callers that cannot allocate."""
     x = _bits(x)
+    m_splits = _splits(m_splits)
     M, K = x.shape
     G = m_splits.numel()
     out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
@@ -296,6 +316,7 @@ def group_quantize_noalloc(x, m_splits, rec, want_row=True, want_col=True, out=N
 
 def group_hadamard_amax(x, m_splits, sign_mask, ws=None):
     x = _bits(x)
+    m_splits = _splits(m_splits)
     M, K = x.shape
     G = m_splits.numel()
     pre = torch.empty(G, dtype=torch.float32, device=x.device)
@@ -309,6 +330,7 @@ def group_hadamard_amax(x, m_splits, sign_mask, ws=None):
 def group_quantize_with_amax(x, m_splits, rec, amax_pre, amax_post, want_row=True, want_col=True, out=None,
                              ws=None):
     x = _bits(x)
+    m_splits = _splits(m_splits)
     M, K = x.shape
     G = m_splits.numel()
     out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
@@ -379,6 +401,7 @@ def _check_out(t, shape, dtype, name):
 
 def grouped_gemm(layout, rec, a, b, m_splits, M, n, k, out_dtype=OUT_BF16, ws=None, out=None):
     """out: the output tensor (required for OUT_FP32_ACCUMULATE, whose product is added to it)."""
+    m_splits = _splits(m_splits)
     G = m_splits.numel()
     dev = m_splits.device
     dt = torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32
@@ -420,6 +443,8 @@ def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute
     fc2 input's amax in the fc1 GEMM's epilogue instead of a pass over h (the same values)."""
     x = _bits(x)
     M, H = x.shape
+    m_splits = _splits(m_splits)
+    probs = _probs(probs, M)
     E = m_splits.numel()
     act, clamp = activation_spec(activation)
     ffn = ffn_from_w2(w2q, rec, E, H)
@@ -427,7 +452,10 @@ def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute
     dev = x.device
     ws = ws if ws is not None else torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
     cbuf = ctx.buf if ctx is not None else torch.empty(sizes["ctx_bytes"], dtype=torch.uint8, device=dev)
-    y = y if y is not None else torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    if y is not None:
+        _check_out(y, (M, H), torch.bfloat16, "y")
+    else:
+        y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     s1, s2 = w1q.struct(), w2q.struct()
     a = FwdArgs(_dev_ptr(x, "x"), _dev_ptr(m_splits, "m_splits"), M, E, H, ffn, ctypes.pointer(s1),
                 ctypes.pointer(s2), _dev_ptr(probs, "probs") if M else None, act, rec, int(recompute), int(input_requires_grad),
@@ -471,16 +499,24 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
     dy = _bits(dy)
     M, H = dy.shape
     E, ffn, act = ctx.E, ctx.ffn, ctx.activation
+    m_splits = _splits(m_splits, E)
+    probs = _probs(probs, M)
     F1 = 2 * ffn if is_glu(act) else ffn
     dev = dy.device
     sizes = query_sizes(M, E, H, ffn, act, ctx.rec, ctx.recompute)
     ws = ws if ws is not None else torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
     wdt = torch.bfloat16 if wgrad_dtype == OUT_BF16 else torch.float32
     o = out or {}
-    dx = o.get("dx") if ctx.input_requires_grad else None
-    if ctx.input_requires_grad and dx is None:
-        dx = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-    dprobs = o.get("dprobs", torch.empty(M, dtype=torch.float32, device=dev))
+
+    def given_or_new(name, shape, dtype):
+        t = o.get(name)
+        if t is None:
+            return torch.empty(shape, dtype=dtype, device=dev)
+        _check_out(t, shape, dtype, name)
+        return t
+
+    dx = given_or_new("dx", (M, H), torch.bfloat16) if ctx.input_requires_grad else None
+    dprobs = given_or_new("dprobs", (M,), torch.float32)
     dw1 = dw2 = None
     if ctx.weight_requires_grad and not defer_wgrad:
         if wgrad_dtype == OUT_FP32_ACCUMULATE:
@@ -488,8 +524,8 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
             _check_out(dw1, (E, F1, H), wdt, "dw1 main_grad")
             _check_out(dw2, (E, H, ffn), wdt, "dw2 main_grad")
         else:
-            dw1 = o.get("dw1", torch.empty((E, F1, H), dtype=wdt, device=dev))
-            dw2 = o.get("dw2", torch.empty((E, H, ffn), dtype=wdt, device=dev))
+            dw1 = given_or_new("dw1", (E, F1, H), wdt)
+            dw2 = given_or_new("dw2", (E, H, ffn), wdt)
     s1, s2 = w1q.struct(), w2q.struct()
     a = BwdArgs(_dev_ptr(dy, "dy"), _dev_ptr(m_splits, "m_splits"), M, E, H, ffn, ctypes.pointer(s1),
                 ctypes.pointer(s2), _dev_ptr(probs, "probs") if M else None, act, ctx.rec, int(ctx.recompute), int(ctx.input_requires_grad),
@@ -526,8 +562,15 @@ def grouped_mlp_wgrad(deferred, wgrad_dtype=OUT_BF16, out=None):
         _check_out(dw1, (E, F1, H), wdt, "dw1 main_grad")
         _check_out(dw2, (E, H, ffn), wdt, "dw2 main_grad")
     else:
-        dw1 = o.get("dw1", torch.empty((E, F1, H), dtype=wdt, device=dev))
-        dw2 = o.get("dw2", torch.empty((E, H, ffn), dtype=wdt, device=dev))
+        dw1, dw2 = o.get("dw1"), o.get("dw2")
+        if dw1 is not None:
+            _check_out(dw1, (E, F1, H), wdt, "dw1")
+        else:
+            dw1 = torch.empty((E, F1, H), dtype=wdt, device=dev)
+        if dw2 is not None:
+            _check_out(dw2, (E, H, ffn), wdt, "dw2")
+        else:
+            dw2 = torch.empty((E, H, ffn), dtype=wdt, device=dev)
     a = BwdArgs()
     a.m_splits, a.M, a.E, a.H, a.ffn = _dev_ptr(deferred.m_splits, "m_splits"), ctx.M, E, H, ffn
     a.activation, a.recipe, a.recompute, a.tanh_clamp_scale = act, ctx.rec, int(ctx.recompute), ctx.clamp

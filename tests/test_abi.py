@@ -161,11 +161,12 @@ def test_accumulating_gradients_need_the_callers_main_grads():
     ctx = g.MlpContext(torch.empty(0, dtype=torch.uint8), M, E, H, ffn, g.SWIGLU, rec, False, True, True)
     dy = torch.zeros(M, H, dtype=torch.bfloat16)
     splits = torch.tensor([M // 2, M // 2], dtype=torch.int32)
+    probs = torch.zeros(M)
     with pytest.raises(ValueError, match="main_grad"):
-        g.grouped_mlp_backward(dy, splits, None, None, None, ctx, wgrad_dtype=g.OUT_FP32_ACCUMULATE)
+        g.grouped_mlp_backward(dy, splits, None, None, probs, ctx, wgrad_dtype=g.OUT_FP32_ACCUMULATE)
     bad = {"dw1": torch.zeros(E, 2 * ffn, H, dtype=torch.bfloat16), "dw2": torch.zeros(E, H, ffn)}
     with pytest.raises(ValueError, match="dw1 main_grad"):
-        g.grouped_mlp_backward(dy, splits, None, None, None, ctx, wgrad_dtype=g.OUT_FP32_ACCUMULATE, out=bad)
+        g.grouped_mlp_backward(dy, splits, None, None, probs, ctx, wgrad_dtype=g.OUT_FP32_ACCUMULATE, out=bad)
     deferred = g.DeferredWgrad(splits, ctx, torch.empty(0, dtype=torch.uint8))
     with pytest.raises(ValueError, match="main_grad"):
         g.grouped_mlp_wgrad(deferred, wgrad_dtype=g.OUT_FP32_ACCUMULATE)
@@ -190,3 +191,31 @@ def test_binding_refuses_host_tensors():
         g.grouped_gemm(g.GEMM_FPROP, rec, q, q, splits, 64, 128, 128)
     with pytest.raises(ValueError, match="GPU tensor"):
         g.read_device_flags(torch.zeros(16, dtype=torch.uint8))
+
+
+def test_binding_checks_the_dtypes_and_sizes_the_kernels_read():
+    """probs is read as M fp32 values and m_splits as G int32 values: other dtypes or sizes would be
+    read past their ends or misread, so the binding refuses them (host check, before any launch);
+    caller-given outputs must have the shapes and dtypes the kernels write."""
+    E, M, H, ffn = 2, 64, 128, 128
+    rec = g.recipe("mxfp8")
+    ctx = g.MlpContext(torch.empty(0, dtype=torch.uint8), M, E, H, ffn, g.SWIGLU, rec, False, True, True)
+    dy = torch.zeros(M, H, dtype=torch.bfloat16)
+    splits = torch.tensor([M // 2, M // 2], dtype=torch.int32)
+    probs = torch.zeros(M)
+    with pytest.raises(TypeError, match="probs"):
+        g.grouped_mlp_backward(dy, splits, None, None, probs.to(torch.bfloat16), ctx)
+    with pytest.raises(TypeError, match="probs"):
+        g.grouped_mlp_backward(dy, splits, None, None, probs[:-1], ctx)
+    with pytest.raises(TypeError, match="m_splits"):
+        g.grouped_mlp_backward(dy, splits.long(), None, None, probs, ctx)
+    with pytest.raises(ValueError, match="m_splits"):
+        g.grouped_mlp_backward(dy, splits[:1], None, None, probs, ctx)
+    with pytest.raises(ValueError, match="dprobs"):
+        g.grouped_mlp_backward(dy, splits, None, None, probs, ctx, out={"dprobs": torch.zeros(M - 1)})
+    with pytest.raises(ValueError, match="dx"):
+        g.grouped_mlp_backward(dy, splits, None, None, probs, ctx, out={"dx": torch.zeros(M, H)})
+    with pytest.raises(TypeError, match="m_splits"):
+        g.group_quantize(dy, splits.long(), rec)
+    with pytest.raises(TypeError, match="probs"):
+        g.grouped_mlp_forward(dy, splits, None, None, probs.double(), "swiglu", rec)
