@@ -292,6 +292,8 @@ def group_quantize(x, m_splits, rec, want_row=True, want_col=True, out=None, ws=
     m_splits = _splits(m_splits)
     M, K = x.shape
     G = m_splits.numel()
+    if out is not None:
+        _check_q_sizes(out, alloc_grouped_q(rec, M, K, G, want_row, want_col, "meta"), "out")
     out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
     ws = ws if ws is not None else quant_workspace(G, x.device)
     q = out.struct()
@@ -307,6 +309,8 @@ def group_quantize_noalloc(x, m_splits, rec, want_row=True, want_col=True, out=N
     m_splits = _splits(m_splits)
     M, K = x.shape
     G = m_splits.numel()
+    if out is not None:
+        _check_q_sizes(out, alloc_grouped_q(rec, M, K, G, want_row, want_col, "meta"), "out")
     out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
     q = out.struct()
     _check(lib().gmlp_group_quantize_noalloc(_p(x), M, K, _p(m_splits), G, rec, int(want_row), int(want_col),
@@ -333,6 +337,8 @@ def group_quantize_with_amax(x, m_splits, rec, amax_pre, amax_post, want_row=Tru
     m_splits = _splits(m_splits)
     M, K = x.shape
     G = m_splits.numel()
+    if out is not None:
+        _check_q_sizes(out, alloc_grouped_q(rec, M, K, G, want_row, want_col, "meta"), "out")
     out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
     out.bufs["amax_pre"] = amax_pre
     out.bufs["amax_post"] = amax_post
@@ -365,21 +371,42 @@ def alloc_weight_q(rec, E, N, K, device="cuda", bf16_panels=True):
     return QTensor(rec.kind, b)
 
 
+def _check_q_sizes(q, spec, name):
+    """Every buffer q holds must be at least as large as the same buffer of spec (the allocator's
+    layout of the call's sizes, made on the meta device): the kernels address the buffers from the
+    call's sizes, not from the buffers.  A buffer q lacks is left to the library's null check."""
+    if not isinstance(q, QTensor):
+        raise TypeError(f"{name}: a QTensor is required")
+    for k, t in spec.bufs.items():
+        b = q.bufs.get(k)
+        if b is None:
+            continue
+        need, have = t.numel() * t.element_size(), b.numel() * b.element_size()
+        if have < need or not b.is_contiguous():
+            raise ValueError(f"{name}.{k}: a contiguous buffer of at least {need} bytes is required, got {have}")
+
+
 def weight_quantize(w, rec, out=None):
     """w: stacked bf16 [E, N, K] tensor, or a list of E [N, K] tensors (discrete weights)."""
     if isinstance(w, (list, tuple)):
         ws_list = [_bits(t) for t in w]
         E = len(ws_list)
         N, K = ws_list[0].shape
+        if any(tuple(t.shape) != (N, K) for t in ws_list):
+            raise ValueError(f"w: every expert's weight must have the shape {(N, K)}")
         dev = ws_list[0].device
-        ptrs = (ctypes.c_void_p * E)(*[_dev_ptr(t, f"w[{i}]") for i, t in enumerate(ws_list)])
-        base = ctypes.c_void_p(0)
     else:
         w = _bits(w)
         E, N, K = w.shape
         dev = w.device
+    if out is not None:
+        _check_q_sizes(out, alloc_weight_q(rec, E, N, K, "meta"), "out")
+    if isinstance(w, (list, tuple)):
+        ptrs = (ctypes.c_void_p * E)(*[_dev_ptr(t, f"w[{i}]") for i, t in enumerate(ws_list)])
+        base = ctypes.c_void_p(0)
+    else:
         ptrs = None
-        base = _p(w)
+        base = _p(w, "w")
     out = out or alloc_weight_q(rec, E, N, K, dev)
     ws = quant_workspace(1, dev)
     q = out.struct()
@@ -448,6 +475,9 @@ def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute
     E = m_splits.numel()
     act, clamp = activation_spec(activation)
     ffn = ffn_from_w2(w2q, rec, E, H)
+    F1 = 2 * ffn if is_glu(act) else ffn
+    _check_q_sizes(w1q, alloc_weight_q(rec, E, F1, H, "meta"), "w1q")
+    _check_q_sizes(w2q, alloc_weight_q(rec, E, H, ffn, "meta"), "w2q")
     sizes = query_sizes(M, E, H, ffn, act, rec, recompute)
     dev = x.device
     ws = ws if ws is not None else torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
@@ -526,6 +556,8 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
         else:
             dw1 = given_or_new("dw1", (E, F1, H), wdt)
             dw2 = given_or_new("dw2", (E, H, ffn), wdt)
+    _check_q_sizes(w1q, alloc_weight_q(ctx.rec, E, F1, H, "meta"), "w1q")
+    _check_q_sizes(w2q, alloc_weight_q(ctx.rec, E, H, ffn, "meta"), "w2q")
     s1, s2 = w1q.struct(), w2q.struct()
     a = BwdArgs(_dev_ptr(dy, "dy"), _dev_ptr(m_splits, "m_splits"), M, E, H, ffn, ctypes.pointer(s1),
                 ctypes.pointer(s2), _dev_ptr(probs, "probs") if M else None, act, ctx.rec, int(ctx.recompute), int(ctx.input_requires_grad),

@@ -219,3 +219,27 @@ def test_binding_checks_the_dtypes_and_sizes_the_kernels_read():
         g.group_quantize(dy, splits.long(), rec)
     with pytest.raises(TypeError, match="probs"):
         g.grouped_mlp_forward(dy, splits, None, None, probs.double(), "swiglu", rec)
+
+
+def test_binding_checks_quantized_buffer_sizes():
+    """A caller-given quantized tensor smaller than the call's sizes need is refused (host check,
+    before any launch): the kernels address it from the sizes, not from the buffers."""
+    rec = g.recipe("mxfp8")
+    x = torch.zeros((64, 128), dtype=torch.bfloat16)
+    splits = torch.tensor([64], dtype=torch.int32)
+    small = g.alloc_grouped_q(rec, 32, 128, 1, device="cpu")
+    with pytest.raises(ValueError, match="row_data"):
+        g.group_quantize(x, splits, rec, out=small)
+    wsmall = g.alloc_weight_q(rec, 2, 128, 64, device="cpu")
+    with pytest.raises(ValueError, match="out.row_data"):
+        g.weight_quantize(torch.zeros((2, 128, 128), dtype=torch.bfloat16), rec, out=wsmall)
+    w1q = g.alloc_weight_q(rec, 2, 256, 128, device="cpu")       # SwiGLU F1 = 2 ffn with ffn 128
+    w2q = g.alloc_weight_q(rec, 2, 128, 128, device="cpu")
+    probs = torch.zeros(64)
+    splits2 = torch.tensor([32, 32], dtype=torch.int32)
+    w1_small = g.alloc_weight_q(rec, 2, 128, 128, device="cpu")  # F1 = ffn: too small for SwiGLU
+    with pytest.raises(ValueError, match="w1q"):
+        g.grouped_mlp_forward(x, splits2, w1_small, w2q, probs, "swiglu", rec)
+    # the right sizes pass the size check and stop at the host-tensor check
+    with pytest.raises(ValueError, match="GPU tensor"):
+        g.grouped_mlp_forward(x, splits2, w1q, w2q, probs, "swiglu", rec)
