@@ -293,7 +293,7 @@ def group_quantize(x, m_splits, rec, want_row=True, want_col=True, out=None, ws=
     M, K = x.shape
     G = m_splits.numel()
     if out is not None:
-        _check_q_sizes(out, alloc_grouped_q(rec, M, K, G, want_row, want_col, "meta"), "out")
+        _check_q_sizes(out, _grouped_need(rec, M, K, G, want_row, want_col), "out")
     out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
     ws = ws if ws is not None else quant_workspace(G, x.device)
     q = out.struct()
@@ -310,7 +310,7 @@ def group_quantize_noalloc(x, m_splits, rec, want_row=True, want_col=True, out=N
     M, K = x.shape
     G = m_splits.numel()
     if out is not None:
-        _check_q_sizes(out, alloc_grouped_q(rec, M, K, G, want_row, want_col, "meta"), "out")
+        _check_q_sizes(out, _grouped_need(rec, M, K, G, want_row, want_col), "out")
     out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
     q = out.struct()
     _check(lib().gmlp_group_quantize_noalloc(_p(x), M, K, _p(m_splits), G, rec, int(want_row), int(want_col),
@@ -338,7 +338,7 @@ def group_quantize_with_amax(x, m_splits, rec, amax_pre, amax_post, want_row=Tru
     M, K = x.shape
     G = m_splits.numel()
     if out is not None:
-        _check_q_sizes(out, alloc_grouped_q(rec, M, K, G, want_row, want_col, "meta"), "out")
+        _check_q_sizes(out, _grouped_need(rec, M, K, G, want_row, want_col), "out")
     out = out or alloc_grouped_q(rec, M, K, G, want_row, want_col, x.device)
     out.bufs["amax_pre"] = amax_pre
     out.bufs["amax_post"] = amax_post
@@ -371,19 +371,46 @@ def alloc_weight_q(rec, E, N, K, device="cuda", bf16_panels=True):
     return QTensor(rec.kind, b)
 
 
-def _check_q_sizes(q, spec, name):
-    """Every buffer q holds must be at least as large as the same buffer of spec (the allocator's
-    layout of the call's sizes, made on the meta device): the kernels address the buffers from the
-    call's sizes, not from the buffers.  A buffer q lacks is left to the library's null check."""
+def _grouped_need(rec, M, K, G, row=True, col=True):
+    """Bytes the kernels address in each buffer of a group-quantized [M, K] tensor (layouts of
+    include/gmlp.h).  Column-wise buffers hold K x sum P_g elements, P_g = m_g rounded up to 128,
+    which depends on the splits on the device: the bound here is the least any splits of M rows
+    need (P = M rounded up to 128); alloc_grouped_q sizes them for the most (M + 127 G)."""
+    P = (M + COL_PAD - 1) // COL_PAD * COL_PAD
+    need = {}
+    if rec.kind == MXFP8:
+        if row:
+            need.update(row_data=M * K, row_scale=M * K // 32, row_scale_mfma=4 * ((K + 127) // 128) * M)
+        if col:
+            need.update(col_data=K * P, col_scale=K * P // 32, col_scale_mfma=4 * K * P // 128)
+    else:
+        if row:
+            need.update(row_data=M * K // 2, row_scale=M * K // 16, row_bf16=2 * M * K)
+        if col:
+            need.update(col_data=K * P // 2, col_scale=K * P // 16, col_bf16=2 * K * P)
+        need.update(amax_pre=4 * G, amax_post=4 * G)
+    return need
+
+
+def _weight_need(rec, E, N, K):
+    """Bytes the kernels address in each buffer of a quantized weight [E, N, K] (alloc_weight_q's
+    layout)."""
+    return {k: t.numel() * t.element_size() for k, t in alloc_weight_q(rec, E, N, K, "meta").bufs.items()}
+
+
+def _check_q_sizes(q, need, name):
+    """Every buffer q holds must be a contiguous buffer of at least need[buffer] bytes: the kernels
+    address the buffers from the call's sizes, not from the buffers.  A buffer q lacks is left to
+    the library's null check."""
     if not isinstance(q, QTensor):
         raise TypeError(f"{name}: a QTensor is required")
-    for k, t in spec.bufs.items():
+    for k, n in need.items():
         b = q.bufs.get(k)
         if b is None:
             continue
-        need, have = t.numel() * t.element_size(), b.numel() * b.element_size()
-        if have < need or not b.is_contiguous():
-            raise ValueError(f"{name}.{k}: a contiguous buffer of at least {need} bytes is required, got {have}")
+        have = b.numel() * b.element_size()
+        if have < n or not b.is_contiguous():
+            raise ValueError(f"{name}.{k}: a contiguous buffer of at least {n} bytes is required, got {have}")
 
 
 def weight_quantize(w, rec, out=None):
@@ -400,7 +427,7 @@ def weight_quantize(w, rec, out=None):
         E, N, K = w.shape
         dev = w.device
     if out is not None:
-        _check_q_sizes(out, alloc_weight_q(rec, E, N, K, "meta"), "out")
+        _check_q_sizes(out, _weight_need(rec, E, N, K), "out")
     if isinstance(w, (list, tuple)):
         ptrs = (ctypes.c_void_p * E)(*[_dev_ptr(t, f"w[{i}]") for i, t in enumerate(ws_list)])
         base = ctypes.c_void_p(0)
@@ -438,6 +465,13 @@ def grouped_gemm(layout, rec, a, b, m_splits, M, n, k, out_dtype=OUT_BF16, ws=No
         c = out
     else:
         c = torch.empty(shape, dtype=dt, device=dev)
+    if layout == GEMM_WGRAD:
+        _check_q_sizes(a, _grouped_need(rec, M, n, G, row=False), "a")
+        _check_q_sizes(b, _grouped_need(rec, M, k, G, row=False), "b")
+    else:
+        _check_q_sizes(a, _grouped_need(rec, M, k, G, col=False), "a")
+        wn, wk = (n, k) if layout == GEMM_FPROP else (k, n)      # the weight's [N, K]
+        _check_q_sizes(b, _weight_need(rec, G, wn, wk), "b")
     if ws is None:
         ws = torch.empty(grouped_gemm_ws_bytes(layout, rec, G, M, n, k), dtype=torch.uint8, device=dev)
     qa, qb = a.struct(), b.struct()
@@ -476,8 +510,8 @@ def grouped_mlp_forward(x, m_splits, w1q, w2q, probs, activation, rec, recompute
     act, clamp = activation_spec(activation)
     ffn = ffn_from_w2(w2q, rec, E, H)
     F1 = 2 * ffn if is_glu(act) else ffn
-    _check_q_sizes(w1q, alloc_weight_q(rec, E, F1, H, "meta"), "w1q")
-    _check_q_sizes(w2q, alloc_weight_q(rec, E, H, ffn, "meta"), "w2q")
+    _check_q_sizes(w1q, _weight_need(rec, E, F1, H), "w1q")
+    _check_q_sizes(w2q, _weight_need(rec, E, H, ffn), "w2q")
     sizes = query_sizes(M, E, H, ffn, act, rec, recompute)
     dev = x.device
     ws = ws if ws is not None else torch.empty(sizes["ws_bytes"], dtype=torch.uint8, device=dev)
@@ -556,8 +590,8 @@ def grouped_mlp_backward(dy, m_splits, w1q, w2q, probs, ctx, wgrad_dtype=OUT_BF1
         else:
             dw1 = given_or_new("dw1", (E, F1, H), wdt)
             dw2 = given_or_new("dw2", (E, H, ffn), wdt)
-    _check_q_sizes(w1q, alloc_weight_q(ctx.rec, E, F1, H, "meta"), "w1q")
-    _check_q_sizes(w2q, alloc_weight_q(ctx.rec, E, H, ffn, "meta"), "w2q")
+    _check_q_sizes(w1q, _weight_need(ctx.rec, E, F1, H), "w1q")
+    _check_q_sizes(w2q, _weight_need(ctx.rec, E, H, ffn), "w2q")
     s1, s2 = w1q.struct(), w2q.struct()
     a = BwdArgs(_dev_ptr(dy, "dy"), _dev_ptr(m_splits, "m_splits"), M, E, H, ffn, ctypes.pointer(s1),
                 ctypes.pointer(s2), _dev_ptr(probs, "probs") if M else None, act, ctx.rec, int(ctx.recompute), int(ctx.input_requires_grad),

@@ -188,7 +188,7 @@ def test_binding_refuses_host_tensors():
         g.weight_quantize([torch.zeros((128, 128), dtype=torch.bfloat16)] * 2, rec)
     q = g.alloc_grouped_q(rec, 64, 128, 1, device="cpu")
     with pytest.raises(ValueError, match="GPU tensor"):
-        g.grouped_gemm(g.GEMM_FPROP, rec, q, q, splits, 64, 128, 128)
+        g.grouped_gemm(g.GEMM_FPROP, rec, q, q, splits, 64, 64, 128)
     with pytest.raises(ValueError, match="GPU tensor"):
         g.read_device_flags(torch.zeros(16, dtype=torch.uint8))
 
