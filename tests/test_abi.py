@@ -243,3 +243,19 @@ def test_binding_checks_quantized_buffer_sizes():
     # the right sizes pass the size check and stop at the host-tensor check
     with pytest.raises(ValueError, match="GPU tensor"):
         g.grouped_mlp_forward(x, splits2, w1q, w2q, probs, "swiglu", rec)
+
+
+@pytest.mark.parametrize("kind", ["mxfp8", "nvfp4"])
+def test_allocators_satisfy_the_size_checks(kind):
+    """What alloc_grouped_q and alloc_weight_q allocate passes the binding's size checks for the
+    same sizes (the checks take the least the kernels address; the allocators the most)."""
+    rec = g.recipe(kind, 1)
+    for M, K, G in ((1, 128, 1), (192, 256, 2), (1000, 384, 7), (0, 128, 3)):
+        g._check_q_sizes(g.alloc_grouped_q(rec, M, K, G, device="meta"), g._grouped_need(rec, M, K, G), "q")
+    for E, N, K in ((1, 128, 128), (3, 256, 384)):
+        g._check_q_sizes(g.alloc_weight_q(rec, E, N, K, device="meta"), g._weight_need(rec, E, N, K), "w")
+    # and one buffer a row short is refused
+    q = g.alloc_grouped_q(rec, 192, 256, 2, device="meta")
+    q.bufs["row_data"] = q.bufs["row_data"][:-1]
+    with pytest.raises(ValueError, match="row_data"):
+        g._check_q_sizes(q, g._grouped_need(rec, 192, 256, 2), "q")
