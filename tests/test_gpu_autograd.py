@@ -111,3 +111,18 @@ def test_autograd_accumulates_into_main_grad(kind, act):
         _same(w1.main_grad, ref1, f"w1.main_grad step {step}")
         _same(w2.main_grad, ref2, f"w2.main_grad step {step}")
         assert w1.grad is None and w2.grad is None
+
+
+def test_autograd_only_the_routing_probabilities_trained():
+    """x and the weights frozen, probs trained: the backward computes dprobs alone (no dgrad or
+    wgrad GEMM of fc1), bit for bit the full backward's."""
+    wl, d, rec, w1q, w2q = _case("nvfp4", "srelu")
+    _, ctx = g.grouped_mlp_forward(d["x"], d["splits"], w1q, w2q, d["probs"], "srelu", rec)
+    ref = g.grouped_mlp_backward(d["dy"], d["splits"], w1q, w2q, d["probs"], ctx)
+    probs = d["probs"].clone().requires_grad_(True)
+    w1, w2 = d["w1"].clone(), d["w2"].clone()
+    y = g.grouped_mlp(d["x"], probs, w1, w2, d["splits"], "srelu", rec, w1q=w1q, w2q=w2q)
+    y.backward(d["dy"])
+    torch.cuda.synchronize()
+    _same(probs.grad, ref["dprobs"], "dprobs")
+    assert w1.grad is None and w2.grad is None
